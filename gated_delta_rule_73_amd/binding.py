@@ -1,0 +1,174 @@
+"""ctypes binding of libgdr.so (the C ABI declared in include/gdr.h).
+
+Argument marshalling only: tensors are passed as device pointers, the workspace and outputs
+are allocated with torch, and every computation runs in the library's HIP kernels.  There
+is no fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgdr.so")
+
+GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
+VARIANTS = {"deltanet": 0, "gated": 1, "kda": 2, "gdn2": 3}
+DTYPES = {"f32": 0, "bf16": 1}
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class GdrProblem(ctypes.Structure):
+    _fields_ = [("variant", _i32), ("dtype", _i32), ("B", _i32), ("H", _i32), ("T", _i32),
+                ("dk", _i32), ("dv", _i32), ("chunk", _i32), ("n_seqs", _i32),
+                ("cu_seqlens_host", ctypes.POINTER(_i32)), ("cu_seqlens_dev", _vp),
+                ("scale", ctypes.c_float)]
+
+
+class GdrInputs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("beta", _vp), ("alpha", _vp),
+                ("erase", _vp), ("write", _vp), ("h0", _vp)]
+
+
+class GdrGrads(ctypes.Structure):
+    _fields_ = [("dq", _vp), ("dk", _vp), ("dv", _vp), ("dbeta", _vp), ("dalpha", _vp),
+                ("derase", _vp), ("dwrite", _vp), ("dh0", _vp)]
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_LIB = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgdr.so once.  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_rule_73_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.gdr_workspace_size.argtypes = [P(GdrProblem), ctypes.c_int, P(ctypes.c_size_t)]
+    lib.gdr_saved_size.argtypes = [P(GdrProblem), P(ctypes.c_size_t)]
+    lib.gdr_forward.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.gdr_backward.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, P(GdrGrads), _vp,
+                                 ctypes.c_size_t, _vp]
+    for f in ("gdr_workspace_size", "gdr_saved_size", "gdr_forward", "gdr_backward"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.gdr_status_string.argtypes = [ctypes.c_int]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_last_error.argtypes = []
+    lib.gdr_last_error.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _check(lib, status: int):
+    if status != GDR_OK:
+        raise GdrError(status, f"{lib.gdr_status_string(status).decode()}: {lib.gdr_last_error().decode()}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def make_problem(q, v, *, variant: str, cu_seqlens=None, scale: float = 1.0, chunk: int = 64):
+    """Build a GdrProblem from the query and value tensors ([B,H,T,dk], [B,H,T,dv]).
+
+    cu_seqlens: None, or a sequence / CPU tensor of n+1 int offsets.  Returns (problem,
+    keepalive) where keepalive holds the host and device copies of the offsets."""
+    import torch
+    B, H, T, dk = q.shape
+    dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}[q.dtype]
+    keep = []
+    p = GdrProblem(variant=VARIANTS[variant], dtype=DTYPES[dtype], B=B, H=H, T=T, dk=dk,
+                   dv=v.shape[-1], chunk=chunk, n_seqs=0, cu_seqlens_host=None, cu_seqlens_dev=None,
+                   scale=float(scale))
+    if cu_seqlens is not None:
+        host = torch.as_tensor(cu_seqlens, dtype=torch.int32).cpu().contiguous()
+        dev = host.to(q.device)
+        keep += [host, dev]
+        p.n_seqs = host.numel() - 1
+        p.cu_seqlens_host = ctypes.cast(host.data_ptr(), ctypes.POINTER(_i32))
+        p.cu_seqlens_dev = dev.data_ptr()
+    return p, keep
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def gdr_workspace_size(problem: GdrProblem, backward: bool) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_workspace_size(ctypes.byref(problem), int(bool(backward)), ctypes.byref(n)))
+    return n.value
+
+
+def gdr_saved_size(problem: GdrProblem) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib, lib.gdr_saved_size(ctypes.byref(problem), ctypes.byref(n)))
+    return n.value
+
+
+def _inputs(q, k, v, beta, alpha, erase, write, h0) -> GdrInputs:
+    return GdrInputs(q=_ptr(q), k=_ptr(k), v=_ptr(v), beta=_ptr(beta), alpha=_ptr(alpha),
+                     erase=_ptr(erase), write=_ptr(write), h0=_ptr(h0))
+
+
+def gdr_forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *, variant: str,
+                cu_seqlens=None, scale: float = 1.0, chunk: int = 64, output_final_state: bool = True,
+                save: bool = False, workspace=None):
+    """Forward.  Returns (o, ht or None, saved or None).  Tensors must be contiguous and on
+    the GPU; the call is asynchronous on torch's current stream."""
+    import torch
+    lib = load_library()
+    p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk)
+    N = p.n_seqs if p.n_seqs > 0 else p.B
+    o = torch.empty(q.shape[:3] + (p.dv,), dtype=q.dtype, device=q.device)
+    ht = torch.empty((N, p.H, p.dv, p.dk), dtype=torch.float32, device=q.device) if output_final_state else None
+    saved = torch.empty(gdr_saved_size(p), dtype=torch.uint8, device=q.device) if save else None
+    need = gdr_workspace_size(p, False)
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ins = _inputs(q, k, v, beta, alpha, erase, write, h0)
+    st = lib.gdr_forward(ctypes.byref(p), ctypes.byref(ins), _ptr(o), _ptr(ht), _ptr(saved), _ptr(ws),
+                         ws.numel(), _stream(q))
+    _check(lib, st)
+    del keep
+    return o, ht, saved
+
+
+def gdr_backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do=None, dht=None, *,
+                 variant: str, cu_seqlens=None, scale: float = 1.0, chunk: int = 64, saved=None,
+                 want_dh0: bool = True, workspace=None) -> dict:
+    """Backward of sum(o * do) + sum(ht * dht).  Returns a dict of gradients (None where the
+    input is absent).  `saved` is the third result of gdr_forward(save=True), or None."""
+    import torch
+    lib = load_library()
+    p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk)
+    N = p.n_seqs if p.n_seqs > 0 else p.B
+    e = lambda x: None if x is None else torch.empty_like(x)
+    out = {"dq": e(q), "dk": e(k), "dv": e(v), "dbeta": e(beta), "dalpha": e(alpha),
+           "derase": e(erase), "dwrite": e(write),
+           "dh0": torch.empty((N, p.H, p.dv, p.dk), dtype=torch.float32, device=q.device) if want_dh0 else None}
+    g = GdrGrads(**{name: _ptr(t) for name, t in out.items()})
+    need = gdr_workspace_size(p, True)
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ins = _inputs(q, k, v, beta, alpha, erase, write, h0)
+    st = lib.gdr_backward(ctypes.byref(p), ctypes.byref(ins), _ptr(do), _ptr(dht), _ptr(saved), ctypes.byref(g),
+                          _ptr(ws), ws.numel(), _stream(q))
+    _check(lib, st)
+    del keep
+    return out

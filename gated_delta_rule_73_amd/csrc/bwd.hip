@@ -1,0 +1,553 @@
+// Backward kernels of the chunked delta-rule operator (Delta family: DeltaNet, Gated DeltaNet).
+//
+// Per chunk, with dO the (scaled) output gradient and dW the gradient w.r.t. the memory at
+// the chunk's end (reverse-mode of the chunk form used by the forward):
+//   dR  = M^T dO + (e^{g_n-g} * K) dW^T
+//   dW0 = e^{g_n} dW + dO^T (e^g * Q) - dR^T X          (carried to the previous chunk)
+//   dQhat = dO W0,  dKbar = R dW,  dX = -dR W0,  dU = dR
+//   dT = dU V^T + dX Khat^T,  dV = T^T dU,  dKhat = T^T dX
+//   dL = -strictlower(L^-T (dT diag beta) L^-T),  dA = diag(beta) dL
+//   dbeta_s = sum_t dT_ts Linv_ts + sum_s' dL_ss' A_ss'
+//   Gram slots: dk += (dA*E) K + (dA*E)^T K + (dM*E)^T Q,  dq += (dM*E) K,  dM = tril(dO R^T)
+// d log(alpha_t) collects every path through which log alpha_t scales a quantity.  Each
+// such term carries the factor alpha_t itself, so it is summed directly (rectangle sums of
+// the Gram pair terms over s < t <= u, suffix sums over u >= t, prefix sums over s < t)
+// rather than as a difference of running sums; dividing by alpha_t then stays accurate
+// even for strongly decaying tokens.
+// Two launches: a sequential reverse scan per (sequence, head, value-row tile) that carries
+// dW in float32 and records dW and dR per chunk, then a chunk-parallel kernel for the rest.
+#include "chunk.hpp"
+#include "launch.hpp"
+
+namespace gdr {
+
+// ---------------------------------------------------------------------------------------
+// Reverse scan over the chunks of one (sequence, head, value tile).
+// ---------------------------------------------------------------------------------------
+template <typename E, int D, int BV, int VAR>
+__global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+                                                  const E* __restrict__ dO, const E* __restrict__ Xg,
+                                                  const E* __restrict__ Mg, const float* __restrict__ Gg,
+                                                  const float* __restrict__ dht, E* __restrict__ dHs,
+                                                  E* __restrict__ dRg, float* __restrict__ dh0) {
+  constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
+  constexpr int NJ = D / 64, NI = BV / 16;
+  __shared__ __align__(16) E Qs[CH * LD];
+  __shared__ __align__(16) E Ks[CH * LD];
+  __shared__ __align__(16) E Xs[CH * LD];
+  __shared__ __align__(16) E Ms[CH * LDR];
+  __shared__ __align__(16) E dOt[BV * LDR];   // scale * dO^T
+  __shared__ __align__(16) E dOg[BV * LDR];   // scale * e^g * dO^T
+  __shared__ __align__(16) E dWs[BV * LD];
+  __shared__ __align__(16) E dRt[BV * LDR];   // -dR^T
+  __shared__ __align__(16) E dRn[CH * LDV];   // dR
+  __shared__ float gs[CH];
+
+  int sq, h, vt;
+  if (!scan_block<D / BV>(geo, sq, h, vt)) return;
+  const int i0 = vt * BV;
+  const SeqPos sp = seq_pos(geo, sq);
+  const int w = wave_id();
+  const long sbase = ((long)sq * geo.H + h) * D;
+
+  f32x4 S[NJ][NI];  // dW^T tiles
+#pragma unroll
+  for (int qq = 0; qq < NJ; ++qq)
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int j0 = acc_row(16 * (w + 4 * qq), 0), i = i0 + acc_col(16 * it);
+      if (dht) {
+        const float4 x = *reinterpret_cast<const float4*>(dht + (sbase + i) * D + j0);
+        S[qq][it] = f32x4{x.x, x.y, x.z, x.w};
+      } else {
+        S[qq][it] = zero4();
+      }
+    }
+
+  for (int c = sp.nchunks - 1; c >= 0; --c) {
+    const long u = (long)(sp.gc0 + c) * geo.H + h;
+    const int n = min(CH, sp.len - c * CH);
+    const long tk = tok_index(geo, sp.b, h, sp.bos + c * CH);
+    g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
+    g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
+    g2s_rows<E, CH, D, NT>(Xs, LD, Xg + u * CH * D, D, CH);
+    g2s_rows<E, CH, CH, NT>(Ms, LDR, Mg + u * CH * CH, CH, CH);
+    if (threadIdx.x < CH) gs[threadIdx.x] = Gg[u * CH + threadIdx.x];
+#pragma unroll
+    for (int qq = 0; qq < NJ; ++qq)
+#pragma unroll
+      for (int it = 0; it < NI; ++it) store4_t(dWs, LD, 16 * (w + 4 * qq), 16 * it, S[qq][it]);
+    __syncthreads();
+    // dO tile, transposed, twice: plain and with e^{g_t} (rows t >= n are zero)
+    for (int idx = threadIdx.x; idx < CH * BV; idx += NT) {
+      const int t = idx % CH, i = idx / CH;
+      float x = 0.f;
+      if (t < n) x = geo.scale * (float)dO[(tk + t) * D + i0 + i];
+      float e = 1.f;
+      if constexpr (VAR == VAR_GATED) e = expf(gs[t]);
+      dOt[i * LDR + t] = (E)x;
+      dOg[i * LDR + t] = (E)(x * e);
+    }
+    s2g_rows<E, BV, D, NT>(dHs + u * D * D + (long)i0 * D, D, dWs, LD, BV);
+    __syncthreads();
+    const float gn = gs[CH - 1];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const f32x4 a1 = mma_k<E, CH>(zero4(), colk(Ms, LDR), 16 * w, rowk(dOt, LDR), 16 * it);
+      const f32x4 a2 = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * w, rowk(dWs, LD), 16 * it);
+      f32x4 dr, ndr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float dec = 1.f;
+        if constexpr (VAR == VAR_GATED) dec = expf(gn - gs[acc_row(16 * w, r)]);
+        dr[r] = a1[r] + dec * a2[r];
+        ndr[r] = -dr[r];
+      }
+      store4_t(dRt, LDR, 16 * w, 16 * it, ndr);
+      store4_n(dRn, LDV, 16 * w, 16 * it, dr);
+    }
+    __syncthreads();
+    s2g_rows<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV, CH);
+    float eg = 1.f;
+    if constexpr (VAR == VAR_GATED) eg = expf(gn);
+#pragma unroll
+    for (int qq = 0; qq < NJ; ++qq)
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        S[qq][it] *= eg;
+        S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Qs, LD), 16 * (w + 4 * qq), rowk(dOg, LDR), 16 * it);
+        S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Xs, LD), 16 * (w + 4 * qq), rowk(dRt, LDR), 16 * it);
+      }
+    __syncthreads();
+  }
+  if (dh0) {
+#pragma unroll
+    for (int qq = 0; qq < NJ; ++qq)
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        const int j0 = acc_row(16 * (w + 4 * qq), 0), i = i0 + acc_col(16 * it);
+        const f32x4 x = S[qq][it];
+        *reinterpret_cast<float4*>(dh0 + (sbase + i) * D + j0) = make_float4(x[0], x[1], x[2], x[3]);
+      }
+  }
+}
+
+// T^T as a matrix-core A operand, read from L^{-1}: element (m = s, k = t) = Linv[t][s] beta_s.
+struct TtView {
+  const float* li;
+  int ld;
+  const float* beta;
+  __device__ __forceinline__ float at(int m, int k) const { return li[k * ld + m] * beta[m]; }
+};
+template <typename E>
+__device__ __forceinline__ typename MMA<E>::frag frag(const TtView& v, int idx0, int k0) {
+  constexpr int KPL = MMA<E>::KPL;
+  const int m = idx0 + lrow(), kk = k0 + KPL * lgrp();
+  if constexpr (KPL == 1) {
+    return (E)v.at(m, kk);
+  } else {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)v.at(m, kk + e);
+    return r;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Chunk-local gradients: per (head, chunk), 512 threads, LDS regions reused across phases.
+// ---------------------------------------------------------------------------------------
+template <typename E, int D>
+struct BwdLds {
+  static constexpr int LD = D + pad16<E>(), LDR = CH + pad16<E>(), LF = CH + 4;
+  static constexpr int TK = CH * LD * (int)sizeof(E);   // 64 x D token tile
+  static constexpr int TH = D * LDR * (int)sizeof(E);   // D x 64 (transposed half memory)
+  static constexpr int SQ = CH * LDR * (int)sizeof(E);  // 64 x 64 in E
+  static constexpr int F = CH * LF * 4;                 // 64 x 64 float
+  static constexpr int oK = 0, odR = TK, odX = 2 * TK, odM = 3 * TK, oU = 3 * TK + SQ;
+  // phase 1 (state part)
+  static constexpr int odO = oU, oR = oU + TK, oWh = oU + 2 * TK, odWh = oU + 2 * TK + TH;
+  static constexpr int endP1 = oU + 2 * TK + 2 * TH;
+  // phase 2 (WY part) and 3 (Gram part)
+  static constexpr int oA = oU, odT = oU + F, oLi = oU + 2 * F, oVP = oU + 3 * F;
+  static constexpr int endP2 = oU + 3 * F + (TK > F ? TK : F);
+  static constexpr int oQ = oLi, oPair = oVP, oAt = odR, oMt = odR + SQ;
+  static constexpr int BIG = endP1 > endP2 ? endP1 : endP2;
+  static_assert(TK <= F, "Q must fit the region of Linv");
+  static_assert(2 * SQ <= 2 * TK, "Gram operand buffers must fit the dR/dX regions");
+};
+
+
+template <typename E, int D, int VAR>
+__global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+                                                   const E* __restrict__ v, const E* __restrict__ beta,
+                                                   const E* __restrict__ alpha, const E* __restrict__ dO,
+                                                   const E* __restrict__ Mg, const float* __restrict__ Gg,
+                                                   const E* __restrict__ Hs, const E* __restrict__ Rg,
+                                                   const E* __restrict__ dHs, const E* __restrict__ dRg,
+                                                   E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
+                                                   E* __restrict__ dbeta, E* __restrict__ dalpha) {
+  using Ly = BwdLds<E, D>;
+  constexpr int NT = 512, LD = Ly::LD, LDR = Ly::LDR, LF = Ly::LF;
+  constexpr int KH = 64, NH = D / KH;  // the memory is read in blocks of 64 value rows
+  constexpr int NQ = D / 32;           // 64 x D tiles per wave when all 8 waves share a matrix
+  constexpr bool GATED = VAR == VAR_GATED;
+  __shared__ __align__(16) char smem[Ly::BIG];
+  __shared__ __align__(16) float scr[4 * 256];
+  __shared__ float gs[CH], bs[CH], dbs[CH], red[NT / 64];
+  __shared__ float rq[4][CH], rkh[8][CH], rkb[8][CH];
+
+  E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
+  E* dRs = reinterpret_cast<E*>(smem + Ly::odR);
+  E* dXs = reinterpret_cast<E*>(smem + Ly::odX);
+  E* dMs = reinterpret_cast<E*>(smem + Ly::odM);
+
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id(), wm = w & 3, wn = w >> 2;
+  const int n = cp.n;
+
+  // ================= phase 1: products with the memory W0 and its gradient dW
+  f32x4 acc1[D / 16];  // row tile w of [dO; dR] times W0: waves 0-3 dQhat, waves 4-7 dR W0
+  f32x4 dka[NQ];       // dk tiles (row tile wm, column tiles wn*NQ + qq)
+  f32x4 acc3[2];       // dM tiles w and w + 8
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) acc1[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) dka[i] = zero4();
+  acc3[0] = acc3[1] = zero4();
+  float gam = 0.f;
+  {
+    E* dOs = reinterpret_cast<E*>(smem + Ly::odO);
+    E* Rs = reinterpret_cast<E*>(smem + Ly::oR);
+    E* Wh = reinterpret_cast<E*>(smem + Ly::oWh);
+    E* dWh = reinterpret_cast<E*>(smem + Ly::odWh);
+    g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
+    g2s_rows<E, CH, D, NT>(dOs, LD, dO + tk * D, D, n);
+    g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
+    g2s_rows<E, CH, D, NT>(dRs, LD, dRg + u * CH * D, D, CH);
+    if (threadIdx.x < CH) {
+      const int t = threadIdx.x;
+      gs[t] = Gg[u * CH + t];
+      bs[t] = (t < n) ? (float)beta[tk + t] : 0.f;
+    }
+    for (int ih = 0; ih < NH; ++ih) {
+      __syncthreads();
+      g2s_rows_t<E, KH, D, NT>(Wh, LDR, Hs + u * D * D + (long)ih * KH * D, D, KH);
+      g2s_rows_t<E, KH, D, NT>(dWh, LDR, dHs + u * D * D + (long)ih * KH * D, D, KH);
+      __syncthreads();
+      const E* Aop = (w < 4 ? dOs : dRs) + ih * KH;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(Aop, LD), 16 * wm, rowk(Wh, LDR), 16 * nt);
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq)
+        dka[qq] = mma_k<E, KH>(dka[qq], rowk(Rs + ih * KH, LD), 16 * wm, rowk(dWh, LDR), 16 * (wn * NQ + qq));
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int id = w + 8 * e;
+        acc3[e] = mma_k<E, KH>(acc3[e], rowk(dOs + ih * KH, LD), 16 * (id >> 2), rowk(Rs + ih * KH, LD), 16 * (id & 3));
+      }
+      if constexpr (GATED) {
+        for (int idx = threadIdx.x; idx < D * KH; idx += NT) {
+          const int j = idx / KH, i = idx % KH;
+          gam += (float)Wh[j * LDR + i] * (float)dWh[j * LDR + i];
+        }
+      }
+    }
+  }
+  const float gn = gs[CH - 1];
+  // dq (first term) stays in acc1 for waves 0-3; dX goes to LDS from waves 4-7
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    if (w < 4) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float e = 1.f;
+        if constexpr (GATED) e = expf(gs[acc_row(16 * wm, r)]);
+        acc1[nt][r] *= geo.scale * e;
+      }
+    } else {
+      store4_n(dXs, LD, 16 * wm, 16 * nt, -acc1[nt]);
+    }
+  }
+  // dk (first term): e^{g_n - g_t} dKbar, and the rows' Kbar . dKbar
+  {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(16 * wm, r);
+        float dec = 1.f;
+        if constexpr (GATED) dec = expf(gn - gs[t]);
+        dka[qq][r] *= dec;
+        part[r] += (float)Ks[t * LD + acc_col(16 * (wn * NQ + qq))] * dka[qq][r];
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = sum16(part[r]);
+      if (lrow() == 0) rkb[w][acc_row(16 * wm, r)] = s;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+    f32x4 x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (acc_col(16 * nt) <= acc_row(16 * mt, r)) ? geo.scale * acc3[e][r] : 0.f;
+    store4_n(dMs, LDR, 16 * mt, 16 * nt, x);
+  }
+  if constexpr (GATED) {
+    gam = wave_sum(gam);
+    if (lane_id() == 0) red[w] = gam;
+  }
+  __syncthreads();
+
+  // ================= phase 2: the WY / triangular-solve part
+  float* As = reinterpret_cast<float*>(smem + Ly::oA);
+  float* dTs = reinterpret_cast<float*>(smem + Ly::odT);
+  float* Li = reinterpret_cast<float*>(smem + Ly::oLi);
+  E* Vs = reinterpret_cast<E*>(smem + Ly::oVP);
+  g2s_rows<E, CH, D, NT>(Vs, LD, v + tk * D, D, n);
+  for (int job = w; job < 10; job += 8) {
+    int mt, nt;
+    tri_tile(job, mt, nt);
+    const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
+      float val = 0.f;
+      if (s < t) {
+        float dec = 1.f;
+        if constexpr (GATED) dec = expf(gs[t] - gs[s]);
+        val = acc[r] * dec;
+      }
+      As[t * LF + s] = val;
+      dTs[t * LF + s] = bs[t] * val;  // L below the diagonal, solved into Li
+    }
+  }
+  __syncthreads();
+  solve_unit_lower64<NT>(dTs, LF, Li, LF, scr);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+    const f32x4 a = mma_k<E, D>(zero4(), rowk(dRs, LD), 16 * mt, rowk(Vs, LD), 16 * nt);
+    const f32x4 b = mma_k<E, D>(zero4(), rowk(dXs, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
+      float es = 1.f;
+      if constexpr (GATED) es = expf(gs[s]);
+      dTs[t * LF + s] = (s <= t) ? a[r] + b[r] * es : 0.f;
+    }
+  }
+  // dV = T^T dR and dKhat = T^T dX with T = Linv diag(beta)
+  const TtView Tt{Li, LF, bs};
+  f32x4 dva[NQ];
+  {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      const int nt = wn * NQ + qq;
+      dva[qq] = mma_k<E, CH>(zero4(), Tt, 16 * wm, colk(dRs, LD), 16 * nt);
+      f32x4 kh = mma_k<E, CH>(zero4(), Tt, 16 * wm, colk(dXs, LD), 16 * nt);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(16 * wm, r);
+        float e = 1.f;
+        if constexpr (GATED) e = expf(gs[t]);
+        kh[r] *= e;
+        part[r] += (float)Ks[t * LD + acc_col(16 * nt)] * kh[r];
+      }
+      dka[qq] += kh;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = sum16(part[r]);
+      if (lrow() == 0) rkh[w][acc_row(16 * wm, r)] = s;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int qq = 0; qq < NQ; ++qq) store4_n(Vs, LD, 16 * wm, 16 * (wn * NQ + qq), dva[qq]);
+  if (threadIdx.x < CH) {  // dbeta from T = Linv diag(beta)
+    const int s = threadIdx.x;
+    float a = 0.f;
+    for (int t = s; t < CH; ++t) a += dTs[t * LF + s] * Li[t * LF + s];
+    dbs[s] = a;
+  }
+  __syncthreads();
+  s2g_rows<E, CH, D, NT>(dv + tk * D, D, Vs, LD, n);
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s = idx & 63;
+    dTs[t * LF + s] *= bs[s];  // gradient w.r.t. Linv
+  }
+  __syncthreads();
+  float* Pt = reinterpret_cast<float*>(smem + Ly::oVP);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+    const f32x4 acc = mma_k<E, CH>(zero4(), rowk(dTs, LF), 16 * mt, rowk(Li, LF), 16 * nt);
+    store4_t(Pt, LF, 16 * mt, 16 * nt, acc);
+  }
+  __syncthreads();
+  f32x4 dl[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+    const f32x4 acc = mma_k<E, CH>(zero4(), colk(Li, LF), 16 * mt, rowk(Pt, LF), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[e][r] = (acc_col(16 * nt) < acc_row(16 * mt, r)) ? -acc[r] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int id = w + 8 * e;
+    store4_n(dTs, LF, 16 * (id >> 2), 16 * (id & 3), dl[e]);  // dTs now holds dL
+  }
+  __syncthreads();
+  if (threadIdx.x < CH) {  // dbeta from L = I + diag(beta) A
+    const int t = threadIdx.x;
+    float a = 0.f;
+    for (int s = 0; s < t; ++s) a += dTs[t * LF + s] * As[t * LF + s];
+    dbs[t] += a;
+  }
+
+  // ================= phase 3: Gram slots and the decay gradient
+  E* Qs = reinterpret_cast<E*>(smem + Ly::oQ);
+  E* Ats = reinterpret_cast<E*>(smem + Ly::oAt);
+  E* Mts = reinterpret_cast<E*>(smem + Ly::oMt);
+  float* Pair = reinterpret_cast<float*>(smem + Ly::oPair);
+  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s = idx & 63;
+    float dec = 0.f;
+    if (s <= t) {
+      dec = 1.f;
+      if constexpr (GATED) dec = expf(gs[t] - gs[s]);
+    }
+    const float dA = (s < t) ? bs[t] * dTs[t * LF + s] : 0.f;
+    const float dM = (s <= t) ? (float)dMs[t * LDR + s] : 0.f;
+    Ats[t * LDR + s] = (E)(dA * dec);
+    Mts[t * LDR + s] = (E)(dM * dec);
+    if constexpr (GATED) Pair[t * LF + s] = (s < t) ? dA * As[t * LF + s] + dM * (float)Mg[(u * CH + t) * CH + s] : 0.f;
+  }
+  __syncthreads();
+  if (w < 4) {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[r] += (float)Qs[acc_row(16 * wm, r) * LD + acc_col(16 * nt)] * acc1[nt][r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = sum16(part[r]);
+      if (lrow() == 0) rq[w][acc_row(16 * wm, r)] = s;
+    }
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, CH>(acc1[nt], rowk(Mts, LDR), 16 * wm, colk(Ks, LD), 16 * nt);
+  }
+#pragma unroll
+  for (int qq = 0; qq < NQ; ++qq) {
+    const int nt = wn * NQ + qq;
+    dka[qq] = mma_k<E, CH>(dka[qq], rowk(Ats, LDR), 16 * wm, colk(Ks, LD), 16 * nt);
+    dka[qq] = mma_k<E, CH>(dka[qq], colk(Ats, LDR), 16 * wm, colk(Ks, LD), 16 * nt);
+    dka[qq] = mma_k<E, CH>(dka[qq], colk(Mts, LDR), 16 * wm, colk(Qs, LD), 16 * nt);
+  }
+  if constexpr (GATED) {
+    if (threadIdx.x < CH) {  // prefix sums along each row of the pair terms
+      const int uu = threadIdx.x;
+      float run = 0.f;
+      for (int s = 0; s < uu; ++s) {
+        run += Pair[uu * LF + s];
+        Pair[uu * LF + s] = run;
+      }
+    }
+  }
+  __syncthreads();
+  // outputs: dq, dk through LDS (the dR/dX regions are free now)
+  E* sq = reinterpret_cast<E*>(smem + Ly::odR);
+  E* sk = reinterpret_cast<E*>(smem + Ly::odX);
+  if (w < 4) {
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) store4_n(sq, LD, 16 * wm, 16 * nt, acc1[nt]);
+  }
+#pragma unroll
+  for (int qq = 0; qq < NQ; ++qq) store4_n(sk, LD, 16 * wm, 16 * (wn * NQ + qq), dka[qq]);
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x;
+    if constexpr (GATED) {
+      float rect = 0.f;  // sum over u >= t of sum_{s < t} pair(u, s)
+      if (t > 0)
+        for (int uu = t; uu < CH; ++uu) rect += Pair[uu * LF + t - 1];
+      // suffix over u >= t of the rows' Qhat.dQhat + Khat.dKhat (reversed inclusive scan)
+      const int tr = CH - 1 - t;
+      const float xr = rq[tr >> 4][tr] + rkh[tr >> 4][tr] + rkh[(tr >> 4) + 4][tr];
+      const float suf_r = wave_incl_scan(xr);
+      const float suf = __shfl(suf_r, CH - 1 - t, 64);
+      // prefix over s < t of Kbar.dKbar (exclusive scan)
+      const float xb = rkb[t >> 4][t] + rkb[(t >> 4) + 4][t];
+      const float inc = wave_incl_scan(xb);
+      float pre = __shfl_up(inc, 1, 64);
+      if (t == 0) pre = 0.f;
+      float g4 = 0.f;
+#pragma unroll
+      for (int i = 0; i < NT / 64; ++i) g4 += red[i];
+      const float dla = rect + suf + pre + expf(gn) * g4;
+      if (t < n) dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
+    }
+    if (t < n) dbeta[tk + t] = (E)dbs[t];
+  }
+  __syncthreads();
+  s2g_rows<E, CH, D, NT>(dq + tk * D, D, sq, LD, n);
+  s2g_rows<E, CH, D, NT>(dk + tk * D, D, sk, LD, n);
+}
+
+// ---------------------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------------------
+template <typename E, int D, int VAR>
+static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht,
+                           const gdr_grads& gr, hipStream_t st) {
+  const Geo& g = p.geo;
+  if (p.bv == 16) {
+    hipLaunchKernelGGL((k_bwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
+                       (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
+                       (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0);
+  } else {
+    hipLaunchKernelGGL((k_bwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
+                       (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
+                       (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0);
+  }
+  if (g.total_chunks > 0) {
+    hipLaunchKernelGGL((k_bwd_chunk<E, D, VAR>), dim3(g.total_chunks, g.H), dim3(512), 0, st, g,
+                       (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
+                       (const E*)dO, (const E*)p.M, (const float*)p.G, (const E*)p.Hs, (const E*)p.R,
+                       (const E*)p.dHs, (const E*)p.dR, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta,
+                       (E*)gr.dalpha);
+  }
+  return hipGetLastError();
+}
+
+hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht, const gdr_grads& gr,
+                        hipStream_t st) {
+  const bool bf = p.dtype == GDR_BF16;
+  switch (p.variant) {
+    case GDR_DELTANET:
+      if (bf && p.D == 128) return bwd_impl<bf16, 128, VAR_DELTANET>(p, in, dO, dht, gr, st);
+      if (bf && p.D == 64) return bwd_impl<bf16, 64, VAR_DELTANET>(p, in, dO, dht, gr, st);
+      if (!bf && p.D == 64) return bwd_impl<float, 64, VAR_DELTANET>(p, in, dO, dht, gr, st);
+      break;
+    case GDR_GATED:
+      if (bf && p.D == 128) return bwd_impl<bf16, 128, VAR_GATED>(p, in, dO, dht, gr, st);
+      if (bf && p.D == 64) return bwd_impl<bf16, 64, VAR_GATED>(p, in, dO, dht, gr, st);
+      if (!bf && p.D == 64) return bwd_impl<float, 64, VAR_GATED>(p, in, dO, dht, gr, st);
+      break;
+    default:
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

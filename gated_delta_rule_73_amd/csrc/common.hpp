@@ -1,0 +1,272 @@
+// Device building blocks shared by the gfx950 kernels of the chunked delta-rule operator.
+//
+// Matrix products use the CDNA3/4 matrix cores through 16x16 output tiles:
+//   bfloat16 operands: v_mfma_f32_16x16x32_bf16 (k = 32 per instruction, 8 values per lane)
+//   float32 operands : v_mfma_f32_16x16x4_f32   (k = 4 per instruction, 1 value per lane)
+// Lane l of a 64-wide wave holds, for an output tile C[m0..m0+15][n0..n0+15]:
+//   A fragment: row m0 + (l & 15), k = k0 + KPL * (l >> 4) + e, e < KPL
+//   B fragment: column n0 + (l & 15), same k
+//   accumulator element r: row m0 + 4 * (l >> 4) + r, column n0 + (l & 15).
+// Operands are read from LDS through View<S, KC>: element (m, k) lives at p[m*ld + k] when
+// KC (k contiguous: one vector load per fragment) and at p[k*ld + m] otherwise (a gather).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace gdr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;  // chunk length (tokens)
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int lrow() { return threadIdx.x & 15; }
+__device__ __forceinline__ int lgrp() { return (threadIdx.x >> 4) & 3; }
+
+template <typename E> struct MMA;
+template <> struct MMA<bf16> {
+  static constexpr int KS = 32, KPL = 8;
+  using frag = bf16x8;
+  __device__ static __forceinline__ f32x4 run(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct MMA<float> {
+  static constexpr int KS = 4, KPL = 1;
+  using frag = float;
+  __device__ static __forceinline__ f32x4 run(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Row padding (elements) that keeps 16-byte alignment and spreads LDS banks.
+template <typename S> constexpr int pad16() { return 16 / (int)sizeof(S); }
+
+template <typename S, bool KC> struct View {
+  const S* p;
+  int ld;
+  __device__ __forceinline__ View(const S* p_, int ld_) : p(p_), ld(ld_) {}
+  __device__ __forceinline__ float at(int m, int k) const {
+    return (float)(KC ? p[m * ld + k] : p[k * ld + m]);
+  }
+};
+
+template <typename S> __device__ __forceinline__ View<S, true> rowk(const S* p, int ld) { return View<S, true>(p, ld); }
+template <typename S> __device__ __forceinline__ View<S, false> colk(const S* p, int ld) { return View<S, false>(p, ld); }
+
+// The calling lane's fragment of rows/columns idx0..idx0+15 and k-slice k0..k0+KS-1.
+template <typename E, typename S, bool KC>
+__device__ __forceinline__ typename MMA<E>::frag frag(const View<S, KC>& v, int idx0, int k0) {
+  constexpr int KPL = MMA<E>::KPL;
+  const int m = idx0 + lrow();
+  const int k = k0 + KPL * lgrp();
+  if constexpr (KPL == 1) {
+    return (E)v.at(m, k);
+  } else if constexpr (KC && std::is_same<S, E>::value) {
+    return *reinterpret_cast<const bf16x8*>(v.p + m * v.ld + k);
+  } else if constexpr (KC && std::is_same<S, float>::value) {
+    const float4 lo = *reinterpret_cast<const float4*>(v.p + m * v.ld + k);
+    const float4 hi = *reinterpret_cast<const float4*>(v.p + m * v.ld + k + 4);
+    bf16x8 r;
+    r[0] = (bf16)lo.x; r[1] = (bf16)lo.y; r[2] = (bf16)lo.z; r[3] = (bf16)lo.w;
+    r[4] = (bf16)hi.x; r[5] = (bf16)hi.y; r[6] = (bf16)hi.z; r[7] = (bf16)hi.w;
+    return r;
+  } else {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)v.at(m, k + e);
+    return r;
+  }
+}
+
+// acc += A[m0.., 0..K) * B[0..K), n0..] for one 16x16 tile.
+template <typename E, int K, class VA, class VB>
+__device__ __forceinline__ f32x4 mma_k(f32x4 acc, const VA& A, int m0, const VB& B, int n0) {
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += MMA<E>::KS) acc = MMA<E>::run(frag<E>(A, m0, k0), frag<E>(B, n0, k0), acc);
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Row / column of accumulator element r of a tile at (m0, n0).
+__device__ __forceinline__ int acc_row(int m0, int r) { return m0 + 4 * lgrp() + r; }
+__device__ __forceinline__ int acc_col(int n0) { return n0 + lrow(); }
+
+// Store 4 accumulator values that are consecutive along the tile's rows as 4 consecutive
+// elements (row-of-output becomes the contiguous index): dst[col*ld + row0 .. row0+3].
+template <typename S>
+__device__ __forceinline__ void store4_t(S* dst, int ld, int m0, int n0, f32x4 v) {
+  S* p = dst + acc_col(n0) * ld + m0 + 4 * lgrp();
+  if constexpr (std::is_same<S, float>::value) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    bf16x4 b;
+    b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+    *reinterpret_cast<bf16x4*>(p) = b;
+  }
+}
+// Store in the tile's own orientation: dst[row*ld + col].
+template <typename S>
+__device__ __forceinline__ void store4_n(S* dst, int ld, int m0, int n0, f32x4 v) {
+  const int c = acc_col(n0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[acc_row(m0, r) * ld + c] = (S)v[r];
+}
+
+// ---------------------------------------------------------------------------------------
+// Tile staging between global memory and LDS (16-byte vectors, whole block cooperates).
+// ---------------------------------------------------------------------------------------
+// LDS[r*ld + c] = G[r*gs + c] for r < nrows, 0 for nrows <= r < ROWS; c < COLS.
+template <typename S, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void g2s_rows(S* lds, int ld, const S* g, long gs, int nrows) {
+  constexpr int VE = 16 / (int)sizeof(S);
+  constexpr int VPR = COLS / VE;
+  static_assert(COLS % VE == 0, "row length must be a multiple of 16 bytes");
+  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
+    const int r = idx / VPR, c = (idx % VPR) * VE;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (r < nrows) val = *reinterpret_cast<const uint4*>(g + (long)r * gs + c);
+    *reinterpret_cast<uint4*>(lds + r * ld + c) = val;
+  }
+}
+// Transposed staging: LDS[c*ld + r] = G[r*gs + c] (zero for r >= nrows), r < ROWS, c < COLS.
+template <typename S, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void g2s_rows_t(S* lds, int ld, const S* g, long gs, int nrows, float mul = 1.f) {
+  constexpr int VE = 16 / (int)sizeof(S);
+  constexpr int VPR = COLS / VE;
+  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
+    const int r = idx % ROWS, c = (idx / ROWS) * VE;
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (r < nrows) val = *reinterpret_cast<const uint4*>(g + (long)r * gs + c);
+    const S* e = reinterpret_cast<const S*>(&val);
+#pragma unroll
+    for (int i = 0; i < VE; ++i) lds[(c + i) * ld + r] = (S)((float)e[i] * mul);
+  }
+}
+// G[r*gs + c] = LDS[r*ld + c] for r < nrows, c < COLS.
+template <typename S, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void s2g_rows(S* g, long gs, const S* lds, int ld, int nrows) {
+  constexpr int VE = 16 / (int)sizeof(S);
+  constexpr int VPR = COLS / VE;
+  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
+    const int r = idx / VPR, c = (idx % VPR) * VE;
+    if (r < nrows) *reinterpret_cast<uint4*>(g + (long)r * gs + c) = *reinterpret_cast<const uint4*>(lds + r * ld + c);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Problem geometry
+// ---------------------------------------------------------------------------------------
+struct Geo {
+  int B, H, T;        // batch, heads, tokens
+  int nseq;           // independent sequences (B, or packed count)
+  int varlen;         // 1: packed sequences, B == 1
+  const int* cu;      // device offsets (varlen)
+  int total_chunks;   // sum over sequences of ceil(len / 64)
+  float scale;
+};
+
+struct ChunkPos {
+  int b, seq, t0, n;  // batch row, sequence, first token (within [0,T)), valid tokens
+};
+struct SeqPos {
+  int b, bos, len, gc0, nchunks;
+};
+
+__device__ __forceinline__ ChunkPos chunk_pos(const Geo& g, int gc) {
+  ChunkPos p;
+  if (!g.varlen) {
+    const int nt = (g.T + CH - 1) / CH;
+    p.b = gc / nt;
+    p.seq = p.b;
+    p.t0 = (gc % nt) * CH;
+    p.n = min(CH, g.T - p.t0);
+    return p;
+  }
+  int off = 0;
+  p.b = 0; p.seq = 0; p.t0 = 0; p.n = 0;
+  for (int s = 0; s < g.nseq; ++s) {
+    const int a = g.cu[s], e = g.cu[s + 1];
+    const int nc = (e - a + CH - 1) / CH;
+    if (gc < off + nc) {
+      p.seq = s;
+      p.t0 = a + (gc - off) * CH;
+      p.n = min(CH, e - p.t0);
+      return p;
+    }
+    off += nc;
+  }
+  return p;
+}
+
+__device__ __forceinline__ SeqPos seq_pos(const Geo& g, int s) {
+  SeqPos p;
+  if (!g.varlen) {
+    const int nt = (g.T + CH - 1) / CH;
+    p.b = s; p.bos = 0; p.len = g.T; p.gc0 = s * nt; p.nchunks = nt;
+    return p;
+  }
+  int off = 0;
+  for (int i = 0; i < s; ++i) off += (g.cu[i + 1] - g.cu[i] + CH - 1) / CH;
+  p.b = 0;
+  p.bos = g.cu[s];
+  p.len = g.cu[s + 1] - g.cu[s];
+  p.gc0 = off;
+  p.nchunks = (p.len + CH - 1) / CH;
+  return p;
+}
+
+// Element offset of token t (absolute within [0,T)) of head h in a [B,H,T,d] tensor, / d.
+__device__ __forceinline__ long tok_index(const Geo& g, int b, int h, int t) {
+  return ((long)b * g.H + h) * g.T + t;
+}
+
+// Scan kernels use a 1-D grid.  Work item (sequence, head) sh and value tile vt run on
+// block L with L % 8 == sh % 8, so the tiles of one memory land on one XCD (workgroups are
+// dealt to the 8 XCDs round-robin) and share its L2 for the chunk operands they all read.
+inline unsigned scan_grid(const Geo& g, int nv) {
+  const unsigned nsh = (unsigned)g.nseq * (unsigned)g.H;
+  return ((nsh + 7u) / 8u) * 8u * (unsigned)nv;
+}
+template <int NV>
+__device__ __forceinline__ bool scan_block(const Geo& g, int& seq, int& h, int& vt) {
+  const int L = blockIdx.x;
+  vt = (L >> 3) % NV;
+  const int sh = ((L >> 3) / NV) * 8 + (L & 7);
+  if (sh >= g.nseq * g.H) return false;
+  seq = sh / g.H;
+  h = sh % g.H;
+  return true;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_up(x, d, 64);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+// Sum over the 16 lanes sharing lgrp() (i.e. over a tile's columns).
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+
+}  // namespace gdr

@@ -1,0 +1,300 @@
+// Forward kernels of the chunked delta-rule operator (Delta family: DeltaNet, Gated DeltaNet).
+//
+// Chunk form of the token recurrence (per chunk of n <= 64 tokens starting from memory W0,
+// g_t = sum_{u<=t} log alpha_u inside the chunk, E_ts = exp(g_t - g_s) for s <= t):
+//   A_ts = (k_t . k_s) E_ts (s < t),  M_ts = (q_t . k_s) E_ts (s <= t)
+//   L = I + diag(beta) A,  T = L^{-1} diag(beta)
+//   X = T (e^g * K),  U = T V                      (WY/UT factors of prod (I - beta k k^T))
+//   R = U - X W0^T                                  (row t: beta_t times the residual r_t)
+//   O = scale * ((e^g * Q) W0^T + M R)
+//   W_next = e^{g_n} W0 + R^T (e^{g_n - g} * K)
+// Three launches: a chunk-parallel prep (A, M, L^{-1}, X, U), a sequential scan over the
+// chunks of each (sequence, head, value-row tile) that carries W in float32 registers and
+// records W0 and R per chunk, and a chunk-parallel output kernel.
+#include "chunk.hpp"
+#include "launch.hpp"
+
+namespace gdr {
+
+// ---------------------------------------------------------------------------------------
+// Prep: per (head, chunk) -- g, M, L^{-1}, X, U.
+// ---------------------------------------------------------------------------------------
+template <typename E, int D, int VAR>
+__global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+                                                  const E* __restrict__ v, const E* __restrict__ beta,
+                                                  const E* __restrict__ alpha, E* __restrict__ Xo,
+                                                  E* __restrict__ Uo, E* __restrict__ Mo, float* __restrict__ Go) {
+  constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 1;
+  __shared__ __align__(16) E Ks[CH * LD];
+  __shared__ __align__(16) E Qs[CH * LD];  // Q, later e^g * K
+  __shared__ __align__(16) E Vs[CH * LD];
+  __shared__ __align__(16) E Ts[CH * LDT];
+  __shared__ __align__(16) float Ls[CH * LF];
+  __shared__ __align__(16) float Li[CH * LF];
+  __shared__ __align__(16) float scr[4 * 256];
+  __shared__ float gs[CH], bs[CH];
+
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id();
+
+  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, cp.n);
+  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, cp.n);
+  g2s_rows<E, CH, D, NT>(Vs, LD, v + tk * D, D, cp.n);
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x;
+    const bool ok = t < cp.n;
+    bs[t] = ok ? (float)beta[tk + t] : 0.f;
+    float la = 0.f;
+    if constexpr (VAR == VAR_GATED) la = ok ? logf((float)alpha[tk + t]) : 0.f;
+    const float g = wave_incl_scan(la);
+    gs[t] = g;
+    Go[u * CH + t] = g;
+  }
+  __syncthreads();
+
+  // Gram tiles: jobs 0..9 -> A (strict lower, times beta_t, into Ls), 10..19 -> M (lower).
+  for (int job = w; job < 20; job += 4) {
+    const bool isM = job >= 10;
+    int mt, nt;
+    tri_tile(isM ? job - 10 : job, mt, nt);
+    const f32x4 acc = mma_k<E, D>(zero4(), rowk(isM ? Qs : Ks, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
+      const bool keep = isM ? (s <= t) : (s < t);
+      float val = 0.f;
+      if (keep) {
+        float dec = 1.f;
+        if constexpr (VAR == VAR_GATED) dec = expf(gs[t] - gs[s]);
+        val = acc[r] * dec;
+      }
+      if (isM) Mo[(u * CH + t) * CH + s] = (E)val;
+      else Ls[t * LF + s] = bs[t] * val;
+    }
+  }
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s = idx & 63;
+    if ((s >> 4) > (t >> 4)) Mo[(u * CH + t) * CH + s] = (E)0.f;
+  }
+  __syncthreads();
+  solve_unit_lower64<NT>(Ls, LF, Li, LF, scr);
+
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s = idx & 63;
+    Ts[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] * bs[s] : 0.f);
+  }
+  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
+    const int t = idx / D, j = idx % D;
+    float e = 1.f;
+    if constexpr (VAR == VAR_GATED) e = expf(gs[t]);
+    Qs[t * LD + j] = (E)(e * (float)Ks[t * LD + j]);
+  }
+  __syncthreads();
+
+  f32x4 xa[D / 16], ua[D / 16];
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    xa[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Qs, LD), 16 * nt);
+    ua[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Vs, LD), 16 * nt);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    store4_n(Ks, LD, 16 * w, 16 * nt, xa[nt]);
+    store4_n(Vs, LD, 16 * w, 16 * nt, ua[nt]);
+  }
+  __syncthreads();
+  s2g_rows<E, CH, D, NT>(Xo + u * CH * D, D, Ks, LD, CH);
+  s2g_rows<E, CH, D, NT>(Uo + u * CH * D, D, Vs, LD, CH);
+}
+
+// ---------------------------------------------------------------------------------------
+// Scan: per (value-row tile, head, sequence), sequential over the sequence's chunks.
+// The tile of W (BV rows x D) lives in accumulators as W^T tiles: wave w owns key tiles
+// jt = w + 4q and every value sub-tile.
+// ---------------------------------------------------------------------------------------
+template <typename E, int D, int BV, int VAR>
+__global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__ k, const E* __restrict__ Xg,
+                                                  const E* __restrict__ Ug, const float* __restrict__ Gg,
+                                                  const float* __restrict__ h0, E* __restrict__ Hs,
+                                                  E* __restrict__ Rg, float* __restrict__ ht) {
+  constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
+  constexpr int NJ = D / 64, NI = BV / 16;
+  __shared__ __align__(16) E Xs[CH * LD];
+  __shared__ __align__(16) E Ks[CH * LD];
+  __shared__ __align__(16) E Us[CH * LDV];
+  __shared__ __align__(16) E Ws[BV * LD];
+  __shared__ __align__(16) E Rn[CH * LDV];
+  __shared__ __align__(16) E Rd[BV * LDR];
+  __shared__ float gs[CH];
+
+  int sq, h, vt;
+  if (!scan_block<D / BV>(geo, sq, h, vt)) return;
+  const int i0 = vt * BV;
+  const SeqPos sp = seq_pos(geo, sq);
+  const int w = wave_id();
+  const long sbase = ((long)sq * geo.H + h) * D;  // row base of this memory in [N,H,D,D]
+
+  f32x4 S[NJ][NI];
+#pragma unroll
+  for (int qq = 0; qq < NJ; ++qq)
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int j0 = acc_row(16 * (w + 4 * qq), 0), i = i0 + acc_col(16 * it);
+      if (h0) {
+        const float4 x = *reinterpret_cast<const float4*>(h0 + (sbase + i) * D + j0);
+        S[qq][it] = f32x4{x.x, x.y, x.z, x.w};
+      } else {
+        S[qq][it] = zero4();
+      }
+    }
+
+  for (int c = 0; c < sp.nchunks; ++c) {
+    const long u = (long)(sp.gc0 + c) * geo.H + h;
+    const int n = min(CH, sp.len - c * CH);
+    const long tk = tok_index(geo, sp.b, h, sp.bos + c * CH);
+    g2s_rows<E, CH, D, NT>(Xs, LD, Xg + u * CH * D, D, CH);
+    g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
+    g2s_rows<E, CH, BV, NT>(Us, LDV, Ug + u * CH * D + i0, D, CH);
+    if (threadIdx.x < CH) gs[threadIdx.x] = Gg[u * CH + threadIdx.x];
+#pragma unroll
+    for (int qq = 0; qq < NJ; ++qq)
+#pragma unroll
+      for (int it = 0; it < NI; ++it) store4_t(Ws, LD, 16 * (w + 4 * qq), 16 * it, S[qq][it]);
+    __syncthreads();
+    s2g_rows<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD, BV);
+    const float gn = gs[CH - 1];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const f32x4 acc = mma_k<E, D>(zero4(), rowk(Xs, LD), 16 * w, rowk(Ws, LD), 16 * it);
+      f32x4 rv, rd;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(16 * w, r), i = acc_col(16 * it);
+        const float val = (float)Us[t * LDV + i] - acc[r];
+        rv[r] = val;
+        float dec = 1.f;
+        if constexpr (VAR == VAR_GATED) dec = expf(gn - gs[t]);
+        rd[r] = val * dec;
+      }
+      store4_n(Rn, LDV, 16 * w, 16 * it, rv);
+      store4_t(Rd, LDR, 16 * w, 16 * it, rd);
+    }
+    __syncthreads();
+    s2g_rows<E, CH, BV, NT>(Rg + u * CH * D + i0, D, Rn, LDV, CH);
+    float eg = 1.f;
+    if constexpr (VAR == VAR_GATED) eg = expf(gn);
+#pragma unroll
+    for (int qq = 0; qq < NJ; ++qq)
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        S[qq][it] *= eg;
+        S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Ks, LD), 16 * (w + 4 * qq), rowk(Rd, LDR), 16 * it);
+      }
+    __syncthreads();
+  }
+  if (ht) {
+#pragma unroll
+    for (int qq = 0; qq < NJ; ++qq)
+#pragma unroll
+      for (int it = 0; it < NI; ++it) {
+        const int j0 = acc_row(16 * (w + 4 * qq), 0), i = i0 + acc_col(16 * it);
+        const f32x4 x = S[qq][it];
+        *reinterpret_cast<float4*>(ht + (sbase + i) * D + j0) = make_float4(x[0], x[1], x[2], x[3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Output: per (head, chunk).  O = scale * (e^g * (Q W0^T) + M R).
+// ---------------------------------------------------------------------------------------
+template <typename E, int D, int VAR>
+__global__ __launch_bounds__(256) void k_fwd_out(Geo geo, const E* __restrict__ q, const E* __restrict__ Mg,
+                                                 const E* __restrict__ Rg, const float* __restrict__ Gg,
+                                                 const E* __restrict__ Hs, E* __restrict__ o) {
+  constexpr int NT = 256, LD = D + pad16<E>(), LDR = CH + pad16<E>();
+  __shared__ __align__(16) E Qs[CH * LD];
+  __shared__ __align__(16) E Ws[D * LD];
+  __shared__ __align__(16) E Ms[CH * LDR];
+  __shared__ __align__(16) E Rt[D * LDR];
+  __shared__ float gs[CH];
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id();
+  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, cp.n);
+  g2s_rows<E, D, D, NT>(Ws, LD, Hs + u * D * D, D, D);
+  g2s_rows<E, CH, CH, NT>(Ms, LDR, Mg + u * CH * CH, CH, CH);
+  g2s_rows_t<E, CH, D, NT>(Rt, LDR, Rg + u * CH * D, D, CH);
+  if (threadIdx.x < CH) gs[threadIdx.x] = Gg[u * CH + threadIdx.x];
+  __syncthreads();
+  f32x4 ov[D / 16];
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    const f32x4 a1 = mma_k<E, D>(zero4(), rowk(Qs, LD), 16 * w, rowk(Ws, LD), 16 * nt);
+    const f32x4 a2 = mma_k<E, CH>(zero4(), rowk(Ms, LDR), 16 * w, rowk(Rt, LDR), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float e = 1.f;
+      if constexpr (VAR == VAR_GATED) e = expf(gs[acc_row(16 * w, r)]);
+      ov[nt][r] = geo.scale * (e * a1[r] + a2[r]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) store4_n(Qs, LD, 16 * w, 16 * nt, ov[nt]);
+  __syncthreads();
+  s2g_rows<E, CH, D, NT>(o + tk * D, D, Qs, LD, cp.n);
+}
+
+// ---------------------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------------------
+template <typename E, int D, int VAR>
+static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st) {
+  const Geo& g = p.geo;
+  const dim3 cgrid(g.total_chunks, g.H);
+  if (g.total_chunks > 0) {
+    hipLaunchKernelGGL((k_fwd_prep<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k,
+                       (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G);
+  }
+  if (p.bv == 16) {
+    hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
+                       (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
+                       (E*)p.R, ht);
+  } else {
+    hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
+                       (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
+                       (E*)p.R, ht);
+  }
+  if (want_out && g.total_chunks > 0) {
+    hipLaunchKernelGGL((k_fwd_out<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)p.M,
+                       (const E*)p.R, (const float*)p.G, (const E*)p.Hs, (E*)o);
+  }
+  return hipGetLastError();
+}
+
+hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st) {
+  const bool bf = p.dtype == GDR_BF16;
+  switch (p.variant) {
+    case GDR_DELTANET:
+      if (bf && p.D == 128) return fwd_impl<bf16, 128, VAR_DELTANET>(p, in, o, ht, want_out, st);
+      if (bf && p.D == 64) return fwd_impl<bf16, 64, VAR_DELTANET>(p, in, o, ht, want_out, st);
+      if (!bf && p.D == 64) return fwd_impl<float, 64, VAR_DELTANET>(p, in, o, ht, want_out, st);
+      break;
+    case GDR_GATED:
+      if (bf && p.D == 128) return fwd_impl<bf16, 128, VAR_GATED>(p, in, o, ht, want_out, st);
+      if (bf && p.D == 64) return fwd_impl<bf16, 64, VAR_GATED>(p, in, o, ht, want_out, st);
+      if (!bf && p.D == 64) return fwd_impl<float, 64, VAR_GATED>(p, in, o, ht, want_out, st);
+      break;
+    default:
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdr

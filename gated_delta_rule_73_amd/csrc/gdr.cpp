@@ -1,0 +1,247 @@
+// C ABI of the chunked delta-rule operator: argument checks, planning, workspace carving and
+// kernel dispatch.  Everything here runs on the host; nothing is launched before every
+// argument has been checked.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/gdr.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdr_status fail(gdr_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Sizes {
+  long long units = 0;   // chunks * heads
+  int total_chunks = 0;
+  int nstates = 0;
+  size_t esz = 0;
+  size_t X, M, G, Hs, R, Ub, dHs, dR;
+  size_t cache() const { return X + M + G + Hs + R; }
+};
+
+// Checks the problem description and computes the buffer sizes.
+gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
+  if (!p) return fail(GDR_ERR_INVALID_ARG, "problem is NULL");
+  if (p->variant < GDR_DELTANET || p->variant > GDR_GDN2)
+    return fail(GDR_ERR_INVALID_ARG, "variant %d is not a gdr_variant", p->variant);
+  if (p->dtype != GDR_F32 && p->dtype != GDR_BF16)
+    return fail(GDR_ERR_INVALID_ARG, "dtype %d is not a gdr_dtype", p->dtype);
+  if (p->B < 1 || p->H < 1 || p->T < 0)
+    return fail(GDR_ERR_INVALID_ARG, "need B >= 1, H >= 1, T >= 0 (got B=%d H=%d T=%d)", p->B, p->H, p->T);
+  if (p->dk < 1 || p->dv < 1) return fail(GDR_ERR_INVALID_ARG, "head sizes must be positive");
+  if (p->chunk < 1) return fail(GDR_ERR_INVALID_ARG, "chunk must be positive");
+  if (!std::isfinite(p->scale)) return fail(GDR_ERR_INVALID_ARG, "scale must be finite");
+  if (p->n_seqs < 0) return fail(GDR_ERR_INVALID_ARG, "n_seqs must be >= 0");
+  if (p->H > 65535) return fail(GDR_ERR_UNSUPPORTED, "H > 65535 is not supported");
+  long long total_chunks = 0;
+  if (p->n_seqs > 0) {
+    if (p->B != 1) return fail(GDR_ERR_INVALID_ARG, "packed sequences need B == 1 (got %d)", p->B);
+    if (!p->cu_seqlens_host || !p->cu_seqlens_dev)
+      return fail(GDR_ERR_INVALID_ARG, "packed sequences need cu_seqlens_host and cu_seqlens_dev");
+    const int32_t* cu = p->cu_seqlens_host;
+    if (cu[0] != 0) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+    if (cu[p->n_seqs] != p->T)
+      return fail(GDR_ERR_INVALID_ARG, "cu_seqlens[%d] must equal T=%d (got %d)", p->n_seqs, p->T, cu[p->n_seqs]);
+    for (int i = 0; i < p->n_seqs; ++i) {
+      if (cu[i + 1] < cu[i]) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (index %d)", i + 1);
+      total_chunks += (cu[i + 1] - cu[i] + gdr::CH - 1) / gdr::CH;
+    }
+  } else {
+    if (p->cu_seqlens_host || p->cu_seqlens_dev)
+      return fail(GDR_ERR_INVALID_ARG, "cu_seqlens given but n_seqs == 0");
+    total_chunks = (long long)p->B * ((p->T + gdr::CH - 1) / gdr::CH);
+  }
+  if (p->chunk != gdr::CH) return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: only 64 is built", p->chunk);
+  if (p->dk != p->dv) return fail(GDR_ERR_UNSUPPORTED, "dk=%d != dv=%d is not built", p->dk, p->dv);
+  if (p->dtype == GDR_BF16 && p->dk != 64 && p->dk != 128)
+    return fail(GDR_ERR_UNSUPPORTED, "bf16 head size %d: only 64 and 128 are built", p->dk);
+  if (p->dtype == GDR_F32 && p->dk != 64)
+    return fail(GDR_ERR_UNSUPPORTED, "float32 head size %d: only 64 is built", p->dk);
+  if (p->variant == GDR_KDA || p->variant == GDR_GDN2)
+    return fail(GDR_ERR_UNSUPPORTED, "variant %d is not built yet", p->variant);
+  if (total_chunks > 0x7fffffffLL) return fail(GDR_ERR_UNSUPPORTED, "too many chunks");
+  if ((long long)p->B * p->H * (long long)p->T * p->dk > (1LL << 40))
+    return fail(GDR_ERR_UNSUPPORTED, "tensor too large");
+  Sizes s;
+  s.total_chunks = (int)total_chunks;
+  s.units = total_chunks * p->H;
+  s.nstates = p->n_seqs > 0 ? p->n_seqs : p->B;
+  s.esz = p->dtype == GDR_BF16 ? 2 : 4;
+  const size_t D = (size_t)p->dk, C = gdr::CH, U = (size_t)s.units, A = 256;
+  s.X = align_up(U * C * D * s.esz, A);
+  s.M = align_up(U * C * C * s.esz, A);
+  s.G = align_up(U * C * 4, A);
+  s.Hs = align_up(U * D * D * s.esz, A);
+  s.R = align_up(U * C * D * s.esz, A);
+  s.Ub = align_up(U * C * D * s.esz, A);
+  s.dHs = align_up(U * D * D * s.esz, A);
+  s.dR = align_up(U * C * D * s.esz, A);
+  *sz = s;
+  return GDR_OK;
+}
+
+gdr_status check_inputs(const gdr_problem* p, const gdr_inputs* in) {
+  if (!in) return fail(GDR_ERR_INVALID_ARG, "inputs is NULL");
+  const void* ptrs[] = {in->q, in->k, in->v, in->beta, in->alpha, in->erase, in->write, in->h0};
+  for (const void* x : ptrs)
+    if (x && !aligned(x, 16)) return fail(GDR_ERR_INVALID_ARG, "input pointers must be 16-byte aligned");
+  if (p->T == 0) return GDR_OK;  // no token is read: token tensors may be empty (NULL)
+  if (!in->q || !in->k || !in->v) return fail(GDR_ERR_INVALID_ARG, "q, k and v are required");
+  const bool gdn2 = p->variant == GDR_GDN2;
+  if (!in->beta && !gdn2) return fail(GDR_ERR_INVALID_ARG, "beta is required for this variant");
+  if ((in->alpha != nullptr) != (p->variant != GDR_DELTANET))
+    return fail(GDR_ERR_INVALID_ARG, p->variant == GDR_DELTANET ? "alpha must be NULL for DeltaNet"
+                                                                 : "alpha is required for this variant");
+  if ((in->erase != nullptr) != gdn2 || (in->write != nullptr) != gdn2)
+    return fail(GDR_ERR_INVALID_ARG, "erase/write gates are given iff the variant is GDR_GDN2");
+  return GDR_OK;
+}
+
+gdr_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return GDR_OK;
+  if (!ws) return fail(GDR_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(ws, 256)) return fail(GDR_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(GDR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return GDR_OK;
+}
+
+gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws) {
+  gdr::Plan pl;
+  pl.geo.B = p->B;
+  pl.geo.H = p->H;
+  pl.geo.T = p->T;
+  pl.geo.nseq = s.nstates;
+  pl.geo.varlen = p->n_seqs > 0;
+  pl.geo.cu = p->cu_seqlens_dev;
+  pl.geo.total_chunks = s.total_chunks;
+  pl.geo.scale = p->scale;
+  pl.variant = p->variant;
+  pl.dtype = p->dtype;
+  pl.D = p->dk;
+  // Value-row tile of the scans: 16 rows when there are few memories to spread over the CUs.
+  const long long mem = (long long)s.nstates * p->H;
+  pl.bv = (mem * (p->dk / 32) >= 256) ? 32 : 16;
+  char* c = cache;
+  pl.X = c; c += s.X;
+  pl.M = c; c += s.M;
+  pl.G = reinterpret_cast<float*>(c); c += s.G;
+  pl.Hs = c; c += s.Hs;
+  pl.R = c; c += s.R;
+  char* w = ws;
+  pl.Ub = w; w += s.Ub;
+  pl.dHs = w; w += s.dHs;
+  pl.dR = w; w += s.dR;
+  return pl;
+}
+
+gdr_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GDR_OK;
+  return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_workspace_size(const gdr_problem* p, int backward, size_t* bytes) {
+  Sizes s;
+  gdr_status st = check_problem(p, &s);
+  if (st != GDR_OK) return st;
+  if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = s.cache() + s.Ub + (backward ? s.dHs + s.dR : 0);
+  return GDR_OK;
+}
+
+gdr_status gdr_saved_size(const gdr_problem* p, size_t* bytes) {
+  Sizes s;
+  gdr_status st = check_problem(p, &s);
+  if (st != GDR_OK) return st;
+  if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = s.cache();
+  return GDR_OK;
+}
+
+gdr_status gdr_forward(const gdr_problem* p, const gdr_inputs* in, void* o, float* ht, void* saved, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Sizes s;
+  gdr_status st = check_problem(p, &s);
+  if (st != GDR_OK) return st;
+  if ((st = check_inputs(p, in)) != GDR_OK) return st;
+  if (!o && p->T > 0) return fail(GDR_ERR_INVALID_ARG, "o is required");
+  if ((o && !aligned(o, 16)) || (ht && !aligned(ht, 16)) || (saved && !aligned(saved, 256)))
+    return fail(GDR_ERR_INVALID_ARG, "o/ht must be 16-byte and saved 256-byte aligned");
+  if ((st = check_ws(ws, ws_bytes, s.cache() + s.Ub)) != GDR_OK) return st;
+  char* cache = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + s.Ub;
+  gdr::Plan pl = make_plan(p, s, cache, static_cast<char*>(ws));
+  g_last_error.clear();
+  return hip_status(gdr::run_forward(pl, *in, o, ht, true, static_cast<hipStream_t>(stream)), "gdr_forward launch");
+}
+
+gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* dO, const float* dht,
+                        const void* saved, gdr_grads* g, void* ws, size_t ws_bytes, void* stream) {
+  Sizes s;
+  gdr_status st = check_problem(p, &s);
+  if (st != GDR_OK) return st;
+  if ((st = check_inputs(p, in)) != GDR_OK) return st;
+  if (!g) return fail(GDR_ERR_INVALID_ARG, "grads is NULL");
+  if (p->T > 0) {
+    if (!dO) return fail(GDR_ERR_INVALID_ARG, "dO is required");
+    if (!g->dq || !g->dk || !g->dv) return fail(GDR_ERR_INVALID_ARG, "dq, dk and dv are required");
+    if ((g->dbeta != nullptr) != (in->beta != nullptr))
+      return fail(GDR_ERR_INVALID_ARG, "dbeta is required iff beta is given");
+    if ((g->dalpha != nullptr) != (in->alpha != nullptr))
+      return fail(GDR_ERR_INVALID_ARG, "dalpha is required iff alpha is given");
+    if ((g->derase != nullptr) != (in->erase != nullptr) || (g->dwrite != nullptr) != (in->write != nullptr))
+      return fail(GDR_ERR_INVALID_ARG, "derase/dwrite are required iff the gates are given");
+  }
+  const void* ptrs[] = {dO, dht, g->dq, g->dk, g->dv, g->dbeta, g->dalpha, g->derase, g->dwrite, g->dh0};
+  for (const void* x : ptrs)
+    if (x && !aligned(x, 16)) return fail(GDR_ERR_INVALID_ARG, "gradient pointers must be 16-byte aligned");
+  if (saved && !aligned(saved, 256)) return fail(GDR_ERR_INVALID_ARG, "saved must be 256-byte aligned");
+  if ((st = check_ws(ws, ws_bytes, s.cache() + s.Ub + s.dHs + s.dR)) != GDR_OK) return st;
+  char* base = static_cast<char*>(ws);
+  char* cache = saved ? const_cast<char*>(static_cast<const char*>(saved)) : base + s.Ub + s.dHs + s.dR;
+  gdr::Plan pl = make_plan(p, s, cache, base);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  g_last_error.clear();
+  if (!saved) {
+    st = hip_status(gdr::run_forward(pl, *in, nullptr, nullptr, false, hs), "gdr_backward recompute launch");
+    if (st != GDR_OK) return st;
+  }
+  return hip_status(gdr::run_backward(pl, *in, dO, dht, *g, hs), "gdr_backward launch");
+}
+
+const char* gdr_status_string(gdr_status s) {
+  switch (s) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED";
+    case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP";
+  }
+  return "GDR_UNKNOWN_STATUS";
+}
+
+const char* gdr_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+/*
+ * gdr.h -- C ABI of the chunked delta-rule memory operator on AMD MI355X (gfx950).
+ *
+ * The operator is the recurrent matrix memory of "Linear Attention Architectures:
+ * Mechanisms, Trade-offs, and Cross-Layer Routing" (section "Metodologia y Marco de
+ * Trabajo", item 1 "Notacion Unificada"): per (sequence, head) a memory W (d_v x d_k)
+ * is updated once per token.  With D_t the token's decay, v_bar = (W D_t) k the memory's
+ * prediction and r = v - v_bar the residual:
+ *
+ *   DeltaNet        W <- W + beta r k^T                         (no decay)
+ *   Gated DeltaNet  W <- alpha W; then the DeltaNet write       (scalar alpha per token)
+ *   Kimi Delta Att. W <- W diag(alpha); then the DeltaNet write (alpha per key channel)
+ *   Gated DeltaNet-2 W <- alpha W; W <- W - v_bar (beta e*k)^T + (beta w*v) k^T
+ *                                    (e: per-key-channel erase gate, w: per-value-channel
+ *                                     write gate; beta may be absent, meaning 1)
+ *   output          o_t = scale * W_t q_t   (memory after token t's write)
+ *
+ * The library computes it in chunkwise-parallel form (chunks of 64 tokens: per-chunk
+ * WY/UT factors of the products of (I - beta k k^T), a triangular solve, an
+ * inter-chunk state carry), forward and backward.
+ *
+ * Conventions (all entry points):
+ *  - Token tensors are contiguous [B, H, T, d] in the problem's I/O dtype (float32 or
+ *    bfloat16), gates included; states (h0, ht, dh0, dht) are float32 [N, H, d_v, d_k].
+ *    N = B for a dense batch, N = n_seqs for packed variable-length sequences (then B == 1
+ *    and sequence n covers tokens [cu_seqlens[n], cu_seqlens[n+1]) of every head).
+ *  - Every pointer is owned by the caller.  The library allocates no device memory and
+ *    keeps no state between calls; scratch lives in the caller's workspace.
+ *  - Calls are asynchronous on the given stream (a hipStream_t passed as void*; NULL is the
+ *    default stream).  cu_seqlens_host is read on the host for checking and planning only.
+ *  - Every argument is checked before anything is launched.  On any non-OK return nothing
+ *    was launched and no output was written; gdr_last_error() gives a thread-local message.
+ *  - Device pointers must be 16-byte aligned, the workspace 256-byte aligned.
+ *  - NaN and Inf inputs are not checked; they propagate.
+ *  - The entry points are reentrant; calls that share a workspace must be ordered.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_ERR_INVALID_ARG = 1,  /* a pointer, size, flag or cu_seqlens entry is wrong */
+  GDR_ERR_UNSUPPORTED = 2,  /* valid, but not built here (e.g. head size or chunk size) */
+  GDR_ERR_WORKSPACE = 3,    /* workspace NULL, misaligned or smaller than required */
+  GDR_ERR_HIP = 4           /* a HIP launch failed; see gdr_last_error() */
+} gdr_status;
+
+typedef enum {
+  GDR_DELTANET = 0, /* alpha absent */
+  GDR_GATED = 1,    /* alpha [B,H,T] */
+  GDR_KDA = 2,      /* alpha [B,H,T,d_k] */
+  GDR_GDN2 = 3      /* alpha [B,H,T]; erase [B,H,T,d_k]; write [B,H,T,d_v]; beta optional */
+} gdr_variant;
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+typedef struct {
+  int32_t variant;                /* gdr_variant */
+  int32_t dtype;                  /* gdr_dtype of every token-indexed tensor */
+  int32_t B, H, T;                /* batch, heads, tokens (T >= 0) */
+  int32_t dk, dv;                 /* head sizes; supported: dk == dv, 64 or 128 (float32: 64) */
+  int32_t chunk;                  /* chunk length; supported: 64 */
+  int32_t n_seqs;                 /* 0: dense batch; > 0: packed sequences, needs B == 1 */
+  const int32_t *cu_seqlens_host; /* n_seqs+1 offsets: [0] = 0, [n_seqs] = T, non-decreasing */
+  const int32_t *cu_seqlens_dev;  /* the same offsets in device memory (read by kernels) */
+  float scale;                    /* o = scale * W q; finite */
+} gdr_problem;
+
+typedef struct {
+  const void *q, *k, *v;   /* [B,H,T,dk], [B,H,T,dk], [B,H,T,dv]; required */
+  const void *beta;        /* [B,H,T]; required except for GDR_GDN2, where NULL means 1 */
+  const void *alpha;       /* NULL for GDR_DELTANET, else see gdr_variant; values in (0,1] */
+  const void *erase;       /* GDR_GDN2 only: [B,H,T,dk]; NULL otherwise */
+  const void *write;       /* GDR_GDN2 only: [B,H,T,dv]; NULL otherwise */
+  const float *h0;         /* [N,H,dv,dk] float32 initial memory, or NULL for zeros */
+} gdr_inputs;
+
+typedef struct {           /* same shape and dtype as the matching input */
+  void *dq, *dk, *dv;      /* required */
+  void *dbeta;             /* required iff inputs->beta != NULL */
+  void *dalpha;            /* required iff inputs->alpha != NULL; gradient w.r.t. alpha */
+  void *derase, *dwrite;   /* required iff the variant is GDR_GDN2 */
+  float *dh0;              /* optional [N,H,dv,dk] float32 */
+} gdr_grads;
+
+/* Bytes of workspace gdr_forward (backward == 0) or gdr_backward (backward != 0) needs.
+ * The backward figure assumes saved == NULL (it recomputes the forward memories); with a
+ * saved buffer the same size is accepted.  Errors: INVALID_ARG, UNSUPPORTED. */
+gdr_status gdr_workspace_size(const gdr_problem *p, int backward, size_t *bytes);
+
+/* Bytes of the optional forward->backward buffer: the memory at the start of every chunk,
+ * in the I/O dtype.  Errors: INVALID_ARG, UNSUPPORTED. */
+gdr_status gdr_saved_size(const gdr_problem *p, size_t *bytes);
+
+/* Forward.  o: [B,H,T,dv] I/O dtype (required).  ht: [N,H,dv,dk] float32 final memory,
+ * or NULL.  saved: gdr_saved_size() bytes or NULL; when given, the chunk-start memories
+ * are written there for a later gdr_backward.  ws: gdr_workspace_size(p, 0) bytes. */
+gdr_status gdr_forward(const gdr_problem *p, const gdr_inputs *in, void *o, float *ht,
+                       void *saved, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of sum(o * dO) + sum(ht * dht).  dO: [B,H,T,dv] I/O dtype (required).
+ * dht: [N,H,dv,dk] float32 or NULL (zeros).  saved: the buffer a gdr_forward with the same
+ * problem and inputs filled, or NULL to recompute it inside the workspace.
+ * ws: gdr_workspace_size(p, 1) bytes.  Gradients are overwritten, not accumulated. */
+gdr_status gdr_backward(const gdr_problem *p, const gdr_inputs *in, const void *dO,
+                        const float *dht, const void *saved, gdr_grads *g, void *ws,
+                        size_t ws_bytes, void *stream);
+
+const char *gdr_status_string(gdr_status s);
+
+/* Thread-local description of the last non-OK return of this thread ("" if none). */
+const char *gdr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

@@ -49,7 +49,9 @@ def _f64(x):
 
 
 def _sequences(B, T, cu_seqlens):
-    """Yield (batch index, begin, end, state index) for every independent sequence."""
+    """Yield (batch index, begin, end, state index) for every independent sequence.
+
+    A packed sequence may be empty; its memory then stays at its initial value."""
     if cu_seqlens is None:
         for b in range(B):
             yield b, 0, T, b
@@ -57,8 +59,8 @@ def _sequences(B, T, cu_seqlens):
         cu = [int(c) for c in cu_seqlens]
         if B != 1:
             raise ValueError("packed variable-length sequences need B == 1")
-        if cu[0] != 0 or cu[-1] != T or any(b <= a for a, b in zip(cu[:-1], cu[1:])):
-            raise ValueError("cu_seqlens must increase strictly from 0 to T")
+        if cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu[:-1], cu[1:])):
+            raise ValueError("cu_seqlens must run from 0 to T without decreasing")
         for n in range(len(cu) - 1):
             yield 0, cu[n], cu[n + 1], n
 

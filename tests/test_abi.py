@@ -1,0 +1,175 @@
+"""The C ABI on a host without a GPU: the library loads, exports every function the header
+declares, and rejects every invalid argument with the right status before launching anything.
+Device pointers here are fake (never dereferenced: each call fails its checks first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_73_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from gated_delta_rule_73_amd import build
+        build.build()
+    return bd.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    header = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    names = set(re.findall(r"^\s*(?:gdr_status|const char \*)\s*(gdr_\w+)\s*\(", header, re.M))
+    assert names >= {"gdr_workspace_size", "gdr_saved_size", "gdr_forward", "gdr_backward",
+                     "gdr_status_string", "gdr_last_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _problem(**kw):
+    p = dict(variant=1, dtype=1, B=2, H=4, T=300, dk=128, dv=128, chunk=64, n_seqs=0,
+             cu_seqlens_host=None, cu_seqlens_dev=None, scale=1.0)
+    p.update(kw)
+    return bd.GdrProblem(**p)
+
+
+def _inputs(**kw):
+    x = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, alpha=FAKE, erase=None, write=None, h0=None)
+    x.update(kw)
+    return bd.GdrInputs(**x)
+
+
+def _fwd(lib, p, ins, o=FAKE, ht=None, saved=None, ws=FAKE, ws_bytes=1 << 40):
+    return lib.gdr_forward(ctypes.byref(p), ctypes.byref(ins) if ins is not None else None, o, ht, saved, ws,
+                           ws_bytes, None)
+
+
+def _ws(lib, p, backward=False):
+    n = ctypes.c_size_t(0)
+    st = lib.gdr_workspace_size(ctypes.byref(p), int(backward), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes(lib):
+    p = _problem(B=8, H=8, T=4096)
+    st, fwd = _ws(lib, p)
+    assert st == bd.GDR_OK
+    st, bwd = _ws(lib, p, True)
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_saved_size(ctypes.byref(p), ctypes.byref(n)) == bd.GDR_OK
+    units = 8 * 64 * 8
+    per = 64 * 128 * 2
+    cache = units * (per + 64 * 64 * 2 + 64 * 4 + 128 * 128 * 2 + per)
+    assert n.value == cache
+    assert fwd == cache + units * per
+    assert bwd == fwd + units * (128 * 128 * 2 + per)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(variant=7), bd.GDR_ERR_INVALID_ARG),
+    (dict(dtype=5), bd.GDR_ERR_INVALID_ARG),
+    (dict(B=0), bd.GDR_ERR_INVALID_ARG),
+    (dict(H=0), bd.GDR_ERR_INVALID_ARG),
+    (dict(T=-1), bd.GDR_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), bd.GDR_ERR_INVALID_ARG),
+    (dict(n_seqs=-1), bd.GDR_ERR_INVALID_ARG),
+    (dict(chunk=32), bd.GDR_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=64), bd.GDR_ERR_UNSUPPORTED),
+    (dict(dk=96, dv=96), bd.GDR_ERR_UNSUPPORTED),
+    (dict(dtype=0, dk=128, dv=128), bd.GDR_ERR_UNSUPPORTED),
+    (dict(n_seqs=2, B=2), bd.GDR_ERR_INVALID_ARG),
+    (dict(n_seqs=2, B=1), bd.GDR_ERR_INVALID_ARG),  # cu_seqlens missing
+])
+def test_problem_checks(lib, kw, status):
+    p = _problem(**kw)
+    st, _ = _ws(lib, p)
+    assert st == status, lib.gdr_last_error()
+    assert _fwd(lib, p, _inputs()) == status
+    assert lib.gdr_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("cu,ok", [
+    ([0, 100, 300], True), ([0, 0, 300], True), ([1, 100, 300], False), ([0, 100, 299], False),
+    ([0, 200, 100, 300], False),
+])
+def test_cu_seqlens_checks(lib, cu, ok):
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    p = _problem(B=1, n_seqs=len(cu) - 1, cu_seqlens_host=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
+                 cu_seqlens_dev=FAKE)
+    st, _ = _ws(lib, p)
+    assert (st == bd.GDR_OK) == ok
+    if not ok:
+        assert st == bd.GDR_ERR_INVALID_ARG
+
+
+def test_cu_seqlens_without_packing_rejected(lib):
+    arr = (ctypes.c_int32 * 2)(0, 300)
+    p = _problem(cu_seqlens_host=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+    assert _ws(lib, p)[0] == bd.GDR_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("variant,kw", [
+    (1, dict(alpha=None)),                 # gated needs alpha
+    (0, dict()),                           # deltanet takes no alpha
+    (1, dict(beta=None)),                  # delta family needs beta
+    (1, dict(erase=FAKE, write=FAKE)),     # gates only for gdn2
+    (1, dict(q=None)),
+    (1, dict(k=FAKE + 8)),                 # misaligned
+])
+def test_input_checks(lib, variant, kw):
+    p = _problem(variant=variant)
+    assert _fwd(lib, p, _inputs(**kw)) == bd.GDR_ERR_INVALID_ARG
+
+
+def test_null_inputs_and_outputs(lib):
+    p = _problem()
+    assert _fwd(lib, p, None) == bd.GDR_ERR_INVALID_ARG
+    assert _fwd(lib, p, _inputs(), o=None) == bd.GDR_ERR_INVALID_ARG
+    assert _fwd(lib, p, _inputs(), o=FAKE + 4) == bd.GDR_ERR_INVALID_ARG
+    assert _fwd(lib, p, _inputs(), saved=FAKE + 16) == bd.GDR_ERR_INVALID_ARG
+
+
+def test_workspace_checks(lib):
+    p = _problem()
+    _, need = _ws(lib, p)
+    assert _fwd(lib, p, _inputs(), ws=None) == bd.GDR_ERR_WORKSPACE
+    assert _fwd(lib, p, _inputs(), ws=FAKE + 16) == bd.GDR_ERR_WORKSPACE
+    assert _fwd(lib, p, _inputs(), ws_bytes=need - 1) == bd.GDR_ERR_WORKSPACE
+
+
+def _bwd(lib, p, ins, grads, dO=FAKE, ws=FAKE, ws_bytes=1 << 40, saved=None):
+    return lib.gdr_backward(ctypes.byref(p), ctypes.byref(ins), dO, None, saved, ctypes.byref(grads) if grads else None,
+                            ws, ws_bytes, None)
+
+
+def _grads(**kw):
+    g = dict(dq=FAKE, dk=FAKE, dv=FAKE, dbeta=FAKE, dalpha=FAKE, derase=None, dwrite=None, dh0=None)
+    g.update(kw)
+    return bd.GdrGrads(**g)
+
+
+@pytest.mark.parametrize("kw", [dict(dq=None), dict(dbeta=None), dict(dalpha=None), dict(derase=FAKE),
+                                dict(dh0=FAKE + 4)])
+def test_backward_gradient_checks(lib, kw):
+    p = _problem()
+    assert _bwd(lib, p, _inputs(), _grads(**kw)) == bd.GDR_ERR_INVALID_ARG
+
+
+def test_backward_other_checks(lib):
+    p = _problem()
+    assert _bwd(lib, p, _inputs(), None) == bd.GDR_ERR_INVALID_ARG
+    assert _bwd(lib, p, _inputs(), _grads(), dO=None) == bd.GDR_ERR_INVALID_ARG
+    _, need = _ws(lib, p, True)
+    assert _bwd(lib, p, _inputs(), _grads(), ws_bytes=need - 1) == bd.GDR_ERR_WORKSPACE
+    assert _bwd(lib, p, _inputs(), _grads(), saved=FAKE + 64) == bd.GDR_ERR_INVALID_ARG
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["GDR_OK", "GDR_ERR_INVALID_ARG", "GDR_ERR_UNSUPPORTED", "GDR_ERR_WORKSPACE",
+                                 "GDR_ERR_HIP"]):
+        assert lib.gdr_status_string(code).decode() == name
+    assert lib.gdr_status_string(99).decode() == "GDR_UNKNOWN_STATUS"
