@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked Gated DeltaNet forward + backward on one MI355X.
+
+One step = gdr_forward (keeping the per-chunk results for the backward) followed by
+gdr_backward, i.e. every stage of the operator's training path, on one batch of seeded
+synthetic inputs already resident in HBM.  The default workload is the long-context Gated
+DeltaNet case: B=1, H=16, T=32768 packed as four sequences (4096, 8192, 12288, 8192 tokens),
+d_k = d_v = 128, bf16 inputs, float32 initial memory per sequence.
+
+Prints one JSON line.  `value` is tokens/s = B*T / (time of one step).  `roofline` is the
+dominant kernel's achieved bandwidth against MI355X's 8 TB/s, timed with HIP events around
+each of its launches inside the timed region; `path_roofline` is the whole step against the
+bytes the operator must move at minimum; `cpu_baseline` is the float64 oracle timed on a
+bounded sample of the same workload on this host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, published
+
+# Bytes each kernel must read and write once per (chunk, head) unit for d = 128, bf16 I/O,
+# C = 64 tokens (see the design notes: its inputs and outputs, each touched once).
+D_, C_, ESZ = 128, 64, 2
+TOK = C_ * D_ * ESZ          # one 64 x 128 token tile
+SQR = D_ * D_ * ESZ          # one 128 x 128 memory
+GRAM = C_ * C_ * ESZ         # one 64 x 64 chunk matrix
+GATE = C_ * ESZ              # one gate vector of the chunk
+GLOG = C_ * 4                # in-chunk log decay (float32)
+KERNEL_BYTES_PER_UNIT = {
+    "fwd_prep": 3 * TOK + 2 * GATE + 2 * TOK + GRAM + GLOG,
+    "fwd_scan": 3 * TOK + GLOG + SQR + TOK,
+    "fwd_out": TOK + GRAM + TOK + SQR + GLOG + TOK,
+    "bwd_scan": 3 * TOK + TOK + GRAM + GLOG + SQR + TOK,
+    "bwd_chunk": 4 * TOK + 2 * GATE + GRAM + GLOG + SQR + TOK + SQR + TOK + 3 * TOK + 2 * GATE,
+}
+# The operator's own minimum per head-token (Gated, d = 128, bf16): forward reads q, k, v,
+# beta, alpha and writes o; backward reads q, k, v, dO, beta, alpha and writes dq, dk, dv,
+# dbeta, dalpha.
+PATH_BYTES_PER_HEAD_TOKEN = (3 * 256 + 4 + 256) + (4 * 256 + 4 + 3 * 256 + 4)
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "gated_delta_rule_73_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken on
+    the current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_sha") != source_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w):
+    """Time the oracle (float64, token by token) on the first tokens of the workload's first
+    sequence, all heads, forward + backward.  BLAS is held to one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import recurrence as R
+    L = 1024
+    wl = w.with_(T=L, cu_seqlens=None, h0_std=0.0, B=1)
+    inp = synth.make_inputs(wl, with_grad=True)
+    kw = {k: inp[k] for k in ("q", "k", "v", "beta", "alpha")}
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        R.forward(**kw, variant=w.variant)
+        R.backward(**kw, do=inp["do"], variant=w.variant)
+        wall = time.perf_counter() - t0
+    # tokens/s of the full workload: each token position carries H heads
+    return {"value": L / wall, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"forward+backward of the first {L} tokens of one sequence, all {w.H} heads, "
+                      f"d={w.dk}, float64 numpy, one thread; {wall:.1f} s"}
+
+
+class Runner:
+    """Holds the device buffers of one workload and calls the C ABI directly."""
+
+    def __init__(self, w, inp):
+        import torch
+
+        from gated_delta_rule_73_amd import binding as bd
+        from tests._helpers import gpu_inputs, to_gpu
+        self.bd = bd
+        self.lib = bd.load_library()
+        self.w = w
+        g = gpu_inputs(inp, w.dtype)
+        self.g = g
+        self.do = to_gpu(inp["do"], w.dtype)
+        self.p, self.keep = bd.make_problem(g["q"], g["v"], variant=w.variant, cu_seqlens=inp.get("cu_seqlens"))
+        N = self.p.n_seqs if self.p.n_seqs > 0 else self.p.B
+        dev = g["q"].device
+        self.o = torch.empty_like(g["v"])
+        self.ht = torch.empty((N, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
+        self.saved = torch.empty(bd.gdr_saved_size(self.p), dtype=torch.uint8, device=dev)
+        nws = bd.gdr_workspace_size(self.p, True)
+        self.ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        self.grads = {n: (None if g[x] is None else torch.empty_like(g[x]))
+                      for n, x in (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dbeta", "beta"),
+                                   ("dalpha", "alpha"), ("derase", "erase"), ("dwrite", "write"))}
+        self.grads["dh0"] = torch.empty_like(self.ht)
+        self.ins = bd._inputs(*(g[n] for n in ("q", "k", "v", "beta", "alpha", "erase", "write", "h0")))
+        self.gr = bd.GdrGrads(**{n: bd._ptr(t) for n, t in self.grads.items()})
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def fwd(self):
+        st = self.lib.gdr_forward(ctypes.byref(self.p), ctypes.byref(self.ins), self.o.data_ptr(),
+                                  self.ht.data_ptr(), self.saved.data_ptr(), self.ws.data_ptr(),
+                                  self.ws.numel(), self.stream)
+        self.bd._check(self.lib, st)
+
+    def bwd(self):
+        st = self.lib.gdr_backward(ctypes.byref(self.p), ctypes.byref(self.ins), self.do.data_ptr(), None,
+                                   self.saved.data_ptr(), ctypes.byref(self.gr), self.ws.data_ptr(),
+                                   self.ws.numel(), self.stream)
+        self.bd._check(self.lib, st)
+
+    def step(self):
+        self.fwd()
+        self.bwd()
+
+
+def make_events(n):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:  # create the underlying hipEvent_t handles
+        e.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def timed(runner, steps: int, warmup: int, trace: bool = True):
+    """Warm up, then time `steps` steps between two events (synchronized on both sides).
+    With trace, every kernel launch of the timed steps is bracketed by its own event pair."""
+    import torch
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    per_call = 16
+    evs = make_events(2 * per_call * 2 * steps) if trace else []
+    handles = (ctypes.c_void_p * max(1, len(evs)))(*[e.cuda_event for e in evs]) if trace else None
+    names = []
+    start, end = make_events(2)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        for j, call in enumerate((runner.fwd, runner.bwd)):
+            if trace:
+                off = (2 * i + j) * 2 * per_call
+                runner.lib.gdr_trace_launches(ctypes.cast(ctypes.byref(handles, off * ctypes.sizeof(ctypes.c_void_p)),
+                                                          ctypes.c_void_p), 2 * per_call)
+            call()
+            if trace:
+                n = runner.lib.gdr_traced_launches()
+                names.append([(off, k, runner.lib.gdr_traced_launch_name(k).decode()) for k in range(n)])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    per_kernel = {}
+    for call in names:
+        for off, k, name in call:
+            t = evs[off + 2 * k].elapsed_time(evs[off + 2 * k + 1])
+            per_kernel.setdefault(name, []).append(t)
+    return ms, per_kernel
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gated_varlen_T32768")
+    ap.add_argument("--sweep", action="store_true", help="also time the T = 4k..32k sweep at B*T = 32768")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): the operator "
+              "has no multi-GPU path here; see the design notes for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS.get(args.workload) or {s.name: s for s in synth.SWEEP}[args.workload]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+    runner = Runner(w, inp)
+    del inp
+    print("[bench] timing", file=sys.stderr, flush=True)
+    ms, per_kernel = timed(runner, args.steps, args.warmup)
+    tokens = w.B * w.T
+    value = tokens / (ms / 1e3)
+    # dominant kernel: largest total time over the timed steps
+    tot = {k: sum(v) for k, v in per_kernel.items()}
+    dom = max(tot, key=tot.get)
+    launches = len(per_kernel[dom])
+    avg_ms = tot[dom] / launches
+    cu = w.cu_seqlens or tuple(range(0, w.B * w.T + 1, w.T))
+    chunks = sum((b - a + 63) // 64 for a, b in zip(cu[:-1], cu[1:]))
+    units = chunks * w.H
+    per_launch_units = units  # each launch of any kernel covers every (chunk, head) unit once
+    kbytes = KERNEL_BYTES_PER_UNIT[dom] * per_launch_units
+    achieved = kbytes / (avg_ms / 1e3) / 1e9
+    traffic = measured_traffic(dom, w.name)
+    path_bytes = PATH_BYTES_PER_HEAD_TOKEN * tokens * w.H
+    path_gbs = path_bytes / (ms / 1e3) / 1e9
+    out = {
+        "metric": "tokens/s chunked gated-delta-rule fwd+bwd, H=16 d=128, T=4k-32k; % of roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; distributions of the workload definition)",
+        "config": {"workload": w.name, "variant": w.variant, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk,
+                   "d_v": w.dv, "chunk": w.chunk, "cu_seqlens": list(w.cu_seqlens) if w.cu_seqlens else None,
+                   "initial_state": w.h0_std > 0},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "avg_launch_ms": round(avg_ms, 4), "launches": launches,
+                     "algorithmic_bytes_per_launch": kbytes},
+        "path_roofline": {"bound": "hbm", "algorithmic_bytes_per_step": path_bytes, "achieved": round(path_gbs, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
+        "kernels_ms_per_step": {k: round(v / args.steps, 4) for k, v in tot.items()},
+    }
+    if args.sweep:
+        sw = {}
+        for s in synth.SWEEP:
+            print(f"[bench] sweep {s.name}", file=sys.stderr, flush=True)
+            r = Runner(s, synth.make_inputs(s))
+            m, _ = timed(r, max(3, args.steps // 2), 2, trace=False)
+            sw[s.name] = {"ms_per_step": round(m, 4), "tokens_per_s": round(s.B * s.T / (m / 1e3), 1)}
+            del r
+            torch.cuda.empty_cache()
+        out["sweep"] = sw
+        names = [s.name for s in synth.SWEEP]
+        out["sweep_ratio_T32k_over_T4k"] = round(sw[names[-1]]["ms_per_step"] / sw[names[0]]["ms_per_step"], 3)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the CPU", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

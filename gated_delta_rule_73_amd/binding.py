@@ -67,6 +67,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
     lib.gdr_last_error.restype = ctypes.c_char_p
+    lib.gdr_trace_launches.argtypes = [_vp, ctypes.c_int]
+    lib.gdr_trace_launches.restype = ctypes.c_int
+    lib.gdr_traced_launches.argtypes = []
+    lib.gdr_traced_launches.restype = ctypes.c_int
+    lib.gdr_traced_launch_name.argtypes = [ctypes.c_int]
+    lib.gdr_traced_launch_name.restype = ctypes.c_char_p
     _LIB = lib
     return lib
 

@@ -24,6 +24,15 @@ namespace gdr {
 // ---------------------------------------------------------------------------------------
 // Reverse scan over the chunks of one (sequence, head, value tile).
 // ---------------------------------------------------------------------------------------
+// Operands of one chunk of the reverse scan, held in registers while they are in flight.
+template <typename E, int D, int BV>
+struct BwdScanOps {
+  RegTile<E, CH, D, 256> q, k, x;
+  RegTile<E, CH, CH, 256> m;
+  RegTile<E, CH, BV, 256> dO;
+  float g;
+};
+
 template <typename E, int D, int BV, int VAR>
 __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ dO, const E* __restrict__ Xg,
@@ -49,6 +58,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
   const SeqPos sp = seq_pos(geo, sq);
   const int w = wave_id();
   const long sbase = ((long)sq * geo.H + h) * D;
+  const int nck = sp.nchunks;
 
   f32x4 S[NJ][NI];  // dW^T tiles
 #pragma unroll
@@ -64,31 +74,54 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
       }
     }
 
-  for (int c = sp.nchunks - 1; c >= 0; --c) {
+  // Chunk c - 2 is loaded while chunk c is computed (two register sets, loop unrolled by two).
+  // Loads before the first chunk repeat it, so every step issues the same memory operations.
+  using Ops = BwdScanOps<E, D, BV>;
+  auto load = [&](Ops& p, int c) {
+    const int cc = max(c, 0);
+    const long u = (long)(sp.gc0 + cc) * geo.H + h;
+    const int n = min(CH, sp.len - cc * CH);
+    const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
+    p.q.load(q + tk * D, D, n);
+    p.k.load(k + tk * D, D, n);
+    p.x.load(Xg + u * CH * D, D, CH);
+    p.m.load(Mg + u * CH * CH, CH, CH);
+    p.dO.load(dO + tk * D + i0, D, n);
+    p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+  };
+  auto step = [&](int c, Ops& p) {
     const long u = (long)(sp.gc0 + c) * geo.H + h;
-    const int n = min(CH, sp.len - c * CH);
-    const long tk = tok_index(geo, sp.b, h, sp.bos + c * CH);
-    g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
-    g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
-    g2s_rows<E, CH, D, NT>(Xs, LD, Xg + u * CH * D, D, CH);
-    g2s_rows<E, CH, CH, NT>(Ms, LDR, Mg + u * CH * CH, CH, CH);
-    if (threadIdx.x < CH) gs[threadIdx.x] = Gg[u * CH + threadIdx.x];
+    p.q.store(Qs, LD);
+    p.k.store(Ks, LD);
+    p.x.store(Xs, LD);
+    p.m.store(Ms, LDR);
+    if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
       for (int it = 0; it < NI; ++it) store4_t(dWs, LD, 16 * (w + 4 * qq), 16 * it, S[qq][it]);
     __syncthreads();
     // dO tile, transposed, twice: plain and with e^{g_t} (rows t >= n are zero)
-    for (int idx = threadIdx.x; idx < CH * BV; idx += NT) {
-      const int t = idx % CH, i = idx / CH;
-      float x = 0.f;
-      if (t < n) x = geo.scale * (float)dO[(tk + t) * D + i0 + i];
-      float e = 1.f;
-      if constexpr (VAR == VAR_GATED) e = expf(gs[t]);
-      dOt[i * LDR + t] = (E)x;
-      dOg[i * LDR + t] = (E)(x * e);
+    {
+      using RT = RegTile<E, CH, BV, NT>;
+#pragma unroll
+      for (int it = 0; it < RT::IT; ++it) {
+        if (RT::TOTAL % NT == 0 || threadIdx.x + it * NT < RT::TOTAL) {
+          const int t = p.dO.row(it), i = p.dO.col(it);
+          const E* e = reinterpret_cast<const E*>(&p.dO.v[it]);
+          float eg = 1.f;
+          if constexpr (VAR == VAR_GATED) eg = __expf(gs[t]);
+#pragma unroll
+          for (int x = 0; x < RT::VE; ++x) {
+            const float val = geo.scale * (float)e[x];
+            dOt[(i + x) * LDR + t] = (E)val;
+            dOg[(i + x) * LDR + t] = (E)(val * eg);
+          }
+        }
+      }
     }
-    s2g_rows<E, BV, D, NT>(dHs + u * D * D + (long)i0 * D, D, dWs, LD, BV);
+    load(p, c - 2);
+    s2g_full<E, BV, D, NT>(dHs + u * D * D + (long)i0 * D, D, dWs, LD);
     __syncthreads();
     const float gn = gs[CH - 1];
 #pragma unroll
@@ -99,7 +132,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float dec = 1.f;
-        if constexpr (VAR == VAR_GATED) dec = expf(gn - gs[acc_row(16 * w, r)]);
+        if constexpr (VAR == VAR_GATED) dec = __expf(gn - gs[acc_row(16 * w, r)]);
         dr[r] = a1[r] + dec * a2[r];
         ndr[r] = -dr[r];
       }
@@ -107,9 +140,9 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
       store4_n(dRn, LDV, 16 * w, 16 * it, dr);
     }
     __syncthreads();
-    s2g_rows<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV, CH);
+    s2g_full<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV);
     float eg = 1.f;
-    if constexpr (VAR == VAR_GATED) eg = expf(gn);
+    if constexpr (VAR == VAR_GATED) eg = __expf(gn);
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
@@ -119,6 +152,15 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
         S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Xs, LD), 16 * (w + 4 * qq), rowk(dRt, LDR), 16 * it);
       }
     __syncthreads();
+  };
+  if (nck > 0) {
+    Ops pa, pb;
+    load(pa, nck - 1);
+    load(pb, nck - 2);
+    for (int c = nck - 1; c >= 0; c -= 2) {
+      step(c, pa);
+      if (c - 1 >= 0) step(c - 1, pb);
+    }
   }
   if (dh0) {
 #pragma unroll
@@ -218,15 +260,30 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   for (int i = 0; i < NQ; ++i) dka[i] = zero4();
   acc3[0] = acc3[1] = zero4();
   float gam = 0.f;
+  RegTile<E, KH, D, NT> pW, pdW;      // one 64-row block of W0 and of dW, next block prefetched
+  RegTile<E, CH, D, NT> pV, pQ;       // V and Q, used in later phases
+  RegTile<E, CH, CH, NT> pM;          // M, used for the decay gradient
   {
     E* dOs = reinterpret_cast<E*>(smem + Ly::odO);
     E* Rs = reinterpret_cast<E*>(smem + Ly::oR);
     E* Wh = reinterpret_cast<E*>(smem + Ly::oWh);
     E* dWh = reinterpret_cast<E*>(smem + Ly::odWh);
-    g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
-    g2s_rows<E, CH, D, NT>(dOs, LD, dO + tk * D, D, n);
-    g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
-    g2s_rows<E, CH, D, NT>(dRs, LD, dRg + u * CH * D, D, CH);
+    {
+      RegTile<E, CH, D, NT> r0, r1, r2, r3;
+      r0.load(k + tk * D, D, n);
+      r1.load(dO + tk * D, D, n);
+      r2.load(Rg + u * CH * D, D, CH);
+      r3.load(dRg + u * CH * D, D, CH);
+      pW.load(Hs + u * D * D, D, KH);
+      pdW.load(dHs + u * D * D, D, KH);
+      pV.load(v + tk * D, D, n);
+      pQ.load(q + tk * D, D, n);
+      pM.load(Mg + u * CH * CH, CH, CH);
+      r0.store(Ks, LD);
+      r1.store(dOs, LD);
+      r2.store(Rs, LD);
+      r3.store(dRs, LD);
+    }
     if (threadIdx.x < CH) {
       const int t = threadIdx.x;
       gs[t] = Gg[u * CH + t];
@@ -234,8 +291,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
     for (int ih = 0; ih < NH; ++ih) {
       __syncthreads();
-      g2s_rows_t<E, KH, D, NT>(Wh, LDR, Hs + u * D * D + (long)ih * KH * D, D, KH);
-      g2s_rows_t<E, KH, D, NT>(dWh, LDR, dHs + u * D * D + (long)ih * KH * D, D, KH);
+      pW.store_t(Wh, LDR);
+      pdW.store_t(dWh, LDR);
+      if (ih + 1 < NH) {
+        pW.load(Hs + u * D * D + (long)(ih + 1) * KH * D, D, KH);
+        pdW.load(dHs + u * D * D + (long)(ih + 1) * KH * D, D, KH);
+      }
       __syncthreads();
       const E* Aop = (w < 4 ? dOs : dRs) + ih * KH;
 #pragma unroll
@@ -309,7 +370,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   float* dTs = reinterpret_cast<float*>(smem + Ly::odT);
   float* Li = reinterpret_cast<float*>(smem + Ly::oLi);
   E* Vs = reinterpret_cast<E*>(smem + Ly::oVP);
-  g2s_rows<E, CH, D, NT>(Vs, LD, v + tk * D, D, n);
+  pV.store(Vs, LD);
   for (int job = w; job < 10; job += 8) {
     int mt, nt;
     tri_tile(job, mt, nt);
@@ -371,10 +432,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   __syncthreads();
 #pragma unroll
   for (int qq = 0; qq < NQ; ++qq) store4_n(Vs, LD, 16 * wm, 16 * (wn * NQ + qq), dva[qq]);
-  if (threadIdx.x < CH) {  // dbeta from T = Linv diag(beta)
+  if (threadIdx.x < CH) {  // dbeta from T = Linv diag(beta) (dT and Linv are zero above the diagonal)
     const int s = threadIdx.x;
     float a = 0.f;
-    for (int t = s; t < CH; ++t) a += dTs[t * LF + s] * Li[t * LF + s];
+#pragma unroll 16
+    for (int t = 0; t < CH; ++t) a += dTs[t * LF + s] * Li[t * LF + s];
     dbs[s] = a;
   }
   __syncthreads();
@@ -407,10 +469,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     store4_n(dTs, LF, 16 * (id >> 2), 16 * (id & 3), dl[e]);  // dTs now holds dL
   }
   __syncthreads();
-  if (threadIdx.x < CH) {  // dbeta from L = I + diag(beta) A
+  if (threadIdx.x < CH) {  // dbeta from L = I + diag(beta) A (dL is zero on and above the diagonal)
     const int t = threadIdx.x;
     float a = 0.f;
-    for (int s = 0; s < t; ++s) a += dTs[t * LF + s] * As[t * LF + s];
+#pragma unroll 16
+    for (int s = 0; s < CH; ++s) a += dTs[t * LF + s] * As[t * LF + s];
     dbs[t] += a;
   }
 
@@ -419,19 +482,30 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   E* Ats = reinterpret_cast<E*>(smem + Ly::oAt);
   E* Mts = reinterpret_cast<E*>(smem + Ly::oMt);
   float* Pair = reinterpret_cast<float*>(smem + Ly::oPair);
-  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
-  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-    const int t = idx >> 6, s = idx & 63;
-    float dec = 0.f;
-    if (s <= t) {
-      dec = 1.f;
-      if constexpr (GATED) dec = expf(gs[t] - gs[s]);
+  pQ.store(Qs, LD);
+  // Each thread handles the (t, s) entries of M it holds in registers.
+  {
+    using RM = RegTile<E, CH, CH, NT>;
+#pragma unroll
+    for (int it = 0; it < RM::IT; ++it) {
+      if (RM::TOTAL % NT == 0 || threadIdx.x + it * NT < RM::TOTAL) {
+        const int t = pM.row(it), s0 = pM.col(it);
+#pragma unroll
+        for (int e = 0; e < RM::VE; ++e) {
+          const int s = s0 + e;
+          float dec = 0.f;
+          if (s <= t) {
+            dec = 1.f;
+            if constexpr (GATED) dec = __expf(gs[t] - gs[s]);
+          }
+          const float dA = (s < t) ? bs[t] * dTs[t * LF + s] : 0.f;
+          const float dM = (s <= t) ? (float)dMs[t * LDR + s] : 0.f;
+          Ats[t * LDR + s] = (E)(dA * dec);
+          Mts[t * LDR + s] = (E)(dM * dec);
+          if constexpr (GATED) Pair[t * LF + s] = (s < t) ? dA * As[t * LF + s] + dM * (float)pM.elem(it, e) : 0.f;
+        }
+      }
     }
-    const float dA = (s < t) ? bs[t] * dTs[t * LF + s] : 0.f;
-    const float dM = (s <= t) ? (float)dMs[t * LDR + s] : 0.f;
-    Ats[t * LDR + s] = (E)(dA * dec);
-    Mts[t * LDR + s] = (E)(dM * dec);
-    if constexpr (GATED) Pair[t * LF + s] = (s < t) ? dA * As[t * LF + s] + dM * (float)Mg[(u * CH + t) * CH + s] : 0.f;
   }
   __syncthreads();
   if (w < 4) {
@@ -459,7 +533,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     if (threadIdx.x < CH) {  // prefix sums along each row of the pair terms
       const int uu = threadIdx.x;
       float run = 0.f;
-      for (int s = 0; s < uu; ++s) {
+#pragma unroll 16
+      for (int s = 0; s < CH; ++s) {  // entries with s >= uu are zero
         run += Pair[uu * LF + s];
         Pair[uu * LF + s] = run;
       }
@@ -479,8 +554,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     const int t = threadIdx.x;
     if constexpr (GATED) {
       float rect = 0.f;  // sum over u >= t of sum_{s < t} pair(u, s)
-      if (t > 0)
-        for (int uu = t; uu < CH; ++uu) rect += Pair[uu * LF + t - 1];
+      if (t > 0) {
+#pragma unroll 16
+        for (int uu = 0; uu < CH; ++uu) rect += (uu >= t) ? Pair[uu * LF + t - 1] : 0.f;
+      }
       // suffix over u >= t of the rows' Qhat.dQhat + Khat.dKhat (reversed inclusive scan)
       const int tr = CH - 1 - t;
       const float xr = rq[tr >> 4][tr] + rkh[tr >> 4][tr] + rkh[(tr >> 4) + 4][tr];
@@ -512,20 +589,29 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
                            const gdr_grads& gr, hipStream_t st) {
   const Geo& g = p.geo;
   if (p.bv == 16) {
-    hipLaunchKernelGGL((k_bwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
-                       (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
-                       (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0);
+    {
+      TraceScope ts_("bwd_scan", st);
+      hipLaunchKernelGGL((k_bwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
+                         (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
+                         (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0);
+    }
   } else {
-    hipLaunchKernelGGL((k_bwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
-                       (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
-                       (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0);
+    {
+      TraceScope ts_("bwd_scan", st);
+      hipLaunchKernelGGL((k_bwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
+                         (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
+                         (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0);
+    }
   }
   if (g.total_chunks > 0) {
-    hipLaunchKernelGGL((k_bwd_chunk<E, D, VAR>), dim3(g.total_chunks, g.H), dim3(512), 0, st, g,
-                       (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
-                       (const E*)dO, (const E*)p.M, (const float*)p.G, (const E*)p.Hs, (const E*)p.R,
-                       (const E*)p.dHs, (const E*)p.dR, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta,
-                       (E*)gr.dalpha);
+    {
+      TraceScope ts_("bwd_chunk", st);
+      hipLaunchKernelGGL((k_bwd_chunk<E, D, VAR>), dim3(g.total_chunks, g.H), dim3(512), 0, st, g,
+                         (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
+                         (const E*)dO, (const E*)p.M, (const float*)p.G, (const E*)p.Hs, (const E*)p.R,
+                         (const E*)p.dHs, (const E*)p.dR, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta,
+                         (E*)gr.dalpha);
+    }
   }
   return hipGetLastError();
 }

@@ -78,6 +78,20 @@ __device__ __forceinline__ typename MMA<E>::frag frag(const View<S, KC>& v, int 
     r[0] = (bf16)lo.x; r[1] = (bf16)lo.y; r[2] = (bf16)lo.z; r[3] = (bf16)lo.w;
     r[4] = (bf16)hi.x; r[5] = (bf16)hi.y; r[6] = (bf16)hi.z; r[7] = (bf16)hi.w;
     return r;
+  } else if constexpr (!KC && std::is_same<S, E>::value) {
+    // k-major bf16 data in LDS: two transposing 64-bit reads.  Within each group of 16
+    // lanes, lane s addresses row k0 + 8*lgrp + s/4 (+4 for the second read), columns
+    // idx0 + 4*(s%4) .. +3, and lane i receives that group's column idx0 + i for the four
+    // rows -- exactly this lane's k-slice of the fragment.
+    const int s = lrow();
+    const S* base = v.p + (k0 + 8 * lgrp() + (s >> 2)) * v.ld + idx0 + 4 * (s & 3);
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * v.ld));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 r = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, r);
   } else {
     bf16x8 r;
 #pragma unroll
@@ -124,31 +138,108 @@ __device__ __forceinline__ void store4_n(S* dst, int ld, int m0, int n0, f32x4 v
 // ---------------------------------------------------------------------------------------
 // Tile staging between global memory and LDS (16-byte vectors, whole block cooperates).
 // ---------------------------------------------------------------------------------------
+template <int B> struct VecT;
+template <> struct VecT<16> { typedef uint4 type; };
+template <> struct VecT<8> { typedef uint2 type; };
+template <> struct VecT<4> { typedef uint32_t type; };
+template <int B> __device__ __forceinline__ typename VecT<B>::type vzero();
+template <> __device__ __forceinline__ uint4 vzero<16>() { return make_uint4(0u, 0u, 0u, 0u); }
+template <> __device__ __forceinline__ uint2 vzero<8>() { return make_uint2(0u, 0u); }
+template <> __device__ __forceinline__ uint32_t vzero<4>() { return 0u; }
+
+// Vector width (bytes) that spreads a tile of `bytes` over NT threads, 4..16.
+constexpr int tile_vec_bytes(int bytes, int nt) {
+  return bytes / nt >= 16 ? 16 : bytes / nt >= 8 ? 8 : 4;
+}
+
+// Register stage of a ROWS x COLS tile: each thread holds its share of vectors, so every
+// global load of the tile is in flight before any of them is waited for.
+template <typename S, int ROWS, int COLS, int NT>
+struct RegTile {
+  static constexpr int VB = tile_vec_bytes(ROWS * COLS * (int)sizeof(S), NT);
+  static constexpr int VE = VB / (int)sizeof(S);
+  static constexpr int VPR = COLS / VE;
+  static constexpr int TOTAL = ROWS * VPR;
+  static constexpr int IT = (TOTAL + NT - 1) / NT;
+  typedef typename VecT<VB>::type V;
+  static_assert(COLS % VE == 0, "row length must be a multiple of the vector width");
+  V v[IT];
+  // v <- G[r*gs + c] for r < nrows (zero below); needs nrows >= 1.  The loads are issued
+  // unconditionally (rows past nrows re-read row nrows-1 and are then zeroed), so the
+  // number of outstanding memory operations does not depend on the data.
+  __device__ __forceinline__ void load(const S* g, long gs, int nrows) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = threadIdx.x + it * NT;
+      const int r = idx / VPR, c = (idx % VPR) * VE;
+      if (TOTAL % NT == 0 || idx < TOTAL) {
+        const V x = *reinterpret_cast<const V*>(g + (long)min(r, nrows - 1) * gs + c);
+        v[it] = (r < nrows) ? x : vzero<VB>();
+      } else {
+        v[it] = vzero<VB>();
+      }
+    }
+  }
+  // LDS[r*ld + c] <- v
+  __device__ __forceinline__ void store(S* lds, int ld) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = threadIdx.x + it * NT;
+      if (TOTAL % NT == 0 || idx < TOTAL) {
+        const int r = idx / VPR, c = (idx % VPR) * VE;
+        *reinterpret_cast<V*>(lds + r * ld + c) = v[it];
+      }
+    }
+  }
+  // LDS[c*ld + r] <- v (transposed), element by element
+  __device__ __forceinline__ void store_t(S* lds, int ld) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = threadIdx.x + it * NT;
+      if (TOTAL % NT == 0 || idx < TOTAL) {
+        const int r = idx / VPR, c = (idx % VPR) * VE;
+        const S* e = reinterpret_cast<const S*>(&v[it]);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) lds[(c + i) * ld + r] = e[i];
+      }
+    }
+  }
+  __device__ __forceinline__ S elem(int it, int i) const { return reinterpret_cast<const S*>(&v[it])[i]; }
+  __device__ __forceinline__ int row(int it) const { return (threadIdx.x + it * NT) / VPR; }
+  __device__ __forceinline__ int col(int it) const { return ((threadIdx.x + it * NT) % VPR) * VE; }
+};
+
 // LDS[r*ld + c] = G[r*gs + c] for r < nrows, 0 for nrows <= r < ROWS; c < COLS.
 template <typename S, int ROWS, int COLS, int NT>
 __device__ __forceinline__ void g2s_rows(S* lds, int ld, const S* g, long gs, int nrows) {
-  constexpr int VE = 16 / (int)sizeof(S);
-  constexpr int VPR = COLS / VE;
-  static_assert(COLS % VE == 0, "row length must be a multiple of 16 bytes");
-  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
-    const int r = idx / VPR, c = (idx % VPR) * VE;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (r < nrows) val = *reinterpret_cast<const uint4*>(g + (long)r * gs + c);
-    *reinterpret_cast<uint4*>(lds + r * ld + c) = val;
-  }
+  RegTile<S, ROWS, COLS, NT> t;
+  t.load(g, gs, nrows);
+  t.store(lds, ld);
 }
-// Transposed staging: LDS[c*ld + r] = G[r*gs + c] (zero for r >= nrows), r < ROWS, c < COLS.
+// Transposed staging: LDS[c*ld + r] = mul * G[r*gs + c] (zero for r >= nrows), r < ROWS, c < COLS.
 template <typename S, int ROWS, int COLS, int NT>
 __device__ __forceinline__ void g2s_rows_t(S* lds, int ld, const S* g, long gs, int nrows, float mul = 1.f) {
   constexpr int VE = 16 / (int)sizeof(S);
   constexpr int VPR = COLS / VE;
-  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
-    const int r = idx % ROWS, c = (idx / ROWS) * VE;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (r < nrows) val = *reinterpret_cast<const uint4*>(g + (long)r * gs + c);
-    const S* e = reinterpret_cast<const S*>(&val);
+  constexpr int TOTAL = ROWS * VPR;
+  constexpr int IT = (TOTAL + NT - 1) / NT;
+  uint4 v[IT];
 #pragma unroll
-    for (int i = 0; i < VE; ++i) lds[(c + i) * ld + r] = (S)((float)e[i] * mul);
+  for (int it = 0; it < IT; ++it) {
+    const int idx = threadIdx.x + it * NT;
+    const int r = idx % ROWS, c = (idx / ROWS) * VE;
+    v[it] = make_uint4(0u, 0u, 0u, 0u);
+    if ((TOTAL % NT == 0 || idx < TOTAL) && r < nrows) v[it] = *reinterpret_cast<const uint4*>(g + (long)r * gs + c);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = threadIdx.x + it * NT;
+    if (TOTAL % NT == 0 || idx < TOTAL) {
+      const int r = idx % ROWS, c = (idx / ROWS) * VE;
+      const S* e = reinterpret_cast<const S*>(&v[it]);
+#pragma unroll
+      for (int i = 0; i < VE; ++i) lds[(c + i) * ld + r] = (S)((float)e[i] * mul);
+    }
   }
 }
 // G[r*gs + c] = LDS[r*ld + c] for r < nrows, c < COLS.
@@ -156,9 +247,31 @@ template <typename S, int ROWS, int COLS, int NT>
 __device__ __forceinline__ void s2g_rows(S* g, long gs, const S* lds, int ld, int nrows) {
   constexpr int VE = 16 / (int)sizeof(S);
   constexpr int VPR = COLS / VE;
-  for (int idx = threadIdx.x; idx < ROWS * VPR; idx += NT) {
+  constexpr int TOTAL = ROWS * VPR;
+  constexpr int IT = (TOTAL + NT - 1) / NT;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = threadIdx.x + it * NT;
     const int r = idx / VPR, c = (idx % VPR) * VE;
-    if (r < nrows) *reinterpret_cast<uint4*>(g + (long)r * gs + c) = *reinterpret_cast<const uint4*>(lds + r * ld + c);
+    if ((TOTAL % NT == 0 || idx < TOTAL) && r < nrows)
+      *reinterpret_cast<uint4*>(g + (long)r * gs + c) = *reinterpret_cast<const uint4*>(lds + r * ld + c);
+  }
+}
+// The same for a tile whose every row is written: no predicate on the stores, so the count
+// of outstanding memory operations stays the same on every path.
+template <typename S, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void s2g_full(S* g, long gs, const S* lds, int ld) {
+  constexpr int VB = tile_vec_bytes(ROWS * COLS * (int)sizeof(S), NT);
+  constexpr int VE = VB / (int)sizeof(S);
+  constexpr int VPR = COLS / VE;
+  constexpr int TOTAL = ROWS * VPR;
+  typedef typename VecT<VB>::type V;
+  static_assert(TOTAL % NT == 0, "tile must split evenly over the block");
+#pragma unroll
+  for (int it = 0; it < TOTAL / NT; ++it) {
+    const int idx = threadIdx.x + it * NT;
+    const int r = idx / VPR, c = (idx % VPR) * VE;
+    *reinterpret_cast<V*>(g + (long)r * gs + c) = *reinterpret_cast<const V*>(lds + r * ld + c);
   }
 }
 

@@ -25,13 +25,12 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
                                                   const E* __restrict__ alpha, E* __restrict__ Xo,
                                                   E* __restrict__ Uo, E* __restrict__ Mo, float* __restrict__ Go) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 1;
-  __shared__ __align__(16) E Ks[CH * LD];
-  __shared__ __align__(16) E Qs[CH * LD];  // Q, later e^g * K
-  __shared__ __align__(16) E Vs[CH * LD];
-  __shared__ __align__(16) E Ts[CH * LDT];
+  static_assert(CH * LDT * (int)sizeof(E) >= 4 * 256 * 4, "T buffer doubles as the solve's scratch");
+  __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g * K, then X
+  __shared__ __align__(16) E QV[CH * LD];   // Q, then V, then U
+  __shared__ __align__(16) E Ts[CH * LDT];  // solve scratch, then T = Linv diag(beta)
   __shared__ __align__(16) float Ls[CH * LF];
   __shared__ __align__(16) float Li[CH * LF];
-  __shared__ __align__(16) float scr[4 * 256];
   __shared__ float gs[CH], bs[CH];
 
   const int gc = blockIdx.x, h = blockIdx.y;
@@ -40,9 +39,12 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id();
 
-  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, cp.n);
-  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, cp.n);
-  g2s_rows<E, CH, D, NT>(Vs, LD, v + tk * D, D, cp.n);
+  RegTile<E, CH, D, NT> rk, rq, rv;
+  rk.load(k + tk * D, D, cp.n);
+  rq.load(q + tk * D, D, cp.n);
+  rv.load(v + tk * D, D, cp.n);
+  rk.store(Ks, LD);
+  rq.store(QV, LD);
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
     const bool ok = t < cp.n;
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
     const bool isM = job >= 10;
     int mt, nt;
     tri_tile(isM ? job - 10 : job, mt, nt);
-    const f32x4 acc = mma_k<E, D>(zero4(), rowk(isM ? Qs : Ks, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
+    const f32x4 acc = mma_k<E, D>(zero4(), rowk(isM ? QV : Ks, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
       float val = 0.f;
       if (keep) {
         float dec = 1.f;
-        if constexpr (VAR == VAR_GATED) dec = expf(gs[t] - gs[s]);
+        if constexpr (VAR == VAR_GATED) dec = __expf(gs[t] - gs[s]);
         val = acc[r] * dec;
       }
       if (isM) Mo[(u * CH + t) * CH + s] = (E)val;
@@ -80,35 +82,36 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
     if ((s >> 4) > (t >> 4)) Mo[(u * CH + t) * CH + s] = (E)0.f;
   }
   __syncthreads();
-  solve_unit_lower64<NT>(Ls, LF, Li, LF, scr);
+  rv.store(QV, LD);
+  solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ts));
 
   for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
     const int t = idx >> 6, s = idx & 63;
     Ts[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] * bs[s] : 0.f);
   }
-  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
-    const int t = idx / D, j = idx % D;
-    float e = 1.f;
-    if constexpr (VAR == VAR_GATED) e = expf(gs[t]);
-    Qs[t * LD + j] = (E)(e * (float)Ks[t * LD + j]);
+  if constexpr (VAR == VAR_GATED) {
+    for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
+      const int t = idx / D, j = idx % D;
+      Ks[t * LD + j] = (E)(__expf(gs[t]) * (float)Ks[t * LD + j]);
+    }
   }
   __syncthreads();
 
   f32x4 xa[D / 16], ua[D / 16];
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
-    xa[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Qs, LD), 16 * nt);
-    ua[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Vs, LD), 16 * nt);
+    xa[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Ks, LD), 16 * nt);
+    ua[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(QV, LD), 16 * nt);
   }
   __syncthreads();
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
     store4_n(Ks, LD, 16 * w, 16 * nt, xa[nt]);
-    store4_n(Vs, LD, 16 * w, 16 * nt, ua[nt]);
+    store4_n(QV, LD, 16 * w, 16 * nt, ua[nt]);
   }
   __syncthreads();
-  s2g_rows<E, CH, D, NT>(Xo + u * CH * D, D, Ks, LD, CH);
-  s2g_rows<E, CH, D, NT>(Uo + u * CH * D, D, Vs, LD, CH);
+  s2g_full<E, CH, D, NT>(Xo + u * CH * D, D, Ks, LD);
+  s2g_full<E, CH, D, NT>(Uo + u * CH * D, D, QV, LD);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -116,6 +119,14 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
 // The tile of W (BV rows x D) lives in accumulators as W^T tiles: wave w owns key tiles
 // jt = w + 4q and every value sub-tile.
 // ---------------------------------------------------------------------------------------
+// Operands of one chunk of the forward scan, held in registers while they are in flight.
+template <typename E, int D, int BV>
+struct FwdScanOps {
+  RegTile<E, CH, D, 256> x, k;
+  RegTile<E, CH, BV, 256> u;
+  float g;
+};
+
 template <typename E, int D, int BV, int VAR>
 __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__ k, const E* __restrict__ Xg,
                                                   const E* __restrict__ Ug, const float* __restrict__ Gg,
@@ -137,6 +148,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
   const SeqPos sp = seq_pos(geo, sq);
   const int w = wave_id();
   const long sbase = ((long)sq * geo.H + h) * D;  // row base of this memory in [N,H,D,D]
+  const int nck = sp.nchunks;
 
   f32x4 S[NJ][NI];
 #pragma unroll
@@ -152,20 +164,31 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
       }
     }
 
-  for (int c = 0; c < sp.nchunks; ++c) {
+  // Chunk c + 2 is loaded while chunk c is computed (two register sets, loop unrolled by two).
+  // Loads past the last chunk repeat it, so every step issues the same memory operations.
+  using Ops = FwdScanOps<E, D, BV>;
+  auto load = [&](Ops& p, int c) {
+    const int cc = min(c, nck - 1);
+    const long u = (long)(sp.gc0 + cc) * geo.H + h;
+    const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
+    p.x.load(Xg + u * CH * D, D, CH);
+    p.k.load(k + tk * D, D, min(CH, sp.len - cc * CH));
+    p.u.load(Ug + u * CH * D + i0, D, CH);
+    p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+  };
+  auto step = [&](int c, Ops& p) {
     const long u = (long)(sp.gc0 + c) * geo.H + h;
-    const int n = min(CH, sp.len - c * CH);
-    const long tk = tok_index(geo, sp.b, h, sp.bos + c * CH);
-    g2s_rows<E, CH, D, NT>(Xs, LD, Xg + u * CH * D, D, CH);
-    g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
-    g2s_rows<E, CH, BV, NT>(Us, LDV, Ug + u * CH * D + i0, D, CH);
-    if (threadIdx.x < CH) gs[threadIdx.x] = Gg[u * CH + threadIdx.x];
+    p.x.store(Xs, LD);
+    p.k.store(Ks, LD);
+    p.u.store(Us, LDV);
+    if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
       for (int it = 0; it < NI; ++it) store4_t(Ws, LD, 16 * (w + 4 * qq), 16 * it, S[qq][it]);
     __syncthreads();
-    s2g_rows<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD, BV);
+    load(p, c + 2);
+    s2g_full<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD);
     const float gn = gs[CH - 1];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
@@ -177,16 +200,16 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
         const float val = (float)Us[t * LDV + i] - acc[r];
         rv[r] = val;
         float dec = 1.f;
-        if constexpr (VAR == VAR_GATED) dec = expf(gn - gs[t]);
+        if constexpr (VAR == VAR_GATED) dec = __expf(gn - gs[t]);
         rd[r] = val * dec;
       }
       store4_n(Rn, LDV, 16 * w, 16 * it, rv);
       store4_t(Rd, LDR, 16 * w, 16 * it, rd);
     }
     __syncthreads();
-    s2g_rows<E, CH, BV, NT>(Rg + u * CH * D + i0, D, Rn, LDV, CH);
+    s2g_full<E, CH, BV, NT>(Rg + u * CH * D + i0, D, Rn, LDV);
     float eg = 1.f;
-    if constexpr (VAR == VAR_GATED) eg = expf(gn);
+    if constexpr (VAR == VAR_GATED) eg = __expf(gn);
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
@@ -195,6 +218,15 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
         S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Ks, LD), 16 * (w + 4 * qq), rowk(Rd, LDR), 16 * it);
       }
     __syncthreads();
+  };
+  if (nck > 0) {
+    Ops pa, pb;
+    load(pa, 0);
+    load(pb, 1);
+    for (int c = 0; c < nck; c += 2) {
+      step(c, pa);
+      if (c + 1 < nck) step(c + 1, pb);
+    }
   }
   if (ht) {
 #pragma unroll
@@ -259,21 +291,33 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, float* 
   const Geo& g = p.geo;
   const dim3 cgrid(g.total_chunks, g.H);
   if (g.total_chunks > 0) {
-    hipLaunchKernelGGL((k_fwd_prep<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k,
-                       (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G);
+    {
+      TraceScope ts_("fwd_prep", st);
+      hipLaunchKernelGGL((k_fwd_prep<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k,
+                         (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G);
+    }
   }
   if (p.bv == 16) {
-    hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
-                       (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
-                       (E*)p.R, ht);
+    {
+      TraceScope ts_("fwd_scan", st);
+      hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
+                         (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
+                         (E*)p.R, ht);
+    }
   } else {
-    hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
-                       (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
-                       (E*)p.R, ht);
+    {
+      TraceScope ts_("fwd_scan", st);
+      hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
+                         (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
+                         (E*)p.R, ht);
+    }
   }
   if (want_out && g.total_chunks > 0) {
-    hipLaunchKernelGGL((k_fwd_out<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)p.M,
-                       (const E*)p.R, (const float*)p.G, (const E*)p.Hs, (E*)o);
+    {
+      TraceScope ts_("fwd_out", st);
+      hipLaunchKernelGGL((k_fwd_out<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)p.M,
+                         (const E*)p.R, (const float*)p.G, (const E*)p.Hs, (E*)o);
+    }
   }
   return hipGetLastError();
 }

@@ -159,7 +159,23 @@ gdr_status hip_status(hipError_t e, const char* what) {
   return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Arms/disarms the per-launch trace around one public call.
+struct TraceCall {
+  TraceCall() {
+    gdr::LaunchTrace& t = gdr::launch_trace();
+    if (t.armed) t.n = 0;
+  }
+  ~TraceCall() { gdr::launch_trace().armed = false; }
+};
+
 }  // namespace
+
+namespace gdr {
+LaunchTrace& launch_trace() {
+  static thread_local LaunchTrace t;
+  return t;
+}
+}  // namespace gdr
 
 extern "C" {
 
@@ -194,6 +210,7 @@ gdr_status gdr_forward(const gdr_problem* p, const gdr_inputs* in, void* o, floa
   char* cache = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + s.Ub;
   gdr::Plan pl = make_plan(p, s, cache, static_cast<char*>(ws));
   g_last_error.clear();
+  TraceCall tc;
   return hip_status(gdr::run_forward(pl, *in, o, ht, true, static_cast<hipStream_t>(stream)), "gdr_forward launch");
 }
 
@@ -224,6 +241,7 @@ gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* 
   gdr::Plan pl = make_plan(p, s, cache, base);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   g_last_error.clear();
+  TraceCall tc;
   if (!saved) {
     st = hip_status(gdr::run_forward(pl, *in, nullptr, nullptr, false, hs), "gdr_backward recompute launch");
     if (st != GDR_OK) return st;
@@ -243,5 +261,23 @@ const char* gdr_status_string(gdr_status s) {
 }
 
 const char* gdr_last_error(void) { return g_last_error.c_str(); }
+
+gdr_status gdr_trace_launches(void** events, int capacity) {
+  if (!events || capacity < 2) return fail(GDR_ERR_INVALID_ARG, "trace needs events and capacity >= 2");
+  gdr::LaunchTrace& t = gdr::launch_trace();
+  t.ev = events;
+  t.cap = capacity;
+  t.n = 0;
+  t.armed = true;
+  return GDR_OK;
+}
+
+int gdr_traced_launches(void) { return gdr::launch_trace().n; }
+
+const char* gdr_traced_launch_name(int i) {
+  const gdr::LaunchTrace& t = gdr::launch_trace();
+  if (i < 0 || i >= t.n || i >= 64 || !t.names[i]) return "";
+  return t.names[i];
+}
 
 }  // extern "C"

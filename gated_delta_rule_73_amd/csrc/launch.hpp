@@ -25,6 +25,34 @@ struct Plan {
   void* dR;   // [units][64][D]  gradient w.r.t. R
 };
 
+// Optional per-launch event recording (see gdr_trace_launches in gdr.h).
+struct LaunchTrace {
+  void** ev = nullptr;
+  int cap = 0;      // events available (pairs = cap / 2)
+  int n = 0;        // launches seen in the traced call
+  bool armed = false;
+  const char* names[64] = {};
+};
+LaunchTrace& launch_trace();
+
+// Records the "before" event on construction and the "after" event on destruction.
+struct TraceScope {
+  hipStream_t st;
+  int idx = -1;
+  TraceScope(const char* name, hipStream_t s) : st(s) {
+    LaunchTrace& t = launch_trace();
+    if (!t.armed) return;
+    idx = t.n++;
+    if (idx < 64) t.names[idx] = name;
+    if (2 * idx + 1 < t.cap) (void)hipEventRecord(static_cast<hipEvent_t>(t.ev[2 * idx]), st);
+    else idx = -1;
+  }
+  ~TraceScope() {
+    if (idx < 0) return;
+    (void)hipEventRecord(static_cast<hipEvent_t>(launch_trace().ev[2 * idx + 1]), st);
+  }
+};
+
 hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st);
 hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht, const gdr_grads& gr,
                         hipStream_t st);

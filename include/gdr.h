@@ -95,13 +95,15 @@ typedef struct {           /* same shape and dtype as the matching input */
  * saved buffer the same size is accepted.  Errors: INVALID_ARG, UNSUPPORTED. */
 gdr_status gdr_workspace_size(const gdr_problem *p, int backward, size_t *bytes);
 
-/* Bytes of the optional forward->backward buffer: the memory at the start of every chunk,
- * in the I/O dtype.  Errors: INVALID_ARG, UNSUPPORTED. */
+/* Bytes of the optional forward->backward buffer: the forward's per-chunk WY factor X, the
+ * decayed causal Gram M, the in-chunk cumulative log decay, the memory at the start of every
+ * chunk and the scaled residuals R (all in the I/O dtype except the log decay, float32).
+ * Errors: INVALID_ARG, UNSUPPORTED. */
 gdr_status gdr_saved_size(const gdr_problem *p, size_t *bytes);
 
 /* Forward.  o: [B,H,T,dv] I/O dtype (required).  ht: [N,H,dv,dk] float32 final memory,
- * or NULL.  saved: gdr_saved_size() bytes or NULL; when given, the chunk-start memories
- * are written there for a later gdr_backward.  ws: gdr_workspace_size(p, 0) bytes. */
+ * or NULL.  saved: gdr_saved_size() bytes or NULL; when given, the per-chunk results the
+ * backward needs are written there for a later gdr_backward.  ws: gdr_workspace_size(p, 0) bytes. */
 gdr_status gdr_forward(const gdr_problem *p, const gdr_inputs *in, void *o, float *ht,
                        void *saved, void *ws, size_t ws_bytes, void *stream);
 
@@ -114,6 +116,17 @@ gdr_status gdr_backward(const gdr_problem *p, const gdr_inputs *in, const void *
                         size_t ws_bytes, void *stream);
 
 const char *gdr_status_string(gdr_status s);
+
+/* Per-launch timing, for profiling tools.  After gdr_trace_launches(events, capacity), the
+ * next gdr_forward or gdr_backward call made by the same thread records events[2i] on its
+ * stream just before its i-th kernel launch and events[2i+1] just after it (i < capacity/2),
+ * then tracing switches itself off.  events: hipEvent_t handles created by the caller.
+ * gdr_traced_launches() gives the number of launches that call made (also those beyond the
+ * capacity) and gdr_traced_launch_name(i) the kernel of launch i ("" when out of range).
+ * Errors: INVALID_ARG when events is NULL or capacity < 2. */
+gdr_status gdr_trace_launches(void **events, int capacity);
+int gdr_traced_launches(void);
+const char *gdr_traced_launch_name(int i);
 
 /* Thread-local description of the last non-OK return of this thread ("" if none). */
 const char *gdr_last_error(void);

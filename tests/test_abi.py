@@ -23,9 +23,10 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     header = open(os.path.join(ROOT, "include", "gdr.h")).read()
-    names = set(re.findall(r"^\s*(?:gdr_status|const char \*)\s*(gdr_\w+)\s*\(", header, re.M))
+    names = set(re.findall(r"^\s*(?:gdr_status|const char \*|int)\s*(gdr_\w+)\s*\(", header, re.M))
     assert names >= {"gdr_workspace_size", "gdr_saved_size", "gdr_forward", "gdr_backward",
-                     "gdr_status_string", "gdr_last_error"}
+                     "gdr_status_string", "gdr_last_error", "gdr_trace_launches", "gdr_traced_launches",
+                     "gdr_traced_launch_name"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -173,3 +174,10 @@ def test_status_strings(lib):
                                  "GDR_ERR_HIP"]):
         assert lib.gdr_status_string(code).decode() == name
     assert lib.gdr_status_string(99).decode() == "GDR_UNKNOWN_STATUS"
+
+
+def test_trace_argument_checks(lib):
+    lib.gdr_trace_launches.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert lib.gdr_trace_launches(None, 8) == bd.GDR_ERR_INVALID_ARG
+    ev = (ctypes.c_void_p * 2)()
+    assert lib.gdr_trace_launches(ev, 1) == bd.GDR_ERR_INVALID_ARG
