@@ -25,12 +25,20 @@ namespace gdr {
 // Reverse scan over the chunks of one (sequence, head, value tile).
 // ---------------------------------------------------------------------------------------
 // Operands of one chunk of the reverse scan, held in registers while they are in flight.
-template <typename E, int D, int BV>
+// Gated DeltaNet-2 also needs the erase gates and beta (for a = beta e*k).
+template <typename E, int D, int BV, bool G2>
 struct BwdScanOps {
   RegTile<E, CH, D, 256> q, k, x;
   RegTile<E, CH, CH, 256> m;
   RegTile<E, CH, BV, 256> dO;
   float g;
+};
+template <typename E, int D, int BV>
+struct BwdScanOps<E, D, BV, true> {
+  RegTile<E, CH, D, 256> q, k, x, e;
+  RegTile<E, CH, CH, 256> m;
+  RegTile<E, CH, BV, 256> dO;
+  float g, b;
 };
 
 template <typename E, int D, int BV, int VAR>
@@ -38,9 +46,14 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
                                                   const E* __restrict__ dO, const E* __restrict__ Xg,
                                                   const E* __restrict__ Mg, const float* __restrict__ Gg,
                                                   const float* __restrict__ dht, E* __restrict__ dHs,
-                                                  E* __restrict__ dRg, float* __restrict__ dh0) {
+                                                  E* __restrict__ dRg, float* __restrict__ dh0,
+                                                  const E* __restrict__ beta, const E* __restrict__ erase) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
+  constexpr bool G2 = VAR == VAR_GDN2;
+  constexpr bool DEC = VAR != VAR_DELTANET;
+  __shared__ __align__(16) E As[G2 ? CH * LD : 8];  // a = beta e*k (GDN-2)
+  __shared__ float bsh[CH];
   __shared__ __align__(16) E Qs[CH * LD];
   __shared__ __align__(16) E Ks[CH * LD];
   __shared__ __align__(16) E Xs[CH * LD];
@@ -76,7 +89,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
 
   // Chunk c - 2 is loaded while chunk c is computed (two register sets, loop unrolled by two).
   // Loads before the first chunk repeat it, so every step issues the same memory operations.
-  using Ops = BwdScanOps<E, D, BV>;
+  using Ops = BwdScanOps<E, D, BV, G2>;
   auto load = [&](Ops& p, int c) {
     const int cc = max(c, 0);
     const long u = (long)(sp.gc0 + cc) * geo.H + h;
@@ -88,6 +101,11 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
     p.m.load(Mg + u * CH * CH, CH, CH);
     p.dO.load(dO + tk * D + i0, D, n);
     p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+    if constexpr (G2) {
+      p.e.load(erase + tk * D, D, n);
+      const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
+      p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+    }
   };
   auto step = [&](int c, Ops& p) {
     const long u = (long)(sp.gc0 + c) * geo.H + h;
@@ -95,7 +113,10 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
     p.k.store(Ks, LD);
     p.x.store(Xs, LD);
     p.m.store(Ms, LDR);
-    if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
+    if (threadIdx.x < CH) {
+      gs[threadIdx.x] = p.g;
+      if constexpr (G2) bsh[threadIdx.x] = p.b;
+    }
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
@@ -110,7 +131,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
           const int t = p.dO.row(it), i = p.dO.col(it);
           const E* e = reinterpret_cast<const E*>(&p.dO.v[it]);
           float eg = 1.f;
-          if constexpr (VAR == VAR_GATED) eg = __expf(gs[t]);
+          if constexpr (DEC) eg = __expf(gs[t]);
 #pragma unroll
           for (int x = 0; x < RT::VE; ++x) {
             const float val = geo.scale * (float)e[x];
@@ -120,6 +141,15 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
         }
       }
     }
+    if constexpr (G2) {
+#pragma unroll
+      for (int it = 0; it < decltype(p.e)::IT; ++it) {
+        const int t = p.e.row(it), j0 = p.e.col(it);
+#pragma unroll
+        for (int x = 0; x < decltype(p.e)::VE; ++x)
+          As[t * LD + j0 + x] = (E)(bsh[t] * (float)p.e.elem(it, x) * (float)p.k.elem(it, x));
+      }
+    }
     load(p, c - 2);
     s2g_full<E, BV, D, NT>(dHs + u * D * D + (long)i0 * D, D, dWs, LD);
     __syncthreads();
@@ -127,12 +157,12 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const f32x4 a1 = mma_k<E, CH>(zero4(), colk(Ms, LDR), 16 * w, rowk(dOt, LDR), 16 * it);
-      const f32x4 a2 = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * w, rowk(dWs, LD), 16 * it);
+      const f32x4 a2 = mma_k<E, D>(zero4(), rowk(G2 ? As : Ks, LD), 16 * w, rowk(dWs, LD), 16 * it);
       f32x4 dr, ndr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float dec = 1.f;
-        if constexpr (VAR == VAR_GATED) dec = __expf(gn - gs[acc_row(16 * w, r)]);
+        if constexpr (DEC) dec = __expf(gn - gs[acc_row(16 * w, r)]);
         dr[r] = a1[r] + dec * a2[r];
         ndr[r] = -dr[r];
       }
@@ -142,7 +172,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
     __syncthreads();
     s2g_full<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV);
     float eg = 1.f;
-    if constexpr (VAR == VAR_GATED) eg = __expf(gn);
+    if constexpr (DEC) eg = __expf(gn);
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
@@ -588,23 +618,22 @@ template <typename E, int D, int VAR>
 static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht,
                            const gdr_grads& gr, hipStream_t st) {
   const Geo& g = p.geo;
-  if (p.bv == 16) {
-    {
-      TraceScope ts_("bwd_scan", st);
+  {
+    TraceScope ts_("bwd_scan", st);
+    if (p.bv == 16) {
       hipLaunchKernelGGL((k_bwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
                          (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
-                         (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0);
-    }
-  } else {
-    {
-      TraceScope ts_("bwd_scan", st);
+                         (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0, (const E*)in.beta, (const E*)in.erase);
+    } else {
       hipLaunchKernelGGL((k_bwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
                          (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
-                         (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0);
+                         (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0, (const E*)in.beta, (const E*)in.erase);
     }
   }
   if (g.total_chunks > 0) {
-    {
+    if constexpr (VAR == VAR_GDN2) {
+      return launch_bwd_gdn2<E, D>(p, in, dO, gr, st);
+    } else {
       TraceScope ts_("bwd_chunk", st);
       hipLaunchKernelGGL((k_bwd_chunk<E, D, VAR>), dim3(g.total_chunks, g.H), dim3(512), 0, st, g,
                          (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
@@ -619,20 +648,18 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
 hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht, const gdr_grads& gr,
                         hipStream_t st) {
   const bool bf = p.dtype == GDR_BF16;
+#define GDR_BWD_CASE(V)                                                                  \
+  if (bf && p.D == 128) return bwd_impl<bf16, 128, V>(p, in, dO, dht, gr, st);           \
+  if (bf && p.D == 64) return bwd_impl<bf16, 64, V>(p, in, dO, dht, gr, st);             \
+  if (!bf && p.D == 64) return bwd_impl<float, 64, V>(p, in, dO, dht, gr, st);           \
+  break;
   switch (p.variant) {
-    case GDR_DELTANET:
-      if (bf && p.D == 128) return bwd_impl<bf16, 128, VAR_DELTANET>(p, in, dO, dht, gr, st);
-      if (bf && p.D == 64) return bwd_impl<bf16, 64, VAR_DELTANET>(p, in, dO, dht, gr, st);
-      if (!bf && p.D == 64) return bwd_impl<float, 64, VAR_DELTANET>(p, in, dO, dht, gr, st);
-      break;
-    case GDR_GATED:
-      if (bf && p.D == 128) return bwd_impl<bf16, 128, VAR_GATED>(p, in, dO, dht, gr, st);
-      if (bf && p.D == 64) return bwd_impl<bf16, 64, VAR_GATED>(p, in, dO, dht, gr, st);
-      if (!bf && p.D == 64) return bwd_impl<float, 64, VAR_GATED>(p, in, dO, dht, gr, st);
-      break;
-    default:
-      break;
+    case GDR_DELTANET: GDR_BWD_CASE(VAR_DELTANET)
+    case GDR_GATED: GDR_BWD_CASE(VAR_GATED)
+    case GDR_GDN2: GDR_BWD_CASE(VAR_GDN2)
+    default: break;
   }
+#undef GDR_BWD_CASE
   return hipErrorInvalidValue;
 }
 

@@ -120,22 +120,37 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
 // jt = w + 4q and every value sub-tile.
 // ---------------------------------------------------------------------------------------
 // Operands of one chunk of the forward scan, held in registers while they are in flight.
-template <typename E, int D, int BV>
+// Gated DeltaNet-2 also needs the erase gates (for the erase direction a = beta e*k) and the
+// value tile's write gates and values (for b = beta w*v).
+template <typename E, int D, int BV, bool G2>
 struct FwdScanOps {
   RegTile<E, CH, D, 256> x, k;
   RegTile<E, CH, BV, 256> u;
   float g;
+};
+template <typename E, int D, int BV>
+struct FwdScanOps<E, D, BV, true> {
+  RegTile<E, CH, D, 256> x, k, e;
+  RegTile<E, CH, BV, 256> u, vt, wt;
+  float g, b;
 };
 
 template <typename E, int D, int BV, int VAR>
 __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__ k, const E* __restrict__ Xg,
                                                   const E* __restrict__ Ug, const float* __restrict__ Gg,
                                                   const float* __restrict__ h0, E* __restrict__ Hs,
-                                                  E* __restrict__ Rg, float* __restrict__ ht) {
+                                                  E* __restrict__ Rg, float* __restrict__ ht,
+                                                  const E* __restrict__ vin, const E* __restrict__ beta,
+                                                  const E* __restrict__ erase, const E* __restrict__ write) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
+  constexpr bool G2 = VAR == VAR_GDN2;
+  constexpr bool DEC = VAR != VAR_DELTANET;
   __shared__ __align__(16) E Xs[CH * LD];
   __shared__ __align__(16) E Ks[CH * LD];
+  __shared__ __align__(16) E As[G2 ? CH * LD : 8];      // a = beta e*k (GDN-2)
+  __shared__ __align__(16) E Bd[G2 ? BV * LDR : 8];     // e^{g_n-g} b^T (GDN-2)
+  __shared__ float bsh[CH];
   __shared__ __align__(16) E Us[CH * LDV];
   __shared__ __align__(16) E Ws[BV * LD];
   __shared__ __align__(16) E Rn[CH * LDV];
@@ -166,27 +181,57 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
 
   // Chunk c + 2 is loaded while chunk c is computed (two register sets, loop unrolled by two).
   // Loads past the last chunk repeat it, so every step issues the same memory operations.
-  using Ops = FwdScanOps<E, D, BV>;
+  using Ops = FwdScanOps<E, D, BV, G2>;
   auto load = [&](Ops& p, int c) {
     const int cc = min(c, nck - 1);
     const long u = (long)(sp.gc0 + cc) * geo.H + h;
+    const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
     p.x.load(Xg + u * CH * D, D, CH);
-    p.k.load(k + tk * D, D, min(CH, sp.len - cc * CH));
+    p.k.load(k + tk * D, D, n);
     p.u.load(Ug + u * CH * D + i0, D, CH);
     p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+    if constexpr (G2) {
+      p.e.load(erase + tk * D, D, n);
+      p.vt.load(vin + tk * D + i0, D, n);
+      p.wt.load(write + tk * D + i0, D, n);
+      const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
+      p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+    }
   };
   auto step = [&](int c, Ops& p) {
     const long u = (long)(sp.gc0 + c) * geo.H + h;
     p.x.store(Xs, LD);
     p.k.store(Ks, LD);
     p.u.store(Us, LDV);
-    if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
+    if (threadIdx.x < CH) {
+      gs[threadIdx.x] = p.g;
+      if constexpr (G2) bsh[threadIdx.x] = p.b;
+    }
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
       for (int it = 0; it < NI; ++it) store4_t(Ws, LD, 16 * (w + 4 * qq), 16 * it, S[qq][it]);
     __syncthreads();
+    if constexpr (G2) {
+      // a = beta e*k (row-major) and e^{g_n-g_t} b_t = e^{g_n-g_t} beta_t w_t*v_t (transposed)
+      const float gn0 = gs[CH - 1];
+#pragma unroll
+      for (int it = 0; it < decltype(p.e)::IT; ++it) {
+        const int t = p.e.row(it), j0 = p.e.col(it);
+#pragma unroll
+        for (int x = 0; x < decltype(p.e)::VE; ++x)
+          As[t * LD + j0 + x] = (E)(bsh[t] * (float)p.e.elem(it, x) * (float)p.k.elem(it, x));
+      }
+#pragma unroll
+      for (int it = 0; it < decltype(p.vt)::IT; ++it) {
+        const int t = p.vt.row(it), i = p.vt.col(it);
+        const float sc = bsh[t] * __expf(gn0 - gs[t]);
+#pragma unroll
+        for (int x = 0; x < decltype(p.vt)::VE; ++x)
+          Bd[(i + x) * LDR + t] = (E)(sc * (float)p.wt.elem(it, x) * (float)p.vt.elem(it, x));
+      }
+    }
     load(p, c + 2);
     s2g_full<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD);
     const float gn = gs[CH - 1];
@@ -200,7 +245,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
         const float val = (float)Us[t * LDV + i] - acc[r];
         rv[r] = val;
         float dec = 1.f;
-        if constexpr (VAR == VAR_GATED) dec = __expf(gn - gs[t]);
+        if constexpr (DEC) dec = __expf(gn - gs[t]);
         rd[r] = val * dec;
       }
       store4_n(Rn, LDV, 16 * w, 16 * it, rv);
@@ -209,13 +254,19 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
     __syncthreads();
     s2g_full<E, CH, BV, NT>(Rg + u * CH * D + i0, D, Rn, LDV);
     float eg = 1.f;
-    if constexpr (VAR == VAR_GATED) eg = __expf(gn);
+    if constexpr (DEC) eg = __expf(gn);
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
         S[qq][it] *= eg;
-        S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Ks, LD), 16 * (w + 4 * qq), rowk(Rd, LDR), 16 * it);
+        if constexpr (G2) {
+          // W_next = e^{g_n} W0 + R'^T (e^{g_n-g} a) + b^T (e^{g_n-g} k)
+          S[qq][it] = mma_k<E, CH>(S[qq][it], colk(As, LD), 16 * (w + 4 * qq), rowk(Rd, LDR), 16 * it);
+          S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Ks, LD), 16 * (w + 4 * qq), rowk(Bd, LDR), 16 * it);
+        } else {
+          S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Ks, LD), 16 * (w + 4 * qq), rowk(Rd, LDR), 16 * it);
+        }
       }
     __syncthreads();
   };
@@ -246,12 +297,17 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
 template <typename E, int D, int VAR>
 __global__ __launch_bounds__(256) void k_fwd_out(Geo geo, const E* __restrict__ q, const E* __restrict__ Mg,
                                                  const E* __restrict__ Rg, const float* __restrict__ Gg,
-                                                 const E* __restrict__ Hs, E* __restrict__ o) {
+                                                 const E* __restrict__ Hs, E* __restrict__ o,
+                                                 const E* __restrict__ M2g, const E* __restrict__ vin,
+                                                 const E* __restrict__ beta, const E* __restrict__ write) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDR = CH + pad16<E>();
+  constexpr bool G2 = VAR == VAR_GDN2;
   __shared__ __align__(16) E Qs[CH * LD];
   __shared__ __align__(16) E Ws[D * LD];
   __shared__ __align__(16) E Ms[CH * LDR];
-  __shared__ __align__(16) E Rt[D * LDR];
+  __shared__ __align__(16) E Rs[CH * LD];
+  __shared__ __align__(16) E M2s[G2 ? CH * LDR : 8];
+  __shared__ __align__(16) E Bs[G2 ? CH * LD : 8];
   __shared__ float gs[CH];
   const int gc = blockIdx.x, h = blockIdx.y;
   const ChunkPos cp = chunk_pos(geo, gc);
@@ -261,18 +317,32 @@ __global__ __launch_bounds__(256) void k_fwd_out(Geo geo, const E* __restrict__ 
   g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, cp.n);
   g2s_rows<E, D, D, NT>(Ws, LD, Hs + u * D * D, D, D);
   g2s_rows<E, CH, CH, NT>(Ms, LDR, Mg + u * CH * CH, CH, CH);
-  g2s_rows_t<E, CH, D, NT>(Rt, LDR, Rg + u * CH * D, D, CH);
+  g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
   if (threadIdx.x < CH) gs[threadIdx.x] = Gg[u * CH + threadIdx.x];
+  if constexpr (G2) {
+    g2s_rows<E, CH, CH, NT>(M2s, LDR, M2g + u * CH * CH, CH, CH);
+    RegTile<E, CH, D, NT> rv, rw;
+    rv.load(vin + tk * D, D, cp.n);
+    rw.load(write + tk * D, D, cp.n);
+#pragma unroll
+    for (int it = 0; it < decltype(rv)::IT; ++it) {
+      const int t = rv.row(it), i = rv.col(it);
+      const float b = (t < cp.n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+#pragma unroll
+      for (int x = 0; x < decltype(rv)::VE; ++x) Bs[t * LD + i + x] = (E)(b * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+    }
+  }
   __syncthreads();
   f32x4 ov[D / 16];
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
     const f32x4 a1 = mma_k<E, D>(zero4(), rowk(Qs, LD), 16 * w, rowk(Ws, LD), 16 * nt);
-    const f32x4 a2 = mma_k<E, CH>(zero4(), rowk(Ms, LDR), 16 * w, rowk(Rt, LDR), 16 * nt);
+    f32x4 a2 = mma_k<E, CH>(zero4(), rowk(Ms, LDR), 16 * w, colk(Rs, LD), 16 * nt);
+    if constexpr (G2) a2 = mma_k<E, CH>(a2, rowk(M2s, LDR), 16 * w, colk(Bs, LD), 16 * nt);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float e = 1.f;
-      if constexpr (VAR == VAR_GATED) e = expf(gs[acc_row(16 * w, r)]);
+      if constexpr (VAR != VAR_DELTANET) e = __expf(gs[acc_row(16 * w, r)]);
       ov[nt][r] = geo.scale * (e * a1[r] + a2[r]);
     }
   }
@@ -291,53 +361,50 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, float* 
   const Geo& g = p.geo;
   const dim3 cgrid(g.total_chunks, g.H);
   if (g.total_chunks > 0) {
-    {
+    if constexpr (VAR == VAR_GDN2) {
+      const hipError_t e = launch_fwd_prep_gdn2<E, D>(p, in, st);
+      if (e != hipSuccess) return e;
+    } else {
       TraceScope ts_("fwd_prep", st);
       hipLaunchKernelGGL((k_fwd_prep<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k,
                          (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G);
     }
   }
-  if (p.bv == 16) {
-    {
-      TraceScope ts_("fwd_scan", st);
+  {
+    TraceScope ts_("fwd_scan", st);
+    if (p.bv == 16) {
       hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
                          (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
-                         (E*)p.R, ht);
-    }
-  } else {
-    {
-      TraceScope ts_("fwd_scan", st);
+                         (E*)p.R, ht, (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
+    } else {
       hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
                          (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
-                         (E*)p.R, ht);
+                         (E*)p.R, ht, (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
     }
   }
   if (want_out && g.total_chunks > 0) {
-    {
-      TraceScope ts_("fwd_out", st);
-      hipLaunchKernelGGL((k_fwd_out<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)p.M,
-                         (const E*)p.R, (const float*)p.G, (const E*)p.Hs, (E*)o);
-    }
+    TraceScope ts_("fwd_out", st);
+    hipLaunchKernelGGL((k_fwd_out<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)p.M,
+                       (const E*)p.R, (const float*)p.G, (const E*)p.Hs, (E*)o, (const E*)p.M2, (const E*)in.v,
+                       (const E*)in.beta, (const E*)in.write);
   }
   return hipGetLastError();
 }
 
 hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st) {
   const bool bf = p.dtype == GDR_BF16;
+#define GDR_FWD_CASE(V)                                                                  \
+  if (bf && p.D == 128) return fwd_impl<bf16, 128, V>(p, in, o, ht, want_out, st);       \
+  if (bf && p.D == 64) return fwd_impl<bf16, 64, V>(p, in, o, ht, want_out, st);         \
+  if (!bf && p.D == 64) return fwd_impl<float, 64, V>(p, in, o, ht, want_out, st);       \
+  break;
   switch (p.variant) {
-    case GDR_DELTANET:
-      if (bf && p.D == 128) return fwd_impl<bf16, 128, VAR_DELTANET>(p, in, o, ht, want_out, st);
-      if (bf && p.D == 64) return fwd_impl<bf16, 64, VAR_DELTANET>(p, in, o, ht, want_out, st);
-      if (!bf && p.D == 64) return fwd_impl<float, 64, VAR_DELTANET>(p, in, o, ht, want_out, st);
-      break;
-    case GDR_GATED:
-      if (bf && p.D == 128) return fwd_impl<bf16, 128, VAR_GATED>(p, in, o, ht, want_out, st);
-      if (bf && p.D == 64) return fwd_impl<bf16, 64, VAR_GATED>(p, in, o, ht, want_out, st);
-      if (!bf && p.D == 64) return fwd_impl<float, 64, VAR_GATED>(p, in, o, ht, want_out, st);
-      break;
-    default:
-      break;
+    case GDR_DELTANET: GDR_FWD_CASE(VAR_DELTANET)
+    case GDR_GATED: GDR_FWD_CASE(VAR_GATED)
+    case GDR_GDN2: GDR_FWD_CASE(VAR_GDN2)
+    default: break;
   }
+#undef GDR_FWD_CASE
   return hipErrorInvalidValue;
 }
 

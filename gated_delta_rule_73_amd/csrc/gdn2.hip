@@ -1,0 +1,736 @@
+// Gated DeltaNet-2 chunk kernels: separate per-key-channel erase gates e and per-value-channel
+// write gates w on top of a scalar decay alpha.  Token update (erase along a = beta e*k, write
+// b = beta w*v at address k):  W_t = alpha_t W_{t-1} (I - k_t a_t^T) + b_t k_t^T.
+//
+// Chunk form (n <= 64 tokens from W0; g = in-chunk cumsum of log alpha, E_ts = e^{g_t - g_s}):
+//   A_kk = tril_strict((K K^T) * E),  A_ak = tril_strict((K A^T) * E)
+//   M_qk = tril((Q K^T) * E),          M_qa = tril((Q A^T) * E)
+//   L = I + A_ak,  X' = L^{-1} (e^g * K),  U'' = -L^{-1} A_kk B
+//   R' = U'' - X' W0^T                  (R' = -Y: minus the memory's predictions W'_t k_t)
+//   O  = scale ((e^g * Q) W0^T + M_qa R' + M_qk B)
+//   W_next = e^{g_n} W0 + R'^T (e^{g_n-g} * A) + B^T (e^{g_n-g} * K)
+// The scan and output kernels are shared with the delta family (fwd.hip); this file holds the
+// prep kernel and the three backward stages.
+#include "chunk.hpp"
+#include "launch.hpp"
+
+namespace gdr {
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+                                                       const E* __restrict__ v, const E* __restrict__ beta,
+                                                       const E* __restrict__ alpha, const E* __restrict__ erase,
+                                                       const E* __restrict__ write, E* __restrict__ Xo,
+                                                       E* __restrict__ Uo, E* __restrict__ U2o, E* __restrict__ Mqa,
+                                                       E* __restrict__ Mqk, float* __restrict__ Go) {
+  constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 1;
+  __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g K, then X'
+  __shared__ __align__(16) E Qs[CH * LD];   // Q, then A_kk B, then U''
+  __shared__ __align__(16) E As[CH * LD];   // a = beta e*k
+  __shared__ __align__(16) E Bs[CH * LD];   // b = beta w*v
+  __shared__ __align__(16) E Akk[CH * LDT];
+  __shared__ __align__(16) E Ti[CH * LDT];  // solve scratch, then L^{-1}
+  __shared__ __align__(16) float Ls[CH * LF];
+  __shared__ __align__(16) float Li[CH * LF];
+  __shared__ float gs[CH], bs[CH];
+
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id();
+  const int n = cp.n;
+
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x;
+    const bool ok = t < n;
+    bs[t] = ok ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+    const float la = ok ? logf((float)alpha[tk + t]) : 0.f;
+    const float g = wave_incl_scan(la);
+    gs[t] = g;
+    Go[u * CH + t] = g;
+  }
+  {
+    RegTile<E, CH, D, NT> rk, re, rv, rw;
+    rk.load(k + tk * D, D, n);
+    re.load(erase + tk * D, D, n);
+    rv.load(v + tk * D, D, n);
+    rw.load(write + tk * D, D, n);
+    g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
+    rk.store(Ks, LD);
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < decltype(rk)::IT; ++it) {
+      const int t = rk.row(it), j = rk.col(it);
+#pragma unroll
+      for (int x = 0; x < decltype(rk)::VE; ++x) {
+        As[t * LD + j + x] = (E)(bs[t] * (float)re.elem(it, x) * (float)rk.elem(it, x));
+        Bs[t * LD + j + x] = (E)(bs[t] * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+      }
+    }
+  }
+  __syncthreads();
+
+  // 40 Gram tile jobs: A_kk, A_ak (strict lower), M_qk, M_qa (lower, to global)
+  for (int job = w; job < 40; job += 4) {
+    const int which = job / 10;
+    int mt, nt;
+    tri_tile(job % 10, mt, nt);
+    const E* lhs = (which < 2) ? Ks : Qs;
+    const E* rhs = (which == 0 || which == 2) ? Ks : As;
+    const f32x4 acc = mma_k<E, D>(zero4(), rowk(lhs, LD), 16 * mt, rowk(rhs, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
+      const bool keep = (which < 2) ? (s < t) : (s <= t);
+      const float val = keep ? acc[r] * __expf(gs[t] - gs[s]) : 0.f;
+      if (which == 0) Akk[t * LDT + s] = (E)val;
+      else if (which == 1) Ls[t * LF + s] = val;
+      else if (which == 2) Mqk[(u * CH + t) * CH + s] = (E)val;
+      else Mqa[(u * CH + t) * CH + s] = (E)val;
+    }
+  }
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s = idx & 63;
+    if ((s >> 4) > (t >> 4)) {
+      Mqk[(u * CH + t) * CH + s] = (E)0.f;
+      Mqa[(u * CH + t) * CH + s] = (E)0.f;
+      Akk[t * LDT + s] = (E)0.f;
+    }
+  }
+  __syncthreads();
+  solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ti));
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s = idx & 63;
+    Ti[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] : 0.f);
+  }
+  // A_kk B into registers (the Q buffer receives it below)
+  f32x4 cu[D / 16];
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) cu[nt] = mma_k<E, CH>(zero4(), rowk(Akk, LDT), 16 * w, colk(Bs, LD), 16 * nt);
+  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
+    const int t = idx / D, j = idx % D;
+    Ks[t * LD + j] = (E)(__expf(gs[t]) * (float)Ks[t * LD + j]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) store4_n(Qs, LD, 16 * w, 16 * nt, cu[nt]);
+  __syncthreads();
+  f32x4 xa[D / 16], ua[D / 16];
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    xa[nt] = mma_k<E, CH>(zero4(), rowk(Ti, LDT), 16 * w, colk(Ks, LD), 16 * nt);
+    ua[nt] = -mma_k<E, CH>(zero4(), rowk(Ti, LDT), 16 * w, colk(Qs, LD), 16 * nt);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    store4_n(Ks, LD, 16 * w, 16 * nt, xa[nt]);
+    store4_n(Qs, LD, 16 * w, 16 * nt, ua[nt]);
+  }
+  __syncthreads();
+  s2g_full<E, CH, D, NT>(Xo + u * CH * D, D, Ks, LD);
+  s2g_full<E, CH, D, NT>(Uo + u * CH * D, D, Qs, LD);
+  s2g_full<E, CH, D, NT>(U2o + u * CH * D, D, Qs, LD);
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward, stage 1: products with the chunk-start memory W0 and the end-of-chunk gradient dW.
+//   dQhat = dO W0, dX' = -dR' W0, dAbar = R' dW, dKbar = B dW, dM_qa = dO R'^T, dM_qk = dO B^T,
+//   dB_state = (e^{g_n-g} K) dW^T, and e^{g_n} <W0, dW>.   (dR' comes from the reverse scan.)
+// ---------------------------------------------------------------------------------------
+template <typename E, int D>
+struct G2StateLds {
+  static constexpr int LD = D + pad16<E>(), LDR = CH + pad16<E>();
+  static constexpr int TK = CH * LD * (int)sizeof(E), TH = D * LDR * (int)sizeof(E);
+  static constexpr int BYTES = 6 * TK + 2 * TH;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
+                                                        const E* __restrict__ beta, const E* __restrict__ erase,
+                                                        const E* __restrict__ write, const E* __restrict__ dO,
+                                                        const float* __restrict__ Gg, const E* __restrict__ Hs,
+                                                        const E* __restrict__ Rg, const E* __restrict__ dHs,
+                                                        const E* __restrict__ dRg, Plan p) {
+  using Ly = G2StateLds<E, D>;
+  constexpr int NT = 512, LD = Ly::LD, LDR = Ly::LDR, KH = 64, NH = D / KH, NQ = D / 32;
+  __shared__ __align__(16) char smem[Ly::BYTES];
+  __shared__ float gs[CH], bs[CH], red[NT / 64];
+  __shared__ float rkb[8][CH], rab[8][CH];
+  E* Ks = reinterpret_cast<E*>(smem);
+  E* As = Ks + CH * LD;
+  E* Bs = As + CH * LD;
+  E* dOs = Bs + CH * LD;
+  E* dRs = dOs + CH * LD;
+  E* Rs = dRs + CH * LD;
+  E* Wh = Rs + CH * LD;
+  E* dWh = Wh + D * LDR;
+
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id(), wm = w & 3, wn = w >> 2, n = cp.n;
+
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x;
+    gs[t] = Gg[u * CH + t];
+    bs[t] = t < n ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+  }
+  {
+    RegTile<E, CH, D, NT> rk, re, rv, rw;
+    rk.load(k + tk * D, D, n);
+    re.load(erase + tk * D, D, n);
+    rv.load(v + tk * D, D, n);
+    rw.load(write + tk * D, D, n);
+    g2s_rows<E, CH, D, NT>(dOs, LD, dO + tk * D, D, n);
+    g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
+    g2s_rows<E, CH, D, NT>(dRs, LD, dRg + u * CH * D, D, CH);
+    rk.store(Ks, LD);
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < decltype(rk)::IT; ++it) {
+      const int t = rk.row(it), j = rk.col(it);
+#pragma unroll
+      for (int x = 0; x < decltype(rk)::VE; ++x) {
+        As[t * LD + j + x] = (E)(bs[t] * (float)re.elem(it, x) * (float)rk.elem(it, x));
+        Bs[t * LD + j + x] = (E)(bs[t] * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+      }
+    }
+  }
+  const float gn = gs[CH - 1];
+  f32x4 acc1[D / 16], dab[NQ], dkb[NQ], mqa[2], mqk[2];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) acc1[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) dab[i] = dkb[i] = zero4();
+  mqa[0] = mqa[1] = mqk[0] = mqk[1] = zero4();
+  float gam = 0.f;
+  float* db1 = p.g2_db + u * CH * D;
+  for (int ih = 0; ih < NH; ++ih) {
+    __syncthreads();
+    g2s_rows_t<E, KH, D, NT>(Wh, LDR, Hs + u * D * D + (long)ih * KH * D, D, KH);
+    g2s_rows_t<E, KH, D, NT>(dWh, LDR, dHs + u * D * D + (long)ih * KH * D, D, KH);
+    __syncthreads();
+    const E* Aop = (w < 4 ? dOs : dRs) + ih * KH;
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(Aop, LD), 16 * wm, rowk(Wh, LDR), 16 * nt);
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      dab[qq] = mma_k<E, KH>(dab[qq], rowk(Rs + ih * KH, LD), 16 * wm, rowk(dWh, LDR), 16 * (wn * NQ + qq));
+      dkb[qq] = mma_k<E, KH>(dkb[qq], rowk(Bs + ih * KH, LD), 16 * wm, rowk(dWh, LDR), 16 * (wn * NQ + qq));
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+      mqa[e] = mma_k<E, KH>(mqa[e], rowk(dOs + ih * KH, LD), 16 * mt, rowk(Rs + ih * KH, LD), 16 * nt);
+      mqk[e] = mma_k<E, KH>(mqk[e], rowk(dOs + ih * KH, LD), 16 * mt, rowk(Bs + ih * KH, LD), 16 * nt);
+      // dB_state for the value columns of this half: (e^{g_n-g} K) dW^T
+      const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * mt, colk(dWh, LDR), 16 * nt);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(16 * mt, r);
+        db1[t * D + ih * KH + acc_col(16 * nt)] = __expf(gn - gs[t]) * acc[r];
+      }
+    }
+    for (int idx = threadIdx.x; idx < D * KH; idx += NT) {
+      const int j = idx / KH, i = idx % KH;
+      gam += (float)Wh[j * LDR + i] * (float)dWh[j * LDR + i];
+    }
+  }
+  float* dq1 = p.g2_dq + u * CH * D;
+  float* dx = p.g2_dx + u * CH * D;
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * wm, r), j = acc_col(16 * nt);
+      if (w < 4) dq1[t * D + j] = geo.scale * __expf(gs[t]) * acc1[nt][r];
+      else dx[t * D + j] = -acc1[nt][r];
+    }
+  {
+    float* dk1 = p.g2_dk + u * CH * D;
+    float* da1 = p.g2_da + u * CH * D;
+    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(16 * wm, r), j = acc_col(16 * (wn * NQ + qq));
+        const float dec = __expf(gn - gs[t]);
+        const float xk = dec * dkb[qq][r], xa = dec * dab[qq][r];
+        dk1[t * D + j] = xk;
+        da1[t * D + j] = xa;
+        pk[r] += (float)Ks[t * LD + j] * xk;
+        pa[r] += (float)As[t * LD + j] * xa;
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = sum16(pk[r]), b = sum16(pa[r]);
+      if (lrow() == 0) {
+        rkb[w][acc_row(16 * wm, r)] = a;
+        rab[w][acc_row(16 * wm, r)] = b;
+      }
+    }
+  }
+  float* dmqa = p.g2_dmqa + u * CH * CH;
+  float* dmqk = p.g2_dmqk + u * CH * CH;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s2 = acc_col(16 * nt);
+      const bool keep = s2 <= t;
+      dmqa[t * CH + s2] = keep ? geo.scale * mqa[e][r] : 0.f;
+      dmqk[t * CH + s2] = keep ? geo.scale * mqk[e][r] : 0.f;
+    }
+  }
+  gam = wave_sum(gam);
+  if (lane_id() == 0) red[w] = gam;
+  __syncthreads();
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x, b0 = t >> 4;
+    float* rows = p.g2_rows + u * 4 * CH;
+    rows[t] = rkb[b0][t] + rkb[b0 + 4][t] + rab[b0][t] + rab[b0 + 4][t];
+    if (t == 0) {
+      float g4 = 0.f;
+#pragma unroll
+      for (int i = 0; i < NT / 64; ++i) g4 += red[i];
+      rows[3 * CH] = __expf(gn) * g4;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward, stage 2: the solve side.  Recomputes A_kk, A_ak and L^{-1}; then
+//   dKhat = L^-T dX',  dC = -L^-T dR',  dA_ak = tril_strict(-dKhat X'^T + dC U''^T),
+//   dA_kk = tril_strict(dC B^T),  dB = dB_state + A_kk^T dC + M_qk^T dO,
+//   dv = beta w*dB, dw = beta v*dB;  dk += e^g dKhat.
+// ---------------------------------------------------------------------------------------
+template <typename E, int D>
+struct G2WyLds {
+  static constexpr int LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 1;
+  static constexpr int TK = CH * LD * (int)sizeof(E), SQ = CH * LDT * (int)sizeof(E), F = CH * LF * 4;
+  static constexpr int U1 = 3 * F, U2 = 4 * TK;
+  static constexpr int BYTES = 2 * TK + 3 * SQ + (U1 > U2 ? U1 : U2);
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
+                                                     const E* __restrict__ beta, const E* __restrict__ erase,
+                                                     const E* __restrict__ write, const E* __restrict__ dO,
+                                                     const float* __restrict__ Gg, const E* __restrict__ Xg,
+                                                     const E* __restrict__ U2g, const E* __restrict__ M2g,
+                                                     const E* __restrict__ dRg, E* __restrict__ dv,
+                                                     E* __restrict__ dw, Plan p) {
+  using Ly = G2WyLds<E, D>;
+  constexpr int NT = 256, LD = Ly::LD, LDT = Ly::LDT, LF = Ly::LF;
+  __shared__ __align__(16) char smem[Ly::BYTES];
+  __shared__ __align__(16) float scr[4 * 256];
+  __shared__ float gs[CH], bs[CH], rk[4][CH], rb[4][CH];
+  E* Ks = reinterpret_cast<E*>(smem);
+  E* As = Ks + CH * LD;
+  E* LiT = As + CH * LD;
+  E* AkkE = LiT + CH * LDT;
+  E* Mqk = AkkE + CH * LDT;
+  char* un = reinterpret_cast<char*>(Mqk + CH * LDT);
+  float* Akk = reinterpret_cast<float*>(un);
+  float* Aak = Akk + CH * LF;
+  float* Li = Aak + CH * LF;
+  E* P1 = reinterpret_cast<E*>(un);
+  E* P2 = P1 + CH * LD;
+  E* P3 = P2 + CH * LD;
+  E* P4 = P3 + CH * LD;
+
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id(), n = cp.n;
+
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x;
+    gs[t] = Gg[u * CH + t];
+    bs[t] = t < n ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+  }
+  {
+    RegTile<E, CH, D, NT> rkk, re;
+    rkk.load(k + tk * D, D, n);
+    re.load(erase + tk * D, D, n);
+    rkk.store(Ks, LD);
+    g2s_rows<E, CH, CH, NT>(Mqk, LDT, M2g + u * CH * CH, CH, CH);
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < decltype(rkk)::IT; ++it) {
+      const int t = rkk.row(it), j = rkk.col(it);
+#pragma unroll
+      for (int x = 0; x < decltype(rkk)::VE; ++x)
+        As[t * LD + j + x] = (E)(bs[t] * (float)re.elem(it, x) * (float)rkk.elem(it, x));
+    }
+  }
+  __syncthreads();
+  float* akk_out = p.g2_akk + u * CH * CH;
+  float* aak_out = p.g2_aak + u * CH * CH;
+  for (int job = w; job < 32; job += 4) {  // 16 tiles each of A_kk and A_ak
+    const bool ak = job >= 16;
+    const int id = job & 15, mt = id >> 2, nt = id & 3;
+    const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * mt, rowk(ak ? As : Ks, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s2 = acc_col(16 * nt);
+      const float val = (s2 < t) ? acc[r] * __expf(gs[t] - gs[s2]) : 0.f;
+      if (ak) {
+        Aak[t * LF + s2] = val;
+        aak_out[t * CH + s2] = val;
+      } else {
+        Akk[t * LF + s2] = val;
+        akk_out[t * CH + s2] = val;
+        AkkE[t * LDT + s2] = (E)val;
+      }
+    }
+  }
+  __syncthreads();
+  solve_unit_lower64<NT>(Aak, LF, Li, LF, scr);
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s2 = idx & 63;
+    LiT[t * LDT + s2] = (E)Li[s2 * LF + t];  // (L^{-1})^T
+  }
+  __syncthreads();
+  {  // dX' (float32 workspace) and dR' into the union region
+    const float* dx = p.g2_dx + u * CH * D;
+    for (int idx = threadIdx.x; idx < CH * D; idx += NT) P1[(idx / D) * LD + idx % D] = (E)dx[idx];
+    g2s_rows<E, CH, D, NT>(P2, LD, dRg + u * CH * D, D, CH);
+  }
+  __syncthreads();
+  f32x4 dkh[D / 16], dc[D / 16];
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    dkh[nt] = mma_k<E, CH>(zero4(), rowk(LiT, LDT), 16 * w, colk(P1, LD), 16 * nt);
+    dc[nt] = -mma_k<E, CH>(zero4(), rowk(LiT, LDT), 16 * w, colk(P2, LD), 16 * nt);
+  }
+  __syncthreads();
+  {
+    float* dk1 = p.g2_dk + u * CH * D;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      store4_n(P1, LD, 16 * w, 16 * nt, dkh[nt]);
+      store4_n(P2, LD, 16 * w, 16 * nt, dc[nt]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(16 * w, r), j = acc_col(16 * nt);
+        const float x = __expf(gs[t]) * dkh[nt][r];
+        dk1[t * D + j] += x;
+        part[r] += (float)Ks[t * LD + j] * x;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = sum16(part[r]);
+      if (lrow() == 0) rk[w][acc_row(16 * w, r)] = a;
+    }
+  }
+  g2s_rows<E, CH, D, NT>(P3, LD, Xg + u * CH * D, D, CH);
+  g2s_rows<E, CH, D, NT>(P4, LD, U2g + u * CH * D, D, CH);
+  __syncthreads();
+  float* daak = p.g2_daak + u * CH * CH;
+  for (int id = w; id < 16; id += 4) {
+    const int mt = id >> 2, nt = id & 3;
+    f32x4 acc = mma_k<E, D>(zero4(), rowk(P2, LD), 16 * mt, rowk(P4, LD), 16 * nt);
+    acc = acc - mma_k<E, D>(zero4(), rowk(P1, LD), 16 * mt, rowk(P3, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s2 = acc_col(16 * nt);
+      daak[t * CH + s2] = (s2 < t) ? acc[r] : 0.f;
+    }
+  }
+  __syncthreads();
+  {  // b = beta w*v into P3, dO into P4
+    RegTile<E, CH, D, NT> rv, rw;
+    rv.load(v + tk * D, D, n);
+    rw.load(write + tk * D, D, n);
+#pragma unroll
+    for (int it = 0; it < decltype(rv)::IT; ++it) {
+      const int t = rv.row(it), i = rv.col(it);
+#pragma unroll
+      for (int x = 0; x < decltype(rv)::VE; ++x) P3[t * LD + i + x] = (E)(bs[t] * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+    }
+    g2s_rows<E, CH, D, NT>(P4, LD, dO + tk * D, D, n);
+  }
+  __syncthreads();
+  float* dakk = p.g2_dakk + u * CH * CH;
+  for (int id = w; id < 16; id += 4) {
+    const int mt = id >> 2, nt = id & 3;
+    const f32x4 acc = mma_k<E, D>(zero4(), rowk(P2, LD), 16 * mt, rowk(P3, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s2 = acc_col(16 * nt);
+      dakk[t * CH + s2] = (s2 < t) ? acc[r] : 0.f;
+    }
+  }
+  // dB = dB_state + A_kk^T dC + M_qk^T (scale dO)
+  f32x4 dbt[D / 16];
+  const float* db1 = p.g2_db + u * CH * D;
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    f32x4 a = mma_k<E, CH>(zero4(), colk(AkkE, LDT), 16 * w, colk(P2, LD), 16 * nt);
+    const f32x4 b = mma_k<E, CH>(zero4(), colk(Mqk, LDT), 16 * w, colk(P4, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * w, r), i = acc_col(16 * nt);
+      a[r] += geo.scale * b[r] + db1[t * D + i];
+    }
+    dbt[nt] = a;
+  }
+  __syncthreads();
+  {  // v and w into P1 / P3 for the gate products; outputs staged through P2 / P4
+    g2s_rows<E, CH, D, NT>(P1, LD, v + tk * D, D, n);
+    g2s_rows<E, CH, D, NT>(P3, LD, write + tk * D, D, n);
+  }
+  __syncthreads();
+  {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      f32x4 ov, ow;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(16 * w, r), i = acc_col(16 * nt);
+        const float vv = (float)P1[t * LD + i], ww = (float)P3[t * LD + i];
+        ov[r] = bs[t] * ww * dbt[nt][r];
+        ow[r] = bs[t] * vv * dbt[nt][r];
+        part[r] += ww * vv * dbt[nt][r];
+      }
+      store4_n(P2, LD, 16 * w, 16 * nt, ov);
+      store4_n(P4, LD, 16 * w, 16 * nt, ow);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = sum16(part[r]);
+      if (lrow() == 0) rb[w][acc_row(16 * w, r)] = a;
+    }
+  }
+  __syncthreads();
+  s2g_rows<E, CH, D, NT>(dv + tk * D, D, P2, LD, n);
+  s2g_rows<E, CH, D, NT>(dw + tk * D, D, P4, LD, n);
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x;
+    float* rows = p.g2_rows + u * 4 * CH;
+    rows[CH + t] = rk[t >> 4][t];
+    rows[2 * CH + t] = rb[t >> 4][t];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward, stage 3: Gram slots, gates and the decay gradient.
+//   dk += At_kk K + At_kk^T K + At_ak A + Mt_qk^T Q,  dq += Mt_qk K + Mt_qa A,
+//   da += At_ak^T K + Mt_qa^T Q   (At = dA * E, Mt = dM * E),
+//   de = beta da*k, dk += beta da*e, dbeta += sum(da*e*k) + sum(dB*w*v),
+//   d log alpha_t = rectangle + suffix + prefix sums + e^{g_n} <W0, dW>;  dalpha = that / alpha.
+// ---------------------------------------------------------------------------------------
+template <typename E, int D>
+struct G2GramLds {
+  static constexpr int LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 1;
+  static constexpr int TK = CH * LD * (int)sizeof(E), SQ = CH * LDT * (int)sizeof(E), F = CH * LF * 4;
+  static constexpr int BYTES = 4 * TK + 4 * SQ + F;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+                                                       const E* __restrict__ beta, const E* __restrict__ alpha,
+                                                       const E* __restrict__ erase, const float* __restrict__ Gg,
+                                                       const E* __restrict__ Mqag, const E* __restrict__ Mqkg,
+                                                       E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dbeta,
+                                                       E* __restrict__ dalpha, E* __restrict__ derase, Plan p) {
+  using Ly = G2GramLds<E, D>;
+  constexpr int NT = 256, LD = Ly::LD, LDT = Ly::LDT, LF = Ly::LF;
+  __shared__ __align__(16) char smem[Ly::BYTES];
+  __shared__ float gs[CH], bs[CH], rq[4][CH], re_[4][CH];
+  E* Ks = reinterpret_cast<E*>(smem);
+  E* As = Ks + CH * LD;
+  E* Qs = As + CH * LD;
+  E* Es = Qs + CH * LD;
+  E* Tkk = Es + CH * LD;
+  E* Tak = Tkk + CH * LDT;
+  E* Tqk = Tak + CH * LDT;
+  E* Tqa = Tqk + CH * LDT;
+  float* Pair = reinterpret_cast<float*>(Tqa + CH * LDT);
+
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id(), n = cp.n;
+
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x;
+    gs[t] = Gg[u * CH + t];
+    bs[t] = t < n ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+  }
+  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
+  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
+  g2s_rows<E, CH, D, NT>(Es, LD, erase + tk * D, D, n);
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
+    const int t = idx / D, j = idx % D;
+    As[t * LD + j] = (E)(bs[t] * (float)Es[t * LD + j] * (float)Ks[t * LD + j]);
+  }
+  {
+    const float* dakk = p.g2_dakk + u * CH * CH;
+    const float* daak = p.g2_daak + u * CH * CH;
+    const float* dmqk = p.g2_dmqk + u * CH * CH;
+    const float* dmqa = p.g2_dmqa + u * CH * CH;
+    const float* akk = p.g2_akk + u * CH * CH;
+    const float* aak = p.g2_aak + u * CH * CH;
+    const E* mqk = Mqkg + u * CH * CH;
+    const E* mqa = Mqag + u * CH * CH;
+    for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+      const int t = idx >> 6, s2 = idx & 63;
+      const float dec = (s2 <= t) ? __expf(gs[t] - gs[s2]) : 0.f;
+      Tkk[t * LDT + s2] = (E)(dakk[idx] * dec);
+      Tak[t * LDT + s2] = (E)(daak[idx] * dec);
+      Tqk[t * LDT + s2] = (E)(dmqk[idx] * dec);
+      Tqa[t * LDT + s2] = (E)(dmqa[idx] * dec);
+      Pair[t * LF + s2] = (s2 < t) ? dakk[idx] * akk[idx] + daak[idx] * aak[idx] + dmqk[idx] * (float)mqk[idx] +
+                                         dmqa[idx] * (float)mqa[idx]
+                                   : 0.f;
+    }
+  }
+  __syncthreads();
+  f32x4 aq[D / 16], ak[D / 16], aa[D / 16];
+  {
+    const float* dq1 = p.g2_dq + u * CH * D;
+    const float* dk1 = p.g2_dk + u * CH * D;
+    const float* da1 = p.g2_da + u * CH * D;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(16 * w, r), j = acc_col(16 * nt);
+        aq[nt][r] = dq1[t * D + j];
+        ak[nt][r] = dk1[t * D + j];
+        aa[nt][r] = da1[t * D + j];
+        part[r] += (float)Qs[t * LD + j] * aq[nt][r];
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = sum16(part[r]);
+      if (lrow() == 0) rq[w][acc_row(16 * w, r)] = a;
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    ak[nt] = mma_k<E, CH>(ak[nt], rowk(Tkk, LDT), 16 * w, colk(Ks, LD), 16 * nt);
+    ak[nt] = mma_k<E, CH>(ak[nt], colk(Tkk, LDT), 16 * w, colk(Ks, LD), 16 * nt);
+    ak[nt] = mma_k<E, CH>(ak[nt], rowk(Tak, LDT), 16 * w, colk(As, LD), 16 * nt);
+    ak[nt] = mma_k<E, CH>(ak[nt], colk(Tqk, LDT), 16 * w, colk(Qs, LD), 16 * nt);
+    aq[nt] = mma_k<E, CH>(aq[nt], rowk(Tqk, LDT), 16 * w, colk(Ks, LD), 16 * nt);
+    aq[nt] = mma_k<E, CH>(aq[nt], rowk(Tqa, LDT), 16 * w, colk(As, LD), 16 * nt);
+    aa[nt] = mma_k<E, CH>(aa[nt], colk(Tak, LDT), 16 * w, colk(Ks, LD), 16 * nt);
+    aa[nt] = mma_k<E, CH>(aa[nt], colk(Tqa, LDT), 16 * w, colk(Qs, LD), 16 * nt);
+  }
+  // gates: de = beta da*k, dk += beta da*e, dbeta_a = sum_j da*e*k
+  {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(16 * w, r), j = acc_col(16 * nt);
+        const float kk = (float)Ks[t * LD + j], ee = (float)Es[t * LD + j], da = aa[nt][r];
+        ak[nt][r] += bs[t] * da * ee;
+        part[r] += da * ee * kk;
+        aa[nt][r] = bs[t] * da * kk;  // now de
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = sum16(part[r]);
+      if (lrow() == 0) re_[w][acc_row(16 * w, r)] = a;
+    }
+  }
+  if (threadIdx.x < CH) {  // prefix sums along each row of the pair terms
+    const int uu = threadIdx.x;
+    float run = 0.f;
+#pragma unroll 16
+    for (int s2 = 0; s2 < CH; ++s2) {
+      run += Pair[uu * LF + s2];
+      Pair[uu * LF + s2] = run;
+    }
+  }
+  __syncthreads();
+  // outputs through LDS (K, A, Q regions are free now)
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    store4_n(Ks, LD, 16 * w, 16 * nt, ak[nt]);
+    store4_n(Qs, LD, 16 * w, 16 * nt, aq[nt]);
+    store4_n(As, LD, 16 * w, 16 * nt, aa[nt]);
+  }
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x;
+    const float* rows = p.g2_rows + u * 4 * CH;
+    float rect = 0.f;
+    if (t > 0) {
+#pragma unroll 16
+      for (int uu = 0; uu < CH; ++uu) rect += (uu >= t) ? Pair[uu * LF + t - 1] : 0.f;
+    }
+    const int tr = CH - 1 - t;
+    const float suf_r = wave_incl_scan(rq[tr >> 4][tr] + rows[CH + tr]);
+    const float suf = __shfl(suf_r, CH - 1 - t, 64);
+    const float inc = wave_incl_scan(rows[t]);
+    float pre = __shfl_up(inc, 1, 64);
+    if (t == 0) pre = 0.f;
+    const float dla = rect + suf + pre + rows[3 * CH];
+    if (t < n) {
+      dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
+      if (dbeta) dbeta[tk + t] = (E)(rows[2 * CH + t] + re_[t >> 4][t]);
+    }
+  }
+  __syncthreads();
+  s2g_rows<E, CH, D, NT>(dk + tk * D, D, Ks, LD, n);
+  s2g_rows<E, CH, D, NT>(dq + tk * D, D, Qs, LD, n);
+  s2g_rows<E, CH, D, NT>(derase + tk * D, D, As, LD, n);
+}
+
+template <typename E, int D>
+hipError_t launch_bwd_gdn2(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr, hipStream_t st) {
+  const dim3 grid(p.geo.total_chunks, p.geo.H);
+  {
+    TraceScope ts_("bwd_gdn2_state", st);
+    hipLaunchKernelGGL((k_bwd_gdn2_state<E, D>), grid, dim3(512), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
+                       (const E*)in.beta, (const E*)in.erase, (const E*)in.write, (const E*)dO, (const float*)p.G,
+                       (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR, p);
+  }
+  {
+    TraceScope ts_("bwd_gdn2_wy", st);
+    hipLaunchKernelGGL((k_bwd_gdn2_wy<E, D>), grid, dim3(256), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
+                       (const E*)in.beta, (const E*)in.erase, (const E*)in.write, (const E*)dO, (const float*)p.G,
+                       (const E*)p.X, (const E*)p.U2, (const E*)p.M2, (const E*)p.dR, (E*)gr.dv, (E*)gr.dwrite, p);
+  }
+  {
+    TraceScope ts_("bwd_gdn2_gram", st);
+    hipLaunchKernelGGL((k_bwd_gdn2_gram<E, D>), grid, dim3(256), 0, st, p.geo, (const E*)in.q, (const E*)in.k,
+                       (const E*)in.beta, (const E*)in.alpha, (const E*)in.erase, (const float*)p.G, (const E*)p.M,
+                       (const E*)p.M2, (E*)gr.dq, (E*)gr.dk, (E*)gr.dbeta, (E*)gr.dalpha, (E*)gr.derase, p);
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_bwd_gdn2<bf16, 128>(const Plan&, const gdr_inputs&, const void*, const gdr_grads&, hipStream_t);
+template hipError_t launch_bwd_gdn2<bf16, 64>(const Plan&, const gdr_inputs&, const void*, const gdr_grads&, hipStream_t);
+template hipError_t launch_bwd_gdn2<float, 64>(const Plan&, const gdr_inputs&, const void*, const gdr_grads&, hipStream_t);
+
+template <typename E, int D>
+hipError_t launch_fwd_prep_gdn2(const Plan& p, const gdr_inputs& in, hipStream_t st) {
+  TraceScope ts_("fwd_prep_gdn2", st);
+  hipLaunchKernelGGL((k_fwd_prep_gdn2<E, D>), dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo,
+                     (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
+                     (const E*)in.erase, (const E*)in.write, (E*)p.X, (E*)p.Ub, (E*)p.U2, (E*)p.M, (E*)p.M2, p.G);
+  return hipGetLastError();
+}
+template hipError_t launch_fwd_prep_gdn2<bf16, 128>(const Plan&, const gdr_inputs&, hipStream_t);
+template hipError_t launch_fwd_prep_gdn2<bf16, 64>(const Plan&, const gdr_inputs&, hipStream_t);
+template hipError_t launch_fwd_prep_gdn2<float, 64>(const Plan&, const gdr_inputs&, hipStream_t);
+
+}  // namespace gdr

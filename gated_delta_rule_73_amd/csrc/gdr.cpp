@@ -35,8 +35,8 @@ struct Sizes {
   int total_chunks = 0;
   int nstates = 0;
   size_t esz = 0;
-  size_t X, M, G, Hs, R, Ub, dHs, dR;
-  size_t cache() const { return X + M + G + Hs + R; }
+  size_t X, M, G, Hs, R, M2, U2, Ub, dHs, dR, g2;
+  size_t cache() const { return X + M + G + Hs + R + M2 + U2; }
 };
 
 // Checks the problem description and computes the buffer sizes.
@@ -77,8 +77,7 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
     return fail(GDR_ERR_UNSUPPORTED, "bf16 head size %d: only 64 and 128 are built", p->dk);
   if (p->dtype == GDR_F32 && p->dk != 64)
     return fail(GDR_ERR_UNSUPPORTED, "float32 head size %d: only 64 is built", p->dk);
-  if (p->variant == GDR_KDA || p->variant == GDR_GDN2)
-    return fail(GDR_ERR_UNSUPPORTED, "variant %d is not built yet", p->variant);
+  if (p->variant == GDR_KDA) return fail(GDR_ERR_UNSUPPORTED, "variant %d is not built yet", p->variant);
   if (total_chunks > 0x7fffffffLL) return fail(GDR_ERR_UNSUPPORTED, "too many chunks");
   if ((long long)p->B * p->H * (long long)p->T * p->dk > (1LL << 40))
     return fail(GDR_ERR_UNSUPPORTED, "tensor too large");
@@ -96,6 +95,11 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   s.Ub = align_up(U * C * D * s.esz, A);
   s.dHs = align_up(U * D * D * s.esz, A);
   s.dR = align_up(U * C * D * s.esz, A);
+  const bool g2 = p->variant == GDR_GDN2;
+  s.M2 = g2 ? align_up(U * C * C * s.esz, A) : 0;
+  s.U2 = g2 ? align_up(U * C * D * s.esz, A) : 0;
+  // GDN-2 backward: 5 float32 64xD + 6 float32 64x64 + 4x64 float32 per unit
+  s.g2 = g2 ? align_up(U * (5 * C * D + 6 * C * C + 4 * C) * 4, A) : 0;
   *sz = s;
   return GDR_OK;
 }
@@ -147,10 +151,26 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws)
   pl.G = reinterpret_cast<float*>(c); c += s.G;
   pl.Hs = c; c += s.Hs;
   pl.R = c; c += s.R;
+  pl.M2 = c; c += s.M2;
+  pl.U2 = c; c += s.U2;
   char* w = ws;
   pl.Ub = w; w += s.Ub;
   pl.dHs = w; w += s.dHs;
   pl.dR = w; w += s.dR;
+  float* f = reinterpret_cast<float*>(w);
+  const size_t U = (size_t)s.units, C = gdr::CH, D = (size_t)p->dk;
+  pl.g2_dq = f; f += U * C * D;
+  pl.g2_dk = f; f += U * C * D;
+  pl.g2_da = f; f += U * C * D;
+  pl.g2_db = f; f += U * C * D;
+  pl.g2_dx = f; f += U * C * D;
+  pl.g2_dakk = f; f += U * C * C;
+  pl.g2_daak = f; f += U * C * C;
+  pl.g2_dmqk = f; f += U * C * C;
+  pl.g2_dmqa = f; f += U * C * C;
+  pl.g2_akk = f; f += U * C * C;
+  pl.g2_aak = f; f += U * C * C;
+  pl.g2_rows = f;
   return pl;
 }
 
@@ -184,7 +204,7 @@ gdr_status gdr_workspace_size(const gdr_problem* p, int backward, size_t* bytes)
   gdr_status st = check_problem(p, &s);
   if (st != GDR_OK) return st;
   if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = s.cache() + s.Ub + (backward ? s.dHs + s.dR : 0);
+  *bytes = s.cache() + s.Ub + (backward ? s.dHs + s.dR + s.g2 : 0);
   return GDR_OK;
 }
 
@@ -235,9 +255,9 @@ gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* 
   for (const void* x : ptrs)
     if (x && !aligned(x, 16)) return fail(GDR_ERR_INVALID_ARG, "gradient pointers must be 16-byte aligned");
   if (saved && !aligned(saved, 256)) return fail(GDR_ERR_INVALID_ARG, "saved must be 256-byte aligned");
-  if ((st = check_ws(ws, ws_bytes, s.cache() + s.Ub + s.dHs + s.dR)) != GDR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, s.cache() + s.Ub + s.dHs + s.dR + s.g2)) != GDR_OK) return st;
   char* base = static_cast<char*>(ws);
-  char* cache = saved ? const_cast<char*>(static_cast<const char*>(saved)) : base + s.Ub + s.dHs + s.dR;
+  char* cache = saved ? const_cast<char*>(static_cast<const char*>(saved)) : base + s.Ub + s.dHs + s.dR + s.g2;
   gdr::Plan pl = make_plan(p, s, cache, base);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   g_last_error.clear();

@@ -19,10 +19,18 @@ struct Plan {
   float* G;   // [units][64]     in-chunk cumulative log decay
   void* Hs;   // [units][D][D]   memory at the start of each chunk
   void* R;    // [units][64][D]  scaled residuals R = U - X W0^T
+  void* M2;   // Gated DeltaNet-2: [units][64][64] decayed causal Q K^T (M holds Q A^T)
+  void* U2;   // Gated DeltaNet-2: [units][64][D]  -L^{-1} A_kk B
   // workspace only
   void* Ub;   // [units][64][D]  WY factor U = T V
   void* dHs;  // [units][D][D]   gradient w.r.t. the memory at the end of each chunk
   void* dR;   // [units][64][D]  gradient w.r.t. R
+  // Gated DeltaNet-2 backward intermediates (float32): per unit 64 x D partial gradients of
+  // q, k, the erase direction a and the write vector b, the gradient of X', then 64 x 64
+  // gradients of the four chunk matrices, the two solve-side Grams, and per-token sums.
+  float *g2_dq, *g2_dk, *g2_da, *g2_db, *g2_dx;
+  float *g2_dakk, *g2_daak, *g2_dmqk, *g2_dmqa, *g2_akk, *g2_aak;
+  float* g2_rows;  // [units][4][64]: prefix-type sums, Khat.dKhat, dbeta from b, gamma term
 };
 
 // Optional per-launch event recording (see gdr_trace_launches in gdr.h).
@@ -52,6 +60,11 @@ struct TraceScope {
     (void)hipEventRecord(static_cast<hipEvent_t>(launch_trace().ev[2 * idx + 1]), st);
   }
 };
+
+template <typename E, int D>
+hipError_t launch_fwd_prep_gdn2(const Plan& p, const gdr_inputs& in, hipStream_t st);
+template <typename E, int D>
+hipError_t launch_bwd_gdn2(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr, hipStream_t st);
 
 hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st);
 hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht, const gdr_grads& gr,

@@ -101,3 +101,37 @@ def test_empty_sequences_and_empty_input():
     assert got["o"].shape == (2, 2, 0, 128)
     np.testing.assert_array_equal(got["ht"], inp0["h0"])
     np.testing.assert_array_equal(got["dh0"], np.zeros_like(inp0["h0"]))
+
+
+@pytest.mark.parametrize("alpha_mode,with_beta", [("config", False), ("weak", False), ("one", True),
+                                                   ("config", True)])
+def test_gdn2_bf16_small(alpha_mode, with_beta):
+    """Gated DeltaNet-2: separate erase (key channels) and write (value channels) gates."""
+    w = synth.Workload("t", "gdn2", "bf16", 2, 2, 190, 128, 128, seed=21, has_beta=with_beta, h0_std=0.5)
+    inp = synth.make_inputs(w, alpha_mode=alpha_mode)
+    dht = np.random.default_rng(7).standard_normal((2, 2, 128, 128)).astype(np.float32) * 0.2
+    rep = []
+    compare(run_hip(inp, "gdn2", "bf16", backward=True, dht=dht, scale=0.9),
+            run_oracle(inp, "gdn2", backward=True, dht=dht, scale=0.9), "bf16", report=rep)
+    print("\n".join(rep))
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 64)])
+def test_gdn2_small_heads(dtype, d):
+    w = synth.Workload("t", "gdn2", dtype, 1, 3, 140, d, d, seed=22, has_beta=True, h0_std=0.3)
+    inp = synth.make_inputs(w, alpha_mode="weak")
+    rep = []
+    compare(run_hip(inp, "gdn2", dtype, backward=True), run_oracle(inp, "gdn2", backward=True), dtype, report=rep)
+    print("\n".join(rep))
+
+
+def test_gdn2_varlen_saved_vs_recomputed():
+    cu = (0, 70, 71, 200)
+    w = synth.Workload("t", "gdn2", "bf16", 1, 2, 200, 128, 128, seed=23, cu_seqlens=cu, h0_std=0.4,
+                       has_beta=False)
+    inp = synth.make_inputs(w, alpha_mode="weak")
+    a = run_hip(inp, "gdn2", "bf16", backward=True, use_saved=True)
+    b = run_hip(inp, "gdn2", "bf16", backward=True, use_saved=False)
+    for name in ("o", "dq", "dk", "dv", "dalpha", "derase", "dwrite", "dh0"):
+        assert np.array_equal(a[name], b[name]), name
+    compare(a, run_oracle(inp, "gdn2", backward=True), "bf16")
