@@ -26,7 +26,9 @@ namespace gdr {
 // ---------------------------------------------------------------------------------------
 // Operands of one chunk of the reverse scan, held in registers while they are in flight.
 // Gated DeltaNet-2 also needs the erase gates and beta (for a = beta e*k).
-template <typename E, int D, int BV, bool G2>
+// Kimi Delta Attention reads Qhat = e^g Q and Kbar = e^{g_n-g} K (prepared per chunk) in
+// place of Q and K, and the per-key-channel decay e^{g_n} of the rows this lane holds.
+template <typename E, int D, int BV, int VAR>
 struct BwdScanOps {
   RegTile<E, CH, D, 256> q, k, x;
   RegTile<E, CH, CH, 256> m;
@@ -34,11 +36,18 @@ struct BwdScanOps {
   float g;
 };
 template <typename E, int D, int BV>
-struct BwdScanOps<E, D, BV, true> {
+struct BwdScanOps<E, D, BV, VAR_GDN2> {
   RegTile<E, CH, D, 256> q, k, x, e;
   RegTile<E, CH, CH, 256> m;
   RegTile<E, CH, BV, 256> dO;
   float g, b;
+};
+template <typename E, int D, int BV>
+struct BwdScanOps<E, D, BV, VAR_KDA> {
+  RegTile<E, CH, D, 256> q, k, x;
+  RegTile<E, CH, CH, 256> m;
+  RegTile<E, CH, BV, 256> dO;
+  f32x4 eg[D / 64];
 };
 
 template <typename E, int D, int BV, int VAR>
@@ -51,7 +60,8 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2;
-  constexpr bool DEC = VAR != VAR_DELTANET;
+  constexpr bool KDA = VAR == VAR_KDA;
+  constexpr bool DEC = VAR == VAR_GATED || VAR == VAR_GDN2;  // scalar decay
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];  // a = beta e*k (GDN-2)
   __shared__ float bsh[CH];
   __shared__ __align__(16) E Qs[CH * LD];
@@ -89,18 +99,25 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
 
   // Chunk c - 2 is loaded while chunk c is computed (two register sets, loop unrolled by two).
   // Loads before the first chunk repeat it, so every step issues the same memory operations.
-  using Ops = BwdScanOps<E, D, BV, G2>;
+  using Ops = BwdScanOps<E, D, BV, VAR>;
   auto load = [&](Ops& p, int c) {
     const int cc = max(c, 0);
     const long u = (long)(sp.gc0 + cc) * geo.H + h;
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
-    p.q.load(q + tk * D, D, n);
-    p.k.load(k + tk * D, D, n);
+    if constexpr (KDA) {
+      p.q.load(q + u * CH * D, D, CH);
+      p.k.load(k + u * CH * D, D, CH);
+#pragma unroll
+      for (int qq = 0; qq < NJ; ++qq) p.eg[qq] = *reinterpret_cast<const f32x4*>(Gg + u * D + acc_row(16 * (w + 4 * qq), 0));
+    } else {
+      p.q.load(q + tk * D, D, n);
+      p.k.load(k + tk * D, D, n);
+      p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+    }
     p.x.load(Xg + u * CH * D, D, CH);
     p.m.load(Mg + u * CH * CH, CH, CH);
     p.dO.load(dO + tk * D + i0, D, n);
-    p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
     if constexpr (G2) {
       p.e.load(erase + tk * D, D, n);
       const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
@@ -113,9 +130,15 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
     p.k.store(Ks, LD);
     p.x.store(Xs, LD);
     p.m.store(Ms, LDR);
-    if (threadIdx.x < CH) {
-      gs[threadIdx.x] = p.g;
-      if constexpr (G2) bsh[threadIdx.x] = p.b;
+    f32x4 egk[NJ];  // KDA: this chunk's per-row decay, kept before p is refilled
+    if constexpr (KDA) {
+#pragma unroll
+      for (int qq = 0; qq < NJ; ++qq) egk[qq] = p.eg[qq];
+    } else {
+      if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
+    }
+    if constexpr (G2) {
+      if (threadIdx.x < CH) bsh[threadIdx.x] = p.b;
     }
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
@@ -177,7 +200,8 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
-        S[qq][it] *= eg;
+        if constexpr (KDA) S[qq][it] *= egk[qq];
+        else S[qq][it] *= eg;
         S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Qs, LD), 16 * (w + 4 * qq), rowk(dOg, LDR), 16 * it);
         S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Xs, LD), 16 * (w + 4 * qq), rowk(dRt, LDR), 16 * it);
       }
@@ -201,27 +225,6 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
         const f32x4 x = S[qq][it];
         *reinterpret_cast<float4*>(dh0 + (sbase + i) * D + j0) = make_float4(x[0], x[1], x[2], x[3]);
       }
-  }
-}
-
-// T^T as a matrix-core A operand, read from L^{-1}: element (m = s, k = t) = Linv[t][s] beta_s.
-struct TtView {
-  const float* li;
-  int ld;
-  const float* beta;
-  __device__ __forceinline__ float at(int m, int k) const { return li[k * ld + m] * beta[m]; }
-};
-template <typename E>
-__device__ __forceinline__ typename MMA<E>::frag frag(const TtView& v, int idx0, int k0) {
-  constexpr int KPL = MMA<E>::KPL;
-  const int m = idx0 + lrow(), kk = k0 + KPL * lgrp();
-  if constexpr (KPL == 1) {
-    return (E)v.at(m, kk);
-  } else {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (bf16)v.at(m, kk + e);
-    return r;
   }
 }
 
@@ -618,21 +621,27 @@ template <typename E, int D, int VAR>
 static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht,
                            const gdr_grads& gr, hipStream_t st) {
   const Geo& g = p.geo;
+  constexpr bool KDA = VAR == VAR_KDA;
+  const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
+  const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
+  const float* gin = KDA ? p.Gn : p.G;
   {
     TraceScope ts_("bwd_scan", st);
     if (p.bv == 16) {
-      hipLaunchKernelGGL((k_bwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
-                         (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
-                         (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0, (const E*)in.beta, (const E*)in.erase);
+      hipLaunchKernelGGL((k_bwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g, qin, kin,
+                         (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dht, (E*)p.dHs, (E*)p.dR, gr.dh0,
+                         (const E*)in.beta, (const E*)in.erase);
     } else {
-      hipLaunchKernelGGL((k_bwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
-                         (const E*)in.q, (const E*)in.k, (const E*)dO, (const E*)p.X, (const E*)p.M,
-                         (const float*)p.G, dht, (E*)p.dHs, (E*)p.dR, gr.dh0, (const E*)in.beta, (const E*)in.erase);
+      hipLaunchKernelGGL((k_bwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g, qin, kin,
+                         (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dht, (E*)p.dHs, (E*)p.dR, gr.dh0,
+                         (const E*)in.beta, (const E*)in.erase);
     }
   }
   if (g.total_chunks > 0) {
     if constexpr (VAR == VAR_GDN2) {
       return launch_bwd_gdn2<E, D>(p, in, dO, gr, st);
+    } else if constexpr (VAR == VAR_KDA) {
+      return launch_bwd_kda<E, D>(p, in, dO, gr, st);
     } else {
       TraceScope ts_("bwd_chunk", st);
       hipLaunchKernelGGL((k_bwd_chunk<E, D, VAR>), dim3(g.total_chunks, g.H), dim3(512), 0, st, g,
@@ -656,6 +665,7 @@ hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, con
   switch (p.variant) {
     case GDR_DELTANET: GDR_BWD_CASE(VAR_DELTANET)
     case GDR_GATED: GDR_BWD_CASE(VAR_GATED)
+    case GDR_KDA: GDR_BWD_CASE(VAR_KDA)
     case GDR_GDN2: GDR_BWD_CASE(VAR_GDN2)
     default: break;
   }

@@ -56,6 +56,27 @@ __device__ void solve_unit_lower64(const float* L, int ldl, float* Li, int ldi, 
   }
 }
 
+// T^T as a matrix-core A operand, read from L^{-1}: element (m = s, k = t) = Linv[t][s] beta_s.
+struct TtView {
+  const float* li;
+  int ld;
+  const float* beta;
+  __device__ __forceinline__ float at(int m, int k) const { return li[k * ld + m] * beta[m]; }
+};
+template <typename E>
+__device__ __forceinline__ typename MMA<E>::frag frag(const TtView& v, int idx0, int k0) {
+  constexpr int KPL = MMA<E>::KPL;
+  const int m = idx0 + lrow(), kk = k0 + KPL * lgrp();
+  if constexpr (KPL == 1) {
+    return (E)v.at(m, kk);
+  } else {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)v.at(m, kk + e);
+    return r;
+  }
+}
+
 // Map a lower-triangle tile index (0..9) of a 4x4 tile grid to (row tile, column tile).
 __device__ __forceinline__ void tri_tile(int jj, int& mt, int& nt) {
   mt = (jj >= 1) + (jj >= 3) + (jj >= 6);

@@ -110,6 +110,39 @@ __device__ __forceinline__ f32x4 mma_k(f32x4 acc, const VA& A, int m0, const VB&
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// acc += A[m0.., k0..k0+16) * B[k0..k0+16, n0..] for one 16x16 tile: a product over exactly
+// 16 values of k (bfloat16: v_mfma_f32_16x16x16_bf16, 4 values of k per lane at
+// k0 + 4*lgrp; float32: four 16x16x4 steps).
+template <typename E, class VA, class VB>
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const VA& A, int m0, const VB& B, int n0, int k0) {
+  if constexpr (std::is_same<E, float>::value) {
+#pragma unroll
+    for (int kk = 0; kk < 16; kk += 4) acc = MMA<float>::run(frag<float>(A, m0, k0 + kk), frag<float>(B, n0, k0 + kk), acc);
+    return acc;
+  } else {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    auto f4 = [](const auto& v, int idx0, int kb) -> s16x4 {
+      using Vw = std::decay_t<decltype(v)>;
+      const int s = lrow();
+      if constexpr (std::is_same<Vw, View<bf16, true>>::value) {
+        return *reinterpret_cast<const s16x4*>(v.p + (idx0 + s) * v.ld + kb + 4 * lgrp());
+      } else if constexpr (std::is_same<Vw, View<bf16, false>>::value) {
+        // lane s of each 16-lane group addresses row kb + 4*lgrp + s/4, columns idx0 + 4*(s%4);
+        // lane i receives column idx0 + i of those four rows.
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const bf16* base = v.p + (kb + 4 * lgrp() + (s >> 2)) * v.ld + idx0 + 4 * (s & 3);
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+      } else {
+        bf16x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (bf16)v.at(idx0 + s, kb + 4 * lgrp() + e);
+        return __builtin_bit_cast(s16x4, r);
+      }
+    };
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(f4(A, m0, k0), f4(B, n0, k0), acc, 0, 0, 0);
+  }
+}
+
 // Row / column of accumulator element r of a tile at (m0, n0).
 __device__ __forceinline__ int acc_row(int m0, int r) { return m0 + 4 * lgrp() + r; }
 __device__ __forceinline__ int acc_col(int n0) { return n0 + lrow(); }

@@ -122,17 +122,25 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
 // Operands of one chunk of the forward scan, held in registers while they are in flight.
 // Gated DeltaNet-2 also needs the erase gates (for the erase direction a = beta e*k) and the
 // value tile's write gates and values (for b = beta w*v).
-template <typename E, int D, int BV, bool G2>
+// Kimi Delta Attention reads Kbar = e^{g_n-g} K (prepared per chunk) in place of K and the
+// per-key-channel decay e^{g_n} of the rows this lane holds.
+template <typename E, int D, int BV, int VAR>
 struct FwdScanOps {
   RegTile<E, CH, D, 256> x, k;
   RegTile<E, CH, BV, 256> u;
   float g;
 };
 template <typename E, int D, int BV>
-struct FwdScanOps<E, D, BV, true> {
+struct FwdScanOps<E, D, BV, VAR_GDN2> {
   RegTile<E, CH, D, 256> x, k, e;
   RegTile<E, CH, BV, 256> u, vt, wt;
   float g, b;
+};
+template <typename E, int D, int BV>
+struct FwdScanOps<E, D, BV, VAR_KDA> {
+  RegTile<E, CH, D, 256> x, k;
+  RegTile<E, CH, BV, 256> u;
+  f32x4 eg[D / 64];
 };
 
 template <typename E, int D, int BV, int VAR>
@@ -145,7 +153,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2;
-  constexpr bool DEC = VAR != VAR_DELTANET;
+  constexpr bool KDA = VAR == VAR_KDA;
+  constexpr bool DEC = VAR == VAR_GATED || VAR == VAR_GDN2;  // scalar decay
   __shared__ __align__(16) E Xs[CH * LD];
   __shared__ __align__(16) E Ks[CH * LD];
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];      // a = beta e*k (GDN-2)
@@ -181,16 +190,22 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
 
   // Chunk c + 2 is loaded while chunk c is computed (two register sets, loop unrolled by two).
   // Loads past the last chunk repeat it, so every step issues the same memory operations.
-  using Ops = FwdScanOps<E, D, BV, G2>;
+  using Ops = FwdScanOps<E, D, BV, VAR>;
   auto load = [&](Ops& p, int c) {
     const int cc = min(c, nck - 1);
     const long u = (long)(sp.gc0 + cc) * geo.H + h;
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
     p.x.load(Xg + u * CH * D, D, CH);
-    p.k.load(k + tk * D, D, n);
     p.u.load(Ug + u * CH * D + i0, D, CH);
-    p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+    if constexpr (KDA) {
+      p.k.load(k + u * CH * D, D, CH);
+#pragma unroll
+      for (int qq = 0; qq < NJ; ++qq) p.eg[qq] = *reinterpret_cast<const f32x4*>(Gg + u * D + acc_row(16 * (w + 4 * qq), 0));
+    } else {
+      p.k.load(k + tk * D, D, n);
+      p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+    }
     if constexpr (G2) {
       p.e.load(erase + tk * D, D, n);
       p.vt.load(vin + tk * D + i0, D, n);
@@ -204,9 +219,15 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
     p.x.store(Xs, LD);
     p.k.store(Ks, LD);
     p.u.store(Us, LDV);
-    if (threadIdx.x < CH) {
-      gs[threadIdx.x] = p.g;
-      if constexpr (G2) bsh[threadIdx.x] = p.b;
+    f32x4 egk[NJ];  // KDA: this chunk's per-row decay, kept before p is refilled
+    if constexpr (KDA) {
+#pragma unroll
+      for (int qq = 0; qq < NJ; ++qq) egk[qq] = p.eg[qq];
+    } else {
+      if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
+    }
+    if constexpr (G2) {
+      if (threadIdx.x < CH) bsh[threadIdx.x] = p.b;
     }
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
@@ -259,7 +280,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
-        S[qq][it] *= eg;
+        if constexpr (KDA) S[qq][it] *= egk[qq];
+        else S[qq][it] *= eg;
         if constexpr (G2) {
           // W_next = e^{g_n} W0 + R'^T (e^{g_n-g} a) + b^T (e^{g_n-g} k)
           S[qq][it] = mma_k<E, CH>(S[qq][it], colk(As, LD), 16 * (w + 4 * qq), rowk(Rd, LDR), 16 * it);
@@ -302,6 +324,7 @@ __global__ __launch_bounds__(256) void k_fwd_out(Geo geo, const E* __restrict__ 
                                                  const E* __restrict__ beta, const E* __restrict__ write) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDR = CH + pad16<E>();
   constexpr bool G2 = VAR == VAR_GDN2;
+  constexpr bool KDA = VAR == VAR_KDA;  // q is Qhat = e^g Q, prepared per chunk
   __shared__ __align__(16) E Qs[CH * LD];
   __shared__ __align__(16) E Ws[D * LD];
   __shared__ __align__(16) E Ms[CH * LDR];
@@ -314,11 +337,12 @@ __global__ __launch_bounds__(256) void k_fwd_out(Geo geo, const E* __restrict__ 
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id();
-  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, cp.n);
+  if constexpr (KDA) g2s_rows<E, CH, D, NT>(Qs, LD, q + u * CH * D, D, CH);
+  else g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, cp.n);
   g2s_rows<E, D, D, NT>(Ws, LD, Hs + u * D * D, D, D);
   g2s_rows<E, CH, CH, NT>(Ms, LDR, Mg + u * CH * CH, CH, CH);
   g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
-  if (threadIdx.x < CH) gs[threadIdx.x] = Gg[u * CH + threadIdx.x];
+  if (!KDA && threadIdx.x < CH) gs[threadIdx.x] = Gg[u * CH + threadIdx.x];
   if constexpr (G2) {
     g2s_rows<E, CH, CH, NT>(M2s, LDR, M2g + u * CH * CH, CH, CH);
     RegTile<E, CH, D, NT> rv, rw;
@@ -342,7 +366,7 @@ __global__ __launch_bounds__(256) void k_fwd_out(Geo geo, const E* __restrict__ 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float e = 1.f;
-      if constexpr (VAR != VAR_DELTANET) e = __expf(gs[acc_row(16 * w, r)]);
+      if constexpr (VAR == VAR_GATED || VAR == VAR_GDN2) e = __expf(gs[acc_row(16 * w, r)]);
       ov[nt][r] = geo.scale * (e * a1[r] + a2[r]);
     }
   }
@@ -364,28 +388,35 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, float* 
     if constexpr (VAR == VAR_GDN2) {
       const hipError_t e = launch_fwd_prep_gdn2<E, D>(p, in, st);
       if (e != hipSuccess) return e;
+    } else if constexpr (VAR == VAR_KDA) {
+      const hipError_t e = launch_fwd_prep_kda<E, D>(p, in, st);
+      if (e != hipSuccess) return e;
     } else {
       TraceScope ts_("fwd_prep", st);
       hipLaunchKernelGGL((k_fwd_prep<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k,
                          (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G);
     }
   }
+  constexpr bool KDA = VAR == VAR_KDA;
+  const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
+  const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
+  const float* gin = KDA ? p.Gn : p.G;
   {
     TraceScope ts_("fwd_scan", st);
     if (p.bv == 16) {
-      hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g,
-                         (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
-                         (E*)p.R, ht, (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
+      hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g, kin,
+                         (const E*)p.X, (const E*)p.Ub, gin, in.h0, (E*)p.Hs, (E*)p.R, ht, (const E*)in.v,
+                         (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
     } else {
-      hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g,
-                         (const E*)in.k, (const E*)p.X, (const E*)p.Ub, (const float*)p.G, in.h0, (E*)p.Hs,
-                         (E*)p.R, ht, (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
+      hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g, kin,
+                         (const E*)p.X, (const E*)p.Ub, gin, in.h0, (E*)p.Hs, (E*)p.R, ht, (const E*)in.v,
+                         (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
     }
   }
   if (want_out && g.total_chunks > 0) {
     TraceScope ts_("fwd_out", st);
-    hipLaunchKernelGGL((k_fwd_out<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)p.M,
-                       (const E*)p.R, (const float*)p.G, (const E*)p.Hs, (E*)o, (const E*)p.M2, (const E*)in.v,
+    hipLaunchKernelGGL((k_fwd_out<E, D, VAR>), cgrid, dim3(256), 0, st, g, qin, (const E*)p.M,
+                       (const E*)p.R, gin, (const E*)p.Hs, (E*)o, (const E*)p.M2, (const E*)in.v,
                        (const E*)in.beta, (const E*)in.write);
   }
   return hipGetLastError();
@@ -401,6 +432,7 @@ hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, 
   switch (p.variant) {
     case GDR_DELTANET: GDR_FWD_CASE(VAR_DELTANET)
     case GDR_GATED: GDR_FWD_CASE(VAR_GATED)
+    case GDR_KDA: GDR_FWD_CASE(VAR_KDA)
     case GDR_GDN2: GDR_FWD_CASE(VAR_GDN2)
     default: break;
   }

@@ -35,8 +35,8 @@ struct Sizes {
   int total_chunks = 0;
   int nstates = 0;
   size_t esz = 0;
-  size_t X, M, G, Hs, R, M2, U2, Ub, dHs, dR, g2;
-  size_t cache() const { return X + M + G + Hs + R + M2 + U2; }
+  size_t X, M, G, Hs, R, M2, U2, Kb, Qh, Gn, Ub, dHs, dR, g2;
+  size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Kb + Qh + Gn; }
 };
 
 // Checks the problem description and computes the buffer sizes.
@@ -77,7 +77,6 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
     return fail(GDR_ERR_UNSUPPORTED, "bf16 head size %d: only 64 and 128 are built", p->dk);
   if (p->dtype == GDR_F32 && p->dk != 64)
     return fail(GDR_ERR_UNSUPPORTED, "float32 head size %d: only 64 is built", p->dk);
-  if (p->variant == GDR_KDA) return fail(GDR_ERR_UNSUPPORTED, "variant %d is not built yet", p->variant);
   if (total_chunks > 0x7fffffffLL) return fail(GDR_ERR_UNSUPPORTED, "too many chunks");
   if ((long long)p->B * p->H * (long long)p->T * p->dk > (1LL << 40))
     return fail(GDR_ERR_UNSUPPORTED, "tensor too large");
@@ -95,11 +94,17 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   s.Ub = align_up(U * C * D * s.esz, A);
   s.dHs = align_up(U * D * D * s.esz, A);
   s.dR = align_up(U * C * D * s.esz, A);
-  const bool g2 = p->variant == GDR_GDN2;
+  const bool g2 = p->variant == GDR_GDN2, kda = p->variant == GDR_KDA;
   s.M2 = g2 ? align_up(U * C * C * s.esz, A) : 0;
   s.U2 = g2 ? align_up(U * C * D * s.esz, A) : 0;
-  // GDN-2 backward: 5 float32 64xD + 6 float32 64x64 + 4x64 float32 per unit
-  s.g2 = g2 ? align_up(U * (5 * C * D + 6 * C * C + 4 * C) * 4, A) : 0;
+  s.Kb = kda ? align_up(U * C * D * s.esz, A) : 0;
+  s.Qh = kda ? align_up(U * C * D * s.esz, A) : 0;
+  s.Gn = kda ? align_up(U * D * 4, A) : 0;
+  // float32 backward intermediates per unit -- GDN-2: 5 of 64xD, 6 of 64x64, 4x64;
+  // KDA: 4 of 64xD, 2 of 64x64, D
+  if (g2) s.g2 = align_up(U * (5 * C * D + 6 * C * C + 4 * C) * 4, A);
+  else if (kda) s.g2 = align_up(U * (4 * C * D + 2 * C * C + D) * 4, A);
+  else s.g2 = 0;
   *sz = s;
   return GDR_OK;
 }
@@ -153,12 +158,25 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws)
   pl.R = c; c += s.R;
   pl.M2 = c; c += s.M2;
   pl.U2 = c; c += s.U2;
+  pl.Kb = c; c += s.Kb;
+  pl.Qh = c; c += s.Qh;
+  pl.Gn = reinterpret_cast<float*>(c); c += s.Gn;
   char* w = ws;
   pl.Ub = w; w += s.Ub;
   pl.dHs = w; w += s.dHs;
   pl.dR = w; w += s.dR;
   float* f = reinterpret_cast<float*>(w);
   const size_t U = (size_t)s.units, C = gdr::CH, D = (size_t)p->dk;
+  {
+    float* fk = f;
+    pl.kd_dqh = fk; fk += U * C * D;
+    pl.kd_dx = fk; fk += U * C * D;
+    pl.kd_dkb = fk; fk += U * C * D;
+    pl.kd_dkh = fk; fk += U * C * D;
+    pl.kd_dm = fk; fk += U * C * C;
+    pl.kd_da = fk; fk += U * C * C;
+    pl.kd_gam = fk;
+  }
   pl.g2_dq = f; f += U * C * D;
   pl.g2_dk = f; f += U * C * D;
   pl.g2_da = f; f += U * C * D;

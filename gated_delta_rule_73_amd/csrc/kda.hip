@@ -1,0 +1,851 @@
+// Kimi Delta Attention chunk kernels: the decay alpha_t is a vector over the key channels,
+// W_t = W_{t-1} diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
+//
+// Chunk form (n <= 64 tokens from W0; g_t = in-chunk cumsum of log alpha, one value per
+// key channel j; all products below are per channel):
+//   A_ts = sum_j k_tj k_sj e^{g_tj - g_sj} (s < t),  M_ts = sum_j q_tj k_sj e^{g_tj - g_sj} (s <= t)
+//   L = I + diag(beta) A,  T = L^{-1} diag(beta),  X = T (e^g * K),  U = T V
+//   R = U - X W0^T,  O = scale ((e^g * Q) W0^T + M R),  W_next = W0 diag(e^{g_n}) + R^T (e^{g_n - g} * K)
+// The per-channel factor e^{g_t - g_s} cannot be pulled out of the sum over j, and e^{-g}
+// overflows over a chunk, so the Grams are taken in 16-token blocks with a reference token
+// between the two indices: e^{g_t - g_s} = e^{g_t - g_r} e^{g_r - g_s}.  For blocks below
+// the diagonal both factors are <= 1; a diagonal block uses its first token as reference,
+// which keeps the factors in range unless the block's decay is stronger than e^{-60} in some
+// channel -- those (rare) diagonal blocks are summed exactly, one exponential per term.
+//
+// The forward scan and output kernels are the delta family's (fwd.hip) fed with
+// Kbar = e^{g_n - g} * K and Qhat = e^g * Q from the prep kernel and a per-row decay of the
+// carried memory.  The backward is the reverse scan (bwd.hip) and three chunk stages here.
+#include "chunk.hpp"
+#include "launch.hpp"
+
+namespace gdr {
+
+namespace {
+// Largest in-block decay (natural log) for which the block-start reference is used.
+constexpr float KDA_REF_LIMIT = -60.f;
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+}  // namespace
+
+// g for JW channels (alpha points at the chunk's first token and first channel; row stride
+// rs): Gs[t*ldg + j] = sum_{u<=t} log alpha_{u,j}, rows >= n taken as log 1 = 0.
+// Every kernel calls this with the same per-column arithmetic, so all of them see the same
+// values of g.  Starts and ends with a block barrier.
+template <typename E, int JW, int NT>
+__device__ void kda_cumlog(const E* __restrict__ alpha, long rs, int n, float* Gs, int ldg) {
+  RegTile<E, CH, JW, NT> ra;
+  ra.load(alpha, rs, n);
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < decltype(ra)::IT; ++it) {
+    if (decltype(ra)::TOTAL % NT == 0 || threadIdx.x + it * NT < decltype(ra)::TOTAL) {
+      const int t = ra.row(it), j = ra.col(it);
+#pragma unroll
+      for (int x = 0; x < decltype(ra)::VE; ++x) Gs[t * ldg + j + x] = (t < n) ? logf((float)ra.elem(it, x)) : 0.f;
+    }
+  }
+  __syncthreads();
+  for (int j = wave_id(); j < JW; j += NT / 64) {
+    float* p = Gs + lane_id() * ldg + j;
+    *p = wave_incl_scan(*p);
+  }
+  __syncthreads();
+}
+
+// unsafe[b] = 1 when some channel decays by more than e^{KDA_REF_LIMIT} inside block b.
+template <int D, int NT>
+__device__ void kda_flags(const float* Gs, int ldg, int* unsafe) {
+  for (int idx = threadIdx.x; idx < 4 * D; idx += NT) {
+    const int b = idx / D, j = idx % D;
+    if (Gs[(16 * b + 15) * ldg + j] - Gs[16 * b * ldg + j] < KDA_REF_LIMIT) unsafe[b] = 1;
+  }
+  __syncthreads();
+}
+
+// The chunk's Grams.  Inputs in LDS: Ks (K), Kr = K e^{g - g_ref} and, WITH_M, Qr = Q e^{g - g_ref}
+// (ref = the first token of the row's 16-token block), Gs, unsafe flags; Cl is scratch.
+// Outputs: Ls[t][s] = lsc_t A_ts below the diagonal, optionally (Af != NULL) Af[t][s] = A_ts
+// (zero on and above the diagonal), Mo[t][s] = M_ts (global, zero above the diagonal).
+// qg: Q in global memory (token rows, used only for exact diagonal blocks).  Ends with a barrier.
+template <typename E, int D, int NT, bool WITH_M>
+__device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const float* Gs, const int* unsafe,
+                          float* Ls, const float* lsc, float* Af, E* Mo, const E* qg, int n) {
+  constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 1;
+  const int w = wave_id();
+  for (int I = 0; I < 4; ++I) {
+    const int ref = 16 * I;
+    const bool uns = unsafe[I] != 0;
+    // column operand of row block I: K_s e^{g_ref - g_s} for s < ref + 16
+    for (int idx = threadIdx.x; idx < (ref + 16) * D; idx += NT) {
+      const int s = idx / D, j = idx % D;
+      float val = 0.f;
+      if (!(uns && s >= ref)) val = (float)Ks[s * LD + j] * __expf(Gs[ref * LDG + j] - Gs[s * LDG + j]);
+      Cl[s * LD + j] = (E)val;
+    }
+    __syncthreads();
+    const int njobs = (WITH_M ? 2 : 1) * (I + 1);
+    for (int job = w; job < njobs; job += NT / 64) {
+      const bool isM = job > I;
+      const int J = isM ? job - I - 1 : job;
+      if (J == I && uns) continue;
+      const f32x4 acc = mma_k<E, D>(zero4(), rowk(isM ? Qr : Kr, LD), ref, rowk(Cl, LD), 16 * J);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = acc_row(ref, r), s = acc_col(16 * J);
+        if (isM) {
+          Mo[t * CH + s] = (E)((s <= t) ? acc[r] : 0.f);
+        } else {
+          const float a = (s < t) ? acc[r] : 0.f;
+          Ls[t * LF + s] = lsc[t] * a;
+          if (Af) Af[t * LF + s] = a;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s = idx & 63;
+    if (s > t) {
+      if (Af) Af[t * LF + s] = 0.f;
+      if constexpr (WITH_M) Mo[t * CH + s] = (E)0.f;
+    }
+  }
+  if (unsafe[0] | unsafe[1] | unsafe[2] | unsafe[3]) {
+    // exact diagonal blocks: one exponential per (t, s, j)
+    for (int idx = threadIdx.x; idx < 4 * 136; idx += NT) {
+      const int I = idx / 136;
+      if (!unsafe[I]) continue;
+      int p = idx % 136, tt = 0;
+      while (p > tt) {
+        p -= tt + 1;
+        ++tt;
+      }
+      const int t = 16 * I + tt, s = 16 * I + p;
+      float a = 0.f, m = 0.f;
+      for (int j = 0; j < D; ++j) {
+        const float e = __expf(Gs[t * LDG + j] - Gs[s * LDG + j]);
+        const float ks = (float)Ks[s * LD + j];
+        a += (float)Ks[t * LD + j] * ks * e;
+        if constexpr (WITH_M) m += (t < n ? (float)qg[(long)t * D + j] : 0.f) * ks * e;
+      }
+      if (s < t) {
+        Ls[t * LF + s] = lsc[t] * a;
+        if (Af) Af[t * LF + s] = a;
+      } else if (Af) {
+        Af[t * LF + s] = 0.f;
+      }
+      if constexpr (WITH_M) Mo[t * CH + s] = (E)m;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------
+// Forward prep: per (chunk, head).  g, Kbar, Qhat, e^{g_n}, M, L^{-1}, X, U.
+// ---------------------------------------------------------------------------------------
+template <typename E, int D>
+struct KdaPrepLds {
+  static constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 1, LDT = CH + pad16<E>();
+  static constexpr int TK = CH * LD * (int)sizeof(E), GB = CH * LDG * 4, F = CH * LF * 4;
+  // G | Kr | Cl | K (then e^g K, then X) | Q (then Qr, then V, then U) | Ls
+  static constexpr int oG = 0, oKr = GB, oCl = GB + TK, oK = GB + 2 * TK, oQ = GB + 3 * TK;
+  static constexpr int oL = GB + 4 * TK, BYTES = oL + F;
+  // after the Grams: L^{-1} (float) and T = L^{-1} diag(beta) over the G / Kr / Cl regions
+  static constexpr int oLi = 0, oT = F;
+  static_assert(F + CH * LDT * (int)sizeof(E) <= GB + 2 * TK, "L^{-1} and T must fit the freed regions");
+  static_assert(CH * LDT * (int)sizeof(E) >= 4 * 256 * 4, "T doubles as the solve's scratch");
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+                                                      const E* __restrict__ v, const E* __restrict__ beta,
+                                                      const E* __restrict__ alpha, E* __restrict__ Xo,
+                                                      E* __restrict__ Uo, E* __restrict__ Mo, E* __restrict__ Kbo,
+                                                      E* __restrict__ Qho, float* __restrict__ Gno) {
+  using Ly = KdaPrepLds<E, D>;
+  constexpr int NT = 256, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, LDT = Ly::LDT;
+  __shared__ __align__(16) char smem[Ly::BYTES];
+  __shared__ float bs[CH];
+  __shared__ int unsafe[4];
+  float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
+  E* Kr = reinterpret_cast<E*>(smem + Ly::oKr);
+  E* Cl = reinterpret_cast<E*>(smem + Ly::oCl);
+  E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
+  E* Qs = reinterpret_cast<E*>(smem + Ly::oQ);
+  float* Ls = reinterpret_cast<float*>(smem + Ly::oL);
+
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id(), n = cp.n;
+
+  RegTile<E, CH, D, NT> rv;
+  rv.load(v + tk * D, D, n);
+  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
+  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
+  if (threadIdx.x < CH) bs[threadIdx.x] = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
+  if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
+  kda_cumlog<E, D, NT>(alpha + tk * D, D, n, Gs, LDG);
+  kda_flags<D, NT>(Gs, LDG, unsafe);
+
+  // Kbar and Qhat for the scans and the output kernel, e^{g_n} per channel, and the row
+  // operands of the Grams (Q's buffer is overwritten in place by Qr).
+  E* kb = Kbo + u * CH * D;
+  E* qh = Qho + u * CH * D;
+  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
+    const int t = idx / D, j = idx % D;
+    const float g = Gs[t * LDG + j], gn = Gs[(CH - 1) * LDG + j], gb = Gs[(t & ~15) * LDG + j];
+    const float kk = (float)Ks[t * LD + j], qq = (float)Qs[t * LD + j];
+    kb[idx] = (E)(kk * __expf(gn - g));
+    qh[idx] = (E)(qq * __expf(g));
+    const float f = __expf(g - gb);
+    Kr[t * LD + j] = (E)(kk * f);
+    Qs[t * LD + j] = (E)(qq * f);
+  }
+  if (threadIdx.x < D) Gno[u * D + threadIdx.x] = __expf(Gs[(CH - 1) * LDG + threadIdx.x]);
+  __syncthreads();
+  E* Mc = Mo + u * CH * CH;
+  kda_grams<E, D, NT, true>(Ks, Qs, Kr, Cl, Gs, unsafe, Ls, bs, nullptr, Mc, q + tk * D, n);
+
+  // Khat = e^g K in place; V into the Q buffer
+  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
+    const int t = idx / D, j = idx % D;
+    Ks[t * LD + j] = (E)((float)Ks[t * LD + j] * __expf(Gs[t * LDG + j]));
+  }
+  rv.store(Qs, LD);
+  __syncthreads();
+  float* Li = reinterpret_cast<float*>(smem + Ly::oLi);
+  E* Ts = reinterpret_cast<E*>(smem + Ly::oT);
+  solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ts));
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s = idx & 63;
+    Ts[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] * bs[s] : 0.f);
+  }
+  __syncthreads();
+  f32x4 xa[D / 16], ua[D / 16];
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    xa[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Ks, LD), 16 * nt);
+    ua[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Qs, LD), 16 * nt);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    store4_n(Ks, LD, 16 * w, 16 * nt, xa[nt]);
+    store4_n(Qs, LD, 16 * w, 16 * nt, ua[nt]);
+  }
+  __syncthreads();
+  s2g_full<E, CH, D, NT>(Xo + u * CH * D, D, Ks, LD);
+  s2g_full<E, CH, D, NT>(Uo + u * CH * D, D, Qs, LD);
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward, stage 1: products with W0 and dW (dR from the reverse scan).
+//   dQhat = scale dO W0,  dX = -dR W0,  dKbar = R dW,  dM = scale tril(dO R^T),
+//   gamma_j = e^{g_nj} sum_i W0_ij dW_ij   (float32 workspace)
+// ---------------------------------------------------------------------------------------
+template <typename E, int D>
+struct KdaStateLds {
+  static constexpr int LD = D + pad16<E>(), LDR = CH + pad16<E>();
+  static constexpr int TK = CH * LD * (int)sizeof(E), TH = D * LDR * (int)sizeof(E);
+  static constexpr int BYTES = 3 * TK + 2 * TH;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restrict__ dO, const float* __restrict__ Gn,
+                                                       const E* __restrict__ Hs, const E* __restrict__ Rg,
+                                                       const E* __restrict__ dHs, const E* __restrict__ dRg, Plan p) {
+  using Ly = KdaStateLds<E, D>;
+  constexpr int NT = 512, LD = Ly::LD, LDR = Ly::LDR, KH = 64, NH = D / KH, NQ = D / 32, NP = NT / D;
+  __shared__ __align__(16) char smem[Ly::BYTES];
+  __shared__ float gpart[NP][D];
+  E* dOs = reinterpret_cast<E*>(smem);
+  E* Rs = dOs + CH * LD;
+  E* dRs = Rs + CH * LD;
+  E* Wh = dRs + CH * LD;
+  E* dWh = Wh + D * LDR;
+
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id(), wm = w & 3, wn = w >> 2, n = cp.n;
+
+  g2s_rows<E, CH, D, NT>(dOs, LD, dO + tk * D, D, n);
+  g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
+  g2s_rows<E, CH, D, NT>(dRs, LD, dRg + u * CH * D, D, CH);
+  f32x4 acc1[D / 16], dkb[NQ], mq[2];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) acc1[i] = zero4();
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) dkb[i] = zero4();
+  mq[0] = mq[1] = zero4();
+  const int gj = threadIdx.x % D, gp = threadIdx.x / D;
+  float gam = 0.f;
+  for (int ih = 0; ih < NH; ++ih) {
+    __syncthreads();
+    g2s_rows_t<E, KH, D, NT>(Wh, LDR, Hs + u * D * D + (long)ih * KH * D, D, KH);
+    g2s_rows_t<E, KH, D, NT>(dWh, LDR, dHs + u * D * D + (long)ih * KH * D, D, KH);
+    __syncthreads();
+    const E* Aop = (w < 4 ? dOs : dRs) + ih * KH;
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(Aop, LD), 16 * wm, rowk(Wh, LDR), 16 * nt);
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq)
+      dkb[qq] = mma_k<E, KH>(dkb[qq], rowk(Rs + ih * KH, LD), 16 * wm, rowk(dWh, LDR), 16 * (wn * NQ + qq));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int id = w + 8 * e;
+      mq[e] = mma_k<E, KH>(mq[e], rowk(dOs + ih * KH, LD), 16 * (id >> 2), rowk(Rs + ih * KH, LD), 16 * (id & 3));
+    }
+    for (int i = gp; i < KH; i += NP) gam += (float)Wh[gj * LDR + i] * (float)dWh[gj * LDR + i];
+  }
+  gpart[gp][gj] = gam;
+  float* dqh = p.kd_dqh + u * CH * D;
+  float* dx = p.kd_dx + u * CH * D;
+  float* dk1 = p.kd_dkb + u * CH * D;
+  float* dm = p.kd_dm + u * CH * CH;
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * wm, r), j = acc_col(16 * nt);
+      if (w < 4) dqh[t * D + j] = geo.scale * acc1[nt][r];
+      else dx[t * D + j] = -acc1[nt][r];
+    }
+#pragma unroll
+  for (int qq = 0; qq < NQ; ++qq)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dk1[acc_row(16 * wm, r) * D + acc_col(16 * (wn * NQ + qq))] = dkb[qq][r];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
+      dm[t * CH + s] = (s <= t) ? geo.scale * mq[e][r] : 0.f;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) s += gpart[i][threadIdx.x];
+    p.kd_gam[u * D + threadIdx.x] = Gn[u * D + threadIdx.x] * s;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward, stage 2: the solve side.  Recomputes g, A and L^{-1}; then
+//   dT = dR V^T + dX Khat^T,  dV = T^T dR,  dKhat = T^T dX,  dbeta_s = sum_t dT_ts Linv_ts,
+//   dL = -strictlower(L^-T (dT diag beta) L^-T),  dbeta_t += sum_s dL_ts A_ts,  dA = diag(beta) dL.
+// ---------------------------------------------------------------------------------------
+template <typename E, int D>
+struct KdaWyLds {
+  static constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 1;
+  static constexpr int TK = CH * LD * (int)sizeof(E), GB = CH * LDG * 4, F = CH * LF * 4;
+  // region 1: G | Kr | Cl during the Grams, then L^{-1} | dT | V | dR
+  static constexpr int R1 = cmax(GB + 2 * TK, 2 * F + 2 * TK);
+  static constexpr int oG = 0, oKr = GB, oCl = GB + TK;
+  static constexpr int oLi = 0, odT = F, oV = 2 * F, odR = 2 * F + TK;
+  static constexpr int oK = R1, oL = R1 + TK, oA = oL + F, odX = oA + F, BYTES = odX + TK;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
+                                                    const E* __restrict__ beta, const E* __restrict__ alpha,
+                                                    const E* __restrict__ dRg, E* __restrict__ dv,
+                                                    E* __restrict__ dbeta, Plan p) {
+  using Ly = KdaWyLds<E, D>;
+  constexpr int NT = 256, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF;
+  __shared__ __align__(16) char smem[Ly::BYTES];
+  __shared__ __align__(16) float scr[4 * 256];
+  __shared__ float bs[CH], dbs[CH];
+  __shared__ int unsafe[4];
+  float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
+  E* Kr = reinterpret_cast<E*>(smem + Ly::oKr);
+  E* Cl = reinterpret_cast<E*>(smem + Ly::oCl);
+  E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
+  float* Ls = reinterpret_cast<float*>(smem + Ly::oL);
+  float* Af = reinterpret_cast<float*>(smem + Ly::oA);
+  E* dXs = reinterpret_cast<E*>(smem + Ly::odX);
+
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id(), n = cp.n;
+
+  RegTile<E, CH, D, NT> rv, rdr;
+  RegTile<float, CH, D, NT> rdx;
+  rv.load(v + tk * D, D, n);
+  rdr.load(dRg + u * CH * D, D, CH);
+  rdx.load(p.kd_dx + u * CH * D, D, CH);
+  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
+  if (threadIdx.x < CH) bs[threadIdx.x] = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
+  if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
+  kda_cumlog<E, D, NT>(alpha + tk * D, D, n, Gs, LDG);
+  kda_flags<D, NT>(Gs, LDG, unsafe);
+  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
+    const int t = idx / D, j = idx % D;
+    Kr[t * LD + j] = (E)((float)Ks[t * LD + j] * __expf(Gs[t * LDG + j] - Gs[(t & ~15) * LDG + j]));
+  }
+  __syncthreads();
+  kda_grams<E, D, NT, false>(Ks, nullptr, Kr, Cl, Gs, unsafe, Ls, bs, Af, nullptr, nullptr, n);
+  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
+    const int t = idx / D, j = idx % D;
+    Ks[t * LD + j] = (E)((float)Ks[t * LD + j] * __expf(Gs[t * LDG + j]));
+  }
+#pragma unroll
+  for (int it = 0; it < decltype(rdx)::IT; ++it) {
+    if (decltype(rdx)::TOTAL % NT == 0 || threadIdx.x + it * NT < decltype(rdx)::TOTAL) {
+      const int t = rdx.row(it), j = rdx.col(it);
+#pragma unroll
+      for (int x = 0; x < decltype(rdx)::VE; ++x) dXs[t * LD + j + x] = (E)rdx.elem(it, x);
+    }
+  }
+  __syncthreads();  // G, Kr, Cl are free from here on
+  float* Li = reinterpret_cast<float*>(smem + Ly::oLi);
+  float* dTs = reinterpret_cast<float*>(smem + Ly::odT);
+  E* Vs = reinterpret_cast<E*>(smem + Ly::oV);
+  E* dRs = reinterpret_cast<E*>(smem + Ly::odR);
+  rv.store(Vs, LD);
+  rdr.store(dRs, LD);
+  solve_unit_lower64<NT>(Ls, LF, Li, LF, scr);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
+    const f32x4 a = mma_k<E, D>(zero4(), rowk(dRs, LD), 16 * mt, rowk(Vs, LD), 16 * nt);
+    const f32x4 b = mma_k<E, D>(zero4(), rowk(dXs, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
+      dTs[t * LF + s] = (s <= t) ? a[r] + b[r] : 0.f;
+    }
+  }
+  const TtView Tt{Li, LF, bs};
+  f32x4 dva[D / 16];
+  {
+    float* dkh = p.kd_dkh + u * CH * D;
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      dva[nt] = mma_k<E, CH>(zero4(), Tt, 16 * w, colk(dRs, LD), 16 * nt);
+      const f32x4 kh = mma_k<E, CH>(zero4(), Tt, 16 * w, colk(dXs, LD), 16 * nt);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dkh[acc_row(16 * w, r) * D + acc_col(16 * nt)] = kh[r];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) store4_n(Vs, LD, 16 * w, 16 * nt, dva[nt]);
+  if (threadIdx.x < CH) {  // dbeta from T = Linv diag(beta)
+    const int s = threadIdx.x;
+    float a = 0.f;
+#pragma unroll 16
+    for (int t = 0; t < CH; ++t) a += dTs[t * LF + s] * Li[t * LF + s];
+    dbs[s] = a;
+  }
+  __syncthreads();
+  s2g_rows<E, CH, D, NT>(dv + tk * D, D, Vs, LD, n);
+  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+    const int t = idx >> 6, s = idx & 63;
+    dTs[t * LF + s] *= bs[s];  // gradient w.r.t. Linv
+  }
+  __syncthreads();
+  float* Pt = Ls;  // L is no longer needed
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
+    const f32x4 acc = mma_k<E, CH>(zero4(), rowk(dTs, LF), 16 * mt, rowk(Li, LF), 16 * nt);
+    store4_t(Pt, LF, 16 * mt, 16 * nt, acc);
+  }
+  __syncthreads();
+  f32x4 dl[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
+    const f32x4 acc = mma_k<E, CH>(zero4(), colk(Li, LF), 16 * mt, rowk(Pt, LF), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[e][r] = (acc_col(16 * nt) < acc_row(16 * mt, r)) ? -acc[r] : 0.f;
+  }
+  __syncthreads();
+  float* da = p.kd_da + u * CH * CH;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
+    store4_n(dTs, LF, 16 * mt, 16 * nt, dl[e]);  // dTs now holds dL
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * mt, r);
+      da[t * CH + acc_col(16 * nt)] = bs[t] * dl[e][r];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < CH) {  // dbeta from L = I + diag(beta) A
+    const int t = threadIdx.x;
+    float a = 0.f;
+#pragma unroll 16
+    for (int s = 0; s < CH; ++s) a += dTs[t * LF + s] * Af[t * LF + s];
+    if (t < n) dbeta[tk + t] = (E)(dbs[t] + a);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward, stage 3: per (chunk, head, 64 key channels).  The Gram slots
+//   dk_s += sum_{t>s} dA_ts k_t e^{g_t-g_s} + sum_{t<s} dA_st k_t e^{g_s-g_t} + sum_{t>=s} dM_ts q_t e^{g_t-g_s}
+//   dq_t += sum_{s<=t} dM_ts k_s e^{g_t-g_s}
+// and d log alpha_t, the sum of every term whose decay factor spans token t:
+//   sum_{s<t<=u} (dA_us k_u + dM_us q_u) k_s e^{g_u-g_s}
+//   + sum_{u>=t} (q_u e^{g_u} dQhat_u + k_u e^{g_u} dKhat_u) + sum_{s<t} k_s e^{g_n-g_s} dKbar_s + gamma
+// all as direct sums (no differences of running sums), so dalpha = d log alpha / alpha stays
+// accurate for strongly decaying channels.  The 64 tokens form four 16-token blocks; wave b
+// owns block b.  Pairs (u, s) in different blocks go through matrix-core products with
+// reference tokens at block boundaries (factors <= 1); the pairs' contribution to d log alpha
+// is assembled from those products' rows, block sums and block-pair totals.  Pairs inside a
+// block use the block's first token as reference for dk and dq (matrix cores) and one lane
+// per channel for their d log alpha terms; a block whose decay is too strong for that
+// reference is summed exactly instead, one exponential per term.
+// ---------------------------------------------------------------------------------------
+template <typename E>
+struct KdaGramLds {
+  static constexpr int JW = 64, LDJ = JW + pad16<E>(), LDT = CH + pad16<E>(), LDF = JW + 1;
+  static constexpr int GB = CH * LDF * 4, TJ = CH * LDJ * (int)sizeof(E), SQ = CH * LDT * (int)sizeof(E);
+  static constexpr int ST = CH * LDF * 4;
+  static constexpr int oG = 0, oK = GB, oQ = GB + TJ, oX = GB + 2 * TJ;
+  // region X: dA | dM | Kend (48 rows) | Kf | Qf | Krf, later two float staging arrays
+  static constexpr int odA = oX, odM = oX + SQ, oKe = oX + 2 * SQ, oKf = oKe + 48 * LDJ * (int)sizeof(E);
+  static constexpr int oQf = oKf + TJ, oKrf = oQf + TJ, endOps = oKrf + TJ;
+  static constexpr int oS1 = oX, oS2 = oX + ST;
+  static constexpr int BYTES = cmax(endOps, oX + 2 * ST);
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+                                                      const E* __restrict__ alpha, E* __restrict__ dq,
+                                                      E* __restrict__ dk, E* __restrict__ dalpha, Plan p) {
+  using Ly = KdaGramLds<E>;
+  constexpr int NT = 256, JW = Ly::JW, LDJ = Ly::LDJ, LDT = Ly::LDT, LDF = Ly::LDF, NC = JW / 16;
+  __shared__ __align__(16) char smem[Ly::BYTES];
+  __shared__ float c1s[3][JW], tota[4][JW], totc[4][JW];
+  __shared__ int unsafe[4];
+  float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
+  E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
+  E* Qs = reinterpret_cast<E*>(smem + Ly::oQ);
+  E* dAs = reinterpret_cast<E*>(smem + Ly::odA);
+  E* dMs = reinterpret_cast<E*>(smem + Ly::odM);
+  E* Ke = reinterpret_cast<E*>(smem + Ly::oKe);
+  E* Kf = reinterpret_cast<E*>(smem + Ly::oKf);
+  E* Qf = reinterpret_cast<E*>(smem + Ly::oQf);
+  E* Krf = reinterpret_cast<E*>(smem + Ly::oKrf);
+  float* S1 = reinterpret_cast<float*>(smem + Ly::oS1);
+  float* S2 = reinterpret_cast<float*>(smem + Ly::oS2);
+
+  const int gc = blockIdx.x, h = blockIdx.y, j0 = blockIdx.z * JW;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int w = wave_id(), l = lane_id(), n = cp.n;
+  const int b = w;  // this wave's 16-token block
+
+  g2s_rows<E, CH, JW, NT>(Ks, LDJ, k + tk * D + j0, D, n);
+  g2s_rows<E, CH, JW, NT>(Qs, LDJ, q + tk * D + j0, D, n);
+  {
+    const float* da = p.kd_da + u * CH * CH;
+    const float* dm = p.kd_dm + u * CH * CH;
+    for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
+      const int t = idx >> 6, s = idx & 63;
+      dAs[t * LDT + s] = (E)da[idx];
+      dMs[t * LDT + s] = (E)dm[idx];
+    }
+  }
+  if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
+  kda_cumlog<E, JW, NT>(alpha + tk * D + j0, D, n, Gs, LDF);
+  kda_flags<JW, NT>(Gs, LDF, unsafe);
+  // Kend_s = k_s e^{g_{16(J+1)} - g_s} (s in block J < 3);  Kf_u, Qf_u = (k_u, q_u) e^{g_u - g_{16I}}
+  // (u in block I);  Krf_s = k_s e^{g_{16I} - g_s} (zero in blocks summed exactly)
+  for (int idx = threadIdx.x; idx < CH * JW; idx += NT) {
+    const int s = idx / JW, j = idx % JW, r0 = s & ~15;
+    const float gs_ = Gs[s * LDF + j], g0 = Gs[r0 * LDF + j];
+    const float kv = (float)Ks[s * LDJ + j];
+    if (s < 48) Ke[s * LDJ + j] = (E)(kv * __expf(Gs[(r0 + 16) * LDF + j] - gs_));
+    const float f = __expf(gs_ - g0);
+    Kf[s * LDJ + j] = (E)(kv * f);
+    Qf[s * LDJ + j] = (E)((float)Qs[s * LDJ + j] * f);
+    Krf[s * LDJ + j] = (E)(unsafe[s >> 4] ? 0.f : kv * __expf(g0 - gs_));
+  }
+  __syncthreads();
+  const bool exact = unsafe[b] != 0;  // wave-uniform
+
+  // ---- pairs inside block b, channel j0 + l: one lane per channel
+  float n4[16], dkd[16], dqd[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) n4[i] = dkd[i] = dqd[i] = 0.f;
+  {
+    const E* dAb = dAs + 16 * b * LDT + 16 * b;
+    const E* dMb = dMs + 16 * b * LDT + 16 * b;
+    const float* gcol = Gs + 16 * b * LDF + l;
+    const E* kcol = Ks + 16 * b * LDJ + l;
+    const E* qcol = Qs + 16 * b * LDJ + l;
+    if (!exact) {
+      // d log alpha terms only: sum_{s<t<=u} c_us y_s with c_us = dA_us kF_u + dM_us qF_u,
+      // y_s = k_s e^{g_b - g_s}, kF_u = k_u e^{g_u - g_b} (b = the block's first token)
+      float kf[16], qf[16], y[16];
+      const float g0 = gcol[0];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float gi = gcol[i * LDF], kv = (float)kcol[i * LDJ];
+        const float f = __expf(gi - g0);
+        kf[i] = kv * f;
+        qf[i] = (float)qcol[i * LDJ] * f;
+        y[i] = kv * __expf(g0 - gi);
+      }
+#pragma unroll
+      for (int uu = 1; uu < 16; ++uu) {
+        float run = 0.f;
+#pragma unroll
+        for (int s = 0; s < uu; ++s) {
+          const float c = fmaf((float)dMb[uu * LDT + s], qf[uu], (float)dAb[uu * LDT + s] * kf[uu]);
+          run = fmaf(c, y[s], run);
+          n4[s + 1] += run;
+        }
+      }
+    } else {
+      // exact: one exponential per pair; also the pairs' dk and dq
+      float kk[16], gg[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        kk[i] = (float)kcol[i * LDJ];
+        gg[i] = gcol[i * LDF];
+      }
+#pragma unroll 1
+      for (int uu = 0; uu < 16; ++uu) {
+        const float guu = gcol[uu * LDF], kuu = (float)kcol[uu * LDJ], quu = (float)qcol[uu * LDJ];
+        float run = 0.f, ak = 0.f, aq = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          const bool m = s < uu;
+          const float e = m ? __expf(guu - gg[s]) : 0.f;
+          const float da = m ? (float)dAb[uu * LDT + s] : 0.f, dm = m ? (float)dMb[uu * LDT + s] : 0.f;
+          const float ce = (da * kuu + dm * quu) * e;
+          dkd[s] += ce;
+          const float ke = kk[s] * e;
+          ak += da * ke;
+          aq += dm * ke;
+          run += ce * kk[s];
+          if (s < 15 && m) n4[s + 1] += run;
+        }
+        const float dmd = (float)dMb[uu * LDT + uu];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (i == uu) {
+            dkd[i] += ak + dmd * quu;
+            dqd[i] += aq + dmd * kuu;
+          }
+        }
+      }
+    }
+  }
+
+  // ---- matrix-core part (wave b owns the output rows of block b).  Accumulated per element:
+  // dkacc, dqacc: every dk / dq term from these products;  y2 = k * (dk lower, other blocks)
+  // + q * (dq, other blocks): block-suffix terms;  x3 = k * (dk upper, other blocks): block-prefix terms.
+  f32x4 dkacc[NC], dqacc[NC], y2[NC], x3[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) dkacc[c] = dqacc[c] = y2[c] = x3[c] = zero4();
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int j = acc_col(16 * c);
+    float kv[4], qv[4], gv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int uu = acc_row(16 * b, r);
+      kv[r] = (float)Ks[uu * LDJ + j];
+      qv[r] = (float)Qs[uu * LDJ + j];
+      gv[r] = Gs[uu * LDF + j];
+    }
+#pragma unroll
+    for (int J = 0; J < 3; ++J) {
+      if (J < b) {  // lower: u in block b, s in block J
+        const f32x4 pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Ke, LDJ), 16 * c, 16 * J);
+        const f32x4 pm = mma16<E>(zero4(), rowk(dMs, LDT), 16 * b, colk(Ke, LDJ), 16 * c, 16 * J);
+        const float gref = Gs[16 * (J + 1) * LDF + j];
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float f = __expf(gv[r] - gref);
+          const float a = f * pa[r], m = f * pm[r];
+          dkacc[c][r] += a;
+          dqacc[c][r] += m;
+          const float pr = kv[r] * a + qv[r] * m;
+          y2[c][r] += pr;
+          ps += pr;
+        }
+        // the pair (b, J)'s total, needed by the blocks strictly between J and b
+        if ((b == 2 && J == 0) || b == 3) {
+          ps += __shfl_xor(ps, 16, 64);
+          ps += __shfl_xor(ps, 32, 64);
+          if (l < 16) c1s[(b == 2) ? 0 : 1 + J][j] = ps;
+        }
+      }
+    }
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+      if (I > b) {  // upper: s in block b, u in block I
+        f32x4 ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * I);
+        ua = mma16<E>(ua, colk(dMs, LDT), 16 * b, colk(Qf, LDJ), 16 * c, 16 * I);
+        const float gref = Gs[16 * I * LDF + j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = __expf(gref - gv[r]) * ua[r];
+          dkacc[c][r] += x;
+          x3[c][r] += kv[r] * x;
+        }
+      }
+    }
+    if (!exact) {  // pairs inside block b, first token of the block as reference
+      const f32x4 pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Krf, LDJ), 16 * c, 16 * b);
+      const f32x4 pm = mma16<E>(zero4(), rowk(dMs, LDT), 16 * b, colk(Krf, LDJ), 16 * c, 16 * b);
+      f32x4 ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * b);
+      ua = mma16<E>(ua, colk(dMs, LDT), 16 * b, colk(Qf, LDJ), 16 * c, 16 * b);
+      const float g0 = Gs[16 * b * LDF + j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = __expf(gv[r] - g0), rf = __expf(g0 - gv[r]);
+        dkacc[c][r] += f * pa[r] + rf * ua[r];
+        dqacc[c][r] += f * pm[r];
+      }
+    }
+  }
+  __syncthreads();  // region X becomes the staging area
+  if (exact) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      S1[(16 * b + i) * LDF + l] = dkd[i];
+      S2[(16 * b + i) * LDF + l] = dqd[i];
+    }
+  }
+  __syncthreads();
+
+  // ---- dq, dk, and the per-row terms of d log alpha (matrix-core layout)
+  const float* dqh = p.kd_dqh + u * CH * D;
+  const float* dkh = p.kd_dkh + u * CH * D;
+  const float* dkb = p.kd_dkb + u * CH * D;
+  float pa_[NC], pc_[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int j = acc_col(16 * c), jg = j0 + j;
+    const float gn = Gs[(CH - 1) * LDF + j];
+    float sa = 0.f, sc = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int uu = acc_row(16 * b, r);
+      const float g = Gs[uu * LDF + j], eg = __expf(g), egb = __expf(gn - g);
+      const float kv = (float)Ks[uu * LDJ + j], qv = (float)Qs[uu * LDJ + j];
+      const long o = (long)uu * D + jg;
+      const float xq = eg * dqh[o], xk = eg * dkh[o], xb = egb * dkb[o];
+      float dkv = dkacc[c][r] + xk + xb, dqv = dqacc[c][r] + xq;
+      if (exact) {
+        dkv += S1[uu * LDF + j];
+        dqv += S2[uu * LDF + j];
+      }
+      if (uu < n) {
+        dk[(tk + uu) * D + jg] = (E)dkv;
+        dq[(tk + uu) * D + jg] = (E)dqv;
+      }
+      const float a = qv * xq + kv * xk, cc = kv * xb;
+      y2[c][r] += a;
+      x3[c][r] += cc;
+      sa += a;
+      sc += cc;
+    }
+    sa += __shfl_xor(sa, 16, 64);
+    sa += __shfl_xor(sa, 32, 64);
+    sc += __shfl_xor(sc, 16, 64);
+    sc += __shfl_xor(sc, 32, 64);
+    pa_[c] = sa;
+    pc_[c] = sc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    store4_n(S1, LDF, 16 * b, 16 * c, y2[c]);
+    store4_n(S2, LDF, 16 * b, 16 * c, x3[c]);
+    if (l < 16) {
+      tota[b][16 * c + l] = pa_[c];
+      totc[b][16 * c + l] = pc_[c];
+    }
+  }
+  __syncthreads();
+
+  // ---- d log alpha, channel layout
+  {
+    float cross = p.kd_gam[u * D + j0 + l];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      if (bb > b) cross += tota[bb][l];
+      if (bb < b) cross += totc[bb][l];
+    }
+    if (b == 1) cross += c1s[0][l] + c1s[1][l];
+    if (b == 2) cross += c1s[1][l] + c1s[2][l];
+    float suf[16];
+    float run = 0.f;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {
+      run += S1[(16 * b + i) * LDF + l];
+      suf[i] = run;
+    }
+    run = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = 16 * b + i;
+      const float dla = n4[i] + suf[i] + run + cross;
+      run += S2[t * LDF + l];
+      if (t < n) {
+        const long o = (tk + t) * D + j0 + l;
+        dalpha[o] = (E)(dla / (float)alpha[o]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------------------
+template <typename E, int D>
+hipError_t launch_fwd_prep_kda(const Plan& p, const gdr_inputs& in, hipStream_t st) {
+  TraceScope ts_("fwd_prep_kda", st);
+  hipLaunchKernelGGL((k_fwd_prep_kda<E, D>), dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo,
+                     (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
+                     (E*)p.X, (E*)p.Ub, (E*)p.M, (E*)p.Kb, (E*)p.Qh, p.Gn);
+  return hipGetLastError();
+}
+template hipError_t launch_fwd_prep_kda<bf16, 128>(const Plan&, const gdr_inputs&, hipStream_t);
+template hipError_t launch_fwd_prep_kda<bf16, 64>(const Plan&, const gdr_inputs&, hipStream_t);
+template hipError_t launch_fwd_prep_kda<float, 64>(const Plan&, const gdr_inputs&, hipStream_t);
+
+template <typename E, int D>
+hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr, hipStream_t st) {
+  const dim3 grid(p.geo.total_chunks, p.geo.H);
+  {
+    TraceScope ts_("bwd_kda_state", st);
+    hipLaunchKernelGGL((k_bwd_kda_state<E, D>), grid, dim3(512), 0, st, p.geo, (const E*)dO, (const float*)p.Gn,
+                       (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR, p);
+  }
+  {
+    TraceScope ts_("bwd_kda_wy", st);
+    hipLaunchKernelGGL((k_bwd_kda_wy<E, D>), grid, dim3(256), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
+                       (const E*)in.beta, (const E*)in.alpha, (const E*)p.dR, (E*)gr.dv, (E*)gr.dbeta, p);
+  }
+  {
+    TraceScope ts_("bwd_kda_gram", st);
+    hipLaunchKernelGGL((k_bwd_kda_gram<E, D>), dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(256), 0, st, p.geo,
+                       (const E*)in.q, (const E*)in.k, (const E*)in.alpha, (E*)gr.dq, (E*)gr.dk, (E*)gr.dalpha, p);
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_bwd_kda<bf16, 128>(const Plan&, const gdr_inputs&, const void*, const gdr_grads&, hipStream_t);
+template hipError_t launch_bwd_kda<bf16, 64>(const Plan&, const gdr_inputs&, const void*, const gdr_grads&, hipStream_t);
+template hipError_t launch_bwd_kda<float, 64>(const Plan&, const gdr_inputs&, const void*, const gdr_grads&, hipStream_t);
+
+}  // namespace gdr

@@ -21,6 +21,9 @@ struct Plan {
   void* R;    // [units][64][D]  scaled residuals R = U - X W0^T
   void* M2;   // Gated DeltaNet-2: [units][64][64] decayed causal Q K^T (M holds Q A^T)
   void* U2;   // Gated DeltaNet-2: [units][64][D]  -L^{-1} A_kk B
+  void* Kb;   // Kimi Delta Attention: [units][64][D] Kbar = e^{g_n - g} K
+  void* Qh;   // Kimi Delta Attention: [units][64][D] Qhat = e^g Q
+  float* Gn;  // Kimi Delta Attention: [units][D]     e^{g_n} per key channel
   // workspace only
   void* Ub;   // [units][64][D]  WY factor U = T V
   void* dHs;  // [units][D][D]   gradient w.r.t. the memory at the end of each chunk
@@ -31,6 +34,10 @@ struct Plan {
   float *g2_dq, *g2_dk, *g2_da, *g2_db, *g2_dx;
   float *g2_dakk, *g2_daak, *g2_dmqk, *g2_dmqa, *g2_akk, *g2_aak;
   float* g2_rows;  // [units][4][64]: prefix-type sums, Khat.dKhat, dbeta from b, gamma term
+  // Kimi Delta Attention backward intermediates (float32, the same workspace region): per unit
+  // 64 x D gradients w.r.t. Qhat, X, Kbar, Khat; 64 x 64 gradients w.r.t. M and A; D values
+  // e^{g_n} <W0, dW> per key channel.
+  float *kd_dqh, *kd_dx, *kd_dkb, *kd_dkh, *kd_dm, *kd_da, *kd_gam;
 };
 
 // Optional per-launch event recording (see gdr_trace_launches in gdr.h).
@@ -65,6 +72,10 @@ template <typename E, int D>
 hipError_t launch_fwd_prep_gdn2(const Plan& p, const gdr_inputs& in, hipStream_t st);
 template <typename E, int D>
 hipError_t launch_bwd_gdn2(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr, hipStream_t st);
+template <typename E, int D>
+hipError_t launch_fwd_prep_kda(const Plan& p, const gdr_inputs& in, hipStream_t st);
+template <typename E, int D>
+hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr, hipStream_t st);
 
 hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st);
 hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht, const gdr_grads& gr,

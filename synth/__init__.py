@@ -117,6 +117,7 @@ def make_inputs(w: Workload, *, alpha_mode: str = "config", with_grad: Optional[
 
     alpha_mode: "config" -> alpha = exp(-softplus(N(0,1) + 2)) (the workloads' law);
                 "weak"   -> alpha = exp(-softplus(N(0,1) - 5)) (about 0.99: long memory);
+                "strong" -> alpha = exp(-softplus(N(0,1) + 6)) (about 0.0025: memory of a few tokens);
                 "one"    -> alpha = 1 exactly.
     Returns a dict of float32 arrays: q, k [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T] or None;
     alpha [B,H,T] (scalar decay) or [B,H,T,dk] (per-channel decay) or None; erase [B,H,T,dk];
@@ -139,7 +140,7 @@ def make_inputs(w: Workload, *, alpha_mode: str = "config", with_grad: Optional[
         if alpha_mode == "one":
             out["alpha"] = np.ones(shape, np.float32)
         else:
-            shift = {"config": 2.0, "weak": -5.0}[alpha_mode]
+            shift = {"config": 2.0, "weak": -5.0, "strong": 6.0}[alpha_mode]
             out["alpha"] = to_io(np.exp(-_softplus(rng.standard_normal(shape) + shift)), w.dtype)
     if w.variant == "gdn2":
         out["erase"] = to_io(_sigmoid(rng.standard_normal((B, H, T, dk))), w.dtype)

@@ -135,3 +135,49 @@ def test_gdn2_varlen_saved_vs_recomputed():
     for name in ("o", "dq", "dk", "dv", "dalpha", "derase", "dwrite", "dh0"):
         assert np.array_equal(a[name], b[name]), name
     compare(a, run_oracle(inp, "gdn2", backward=True), "bf16")
+
+
+@pytest.mark.parametrize("alpha_mode", ["config", "weak", "strong"])
+def test_kda_bf16_small(alpha_mode):
+    """Kimi Delta Attention: decay per key channel.  "strong" decays by more than e^-60 within
+    16 tokens, so every diagonal block takes the exact path."""
+    w = synth.Workload("t", "kda", "bf16", 2, 2, 190, 128, 128, seed=31, h0_std=0.5)
+    inp = synth.make_inputs(w, alpha_mode=alpha_mode)
+    dht = np.random.default_rng(8).standard_normal((2, 2, 128, 128)).astype(np.float32) * 0.2
+    rep = []
+    compare(run_hip(inp, "kda", "bf16", backward=True, dht=dht, scale=0.8),
+            run_oracle(inp, "kda", backward=True, dht=dht, scale=0.8), "bf16", report=rep)
+    print("\n".join(rep))
+
+
+@pytest.mark.parametrize("dtype,alpha_mode", [("bf16", "config"), ("f32", "config"), ("f32", "weak"),
+                                              ("f32", "strong")])
+def test_kda_small_heads(dtype, alpha_mode):
+    w = synth.Workload("t", "kda", dtype, 1, 3, 150, 64, 64, seed=32, h0_std=0.3)
+    inp = synth.make_inputs(w, alpha_mode=alpha_mode)
+    rep = []
+    compare(run_hip(inp, "kda", dtype, backward=True), run_oracle(inp, "kda", backward=True), dtype, report=rep)
+    print("\n".join(rep))
+
+
+def test_kda_mixed_decay_channels():
+    """A quarter of the key channels decay strongly: exact diagonal blocks sit next to
+    blocks that use the block-start reference, in the same chunk."""
+    w = synth.Workload("t", "kda", "f32", 1, 2, 130, 64, 64, seed=33, h0_std=0.3)
+    inp = synth.make_inputs(w, alpha_mode="config")
+    strong = synth.make_inputs(w, alpha_mode="strong")
+    inp["alpha"][..., :16] = strong["alpha"][..., :16]
+    rep = []
+    compare(run_hip(inp, "kda", "f32", backward=True), run_oracle(inp, "kda", backward=True), "f32", report=rep)
+    print("\n".join(rep))
+
+
+def test_kda_varlen_saved_vs_recomputed():
+    cu = (0, 70, 71, 200)
+    w = synth.Workload("t", "kda", "bf16", 1, 2, 200, 128, 128, seed=34, cu_seqlens=cu, h0_std=0.4)
+    inp = synth.make_inputs(w, alpha_mode="weak")
+    a = run_hip(inp, "kda", "bf16", backward=True, use_saved=True)
+    b = run_hip(inp, "kda", "bf16", backward=True, use_saved=False)
+    for name in ("o", "dq", "dk", "dv", "dbeta", "dalpha", "dh0"):
+        assert np.array_equal(a[name], b[name]), name
+    compare(a, run_oracle(inp, "kda", backward=True), "bf16")
