@@ -33,25 +33,45 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 COPY_CAL_BYTES = 256 << 20   # size of the calibration copy (read + write of this many bytes)
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, published
 
-# Bytes each kernel must read and write once per (chunk, head) unit for d = 128, bf16 I/O,
-# C = 64 tokens (see the design notes: its inputs and outputs, each touched once).
-D_, C_, ESZ = 128, 64, 2
-TOK = C_ * D_ * ESZ          # one 64 x 128 token tile
-SQR = D_ * D_ * ESZ          # one 128 x 128 memory
-GRAM = C_ * C_ * ESZ         # one 64 x 64 chunk matrix
-GATE = C_ * ESZ              # one gate vector of the chunk
-GLOG = C_ * 4                # in-chunk log decay (float32)
-KERNEL_BYTES_PER_UNIT = {
-    "fwd_prep": 3 * TOK + 2 * GATE + 2 * TOK + GRAM + GLOG,
-    "fwd_scan": 3 * TOK + GLOG + SQR + TOK,
-    "fwd_out": TOK + GRAM + TOK + SQR + GLOG + TOK,
-    "bwd_scan": 3 * TOK + TOK + GRAM + GLOG + SQR + TOK,
-    "bwd_chunk": 4 * TOK + 2 * GATE + GRAM + GLOG + SQR + TOK + SQR + TOK + 3 * TOK + 2 * GATE,
-}
-# The operator's own minimum per head-token (Gated, d = 128, bf16): forward reads q, k, v,
-# beta, alpha and writes o; backward reads q, k, v, dO, beta, alpha and writes dq, dk, dv,
-# dbeta, dalpha.
-PATH_BYTES_PER_HEAD_TOKEN = (3 * 256 + 4 + 256) + (4 * 256 + 4 + 3 * 256 + 4)
+def kernel_bytes_per_unit(variant: str, kernel: str, D: int = 128, esz: int = 2, has_beta: bool = True) -> int:
+    """Bytes a kernel must read and write once per (chunk, head) unit: its inputs and outputs,
+    each touched once (C = 64 tokens, head size D, I/O element size esz).  The per-chunk
+    intermediates the kernels hand to each other (X, U, M, R, memories, float32 partial
+    gradients) are inputs and outputs of the kernels that use them."""
+    C = 64
+    TOK, SQR, GRAM, GATE = C * D * esz, D * D * esz, C * C * esz, C * esz
+    GLOG, FTOK, FGRAM, FD = C * 4, C * D * 4, C * C * 4, D * 4
+    kda, g2 = variant == "kda", variant == "gdn2"
+    ALPHA = 0 if variant == "deltanet" else (TOK if kda else GATE)
+    BETA = GATE if has_beta else 0
+    DEC = FD if kda else GLOG  # per-chunk decay handed to the scans
+    table = {
+        "fwd_prep": 3 * TOK + BETA + ALPHA + 2 * TOK + GRAM + GLOG,
+        "fwd_prep_kda": 3 * TOK + BETA + ALPHA + 4 * TOK + GRAM + FD,
+        "fwd_prep_gdn2": 5 * TOK + BETA + ALPHA + 3 * TOK + 2 * GRAM + GLOG,
+        "fwd_scan": (6 * TOK + BETA if g2 else 3 * TOK) + DEC + SQR + TOK,
+        "fwd_out": TOK + GRAM + TOK + SQR + DEC + TOK + ((GRAM + 2 * TOK + BETA) if g2 else 0),
+        "bwd_scan": 3 * TOK + TOK + GRAM + DEC + SQR + TOK + ((TOK + BETA) if g2 else 0),
+        "bwd_chunk": 4 * TOK + BETA + ALPHA + GRAM + GLOG + 2 * SQR + 2 * TOK + 3 * TOK + BETA + ALPHA,
+        "bwd_kda_state": 3 * TOK + 2 * SQR + FD + 3 * FTOK + FGRAM + FD,
+        "bwd_kda_wy": 3 * TOK + BETA + ALPHA + FTOK + TOK + BETA + FTOK + FGRAM,
+        "bwd_kda_gram": 2 * TOK + ALPHA + 2 * FGRAM + 3 * FTOK + FD + 2 * TOK + ALPHA,
+        "bwd_gdn2_state": 5 * TOK + GLOG + BETA + 2 * SQR + 2 * TOK + 5 * FTOK + 2 * FGRAM + 4 * GLOG,
+        "bwd_gdn2_wy": 5 * TOK + GLOG + BETA + 3 * TOK + GRAM + 3 * FTOK + 2 * TOK + 4 * FGRAM + FTOK + 4 * GLOG,
+        "bwd_gdn2_gram": 3 * TOK + BETA + ALPHA + GLOG + 2 * GRAM + 6 * FGRAM + 3 * FTOK + 4 * GLOG
+                         + 3 * TOK + BETA + ALPHA,
+    }
+    return table[kernel]
+
+
+def path_bytes_per_head_token(variant: str, D: int = 128, esz: int = 2, has_beta: bool = True) -> int:
+    """The operator's own minimum per head-token: the forward reads q, k, v and the gates and
+    writes o; the backward reads q, k, v, the gates and dO and writes the gradients of q, k,
+    v and of every gate (Gated, d = 128, bf16: 2828 bytes)."""
+    tok = D * esz
+    beta = esz if has_beta else 0
+    gates = beta + {"deltanet": 0, "gated": esz, "kda": tok, "gdn2": esz + 2 * tok}[variant]
+    return (3 * tok + gates + tok) + (4 * tok + gates + 3 * tok + gates)
 
 
 def source_sha() -> str:
@@ -229,16 +249,17 @@ def main():
     chunks = sum((b - a + 63) // 64 for a, b in zip(cu[:-1], cu[1:]))
     units = chunks * w.H
     per_launch_units = units  # each launch of any kernel covers every (chunk, head) unit once
-    kbytes = KERNEL_BYTES_PER_UNIT[dom] * per_launch_units
+    esz = 2 if w.dtype == "bf16" else 4
+    kbytes = kernel_bytes_per_unit(w.variant, dom, w.dk, esz, w.has_beta) * per_launch_units
     achieved = kbytes / (avg_ms / 1e3) / 1e9
     traffic = measured_traffic(dom, w.name)
-    path_bytes = PATH_BYTES_PER_HEAD_TOKEN * tokens * w.H
+    path_bytes = path_bytes_per_head_token(w.variant, w.dk, esz, w.has_beta) * tokens * w.H
     path_gbs = path_bytes / (ms / 1e3) / 1e9
     out = {
         "metric": "tokens/s chunked gated-delta-rule fwd+bwd, H=16 d=128, T=4k-32k; % of roofline",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded; distributions of the workload definition)",
+        "dtype": w.dtype, "data": "synthetic (seeded; distributions of the workload definition)",
         "config": {"workload": w.name, "variant": w.variant, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk,
                    "d_v": w.dv, "chunk": w.chunk, "cu_seqlens": list(w.cu_seqlens) if w.cu_seqlens else None,
                    "initial_state": w.h0_std > 0},
