@@ -51,7 +51,7 @@ struct BwdScanOps<E, D, BV, VAR_KDA> {
 };
 
 template <typename E, int D, int BV, int VAR>
-__global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ dO, const E* __restrict__ Xg,
                                                   const E* __restrict__ Mg, const float* __restrict__ Gg,
                                                   const float* __restrict__ dht, E* __restrict__ dHs,
@@ -75,13 +75,26 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
   __shared__ __align__(16) E dRn[CH * LDV];   // dR
   __shared__ float gs[CH];
 
+  constexpr int NVR = D / BV;
   int sq, h, vt;
-  if (!scan_block<D / BV>(geo, sq, h, vt)) return;
-  const int i0 = vt * BV;
+  if (!scan_block(geo, sg.mode == 1 ? 2 * NVR : NVR, sq, h, vt)) return;
+  const bool virt = vt >= NVR;  // mode 1: rows of the segment's linear part (no dO term)
+  const int i0 = (virt ? vt - NVR : vt) * BV;
   const SeqPos sp = seq_pos(geo, sq);
   const int w = wave_id();
-  const long sbase = ((long)sq * geo.H + h) * D;
-  const int nck = sp.nchunks;
+  const long mem = (long)sq * geo.H + h;
+  const long sbase = mem * D;
+  const int seg = blockIdx.y;
+  int c0 = 0, c1 = sp.nchunks;
+  if (sg.mode != 0) {
+    if (seg >= seg_count(sg, sp.nchunks)) return;
+    c0 = seg * sg.lseg;
+    c1 = min(sp.nchunks, c0 + sg.lseg);
+  }
+  const bool snap = sg.mode != 1;  // record dW and dR per chunk
+  const float* init = nullptr;      // memory gradient at the end of the covered chunks
+  if (sg.mode == 2) init = sg.starts + (mem * sg.max_seg + seg) * D * D;
+  else if (sg.mode == 0 && dht) init = dht + sbase * D;
 
   f32x4 S[NJ][NI];  // dW^T tiles
 #pragma unroll
@@ -89,11 +102,12 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const int j0 = acc_row(16 * (w + 4 * qq), 0), i = i0 + acc_col(16 * it);
-      if (dht) {
-        const float4 x = *reinterpret_cast<const float4*>(dht + (sbase + i) * D + j0);
+      if (init) {
+        const float4 x = *reinterpret_cast<const float4*>(init + (long)i * D + j0);
         S[qq][it] = f32x4{x.x, x.y, x.z, x.w};
       } else {
-        S[qq][it] = zero4();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[qq][it][r] = (virt && j0 + r == i) ? 1.f : 0.f;
       }
     }
 
@@ -101,7 +115,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
   // Loads before the first chunk repeat it, so every step issues the same memory operations.
   using Ops = BwdScanOps<E, D, BV, VAR>;
   auto load = [&](Ops& p, int c) {
-    const int cc = max(c, 0);
+    const int cc = max(c, c0);
     const long u = (long)(sp.gc0 + cc) * geo.H + h;
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
@@ -157,7 +171,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
           if constexpr (DEC) eg = __expf(gs[t]);
 #pragma unroll
           for (int x = 0; x < RT::VE; ++x) {
-            const float val = geo.scale * (float)e[x];
+            const float val = virt ? 0.f : geo.scale * (float)e[x];
             dOt[(i + x) * LDR + t] = (E)val;
             dOg[(i + x) * LDR + t] = (E)(val * eg);
           }
@@ -174,7 +188,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
       }
     }
     load(p, c - 2);
-    s2g_full<E, BV, D, NT>(dHs + u * D * D + (long)i0 * D, D, dWs, LD);
+    if (snap) s2g_full<E, BV, D, NT>(dHs + u * D * D + (long)i0 * D, D, dWs, LD);
     __syncthreads();
     const float gn = gs[CH - 1];
 #pragma unroll
@@ -193,7 +207,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
       store4_n(dRn, LDV, 16 * w, 16 * it, dr);
     }
     __syncthreads();
-    s2g_full<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV);
+    if (snap) s2g_full<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV);
     float eg = 1.f;
     if constexpr (DEC) eg = __expf(gn);
 #pragma unroll
@@ -207,23 +221,26 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, const E* __restrict__
       }
     __syncthreads();
   };
-  if (nck > 0) {
+  if (c1 > c0) {
     Ops pa, pb;
-    load(pa, nck - 1);
-    load(pb, nck - 2);
-    for (int c = nck - 1; c >= 0; c -= 2) {
+    load(pa, c1 - 1);
+    load(pb, c1 - 2);
+    for (int c = c1 - 1; c >= c0; c -= 2) {
       step(c, pa);
-      if (c - 1 >= 0) step(c - 1, pb);
+      if (c - 1 >= c0) step(c - 1, pb);
     }
   }
-  if (dh0) {
+  float* out = nullptr;  // dh0, or this segment's map
+  if (sg.mode == 1) out = sg.maps + ((mem * sg.max_seg + seg) * 2 + (virt ? 1 : 0)) * D * D;
+  else if (dh0 && seg == 0) out = dh0 + sbase * D;
+  if (out) {
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
         const int j0 = acc_row(16 * (w + 4 * qq), 0), i = i0 + acc_col(16 * it);
         const f32x4 x = S[qq][it];
-        *reinterpret_cast<float4*>(dh0 + (sbase + i) * D + j0) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(out + (long)i * D + j0) = make_float4(x[0], x[1], x[2], x[3]);
       }
   }
 }
@@ -235,7 +252,7 @@ template <typename E, int D>
 struct BwdLds {
   static constexpr int LD = D + pad16<E>(), LDR = CH + pad16<E>(), LF = CH + 4;
   static constexpr int TK = CH * LD * (int)sizeof(E);   // 64 x D token tile
-  static constexpr int TH = D * LDR * (int)sizeof(E);   // D x 64 (transposed half memory)
+  static constexpr int TH = CH * LD * (int)sizeof(E);  // 64 value rows of the memory
   static constexpr int SQ = CH * LDR * (int)sizeof(E);  // 64 x 64 in E
   static constexpr int F = CH * LF * 4;                 // 64 x 64 float
   static constexpr int oK = 0, odR = TK, odX = 2 * TK, odM = 3 * TK, oU = 3 * TK + SQ;
@@ -259,6 +276,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
                                                    const E* __restrict__ Mg, const float* __restrict__ Gg,
                                                    const E* __restrict__ Hs, const E* __restrict__ Rg,
                                                    const E* __restrict__ dHs, const E* __restrict__ dRg,
+                                                   const float* __restrict__ Ag, const float* __restrict__ Lig,
                                                    E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
                                                    E* __restrict__ dbeta, E* __restrict__ dalpha) {
   using Ly = BwdLds<E, D>;
@@ -267,7 +285,6 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   constexpr int NQ = D / 32;           // 64 x D tiles per wave when all 8 waves share a matrix
   constexpr bool GATED = VAR == VAR_GATED;
   __shared__ __align__(16) char smem[Ly::BIG];
-  __shared__ __align__(16) float scr[4 * 256];
   __shared__ float gs[CH], bs[CH], dbs[CH], red[NT / 64];
   __shared__ float rq[4][CH], rkh[8][CH], rkb[8][CH];
 
@@ -296,6 +313,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   RegTile<E, KH, D, NT> pW, pdW;      // one 64-row block of W0 and of dW, next block prefetched
   RegTile<E, CH, D, NT> pV, pQ;       // V and Q, used in later phases
   RegTile<E, CH, CH, NT> pM;          // M, used for the decay gradient
+  RegTile<float, CH, CH, NT> pA, pLi;  // the forward's A and L^{-1}, used in phase 2
   {
     E* dOs = reinterpret_cast<E*>(smem + Ly::odO);
     E* Rs = reinterpret_cast<E*>(smem + Ly::oR);
@@ -312,6 +330,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       pV.load(v + tk * D, D, n);
       pQ.load(q + tk * D, D, n);
       pM.load(Mg + u * CH * CH, CH, CH);
+      pA.load(Ag + u * CH * CH, CH, CH);
+      pLi.load(Lig + u * CH * CH, CH, CH);
       r0.store(Ks, LD);
       r1.store(dOs, LD);
       r2.store(Rs, LD);
@@ -324,8 +344,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
     for (int ih = 0; ih < NH; ++ih) {
       __syncthreads();
-      pW.store_t(Wh, LDR);
-      pdW.store_t(dWh, LDR);
+      pW.store(Wh, LD);  // rows i (value), columns j (key): read k-major below
+      pdW.store(dWh, LD);
       if (ih + 1 < NH) {
         pW.load(Hs + u * D * D + (long)(ih + 1) * KH * D, D, KH);
         pdW.load(dHs + u * D * D + (long)(ih + 1) * KH * D, D, KH);
@@ -333,10 +353,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       __syncthreads();
       const E* Aop = (w < 4 ? dOs : dRs) + ih * KH;
 #pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(Aop, LD), 16 * wm, rowk(Wh, LDR), 16 * nt);
+      for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(Aop, LD), 16 * wm, colk(Wh, LD), 16 * nt);
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq)
-        dka[qq] = mma_k<E, KH>(dka[qq], rowk(Rs + ih * KH, LD), 16 * wm, rowk(dWh, LDR), 16 * (wn * NQ + qq));
+        dka[qq] = mma_k<E, KH>(dka[qq], rowk(Rs + ih * KH, LD), 16 * wm, colk(dWh, LD), 16 * (wn * NQ + qq));
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int id = w + 8 * e;
@@ -344,8 +364,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       }
       if constexpr (GATED) {
         for (int idx = threadIdx.x; idx < D * KH; idx += NT) {
-          const int j = idx / KH, i = idx % KH;
-          gam += (float)Wh[j * LDR + i] * (float)dWh[j * LDR + i];
+          const int i = idx / D, j = idx % D;
+          gam += (float)Wh[i * LD + j] * (float)dWh[i * LD + j];
         }
       }
     }
@@ -404,25 +424,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   float* Li = reinterpret_cast<float*>(smem + Ly::oLi);
   E* Vs = reinterpret_cast<E*>(smem + Ly::oVP);
   pV.store(Vs, LD);
-  for (int job = w; job < 10; job += 8) {
-    int mt, nt;
-    tri_tile(job, mt, nt);
-    const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
-      float val = 0.f;
-      if (s < t) {
-        float dec = 1.f;
-        if constexpr (GATED) dec = expf(gs[t] - gs[s]);
-        val = acc[r] * dec;
-      }
-      As[t * LF + s] = val;
-      dTs[t * LF + s] = bs[t] * val;  // L below the diagonal, solved into Li
-    }
-  }
+  pA.store(As, LF);  // A and L^{-1} as the forward computed them
+  pLi.store(Li, LF);
   __syncthreads();
-  solve_unit_lower64<NT>(dTs, LF, Li, LF, scr);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
@@ -625,17 +629,29 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
   const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
   const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
   const float* gin = KDA ? p.Gn : p.G;
-  {
-    TraceScope ts_("bwd_scan", st);
+  auto scan = [&](const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult) {
     if (p.bv == 16) {
-      hipLaunchKernelGGL((k_bwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g, qin, kin,
-                         (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dht, (E*)p.dHs, (E*)p.dR, gr.dh0,
-                         (const E*)in.beta, (const E*)in.erase);
+      hipLaunchKernelGGL((k_bwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, nv_mult * D / 16), sg.mode ? sg.max_seg : 1),
+                         dim3(256), 0, st, g, sg, qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp,
+                         (E*)p.dHs, (E*)p.dR, dh0p, (const E*)in.beta, (const E*)in.erase);
     } else {
-      hipLaunchKernelGGL((k_bwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g, qin, kin,
-                         (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dht, (E*)p.dHs, (E*)p.dR, gr.dh0,
-                         (const E*)in.beta, (const E*)in.erase);
+      hipLaunchKernelGGL((k_bwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, nv_mult * D / 32), sg.mode ? sg.max_seg : 1),
+                         dim3(256), 0, st, g, sg, qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp,
+                         (E*)p.dHs, (E*)p.dR, dh0p, (const E*)in.beta, (const E*)in.erase);
     }
+  };
+  if (p.lseg == 0) {
+    TraceScope ts_("bwd_scan", st);
+    scan(ScanSeg{0, 0, 1, nullptr, nullptr}, dht, gr.dh0, 1);
+  } else {
+    {
+      TraceScope ts_("bwd_scan_maps", st);
+      scan(ScanSeg{1, p.lseg, p.max_seg, p.seg_maps, nullptr}, nullptr, nullptr, 2);
+    }
+    const hipError_t e = launch_seg_combine(p, ScanSeg{0, p.lseg, p.max_seg, p.seg_maps, nullptr}, dht, true, st);
+    if (e != hipSuccess) return e;
+    TraceScope ts_("bwd_scan", st);
+    scan(ScanSeg{2, p.lseg, p.max_seg, nullptr, p.seg_starts}, nullptr, gr.dh0, 1);
   }
   if (g.total_chunks > 0) {
     if constexpr (VAR == VAR_GDN2) {
@@ -647,8 +663,8 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
       hipLaunchKernelGGL((k_bwd_chunk<E, D, VAR>), dim3(g.total_chunks, g.H), dim3(512), 0, st, g,
                          (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
                          (const E*)dO, (const E*)p.M, (const float*)p.G, (const E*)p.Hs, (const E*)p.R,
-                         (const E*)p.dHs, (const E*)p.dR, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta,
-                         (E*)gr.dalpha);
+                         (const E*)p.dHs, (const E*)p.dR, p.A1, p.Li, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv,
+                         (E*)gr.dbeta, (E*)gr.dalpha);
     }
   }
   return hipGetLastError();

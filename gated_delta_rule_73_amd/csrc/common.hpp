@@ -375,22 +375,39 @@ __device__ __forceinline__ long tok_index(const Geo& g, int b, int h, int t) {
   return ((long)b * g.H + h) * g.T + t;
 }
 
-// Scan kernels use a 1-D grid.  Work item (sequence, head) sh and value tile vt run on
-// block L with L % 8 == sh % 8, so the tiles of one memory land on one XCD (workgroups are
-// dealt to the 8 XCDs round-robin) and share its L2 for the chunk operands they all read.
+// Scan kernels use a 1-D grid (times the segment count in y for segmented scans).  Work item
+// (sequence, head) sh and value tile vt run on block L with L % 8 == sh % 8, so the tiles of
+// one memory land on one XCD (workgroups are dealt to the 8 XCDs round-robin) and share its
+// L2 for the chunk operands they all read.
 inline unsigned scan_grid(const Geo& g, int nv) {
   const unsigned nsh = (unsigned)g.nseq * (unsigned)g.H;
   return ((nsh + 7u) / 8u) * 8u * (unsigned)nv;
 }
-template <int NV>
-__device__ __forceinline__ bool scan_block(const Geo& g, int& seq, int& h, int& vt) {
+__device__ __forceinline__ bool scan_block(const Geo& g, int nv, int& seq, int& h, int& vt) {
   const int L = blockIdx.x;
-  vt = (L >> 3) % NV;
-  const int sh = ((L >> 3) / NV) * 8 + (L & 7);
+  vt = (L >> 3) % nv;
+  const int sh = ((L >> 3) / nv) * 8 + (L & 7);
   if (sh >= g.nseq * g.H) return false;
   seq = sh / g.H;
   h = sh % g.H;
   return true;
+}
+
+// Segmented scans.  The chunk-to-chunk map of a memory is affine, W_next = W P_c + H_c (and
+// dW_prev = dW Q_c + G_c in the backward), so a sequence's chunks can be cut into segments of
+// lseg chunks: mode 1 runs every segment from a zero memory (giving its additive part) and,
+// in extra "virtual" value tiles, from the identity with the write term removed (giving its
+// linear part); a combine kernel composes the segments' maps in order to find each segment's
+// start memory; mode 2 reruns every segment from that start, writing the per-chunk results.
+// A sequence has max(1, ceil(chunks / lseg)) segments; mode 0 is the unsegmented scan.
+struct ScanSeg {
+  int mode;             // 0, 1 or 2 as above
+  int lseg, max_seg;    // chunks per segment; largest segment count of any sequence
+  float* maps;          // mode 1 output: [memories][max_seg][2][D][D] (additive part, linear part)
+  const float* starts;  // mode 2 input: [memories][max_seg][D][D] start memory of each segment
+};
+__device__ __forceinline__ int seg_count(const ScanSeg& sg, int nchunks) {
+  return max(1, (nchunks + sg.lseg - 1) / sg.lseg);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -23,8 +23,9 @@ template <typename E, int D, int VAR>
 __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ v, const E* __restrict__ beta,
                                                   const E* __restrict__ alpha, E* __restrict__ Xo,
-                                                  E* __restrict__ Uo, E* __restrict__ Mo, float* __restrict__ Go) {
-  constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 1;
+                                                  E* __restrict__ Uo, E* __restrict__ Mo, float* __restrict__ Go,
+                                                  float* __restrict__ Lio, float* __restrict__ Ao) {
+  constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   static_assert(CH * LDT * (int)sizeof(E) >= 4 * 256 * 4, "T buffer doubles as the solve's scratch");
   __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g * K, then X
   __shared__ __align__(16) E QV[CH * LD];   // Q, then V, then U
@@ -73,13 +74,20 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
         if constexpr (VAR == VAR_GATED) dec = __expf(gs[t] - gs[s]);
         val = acc[r] * dec;
       }
-      if (isM) Mo[(u * CH + t) * CH + s] = (E)val;
-      else Ls[t * LF + s] = bs[t] * val;
+      if (isM) {
+        Mo[(u * CH + t) * CH + s] = (E)val;
+      } else {
+        Ls[t * LF + s] = bs[t] * val;
+        Ao[(u * CH + t) * CH + s] = val;
+      }
     }
   }
   for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
     const int t = idx >> 6, s = idx & 63;
-    if ((s >> 4) > (t >> 4)) Mo[(u * CH + t) * CH + s] = (E)0.f;
+    if ((s >> 4) > (t >> 4)) {
+      Mo[(u * CH + t) * CH + s] = (E)0.f;
+      Ao[(u * CH + t) * CH + s] = 0.f;
+    }
   }
   __syncthreads();
   rv.store(QV, LD);
@@ -89,6 +97,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
     const int t = idx >> 6, s = idx & 63;
     Ts[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] * bs[s] : 0.f);
   }
+  s2g_full<float, CH, CH, NT>(Lio + u * CH * CH, CH, Li, LF);  // L^{-1} for the backward
   if constexpr (VAR == VAR_GATED) {
     for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
       const int t = idx / D, j = idx % D;
@@ -144,7 +153,7 @@ struct FwdScanOps<E, D, BV, VAR_KDA> {
 };
 
 template <typename E, int D, int BV, int VAR>
-__global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__ k, const E* __restrict__ Xg,
+__global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ k, const E* __restrict__ Xg,
                                                   const E* __restrict__ Ug, const float* __restrict__ Gg,
                                                   const float* __restrict__ h0, E* __restrict__ Hs,
                                                   E* __restrict__ Rg, float* __restrict__ ht,
@@ -166,13 +175,27 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
   __shared__ __align__(16) E Rd[BV * LDR];
   __shared__ float gs[CH];
 
+  constexpr int NVR = D / BV;
   int sq, h, vt;
-  if (!scan_block<D / BV>(geo, sq, h, vt)) return;
-  const int i0 = vt * BV;
+  if (!scan_block(geo, sg.mode == 1 ? 2 * NVR : NVR, sq, h, vt)) return;
+  const bool virt = vt >= NVR;  // mode 1: rows of the segment's linear part
+  const int i0 = (virt ? vt - NVR : vt) * BV;
   const SeqPos sp = seq_pos(geo, sq);
   const int w = wave_id();
-  const long sbase = ((long)sq * geo.H + h) * D;  // row base of this memory in [N,H,D,D]
-  const int nck = sp.nchunks;
+  const long mem = (long)sq * geo.H + h;
+  const long sbase = mem * D;  // row base of this memory in [N,H,D,D]
+  const int seg = blockIdx.y;
+  int c0 = 0, c1 = sp.nchunks, nseg = 1;
+  if (sg.mode != 0) {
+    nseg = seg_count(sg, sp.nchunks);
+    if (seg >= nseg) return;
+    c0 = seg * sg.lseg;
+    c1 = min(sp.nchunks, c0 + sg.lseg);
+  }
+  const bool snap = sg.mode != 1;  // record W0 and R per chunk
+  const float* init = nullptr;  // start memory (rows i, columns j); none: zero, or identity rows
+  if (sg.mode == 2) init = sg.starts + (mem * sg.max_seg + seg) * D * D;
+  else if (sg.mode == 0 && h0) init = h0 + sbase * D;
 
   f32x4 S[NJ][NI];
 #pragma unroll
@@ -180,11 +203,12 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const int j0 = acc_row(16 * (w + 4 * qq), 0), i = i0 + acc_col(16 * it);
-      if (h0) {
-        const float4 x = *reinterpret_cast<const float4*>(h0 + (sbase + i) * D + j0);
+      if (init) {
+        const float4 x = *reinterpret_cast<const float4*>(init + (long)i * D + j0);
         S[qq][it] = f32x4{x.x, x.y, x.z, x.w};
       } else {
-        S[qq][it] = zero4();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[qq][it][r] = (virt && j0 + r == i) ? 1.f : 0.f;
       }
     }
 
@@ -192,7 +216,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
   // Loads past the last chunk repeat it, so every step issues the same memory operations.
   using Ops = FwdScanOps<E, D, BV, VAR>;
   auto load = [&](Ops& p, int c) {
-    const int cc = min(c, nck - 1);
+    const int cc = min(c, c1 - 1);
     const long u = (long)(sp.gc0 + cc) * geo.H + h;
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
@@ -247,14 +271,14 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
 #pragma unroll
       for (int it = 0; it < decltype(p.vt)::IT; ++it) {
         const int t = p.vt.row(it), i = p.vt.col(it);
-        const float sc = bsh[t] * __expf(gn0 - gs[t]);
+        const float sc = virt ? 0.f : bsh[t] * __expf(gn0 - gs[t]);
 #pragma unroll
         for (int x = 0; x < decltype(p.vt)::VE; ++x)
           Bd[(i + x) * LDR + t] = (E)(sc * (float)p.wt.elem(it, x) * (float)p.vt.elem(it, x));
       }
     }
     load(p, c + 2);
-    s2g_full<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD);
+    if (snap) s2g_full<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD);
     const float gn = gs[CH - 1];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
@@ -263,7 +287,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = acc_row(16 * w, r), i = acc_col(16 * it);
-        const float val = (float)Us[t * LDV + i] - acc[r];
+        const float val = (virt ? 0.f : (float)Us[t * LDV + i]) - acc[r];
         rv[r] = val;
         float dec = 1.f;
         if constexpr (DEC) dec = __expf(gn - gs[t]);
@@ -273,7 +297,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
       store4_t(Rd, LDR, 16 * w, 16 * it, rd);
     }
     __syncthreads();
-    s2g_full<E, CH, BV, NT>(Rg + u * CH * D + i0, D, Rn, LDV);
+    if (snap) s2g_full<E, CH, BV, NT>(Rg + u * CH * D + i0, D, Rn, LDV);
     float eg = 1.f;
     if constexpr (DEC) eg = __expf(gn);
 #pragma unroll
@@ -292,23 +316,26 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, const E* __restrict__
       }
     __syncthreads();
   };
-  if (nck > 0) {
+  if (c1 > c0) {
     Ops pa, pb;
-    load(pa, 0);
-    load(pb, 1);
-    for (int c = 0; c < nck; c += 2) {
+    load(pa, c0);
+    load(pb, c0 + 1);
+    for (int c = c0; c < c1; c += 2) {
       step(c, pa);
-      if (c + 1 < nck) step(c + 1, pb);
+      if (c + 1 < c1) step(c + 1, pb);
     }
   }
-  if (ht) {
+  float* out = nullptr;  // final memory: ht, or this segment's map
+  if (sg.mode == 1) out = sg.maps + ((mem * sg.max_seg + seg) * 2 + (virt ? 1 : 0)) * D * D;
+  else if (ht && seg == nseg - 1) out = ht + sbase * D;
+  if (out) {
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
 #pragma unroll
       for (int it = 0; it < NI; ++it) {
         const int j0 = acc_row(16 * (w + 4 * qq), 0), i = i0 + acc_col(16 * it);
         const f32x4 x = S[qq][it];
-        *reinterpret_cast<float4*>(ht + (sbase + i) * D + j0) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(out + (long)i * D + j0) = make_float4(x[0], x[1], x[2], x[3]);
       }
   }
 }
@@ -394,24 +421,37 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, float* 
     } else {
       TraceScope ts_("fwd_prep", st);
       hipLaunchKernelGGL((k_fwd_prep<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k,
-                         (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G);
+                         (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G,
+                         p.Li, p.A1);
     }
   }
   constexpr bool KDA = VAR == VAR_KDA;
   const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
   const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
   const float* gin = KDA ? p.Gn : p.G;
-  {
-    TraceScope ts_("fwd_scan", st);
+  auto scan = [&](const ScanSeg& sg, const float* h0, float* htp, int nv_mult) {
     if (p.bv == 16) {
-      hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, D / 16)), dim3(256), 0, st, g, kin,
-                         (const E*)p.X, (const E*)p.Ub, gin, in.h0, (E*)p.Hs, (E*)p.R, ht, (const E*)in.v,
-                         (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
+      hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, nv_mult * D / 16), sg.mode ? sg.max_seg : 1),
+                         dim3(256), 0, st, g, sg, kin, (const E*)p.X, (const E*)p.Ub, gin, h0, (E*)p.Hs, (E*)p.R, htp,
+                         (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
     } else {
-      hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, D / 32)), dim3(256), 0, st, g, kin,
-                         (const E*)p.X, (const E*)p.Ub, gin, in.h0, (E*)p.Hs, (E*)p.R, ht, (const E*)in.v,
-                         (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
+      hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, nv_mult * D / 32), sg.mode ? sg.max_seg : 1),
+                         dim3(256), 0, st, g, sg, kin, (const E*)p.X, (const E*)p.Ub, gin, h0, (E*)p.Hs, (E*)p.R, htp,
+                         (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
     }
+  };
+  if (p.lseg == 0) {
+    TraceScope ts_("fwd_scan", st);
+    scan(ScanSeg{0, 0, 1, nullptr, nullptr}, in.h0, ht, 1);
+  } else {
+    {
+      TraceScope ts_("fwd_scan_maps", st);
+      scan(ScanSeg{1, p.lseg, p.max_seg, p.seg_maps, nullptr}, nullptr, nullptr, 2);
+    }
+    const hipError_t e = launch_seg_combine(p, ScanSeg{0, p.lseg, p.max_seg, p.seg_maps, nullptr}, in.h0, false, st);
+    if (e != hipSuccess) return e;
+    TraceScope ts_("fwd_scan", st);
+    scan(ScanSeg{2, p.lseg, p.max_seg, nullptr, p.seg_starts}, nullptr, ht, 1);
   }
   if (want_out && g.total_chunks > 0) {
     TraceScope ts_("fwd_out", st);

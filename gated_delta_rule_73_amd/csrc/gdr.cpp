@@ -3,9 +3,11 @@
 // argument has been checked.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -35,9 +37,32 @@ struct Sizes {
   int total_chunks = 0;
   int nstates = 0;
   size_t esz = 0;
-  size_t X, M, G, Hs, R, M2, U2, Kb, Qh, Gn, Ub, dHs, dR, g2;
-  size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Kb + Qh + Gn; }
+  int bv = 16, lseg = 0, max_seg = 1;  // scan value tile; segmented scans (see plan_scans)
+  size_t X, M, G, Hs, R, M2, U2, Li, A1, A2, Kb, Qh, Gn, Ub, dHs, dR, g2, seg;
+  size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Li + A1 + A2 + Kb + Qh + Gn; }
+  size_t fwd_ws() const { return Ub + seg; }                   // workspace before the cache
+  size_t bwd_ws() const { return Ub + dHs + dR + g2 + seg; }
 };
+
+// Scan shape.  Value tiles of 32 rows when the memories give at least one per CU, else 16.
+// When even then the memories' tiles number under 256 (fewer than one workgroup per CU), each
+// sequence's chunks are cut into segments (see ScanSeg) so that about 1024 workgroups run,
+// with at least 16 chunks per segment.  GDR_SEG_CHUNKS, if set, forces the segment length in
+// chunks (0: never segment); it exists for tuning and changes nothing but speed.
+void plan_scans(long long memories, int d, int max_chunks, Sizes* s) {
+  s->bv = (memories * (d / 32) >= 256) ? 32 : 16;
+  const long long tiles = memories * (d / s->bv);
+  int lseg = 0;
+  if (const char* env = std::getenv("GDR_SEG_CHUNKS")) {
+    lseg = std::atoi(env);
+  } else if (tiles < 256 && max_chunks >= 32) {
+    const long long want = (1024 + tiles - 1) / tiles;
+    lseg = (int)std::max<long long>(16, (max_chunks + want - 1) / want);
+  }
+  if (lseg <= 0 || lseg >= max_chunks) lseg = 0;
+  s->lseg = lseg;
+  s->max_seg = lseg ? (max_chunks + lseg - 1) / lseg : 1;
+}
 
 // Checks the problem description and computes the buffer sizes.
 gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
@@ -54,6 +79,7 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   if (p->n_seqs < 0) return fail(GDR_ERR_INVALID_ARG, "n_seqs must be >= 0");
   if (p->H > 65535) return fail(GDR_ERR_UNSUPPORTED, "H > 65535 is not supported");
   long long total_chunks = 0;
+  int max_chunks = 0;
   if (p->n_seqs > 0) {
     if (p->B != 1) return fail(GDR_ERR_INVALID_ARG, "packed sequences need B == 1 (got %d)", p->B);
     if (!p->cu_seqlens_host || !p->cu_seqlens_dev)
@@ -64,12 +90,15 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
       return fail(GDR_ERR_INVALID_ARG, "cu_seqlens[%d] must equal T=%d (got %d)", p->n_seqs, p->T, cu[p->n_seqs]);
     for (int i = 0; i < p->n_seqs; ++i) {
       if (cu[i + 1] < cu[i]) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (index %d)", i + 1);
-      total_chunks += (cu[i + 1] - cu[i] + gdr::CH - 1) / gdr::CH;
+      const int nc = (cu[i + 1] - cu[i] + gdr::CH - 1) / gdr::CH;
+      total_chunks += nc;
+      max_chunks = std::max(max_chunks, nc);
     }
   } else {
     if (p->cu_seqlens_host || p->cu_seqlens_dev)
       return fail(GDR_ERR_INVALID_ARG, "cu_seqlens given but n_seqs == 0");
-    total_chunks = (long long)p->B * ((p->T + gdr::CH - 1) / gdr::CH);
+    max_chunks = (p->T + gdr::CH - 1) / gdr::CH;
+    total_chunks = (long long)p->B * max_chunks;
   }
   if (p->chunk != gdr::CH) return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: only 64 is built", p->chunk);
   if (p->dk != p->dv) return fail(GDR_ERR_UNSUPPORTED, "dk=%d != dv=%d is not built", p->dk, p->dv);
@@ -97,6 +126,9 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   const bool g2 = p->variant == GDR_GDN2, kda = p->variant == GDR_KDA;
   s.M2 = g2 ? align_up(U * C * C * s.esz, A) : 0;
   s.U2 = g2 ? align_up(U * C * D * s.esz, A) : 0;
+  s.Li = align_up(U * C * C * 4, A);
+  s.A1 = align_up(U * C * C * 4, A);
+  s.A2 = g2 ? align_up(U * C * C * 4, A) : 0;
   s.Kb = kda ? align_up(U * C * D * s.esz, A) : 0;
   s.Qh = kda ? align_up(U * C * D * s.esz, A) : 0;
   s.Gn = kda ? align_up(U * D * 4, A) : 0;
@@ -105,6 +137,8 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   if (g2) s.g2 = align_up(U * (5 * C * D + 6 * C * C + 4 * C) * 4, A);
   else if (kda) s.g2 = align_up(U * (4 * C * D + 2 * C * C + D) * 4, A);
   else s.g2 = 0;
+  plan_scans((long long)s.nstates * p->H, p->dk, max_chunks, &s);
+  s.seg = s.lseg ? align_up((size_t)s.nstates * p->H * s.max_seg * 3 * D * D * 4, A) : 0;
   *sz = s;
   return GDR_OK;
 }
@@ -134,8 +168,8 @@ gdr_status check_ws(void* ws, size_t have, size_t need) {
   return GDR_OK;
 }
 
-gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws) {
-  gdr::Plan pl;
+gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws, bool backward) {
+  gdr::Plan pl{};
   pl.geo.B = p->B;
   pl.geo.H = p->H;
   pl.geo.T = p->T;
@@ -147,9 +181,9 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws)
   pl.variant = p->variant;
   pl.dtype = p->dtype;
   pl.D = p->dk;
-  // Value-row tile of the scans: 16 rows when there are few memories to spread over the CUs.
-  const long long mem = (long long)s.nstates * p->H;
-  pl.bv = (mem * (p->dk / 32) >= 256) ? 32 : 16;
+  pl.bv = s.bv;
+  pl.lseg = s.lseg;
+  pl.max_seg = s.max_seg;
   char* c = cache;
   pl.X = c; c += s.X;
   pl.M = c; c += s.M;
@@ -158,17 +192,24 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws)
   pl.R = c; c += s.R;
   pl.M2 = c; c += s.M2;
   pl.U2 = c; c += s.U2;
+  pl.Li = reinterpret_cast<float*>(c); c += s.Li;
+  pl.A1 = reinterpret_cast<float*>(c); c += s.A1;
+  pl.A2 = reinterpret_cast<float*>(c); c += s.A2;
   pl.Kb = c; c += s.Kb;
   pl.Qh = c; c += s.Qh;
   pl.Gn = reinterpret_cast<float*>(c); c += s.Gn;
   char* w = ws;
   pl.Ub = w; w += s.Ub;
-  pl.dHs = w; w += s.dHs;
-  pl.dR = w; w += s.dR;
-  float* f = reinterpret_cast<float*>(w);
-  const size_t U = (size_t)s.units, C = gdr::CH, D = (size_t)p->dk;
-  {
-    float* fk = f;
+  pl.seg_maps = reinterpret_cast<float*>(w);
+  pl.seg_starts = pl.seg_maps + (size_t)s.nstates * p->H * s.max_seg * 2 * p->dk * p->dk;
+  w += s.seg;
+  pl.dHs = pl.dR = nullptr;
+  if (backward) {
+    pl.dHs = w; w += s.dHs;
+    pl.dR = w; w += s.dR;
+    // float32 backward intermediates: GDN-2 and KDA carve the same region differently
+    const size_t U = (size_t)s.units, C = gdr::CH, D = (size_t)p->dk;
+    float* fk = reinterpret_cast<float*>(w);
     pl.kd_dqh = fk; fk += U * C * D;
     pl.kd_dx = fk; fk += U * C * D;
     pl.kd_dkb = fk; fk += U * C * D;
@@ -176,19 +217,20 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws)
     pl.kd_dm = fk; fk += U * C * C;
     pl.kd_da = fk; fk += U * C * C;
     pl.kd_gam = fk;
+    float* f = reinterpret_cast<float*>(w);
+    pl.g2_dq = f; f += U * C * D;
+    pl.g2_dk = f; f += U * C * D;
+    pl.g2_da = f; f += U * C * D;
+    pl.g2_db = f; f += U * C * D;
+    pl.g2_dx = f; f += U * C * D;
+    pl.g2_dakk = f; f += U * C * C;
+    pl.g2_daak = f; f += U * C * C;
+    pl.g2_dmqk = f; f += U * C * C;
+    pl.g2_dmqa = f; f += U * C * C;
+    pl.g2_akk = f; f += U * C * C;
+    pl.g2_aak = f; f += U * C * C;
+    pl.g2_rows = f;
   }
-  pl.g2_dq = f; f += U * C * D;
-  pl.g2_dk = f; f += U * C * D;
-  pl.g2_da = f; f += U * C * D;
-  pl.g2_db = f; f += U * C * D;
-  pl.g2_dx = f; f += U * C * D;
-  pl.g2_dakk = f; f += U * C * C;
-  pl.g2_daak = f; f += U * C * C;
-  pl.g2_dmqk = f; f += U * C * C;
-  pl.g2_dmqa = f; f += U * C * C;
-  pl.g2_akk = f; f += U * C * C;
-  pl.g2_aak = f; f += U * C * C;
-  pl.g2_rows = f;
   return pl;
 }
 
@@ -222,7 +264,7 @@ gdr_status gdr_workspace_size(const gdr_problem* p, int backward, size_t* bytes)
   gdr_status st = check_problem(p, &s);
   if (st != GDR_OK) return st;
   if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = s.cache() + s.Ub + (backward ? s.dHs + s.dR + s.g2 : 0);
+  *bytes = s.cache() + (backward ? s.bwd_ws() : s.fwd_ws());
   return GDR_OK;
 }
 
@@ -244,9 +286,9 @@ gdr_status gdr_forward(const gdr_problem* p, const gdr_inputs* in, void* o, floa
   if (!o && p->T > 0) return fail(GDR_ERR_INVALID_ARG, "o is required");
   if ((o && !aligned(o, 16)) || (ht && !aligned(ht, 16)) || (saved && !aligned(saved, 256)))
     return fail(GDR_ERR_INVALID_ARG, "o/ht must be 16-byte and saved 256-byte aligned");
-  if ((st = check_ws(ws, ws_bytes, s.cache() + s.Ub)) != GDR_OK) return st;
-  char* cache = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + s.Ub;
-  gdr::Plan pl = make_plan(p, s, cache, static_cast<char*>(ws));
+  if ((st = check_ws(ws, ws_bytes, s.cache() + s.fwd_ws())) != GDR_OK) return st;
+  char* cache = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + s.fwd_ws();
+  gdr::Plan pl = make_plan(p, s, cache, static_cast<char*>(ws), false);
   g_last_error.clear();
   TraceCall tc;
   return hip_status(gdr::run_forward(pl, *in, o, ht, true, static_cast<hipStream_t>(stream)), "gdr_forward launch");
@@ -273,10 +315,10 @@ gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* 
   for (const void* x : ptrs)
     if (x && !aligned(x, 16)) return fail(GDR_ERR_INVALID_ARG, "gradient pointers must be 16-byte aligned");
   if (saved && !aligned(saved, 256)) return fail(GDR_ERR_INVALID_ARG, "saved must be 256-byte aligned");
-  if ((st = check_ws(ws, ws_bytes, s.cache() + s.Ub + s.dHs + s.dR + s.g2)) != GDR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, s.cache() + s.bwd_ws())) != GDR_OK) return st;
   char* base = static_cast<char*>(ws);
-  char* cache = saved ? const_cast<char*>(static_cast<const char*>(saved)) : base + s.Ub + s.dHs + s.dR + s.g2;
-  gdr::Plan pl = make_plan(p, s, cache, base);
+  char* cache = saved ? const_cast<char*>(static_cast<const char*>(saved)) : base + s.bwd_ws();
+  gdr::Plan pl = make_plan(p, s, cache, base, true);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   g_last_error.clear();
   TraceCall tc;

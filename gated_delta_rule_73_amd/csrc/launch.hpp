@@ -13,6 +13,9 @@ namespace gdr {
 struct Plan {
   Geo geo;
   int variant, dtype, D, bv;
+  int lseg, max_seg;  // segmented scans: chunks per segment (0: off), largest segment count
+  float* seg_maps;    // [memories][max_seg][2][D][D] float32 (workspace)
+  float* seg_starts;  // [memories][max_seg][D][D] float32 (workspace)
   // forward cache (in the caller's saved buffer or in the workspace)
   void* X;    // [units][64][D]  WY factor X = T (e^g K)
   void* M;    // [units][64][64] decayed causal Q K^T
@@ -21,6 +24,9 @@ struct Plan {
   void* R;    // [units][64][D]  scaled residuals R = U - X W0^T
   void* M2;   // Gated DeltaNet-2: [units][64][64] decayed causal Q K^T (M holds Q A^T)
   void* U2;   // Gated DeltaNet-2: [units][64][D]  -L^{-1} A_kk B
+  float* Li;  // [units][64][64] L^{-1} (float32) of the chunk's unit lower-triangular L
+  float* A1;  // [units][64][64] the chunk's strictly lower Gram (float32): A, or GDN-2's A_kk
+  float* A2;  // Gated DeltaNet-2: [units][64][64] A_ak (float32)
   void* Kb;   // Kimi Delta Attention: [units][64][D] Kbar = e^{g_n - g} K
   void* Qh;   // Kimi Delta Attention: [units][64][D] Qhat = e^g Q
   float* Gn;  // Kimi Delta Attention: [units][D]     e^{g_n} per key channel
@@ -76,6 +82,8 @@ template <typename E, int D>
 hipError_t launch_fwd_prep_kda(const Plan& p, const gdr_inputs& in, hipStream_t st);
 template <typename E, int D>
 hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr, hipStream_t st);
+
+hipError_t launch_seg_combine(const Plan& p, const ScanSeg& sg, const float* init, bool reverse, hipStream_t st);
 
 hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st);
 hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht, const gdr_grads& gr,

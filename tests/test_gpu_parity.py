@@ -181,3 +181,42 @@ def test_kda_varlen_saved_vs_recomputed():
     for name in ("o", "dq", "dk", "dv", "dbeta", "dalpha", "dh0"):
         assert np.array_equal(a[name], b[name]), name
     compare(a, run_oracle(inp, "kda", backward=True), "bf16")
+
+
+@pytest.fixture
+def segments(monkeypatch):
+    """Force segmented scans (segments of the given number of chunks) for small problems."""
+    def force(n):
+        monkeypatch.setenv("GDR_SEG_CHUNKS", str(n))
+    return force
+
+
+@pytest.mark.parametrize("variant,dtype,lseg", [("gated", "bf16", 2), ("gated", "f32", 3), ("deltanet", "f32", 2),
+                                                ("kda", "f32", 2), ("gdn2", "bf16", 3)])
+def test_segmented_scans(segments, variant, dtype, lseg):
+    """Sequences cut into segments whose affine maps are composed: same results as the oracle,
+    with packed sequences of 1..5 segments, an initial memory and a final-memory gradient."""
+    cu = (0, 40, 300, 301, 620)
+    d = 64 if dtype == "f32" else 128
+    w = synth.Workload("t", variant, dtype, 1, 2, 620, d, d, seed=41, cu_seqlens=cu, h0_std=0.4,
+                       has_beta=variant != "gdn2")
+    inp = synth.make_inputs(w, alpha_mode="weak")
+    dht = np.random.default_rng(9).standard_normal((4, 2, d, d)).astype(np.float32) * 0.3
+    segments(lseg)
+    rep = []
+    compare(run_hip(inp, variant, dtype, backward=True, dht=dht), run_oracle(inp, variant, backward=True, dht=dht),
+            dtype, report=rep)
+    print("\n".join(rep))
+
+
+def test_segmented_matches_unsegmented(segments):
+    w = synth.Workload("t", "gated", "f32", 2, 2, 500, 64, 64, seed=42, h0_std=0.3)
+    inp = synth.make_inputs(w, alpha_mode="one")
+    segments(0)
+    a = run_hip(inp, "gated", "f32", backward=True)
+    segments(2)
+    b = run_hip(inp, "gated", "f32", backward=True)
+    for name in a:
+        if a[name] is not None:
+            err = np.max(np.abs(a[name] - b[name]))
+            assert err <= 1e-4 * max(1e-30, np.max(np.abs(a[name]))), (name, err)
