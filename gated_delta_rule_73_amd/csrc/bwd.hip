@@ -286,6 +286,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   constexpr bool GATED = VAR == VAR_GATED;
   __shared__ __align__(16) char smem[Ly::BIG];
   __shared__ float gs[CH], bs[CH], dbs[CH], red[NT / 64];
+  __shared__ float part8[NT / CH][CH], part8b[NT / CH][CH];  // partial column / row sums
   __shared__ float rq[4][CH], rkh[8][CH], rkb[8][CH];
 
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
@@ -346,6 +347,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       __syncthreads();
       pW.store(Wh, LD);  // rows i (value), columns j (key): read k-major below
       pdW.store(dWh, LD);
+      if constexpr (GATED) {  // <W0, dW> over this block of rows, from the registers
+#pragma unroll
+        for (int it = 0; it < decltype(pW)::IT; ++it)
+#pragma unroll
+          for (int x = 0; x < decltype(pW)::VE; ++x) gam += (float)pW.elem(it, x) * (float)pdW.elem(it, x);
+      }
       if (ih + 1 < NH) {
         pW.load(Hs + u * D * D + (long)(ih + 1) * KH * D, D, KH);
         pdW.load(dHs + u * D * D + (long)(ih + 1) * KH * D, D, KH);
@@ -361,12 +368,6 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       for (int e = 0; e < 2; ++e) {
         const int id = w + 8 * e;
         acc3[e] = mma_k<E, KH>(acc3[e], rowk(dOs + ih * KH, LD), 16 * (id >> 2), rowk(Rs + ih * KH, LD), 16 * (id & 3));
-      }
-      if constexpr (GATED) {
-        for (int idx = threadIdx.x; idx < D * KH; idx += NT) {
-          const int i = idx / D, j = idx % D;
-          gam += (float)Wh[i * LD + j] * (float)dWh[i * LD + j];
-        }
       }
     }
   }
@@ -469,12 +470,19 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   __syncthreads();
 #pragma unroll
   for (int qq = 0; qq < NQ; ++qq) store4_n(Vs, LD, 16 * wm, 16 * (wn * NQ + qq), dva[qq]);
-  if (threadIdx.x < CH) {  // dbeta from T = Linv diag(beta) (dT and Linv are zero above the diagonal)
-    const int s = threadIdx.x;
+  {  // dbeta from T = Linv diag(beta): column sums, eight threads per column
+    const int s = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
-#pragma unroll 16
-    for (int t = 0; t < CH; ++t) a += dTs[t * LF + s] * Li[t * LF + s];
-    dbs[s] = a;
+#pragma unroll
+    for (int t = pt; t < CH; t += NT / CH) a += dTs[t * LF + s] * Li[t * LF + s];
+    part8[pt][s] = a;
+  }
+  __syncthreads();
+  if (threadIdx.x < CH) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / CH; ++i) a += part8[i][threadIdx.x];
+    dbs[threadIdx.x] = a;
   }
   __syncthreads();
   s2g_rows<E, CH, D, NT>(dv + tk * D, D, Vs, LD, n);
@@ -506,12 +514,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     store4_n(dTs, LF, 16 * (id >> 2), 16 * (id & 3), dl[e]);  // dTs now holds dL
   }
   __syncthreads();
-  if (threadIdx.x < CH) {  // dbeta from L = I + diag(beta) A (dL is zero on and above the diagonal)
-    const int t = threadIdx.x;
+  {  // dbeta from L = I + diag(beta) A: row sums (dL is zero on and above the diagonal)
+    const int t = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
-#pragma unroll 16
-    for (int s = 0; s < CH; ++s) a += dTs[t * LF + s] * As[t * LF + s];
-    dbs[t] += a;
+#pragma unroll
+    for (int s = pt; s < CH; s += NT / CH) a += dTs[t * LF + s] * As[t * LF + s];
+    part8b[pt][t] = a;
   }
 
   // ================= phase 3: Gram slots and the decay gradient
@@ -566,16 +574,21 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     dka[qq] = mma_k<E, CH>(dka[qq], colk(Ats, LDR), 16 * wm, colk(Ks, LD), 16 * nt);
     dka[qq] = mma_k<E, CH>(dka[qq], colk(Mts, LDR), 16 * wm, colk(Qs, LD), 16 * nt);
   }
-  if constexpr (GATED) {
-    if (threadIdx.x < CH) {  // prefix sums along each row of the pair terms
-      const int uu = threadIdx.x;
-      float run = 0.f;
-#pragma unroll 16
-      for (int s = 0; s < CH; ++s) {  // entries with s >= uu are zero
-        run += Pair[uu * LF + s];
-        Pair[uu * LF + s] = run;
-      }
+  if constexpr (GATED) {  // prefix sums along each row of the pair terms: lanes over columns
+    for (int uu = w; uu < CH; uu += NT / 64) {
+      float* row = Pair + uu * LF;
+      row[lane_id()] = wave_incl_scan(row[lane_id()]);
     }
+  }
+  __syncthreads();
+  if constexpr (GATED) {  // rectangle sums: sum over u >= t of the prefix at column t-1
+    const int t = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
+    float a = 0.f;
+    if (t > 0) {
+#pragma unroll
+      for (int uu = pt; uu < CH; uu += NT / CH) a += (uu >= t) ? Pair[uu * LF + t - 1] : 0.f;
+    }
+    part8[pt][t] = a;
   }
   __syncthreads();
   // outputs: dq, dk through LDS (the dR/dX regions are free now)
@@ -591,10 +604,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     const int t = threadIdx.x;
     if constexpr (GATED) {
       float rect = 0.f;  // sum over u >= t of sum_{s < t} pair(u, s)
-      if (t > 0) {
-#pragma unroll 16
-        for (int uu = 0; uu < CH; ++uu) rect += (uu >= t) ? Pair[uu * LF + t - 1] : 0.f;
-      }
+#pragma unroll
+      for (int i = 0; i < NT / CH; ++i) rect += part8[i][t];
       // suffix over u >= t of the rows' Qhat.dQhat + Khat.dKhat (reversed inclusive scan)
       const int tr = CH - 1 - t;
       const float xr = rq[tr >> 4][tr] + rkh[tr >> 4][tr] + rkh[(tr >> 4) + 4][tr];
@@ -611,7 +622,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       const float dla = rect + suf + pre + expf(gn) * g4;
       if (t < n) dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
     }
-    if (t < n) dbeta[tk + t] = (E)dbs[t];
+    float db = dbs[t];
+#pragma unroll
+    for (int i = 0; i < NT / CH; ++i) db += part8b[i][t];
+    if (t < n) dbeta[tk + t] = (E)db;
   }
   __syncthreads();
   s2g_rows<E, CH, D, NT>(dq + tk * D, D, sq, LD, n);

@@ -8,11 +8,15 @@ namespace gdr {
 enum Var { VAR_DELTANET = 0, VAR_GATED = 1, VAR_KDA = 2, VAR_GDN2 = 3 };
 
 // Li = L^{-1} for a unit lower-triangular 64x64 float matrix L (only entries strictly below
-// the diagonal are read).  Blocked in 16x16 tiles: each diagonal tile is inverted by
-// right-looking substitution (one lane per column), then the tiles below the diagonal are
-// filled in order of their distance from it, X_ij = -inv(L_ii) * sum_{j<=m<i} L_im X_mj,
-// with float32 matrix-core products.  scratch: 4*256 floats.  Needs >= 256 threads; ends
-// with a block barrier.  Li's tiles above the diagonal are set to zero.
+// the diagonal are read).  Blocked:
+//   1. each 16x16 diagonal tile is inverted by forward substitution, one lane per column,
+//      rows of L read as 16-byte vectors;
+//   2. inside each 32x32 diagonal half, X_10 = -inv(L_11) L_10 inv(L_00) on 16x16 tiles
+//      (one wave per half; the intermediate stays in that wave's scratch);
+//   3. the lower-left 32x32 block, X = -inv(L_hh) L_hl inv(L_ll), with all four waves.
+// Float32 matrix-core products throughout.  scratch: 4*256 floats.  Needs >= 256 threads;
+// ends with a block barrier.  Li's entries above the diagonal are set to zero.  ldl, ldi must
+// be multiples of 4 (16-byte rows).
 template <int NT>
 __device__ void solve_unit_lower64(const float* L, int ldl, float* Li, int ldi, float* scratch) {
   static_assert(NT >= 256, "solve needs four waves");
@@ -21,39 +25,50 @@ __device__ void solve_unit_lower64(const float* L, int ldl, float* Li, int ldi, 
     const int c = l, o = 16 * w;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      // x_r = [r == c] - sum_{k<r} L_rk x_k
+      float row[16];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(L + (o + r) * ldl + o + 4 * q);
+        row[4 * q] = v.x; row[4 * q + 1] = v.y; row[4 * q + 2] = v.z; row[4 * q + 3] = v.w;
+      }
+      float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int r = kk + 1; r < 16; ++r) x[r] = fmaf(-L[(o + r) * ldl + o + kk], x[kk], x[r]);
+      for (int k = 0; k < r; ++k) acc = fmaf(-row[k], x[k], acc);
+      x[r] = acc;
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) Li[(o + r) * ldi + o + c] = x[r];
   }
   for (int idx = threadIdx.x; idx < 64 * 64; idx += NT) {
-    const int r = idx >> 6, c = idx & 63;
-    if ((c >> 4) > (r >> 4)) Li[r * ldi + c] = 0.f;
+    const int r = idx >> 6, cc = idx & 63;
+    if ((cc >> 4) > (r >> 4)) Li[r * ldi + cc] = 0.f;
   }
   __syncthreads();
-  for (int dist = 1; dist < 4; ++dist) {
-    const bool act = w < 4 - dist;
-    const int j = w, i = w + dist;
-    if (act) {
-      f32x4 acc = zero4();
-      for (int m = j; m < i; ++m)
-        acc = mma_k<float, 16>(acc, rowk(L + (16 * i) * ldl + 16 * m, ldl), 0,
-                               colk(Li + (16 * m) * ldi + 16 * j, ldi), 0);
-      store4_n(scratch + w * 256, 16, 0, 0, acc);
-    }
-    __syncthreads();
-    if (act) {
-      const f32x4 acc = mma_k<float, 16>(zero4(), rowk(Li + (16 * i) * ldi + 16 * i, ldi), 0,
-                                         colk(scratch + w * 256, 16), 0);
+  if (w < 2) {  // 16x16 merge inside half w: rows 32w+16.., columns 32w..
+    const int a = 32 * w;
+    const f32x4 y = mma_k<float, 16>(zero4(), rowk(L + (a + 16) * ldl + a, ldl), 0, colk(Li + a * ldi + a, ldi), 0);
+    float* sc = scratch + w * 256;
+    store4_n(sc, 16, 0, 0, y);
+    const f32x4 xv = mma_k<float, 16>(zero4(), rowk(Li + (a + 16) * ldi + a + 16, ldi), 0, colk(sc, 16), 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Li[(16 * i + acc_row(0, r)) * ldi + 16 * j + acc_col(0)] = -acc[r];
-    }
-    __syncthreads();
+    for (int r = 0; r < 4; ++r) Li[(a + 16 + acc_row(0, r)) * ldi + a + acc_col(0)] = -xv[r];
   }
+  __syncthreads();
+  if (w < 4) {  // Y = L_hl inv(L_ll): rows 32.., columns 0..31; one 16x16 tile per wave
+    const int mt = w >> 1, nt = w & 1;
+    const f32x4 y = mma_k<float, 32>(zero4(), rowk(L + 32 * ldl, ldl), 16 * mt, colk(Li, ldi), 16 * nt);
+    store4_n(scratch, 32, 16 * mt, 16 * nt, y);
+  }
+  __syncthreads();
+  if (w < 4) {  // X = -inv(L_hh) Y
+    const int mt = w >> 1, nt = w & 1;
+    const f32x4 xv = mma_k<float, 32>(zero4(), rowk(Li + 32 * ldi + 32, ldi), 16 * mt, colk(scratch, 32), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Li[(32 + acc_row(16 * mt, r)) * ldi + acc_col(16 * nt)] = -xv[r];
+  }
+  __syncthreads();
 }
 
 // T^T as a matrix-core A operand, read from L^{-1}: element (m = s, k = t) = Linv[t][s] beta_s.

@@ -125,60 +125,62 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
 
 // ---------------------------------------------------------------------------------------
 // Scan: per (value-row tile, head, sequence), sequential over the sequence's chunks.
-// The tile of W (BV rows x D) lives in accumulators as W^T tiles: wave w owns key tiles
-// jt = w + 4q and every value sub-tile.
+// The tile of W (BV value rows x D) lives in accumulators as W^T tiles: wave w owns key tiles
+// jt = w + 4q and every value sub-tile.  Each step computes R = U - X W0^T for the tile's
+// value columns, the output columns O = scale (e^g (Q W0^T) + M R) (the tile holds every
+// key column of its value rows, so the output needs nothing from other tiles), records W0
+// and R for the backward, and carries W_next = e^{g_n} W0 + R^T (e^{g_n-g} K).
+// FULL = false is the segment-map pass (ScanSeg mode 1): no output and nothing recorded.
 // ---------------------------------------------------------------------------------------
 // Operands of one chunk of the forward scan, held in registers while they are in flight.
 // Gated DeltaNet-2 also needs the erase gates (for the erase direction a = beta e*k) and the
-// value tile's write gates and values (for b = beta w*v).
-// Kimi Delta Attention reads Kbar = e^{g_n-g} K (prepared per chunk) in place of K and the
-// per-key-channel decay e^{g_n} of the rows this lane holds.
-template <typename E, int D, int BV, int VAR>
+// value tile's write gates and values (for b = beta w*v), and M_qk for the output.
+// Kimi Delta Attention reads Kbar = e^{g_n-g} K and Qhat = e^g Q (prepared per chunk) in
+// place of K and Q, and the per-key-channel decay e^{g_n} of the rows this lane holds.
+template <typename E, int D, int BV, int VAR, bool FULL>
 struct FwdScanOps {
-  RegTile<E, CH, D, 256> x, k;
-  RegTile<E, CH, BV, 256> u;
-  float g;
-};
-template <typename E, int D, int BV>
-struct FwdScanOps<E, D, BV, VAR_GDN2> {
-  RegTile<E, CH, D, 256> x, k, e;
+  RegTile<E, CH, D, 256> x, k, q, e;
   RegTile<E, CH, BV, 256> u, vt, wt;
+  RegTile<E, CH, CH, 256> m, m2;
   float g, b;
-};
-template <typename E, int D, int BV>
-struct FwdScanOps<E, D, BV, VAR_KDA> {
-  RegTile<E, CH, D, 256> x, k;
-  RegTile<E, CH, BV, 256> u;
   f32x4 eg[D / 64];
 };
 
-template <typename E, int D, int BV, int VAR>
+template <typename E, int D, int BV, int VAR, bool FULL>
 __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ k, const E* __restrict__ Xg,
                                                   const E* __restrict__ Ug, const float* __restrict__ Gg,
                                                   const float* __restrict__ h0, E* __restrict__ Hs,
                                                   E* __restrict__ Rg, float* __restrict__ ht,
                                                   const E* __restrict__ vin, const E* __restrict__ beta,
-                                                  const E* __restrict__ erase, const E* __restrict__ write) {
+                                                  const E* __restrict__ erase, const E* __restrict__ write,
+                                                  const E* __restrict__ q, const E* __restrict__ Mg,
+                                                  const E* __restrict__ M2g, E* __restrict__ o) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2;
   constexpr bool KDA = VAR == VAR_KDA;
   constexpr bool DEC = VAR == VAR_GATED || VAR == VAR_GDN2;  // scalar decay
+  constexpr bool OUT_G2 = FULL && G2;
   __shared__ __align__(16) E Xs[CH * LD];
   __shared__ __align__(16) E Ks[CH * LD];
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];      // a = beta e*k (GDN-2)
   __shared__ __align__(16) E Bd[G2 ? BV * LDR : 8];     // e^{g_n-g} b^T (GDN-2)
+  __shared__ __align__(16) E Bn[OUT_G2 ? CH * LDV : 8]; // b (GDN-2 output)
   __shared__ float bsh[CH];
   __shared__ __align__(16) E Us[CH * LDV];
   __shared__ __align__(16) E Ws[BV * LD];
   __shared__ __align__(16) E Rn[CH * LDV];
   __shared__ __align__(16) E Rd[BV * LDR];
+  __shared__ __align__(16) E Qs[FULL ? CH * LD : 8];
+  __shared__ __align__(16) E Ms[FULL ? CH * LDR : 8];
+  __shared__ __align__(16) E M2s[OUT_G2 ? CH * LDR : 8];
+  __shared__ __align__(16) E Os[FULL ? CH * LDV : 8];
   __shared__ float gs[CH];
 
   constexpr int NVR = D / BV;
   int sq, h, vt;
-  if (!scan_block(geo, sg.mode == 1 ? 2 * NVR : NVR, sq, h, vt)) return;
-  const bool virt = vt >= NVR;  // mode 1: rows of the segment's linear part
+  if (!scan_block(geo, FULL ? NVR : 2 * NVR, sq, h, vt)) return;
+  const bool virt = !FULL && vt >= NVR;  // segment-map pass: rows of the segment's linear part
   const int i0 = (virt ? vt - NVR : vt) * BV;
   const SeqPos sp = seq_pos(geo, sq);
   const int w = wave_id();
@@ -192,7 +194,6 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     c0 = seg * sg.lseg;
     c1 = min(sp.nchunks, c0 + sg.lseg);
   }
-  const bool snap = sg.mode != 1;  // record W0 and R per chunk
   const float* init = nullptr;  // start memory (rows i, columns j); none: zero, or identity rows
   if (sg.mode == 2) init = sg.starts + (mem * sg.max_seg + seg) * D * D;
   else if (sg.mode == 0 && h0) init = h0 + sbase * D;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
 
   // Chunk c + 2 is loaded while chunk c is computed (two register sets, loop unrolled by two).
   // Loads past the last chunk repeat it, so every step issues the same memory operations.
-  using Ops = FwdScanOps<E, D, BV, VAR>;
+  using Ops = FwdScanOps<E, D, BV, VAR, FULL>;
   auto load = [&](Ops& p, int c) {
     const int cc = min(c, c1 - 1);
     const long u = (long)(sp.gc0 + cc) * geo.H + h;
@@ -226,23 +227,34 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       p.k.load(k + u * CH * D, D, CH);
 #pragma unroll
       for (int qq = 0; qq < NJ; ++qq) p.eg[qq] = *reinterpret_cast<const f32x4*>(Gg + u * D + acc_row(16 * (w + 4 * qq), 0));
+      if constexpr (FULL) p.q.load(q + u * CH * D, D, CH);
     } else {
       p.k.load(k + tk * D, D, n);
       p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+      if constexpr (FULL) p.q.load(q + tk * D, D, n);
     }
+    if constexpr (FULL) p.m.load(Mg + u * CH * CH, CH, CH);
     if constexpr (G2) {
       p.e.load(erase + tk * D, D, n);
       p.vt.load(vin + tk * D + i0, D, n);
       p.wt.load(write + tk * D + i0, D, n);
       const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
       p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+      if constexpr (FULL) p.m2.load(M2g + u * CH * CH, CH, CH);
     }
   };
   auto step = [&](int c, Ops& p) {
     const long u = (long)(sp.gc0 + c) * geo.H + h;
+    const int n = min(CH, sp.len - c * CH);
+    const long tk = tok_index(geo, sp.b, h, sp.bos + c * CH);
     p.x.store(Xs, LD);
     p.k.store(Ks, LD);
     p.u.store(Us, LDV);
+    if constexpr (FULL) {
+      p.q.store(Qs, LD);
+      p.m.store(Ms, LDR);
+      if constexpr (G2) p.m2.store(M2s, LDR);
+    }
     f32x4 egk[NJ];  // KDA: this chunk's per-row decay, kept before p is refilled
     if constexpr (KDA) {
 #pragma unroll
@@ -271,14 +283,17 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
 #pragma unroll
       for (int it = 0; it < decltype(p.vt)::IT; ++it) {
         const int t = p.vt.row(it), i = p.vt.col(it);
-        const float sc = virt ? 0.f : bsh[t] * __expf(gn0 - gs[t]);
+        const float bt = virt ? 0.f : bsh[t];
+        const float sc = bt * __expf(gn0 - gs[t]);
 #pragma unroll
-        for (int x = 0; x < decltype(p.vt)::VE; ++x)
-          Bd[(i + x) * LDR + t] = (E)(sc * (float)p.wt.elem(it, x) * (float)p.vt.elem(it, x));
+        for (int x = 0; x < decltype(p.vt)::VE; ++x) {
+          const float bv = (float)p.wt.elem(it, x) * (float)p.vt.elem(it, x);
+          Bd[(i + x) * LDR + t] = (E)(sc * bv);
+          if constexpr (FULL) Bn[t * LDV + i + x] = (E)(bt * bv);
+        }
       }
     }
     load(p, c + 2);
-    if (snap) s2g_full<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD);
     const float gn = gs[CH - 1];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
@@ -296,8 +311,28 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       store4_n(Rn, LDV, 16 * w, 16 * it, rv);
       store4_t(Rd, LDR, 16 * w, 16 * it, rd);
     }
+    if constexpr (FULL) s2g_full<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD);
     __syncthreads();
-    if (snap) s2g_full<E, CH, BV, NT>(Rg + u * CH * D + i0, D, Rn, LDV);
+    if constexpr (FULL) {
+      s2g_full<E, CH, BV, NT>(Rg + u * CH * D + i0, D, Rn, LDV);
+      if (o) {
+        // O = scale (e^g (Q W0^T) + M R [+ M_qk b]) for this tile's value columns
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+          const f32x4 a1 = mma_k<E, D>(zero4(), rowk(Qs, LD), 16 * w, rowk(Ws, LD), 16 * it);
+          f32x4 a2 = mma_k<E, CH>(zero4(), rowk(Ms, LDR), 16 * w, colk(Rn, LDV), 16 * it);
+          if constexpr (G2) a2 = mma_k<E, CH>(a2, rowk(M2s, LDR), 16 * w, colk(Bn, LDV), 16 * it);
+          f32x4 ov;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float e = 1.f;
+            if constexpr (DEC) e = __expf(gs[acc_row(16 * w, r)]);
+            ov[r] = geo.scale * (e * a1[r] + a2[r]);
+          }
+          store4_n(Os, LDV, 16 * w, 16 * it, ov);
+        }
+      }
+    }
     float eg = 1.f;
     if constexpr (DEC) eg = __expf(gn);
 #pragma unroll
@@ -315,6 +350,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         }
       }
     __syncthreads();
+    if constexpr (FULL) {
+      if (o) s2g_rows<E, CH, BV, NT>(o + tk * D + i0, D, Os, LDV, n);
+    }
   };
   if (c1 > c0) {
     Ops pa, pb;
@@ -326,7 +364,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     }
   }
   float* out = nullptr;  // final memory: ht, or this segment's map
-  if (sg.mode == 1) out = sg.maps + ((mem * sg.max_seg + seg) * 2 + (virt ? 1 : 0)) * D * D;
+  if (!FULL) out = sg.maps + ((mem * sg.max_seg + seg) * 2 + (virt ? 1 : 0)) * D * D;
   else if (ht && seg == nseg - 1) out = ht + sbase * D;
   if (out) {
 #pragma unroll
@@ -338,70 +376,6 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         *reinterpret_cast<float4*>(out + (long)i * D + j0) = make_float4(x[0], x[1], x[2], x[3]);
       }
   }
-}
-
-// ---------------------------------------------------------------------------------------
-// Output: per (head, chunk).  O = scale * (e^g * (Q W0^T) + M R).
-// ---------------------------------------------------------------------------------------
-template <typename E, int D, int VAR>
-__global__ __launch_bounds__(256) void k_fwd_out(Geo geo, const E* __restrict__ q, const E* __restrict__ Mg,
-                                                 const E* __restrict__ Rg, const float* __restrict__ Gg,
-                                                 const E* __restrict__ Hs, E* __restrict__ o,
-                                                 const E* __restrict__ M2g, const E* __restrict__ vin,
-                                                 const E* __restrict__ beta, const E* __restrict__ write) {
-  constexpr int NT = 256, LD = D + pad16<E>(), LDR = CH + pad16<E>();
-  constexpr bool G2 = VAR == VAR_GDN2;
-  constexpr bool KDA = VAR == VAR_KDA;  // q is Qhat = e^g Q, prepared per chunk
-  __shared__ __align__(16) E Qs[CH * LD];
-  __shared__ __align__(16) E Ws[D * LD];
-  __shared__ __align__(16) E Ms[CH * LDR];
-  __shared__ __align__(16) E Rs[CH * LD];
-  __shared__ __align__(16) E M2s[G2 ? CH * LDR : 8];
-  __shared__ __align__(16) E Bs[G2 ? CH * LD : 8];
-  __shared__ float gs[CH];
-  const int gc = blockIdx.x, h = blockIdx.y;
-  const ChunkPos cp = chunk_pos(geo, gc);
-  const long u = (long)gc * geo.H + h;
-  const long tk = tok_index(geo, cp.b, h, cp.t0);
-  const int w = wave_id();
-  if constexpr (KDA) g2s_rows<E, CH, D, NT>(Qs, LD, q + u * CH * D, D, CH);
-  else g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, cp.n);
-  g2s_rows<E, D, D, NT>(Ws, LD, Hs + u * D * D, D, D);
-  g2s_rows<E, CH, CH, NT>(Ms, LDR, Mg + u * CH * CH, CH, CH);
-  g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
-  if (!KDA && threadIdx.x < CH) gs[threadIdx.x] = Gg[u * CH + threadIdx.x];
-  if constexpr (G2) {
-    g2s_rows<E, CH, CH, NT>(M2s, LDR, M2g + u * CH * CH, CH, CH);
-    RegTile<E, CH, D, NT> rv, rw;
-    rv.load(vin + tk * D, D, cp.n);
-    rw.load(write + tk * D, D, cp.n);
-#pragma unroll
-    for (int it = 0; it < decltype(rv)::IT; ++it) {
-      const int t = rv.row(it), i = rv.col(it);
-      const float b = (t < cp.n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
-#pragma unroll
-      for (int x = 0; x < decltype(rv)::VE; ++x) Bs[t * LD + i + x] = (E)(b * (float)rw.elem(it, x) * (float)rv.elem(it, x));
-    }
-  }
-  __syncthreads();
-  f32x4 ov[D / 16];
-#pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    const f32x4 a1 = mma_k<E, D>(zero4(), rowk(Qs, LD), 16 * w, rowk(Ws, LD), 16 * nt);
-    f32x4 a2 = mma_k<E, CH>(zero4(), rowk(Ms, LDR), 16 * w, colk(Rs, LD), 16 * nt);
-    if constexpr (G2) a2 = mma_k<E, CH>(a2, rowk(M2s, LDR), 16 * w, colk(Bs, LD), 16 * nt);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float e = 1.f;
-      if constexpr (VAR == VAR_GATED || VAR == VAR_GDN2) e = __expf(gs[acc_row(16 * w, r)]);
-      ov[nt][r] = geo.scale * (e * a1[r] + a2[r]);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) store4_n(Qs, LD, 16 * w, 16 * nt, ov[nt]);
-  __syncthreads();
-  s2g_rows<E, CH, D, NT>(o + tk * D, D, Qs, LD, cp.n);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -429,35 +403,34 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, float* 
   const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
   const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
   const float* gin = KDA ? p.Gn : p.G;
-  auto scan = [&](const ScanSeg& sg, const float* h0, float* htp, int nv_mult) {
-    if (p.bv == 16) {
-      hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, nv_mult * D / 16), sg.mode ? sg.max_seg : 1),
+  E* out = want_out ? (E*)o : nullptr;
+  auto scan = [&](auto full, const ScanSeg& sg, const float* h0, float* htp) {
+    constexpr bool F = decltype(full)::value;
+    const int nvm = F ? 1 : 2;
+    if (std::is_same<E, float>::value || p.bv == 16) {
+      hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR, F>), dim3(scan_grid(g, nvm * D / 16), sg.mode ? sg.max_seg : 1),
                          dim3(256), 0, st, g, sg, kin, (const E*)p.X, (const E*)p.Ub, gin, h0, (E*)p.Hs, (E*)p.R, htp,
-                         (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
-    } else {
-      hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, nv_mult * D / 32), sg.mode ? sg.max_seg : 1),
+                         (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write, qin,
+                         (const E*)p.M, (const E*)p.M2, out);
+    } else if constexpr (!std::is_same<E, float>::value) {
+      hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR, F>), dim3(scan_grid(g, nvm * D / 32), sg.mode ? sg.max_seg : 1),
                          dim3(256), 0, st, g, sg, kin, (const E*)p.X, (const E*)p.Ub, gin, h0, (E*)p.Hs, (E*)p.R, htp,
-                         (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write);
+                         (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write, qin,
+                         (const E*)p.M, (const E*)p.M2, out);
     }
   };
   if (p.lseg == 0) {
     TraceScope ts_("fwd_scan", st);
-    scan(ScanSeg{0, 0, 1, nullptr, nullptr}, in.h0, ht, 1);
+    scan(std::true_type{}, ScanSeg{0, 0, 1, nullptr, nullptr}, in.h0, ht);
   } else {
     {
       TraceScope ts_("fwd_scan_maps", st);
-      scan(ScanSeg{1, p.lseg, p.max_seg, p.seg_maps, nullptr}, nullptr, nullptr, 2);
+      scan(std::false_type{}, ScanSeg{1, p.lseg, p.max_seg, p.seg_maps, nullptr}, nullptr, nullptr);
     }
     const hipError_t e = launch_seg_combine(p, ScanSeg{0, p.lseg, p.max_seg, p.seg_maps, nullptr}, in.h0, false, st);
     if (e != hipSuccess) return e;
     TraceScope ts_("fwd_scan", st);
-    scan(ScanSeg{2, p.lseg, p.max_seg, nullptr, p.seg_starts}, nullptr, ht, 1);
-  }
-  if (want_out && g.total_chunks > 0) {
-    TraceScope ts_("fwd_out", st);
-    hipLaunchKernelGGL((k_fwd_out<E, D, VAR>), cgrid, dim3(256), 0, st, g, qin, (const E*)p.M,
-                       (const E*)p.R, gin, (const E*)p.Hs, (E*)o, (const E*)p.M2, (const E*)in.v,
-                       (const E*)in.beta, (const E*)in.write);
+    scan(std::true_type{}, ScanSeg{2, p.lseg, p.max_seg, nullptr, p.seg_starts}, nullptr, ht);
   }
   return hipGetLastError();
 }

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
                                                        const E* __restrict__ write, E* __restrict__ Xo,
                                                        E* __restrict__ Uo, E* __restrict__ U2o, E* __restrict__ Mqa,
                                                        E* __restrict__ Mqk, float* __restrict__ Go) {
-  constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 1;
+  constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g K, then X'
   __shared__ __align__(16) E Qs[CH * LD];   // Q, then A_kk B, then U''
   __shared__ __align__(16) E As[CH * LD];   // a = beta e*k
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
 // ---------------------------------------------------------------------------------------
 template <typename E, int D>
 struct G2WyLds {
-  static constexpr int LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 1;
+  static constexpr int LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   static constexpr int TK = CH * LD * (int)sizeof(E), SQ = CH * LDT * (int)sizeof(E), F = CH * LF * 4;
   static constexpr int U1 = 3 * F, U2 = 4 * TK;
   static constexpr int BYTES = 2 * TK + 3 * SQ + (U1 > U2 ? U1 : U2);
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
 // ---------------------------------------------------------------------------------------
 template <typename E, int D>
 struct G2GramLds {
-  static constexpr int LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 1;
+  static constexpr int LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   static constexpr int TK = CH * LD * (int)sizeof(E), SQ = CH * LDT * (int)sizeof(E), F = CH * LF * 4;
   static constexpr int BYTES = 4 * TK + 4 * SQ + F;
 };

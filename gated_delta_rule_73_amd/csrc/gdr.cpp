@@ -44,13 +44,19 @@ struct Sizes {
   size_t bwd_ws() const { return Ub + dHs + dR + g2 + seg; }
 };
 
-// Scan shape.  Value tiles of 32 rows when the memories give at least one per CU, else 16.
+// Scan shape.  Value tiles of 32 rows when the memories give at least one per CU, else 16
+// (always 16 for float32 I/O, whose operand tiles take twice the LDS).
 // When even then the memories' tiles number under 256 (fewer than one workgroup per CU), each
 // sequence's chunks are cut into segments (see ScanSeg) so that about 1024 workgroups run,
 // with at least 16 chunks per segment.  GDR_SEG_CHUNKS, if set, forces the segment length in
-// chunks (0: never segment); it exists for tuning and changes nothing but speed.
-void plan_scans(long long memories, int d, int max_chunks, Sizes* s) {
-  s->bv = (memories * (d / 32) >= 256) ? 32 : 16;
+// chunks (0: never segment) and GDR_SCAN_BV the value tile (16 or 32); they exist for tuning
+// and change nothing but speed.
+void plan_scans(long long memories, int d, int max_chunks, bool f32, Sizes* s) {
+  s->bv = (!f32 && memories * (d / 32) >= 256) ? 32 : 16;
+  if (const char* env = std::getenv("GDR_SCAN_BV")) {
+    const int bv = std::atoi(env);
+    if (bv == 16 || (bv == 32 && !f32)) s->bv = bv;
+  }
   const long long tiles = memories * (d / s->bv);
   int lseg = 0;
   if (const char* env = std::getenv("GDR_SEG_CHUNKS")) {
@@ -137,7 +143,7 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   if (g2) s.g2 = align_up(U * (5 * C * D + 6 * C * C + 4 * C) * 4, A);
   else if (kda) s.g2 = align_up(U * (4 * C * D + 2 * C * C + D) * 4, A);
   else s.g2 = 0;
-  plan_scans((long long)s.nstates * p->H, p->dk, max_chunks, &s);
+  plan_scans((long long)s.nstates * p->H, p->dk, max_chunks, p->dtype == GDR_F32, &s);
   s.seg = s.lseg ? align_up((size_t)s.nstates * p->H * s.max_seg * 3 * D * D * 4, A) : 0;
   *sz = s;
   return GDR_OK;

@@ -70,7 +70,7 @@ __device__ void kda_flags(const float* Gs, int ldg, int* unsafe) {
 template <typename E, int D, int NT, bool WITH_M>
 __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const float* Gs, const int* unsafe,
                           float* Ls, const float* lsc, float* Af, E* Mo, const E* qg, int n) {
-  constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 1;
+  constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 4;
   const int w = wave_id();
   for (int I = 0; I < 4; ++I) {
     const int ref = 16 * I;
@@ -145,7 +145,7 @@ __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const fl
 // ---------------------------------------------------------------------------------------
 template <typename E, int D>
 struct KdaPrepLds {
-  static constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 1, LDT = CH + pad16<E>();
+  static constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 4, LDT = CH + pad16<E>();
   static constexpr int TK = CH * LD * (int)sizeof(E), GB = CH * LDG * 4, F = CH * LF * 4;
   // G | Kr | Cl | K (then e^g K, then X) | Q (then Qr, then V, then U) | Ls
   static constexpr int oG = 0, oKr = GB, oCl = GB + TK, oK = GB + 2 * TK, oQ = GB + 3 * TK;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restr
 // ---------------------------------------------------------------------------------------
 template <typename E, int D>
 struct KdaWyLds {
-  static constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 1;
+  static constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 4;
   static constexpr int TK = CH * LD * (int)sizeof(E), GB = CH * LDG * 4, F = CH * LF * 4;
   // region 1: G | Kr | Cl during the Grams, then L^{-1} | dT | V | dR
   static constexpr int R1 = cmax(GB + 2 * TK, 2 * F + 2 * TK);
