@@ -22,7 +22,9 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
                                                        const E* __restrict__ alpha, const E* __restrict__ erase,
                                                        const E* __restrict__ write, E* __restrict__ Xo,
                                                        E* __restrict__ Uo, E* __restrict__ U2o, E* __restrict__ Mqa,
-                                                       E* __restrict__ Mqk, float* __restrict__ Go) {
+                                                       E* __restrict__ Mqk, float* __restrict__ Go,
+                                                       float* __restrict__ Lio, float* __restrict__ Akko,
+                                                       float* __restrict__ Aako) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g K, then X'
   __shared__ __align__(16) E Qs[CH * LD];   // Q, then A_kk B, then U''
@@ -84,8 +86,13 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
       const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
       const bool keep = (which < 2) ? (s < t) : (s <= t);
       const float val = keep ? acc[r] * __expf(gs[t] - gs[s]) : 0.f;
-      if (which == 0) Akk[t * LDT + s] = (E)val;
-      else if (which == 1) Ls[t * LF + s] = val;
+      if (which == 0) {
+        Akk[t * LDT + s] = (E)val;
+        Akko[(u * CH + t) * CH + s] = val;
+      } else if (which == 1) {
+        Ls[t * LF + s] = val;
+        Aako[(u * CH + t) * CH + s] = val;
+      }
       else if (which == 2) Mqk[(u * CH + t) * CH + s] = (E)val;
       else Mqa[(u * CH + t) * CH + s] = (E)val;
     }
@@ -96,10 +103,13 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
       Mqk[(u * CH + t) * CH + s] = (E)0.f;
       Mqa[(u * CH + t) * CH + s] = (E)0.f;
       Akk[t * LDT + s] = (E)0.f;
+      Akko[(u * CH + t) * CH + s] = 0.f;
+      Aako[(u * CH + t) * CH + s] = 0.f;
     }
   }
   __syncthreads();
   solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ti));
+  s2g_full<float, CH, CH, NT>(Lio + u * CH * CH, CH, Li, LF);  // L^{-1} for the backward
   for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
     const int t = idx >> 6, s = idx & 63;
     Ti[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] : 0.f);
@@ -304,17 +314,16 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
 }
 
 // ---------------------------------------------------------------------------------------
-// Backward, stage 2: the solve side.  Recomputes A_kk, A_ak and L^{-1}; then
+// Backward, stage 2: the solve side.  With A_kk and L^{-1} as the forward computed them,
 //   dKhat = L^-T dX',  dC = -L^-T dR',  dA_ak = tril_strict(-dKhat X'^T + dC U''^T),
 //   dA_kk = tril_strict(dC B^T),  dB = dB_state + A_kk^T dC + M_qk^T dO,
 //   dv = beta w*dB, dw = beta v*dB;  dk += e^g dKhat.
 // ---------------------------------------------------------------------------------------
 template <typename E, int D>
 struct G2WyLds {
-  static constexpr int LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
-  static constexpr int TK = CH * LD * (int)sizeof(E), SQ = CH * LDT * (int)sizeof(E), F = CH * LF * 4;
-  static constexpr int U1 = 3 * F, U2 = 4 * TK;
-  static constexpr int BYTES = 2 * TK + 3 * SQ + (U1 > U2 ? U1 : U2);
+  static constexpr int LD = D + pad16<E>(), LDT = CH + pad16<E>();
+  static constexpr int TK = CH * LD * (int)sizeof(E), SQ = CH * LDT * (int)sizeof(E);
+  static constexpr int BYTES = TK + 3 * SQ + 4 * TK;
 };
 
 template <typename E, int D>
@@ -326,19 +335,14 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
                                                      const E* __restrict__ dRg, E* __restrict__ dv,
                                                      E* __restrict__ dw, Plan p) {
   using Ly = G2WyLds<E, D>;
-  constexpr int NT = 256, LD = Ly::LD, LDT = Ly::LDT, LF = Ly::LF;
+  constexpr int NT = 256, LD = Ly::LD, LDT = Ly::LDT;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ __align__(16) float scr[4 * 256];
   __shared__ float gs[CH], bs[CH], rk[4][CH], rb[4][CH];
   E* Ks = reinterpret_cast<E*>(smem);
-  E* As = Ks + CH * LD;
-  E* LiT = As + CH * LD;
+  E* LiT = Ks + CH * LD;
   E* AkkE = LiT + CH * LDT;
   E* Mqk = AkkE + CH * LDT;
   char* un = reinterpret_cast<char*>(Mqk + CH * LDT);
-  float* Akk = reinterpret_cast<float*>(un);
-  float* Aak = Akk + CH * LF;
-  float* Li = Aak + CH * LF;
   E* P1 = reinterpret_cast<E*>(un);
   E* P2 = P1 + CH * LD;
   E* P3 = P2 + CH * LD;
@@ -355,47 +359,21 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
     gs[t] = Gg[u * CH + t];
     bs[t] = t < n ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
   }
-  {
-    RegTile<E, CH, D, NT> rkk, re;
-    rkk.load(k + tk * D, D, n);
-    re.load(erase + tk * D, D, n);
-    rkk.store(Ks, LD);
-    g2s_rows<E, CH, CH, NT>(Mqk, LDT, M2g + u * CH * CH, CH, CH);
-    __syncthreads();
+  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
+  g2s_rows<E, CH, CH, NT>(Mqk, LDT, M2g + u * CH * CH, CH, CH);
+  {  // (L^{-1})^T and A_kk as the forward computed them
+    RegTile<float, CH, CH, NT> rli, rakk;
+    rli.load(p.Li + u * CH * CH, CH, CH);
+    rakk.load(p.A1 + u * CH * CH, CH, CH);
 #pragma unroll
-    for (int it = 0; it < decltype(rkk)::IT; ++it) {
-      const int t = rkk.row(it), j = rkk.col(it);
+    for (int it = 0; it < decltype(rli)::IT; ++it) {
+      const int t = rli.row(it), s0 = rli.col(it);
 #pragma unroll
-      for (int x = 0; x < decltype(rkk)::VE; ++x)
-        As[t * LD + j + x] = (E)(bs[t] * (float)re.elem(it, x) * (float)rkk.elem(it, x));
-    }
-  }
-  __syncthreads();
-  float* akk_out = p.g2_akk + u * CH * CH;
-  float* aak_out = p.g2_aak + u * CH * CH;
-  for (int job = w; job < 32; job += 4) {  // 16 tiles each of A_kk and A_ak
-    const bool ak = job >= 16;
-    const int id = job & 15, mt = id >> 2, nt = id & 3;
-    const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * mt, rowk(ak ? As : Ks, LD), 16 * nt);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s2 = acc_col(16 * nt);
-      const float val = (s2 < t) ? acc[r] * __expf(gs[t] - gs[s2]) : 0.f;
-      if (ak) {
-        Aak[t * LF + s2] = val;
-        aak_out[t * CH + s2] = val;
-      } else {
-        Akk[t * LF + s2] = val;
-        akk_out[t * CH + s2] = val;
-        AkkE[t * LDT + s2] = (E)val;
+      for (int x = 0; x < decltype(rli)::VE; ++x) {
+        LiT[(s0 + x) * LDT + t] = (E)rli.elem(it, x);
+        AkkE[t * LDT + s0 + x] = (E)rakk.elem(it, x);
       }
     }
-  }
-  __syncthreads();
-  solve_unit_lower64<NT>(Aak, LF, Li, LF, scr);
-  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-    const int t = idx >> 6, s2 = idx & 63;
-    LiT[t * LDT + s2] = (E)Li[s2 * LF + t];  // (L^{-1})^T
   }
   __syncthreads();
   {  // dX' (float32 workspace) and dR' into the union region
@@ -582,8 +560,8 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
     const float* daak = p.g2_daak + u * CH * CH;
     const float* dmqk = p.g2_dmqk + u * CH * CH;
     const float* dmqa = p.g2_dmqa + u * CH * CH;
-    const float* akk = p.g2_akk + u * CH * CH;
-    const float* aak = p.g2_aak + u * CH * CH;
+    const float* akk = p.A1 + u * CH * CH;
+    const float* aak = p.A2 + u * CH * CH;
     const E* mqk = Mqkg + u * CH * CH;
     const E* mqa = Mqag + u * CH * CH;
     for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
@@ -726,7 +704,8 @@ hipError_t launch_fwd_prep_gdn2(const Plan& p, const gdr_inputs& in, hipStream_t
   TraceScope ts_("fwd_prep_gdn2", st);
   hipLaunchKernelGGL((k_fwd_prep_gdn2<E, D>), dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo,
                      (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
-                     (const E*)in.erase, (const E*)in.write, (E*)p.X, (E*)p.Ub, (E*)p.U2, (E*)p.M, (E*)p.M2, p.G);
+                     (const E*)in.erase, (const E*)in.write, (E*)p.X, (E*)p.Ub, (E*)p.U2, (E*)p.M, (E*)p.M2, p.G,
+                     p.Li, p.A1, p.A2);
   return hipGetLastError();
 }
 template hipError_t launch_fwd_prep_gdn2<bf16, 128>(const Plan&, const gdr_inputs&, hipStream_t);

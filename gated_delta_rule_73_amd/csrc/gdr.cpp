@@ -138,9 +138,9 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   s.Kb = kda ? align_up(U * C * D * s.esz, A) : 0;
   s.Qh = kda ? align_up(U * C * D * s.esz, A) : 0;
   s.Gn = kda ? align_up(U * D * 4, A) : 0;
-  // float32 backward intermediates per unit -- GDN-2: 5 of 64xD, 6 of 64x64, 4x64;
+  // float32 backward intermediates per unit -- GDN-2: 5 of 64xD, 4 of 64x64, 4x64;
   // KDA: 4 of 64xD, 2 of 64x64, D
-  if (g2) s.g2 = align_up(U * (5 * C * D + 6 * C * C + 4 * C) * 4, A);
+  if (g2) s.g2 = align_up(U * (5 * C * D + 4 * C * C + 4 * C) * 4, A);
   else if (kda) s.g2 = align_up(U * (4 * C * D + 2 * C * C + D) * 4, A);
   else s.g2 = 0;
   plan_scans((long long)s.nstates * p->H, p->dk, max_chunks, p->dtype == GDR_F32, &s);
@@ -233,8 +233,6 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
     pl.g2_daak = f; f += U * C * C;
     pl.g2_dmqk = f; f += U * C * C;
     pl.g2_dmqa = f; f += U * C * C;
-    pl.g2_akk = f; f += U * C * C;
-    pl.g2_aak = f; f += U * C * C;
     pl.g2_rows = f;
   }
   return pl;

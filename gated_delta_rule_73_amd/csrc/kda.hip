@@ -64,12 +64,12 @@ __device__ void kda_flags(const float* Gs, int ldg, int* unsafe) {
 
 // The chunk's Grams.  Inputs in LDS: Ks (K), Kr = K e^{g - g_ref} and, WITH_M, Qr = Q e^{g - g_ref}
 // (ref = the first token of the row's 16-token block), Gs, unsafe flags; Cl is scratch.
-// Outputs: Ls[t][s] = lsc_t A_ts below the diagonal, optionally (Af != NULL) Af[t][s] = A_ts
+// Outputs: Ls[t][s] = lsc_t A_ts below the diagonal, optionally (Af != NULL) Af[t*ldaf + s] = A_ts
 // (zero on and above the diagonal), Mo[t][s] = M_ts (global, zero above the diagonal).
 // qg: Q in global memory (token rows, used only for exact diagonal blocks).  Ends with a barrier.
 template <typename E, int D, int NT, bool WITH_M>
 __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const float* Gs, const int* unsafe,
-                          float* Ls, const float* lsc, float* Af, E* Mo, const E* qg, int n) {
+                          float* Ls, const float* lsc, float* Af, int ldaf, E* Mo, const E* qg, int n) {
   constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 4;
   const int w = wave_id();
   for (int I = 0; I < 4; ++I) {
@@ -97,7 +97,7 @@ __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const fl
         } else {
           const float a = (s < t) ? acc[r] : 0.f;
           Ls[t * LF + s] = lsc[t] * a;
-          if (Af) Af[t * LF + s] = a;
+          if (Af) Af[t * ldaf + s] = a;
         }
       }
     }
@@ -106,7 +106,7 @@ __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const fl
   for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
     const int t = idx >> 6, s = idx & 63;
     if (s > t) {
-      if (Af) Af[t * LF + s] = 0.f;
+      if (Af) Af[t * ldaf + s] = 0.f;
       if constexpr (WITH_M) Mo[t * CH + s] = (E)0.f;
     }
   }
@@ -130,9 +130,9 @@ __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const fl
       }
       if (s < t) {
         Ls[t * LF + s] = lsc[t] * a;
-        if (Af) Af[t * LF + s] = a;
+        if (Af) Af[t * ldaf + s] = a;
       } else if (Af) {
-        Af[t * LF + s] = 0.f;
+        Af[t * ldaf + s] = 0.f;
       }
       if constexpr (WITH_M) Mo[t * CH + s] = (E)m;
     }
@@ -161,7 +161,8 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
                                                       const E* __restrict__ v, const E* __restrict__ beta,
                                                       const E* __restrict__ alpha, E* __restrict__ Xo,
                                                       E* __restrict__ Uo, E* __restrict__ Mo, E* __restrict__ Kbo,
-                                                      E* __restrict__ Qho, float* __restrict__ Gno) {
+                                                      E* __restrict__ Qho, float* __restrict__ Gno,
+                                                      float* __restrict__ Lio, float* __restrict__ Ao) {
   using Ly = KdaPrepLds<E, D>;
   constexpr int NT = 256, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, LDT = Ly::LDT;
   __shared__ __align__(16) char smem[Ly::BYTES];
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   if (threadIdx.x < D) Gno[u * D + threadIdx.x] = __expf(Gs[(CH - 1) * LDG + threadIdx.x]);
   __syncthreads();
   E* Mc = Mo + u * CH * CH;
-  kda_grams<E, D, NT, true>(Ks, Qs, Kr, Cl, Gs, unsafe, Ls, bs, nullptr, Mc, q + tk * D, n);
+  kda_grams<E, D, NT, true>(Ks, Qs, Kr, Cl, Gs, unsafe, Ls, bs, Ao + u * CH * CH, CH, Mc, q + tk * D, n);
 
   // Khat = e^g K in place; V into the Q buffer
   for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
@@ -218,6 +219,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   float* Li = reinterpret_cast<float*>(smem + Ly::oLi);
   E* Ts = reinterpret_cast<E*>(smem + Ly::oT);
   solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ts));
+  s2g_full<float, CH, CH, NT>(Lio + u * CH * CH, CH, Li, LF);  // L^{-1} for the backward
   for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
     const int t = idx >> 6, s = idx & 63;
     Ts[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] * bs[s] : 0.f);
@@ -337,7 +339,8 @@ __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restr
 }
 
 // ---------------------------------------------------------------------------------------
-// Backward, stage 2: the solve side.  Recomputes g, A and L^{-1}; then
+// Backward, stage 2: the solve side.  With A and L^{-1} as the forward computed them (and g
+// recomputed for Khat = e^g K),
 //   dT = dR V^T + dX Khat^T,  dV = T^T dR,  dKhat = T^T dX,  dbeta_s = sum_t dT_ts Linv_ts,
 //   dL = -strictlower(L^-T (dT diag beta) L^-T),  dbeta_t += sum_s dL_ts A_ts,  dA = diag(beta) dL.
 // ---------------------------------------------------------------------------------------
@@ -345,9 +348,9 @@ template <typename E, int D>
 struct KdaWyLds {
   static constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 4;
   static constexpr int TK = CH * LD * (int)sizeof(E), GB = CH * LDG * 4, F = CH * LF * 4;
-  // region 1: G | Kr | Cl during the Grams, then L^{-1} | dT | V | dR
-  static constexpr int R1 = cmax(GB + 2 * TK, 2 * F + 2 * TK);
-  static constexpr int oG = 0, oKr = GB, oCl = GB + TK;
+  // region 1: G while Khat is formed, then L^{-1} | dT | V | dR
+  static constexpr int R1 = cmax(GB, 2 * F + 2 * TK);
+  static constexpr int oG = 0;
   static constexpr int oLi = 0, odT = F, oV = 2 * F, odR = 2 * F + TK;
   static constexpr int oK = R1, oL = R1 + TK, oA = oL + F, odX = oA + F, BYTES = odX + TK;
 };
@@ -360,12 +363,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   using Ly = KdaWyLds<E, D>;
   constexpr int NT = 256, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ __align__(16) float scr[4 * 256];
   __shared__ float bs[CH], dbs[CH];
-  __shared__ int unsafe[4];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
-  E* Kr = reinterpret_cast<E*>(smem + Ly::oKr);
-  E* Cl = reinterpret_cast<E*>(smem + Ly::oCl);
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
   float* Ls = reinterpret_cast<float*>(smem + Ly::oL);
   float* Af = reinterpret_cast<float*>(smem + Ly::oA);
@@ -379,20 +378,15 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
 
   RegTile<E, CH, D, NT> rv, rdr;
   RegTile<float, CH, D, NT> rdx;
+  RegTile<float, CH, CH, NT> rli, raf;
   rv.load(v + tk * D, D, n);
   rdr.load(dRg + u * CH * D, D, CH);
   rdx.load(p.kd_dx + u * CH * D, D, CH);
+  rli.load(p.Li + u * CH * CH, CH, CH);
+  raf.load(p.A1 + u * CH * CH, CH, CH);
   g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
   if (threadIdx.x < CH) bs[threadIdx.x] = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
-  if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
   kda_cumlog<E, D, NT>(alpha + tk * D, D, n, Gs, LDG);
-  kda_flags<D, NT>(Gs, LDG, unsafe);
-  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
-    const int t = idx / D, j = idx % D;
-    Kr[t * LD + j] = (E)((float)Ks[t * LD + j] * __expf(Gs[t * LDG + j] - Gs[(t & ~15) * LDG + j]));
-  }
-  __syncthreads();
-  kda_grams<E, D, NT, false>(Ks, nullptr, Kr, Cl, Gs, unsafe, Ls, bs, Af, nullptr, nullptr, n);
   for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
     const int t = idx / D, j = idx % D;
     Ks[t * LD + j] = (E)((float)Ks[t * LD + j] * __expf(Gs[t * LDG + j]));
@@ -405,14 +399,16 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
       for (int x = 0; x < decltype(rdx)::VE; ++x) dXs[t * LD + j + x] = (E)rdx.elem(it, x);
     }
   }
-  __syncthreads();  // G, Kr, Cl are free from here on
+  raf.store(Af, LF);
+  __syncthreads();  // G is free from here on
   float* Li = reinterpret_cast<float*>(smem + Ly::oLi);
   float* dTs = reinterpret_cast<float*>(smem + Ly::odT);
   E* Vs = reinterpret_cast<E*>(smem + Ly::oV);
   E* dRs = reinterpret_cast<E*>(smem + Ly::odR);
+  rli.store(Li, LF);
   rv.store(Vs, LD);
   rdr.store(dRs, LD);
-  solve_unit_lower64<NT>(Ls, LF, Li, LF, scr);
+  __syncthreads();
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
@@ -817,7 +813,7 @@ hipError_t launch_fwd_prep_kda(const Plan& p, const gdr_inputs& in, hipStream_t 
   TraceScope ts_("fwd_prep_kda", st);
   hipLaunchKernelGGL((k_fwd_prep_kda<E, D>), dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo,
                      (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
-                     (E*)p.X, (E*)p.Ub, (E*)p.M, (E*)p.Kb, (E*)p.Qh, p.Gn);
+                     (E*)p.X, (E*)p.Ub, (E*)p.M, (E*)p.Kb, (E*)p.Qh, p.Gn, p.Li, p.A1);
   return hipGetLastError();
 }
 template hipError_t launch_fwd_prep_kda<bf16, 128>(const Plan&, const gdr_inputs&, hipStream_t);

@@ -36,9 +36,9 @@ struct Plan {
   void* dR;   // [units][64][D]  gradient w.r.t. R
   // Gated DeltaNet-2 backward intermediates (float32): per unit 64 x D partial gradients of
   // q, k, the erase direction a and the write vector b, the gradient of X', then 64 x 64
-  // gradients of the four chunk matrices, the two solve-side Grams, and per-token sums.
+  // gradients of the four chunk matrices, and per-token sums.
   float *g2_dq, *g2_dk, *g2_da, *g2_db, *g2_dx;
-  float *g2_dakk, *g2_daak, *g2_dmqk, *g2_dmqa, *g2_akk, *g2_aak;
+  float *g2_dakk, *g2_daak, *g2_dmqk, *g2_dmqa;
   float* g2_rows;  // [units][4][64]: prefix-type sums, Khat.dKhat, dbeta from b, gamma term
   // Kimi Delta Attention backward intermediates (float32, the same workspace region): per unit
   // 64 x D gradients w.r.t. Qhat, X, Kbar, Khat; 64 x 64 gradients w.r.t. M and A; D values
