@@ -27,27 +27,38 @@ constexpr float KDA_REF_LIMIT = -60.f;
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 }  // namespace
 
-// g for JW channels (alpha points at the chunk's first token and first channel; row stride
-// rs): Gs[t*ldg + j] = sum_{u<=t} log alpha_{u,j}, rows >= n taken as log 1 = 0.
-// Every kernel calls this with the same per-column arithmetic, so all of them see the same
-// values of g.  Starts and ends with a block barrier.
+// g for JW channels from a tile of alpha already loaded (rows >= n taken as log 1 = 0):
+// Gs[t*ldg + j] = sum_{u<=t} log alpha_{u,j}.  Each column is summed in four runs of 16 rows
+// whose totals are then carried in order, the same arithmetic in every kernel, so all of them
+// see the same values of g.  tot: 4*JW floats of scratch.  Ends with a block barrier.
 template <typename E, int JW, int NT>
-__device__ void kda_cumlog(const E* __restrict__ alpha, long rs, int n, float* Gs, int ldg) {
-  RegTile<E, CH, JW, NT> ra;
-  ra.load(alpha, rs, n);
-  __syncthreads();
+__device__ void kda_cumlog(const RegTile<E, CH, JW, NT>& ra, int n, float* Gs, int ldg, float* tot) {
 #pragma unroll
-  for (int it = 0; it < decltype(ra)::IT; ++it) {
-    if (decltype(ra)::TOTAL % NT == 0 || threadIdx.x + it * NT < decltype(ra)::TOTAL) {
+  for (int it = 0; it < RegTile<E, CH, JW, NT>::IT; ++it) {
+    if (RegTile<E, CH, JW, NT>::TOTAL % NT == 0 || threadIdx.x + it * NT < RegTile<E, CH, JW, NT>::TOTAL) {
       const int t = ra.row(it), j = ra.col(it);
 #pragma unroll
-      for (int x = 0; x < decltype(ra)::VE; ++x) Gs[t * ldg + j + x] = (t < n) ? logf((float)ra.elem(it, x)) : 0.f;
+      for (int x = 0; x < RegTile<E, CH, JW, NT>::VE; ++x) Gs[t * ldg + j + x] = (t < n) ? logf((float)ra.elem(it, x)) : 0.f;
     }
   }
   __syncthreads();
-  for (int j = wave_id(); j < JW; j += NT / 64) {
-    float* p = Gs + lane_id() * ldg + j;
-    *p = wave_incl_scan(*p);
+  for (int idx = threadIdx.x; idx < 4 * JW; idx += NT) {
+    const int j = idx % JW, r0 = 16 * (idx / JW);
+    float run = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      run += Gs[(r0 + r) * ldg + j];
+      Gs[(r0 + r) * ldg + j] = run;
+    }
+    tot[idx] = run;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x + JW; idx < 4 * JW; idx += NT) {
+    const int j = idx % JW, part = idx / JW, r0 = 16 * part;
+    float off = tot[j];
+    for (int q = 1; q < part; ++q) off += tot[q * JW + j];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Gs[(r0 + r) * ldg + j] += off;
   }
   __syncthreads();
 }
@@ -166,7 +177,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   using Ly = KdaPrepLds<E, D>;
   constexpr int NT = 256, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, LDT = Ly::LDT;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ float bs[CH];
+  __shared__ float bs[CH], tot[4 * D];
   __shared__ int unsafe[4];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
   E* Kr = reinterpret_cast<E*>(smem + Ly::oKr);
@@ -181,13 +192,16 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id(), n = cp.n;
 
-  RegTile<E, CH, D, NT> rv;
+  RegTile<E, CH, D, NT> rv, rk, rq, ra;
+  ra.load(alpha + tk * D, D, n);
+  rk.load(k + tk * D, D, n);
+  rq.load(q + tk * D, D, n);
   rv.load(v + tk * D, D, n);
-  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
-  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
   if (threadIdx.x < CH) bs[threadIdx.x] = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
   if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
-  kda_cumlog<E, D, NT>(alpha + tk * D, D, n, Gs, LDG);
+  rk.store(Ks, LD);
+  rq.store(Qs, LD);
+  kda_cumlog<E, D, NT>(ra, n, Gs, LDG, tot);
   kda_flags<D, NT>(Gs, LDG, unsafe);
 
   // Kbar and Qhat for the scans and the output kernel, e^{g_n} per channel, and the row
@@ -363,7 +377,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   using Ly = KdaWyLds<E, D>;
   constexpr int NT = 256, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ float bs[CH], dbs[CH];
+  __shared__ float bs[CH], dbs[CH], tot[4 * D];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
   float* Ls = reinterpret_cast<float*>(smem + Ly::oL);
@@ -376,17 +390,19 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id(), n = cp.n;
 
-  RegTile<E, CH, D, NT> rv, rdr;
+  RegTile<E, CH, D, NT> rv, rdr, rk, ra;
   RegTile<float, CH, D, NT> rdx;
   RegTile<float, CH, CH, NT> rli, raf;
+  ra.load(alpha + tk * D, D, n);
+  rk.load(k + tk * D, D, n);
   rv.load(v + tk * D, D, n);
   rdr.load(dRg + u * CH * D, D, CH);
   rdx.load(p.kd_dx + u * CH * D, D, CH);
   rli.load(p.Li + u * CH * CH, CH, CH);
   raf.load(p.A1 + u * CH * CH, CH, CH);
-  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
   if (threadIdx.x < CH) bs[threadIdx.x] = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
-  kda_cumlog<E, D, NT>(alpha + tk * D, D, n, Gs, LDG);
+  rk.store(Ks, LD);
+  kda_cumlog<E, D, NT>(ra, n, Gs, LDG, tot);
   for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
     const int t = idx / D, j = idx % D;
     Ks[t * LD + j] = (E)((float)Ks[t * LD + j] * __expf(Gs[t * LDG + j]));
@@ -523,7 +539,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
   using Ly = KdaGramLds<E>;
   constexpr int NT = 256, JW = Ly::JW, LDJ = Ly::LDJ, LDT = Ly::LDT, LDF = Ly::LDF, NC = JW / 16;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ float c1s[3][JW], tota[4][JW], totc[4][JW];
+  __shared__ float c1s[3][JW], tota[4][JW], totc[4][JW], tot[4 * JW];
   __shared__ int unsafe[4];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
@@ -544,19 +560,28 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
   const int w = wave_id(), l = lane_id(), n = cp.n;
   const int b = w;  // this wave's 16-token block
 
-  g2s_rows<E, CH, JW, NT>(Ks, LDJ, k + tk * D + j0, D, n);
-  g2s_rows<E, CH, JW, NT>(Qs, LDJ, q + tk * D + j0, D, n);
   {
-    const float* da = p.kd_da + u * CH * CH;
-    const float* dm = p.kd_dm + u * CH * CH;
-    for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-      const int t = idx >> 6, s = idx & 63;
-      dAs[t * LDT + s] = (E)da[idx];
-      dMs[t * LDT + s] = (E)dm[idx];
+    RegTile<E, CH, JW, NT> rk, rq, ra;
+    RegTile<float, CH, CH, NT> rda, rdm;
+    ra.load(alpha + tk * D + j0, D, n);
+    rk.load(k + tk * D + j0, D, n);
+    rq.load(q + tk * D + j0, D, n);
+    rda.load(p.kd_da + u * CH * CH, CH, CH);
+    rdm.load(p.kd_dm + u * CH * CH, CH, CH);
+    if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
+    rk.store(Ks, LDJ);
+    rq.store(Qs, LDJ);
+#pragma unroll
+    for (int it = 0; it < decltype(rda)::IT; ++it) {
+      const int t = rda.row(it), s0 = rda.col(it);
+#pragma unroll
+      for (int x = 0; x < decltype(rda)::VE; ++x) {
+        dAs[t * LDT + s0 + x] = (E)rda.elem(it, x);
+        dMs[t * LDT + s0 + x] = (E)rdm.elem(it, x);
+      }
     }
+    kda_cumlog<E, JW, NT>(ra, n, Gs, LDF, tot);
   }
-  if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
-  kda_cumlog<E, JW, NT>(alpha + tk * D + j0, D, n, Gs, LDF);
   kda_flags<JW, NT>(Gs, LDF, unsafe);
   // Kend_s = k_s e^{g_{16(J+1)} - g_s} (s in block J < 3);  Kf_u, Qf_u = (k_u, q_u) e^{g_u - g_{16I}}
   // (u in block I);  Krf_s = k_s e^{g_{16I} - g_s} (zero in blocks summed exactly)
@@ -572,6 +597,29 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
   }
   __syncthreads();
   const bool exact = unsafe[b] != 0;  // wave-uniform
+
+  // Loads of the last phases, issued now so that their latency is hidden: the partial
+  // gradients from the earlier stages at this wave's matrix-core elements, and alpha and the
+  // memory term at this lane's channel.
+  const float* dqh = p.kd_dqh + u * CH * D;
+  const float* dkh = p.kd_dkh + u * CH * D;
+  const float* dkb = p.kd_dkb + u * CH * D;
+  float lq[NC][4], lk[NC][4], lb[NC][4], la[16];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const long o = (long)acc_row(16 * b, r) * D + j0 + acc_col(16 * c);
+      lq[c][r] = dqh[o];
+      lk[c][r] = dkh[o];
+      lb[c][r] = dkb[o];
+    }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = min(16 * b + i, n - 1);
+    la[i] = (float)alpha[(tk + t) * D + j0 + l];
+  }
+  const float gam_l = p.kd_gam[u * D + j0 + l];
 
   // ---- pairs inside block b, channel j0 + l: one lane per channel
   float n4[16], dkd[16], dqd[16];
@@ -724,9 +772,6 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
   __syncthreads();
 
   // ---- dq, dk, and the per-row terms of d log alpha (matrix-core layout)
-  const float* dqh = p.kd_dqh + u * CH * D;
-  const float* dkh = p.kd_dkh + u * CH * D;
-  const float* dkb = p.kd_dkb + u * CH * D;
   float pa_[NC], pc_[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -738,8 +783,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
       const int uu = acc_row(16 * b, r);
       const float g = Gs[uu * LDF + j], eg = __expf(g), egb = __expf(gn - g);
       const float kv = (float)Ks[uu * LDJ + j], qv = (float)Qs[uu * LDJ + j];
-      const long o = (long)uu * D + jg;
-      const float xq = eg * dqh[o], xk = eg * dkh[o], xb = egb * dkb[o];
+      const float xq = eg * lq[c][r], xk = eg * lk[c][r], xb = egb * lb[c][r];
       float dkv = dkacc[c][r] + xk + xb, dqv = dqacc[c][r] + xq;
       if (exact) {
         dkv += S1[uu * LDF + j];
@@ -776,7 +820,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
 
   // ---- d log alpha, channel layout
   {
-    float cross = p.kd_gam[u * D + j0 + l];
+    float cross = gam_l;
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
       if (bb > b) cross += tota[bb][l];
@@ -797,10 +841,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
       const int t = 16 * b + i;
       const float dla = n4[i] + suf[i] + run + cross;
       run += S2[t * LDF + l];
-      if (t < n) {
-        const long o = (tk + t) * D + j0 + l;
-        dalpha[o] = (E)(dla / (float)alpha[o]);
-      }
+      if (t < n) dalpha[(tk + t) * D + j0 + l] = (E)(dla / la[i]);
     }
   }
 }
