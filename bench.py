@@ -45,22 +45,27 @@ def kernel_bytes_per_unit(variant: str, kernel: str, D: int = 128, esz: int = 2,
     ALPHA = 0 if variant == "deltanet" else (TOK if kda else GATE)
     BETA = GATE if has_beta else 0
     DEC = FD if kda else GLOG  # per-chunk decay handed to the scans
+    OUT = TOK + GRAM + TOK  # the forward scan also reads q and M and writes o
     table = {
-        "fwd_prep": 3 * TOK + BETA + ALPHA + 2 * TOK + GRAM + GLOG,
-        "fwd_prep_kda": 3 * TOK + BETA + ALPHA + 4 * TOK + GRAM + FD,
-        "fwd_prep_gdn2": 5 * TOK + BETA + ALPHA + 3 * TOK + 2 * GRAM + GLOG,
-        "fwd_scan": (6 * TOK + BETA if g2 else 3 * TOK) + DEC + SQR + TOK,
-        "fwd_out": TOK + GRAM + TOK + SQR + DEC + TOK + ((GRAM + 2 * TOK + BETA) if g2 else 0),
+        "fwd_prep": 3 * TOK + BETA + ALPHA + 2 * TOK + GRAM + GLOG + 2 * FGRAM,
+        "fwd_prep_kda": 3 * TOK + BETA + ALPHA + 4 * TOK + GRAM + FD + 2 * FGRAM,
+        "fwd_prep_gdn2": 5 * TOK + BETA + ALPHA + 3 * TOK + 2 * GRAM + GLOG + 3 * FGRAM,
+        "fwd_scan": (6 * TOK + BETA if g2 else 3 * TOK) + DEC + SQR + TOK + OUT + (GRAM if g2 else 0),
         "bwd_scan": 3 * TOK + TOK + GRAM + DEC + SQR + TOK + ((TOK + BETA) if g2 else 0),
-        "bwd_chunk": 4 * TOK + BETA + ALPHA + GRAM + GLOG + 2 * SQR + 2 * TOK + 3 * TOK + BETA + ALPHA,
+        "bwd_chunk": 4 * TOK + BETA + ALPHA + GRAM + GLOG + 2 * SQR + 2 * TOK + 3 * TOK + BETA + ALPHA + 2 * FGRAM,
         "bwd_kda_state": 3 * TOK + 2 * SQR + FD + 3 * FTOK + FGRAM + FD,
-        "bwd_kda_wy": 3 * TOK + BETA + ALPHA + FTOK + TOK + BETA + FTOK + FGRAM,
+        "bwd_kda_wy": 3 * TOK + BETA + ALPHA + FTOK + 2 * FGRAM + TOK + BETA + FTOK + FGRAM,
         "bwd_kda_gram": 2 * TOK + ALPHA + 2 * FGRAM + 3 * FTOK + FD + 2 * TOK + ALPHA,
         "bwd_gdn2_state": 5 * TOK + GLOG + BETA + 2 * SQR + 2 * TOK + 5 * FTOK + 2 * FGRAM + 4 * GLOG,
-        "bwd_gdn2_wy": 5 * TOK + GLOG + BETA + 3 * TOK + GRAM + 3 * FTOK + 2 * TOK + 4 * FGRAM + FTOK + 4 * GLOG,
+        "bwd_gdn2_wy": 3 * TOK + GLOG + BETA + 2 * FGRAM + 3 * TOK + GRAM + 3 * FTOK + 2 * TOK + 2 * FGRAM + FTOK
+                       + 4 * GLOG,
         "bwd_gdn2_gram": 3 * TOK + BETA + ALPHA + GLOG + 2 * GRAM + 6 * FGRAM + 3 * FTOK + 4 * GLOG
                          + 3 * TOK + BETA + ALPHA,
+        "fwd_seg_combine": 0, "bwd_seg_combine": 0,
     }
+    if kernel in ("fwd_scan_maps", "bwd_scan_maps"):  # no per-chunk records, twice the value tiles
+        base = table[kernel[:8]] - (SQR + TOK + (OUT if kernel.startswith("fwd") else 0))
+        return base
     return table[kernel]
 
 
