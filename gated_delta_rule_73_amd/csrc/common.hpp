@@ -180,6 +180,23 @@ template <> __device__ __forceinline__ uint4 vzero<16>() { return make_uint4(0u,
 template <> __device__ __forceinline__ uint2 vzero<8>() { return make_uint2(0u, 0u); }
 template <> __device__ __forceinline__ uint32_t vzero<4>() { return 0u; }
 
+// Raw buffer resource over [base, base + bytes): a load at an offset at or past `bytes` returns
+// zero in hardware, so a ragged tile needs neither a clamp nor a select on the loaded data.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, long bytes) {
+  const long lim = bytes < 0x7fffffffL ? bytes : 0x7fffffffL;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim, 0x00020000);
+}
+template <int B> __device__ __forceinline__ typename VecT<B>::type buf_load(__amdgpu_buffer_rsrc_t r, int off);
+template <> __device__ __forceinline__ uint4 buf_load<16>(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+template <> __device__ __forceinline__ uint2 buf_load<8>(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+template <> __device__ __forceinline__ uint32_t buf_load<4>(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 // Vector width (bytes) that spreads a tile of `bytes` over NT threads, 4..16.
 constexpr int tile_vec_bytes(int bytes, int nt) {
   return bytes / nt >= 16 ? 16 : bytes / nt >= 8 ? 8 : 4;
@@ -197,17 +214,17 @@ struct RegTile {
   typedef typename VecT<VB>::type V;
   static_assert(COLS % VE == 0, "row length must be a multiple of the vector width");
   V v[IT];
-  // v <- G[r*gs + c] for r < nrows (zero below); needs nrows >= 1.  The loads are issued
-  // unconditionally (rows past nrows re-read row nrows-1 and are then zeroed), so the
-  // number of outstanding memory operations does not depend on the data.
+  // v <- G[r*gs + c] for r < nrows (zero below).  Buffer loads with the resource ending at
+  // row nrows: every load is issued unconditionally and rows past the end read as zero, so
+  // there is no branch around a load and no select waiting on its data.
   __device__ __forceinline__ void load(const S* g, long gs, int nrows) {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(g, (long)nrows * gs * (long)sizeof(S));
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int idx = threadIdx.x + it * NT;
       const int r = idx / VPR, c = (idx % VPR) * VE;
       if (TOTAL % NT == 0 || idx < TOTAL) {
-        const V x = *reinterpret_cast<const V*>(g + (long)min(r, nrows - 1) * gs + c);
-        v[it] = (r < nrows) ? x : vzero<VB>();
+        v[it] = buf_load<VB>(rs, (int)(((long)r * gs + c) * (long)sizeof(S)));
       } else {
         v[it] = vzero<VB>();
       }
