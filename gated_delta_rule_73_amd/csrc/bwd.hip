@@ -113,29 +113,36 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
 
   // Chunk c - 2 is loaded while chunk c is computed (two register sets, loop unrolled by two).
   // Loads before the first chunk repeat it, so every step issues the same memory operations.
+  // The loads of a step are issued in two parts (part < 0: all), each in a stretch of matrix-
+  // core work that hides its issue: X, M and dO with dR, the queries, keys and gates with the
+  // update of dW.
   using Ops = BwdScanOps<E, D, BV, VAR>;
-  auto load = [&](Ops& p, int c) {
+  auto load = [&](Ops& p, int c, int part) {
     const int cc = max(c, c0);
     const long u = (long)(sp.gc0 + cc) * geo.H + h;
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
-    if constexpr (KDA) {
-      p.q.load(q + u * CH * D, D, CH);
-      p.k.load(k + u * CH * D, D, CH);
-#pragma unroll
-      for (int qq = 0; qq < NJ; ++qq) p.eg[qq] = *reinterpret_cast<const f32x4*>(Gg + u * D + acc_row(16 * (w + 4 * qq), 0));
-    } else {
-      p.q.load(q + tk * D, D, n);
-      p.k.load(k + tk * D, D, n);
-      p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+    if (part <= 0) {
+      p.x.load(Xg + u * CH * D, D, CH);
+      p.m.load(Mg + u * CH * CH, CH, CH);
+      p.dO.load(dO + tk * D + i0, D, n);
     }
-    p.x.load(Xg + u * CH * D, D, CH);
-    p.m.load(Mg + u * CH * CH, CH, CH);
-    p.dO.load(dO + tk * D + i0, D, n);
-    if constexpr (G2) {
-      p.e.load(erase + tk * D, D, n);
-      const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
-      p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+    if (part != 0) {
+      if constexpr (KDA) {
+        p.q.load(q + u * CH * D, D, CH);
+        p.k.load(k + u * CH * D, D, CH);
+#pragma unroll
+        for (int qq = 0; qq < NJ; ++qq) p.eg[qq] = *reinterpret_cast<const f32x4*>(Gg + u * D + acc_row(16 * (w + 4 * qq), 0));
+      } else {
+        p.q.load(q + tk * D, D, n);
+        p.k.load(k + tk * D, D, n);
+        p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+      }
+      if constexpr (G2) {
+        p.e.load(erase + tk * D, D, n);
+        const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
+        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+      }
     }
   };
   auto step = [&](int c, Ops& p) {
@@ -187,9 +194,9 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
           As[t * LD + j0 + x] = (E)(bsh[t] * (float)p.e.elem(it, x) * (float)p.k.elem(it, x));
       }
     }
-    load(p, c - 2);
     if (snap) s2g_full<E, BV, D, NT>(dHs + u * D * D + (long)i0 * D, D, dWs, LD);
     __syncthreads();
+    load(p, c - 2, 0);
     const float gn = gs[CH - 1];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
@@ -208,6 +215,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     }
     __syncthreads();
     if (snap) s2g_full<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV);
+    load(p, c - 2, 1);
     float eg = 1.f;
     if constexpr (DEC) eg = __expf(gn);
 #pragma unroll
@@ -223,12 +231,16 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   };
   if (c1 > c0) {
     Ops pa, pb;
-    load(pa, c1 - 1);
-    load(pb, c1 - 2);
-    for (int c = c1 - 1; c >= c0; c -= 2) {
+    load(pa, c1 - 1, -1);
+    load(pb, c1 - 2, -1);
+    // Every trip of the loop runs both steps (an odd first chunk runs after it), so the
+    // memory operations in flight at the top of the loop are the same on every path.
+    int c = c1 - 1;
+    for (; c - 1 >= c0; c -= 2) {
       step(c, pa);
-      if (c - 1 >= c0) step(c - 1, pb);
+      step(c - 1, pb);
     }
+    if (c >= c0) step(c, pa);
   }
   float* out = nullptr;  // dh0, or this segment's map
   if (sg.mode == 1) out = sg.maps + ((mem * sg.max_seg + seg) * 2 + (virt ? 1 : 0)) * D * D;
@@ -261,7 +273,10 @@ struct BwdLds {
   static constexpr int endP1 = oU + 2 * TK + 2 * TH;
   // phase 2 (WY part) and 3 (Gram part)
   static constexpr int oA = oU, odT = oU + F, oLi = oU + 2 * F, oVP = oU + 3 * F;
-  static constexpr int endP2 = oU + 3 * F + (TK > F ? TK : F);
+  static constexpr int endVP = oU + 3 * F + (TK > F ? TK : F);
+  // (dT diag(beta)) Linv^T: in the dX region when a 64 x 64 float tile fits there
+  static constexpr int oPt = TK >= F ? odX : endVP;
+  static constexpr int endP2 = TK >= F ? endVP : endVP + F;
   static constexpr int oQ = oLi, oPair = oVP, oAt = odR, oMt = odR + SQ;
   static constexpr int BIG = endP1 > endP2 ? endP1 : endP2;
   static_assert(TK <= F, "Q must fit the region of Linv");
@@ -285,8 +300,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   constexpr int NQ = D / 32;           // 64 x D tiles per wave when all 8 waves share a matrix
   constexpr bool GATED = VAR == VAR_GATED;
   __shared__ __align__(16) char smem[Ly::BIG];
-  __shared__ float gs[CH], bs[CH], dbs[CH], red[NT / 64];
-  __shared__ float part8[NT / CH][CH], part8b[NT / CH][CH];  // partial column / row sums
+  __shared__ __align__(16) float gs[CH], bs[CH], red[NT / 64];
+  __shared__ float part8[NT / CH][CH], part8b[NT / CH][CH], part8c[NT / CH][CH];  // partial sums
   __shared__ float rq[4][CH], rkh[8][CH], rkb[8][CH];
 
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
@@ -372,16 +387,22 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
   }
   const float gn = gs[CH - 1];
+  // e^{g_t} and e^{g_n - g_t} for the four accumulator rows this lane holds (row tile wm)
+  float egr[4] = {1.f, 1.f, 1.f, 1.f}, egd[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (GATED) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float gt = gs[acc_row(16 * wm, r)];
+      egr[r] = expf(gt);
+      egd[r] = expf(gn - gt);
+    }
+  }
   // dq (first term) stays in acc1 for waves 0-3; dX goes to LDS from waves 4-7
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
     if (w < 4) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float e = 1.f;
-        if constexpr (GATED) e = expf(gs[acc_row(16 * wm, r)]);
-        acc1[nt][r] *= geo.scale * e;
-      }
+      for (int r = 0; r < 4; ++r) acc1[nt][r] *= geo.scale * egr[r];
     } else {
       store4_n(dXs, LD, 16 * wm, 16 * nt, -acc1[nt]);
     }
@@ -394,9 +415,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = acc_row(16 * wm, r);
-        float dec = 1.f;
-        if constexpr (GATED) dec = expf(gn - gs[t]);
-        dka[qq][r] *= dec;
+        dka[qq][r] *= egd[r];
         part[r] += (float)Ks[t * LD + acc_col(16 * (wn * NQ + qq))] * dka[qq][r];
       }
 #pragma unroll
@@ -433,11 +452,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
     const f32x4 a = mma_k<E, D>(zero4(), rowk(dRs, LD), 16 * mt, rowk(Vs, LD), 16 * nt);
     const f32x4 b = mma_k<E, D>(zero4(), rowk(dXs, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
+    const int s = acc_col(16 * nt);
+    float es = 1.f;
+    if constexpr (GATED) es = expf(gs[s]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
-      float es = 1.f;
-      if constexpr (GATED) es = expf(gs[s]);
+      const int t = acc_row(16 * mt, r);
       dTs[t * LF + s] = (s <= t) ? a[r] + b[r] * es : 0.f;
     }
   }
@@ -454,9 +474,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = acc_row(16 * wm, r);
-        float e = 1.f;
-        if constexpr (GATED) e = expf(gs[t]);
-        kh[r] *= e;
+        kh[r] *= egr[r];
         part[r] += (float)Ks[t * LD + acc_col(16 * nt)] * kh[r];
       }
       dka[qq] += kh;
@@ -475,43 +493,29 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     float a = 0.f;
 #pragma unroll
     for (int t = pt; t < CH; t += NT / CH) a += dTs[t * LF + s] * Li[t * LF + s];
-    part8[pt][s] = a;
-  }
-  __syncthreads();
-  if (threadIdx.x < CH) {
-    float a = 0.f;
-#pragma unroll
-    for (int i = 0; i < NT / CH; ++i) a += part8[i][threadIdx.x];
-    dbs[threadIdx.x] = a;
+    part8c[pt][s] = a;  // summed when dbeta is written
   }
   __syncthreads();
   s2g_rows<E, CH, D, NT>(dv + tk * D, D, Vs, LD, n);
-  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-    const int t = idx >> 6, s = idx & 63;
-    dTs[t * LF + s] *= bs[s];  // gradient w.r.t. Linv
-  }
-  __syncthreads();
-  float* Pt = reinterpret_cast<float*>(smem + Ly::oVP);
+  // gradient w.r.t. Linv is dT diag(beta); Pt = (dT diag(beta)) Linv^T, staged where dX was
+  // (free once dT and dKhat have been formed) or in a region of its own
+  float* Pt = reinterpret_cast<float*>(smem + Ly::oPt);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
-    const f32x4 acc = mma_k<E, CH>(zero4(), rowk(dTs, LF), 16 * mt, rowk(Li, LF), 16 * nt);
+    const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * mt, rowk(Li, LF), 16 * nt);
     store4_t(Pt, LF, 16 * mt, 16 * nt, acc);
   }
   __syncthreads();
-  f32x4 dl[2];
+  // dL (strictly lower); dT is no longer read, so dL overwrites it in place
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
     const f32x4 acc = mma_k<E, CH>(zero4(), colk(Li, LF), 16 * mt, rowk(Pt, LF), 16 * nt);
+    f32x4 dl;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dl[e][r] = (acc_col(16 * nt) < acc_row(16 * mt, r)) ? -acc[r] : 0.f;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int id = w + 8 * e;
-    store4_n(dTs, LF, 16 * (id >> 2), 16 * (id & 3), dl[e]);  // dTs now holds dL
+    for (int r = 0; r < 4; ++r) dl[r] = (acc_col(16 * nt) < acc_row(16 * mt, r)) ? -acc[r] : 0.f;
+    store4_n(dTs, LF, 16 * mt, 16 * nt, dl);
   }
   __syncthreads();
   {  // dbeta from L = I + diag(beta) A: row sums (dL is zero on and above the diagonal)
@@ -622,9 +626,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       const float dla = rect + suf + pre + expf(gn) * g4;
       if (t < n) dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
     }
-    float db = dbs[t];
+    float db = 0.f;
 #pragma unroll
-    for (int i = 0; i < NT / CH; ++i) db += part8b[i][t];
+    for (int i = 0; i < NT / CH; ++i) db += part8c[i][t] + part8b[i][t];
     if (t < n) dbeta[tk + t] = (E)db;
   }
   __syncthreads();

@@ -61,6 +61,14 @@ template <typename S, bool KC> struct View {
 template <typename S> __device__ __forceinline__ View<S, true> rowk(const S* p, int ld) { return View<S, true>(p, ld); }
 template <typename S> __device__ __forceinline__ View<S, false> colk(const S* p, int ld) { return View<S, false>(p, ld); }
 
+// Row-major float data with column k scaled by sc[k]: element (m, k) = p[m*ld + k] * sc[k].
+struct RowKScaled {
+  const float* p;
+  int ld;
+  const float* sc;
+  __device__ __forceinline__ float at(int m, int k) const { return p[m * ld + k] * sc[k]; }
+};
+
 // The calling lane's fragment of rows/columns idx0..idx0+15 and k-slice k0..k0+KS-1.
 template <typename E, typename S, bool KC>
 __device__ __forceinline__ typename MMA<E>::frag frag(const View<S, KC>& v, int idx0, int k0) {
@@ -96,6 +104,24 @@ __device__ __forceinline__ typename MMA<E>::frag frag(const View<S, KC>& v, int 
     bf16x8 r;
 #pragma unroll
     for (int e = 0; e < 8; ++e) r[e] = (bf16)v.at(m, k + e);
+    return r;
+  }
+}
+
+template <typename E>
+__device__ __forceinline__ typename MMA<E>::frag frag(const RowKScaled& v, int idx0, int k0) {
+  constexpr int KPL = MMA<E>::KPL;
+  const int m = idx0 + lrow(), k = k0 + KPL * lgrp();
+  if constexpr (KPL == 1) {
+    return (E)v.at(m, k);
+  } else {
+    const float4 lo = *reinterpret_cast<const float4*>(v.p + m * v.ld + k);
+    const float4 hi = *reinterpret_cast<const float4*>(v.p + m * v.ld + k + 4);
+    const float4 slo = *reinterpret_cast<const float4*>(v.sc + k);
+    const float4 shi = *reinterpret_cast<const float4*>(v.sc + k + 4);
+    bf16x8 r;
+    r[0] = (bf16)(lo.x * slo.x); r[1] = (bf16)(lo.y * slo.y); r[2] = (bf16)(lo.z * slo.z); r[3] = (bf16)(lo.w * slo.w);
+    r[4] = (bf16)(hi.x * shi.x); r[5] = (bf16)(hi.y * shi.y); r[6] = (bf16)(hi.z * shi.z); r[7] = (bf16)(hi.w * shi.w);
     return r;
   }
 }

@@ -215,32 +215,44 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
 
   // Chunk c + 2 is loaded while chunk c is computed (two register sets, loop unrolled by two).
   // Loads past the last chunk repeat it, so every step issues the same memory operations.
+  // The loads of a step are issued in three parts (part < 0: all), each in the stretch of the
+  // step whose matrix-core work hides its issue: X and U with R, Q and M with the output,
+  // the keys and gates with the memory update.
   using Ops = FwdScanOps<E, D, BV, VAR, FULL>;
-  auto load = [&](Ops& p, int c) {
+  auto load = [&](Ops& p, int c, int part) {
     const int cc = min(c, c1 - 1);
     const long u = (long)(sp.gc0 + cc) * geo.H + h;
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
-    p.x.load(Xg + u * CH * D, D, CH);
-    p.u.load(Ug + u * CH * D + i0, D, CH);
-    if constexpr (KDA) {
-      p.k.load(k + u * CH * D, D, CH);
+    if (part <= 0) {
+      p.x.load(Xg + u * CH * D, D, CH);
+      p.u.load(Ug + u * CH * D + i0, D, CH);
+      if constexpr (KDA) {
 #pragma unroll
-      for (int qq = 0; qq < NJ; ++qq) p.eg[qq] = *reinterpret_cast<const f32x4*>(Gg + u * D + acc_row(16 * (w + 4 * qq), 0));
-      if constexpr (FULL) p.q.load(q + u * CH * D, D, CH);
-    } else {
-      p.k.load(k + tk * D, D, n);
-      p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
-      if constexpr (FULL) p.q.load(q + tk * D, D, n);
+        for (int qq = 0; qq < NJ; ++qq) p.eg[qq] = *reinterpret_cast<const f32x4*>(Gg + u * D + acc_row(16 * (w + 4 * qq), 0));
+      }
     }
-    if constexpr (FULL) p.m.load(Mg + u * CH * CH, CH, CH);
-    if constexpr (G2) {
-      p.e.load(erase + tk * D, D, n);
-      p.vt.load(vin + tk * D + i0, D, n);
-      p.wt.load(write + tk * D + i0, D, n);
-      const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
-      p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
-      if constexpr (FULL) p.m2.load(M2g + u * CH * CH, CH, CH);
+    if (part < 0 || part == 1) {
+      if constexpr (FULL) {
+        p.q.load(q + (KDA ? u * CH : tk) * D, D, KDA ? CH : n);
+        p.m.load(Mg + u * CH * CH, CH, CH);
+        if constexpr (G2) p.m2.load(M2g + u * CH * CH, CH, CH);
+      }
+    }
+    if (part < 0 || part == 2) {
+      if constexpr (KDA) {
+        p.k.load(k + u * CH * D, D, CH);
+      } else {
+        p.k.load(k + tk * D, D, n);
+        p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+      }
+      if constexpr (G2) {
+        p.e.load(erase + tk * D, D, n);
+        p.vt.load(vin + tk * D + i0, D, n);
+        p.wt.load(write + tk * D + i0, D, n);
+        const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
+        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+      }
     }
   };
   auto step = [&](int c, Ops& p) {
@@ -293,7 +305,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         }
       }
     }
-    load(p, c + 2);
+    load(p, c + 2, 0);
     const float gn = gs[CH - 1];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
@@ -314,6 +326,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     if constexpr (FULL) s2g_full<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD);
     __syncthreads();
     if constexpr (FULL) {
+      load(p, c + 2, 1);
       s2g_full<E, CH, BV, NT>(Rg + u * CH * D + i0, D, Rn, LDV);
       if (o) {
         // O = scale (e^g (Q W0^T) + M R [+ M_qk b]) for this tile's value columns
@@ -333,6 +346,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         }
       }
     }
+    load(p, c + 2, 2);
     float eg = 1.f;
     if constexpr (DEC) eg = __expf(gn);
 #pragma unroll
@@ -356,12 +370,16 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
   };
   if (c1 > c0) {
     Ops pa, pb;
-    load(pa, c0);
-    load(pb, c0 + 1);
-    for (int c = c0; c < c1; c += 2) {
+    load(pa, c0, -1);
+    load(pb, c0 + 1, -1);
+    // Every trip of the loop runs both steps (an odd last chunk runs after it), so the
+    // memory operations in flight at the top of the loop are the same on every path.
+    int c = c0;
+    for (; c + 1 < c1; c += 2) {
       step(c, pa);
-      if (c + 1 < c1) step(c + 1, pb);
+      step(c + 1, pb);
     }
+    if (c < c1) step(c, pa);
   }
   float* out = nullptr;  // final memory: ht, or this segment's map
   if (!FULL) out = sg.maps + ((mem * sg.max_seg + seg) * 2 + (virt ? 1 : 0)) * D * D;
