@@ -86,42 +86,73 @@ __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const fl
   for (int I = 0; I < 4; ++I) {
     const int ref = 16 * I;
     const bool uns = unsafe[I] != 0;
-    // column operand of row block I: K_s e^{g_ref - g_s} for s < ref + 16
-    for (int idx = threadIdx.x; idx < (ref + 16) * D; idx += NT) {
-      const int s = idx / D, j = idx % D;
-      float val = 0.f;
-      if (!(uns && s >= ref)) val = (float)Ks[s * LD + j] * __expf(Gs[ref * LDG + j] - Gs[s * LDG + j]);
-      Cl[s * LD + j] = (E)val;
+    // column operand of row block I: K_s e^{g_ref - g_s} for s < ref + 16, 16 bytes at a time
+    constexpr int VE = 16 / (int)sizeof(E);
+    for (int idx = threadIdx.x; idx < (ref + 16) * (D / VE); idx += NT) {
+      const int s = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
+      const uint4 kv = *reinterpret_cast<const uint4*>(Ks + s * LD + j0);
+      const E* ke = reinterpret_cast<const E*>(&kv);
+      uint4 cv;
+      E* ce = reinterpret_cast<E*>(&cv);
+      const bool zero = uns && s >= ref;
+#pragma unroll
+      for (int e = 0; e < VE; ++e)
+        ce[e] = (E)(zero ? 0.f : (float)ke[e] * __expf(Gs[ref * LDG + j0 + e] - Gs[s * LDG + j0 + e]));
+      *reinterpret_cast<uint4*>(Cl + s * LD + j0) = cv;
     }
     __syncthreads();
+    // Tiles (row block I, column block J <= I), formed transposed so each lane holds four
+    // consecutive columns s of one row t and writes them with one vector store.
     const int njobs = (WITH_M ? 2 : 1) * (I + 1);
     for (int job = w; job < njobs; job += NT / 64) {
       const bool isM = job > I;
       const int J = isM ? job - I - 1 : job;
       if (J == I && uns) continue;
-      const f32x4 acc = mma_k<E, D>(zero4(), rowk(isM ? Qr : Kr, LD), ref, rowk(Cl, LD), 16 * J);
+      const f32x4 acc = mma_k<E, D>(zero4(), rowk(Cl, LD), 16 * J, rowk(isM ? Qr : Kr, LD), ref);
+      const int t = ref + lrow(), s0 = 16 * J + 4 * lgrp();
+      if (isM) {
+        if constexpr (WITH_M) {
+          E m[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(ref, r), s = acc_col(16 * J);
-        if (isM) {
-          Mo[t * CH + s] = (E)((s <= t) ? acc[r] : 0.f);
-        } else {
-          const float a = (s < t) ? acc[r] : 0.f;
-          Ls[t * LF + s] = lsc[t] * a;
-          if (Af) Af[t * ldaf + s] = a;
+          for (int r = 0; r < 4; ++r) m[r] = (E)((s0 + r <= t) ? acc[r] : 0.f);
+          if constexpr (sizeof(E) == 2) {
+            *reinterpret_cast<bf16x4*>(Mo + t * CH + s0) = bf16x4{m[0], m[1], m[2], m[3]};
+          } else {
+            *reinterpret_cast<float4*>(Mo + t * CH + s0) = make_float4(m[0], m[1], m[2], m[3]);
+          }
         }
+      } else {
+        float4 a;
+        a.x = (s0 < t) ? acc[0] : 0.f;
+        a.y = (s0 + 1 < t) ? acc[1] : 0.f;
+        a.z = (s0 + 2 < t) ? acc[2] : 0.f;
+        a.w = (s0 + 3 < t) ? acc[3] : 0.f;
+        const float l = lsc[t];
+        *reinterpret_cast<float4*>(Ls + t * LF + s0) = make_float4(l * a.x, l * a.y, l * a.z, l * a.w);
+        if (Af) *reinterpret_cast<float4*>(Af + t * ldaf + s0) = a;
       }
     }
     __syncthreads();
   }
-  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-    const int t = idx >> 6, s = idx & 63;
-    if (s > t) {
-      if (Af) Af[t * ldaf + s] = 0.f;
-      if constexpr (WITH_M) Mo[t * CH + s] = (E)0.f;
+  // blocks above the diagonal are zero
+  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {
+    const int t = idx >> 4, s0 = (idx & 15) * 4;
+    if (s0 >= 16 * ((t >> 4) + 1)) {
+      if (Af) *reinterpret_cast<float4*>(Af + t * ldaf + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (WITH_M) {
+        if constexpr (sizeof(E) == 2) *reinterpret_cast<bf16x4*>(Mo + t * CH + s0) = bf16x4{(E)0.f, (E)0.f, (E)0.f, (E)0.f};
+        else *reinterpret_cast<float4*>(Mo + t * CH + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
   }
   if (unsafe[0] | unsafe[1] | unsafe[2] | unsafe[3]) {
+    // upper triangles of the diagonal blocks summed exactly below (the products wrote the others)
+    for (int idx = threadIdx.x; idx < 4 * 256; idx += NT) {
+      const int I = idx >> 8, t = 16 * I + ((idx >> 4) & 15), s = 16 * I + (idx & 15);
+      if (!unsafe[I] || s <= t) continue;
+      if (Af) Af[t * ldaf + s] = 0.f;
+      if constexpr (WITH_M) Mo[t * CH + s] = (E)0.f;
+    }
     // exact diagonal blocks: one exponential per (t, s, j)
     for (int idx = threadIdx.x; idx < 4 * 136; idx += NT) {
       const int I = idx / 136;
@@ -208,15 +239,33 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   // operands of the Grams (Q's buffer is overwritten in place by Qr).
   E* kb = Kbo + u * CH * D;
   E* qh = Qho + u * CH * D;
-  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
-    const int t = idx / D, j = idx % D;
-    const float g = Gs[t * LDG + j], gn = Gs[(CH - 1) * LDG + j], gb = Gs[(t & ~15) * LDG + j];
-    const float kk = (float)Ks[t * LD + j], qq = (float)Qs[t * LD + j];
-    kb[idx] = (E)(kk * __expf(gn - g));
-    qh[idx] = (E)(qq * __expf(g));
-    const float f = __expf(g - gb);
-    Kr[t * LD + j] = (E)(kk * f);
-    Qs[t * LD + j] = (E)(qq * f);
+  constexpr int VE = 16 / (int)sizeof(E);
+  for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
+    const int t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
+    const uint4 kv = *reinterpret_cast<const uint4*>(Ks + t * LD + j0);
+    const uint4 qv = *reinterpret_cast<const uint4*>(Qs + t * LD + j0);
+    const E* ke = reinterpret_cast<const E*>(&kv);
+    const E* qe = reinterpret_cast<const E*>(&qv);
+    uint4 kbv, qhv, krv, qrv;
+    E* kbe = reinterpret_cast<E*>(&kbv);
+    E* qhe = reinterpret_cast<E*>(&qhv);
+    E* kre = reinterpret_cast<E*>(&krv);
+    E* qre = reinterpret_cast<E*>(&qrv);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const int j = j0 + e;
+      const float g = Gs[t * LDG + j], gn = Gs[(CH - 1) * LDG + j], gb = Gs[(t & ~15) * LDG + j];
+      const float kk = (float)ke[e], qq = (float)qe[e];
+      kbe[e] = (E)(kk * __expf(gn - g));
+      qhe[e] = (E)(qq * __expf(g));
+      const float f = __expf(g - gb);
+      kre[e] = (E)(kk * f);
+      qre[e] = (E)(qq * f);
+    }
+    *reinterpret_cast<uint4*>(kb + t * D + j0) = kbv;
+    *reinterpret_cast<uint4*>(qh + t * D + j0) = qhv;
+    *reinterpret_cast<uint4*>(Kr + t * LD + j0) = krv;
+    *reinterpret_cast<uint4*>(Qs + t * LD + j0) = qrv;
   }
   if (threadIdx.x < D) Gno[u * D + threadIdx.x] = __expf(Gs[(CH - 1) * LDG + threadIdx.x]);
   __syncthreads();
@@ -224,9 +273,13 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   kda_grams<E, D, NT, true>(Ks, Qs, Kr, Cl, Gs, unsafe, Ls, bs, Ao + u * CH * CH, CH, Mc, q + tk * D, n);
 
   // Khat = e^g K in place; V into the Q buffer
-  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
-    const int t = idx / D, j = idx % D;
-    Ks[t * LD + j] = (E)((float)Ks[t * LD + j] * __expf(Gs[t * LDG + j]));
+  for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
+    const int t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
+    uint4 kv = *reinterpret_cast<const uint4*>(Ks + t * LD + j0);
+    E* ke = reinterpret_cast<E*>(&kv);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) ke[e] = (E)((float)ke[e] * __expf(Gs[t * LDG + j0 + e]));
+    *reinterpret_cast<uint4*>(Ks + t * LD + j0) = kv;
   }
   rv.store(Qs, LD);
   __syncthreads();
