@@ -638,15 +638,36 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
   kda_flags<JW, NT>(Gs, LDF, unsafe);
   // Kend_s = k_s e^{g_{16(J+1)} - g_s} (s in block J < 3);  Kf_u, Qf_u = (k_u, q_u) e^{g_u - g_{16I}}
   // (u in block I);  Krf_s = k_s e^{g_{16I} - g_s} (zero in blocks summed exactly)
-  for (int idx = threadIdx.x; idx < CH * JW; idx += NT) {
-    const int s = idx / JW, j = idx % JW, r0 = s & ~15;
-    const float gs_ = Gs[s * LDF + j], g0 = Gs[r0 * LDF + j];
-    const float kv = (float)Ks[s * LDJ + j];
-    if (s < 48) Ke[s * LDJ + j] = (E)(kv * __expf(Gs[(r0 + 16) * LDF + j] - gs_));
-    const float f = __expf(gs_ - g0);
-    Kf[s * LDJ + j] = (E)(kv * f);
-    Qf[s * LDJ + j] = (E)((float)Qs[s * LDJ + j] * f);
-    Krf[s * LDJ + j] = (E)(unsafe[s >> 4] ? 0.f : kv * __expf(g0 - gs_));
+  {
+    constexpr int VE = 16 / (int)sizeof(E);  // 16 bytes per step
+    for (int idx = threadIdx.x; idx < CH * JW / VE; idx += NT) {
+      const int s = idx / (JW / VE), jv = (idx % (JW / VE)) * VE, r0 = s & ~15;
+      const bool uns = unsafe[s >> 4] != 0;
+      const uint4 kv4 = *reinterpret_cast<const uint4*>(Ks + s * LDJ + jv);
+      const uint4 qv4 = *reinterpret_cast<const uint4*>(Qs + s * LDJ + jv);
+      const E* ke = reinterpret_cast<const E*>(&kv4);
+      const E* qe = reinterpret_cast<const E*>(&qv4);
+      uint4 ev, fv, qfv, rv;
+      E* eo = reinterpret_cast<E*>(&ev);
+      E* fo = reinterpret_cast<E*>(&fv);
+      E* qo = reinterpret_cast<E*>(&qfv);
+      E* ro = reinterpret_cast<E*>(&rv);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const int j = jv + e;
+        const float gs_ = Gs[s * LDF + j], g0 = Gs[r0 * LDF + j];
+        const float kv = (float)ke[e];
+        eo[e] = (E)(s < 48 ? kv * __expf(Gs[(min(r0 + 16, CH - 1)) * LDF + j] - gs_) : 0.f);
+        const float f = __expf(gs_ - g0);
+        fo[e] = (E)(kv * f);
+        qo[e] = (E)((float)qe[e] * f);
+        ro[e] = (E)(uns ? 0.f : kv * __expf(g0 - gs_));
+      }
+      if (s < 48) *reinterpret_cast<uint4*>(Ke + s * LDJ + jv) = ev;
+      *reinterpret_cast<uint4*>(Kf + s * LDJ + jv) = fv;
+      *reinterpret_cast<uint4*>(Qf + s * LDJ + jv) = qfv;
+      *reinterpret_cast<uint4*>(Krf + s * LDJ + jv) = rv;
+    }
   }
   __syncthreads();
   const bool exact = unsafe[b] != 0;  // wave-uniform
