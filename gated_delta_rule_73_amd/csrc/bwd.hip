@@ -317,7 +317,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   const int n = cp.n;
 
   // ================= phase 1: products with the memory W0 and its gradient dW
-  f32x4 acc1[D / 16];  // row tile w of [dO; dR] times W0: waves 0-3 dQhat, waves 4-7 dR W0
+  f32x4 acc1[D / 16];  // waves 0-3: row tile wm of dQhat = dO W0; waves 4-7: (dR W0)^T, column
+                       // tile wm (stored four columns at a time)
   f32x4 dka[NQ];       // dk tiles (row tile wm, column tiles wn*NQ + qq)
   f32x4 acc3[2];       // dM tiles w and w + 8
 #pragma unroll
@@ -373,16 +374,20 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
         pdW.load(dHs + u * D * D + (long)(ih + 1) * KH * D, D, KH);
       }
       __syncthreads();
-      const E* Aop = (w < 4 ? dOs : dRs) + ih * KH;
+      if (w < 4) {
 #pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(Aop, LD), 16 * wm, colk(Wh, LD), 16 * nt);
+        for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(dOs + ih * KH, LD), 16 * wm, colk(Wh, LD), 16 * nt);
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], colk(Wh, LD), 16 * nt, rowk(dRs + ih * KH, LD), 16 * wm);
+      }
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq)
         dka[qq] = mma_k<E, KH>(dka[qq], rowk(Rs + ih * KH, LD), 16 * wm, colk(dWh, LD), 16 * (wn * NQ + qq));
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int id = w + 8 * e;
-        acc3[e] = mma_k<E, KH>(acc3[e], rowk(dOs + ih * KH, LD), 16 * (id >> 2), rowk(Rs + ih * KH, LD), 16 * (id & 3));
+        acc3[e] = mma_k<E, KH>(acc3[e], rowk(Rs + ih * KH, LD), 16 * (id & 3), rowk(dOs + ih * KH, LD), 16 * (id >> 2));  // dM^T
       }
     }
   }
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc1[nt][r] *= geo.scale * egr[r];
     } else {
-      store4_n(dXs, LD, 16 * wm, 16 * nt, -acc1[nt]);
+      store4_t(dXs, LD, 16 * nt, 16 * wm, -acc1[nt]);
     }
   }
   // dk (first term): e^{g_n - g_t} dKbar, and the rows' Kbar . dKbar
@@ -426,11 +431,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+    const int id = w + 8 * e, mt = id >> 2, nt = id & 3;  // dM tile (rows mt, columns nt), held transposed
     f32x4 x;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = (acc_col(16 * nt) <= acc_row(16 * mt, r)) ? geo.scale * acc3[e][r] : 0.f;
-    store4_n(dMs, LDR, 16 * mt, 16 * nt, x);
+    for (int r = 0; r < 4; ++r) x[r] = (acc_row(16 * nt, r) <= acc_col(16 * mt)) ? geo.scale * acc3[e][r] : 0.f;
+    store4_t(dMs, LDR, 16 * nt, 16 * mt, x);
   }
   if constexpr (GATED) {
     gam = wave_sum(gam);
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
       const int nt = wn * NQ + qq;
-      dva[qq] = mma_k<E, CH>(zero4(), Tt, 16 * wm, colk(dRs, LD), 16 * nt);
+      dva[qq] = mma_k<E, CH>(zero4(), colk(dRs, LD), 16 * nt, Tt, 16 * wm);  // dV^T
       f32x4 kh = mma_k<E, CH>(zero4(), Tt, 16 * wm, colk(dXs, LD), 16 * nt);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   }
   __syncthreads();
 #pragma unroll
-  for (int qq = 0; qq < NQ; ++qq) store4_n(Vs, LD, 16 * wm, 16 * (wn * NQ + qq), dva[qq]);
+  for (int qq = 0; qq < NQ; ++qq) store4_t(Vs, LD, 16 * (wn * NQ + qq), 16 * wm, dva[qq]);
   {  // dbeta from T = Linv diag(beta): column sums, eight threads per column
     const int s = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
@@ -533,25 +538,53 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   float* Pair = reinterpret_cast<float*>(smem + Ly::oPair);
   pQ.store(Qs, LD);
   // Each thread handles the (t, s) entries of M it holds in registers.
-  {
+  {  // VE consecutive columns per thread: vector LDS reads and writes
     using RM = RegTile<E, CH, CH, NT>;
+    constexpr int VE = RM::VE;
+    static_assert(VE % 4 == 0, "four float columns per vector");
 #pragma unroll
     for (int it = 0; it < RM::IT; ++it) {
       if (RM::TOTAL % NT == 0 || threadIdx.x + it * NT < RM::TOTAL) {
         const int t = pM.row(it), s0 = pM.col(it);
+        const float gt = gs[t], bt = bs[t];
+        float dTv[VE], Av[VE], gv[VE];
 #pragma unroll
-        for (int e = 0; e < RM::VE; ++e) {
+        for (int e = 0; e < VE; e += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(dTs + t * LF + s0 + e);
+          dTv[e] = x.x; dTv[e + 1] = x.y; dTv[e + 2] = x.z; dTv[e + 3] = x.w;
+          const float4 y = *reinterpret_cast<const float4*>(gs + s0 + e);
+          gv[e] = y.x; gv[e + 1] = y.y; gv[e + 2] = y.z; gv[e + 3] = y.w;
+          if constexpr (GATED) {
+            const float4 a = *reinterpret_cast<const float4*>(As + t * LF + s0 + e);
+            Av[e] = a.x; Av[e + 1] = a.y; Av[e + 2] = a.z; Av[e + 3] = a.w;
+          }
+        }
+        typename RM::V mv = *reinterpret_cast<const typename RM::V*>(dMs + t * LDR + s0), av, tv;
+        const E* me = reinterpret_cast<const E*>(&mv);
+        E* ae = reinterpret_cast<E*>(&av);
+        E* te = reinterpret_cast<E*>(&tv);
+        float pr[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
           const int s = s0 + e;
           float dec = 0.f;
           if (s <= t) {
             dec = 1.f;
-            if constexpr (GATED) dec = __expf(gs[t] - gs[s]);
+            if constexpr (GATED) dec = __expf(gt - gv[e]);
           }
-          const float dA = (s < t) ? bs[t] * dTs[t * LF + s] : 0.f;
-          const float dM = (s <= t) ? (float)dMs[t * LDR + s] : 0.f;
-          Ats[t * LDR + s] = (E)(dA * dec);
-          Mts[t * LDR + s] = (E)(dM * dec);
-          if constexpr (GATED) Pair[t * LF + s] = (s < t) ? dA * As[t * LF + s] + dM * (float)pM.elem(it, e) : 0.f;
+          const float dA = (s < t) ? bt * dTv[e] : 0.f;
+          const float dM = (s <= t) ? (float)me[e] : 0.f;
+          ae[e] = (E)(dA * dec);
+          te[e] = (E)(dM * dec);
+          pr[e] = 0.f;
+          if constexpr (GATED) pr[e] = (s < t) ? dA * Av[e] + dM * (float)pM.elem(it, e) : 0.f;
+        }
+        *reinterpret_cast<typename RM::V*>(Ats + t * LDR + s0) = av;
+        *reinterpret_cast<typename RM::V*>(Mts + t * LDR + s0) = tv;
+        if constexpr (GATED) {
+#pragma unroll
+          for (int e = 0; e < VE; e += 4)
+            *reinterpret_cast<float4*>(Pair + t * LF + s0 + e) = make_float4(pr[e], pr[e + 1], pr[e + 2], pr[e + 3]);
         }
       }
     }
