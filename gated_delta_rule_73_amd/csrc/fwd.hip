@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   __shared__ __align__(16) E Ts[CH * LDT];  // solve scratch, then T = Linv diag(beta)
   __shared__ __align__(16) float Ls[CH * LF];
   __shared__ __align__(16) float Li[CH * LF];
-  __shared__ float gs[CH], bs[CH];
+  __shared__ __align__(16) float gs[CH], bs[CH];
 
   const int gc = blockIdx.x, h = blockIdx.y;
   const ChunkPos cp = chunk_pos(geo, gc);
@@ -59,64 +59,88 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   __syncthreads();
 
   // Gram tiles: jobs 0..9 -> A (strict lower, times beta_t, into Ls), 10..19 -> M (lower).
+  // Formed transposed, so each lane holds four consecutive columns s of one row t and writes
+  // them with one vector store.
   for (int job = w; job < 20; job += 4) {
     const bool isM = job >= 10;
     int mt, nt;
     tri_tile(isM ? job - 10 : job, mt, nt);
-    const f32x4 acc = mma_k<E, D>(zero4(), rowk(isM ? QV : Ks, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
+    const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * nt, rowk(isM ? QV : Ks, LD), 16 * mt);
+    const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
+    float val[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
+      const int s = s0 + r;
       const bool keep = isM ? (s <= t) : (s < t);
-      float val = 0.f;
-      if (keep) {
-        float dec = 1.f;
-        if constexpr (VAR == VAR_GATED) dec = __expf(gs[t] - gs[s]);
-        val = acc[r] * dec;
-      }
-      if (isM) {
-        Mo[(u * CH + t) * CH + s] = (E)val;
+      float dec = 1.f;
+      if constexpr (VAR == VAR_GATED) dec = __expf(gs[t] - gs[s]);
+      val[r] = keep ? acc[r] * dec : 0.f;
+    }
+    if (isM) {
+      if constexpr (sizeof(E) == 2) {
+        *reinterpret_cast<bf16x4*>(Mo + (u * CH + t) * CH + s0) = bf16x4{(E)val[0], (E)val[1], (E)val[2], (E)val[3]};
       } else {
-        Ls[t * LF + s] = bs[t] * val;
-        Ao[(u * CH + t) * CH + s] = val;
+        *reinterpret_cast<float4*>(Mo + (u * CH + t) * CH + s0) = make_float4(val[0], val[1], val[2], val[3]);
       }
+    } else {
+      const float bt = bs[t];
+      *reinterpret_cast<float4*>(Ls + t * LF + s0) = make_float4(bt * val[0], bt * val[1], bt * val[2], bt * val[3]);
+      *reinterpret_cast<float4*>(Ao + (u * CH + t) * CH + s0) = make_float4(val[0], val[1], val[2], val[3]);
     }
   }
-  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-    const int t = idx >> 6, s = idx & 63;
-    if ((s >> 4) > (t >> 4)) {
-      Mo[(u * CH + t) * CH + s] = (E)0.f;
-      Ao[(u * CH + t) * CH + s] = 0.f;
+  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // tiles above the diagonal
+    const int t = idx >> 4, s0 = (idx & 15) * 4;
+    if ((s0 >> 4) > (t >> 4)) {
+      if constexpr (sizeof(E) == 2) {
+        *reinterpret_cast<bf16x4*>(Mo + (u * CH + t) * CH + s0) = bf16x4{(E)0.f, (E)0.f, (E)0.f, (E)0.f};
+      } else {
+        *reinterpret_cast<float4*>(Mo + (u * CH + t) * CH + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      *reinterpret_cast<float4*>(Ao + (u * CH + t) * CH + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   __syncthreads();
   rv.store(QV, LD);
   solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ts));
 
-  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-    const int t = idx >> 6, s = idx & 63;
-    Ts[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] * bs[s] : 0.f);
+  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // T = L^{-1} diag(beta), four columns at a time
+    const int t = idx >> 4, s0 = (idx & 15) * 4;
+    const float4 l = *reinterpret_cast<const float4*>(Li + t * LF + s0);
+    const float4 bb = *reinterpret_cast<const float4*>(bs + s0);
+    const float lv[4] = {l.x * bb.x, l.y * bb.y, l.z * bb.z, l.w * bb.w};
+    E tv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tv[r] = (E)(s0 + r <= t ? lv[r] : 0.f);
+    if constexpr (sizeof(E) == 2) *reinterpret_cast<bf16x4*>(Ts + t * LDT + s0) = bf16x4{tv[0], tv[1], tv[2], tv[3]};
+    else *reinterpret_cast<float4*>(Ts + t * LDT + s0) = make_float4(tv[0], tv[1], tv[2], tv[3]);
   }
   s2g_full<float, CH, CH, NT>(Lio + u * CH * CH, CH, Li, LF);  // L^{-1} for the backward
-  if constexpr (VAR == VAR_GATED) {
-    for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
-      const int t = idx / D, j = idx % D;
-      Ks[t * LD + j] = (E)(__expf(gs[t]) * (float)Ks[t * LD + j]);
+  if constexpr (VAR == VAR_GATED) {  // Khat = e^g K in place, 16 bytes at a time
+    constexpr int VE = 16 / (int)sizeof(E);
+    for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
+      const int t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
+      const float f = __expf(gs[t]);
+      uint4 kv = *reinterpret_cast<const uint4*>(Ks + t * LD + j0);
+      E* ke = reinterpret_cast<E*>(&kv);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) ke[e] = (E)(f * (float)ke[e]);
+      *reinterpret_cast<uint4*>(Ks + t * LD + j0) = kv;
     }
   }
   __syncthreads();
 
+  // X^T and U^T tiles (columns j of row tile w): each lane writes four consecutive columns
   f32x4 xa[D / 16], ua[D / 16];
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
-    xa[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Ks, LD), 16 * nt);
-    ua[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(QV, LD), 16 * nt);
+    xa[nt] = mma_k<E, CH>(zero4(), colk(Ks, LD), 16 * nt, rowk(Ts, LDT), 16 * w);
+    ua[nt] = mma_k<E, CH>(zero4(), colk(QV, LD), 16 * nt, rowk(Ts, LDT), 16 * w);
   }
   __syncthreads();
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
-    store4_n(Ks, LD, 16 * w, 16 * nt, xa[nt]);
-    store4_n(QV, LD, 16 * w, 16 * nt, ua[nt]);
+    store4_t(Ks, LD, 16 * nt, 16 * w, xa[nt]);
+    store4_t(QV, LD, 16 * nt, 16 * w, ua[nt]);
   }
   __syncthreads();
   s2g_full<E, CH, D, NT>(Xo + u * CH * D, D, Ks, LD);
