@@ -61,82 +61,109 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
     g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
     rk.store(Ks, LD);
     __syncthreads();
+    using RT = decltype(rk);
 #pragma unroll
-    for (int it = 0; it < decltype(rk)::IT; ++it) {
+    for (int it = 0; it < RT::IT; ++it) {
       const int t = rk.row(it), j = rk.col(it);
+      typename RT::V av, bv;
+      E* ae = reinterpret_cast<E*>(&av);
+      E* be = reinterpret_cast<E*>(&bv);
+      const float bt = bs[t];
 #pragma unroll
-      for (int x = 0; x < decltype(rk)::VE; ++x) {
-        As[t * LD + j + x] = (E)(bs[t] * (float)re.elem(it, x) * (float)rk.elem(it, x));
-        Bs[t * LD + j + x] = (E)(bs[t] * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+      for (int x = 0; x < RT::VE; ++x) {
+        ae[x] = (E)(bt * (float)re.elem(it, x) * (float)rk.elem(it, x));
+        be[x] = (E)(bt * (float)rw.elem(it, x) * (float)rv.elem(it, x));
       }
+      *reinterpret_cast<typename RT::V*>(As + t * LD + j) = av;
+      *reinterpret_cast<typename RT::V*>(Bs + t * LD + j) = bv;
     }
   }
   __syncthreads();
 
-  // 40 Gram tile jobs: A_kk, A_ak (strict lower), M_qk, M_qa (lower, to global)
+  // 40 Gram tile jobs: A_kk, A_ak (strict lower), M_qk, M_qa (lower, to global).  Formed
+  // transposed, so each lane holds four consecutive columns s of one row t (one vector store).
+  auto put4 = [](E* dst, const float* v) {
+    if constexpr (sizeof(E) == 2) *reinterpret_cast<bf16x4*>(dst) = bf16x4{(E)v[0], (E)v[1], (E)v[2], (E)v[3]};
+    else *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  };
   for (int job = w; job < 40; job += 4) {
     const int which = job / 10;
     int mt, nt;
     tri_tile(job % 10, mt, nt);
     const E* lhs = (which < 2) ? Ks : Qs;
     const E* rhs = (which == 0 || which == 2) ? Ks : As;
-    const f32x4 acc = mma_k<E, D>(zero4(), rowk(lhs, LD), 16 * mt, rowk(rhs, LD), 16 * nt);
+    const f32x4 acc = mma_k<E, D>(zero4(), rowk(rhs, LD), 16 * nt, rowk(lhs, LD), 16 * mt);
+    const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
+    float val[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
+      const int s = s0 + r;
       const bool keep = (which < 2) ? (s < t) : (s <= t);
-      const float val = keep ? acc[r] * __expf(gs[t] - gs[s]) : 0.f;
-      if (which == 0) {
-        Akk[t * LDT + s] = (E)val;
-        Akko[(u * CH + t) * CH + s] = val;
-      } else if (which == 1) {
-        Ls[t * LF + s] = val;
-        Aako[(u * CH + t) * CH + s] = val;
-      }
-      else if (which == 2) Mqk[(u * CH + t) * CH + s] = (E)val;
-      else Mqa[(u * CH + t) * CH + s] = (E)val;
+      val[r] = keep ? acc[r] * __expf(gs[t] - gs[s]) : 0.f;
+    }
+    const float4 v4 = make_float4(val[0], val[1], val[2], val[3]);
+    if (which == 0) {
+      put4(Akk + t * LDT + s0, val);
+      *reinterpret_cast<float4*>(Akko + (u * CH + t) * CH + s0) = v4;
+    } else if (which == 1) {
+      *reinterpret_cast<float4*>(Ls + t * LF + s0) = v4;
+      *reinterpret_cast<float4*>(Aako + (u * CH + t) * CH + s0) = v4;
+    } else {
+      put4((which == 2 ? Mqk : Mqa) + (u * CH + t) * CH + s0, val);
     }
   }
-  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-    const int t = idx >> 6, s = idx & 63;
-    if ((s >> 4) > (t >> 4)) {
-      Mqk[(u * CH + t) * CH + s] = (E)0.f;
-      Mqa[(u * CH + t) * CH + s] = (E)0.f;
-      Akk[t * LDT + s] = (E)0.f;
-      Akko[(u * CH + t) * CH + s] = 0.f;
-      Aako[(u * CH + t) * CH + s] = 0.f;
+  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // tiles above the diagonal
+    const int t = idx >> 4, s0 = (idx & 15) * 4;
+    if ((s0 >> 4) > (t >> 4)) {
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      put4(Mqk + (u * CH + t) * CH + s0, z);
+      put4(Mqa + (u * CH + t) * CH + s0, z);
+      put4(Akk + t * LDT + s0, z);
+      *reinterpret_cast<float4*>(Akko + (u * CH + t) * CH + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(Aako + (u * CH + t) * CH + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   __syncthreads();
   solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ti));
   s2g_full<float, CH, CH, NT>(Lio + u * CH * CH, CH, Li, LF);  // L^{-1} for the backward
-  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-    const int t = idx >> 6, s = idx & 63;
-    Ti[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] : 0.f);
+  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // L^{-1} as an operand, four columns at a time
+    const int t = idx >> 4, s0 = (idx & 15) * 4;
+    const float4 l = *reinterpret_cast<const float4*>(Li + t * LF + s0);
+    const float v[4] = {s0 <= t ? l.x : 0.f, s0 + 1 <= t ? l.y : 0.f, s0 + 2 <= t ? l.z : 0.f, s0 + 3 <= t ? l.w : 0.f};
+    put4(Ti + t * LDT + s0, v);
   }
-  // A_kk B into registers (the Q buffer receives it below)
+  // (A_kk B)^T into registers (the Q buffer receives it below)
   f32x4 cu[D / 16];
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) cu[nt] = mma_k<E, CH>(zero4(), rowk(Akk, LDT), 16 * w, colk(Bs, LD), 16 * nt);
-  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
-    const int t = idx / D, j = idx % D;
-    Ks[t * LD + j] = (E)(__expf(gs[t]) * (float)Ks[t * LD + j]);
+  for (int nt = 0; nt < D / 16; ++nt) cu[nt] = mma_k<E, CH>(zero4(), colk(Bs, LD), 16 * nt, rowk(Akk, LDT), 16 * w);
+  {  // Khat = e^g K in place, 16 bytes at a time
+    constexpr int VE = 16 / (int)sizeof(E);
+    for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
+      const int t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
+      const float f = __expf(gs[t]);
+      uint4 kv = *reinterpret_cast<const uint4*>(Ks + t * LD + j0);
+      E* ke = reinterpret_cast<E*>(&kv);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) ke[e] = (E)(f * (float)ke[e]);
+      *reinterpret_cast<uint4*>(Ks + t * LD + j0) = kv;
+    }
   }
   __syncthreads();
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) store4_n(Qs, LD, 16 * w, 16 * nt, cu[nt]);
+  for (int nt = 0; nt < D / 16; ++nt) store4_t(Qs, LD, 16 * nt, 16 * w, cu[nt]);
   __syncthreads();
+  // X'^T and U''^T tiles: each lane writes four consecutive columns
   f32x4 xa[D / 16], ua[D / 16];
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
-    xa[nt] = mma_k<E, CH>(zero4(), rowk(Ti, LDT), 16 * w, colk(Ks, LD), 16 * nt);
-    ua[nt] = -mma_k<E, CH>(zero4(), rowk(Ti, LDT), 16 * w, colk(Qs, LD), 16 * nt);
+    xa[nt] = mma_k<E, CH>(zero4(), colk(Ks, LD), 16 * nt, rowk(Ti, LDT), 16 * w);
+    ua[nt] = -mma_k<E, CH>(zero4(), colk(Qs, LD), 16 * nt, rowk(Ti, LDT), 16 * w);
   }
   __syncthreads();
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
-    store4_n(Ks, LD, 16 * w, 16 * nt, xa[nt]);
-    store4_n(Qs, LD, 16 * w, 16 * nt, ua[nt]);
+    store4_t(Ks, LD, 16 * nt, 16 * w, xa[nt]);
+    store4_t(Qs, LD, 16 * nt, 16 * w, ua[nt]);
   }
   __syncthreads();
   s2g_full<E, CH, D, NT>(Xo + u * CH * D, D, Ks, LD);
