@@ -186,6 +186,28 @@ __device__ __forceinline__ void store4_t(S* dst, int ld, int m0, int n0, f32x4 v
     *reinterpret_cast<bf16x4*>(p) = b;
   }
 }
+// Four consecutive elements dst[0..3] = v (one 8-byte bfloat16 or 16-byte float store).
+template <typename S>
+__device__ __forceinline__ void put4(S* dst, f32x4 v) {
+  if constexpr (std::is_same<S, float>::value) {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    bf16x4 b;
+    b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+    *reinterpret_cast<bf16x4*>(dst) = b;
+  }
+}
+// Four consecutive elements src[0..3] as float.
+template <typename S>
+__device__ __forceinline__ f32x4 get4(const S* src) {
+  if constexpr (std::is_same<S, float>::value) {
+    const float4 x = *reinterpret_cast<const float4*>(src);
+    return f32x4{x.x, x.y, x.z, x.w};
+  } else {
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(src);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+  }
+}
 // Store in the tile's own orientation: dst[row*ld + col].
 template <typename S>
 __device__ __forceinline__ void store4_n(S* dst, int ld, int m0, int n0, f32x4 v) {

@@ -366,8 +366,8 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   __shared__ __align__(16) char smem[Ly::BYTES];
   __shared__ float gs[CH], bs[CH], rk[4][CH], rb[4][CH];
   E* Ks = reinterpret_cast<E*>(smem);
-  E* LiT = Ks + CH * LD;
-  E* AkkE = LiT + CH * LDT;
+  E* LiN = Ks + CH * LD;  // L^{-1}, row-major (read k-major where its transpose is needed)
+  E* AkkE = LiN + CH * LDT;
   E* Mqk = AkkE + CH * LDT;
   char* un = reinterpret_cast<char*>(Mqk + CH * LDT);
   E* P1 = reinterpret_cast<E*>(un);
@@ -380,6 +380,10 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id(), n = cp.n;
+  // Products below are formed transposed: lane (lrow, lgrp) of wave w holds row t = 16w + lrow
+  // and four consecutive columns 4 lgrp .. +3 of each 16-column tile, so every global or LDS
+  // access of a result is one vector access.
+  const int tr = 16 * w + lrow();
 
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
@@ -388,54 +392,55 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   }
   g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
   g2s_rows<E, CH, CH, NT>(Mqk, LDT, M2g + u * CH * CH, CH, CH);
-  {  // (L^{-1})^T and A_kk as the forward computed them
+  {  // L^{-1} and A_kk as the forward computed them
     RegTile<float, CH, CH, NT> rli, rakk;
     rli.load(p.Li + u * CH * CH, CH, CH);
     rakk.load(p.A1 + u * CH * CH, CH, CH);
+    static_assert(decltype(rli)::VE == 4, "four floats per vector");
 #pragma unroll
     for (int it = 0; it < decltype(rli)::IT; ++it) {
       const int t = rli.row(it), s0 = rli.col(it);
-#pragma unroll
-      for (int x = 0; x < decltype(rli)::VE; ++x) {
-        LiT[(s0 + x) * LDT + t] = (E)rli.elem(it, x);
-        AkkE[t * LDT + s0 + x] = (E)rakk.elem(it, x);
-      }
+      put4(LiN + t * LDT + s0, f32x4{rli.elem(it, 0), rli.elem(it, 1), rli.elem(it, 2), rli.elem(it, 3)});
+      put4(AkkE + t * LDT + s0, f32x4{rakk.elem(it, 0), rakk.elem(it, 1), rakk.elem(it, 2), rakk.elem(it, 3)});
     }
   }
-  __syncthreads();
   {  // dX' (float32 workspace) and dR' into the union region
     const float* dx = p.g2_dx + u * CH * D;
-    for (int idx = threadIdx.x; idx < CH * D; idx += NT) P1[(idx / D) * LD + idx % D] = (E)dx[idx];
+    for (int idx = threadIdx.x; idx < CH * D / 4; idx += NT) {
+      const int t = idx / (D / 4), j0 = (idx % (D / 4)) * 4;
+      const float4 x = *reinterpret_cast<const float4*>(dx + t * D + j0);
+      put4(P1 + t * LD + j0, f32x4{x.x, x.y, x.z, x.w});
+    }
     g2s_rows<E, CH, D, NT>(P2, LD, dRg + u * CH * D, D, CH);
   }
   __syncthreads();
+  // dKhat^T = dX'^T L^{-1} and dC^T = -dR'^T L^{-1} (columns j, rows t)
   f32x4 dkh[D / 16], dc[D / 16];
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
-    dkh[nt] = mma_k<E, CH>(zero4(), rowk(LiT, LDT), 16 * w, colk(P1, LD), 16 * nt);
-    dc[nt] = -mma_k<E, CH>(zero4(), rowk(LiT, LDT), 16 * w, colk(P2, LD), 16 * nt);
+    dkh[nt] = mma_k<E, CH>(zero4(), colk(P1, LD), 16 * nt, colk(LiN, LDT), 16 * w);
+    dc[nt] = -mma_k<E, CH>(zero4(), colk(P2, LD), 16 * nt, colk(LiN, LDT), 16 * w);
   }
   __syncthreads();
   {
     float* dk1 = p.g2_dk + u * CH * D;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    const float et = __expf(gs[tr]);
+    float part = 0.f;
 #pragma unroll
     for (int nt = 0; nt < D / 16; ++nt) {
-      store4_n(P1, LD, 16 * w, 16 * nt, dkh[nt]);
-      store4_n(P2, LD, 16 * w, 16 * nt, dc[nt]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(16 * w, r), j = acc_col(16 * nt);
-        const float x = __expf(gs[t]) * dkh[nt][r];
-        dk1[t * D + j] += x;
-        part[r] += (float)Ks[t * LD + j] * x;
-      }
+      store4_t(P1, LD, 16 * nt, 16 * w, dkh[nt]);
+      store4_t(P2, LD, 16 * nt, 16 * w, dc[nt]);
+      const int j0 = 16 * nt + 4 * lgrp();
+      const f32x4 x = et * dkh[nt];
+      float4 d = *reinterpret_cast<const float4*>(dk1 + tr * D + j0);
+      d.x += x[0]; d.y += x[1]; d.z += x[2]; d.w += x[3];
+      *reinterpret_cast<float4*>(dk1 + tr * D + j0) = d;
+      const f32x4 kv = get4(Ks + tr * LD + j0);
+      part += kv[0] * x[0] + kv[1] * x[1] + kv[2] * x[2] + kv[3] * x[3];
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float a = sum16(part[r]);
-      if (lrow() == 0) rk[w][acc_row(16 * w, r)] = a;
-    }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (lgrp() == 0) rk[w][tr] = part;
   }
   g2s_rows<E, CH, D, NT>(P3, LD, Xg + u * CH * D, D, CH);
   g2s_rows<E, CH, D, NT>(P4, LD, U2g + u * CH * D, D, CH);
@@ -443,24 +448,28 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   float* daak = p.g2_daak + u * CH * CH;
   for (int id = w; id < 16; id += 4) {
     const int mt = id >> 2, nt = id & 3;
-    f32x4 acc = mma_k<E, D>(zero4(), rowk(P2, LD), 16 * mt, rowk(P4, LD), 16 * nt);
-    acc = acc - mma_k<E, D>(zero4(), rowk(P1, LD), 16 * mt, rowk(P3, LD), 16 * nt);
+    f32x4 acc = mma_k<E, D>(zero4(), rowk(P4, LD), 16 * nt, rowk(P2, LD), 16 * mt);
+    acc = acc - mma_k<E, D>(zero4(), rowk(P3, LD), 16 * nt, rowk(P1, LD), 16 * mt);
+    const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s2 = acc_col(16 * nt);
-      daak[t * CH + s2] = (s2 < t) ? acc[r] : 0.f;
-    }
+    for (int r = 0; r < 4; ++r) acc[r] = (s0 + r < t) ? acc[r] : 0.f;
+    put4(daak + t * CH + s0, acc);
   }
   __syncthreads();
   {  // b = beta w*v into P3, dO into P4
     RegTile<E, CH, D, NT> rv, rw;
     rv.load(v + tk * D, D, n);
     rw.load(write + tk * D, D, n);
+    using RT = decltype(rv);
 #pragma unroll
-    for (int it = 0; it < decltype(rv)::IT; ++it) {
+    for (int it = 0; it < RT::IT; ++it) {
       const int t = rv.row(it), i = rv.col(it);
+      typename RT::V bv;
+      E* be = reinterpret_cast<E*>(&bv);
+      const float bt = bs[t];
 #pragma unroll
-      for (int x = 0; x < decltype(rv)::VE; ++x) P3[t * LD + i + x] = (E)(bs[t] * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+      for (int x = 0; x < RT::VE; ++x) be[x] = (E)(bt * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+      *reinterpret_cast<typename RT::V*>(P3 + t * LD + i) = bv;
     }
     g2s_rows<E, CH, D, NT>(P4, LD, dO + tk * D, D, n);
   }
@@ -468,25 +477,24 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   float* dakk = p.g2_dakk + u * CH * CH;
   for (int id = w; id < 16; id += 4) {
     const int mt = id >> 2, nt = id & 3;
-    const f32x4 acc = mma_k<E, D>(zero4(), rowk(P2, LD), 16 * mt, rowk(P3, LD), 16 * nt);
+    f32x4 acc = mma_k<E, D>(zero4(), rowk(P3, LD), 16 * nt, rowk(P2, LD), 16 * mt);
+    const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s2 = acc_col(16 * nt);
-      dakk[t * CH + s2] = (s2 < t) ? acc[r] : 0.f;
-    }
+    for (int r = 0; r < 4; ++r) acc[r] = (s0 + r < t) ? acc[r] : 0.f;
+    put4(dakk + t * CH + s0, acc);
   }
-  // dB = dB_state + A_kk^T dC + M_qk^T (scale dO)
+  // dB^T = dB_state^T + dC^T A_kk + (scale dO)^T M_qk
   f32x4 dbt[D / 16];
   const float* db1 = p.g2_db + u * CH * D;
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
-    f32x4 a = mma_k<E, CH>(zero4(), colk(AkkE, LDT), 16 * w, colk(P2, LD), 16 * nt);
-    const f32x4 b = mma_k<E, CH>(zero4(), colk(Mqk, LDT), 16 * w, colk(P4, LD), 16 * nt);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * w, r), i = acc_col(16 * nt);
-      a[r] += geo.scale * b[r] + db1[t * D + i];
-    }
+    f32x4 a = mma_k<E, CH>(zero4(), colk(P2, LD), 16 * nt, colk(AkkE, LDT), 16 * w);
+    const f32x4 bq = mma_k<E, CH>(zero4(), colk(P4, LD), 16 * nt, colk(Mqk, LDT), 16 * w);
+    const float4 d = *reinterpret_cast<const float4*>(db1 + tr * D + 16 * nt + 4 * lgrp());
+    a[0] += geo.scale * bq[0] + d.x;
+    a[1] += geo.scale * bq[1] + d.y;
+    a[2] += geo.scale * bq[2] + d.z;
+    a[3] += geo.scale * bq[3] + d.w;
     dbt[nt] = a;
   }
   __syncthreads();
@@ -496,26 +504,20 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   }
   __syncthreads();
   {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    const float bt = bs[tr];
+    float part = 0.f;
 #pragma unroll
     for (int nt = 0; nt < D / 16; ++nt) {
-      f32x4 ov, ow;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(16 * w, r), i = acc_col(16 * nt);
-        const float vv = (float)P1[t * LD + i], ww = (float)P3[t * LD + i];
-        ov[r] = bs[t] * ww * dbt[nt][r];
-        ow[r] = bs[t] * vv * dbt[nt][r];
-        part[r] += ww * vv * dbt[nt][r];
-      }
-      store4_n(P2, LD, 16 * w, 16 * nt, ov);
-      store4_n(P4, LD, 16 * w, 16 * nt, ow);
+      const int i0 = 16 * nt + 4 * lgrp();
+      const f32x4 vv = get4(P1 + tr * LD + i0), ww = get4(P3 + tr * LD + i0);
+      const f32x4 ov = bt * ww * dbt[nt], ow = bt * vv * dbt[nt];
+      part += ww[0] * vv[0] * dbt[nt][0] + ww[1] * vv[1] * dbt[nt][1] + ww[2] * vv[2] * dbt[nt][2] + ww[3] * vv[3] * dbt[nt][3];
+      store4_t(P2, LD, 16 * nt, 16 * w, ov);
+      store4_t(P4, LD, 16 * nt, 16 * w, ow);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float a = sum16(part[r]);
-      if (lrow() == 0) rb[w][acc_row(16 * w, r)] = a;
-    }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (lgrp() == 0) rb[w][tr] = part;
   }
   __syncthreads();
   s2g_rows<E, CH, D, NT>(dv + tk * D, D, P2, LD, n);
