@@ -579,101 +579,126 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
   g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
   g2s_rows<E, CH, D, NT>(Es, LD, erase + tk * D, D, n);
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
-    const int t = idx / D, j = idx % D;
-    As[t * LD + j] = (E)(bs[t] * (float)Es[t * LD + j] * (float)Ks[t * LD + j]);
-  }
-  {
-    const float* dakk = p.g2_dakk + u * CH * CH;
-    const float* daak = p.g2_daak + u * CH * CH;
-    const float* dmqk = p.g2_dmqk + u * CH * CH;
-    const float* dmqa = p.g2_dmqa + u * CH * CH;
-    const float* akk = p.A1 + u * CH * CH;
-    const float* aak = p.A2 + u * CH * CH;
-    const E* mqk = Mqkg + u * CH * CH;
-    const E* mqa = Mqag + u * CH * CH;
-    for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-      const int t = idx >> 6, s2 = idx & 63;
-      const float dec = (s2 <= t) ? __expf(gs[t] - gs[s2]) : 0.f;
-      Tkk[t * LDT + s2] = (E)(dakk[idx] * dec);
-      Tak[t * LDT + s2] = (E)(daak[idx] * dec);
-      Tqk[t * LDT + s2] = (E)(dmqk[idx] * dec);
-      Tqa[t * LDT + s2] = (E)(dmqa[idx] * dec);
-      Pair[t * LF + s2] = (s2 < t) ? dakk[idx] * akk[idx] + daak[idx] * aak[idx] + dmqk[idx] * (float)mqk[idx] +
-                                         dmqa[idx] * (float)mqa[idx]
-                                   : 0.f;
+  // Products are formed transposed: lane (lrow, lgrp) of wave w holds row t = 16w + lrow and
+  // four consecutive columns 4 lgrp .. +3 of each 16-column tile, so every access of a result
+  // is one vector access.
+  const int tr = 16 * w + lrow();
+  f32x4 aq[D / 16], ak[D / 16], aa[D / 16];
+  {  // the partial gradients from the earlier stages, issued early
+    const float* dq1 = p.g2_dq + u * CH * D + tr * D + 4 * lgrp();
+    const float* dk1 = p.g2_dk + u * CH * D + tr * D + 4 * lgrp();
+    const float* da1 = p.g2_da + u * CH * D + tr * D + 4 * lgrp();
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      const float4 x = *reinterpret_cast<const float4*>(dq1 + 16 * nt);
+      const float4 y = *reinterpret_cast<const float4*>(dk1 + 16 * nt);
+      const float4 z = *reinterpret_cast<const float4*>(da1 + 16 * nt);
+      aq[nt] = f32x4{x.x, x.y, x.z, x.w};
+      ak[nt] = f32x4{y.x, y.y, y.z, y.w};
+      aa[nt] = f32x4{z.x, z.y, z.z, z.w};
     }
   }
   __syncthreads();
-  f32x4 aq[D / 16], ak[D / 16], aa[D / 16];
-  {
-    const float* dq1 = p.g2_dq + u * CH * D;
-    const float* dk1 = p.g2_dk + u * CH * D;
-    const float* da1 = p.g2_da + u * CH * D;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+  {  // a = beta e*k, 16 bytes at a time
+    constexpr int VE = 16 / (int)sizeof(E);
+    for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
+      const int t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
+      const uint4 ev = *reinterpret_cast<const uint4*>(Es + t * LD + j0);
+      const uint4 kv = *reinterpret_cast<const uint4*>(Ks + t * LD + j0);
+      const E* ee = reinterpret_cast<const E*>(&ev);
+      const E* ke = reinterpret_cast<const E*>(&kv);
+      uint4 av;
+      E* ae = reinterpret_cast<E*>(&av);
+      const float bt = bs[t];
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt)
+      for (int e = 0; e < VE; ++e) ae[e] = (E)(bt * (float)ee[e] * (float)ke[e]);
+      *reinterpret_cast<uint4*>(As + t * LD + j0) = av;
+    }
+  }
+  {  // decayed gradients of the chunk matrices and the pair terms, four columns at a time
+    const long o0 = u * CH * CH;
+    for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {
+      const int t = idx >> 4, s0 = (idx & 15) * 4;
+      const long o = o0 + t * CH + s0;
+      const float4 d1 = *reinterpret_cast<const float4*>(p.g2_dakk + o);
+      const float4 d2 = *reinterpret_cast<const float4*>(p.g2_daak + o);
+      const float4 d3 = *reinterpret_cast<const float4*>(p.g2_dmqk + o);
+      const float4 d4 = *reinterpret_cast<const float4*>(p.g2_dmqa + o);
+      const float4 a1 = *reinterpret_cast<const float4*>(p.A1 + o);
+      const float4 a2 = *reinterpret_cast<const float4*>(p.A2 + o);
+      const f32x4 m1 = get4(Mqkg + o), m2 = get4(Mqag + o);
+      const float e1[4] = {d1.x, d1.y, d1.z, d1.w}, e2[4] = {d2.x, d2.y, d2.z, d2.w};
+      const float e3[4] = {d3.x, d3.y, d3.z, d3.w}, e4[4] = {d4.x, d4.y, d4.z, d4.w};
+      const float f1[4] = {a1.x, a1.y, a1.z, a1.w}, f2[4] = {a2.x, a2.y, a2.z, a2.w};
+      f32x4 tkk, tak, tqk, tqa, pr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(16 * w, r), j = acc_col(16 * nt);
-        aq[nt][r] = dq1[t * D + j];
-        ak[nt][r] = dk1[t * D + j];
-        aa[nt][r] = da1[t * D + j];
-        part[r] += (float)Qs[t * LD + j] * aq[nt][r];
+        const int s2 = s0 + r;
+        const float dec = (s2 <= t) ? __expf(gs[t] - gs[s2]) : 0.f;
+        tkk[r] = e1[r] * dec;
+        tak[r] = e2[r] * dec;
+        tqk[r] = e3[r] * dec;
+        tqa[r] = e4[r] * dec;
+        pr[r] = (s2 < t) ? e1[r] * f1[r] + e2[r] * f2[r] + e3[r] * m1[r] + e4[r] * m2[r] : 0.f;
       }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float a = sum16(part[r]);
-      if (lrow() == 0) rq[w][acc_row(16 * w, r)] = a;
+      put4(Tkk + t * LDT + s0, tkk);
+      put4(Tak + t * LDT + s0, tak);
+      put4(Tqk + t * LDT + s0, tqk);
+      put4(Tqa + t * LDT + s0, tqa);
+      put4(Pair + t * LF + s0, pr);
     }
+  }
+  __syncthreads();
+  {
+    float part = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      const f32x4 qv = get4(Qs + tr * LD + 16 * nt + 4 * lgrp());
+      part += qv[0] * aq[nt][0] + qv[1] * aq[nt][1] + qv[2] * aq[nt][2] + qv[3] * aq[nt][3];
+    }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (lgrp() == 0) rq[w][tr] = part;
   }
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
-    ak[nt] = mma_k<E, CH>(ak[nt], rowk(Tkk, LDT), 16 * w, colk(Ks, LD), 16 * nt);
-    ak[nt] = mma_k<E, CH>(ak[nt], colk(Tkk, LDT), 16 * w, colk(Ks, LD), 16 * nt);
-    ak[nt] = mma_k<E, CH>(ak[nt], rowk(Tak, LDT), 16 * w, colk(As, LD), 16 * nt);
-    ak[nt] = mma_k<E, CH>(ak[nt], colk(Tqk, LDT), 16 * w, colk(Qs, LD), 16 * nt);
-    aq[nt] = mma_k<E, CH>(aq[nt], rowk(Tqk, LDT), 16 * w, colk(Ks, LD), 16 * nt);
-    aq[nt] = mma_k<E, CH>(aq[nt], rowk(Tqa, LDT), 16 * w, colk(As, LD), 16 * nt);
-    aa[nt] = mma_k<E, CH>(aa[nt], colk(Tak, LDT), 16 * w, colk(Ks, LD), 16 * nt);
-    aa[nt] = mma_k<E, CH>(aa[nt], colk(Tqa, LDT), 16 * w, colk(Qs, LD), 16 * nt);
+    ak[nt] = mma_k<E, CH>(ak[nt], colk(Ks, LD), 16 * nt, rowk(Tkk, LDT), 16 * w);
+    ak[nt] = mma_k<E, CH>(ak[nt], colk(Ks, LD), 16 * nt, colk(Tkk, LDT), 16 * w);
+    ak[nt] = mma_k<E, CH>(ak[nt], colk(As, LD), 16 * nt, rowk(Tak, LDT), 16 * w);
+    ak[nt] = mma_k<E, CH>(ak[nt], colk(Qs, LD), 16 * nt, colk(Tqk, LDT), 16 * w);
+    aq[nt] = mma_k<E, CH>(aq[nt], colk(Ks, LD), 16 * nt, rowk(Tqk, LDT), 16 * w);
+    aq[nt] = mma_k<E, CH>(aq[nt], colk(As, LD), 16 * nt, rowk(Tqa, LDT), 16 * w);
+    aa[nt] = mma_k<E, CH>(aa[nt], colk(Ks, LD), 16 * nt, colk(Tak, LDT), 16 * w);
+    aa[nt] = mma_k<E, CH>(aa[nt], colk(Qs, LD), 16 * nt, colk(Tqa, LDT), 16 * w);
   }
   // gates: de = beta da*k, dk += beta da*e, dbeta_a = sum_j da*e*k
   {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    const float bt = bs[tr];
+    float part = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(16 * w, r), j = acc_col(16 * nt);
-        const float kk = (float)Ks[t * LD + j], ee = (float)Es[t * LD + j], da = aa[nt][r];
-        ak[nt][r] += bs[t] * da * ee;
-        part[r] += da * ee * kk;
-        aa[nt][r] = bs[t] * da * kk;  // now de
-      }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float a = sum16(part[r]);
-      if (lrow() == 0) re_[w][acc_row(16 * w, r)] = a;
+    for (int nt = 0; nt < D / 16; ++nt) {
+      const int j0 = 16 * nt + 4 * lgrp();
+      const f32x4 kk = get4(Ks + tr * LD + j0), ee = get4(Es + tr * LD + j0), da = aa[nt];
+      ak[nt] += bt * da * ee;
+      part += da[0] * ee[0] * kk[0] + da[1] * ee[1] * kk[1] + da[2] * ee[2] * kk[2] + da[3] * ee[3] * kk[3];
+      aa[nt] = bt * da * kk;  // now de
     }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (lgrp() == 0) re_[w][tr] = part;
   }
-  if (threadIdx.x < CH) {  // prefix sums along each row of the pair terms
-    const int uu = threadIdx.x;
-    float run = 0.f;
-#pragma unroll 16
-    for (int s2 = 0; s2 < CH; ++s2) {
-      run += Pair[uu * LF + s2];
-      Pair[uu * LF + s2] = run;
-    }
+  // prefix sums along each row of the pair terms: lanes over columns, rows over the waves
+  for (int uu = w; uu < CH; uu += NT / 64) {
+    float* row = Pair + uu * LF;
+    row[lane_id()] = wave_incl_scan(row[lane_id()]);
   }
   __syncthreads();
   // outputs through LDS (K, A, Q regions are free now)
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
-    store4_n(Ks, LD, 16 * w, 16 * nt, ak[nt]);
-    store4_n(Qs, LD, 16 * w, 16 * nt, aq[nt]);
-    store4_n(As, LD, 16 * w, 16 * nt, aa[nt]);
+    store4_t(Ks, LD, 16 * nt, 16 * w, ak[nt]);
+    store4_t(Qs, LD, 16 * nt, 16 * w, aq[nt]);
+    store4_t(As, LD, 16 * nt, 16 * w, aa[nt]);
   }
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
@@ -683,8 +708,8 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
 #pragma unroll 16
       for (int uu = 0; uu < CH; ++uu) rect += (uu >= t) ? Pair[uu * LF + t - 1] : 0.f;
     }
-    const int tr = CH - 1 - t;
-    const float suf_r = wave_incl_scan(rq[tr >> 4][tr] + rows[CH + tr]);
+    const int tq = CH - 1 - t;
+    const float suf_r = wave_incl_scan(rq[tq >> 4][tq] + rows[CH + tq]);
     const float suf = __shfl(suf_r, CH - 1 - t, 64);
     const float inc = wave_incl_scan(rows[t]);
     float pre = __shfl_up(inc, 1, 64);
