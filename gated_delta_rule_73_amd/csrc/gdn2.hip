@@ -201,14 +201,18 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
   E* dOs = Bs + CH * LD;
   E* dRs = dOs + CH * LD;
   E* Rs = dRs + CH * LD;
-  E* Wh = Rs + CH * LD;
-  E* dWh = Wh + D * LDR;
+  E* Wh = Rs + CH * LD;   // one 64-row block of W0, row-major (rows i, columns j)
+  E* dWh = Wh + D * LDR;  // the same block of dW
+  static_assert(KH * LD <= D * LDR, "a row-major block fits the region");
 
   const int gc = blockIdx.x, h = blockIdx.y;
   const ChunkPos cp = chunk_pos(geo, gc);
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id(), wm = w & 3, wn = w >> 2, n = cp.n;
+  // Products are formed transposed: a lane holds row t = 16 (row tile) + lrow and four
+  // consecutive columns 4 lgrp .. +3 of each 16-column tile, so results go out as vectors.
+  const int tr = 16 * wm + lrow();
 
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
@@ -226,14 +230,21 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
     g2s_rows<E, CH, D, NT>(dRs, LD, dRg + u * CH * D, D, CH);
     rk.store(Ks, LD);
     __syncthreads();
+    using RT = decltype(rk);
 #pragma unroll
-    for (int it = 0; it < decltype(rk)::IT; ++it) {
+    for (int it = 0; it < RT::IT; ++it) {
       const int t = rk.row(it), j = rk.col(it);
+      typename RT::V av, bv;
+      E* ae = reinterpret_cast<E*>(&av);
+      E* be = reinterpret_cast<E*>(&bv);
+      const float bt = bs[t];
 #pragma unroll
-      for (int x = 0; x < decltype(rk)::VE; ++x) {
-        As[t * LD + j + x] = (E)(bs[t] * (float)re.elem(it, x) * (float)rk.elem(it, x));
-        Bs[t * LD + j + x] = (E)(bs[t] * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+      for (int x = 0; x < RT::VE; ++x) {
+        ae[x] = (E)(bt * (float)re.elem(it, x) * (float)rk.elem(it, x));
+        be[x] = (E)(bt * (float)rw.elem(it, x) * (float)rv.elem(it, x));
       }
+      *reinterpret_cast<typename RT::V*>(As + t * LD + j) = av;
+      *reinterpret_cast<typename RT::V*>(Bs + t * LD + j) = bv;
     }
   }
   const float gn = gs[CH - 1];
@@ -247,68 +258,71 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
   float* db1 = p.g2_db + u * CH * D;
   for (int ih = 0; ih < NH; ++ih) {
     __syncthreads();
-    g2s_rows_t<E, KH, D, NT>(Wh, LDR, Hs + u * D * D + (long)ih * KH * D, D, KH);
-    g2s_rows_t<E, KH, D, NT>(dWh, LDR, dHs + u * D * D + (long)ih * KH * D, D, KH);
+    g2s_rows<E, KH, D, NT>(Wh, LD, Hs + u * D * D + (long)ih * KH * D, D, KH);
+    g2s_rows<E, KH, D, NT>(dWh, LD, dHs + u * D * D + (long)ih * KH * D, D, KH);
     __syncthreads();
     const E* Aop = (w < 4 ? dOs : dRs) + ih * KH;
+    // (dO W0)^T or (dR W0)^T: columns j, rows t
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(Aop, LD), 16 * wm, rowk(Wh, LDR), 16 * nt);
+    for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], colk(Wh, LD), 16 * nt, rowk(Aop, LD), 16 * wm);
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
-      dab[qq] = mma_k<E, KH>(dab[qq], rowk(Rs + ih * KH, LD), 16 * wm, rowk(dWh, LDR), 16 * (wn * NQ + qq));
-      dkb[qq] = mma_k<E, KH>(dkb[qq], rowk(Bs + ih * KH, LD), 16 * wm, rowk(dWh, LDR), 16 * (wn * NQ + qq));
+      dab[qq] = mma_k<E, KH>(dab[qq], colk(dWh, LD), 16 * (wn * NQ + qq), rowk(Rs + ih * KH, LD), 16 * wm);
+      dkb[qq] = mma_k<E, KH>(dkb[qq], colk(dWh, LD), 16 * (wn * NQ + qq), rowk(Bs + ih * KH, LD), 16 * wm);
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
-      mqa[e] = mma_k<E, KH>(mqa[e], rowk(dOs + ih * KH, LD), 16 * mt, rowk(Rs + ih * KH, LD), 16 * nt);
-      mqk[e] = mma_k<E, KH>(mqk[e], rowk(dOs + ih * KH, LD), 16 * mt, rowk(Bs + ih * KH, LD), 16 * nt);
-      // dB_state for the value columns of this half: (e^{g_n-g} K) dW^T
-      const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * mt, colk(dWh, LDR), 16 * nt);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(16 * mt, r);
-        db1[t * D + ih * KH + acc_col(16 * nt)] = __expf(gn - gs[t]) * acc[r];
-      }
+      mqa[e] = mma_k<E, KH>(mqa[e], rowk(Rs + ih * KH, LD), 16 * nt, rowk(dOs + ih * KH, LD), 16 * mt);
+      mqk[e] = mma_k<E, KH>(mqk[e], rowk(Bs + ih * KH, LD), 16 * nt, rowk(dOs + ih * KH, LD), 16 * mt);
+      // dB_state for the value columns of this block: (e^{g_n-g} K) dW^T, held transposed
+      const f32x4 acc = mma_k<E, D>(zero4(), rowk(dWh, LD), 16 * nt, rowk(Ks, LD), 16 * mt);
+      const int t = 16 * mt + lrow();
+      put4(db1 + t * D + ih * KH + 16 * nt + 4 * lgrp(), __expf(gn - gs[t]) * acc);
     }
-    for (int idx = threadIdx.x; idx < D * KH; idx += NT) {
-      const int j = idx / KH, i = idx % KH;
-      gam += (float)Wh[j * LDR + i] * (float)dWh[j * LDR + i];
+    {  // <W0, dW> over this block, 16 bytes at a time
+      constexpr int VE = 16 / (int)sizeof(E);
+      for (int idx = threadIdx.x; idx < KH * D / VE; idx += NT) {
+        const int i = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
+        const uint4 a = *reinterpret_cast<const uint4*>(Wh + i * LD + j0);
+        const uint4 c = *reinterpret_cast<const uint4*>(dWh + i * LD + j0);
+        const E* ae = reinterpret_cast<const E*>(&a);
+        const E* ce = reinterpret_cast<const E*>(&c);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) gam += (float)ae[e] * (float)ce[e];
+      }
     }
   }
   float* dq1 = p.g2_dq + u * CH * D;
   float* dx = p.g2_dx + u * CH * D;
+  {
+    const float f = (w < 4) ? geo.scale * __expf(gs[tr]) : -1.f;
+    float* dst = (w < 4 ? dq1 : dx) + tr * D + 4 * lgrp();
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * wm, r), j = acc_col(16 * nt);
-      if (w < 4) dq1[t * D + j] = geo.scale * __expf(gs[t]) * acc1[nt][r];
-      else dx[t * D + j] = -acc1[nt][r];
-    }
+    for (int nt = 0; nt < D / 16; ++nt) put4(dst + 16 * nt, f * acc1[nt]);
+  }
   {
     float* dk1 = p.g2_dk + u * CH * D;
     float* da1 = p.g2_da + u * CH * D;
-    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pa[4] = {0.f, 0.f, 0.f, 0.f};
+    const float dec = __expf(gn - gs[tr]);
+    float pk = 0.f, pa = 0.f;
 #pragma unroll
-    for (int qq = 0; qq < NQ; ++qq)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(16 * wm, r), j = acc_col(16 * (wn * NQ + qq));
-        const float dec = __expf(gn - gs[t]);
-        const float xk = dec * dkb[qq][r], xa = dec * dab[qq][r];
-        dk1[t * D + j] = xk;
-        da1[t * D + j] = xa;
-        pk[r] += (float)Ks[t * LD + j] * xk;
-        pa[r] += (float)As[t * LD + j] * xa;
-      }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float a = sum16(pk[r]), b = sum16(pa[r]);
-      if (lrow() == 0) {
-        rkb[w][acc_row(16 * wm, r)] = a;
-        rab[w][acc_row(16 * wm, r)] = b;
-      }
+    for (int qq = 0; qq < NQ; ++qq) {
+      const int j0 = 16 * (wn * NQ + qq) + 4 * lgrp();
+      const f32x4 xk = dec * dkb[qq], xa = dec * dab[qq];
+      put4(dk1 + tr * D + j0, xk);
+      put4(da1 + tr * D + j0, xa);
+      const f32x4 kk = get4(Ks + tr * LD + j0), aa = get4(As + tr * LD + j0);
+      pk += kk[0] * xk[0] + kk[1] * xk[1] + kk[2] * xk[2] + kk[3] * xk[3];
+      pa += aa[0] * xa[0] + aa[1] * xa[1] + aa[2] * xa[2] + aa[3] * xa[3];
+    }
+    pk += __shfl_xor(pk, 16, 64);
+    pk += __shfl_xor(pk, 32, 64);
+    pa += __shfl_xor(pa, 16, 64);
+    pa += __shfl_xor(pa, 32, 64);
+    if (lgrp() == 0) {
+      rkb[w][tr] = pk;
+      rab[w][tr] = pa;
     }
   }
   float* dmqa = p.g2_dmqa + u * CH * CH;
@@ -316,13 +330,16 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+    const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
+    f32x4 xa, xk;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s2 = acc_col(16 * nt);
-      const bool keep = s2 <= t;
-      dmqa[t * CH + s2] = keep ? geo.scale * mqa[e][r] : 0.f;
-      dmqk[t * CH + s2] = keep ? geo.scale * mqk[e][r] : 0.f;
+      const bool keep = s0 + r <= t;
+      xa[r] = keep ? geo.scale * mqa[e][r] : 0.f;
+      xk[r] = keep ? geo.scale * mqk[e][r] : 0.f;
     }
+    put4(dmqa + t * CH + s0, xa);
+    put4(dmqk + t * CH + s0, xk);
   }
   gam = wave_sum(gam);
   if (lane_id() == 0) red[w] = gam;
