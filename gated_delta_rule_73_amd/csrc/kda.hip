@@ -430,7 +430,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   using Ly = KdaWyLds<E, D>;
   constexpr int NT = 256, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ float bs[CH], dbs[CH], tot[4 * D];
+  __shared__ __align__(16) float bs[CH], tot[4 * D];
+  __shared__ float partc[4][CH], partr[4][CH];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
   float* Ls = reinterpret_cast<float*>(smem + Ly::oL);
@@ -456,17 +457,22 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   if (threadIdx.x < CH) bs[threadIdx.x] = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
   rk.store(Ks, LD);
   kda_cumlog<E, D, NT>(ra, n, Gs, LDG, tot);
-  for (int idx = threadIdx.x; idx < CH * D; idx += NT) {
-    const int t = idx / D, j = idx % D;
-    Ks[t * LD + j] = (E)((float)Ks[t * LD + j] * __expf(Gs[t * LDG + j]));
+  {  // Khat = e^g K in place, 16 bytes at a time
+    constexpr int VE = 16 / (int)sizeof(E);
+    for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
+      const int t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
+      uint4 kv = *reinterpret_cast<const uint4*>(Ks + t * LD + j0);
+      E* ke = reinterpret_cast<E*>(&kv);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) ke[e] = (E)((float)ke[e] * __expf(Gs[t * LDG + j0 + e]));
+      *reinterpret_cast<uint4*>(Ks + t * LD + j0) = kv;
+    }
   }
+  static_assert(decltype(rdx)::VE == 4, "four floats per vector");
 #pragma unroll
   for (int it = 0; it < decltype(rdx)::IT; ++it) {
-    if (decltype(rdx)::TOTAL % NT == 0 || threadIdx.x + it * NT < decltype(rdx)::TOTAL) {
-      const int t = rdx.row(it), j = rdx.col(it);
-#pragma unroll
-      for (int x = 0; x < decltype(rdx)::VE; ++x) dXs[t * LD + j + x] = (E)rdx.elem(it, x);
-    }
+    if (decltype(rdx)::TOTAL % NT == 0 || threadIdx.x + it * NT < decltype(rdx)::TOTAL)
+      put4(dXs + rdx.row(it) * LD + rdx.col(it), f32x4{rdx.elem(it, 0), rdx.elem(it, 1), rdx.elem(it, 2), rdx.elem(it, 3)});
   }
   raf.store(Af, LF);
   __syncthreads();  // G is free from here on
@@ -478,81 +484,77 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   rv.store(Vs, LD);
   rdr.store(dRs, LD);
   __syncthreads();
+  // dT^T tiles (columns s, rows t), four consecutive columns per lane
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
-    const f32x4 a = mma_k<E, D>(zero4(), rowk(dRs, LD), 16 * mt, rowk(Vs, LD), 16 * nt);
-    const f32x4 b = mma_k<E, D>(zero4(), rowk(dXs, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
+    const f32x4 a = mma_k<E, D>(zero4(), rowk(Vs, LD), 16 * nt, rowk(dRs, LD), 16 * mt);
+    const f32x4 bb = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * nt, rowk(dXs, LD), 16 * mt);
+    const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
+    f32x4 x;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
-      dTs[t * LF + s] = (s <= t) ? a[r] + b[r] : 0.f;
-    }
+    for (int r = 0; r < 4; ++r) x[r] = (s0 + r <= t) ? a[r] + bb[r] : 0.f;
+    put4(dTs + t * LF + s0, x);
   }
   const TtView Tt{Li, LF, bs};
   f32x4 dva[D / 16];
-  {
-    float* dkh = p.kd_dkh + u * CH * D;
+  {  // dV^T and dKhat^T (columns j, rows t)
+    float* dkh = p.kd_dkh + u * CH * D + (16 * w + lrow()) * D + 4 * lgrp();
 #pragma unroll
     for (int nt = 0; nt < D / 16; ++nt) {
-      dva[nt] = mma_k<E, CH>(zero4(), Tt, 16 * w, colk(dRs, LD), 16 * nt);
-      const f32x4 kh = mma_k<E, CH>(zero4(), Tt, 16 * w, colk(dXs, LD), 16 * nt);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dkh[acc_row(16 * w, r) * D + acc_col(16 * nt)] = kh[r];
+      dva[nt] = mma_k<E, CH>(zero4(), colk(dRs, LD), 16 * nt, Tt, 16 * w);
+      put4(dkh + 16 * nt, mma_k<E, CH>(zero4(), colk(dXs, LD), 16 * nt, Tt, 16 * w));
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) store4_n(Vs, LD, 16 * w, 16 * nt, dva[nt]);
-  if (threadIdx.x < CH) {  // dbeta from T = Linv diag(beta)
-    const int s = threadIdx.x;
+  for (int nt = 0; nt < D / 16; ++nt) store4_t(Vs, LD, 16 * nt, 16 * w, dva[nt]);
+  {  // dbeta from T = Linv diag(beta): column sums, four threads per column
+    const int s = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
-#pragma unroll 16
-    for (int t = 0; t < CH; ++t) a += dTs[t * LF + s] * Li[t * LF + s];
-    dbs[s] = a;
+#pragma unroll
+    for (int t = pt; t < CH; t += NT / CH) a += dTs[t * LF + s] * Li[t * LF + s];
+    partc[pt][s] = a;
   }
   __syncthreads();
   s2g_rows<E, CH, D, NT>(dv + tk * D, D, Vs, LD, n);
-  for (int idx = threadIdx.x; idx < CH * CH; idx += NT) {
-    const int t = idx >> 6, s = idx & 63;
-    dTs[t * LF + s] *= bs[s];  // gradient w.r.t. Linv
-  }
-  __syncthreads();
+  // the gradient w.r.t. Linv is dT diag(beta): Pt = (dT diag(beta)) Linv^T
   float* Pt = Ls;  // L is no longer needed
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
-    const f32x4 acc = mma_k<E, CH>(zero4(), rowk(dTs, LF), 16 * mt, rowk(Li, LF), 16 * nt);
+    const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * mt, rowk(Li, LF), 16 * nt);
     store4_t(Pt, LF, 16 * mt, 16 * nt, acc);
   }
   __syncthreads();
-  f32x4 dl[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
-    const f32x4 acc = mma_k<E, CH>(zero4(), colk(Li, LF), 16 * mt, rowk(Pt, LF), 16 * nt);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dl[e][r] = (acc_col(16 * nt) < acc_row(16 * mt, r)) ? -acc[r] : 0.f;
-  }
-  __syncthreads();
+  // dL (strictly lower), transposed: dT is no longer read, so dL overwrites it in place
   float* da = p.kd_da + u * CH * CH;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
-    store4_n(dTs, LF, 16 * mt, 16 * nt, dl[e]);  // dTs now holds dL
+    const f32x4 acc = mma_k<E, CH>(zero4(), rowk(Pt, LF), 16 * nt, colk(Li, LF), 16 * mt);
+    const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
+    f32x4 dl;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r);
-      da[t * CH + acc_col(16 * nt)] = bs[t] * dl[e][r];
-    }
+    for (int r = 0; r < 4; ++r) dl[r] = (s0 + r < t) ? -acc[r] : 0.f;
+    put4(dTs + t * LF + s0, dl);
+    put4(da + t * CH + s0, bs[t] * dl);
   }
   __syncthreads();
-  if (threadIdx.x < CH) {  // dbeta from L = I + diag(beta) A
-    const int t = threadIdx.x;
+  {  // dbeta from L = I + diag(beta) A: row sums, four threads per row
+    const int t = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
-#pragma unroll 16
-    for (int s = 0; s < CH; ++s) a += dTs[t * LF + s] * Af[t * LF + s];
-    if (t < n) dbeta[tk + t] = (E)(dbs[t] + a);
+#pragma unroll
+    for (int s = pt; s < CH; s += NT / CH) a += dTs[t * LF + s] * Af[t * LF + s];
+    partr[pt][t] = a;
+  }
+  __syncthreads();
+  if (threadIdx.x < CH) {
+    const int t = threadIdx.x;
+    float db = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / CH; ++i) db += partc[i][t] + partr[i][t];
+    if (t < n) dbeta[tk + t] = (E)db;
   }
 }
 
