@@ -851,7 +851,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
   float pa_[NC], pc_[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int j = acc_col(16 * c), jg = j0 + j;
+    const int j = acc_col(16 * c);
     const float gn = Gs[(CH - 1) * LDF + j];
     float sa = 0.f, sc = 0.f;
 #pragma unroll
@@ -865,10 +865,10 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
         dkv += S1[uu * LDF + j];
         dqv += S2[uu * LDF + j];
       }
-      if (uu < n) {
-        dk[(tk + uu) * D + jg] = (E)dkv;
-        dq[(tk + uu) * D + jg] = (E)dqv;
-      }
+      // dk, dq replace this lane's own elements of K and Q (read just above; rows of block b
+      // are read by this wave only) and go out as whole rows below
+      Ks[uu * LDJ + j] = (E)dkv;
+      Qs[uu * LDJ + j] = (E)dqv;
       const float a = qv * xq + kv * xk, cc = kv * xb;
       y2[c][r] += a;
       x3[c][r] += cc;
@@ -883,6 +883,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
     pc_[c] = sc;
   }
   __syncthreads();
+  s2g_rows<E, CH, JW, NT>(dk + tk * D + j0, D, Ks, LDJ, n);
+  s2g_rows<E, CH, JW, NT>(dq + tk * D + j0, D, Qs, LDJ, n);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     store4_n(S1, LDF, 16 * b, 16 * c, y2[c]);
