@@ -186,12 +186,16 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
       }
     }
     if constexpr (G2) {
+      using RE = decltype(p.e);
 #pragma unroll
-      for (int it = 0; it < decltype(p.e)::IT; ++it) {
+      for (int it = 0; it < RE::IT; ++it) {  // one vector store per register vector
         const int t = p.e.row(it), j0 = p.e.col(it);
+        const float bt = bsh[t];
+        typename RE::V av;
+        E* ae = reinterpret_cast<E*>(&av);
 #pragma unroll
-        for (int x = 0; x < decltype(p.e)::VE; ++x)
-          As[t * LD + j0 + x] = (E)(bsh[t] * (float)p.e.elem(it, x) * (float)p.k.elem(it, x));
+        for (int x = 0; x < RE::VE; ++x) ae[x] = (E)(bt * (float)p.e.elem(it, x) * (float)p.k.elem(it, x));
+        *reinterpret_cast<typename RE::V*>(As + t * LD + j0) = av;
       }
     }
     if (snap) s2g_full<E, BV, D, NT>(dHs + u * D * D + (long)i0 * D, D, dWs, LD);

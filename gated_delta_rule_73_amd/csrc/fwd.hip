@@ -309,24 +309,32 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     if constexpr (G2) {
       // a = beta e*k (row-major) and e^{g_n-g_t} b_t = e^{g_n-g_t} beta_t w_t*v_t (transposed)
       const float gn0 = gs[CH - 1];
+      using RE = decltype(p.e);
+      using RV = decltype(p.vt);
 #pragma unroll
-      for (int it = 0; it < decltype(p.e)::IT; ++it) {
+      for (int it = 0; it < RE::IT; ++it) {  // one vector store per register vector
         const int t = p.e.row(it), j0 = p.e.col(it);
+        const float bt = bsh[t];
+        typename RE::V av;
+        E* ae = reinterpret_cast<E*>(&av);
 #pragma unroll
-        for (int x = 0; x < decltype(p.e)::VE; ++x)
-          As[t * LD + j0 + x] = (E)(bsh[t] * (float)p.e.elem(it, x) * (float)p.k.elem(it, x));
+        for (int x = 0; x < RE::VE; ++x) ae[x] = (E)(bt * (float)p.e.elem(it, x) * (float)p.k.elem(it, x));
+        *reinterpret_cast<typename RE::V*>(As + t * LD + j0) = av;
       }
 #pragma unroll
-      for (int it = 0; it < decltype(p.vt)::IT; ++it) {
+      for (int it = 0; it < RV::IT; ++it) {
         const int t = p.vt.row(it), i = p.vt.col(it);
         const float bt = virt ? 0.f : bsh[t];
         const float sc = bt * __expf(gn0 - gs[t]);
+        typename RV::V bnv;
+        E* bn = reinterpret_cast<E*>(&bnv);
 #pragma unroll
-        for (int x = 0; x < decltype(p.vt)::VE; ++x) {
+        for (int x = 0; x < RV::VE; ++x) {
           const float bv = (float)p.wt.elem(it, x) * (float)p.vt.elem(it, x);
           Bd[(i + x) * LDR + t] = (E)(sc * bv);
-          if constexpr (FULL) Bn[t * LDV + i + x] = (E)(bt * bv);
+          bn[x] = (E)(bt * bv);
         }
+        if constexpr (FULL) *reinterpret_cast<typename RV::V*>(Bn + t * LDV + i) = bnv;
       }
     }
     load(p, c + 2, 0);
