@@ -8,9 +8,10 @@
 //   R = U - X W0^T                                  (row t: beta_t times the residual r_t)
 //   O = scale * ((e^g * Q) W0^T + M R)
 //   W_next = e^{g_n} W0 + R^T (e^{g_n - g} * K)
-// Three launches: a chunk-parallel prep (A, M, L^{-1}, X, U), a sequential scan over the
-// chunks of each (sequence, head, value-row tile) that carries W in float32 registers and
-// records W0 and R per chunk, and a chunk-parallel output kernel.
+// Two launches: a chunk-parallel prep (A, M, L^{-1}, X, U) and a sequential scan over the
+// chunks of each (sequence, head, value-row tile) that carries W in float32 registers, records
+// W0 and R per chunk and writes the tile's output columns (segmented scans add a map pass and
+// a combine, see seg.hip).
 #include "chunk.hpp"
 #include "launch.hpp"
 

@@ -9,8 +9,8 @@
 //   R' = U'' - X' W0^T                  (R' = -Y: minus the memory's predictions W'_t k_t)
 //   O  = scale ((e^g * Q) W0^T + M_qa R' + M_qk B)
 //   W_next = e^{g_n} W0 + R'^T (e^{g_n-g} * A) + B^T (e^{g_n-g} * K)
-// The scan and output kernels are shared with the delta family (fwd.hip); this file holds the
-// prep kernel and the three backward stages.
+// The scans (which also write the output) are shared with the delta family (fwd.hip, bwd.hip);
+// this file holds the prep kernel and the three backward stages.
 #include "chunk.hpp"
 #include "launch.hpp"
 

@@ -13,7 +13,7 @@
 // which keeps the factors in range unless the block's decay is stronger than e^{-60} in some
 // channel -- those (rare) diagonal blocks are summed exactly, one exponential per term.
 //
-// The forward scan and output kernels are the delta family's (fwd.hip) fed with
+// The forward scan (which also writes the output) is the delta family's (fwd.hip) fed with
 // Kbar = e^{g_n - g} * K and Qhat = e^g * Q from the prep kernel and a per-row decay of the
 // carried memory.  The backward is the reverse scan (bwd.hip) and three chunk stages here.
 #include "chunk.hpp"
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   kda_cumlog<E, D, NT>(ra, n, Gs, LDG, tot);
   kda_flags<D, NT>(Gs, LDG, unsafe);
 
-  // Kbar and Qhat for the scans and the output kernel, e^{g_n} per channel, and the row
+  // Kbar and Qhat for the scans, e^{g_n} per channel, and the row
   // operands of the Grams (Q's buffer is overwritten in place by Qr).
   E* kb = Kbo + u * CH * D;
   E* qh = Qho + u * CH * D;
