@@ -282,7 +282,12 @@ struct BwdLds {
   static constexpr int oPt = TK >= F ? odX : endVP;
   static constexpr int endP2 = TK >= F ? endVP : endVP + F;
   static constexpr int oQ = oLi, oPair = oVP, oAt = odR, oMt = odR + SQ;
-  static constexpr int BIG = endP1 > endP2 ? endP1 : endP2;
+  // bfloat16 copies of L^{-1} and T = L^{-1} diag(beta) as matrix-core operands (the float32
+  // path reads L^{-1} directly)
+  static constexpr bool BCOPY = !std::is_same<E, float>::value;
+  static constexpr int BIG0 = endP1 > endP2 ? endP1 : endP2;
+  static constexpr int oLb = BIG0, oTb = BIG0 + SQ;
+  static constexpr int BIG = BIG0 + (BCOPY ? 2 * SQ : 0);
   static_assert(TK <= F, "Q must fit the region of Linv");
   static_assert(2 * SQ <= 2 * TK, "Gram operand buffers must fit the dR/dX regions");
 };
@@ -455,6 +460,23 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   pV.store(Vs, LD);
   pA.store(As, LF);  // A and L^{-1} as the forward computed them
   pLi.store(Li, LF);
+  E* Lb = reinterpret_cast<E*>(smem + Ly::oLb);
+  E* Tb = reinterpret_cast<E*>(smem + Ly::oTb);
+  if constexpr (Ly::BCOPY) {  // from the registers: L^{-1} and L^{-1} diag(beta) in bfloat16
+    using RL = decltype(pLi);
+    static_assert(RL::VE == 4, "four floats per vector");
+#pragma unroll
+    for (int it = 0; it < RL::IT; ++it) {
+      const int t = pLi.row(it), s0 = pLi.col(it);
+      const f32x4 l = {pLi.elem(it, 0), pLi.elem(it, 1), pLi.elem(it, 2), pLi.elem(it, 3)};
+      const float4 b4 = *reinterpret_cast<const float4*>(bs + s0);
+      put4(Lb + t * LDR + s0, l);
+      put4(Tb + t * LDR + s0, l * f32x4{b4.x, b4.y, b4.z, b4.w});
+    }
+  }
+  // operand views of L^{-1} (rows t, columns s) and of T^T
+  const auto LiRow = [&]() { if constexpr (Ly::BCOPY) return rowk(Lb, LDR); else return rowk(Li, LF); }();
+  const auto LiCol = [&]() { if constexpr (Ly::BCOPY) return colk(Lb, LDR); else return colk(Li, LF); }();
   __syncthreads();
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -471,7 +493,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
   }
   // dV = T^T dR and dKhat = T^T dX with T = Linv diag(beta)
-  const TtView Tt{Li, LF, bs};
+  const auto Tt = [&]() { if constexpr (Ly::BCOPY) return colk(Tb, LDR); else return TtView{Li, LF, bs}; }();
   f32x4 dva[NQ];
   {
     float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -512,7 +534,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
-    const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * mt, rowk(Li, LF), 16 * nt);
+    const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * mt, LiRow, 16 * nt);
     store4_t(Pt, LF, 16 * mt, 16 * nt, acc);
   }
   __syncthreads();
@@ -520,7 +542,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
-    const f32x4 acc = mma_k<E, CH>(zero4(), colk(Li, LF), 16 * mt, rowk(Pt, LF), 16 * nt);
+    const f32x4 acc = mma_k<E, CH>(zero4(), LiCol, 16 * mt, rowk(Pt, LF), 16 * nt);
     f32x4 dl;
 #pragma unroll
     for (int r = 0; r < 4; ++r) dl[r] = (acc_col(16 * nt) < acc_row(16 * mt, r)) ? -acc[r] : 0.f;
