@@ -419,7 +419,12 @@ struct KdaWyLds {
   static constexpr int R1 = cmax(GB, 2 * F + 2 * TK);
   static constexpr int oG = 0;
   static constexpr int oLi = 0, odT = F, oV = 2 * F, odR = 2 * F + TK;
-  static constexpr int oK = R1, oL = R1 + TK, oA = oL + F, odX = oA + F, BYTES = odX + TK;
+  static constexpr int oK = R1, oL = R1 + TK, oA = oL + F, odX = oA + F, END = odX + TK;
+  // bfloat16 copies of L^{-1} and T = L^{-1} diag(beta) as matrix-core operands (the float32
+  // path reads L^{-1} directly)
+  static constexpr bool BCOPY = !std::is_same<E, float>::value;
+  static constexpr int LDT = CH + pad16<E>(), SQ = CH * LDT * (int)sizeof(E);
+  static constexpr int oLb = END, oTb = END + SQ, BYTES = END + (BCOPY ? 2 * SQ : 0);
 };
 
 template <typename E, int D>
@@ -483,6 +488,23 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   rli.store(Li, LF);
   rv.store(Vs, LD);
   rdr.store(dRs, LD);
+  constexpr int LDT = Ly::LDT;
+  E* Lb = reinterpret_cast<E*>(smem + Ly::oLb);
+  E* Tb = reinterpret_cast<E*>(smem + Ly::oTb);
+  if constexpr (Ly::BCOPY) {  // from the registers: L^{-1} and L^{-1} diag(beta) in bfloat16
+    using RL = decltype(rli);
+    static_assert(RL::VE == 4, "four floats per vector");
+#pragma unroll
+    for (int it = 0; it < RL::IT; ++it) {
+      const int t = rli.row(it), s0 = rli.col(it);
+      const f32x4 l = {rli.elem(it, 0), rli.elem(it, 1), rli.elem(it, 2), rli.elem(it, 3)};
+      const float4 b4 = *reinterpret_cast<const float4*>(bs + s0);
+      put4(Lb + t * LDT + s0, l);
+      put4(Tb + t * LDT + s0, l * f32x4{b4.x, b4.y, b4.z, b4.w});
+    }
+  }
+  const auto LiRow = [&]() { if constexpr (Ly::BCOPY) return rowk(Lb, LDT); else return rowk(Li, LF); }();
+  const auto LiCol = [&]() { if constexpr (Ly::BCOPY) return colk(Lb, LDT); else return colk(Li, LF); }();
   __syncthreads();
   // dT^T tiles (columns s, rows t), four consecutive columns per lane
 #pragma unroll
@@ -496,7 +518,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
     for (int r = 0; r < 4; ++r) x[r] = (s0 + r <= t) ? a[r] + bb[r] : 0.f;
     put4(dTs + t * LF + s0, x);
   }
-  const TtView Tt{Li, LF, bs};
+  const auto Tt = [&]() { if constexpr (Ly::BCOPY) return colk(Tb, LDT); else return TtView{Li, LF, bs}; }();
   f32x4 dva[D / 16];
   {  // dV^T and dKhat^T (columns j, rows t)
     float* dkh = p.kd_dkh + u * CH * D + (16 * w + lrow()) * D + 4 * lgrp();
@@ -523,7 +545,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
-    const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * mt, rowk(Li, LF), 16 * nt);
+    const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * mt, LiRow, 16 * nt);
     store4_t(Pt, LF, 16 * mt, 16 * nt, acc);
   }
   __syncthreads();
@@ -532,7 +554,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
-    const f32x4 acc = mma_k<E, CH>(zero4(), rowk(Pt, LF), 16 * nt, colk(Li, LF), 16 * mt);
+    const f32x4 acc = mma_k<E, CH>(zero4(), rowk(Pt, LF), 16 * nt, LiCol, 16 * mt);
     const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
     f32x4 dl;
 #pragma unroll
