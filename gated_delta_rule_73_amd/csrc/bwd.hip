@@ -68,8 +68,12 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   __shared__ __align__(16) E Ks[CH * LD];
   __shared__ __align__(16) E Xs[CH * LD];
   __shared__ __align__(16) E Ms[CH * LDR];
-  __shared__ __align__(16) E dOt[BV * LDR];   // scale * dO^T
-  __shared__ __align__(16) E dOg[BV * LDR];   // scale * e^g * dO^T
+  // scale * dO and scale * e^g * dO, row-major, read through transposing reads; for bfloat16,
+  // rows 64 bytes apart keep those reads free of bank conflicts
+  constexpr int LDO = std::is_same<E, float>::value ? BV + 4 : 32;
+  static_assert(LDO >= BV, "a dO row fits");
+  __shared__ __align__(16) E dOt[CH * LDO];
+  __shared__ __align__(16) E dOg[CH * LDO];
   __shared__ __align__(16) E dWs[BV * LD];
   __shared__ __align__(16) E dRt[BV * LDR];   // -dR^T
   __shared__ __align__(16) E dRn[CH * LDV];   // dR
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
 #pragma unroll
       for (int it = 0; it < NI; ++it) store4_t(dWs, LD, 16 * (w + 4 * qq), 16 * it, S[qq][it]);
     __syncthreads();
-    // dO tile, transposed, twice: plain and with e^{g_t} (rows t >= n are zero)
+    // dO tile twice, plain and with e^{g_t} (rows t >= n are zero), one vector store each
     {
       using RT = RegTile<E, CH, BV, NT>;
 #pragma unroll
@@ -176,12 +180,17 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
           const E* e = reinterpret_cast<const E*>(&p.dO.v[it]);
           float eg = 1.f;
           if constexpr (DEC) eg = __expf(gs[t]);
+          typename RT::V pv, gv;
+          E* pe = reinterpret_cast<E*>(&pv);
+          E* ge = reinterpret_cast<E*>(&gv);
 #pragma unroll
           for (int x = 0; x < RT::VE; ++x) {
             const float val = virt ? 0.f : geo.scale * (float)e[x];
-            dOt[(i + x) * LDR + t] = (E)val;
-            dOg[(i + x) * LDR + t] = (E)(val * eg);
+            pe[x] = (E)val;
+            ge[x] = (E)(val * eg);
           }
+          *reinterpret_cast<typename RT::V*>(dOt + t * LDO + i) = pv;
+          *reinterpret_cast<typename RT::V*>(dOg + t * LDO + i) = gv;
         }
       }
     }
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     const float gn = gs[CH - 1];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const f32x4 a1 = mma_k<E, CH>(zero4(), colk(Ms, LDR), 16 * w, rowk(dOt, LDR), 16 * it);
+      const f32x4 a1 = mma_k<E, CH>(zero4(), colk(Ms, LDR), 16 * w, colk(dOt, LDO), 16 * it);
       const f32x4 a2 = mma_k<E, D>(zero4(), rowk(G2 ? As : Ks, LD), 16 * w, rowk(dWs, LD), 16 * it);
       f32x4 dr, ndr;
 #pragma unroll
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
       for (int it = 0; it < NI; ++it) {
         if constexpr (KDA) S[qq][it] *= egk[qq];
         else S[qq][it] *= eg;
-        S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Qs, LD), 16 * (w + 4 * qq), rowk(dOg, LDR), 16 * it);
+        S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Qs, LD), 16 * (w + 4 * qq), colk(dOg, LDO), 16 * it);
         S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Xs, LD), 16 * (w + 4 * qq), rowk(dRt, LDR), 16 * it);
       }
     __syncthreads();
