@@ -195,7 +195,11 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
   __shared__ __align__(16) E Us[CH * LDV];
   __shared__ __align__(16) E Ws[BV * LD];
   __shared__ __align__(16) E Rn[CH * LDV];
-  __shared__ __align__(16) E Rd[BV * LDR];
+  // e^{g_n-g} R, row-major, read through transposing reads by the update; for bfloat16, rows
+  // 64 bytes apart keep those reads free of bank conflicts
+  constexpr int LDD = std::is_same<E, float>::value ? BV + 4 : 32;
+  static_assert(LDD >= BV, "an R row fits");
+  __shared__ __align__(16) E Rd[CH * LDD];
   __shared__ __align__(16) E Qs[FULL ? CH * LD : 8];
   __shared__ __align__(16) E Ms[FULL ? CH * LDR : 8];
   __shared__ __align__(16) E M2s[OUT_G2 ? CH * LDR : 8];
@@ -340,21 +344,17 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     }
     load(p, c + 2, 0);
     const float gn = gs[CH - 1];
+    // R^T = U^T - W X^T: the lane holds chunk row tl and four consecutive value columns
+    const int tl = 16 * w + lrow();
+    float dec = 1.f;
+    if constexpr (DEC) dec = __expf(gn - gs[tl]);
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const f32x4 acc = mma_k<E, D>(zero4(), rowk(Xs, LD), 16 * w, rowk(Ws, LD), 16 * it);
-      f32x4 rv, rd;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(16 * w, r), i = acc_col(16 * it);
-        const float val = (virt ? 0.f : (float)Us[t * LDV + i]) - acc[r];
-        rv[r] = val;
-        float dec = 1.f;
-        if constexpr (DEC) dec = __expf(gn - gs[t]);
-        rd[r] = val * dec;
-      }
-      store4_n(Rn, LDV, 16 * w, 16 * it, rv);
-      store4_t(Rd, LDR, 16 * w, 16 * it, rd);
+      const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ws, LD), 16 * it, rowk(Xs, LD), 16 * w);
+      const int c4 = 16 * it + 4 * lgrp();
+      const f32x4 rv = (virt ? zero4() : get4(Us + tl * LDV + c4)) - acc;
+      put4(Rn + tl * LDV + c4, rv);
+      put4(Rd + tl * LDD + c4, dec * rv);
     }
     if constexpr (FULL) s2g_full<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD);
     __syncthreads();
@@ -365,17 +365,13 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         // O = scale (e^g (Q W0^T) + M R [+ M_qk b]) for this tile's value columns
 #pragma unroll
         for (int it = 0; it < NI; ++it) {
-          const f32x4 a1 = mma_k<E, D>(zero4(), rowk(Qs, LD), 16 * w, rowk(Ws, LD), 16 * it);
-          f32x4 a2 = mma_k<E, CH>(zero4(), rowk(Ms, LDR), 16 * w, colk(Rn, LDV), 16 * it);
-          if constexpr (G2) a2 = mma_k<E, CH>(a2, rowk(M2s, LDR), 16 * w, colk(Bn, LDV), 16 * it);
-          f32x4 ov;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float e = 1.f;
-            if constexpr (DEC) e = __expf(gs[acc_row(16 * w, r)]);
-            ov[r] = geo.scale * (e * a1[r] + a2[r]);
-          }
-          store4_n(Os, LDV, 16 * w, 16 * it, ov);
+          // O^T = W (e^g Q)^T + R^T M^T (+ b^T M_qk^T), four consecutive columns per lane
+          const f32x4 a1 = mma_k<E, D>(zero4(), rowk(Ws, LD), 16 * it, rowk(Qs, LD), 16 * w);
+          f32x4 a2 = mma_k<E, CH>(zero4(), colk(Rn, LDV), 16 * it, rowk(Ms, LDR), 16 * w);
+          if constexpr (G2) a2 = mma_k<E, CH>(a2, colk(Bn, LDV), 16 * it, rowk(M2s, LDR), 16 * w);
+          float e = 1.f;
+          if constexpr (DEC) e = __expf(gs[tl]);
+          put4(Os + tl * LDV + 16 * it + 4 * lgrp(), geo.scale * (e * a1 + a2));
         }
       }
     }
@@ -390,10 +386,10 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         else S[qq][it] *= eg;
         if constexpr (G2) {
           // W_next = e^{g_n} W0 + R'^T (e^{g_n-g} a) + b^T (e^{g_n-g} k)
-          S[qq][it] = mma_k<E, CH>(S[qq][it], colk(As, LD), 16 * (w + 4 * qq), rowk(Rd, LDR), 16 * it);
+          S[qq][it] = mma_k<E, CH>(S[qq][it], colk(As, LD), 16 * (w + 4 * qq), colk(Rd, LDD), 16 * it);
           S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Ks, LD), 16 * (w + 4 * qq), rowk(Bd, LDR), 16 * it);
         } else {
-          S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Ks, LD), 16 * (w + 4 * qq), rowk(Rd, LDR), 16 * it);
+          S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Ks, LD), 16 * (w + 4 * qq), colk(Rd, LDD), 16 * it);
         }
       }
     __syncthreads();
