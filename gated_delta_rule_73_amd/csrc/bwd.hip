@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   __shared__ __align__(16) E dOt[CH * LDO];
   __shared__ __align__(16) E dOg[CH * LDO];
   __shared__ __align__(16) E dWs[BV * LD];
-  __shared__ __align__(16) E dRt[BV * LDR];   // -dR^T
+  __shared__ __align__(16) E dRt[CH * LDO];   // -dR, row-major, read like dO
   __shared__ __align__(16) E dRn[CH * LDV];   // dR
   __shared__ float gs[CH];
 
@@ -211,20 +211,18 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     __syncthreads();
     load(p, c - 2, 0);
     const float gn = gs[CH - 1];
+    // dR^T: the lane holds chunk row tl and four consecutive value columns
+    const int tl = 16 * w + lrow();
+    float dec = 1.f;
+    if constexpr (DEC) dec = __expf(gn - gs[tl]);
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const f32x4 a1 = mma_k<E, CH>(zero4(), colk(Ms, LDR), 16 * w, colk(dOt, LDO), 16 * it);
-      const f32x4 a2 = mma_k<E, D>(zero4(), rowk(G2 ? As : Ks, LD), 16 * w, rowk(dWs, LD), 16 * it);
-      f32x4 dr, ndr;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float dec = 1.f;
-        if constexpr (DEC) dec = __expf(gn - gs[acc_row(16 * w, r)]);
-        dr[r] = a1[r] + dec * a2[r];
-        ndr[r] = -dr[r];
-      }
-      store4_t(dRt, LDR, 16 * w, 16 * it, ndr);
-      store4_n(dRn, LDV, 16 * w, 16 * it, dr);
+      const f32x4 a1 = mma_k<E, CH>(zero4(), colk(dOt, LDO), 16 * it, colk(Ms, LDR), 16 * w);
+      const f32x4 a2 = mma_k<E, D>(zero4(), rowk(dWs, LD), 16 * it, rowk(G2 ? As : Ks, LD), 16 * w);
+      const f32x4 dr = a1 + dec * a2;
+      const int c4 = 16 * it + 4 * lgrp();
+      put4(dRt + tl * LDO + c4, -dr);
+      put4(dRn + tl * LDV + c4, dr);
     }
     __syncthreads();
     if (snap) s2g_full<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV);
@@ -238,7 +236,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
         if constexpr (KDA) S[qq][it] *= egk[qq];
         else S[qq][it] *= eg;
         S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Qs, LD), 16 * (w + 4 * qq), colk(dOg, LDO), 16 * it);
-        S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Xs, LD), 16 * (w + 4 * qq), rowk(dRt, LDR), 16 * it);
+        S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Xs, LD), 16 * (w + 4 * qq), colk(dRt, LDO), 16 * it);
       }
     __syncthreads();
   };
