@@ -335,7 +335,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   // ================= phase 1: products with the memory W0 and its gradient dW
   f32x4 acc1[D / 16];  // waves 0-3: row tile wm of dQhat = dO W0; waves 4-7: (dR W0)^T, column
                        // tile wm (stored four columns at a time)
-  f32x4 dka[NQ];       // dk tiles (row tile wm, column tiles wn*NQ + qq)
+  f32x4 dka[NQ];       // dk, held transposed: row t = 16 wm + lrow, four consecutive columns
+                       // of column tiles wn*NQ + qq
   f32x4 acc3[2];       // dM tiles w and w + 8
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc1[i] = zero4();
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       }
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq)
-        dka[qq] = mma_k<E, KH>(dka[qq], rowk(Rs + ih * KH, LD), 16 * wm, colk(dWh, LD), 16 * (wn * NQ + qq));
+        dka[qq] = mma_k<E, KH>(dka[qq], colk(dWh, LD), 16 * (wn * NQ + qq), rowk(Rs + ih * KH, LD), 16 * wm);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int id = w + 8 * e;
@@ -408,15 +409,15 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
   }
   const float gn = gs[CH - 1];
-  // e^{g_t} and e^{g_n - g_t} for the four accumulator rows this lane holds (row tile wm)
-  float egr[4] = {1.f, 1.f, 1.f, 1.f}, egd[4] = {1.f, 1.f, 1.f, 1.f};
+  // e^{g_t} for the four accumulator rows this lane holds (row tile wm), and e^{g_t},
+  // e^{g_n - g_t} for the row of the transposed dk tiles
+  const int tr = 16 * wm + lrow();
+  float egr[4] = {1.f, 1.f, 1.f, 1.f}, egt = 1.f, egdt = 1.f;
   if constexpr (GATED) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float gt = gs[acc_row(16 * wm, r)];
-      egr[r] = expf(gt);
-      egd[r] = expf(gn - gt);
-    }
+    for (int r = 0; r < 4; ++r) egr[r] = expf(gs[acc_row(16 * wm, r)]);
+    egt = expf(gs[tr]);
+    egdt = expf(gn - gs[tr]);
   }
   // dq (first term) stays in acc1 for waves 0-3; dX goes to LDS from waves 4-7
 #pragma unroll
@@ -430,20 +431,16 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   }
   // dk (first term): e^{g_n - g_t} dKbar, and the rows' Kbar . dKbar
   {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float part = 0.f;
 #pragma unroll
-    for (int qq = 0; qq < NQ; ++qq)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(16 * wm, r);
-        dka[qq][r] *= egd[r];
-        part[r] += (float)Ks[t * LD + acc_col(16 * (wn * NQ + qq))] * dka[qq][r];
-      }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float s = sum16(part[r]);
-      if (lrow() == 0) rkb[w][acc_row(16 * wm, r)] = s;
+    for (int qq = 0; qq < NQ; ++qq) {
+      dka[qq] *= egdt;
+      const f32x4 kv = get4(Ks + tr * LD + 16 * (wn * NQ + qq) + 4 * lgrp());
+      part += kv[0] * dka[qq][0] + kv[1] * dka[qq][1] + kv[2] * dka[qq][2] + kv[3] * dka[qq][3];
     }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (lgrp() == 0) rkb[w][tr] = part;
   }
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -503,25 +500,19 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   const auto Tt = [&]() { if constexpr (Ly::BCOPY) return colk(Tb, LDR); else return TtView{Li, LF, bs}; }();
   f32x4 dva[NQ];
   {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    float part = 0.f;
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq) {
       const int nt = wn * NQ + qq;
       dva[qq] = mma_k<E, CH>(zero4(), colk(dRs, LD), 16 * nt, Tt, 16 * wm);  // dV^T
-      f32x4 kh = mma_k<E, CH>(zero4(), Tt, 16 * wm, colk(dXs, LD), 16 * nt);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = acc_row(16 * wm, r);
-        kh[r] *= egr[r];
-        part[r] += (float)Ks[t * LD + acc_col(16 * nt)] * kh[r];
-      }
+      const f32x4 kh = egt * mma_k<E, CH>(zero4(), colk(dXs, LD), 16 * nt, Tt, 16 * wm);  // dKhat^T
+      const f32x4 kv = get4(Ks + tr * LD + 16 * nt + 4 * lgrp());
+      part += kv[0] * kh[0] + kv[1] * kh[1] + kv[2] * kh[2] + kv[3] * kh[3];
       dka[qq] += kh;
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float s = sum16(part[r]);
-      if (lrow() == 0) rkh[w][acc_row(16 * wm, r)] = s;
-    }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (lgrp() == 0) rkh[w][tr] = part;
   }
   __syncthreads();
 #pragma unroll
@@ -640,9 +631,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
   for (int qq = 0; qq < NQ; ++qq) {
     const int nt = wn * NQ + qq;
-    dka[qq] = mma_k<E, CH>(dka[qq], rowk(Ats, LDR), 16 * wm, colk(Ks, LD), 16 * nt);
-    dka[qq] = mma_k<E, CH>(dka[qq], colk(Ats, LDR), 16 * wm, colk(Ks, LD), 16 * nt);
-    dka[qq] = mma_k<E, CH>(dka[qq], colk(Mts, LDR), 16 * wm, colk(Qs, LD), 16 * nt);
+    dka[qq] = mma_k<E, CH>(dka[qq], colk(Ks, LD), 16 * nt, rowk(Ats, LDR), 16 * wm);
+    dka[qq] = mma_k<E, CH>(dka[qq], colk(Ks, LD), 16 * nt, colk(Ats, LDR), 16 * wm);
+    dka[qq] = mma_k<E, CH>(dka[qq], colk(Qs, LD), 16 * nt, colk(Mts, LDR), 16 * wm);
   }
   if constexpr (GATED) {  // prefix sums along each row of the pair terms: lanes over columns
     for (int uu = w; uu < CH; uu += NT / 64) {
@@ -669,7 +660,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     for (int nt = 0; nt < D / 16; ++nt) store4_n(sq, LD, 16 * wm, 16 * nt, acc1[nt]);
   }
 #pragma unroll
-  for (int qq = 0; qq < NQ; ++qq) store4_n(sk, LD, 16 * wm, 16 * (wn * NQ + qq), dka[qq]);
+  for (int qq = 0; qq < NQ; ++qq) store4_t(sk, LD, 16 * (wn * NQ + qq), 16 * wm, dka[qq]);
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
     if constexpr (GATED) {
@@ -677,8 +668,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
       for (int i = 0; i < NT / CH; ++i) rect += part8[i][t];
       // suffix over u >= t of the rows' Qhat.dQhat + Khat.dKhat (reversed inclusive scan)
-      const int tr = CH - 1 - t;
-      const float xr = rq[tr >> 4][tr] + rkh[tr >> 4][tr] + rkh[(tr >> 4) + 4][tr];
+      const int tq = CH - 1 - t;
+      const float xr = rq[tq >> 4][tq] + rkh[tq >> 4][tq] + rkh[(tq >> 4) + 4][tq];
       const float suf_r = wave_incl_scan(xr);
       const float suf = __shfl(suf_r, CH - 1 - t, 64);
       // prefix over s < t of Kbar.dKbar (exclusive scan)
