@@ -163,9 +163,93 @@ class Runner:
                                    self.ws.numel(), self.stream)
         self.bd._check(self.lib, st)
 
+    calls = property(lambda self: (self.fwd, self.bwd))
+
     def step(self):
         self.fwd()
         self.bwd()
+
+
+class DecodeRunner:
+    """Device buffers of a decoding workload; one step = one gdr_decode call (every sequence's
+    new tokens through its memory, updated in place)."""
+
+    def __init__(self, w, inp):
+        import torch
+
+        from gated_delta_rule_73_amd import binding as bd
+        from tests._helpers import gpu_inputs
+        self.bd = bd
+        self.lib = bd.load_library()
+        g = gpu_inputs(inp, w.dtype)
+        self.p, self.keep = bd.make_problem(g["q"], g["v"], variant=w.variant, cu_seqlens=inp.get("cu_seqlens"))
+        self.state = g["h0"]
+        self.o = torch.empty_like(g["v"])
+        self.g = g
+        self.ins = bd._inputs(*(g[n] for n in ("q", "k", "v", "beta", "alpha", "erase", "write")), None)
+        self.stream = torch.cuda.current_stream().cuda_stream
+
+    def dec(self):
+        st = self.lib.gdr_decode(ctypes.byref(self.p), ctypes.byref(self.ins), self.state.data_ptr(),
+                                 self.o.data_ptr(), self.stream)
+        self.bd._check(self.lib, st)
+
+    calls = property(lambda self: (self.dec,))
+
+    def step(self):
+        self.dec()
+
+
+def decode_bytes(w, esz: int) -> int:
+    """Bytes one decoding step must move: every float32 memory read and written once, plus the
+    new tokens' q, k, v, gates and o."""
+    N = w.n_states
+    state = 2 * N * w.H * w.dv * w.dk * 4
+    per_tok = (2 * w.dk + w.dv + w.dv) * esz + (esz if w.has_beta else 0)
+    per_tok += {"deltanet": 0, "gated": esz, "kda": w.dk * esz, "gdn2": esz + (w.dk + w.dv) * esz}[w.variant]
+    return state + w.B * w.H * w.T * per_tok
+
+
+def bench_decode(args, w):
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import synth
+    from oracle import recurrence as R
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w)
+    runner = DecodeRunner(w, inp)
+    print("[bench] timing", file=sys.stderr, flush=True)
+    ms, per_kernel = timed(runner, args.steps, args.warmup)
+    esz = 2 if w.dtype == "bf16" else 4
+    nbytes = decode_bytes(w, esz)
+    avg_ms = sum(per_kernel["decode"]) / len(per_kernel["decode"])
+    achieved = nbytes / (avg_ms / 1e3) / 1e9
+    tokens = w.B * w.T
+    out = {
+        "metric": "tokens/s recurrent decode step (gdr_decode), H=16 d=128; % of HBM roofline",
+        "value": round(tokens / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded; distributions of the workload definition)",
+        "config": {"workload": w.name, "variant": w.variant, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk,
+                   "d_v": w.dv, "state": "float32, updated in place"},
+        "roofline": {"bound": "hbm", "kernel": "decode", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode", w.name),
+                     "avg_launch_ms": round(avg_ms, 4), "launches": len(per_kernel["decode"]),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the CPU", file=sys.stderr, flush=True)
+        kw = {n: inp[n] for n in ("q", "k", "v", "beta", "alpha", "erase", "write")}
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            R.forward(**kw, h0=inp["h0"], variant=w.variant)
+            wall = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(tokens / wall, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the whole step ({w.B} sequences x {w.H} heads, {w.T} token each), "
+                                         f"float64 numpy, one thread; {wall:.2f} s"}
+    print(json.dumps(out))
 
 
 def make_events(n):
@@ -192,7 +276,7 @@ def timed(runner, steps: int, warmup: int, trace: bool = True):
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        for j, call in enumerate((runner.fwd, runner.bwd)):
+        for j, call in enumerate(runner.calls):
             if trace:
                 off = (2 * i + j) * 2 * per_call
                 runner.lib.gdr_trace_launches(ctypes.cast(ctypes.byref(handles, off * ctypes.sizeof(ctypes.c_void_p)),
@@ -230,6 +314,9 @@ def main():
 
     import synth
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload in synth.DECODE_WORKLOADS:
+        bench_decode(args, synth.DECODE_WORKLOADS[args.workload])
+        return
     w = synth.WORKLOADS.get(args.workload) or {s.name: s for s in synth.SWEEP}[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(w)

@@ -61,7 +61,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_forward.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.gdr_backward.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, P(GdrGrads), _vp,
                                  ctypes.c_size_t, _vp]
-    for f in ("gdr_workspace_size", "gdr_saved_size", "gdr_forward", "gdr_backward"):
+    lib.gdr_decode.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp]
+    for f in ("gdr_workspace_size", "gdr_saved_size", "gdr_forward", "gdr_backward", "gdr_decode"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -178,3 +179,19 @@ def gdr_backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None
     _check(lib, st)
     del keep
     return out
+
+
+def gdr_decode(q, k, v, beta=None, alpha=None, erase=None, write=None, *, state, variant: str,
+               cu_seqlens=None, scale: float = 1.0, out=None):
+    """Recurrent form (decoding): runs every sequence's tokens in order through its memory.
+    `state` ([N,H,dv,dk] float32) is updated in place; returns o ([B,H,T,dv]).  The call is
+    asynchronous on torch's current stream."""
+    import torch
+    lib = load_library()
+    p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale)
+    o = out if out is not None else torch.empty(q.shape[:3] + (p.dv,), dtype=q.dtype, device=q.device)
+    ins = _inputs(q, k, v, beta, alpha, erase, write, None)
+    st = lib.gdr_decode(ctypes.byref(p), ctypes.byref(ins), _ptr(state), _ptr(o), _stream(q))
+    _check(lib, st)
+    del keep
+    return o

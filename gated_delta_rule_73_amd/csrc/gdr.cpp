@@ -70,8 +70,9 @@ void plan_scans(long long memories, int d, int max_chunks, bool f32, Sizes* s) {
   s->max_seg = lseg ? (max_chunks + lseg - 1) / lseg : 1;
 }
 
-// Checks the problem description and computes the buffer sizes.
-gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
+// Checks the fields every entry point reads (variant, dtype, sizes, scale, packed offsets) and
+// counts the chunks of 64 tokens over all sequences.
+gdr_status check_shape(const gdr_problem* p, long long* total_chunks_out, int* max_chunks_out) {
   if (!p) return fail(GDR_ERR_INVALID_ARG, "problem is NULL");
   if (p->variant < GDR_DELTANET || p->variant > GDR_GDN2)
     return fail(GDR_ERR_INVALID_ARG, "variant %d is not a gdr_variant", p->variant);
@@ -106,6 +107,19 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
     max_chunks = (p->T + gdr::CH - 1) / gdr::CH;
     total_chunks = (long long)p->B * max_chunks;
   }
+  if ((long long)p->B * p->H * (long long)p->T * p->dk > (1LL << 40))
+    return fail(GDR_ERR_UNSUPPORTED, "tensor too large");
+  *total_chunks_out = total_chunks;
+  *max_chunks_out = max_chunks;
+  return GDR_OK;
+}
+
+// Checks the problem description for the chunked entry points and computes the buffer sizes.
+gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
+  long long total_chunks = 0;
+  int max_chunks = 0;
+  const gdr_status st0 = check_shape(p, &total_chunks, &max_chunks);
+  if (st0 != GDR_OK) return st0;
   if (p->chunk != gdr::CH) return fail(GDR_ERR_UNSUPPORTED, "chunk=%d: only 64 is built", p->chunk);
   if (p->dk != p->dv) return fail(GDR_ERR_UNSUPPORTED, "dk=%d != dv=%d is not built", p->dk, p->dv);
   if (p->dtype == GDR_BF16 && p->dk != 64 && p->dk != 128)
@@ -113,8 +127,6 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   if (p->dtype == GDR_F32 && p->dk != 64)
     return fail(GDR_ERR_UNSUPPORTED, "float32 head size %d: only 64 is built", p->dk);
   if (total_chunks > 0x7fffffffLL) return fail(GDR_ERR_UNSUPPORTED, "too many chunks");
-  if ((long long)p->B * p->H * (long long)p->T * p->dk > (1LL << 40))
-    return fail(GDR_ERR_UNSUPPORTED, "tensor too large");
   Sizes s;
   s.total_chunks = (int)total_chunks;
   s.units = total_chunks * p->H;
@@ -331,6 +343,34 @@ gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* 
     if (st != GDR_OK) return st;
   }
   return hip_status(gdr::run_backward(pl, *in, dO, dht, *g, hs), "gdr_backward launch");
+}
+
+gdr_status gdr_decode(const gdr_problem* p, const gdr_inputs* in, float* state, void* o, void* stream) {
+  long long total_chunks = 0;
+  int max_chunks = 0;
+  gdr_status st = check_shape(p, &total_chunks, &max_chunks);
+  if (st != GDR_OK) return st;
+  if (p->dk != p->dv) return fail(GDR_ERR_UNSUPPORTED, "dk=%d != dv=%d is not built", p->dk, p->dv);
+  if (p->dk != 64 && p->dk != 128) return fail(GDR_ERR_UNSUPPORTED, "head size %d: only 64 and 128 are built", p->dk);
+  if ((st = check_inputs(p, in)) != GDR_OK) return st;
+  if (in->h0) return fail(GDR_ERR_INVALID_ARG, "decode takes the memory through state; h0 must be NULL");
+  if (!state) return fail(GDR_ERR_INVALID_ARG, "state is required");
+  if (!o && p->T > 0) return fail(GDR_ERR_INVALID_ARG, "o is required");
+  if (!aligned(state, 16) || (o && !aligned(o, 16)))
+    return fail(GDR_ERR_INVALID_ARG, "state and o must be 16-byte aligned");
+  gdr::Geo g{};
+  g.B = p->B;
+  g.H = p->H;
+  g.T = p->T;
+  g.nseq = p->n_seqs > 0 ? p->n_seqs : p->B;
+  g.varlen = p->n_seqs > 0;
+  g.cu = p->cu_seqlens_dev;
+  g.total_chunks = (int)std::min<long long>(total_chunks, 0x7fffffffLL);
+  g.scale = p->scale;
+  g_last_error.clear();
+  TraceCall tc;
+  return hip_status(gdr::run_decode(g, p->variant, p->dtype, p->dk, *in, state, o, static_cast<hipStream_t>(stream)),
+                    "gdr_decode launch");
 }
 
 const char* gdr_status_string(gdr_status s) {

@@ -85,6 +85,9 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
 
 hipError_t launch_seg_combine(const Plan& p, const ScanSeg& sg, const float* init, bool reverse, hipStream_t st);
 
+// Recurrent form over every sequence's tokens, memory updated in place (decoding).
+hipError_t run_decode(const Geo& g, int variant, int dtype, int D, const gdr_inputs& in, float* state, void* o,
+                      hipStream_t st);
 hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st);
 hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht, const gdr_grads& gr,
                         hipStream_t st);

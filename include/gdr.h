@@ -115,6 +115,26 @@ gdr_status gdr_backward(const gdr_problem *p, const gdr_inputs *in, const void *
                         const float *dht, const void *saved, gdr_grads *g, void *ws,
                         size_t ws_bytes, void *stream);
 
+/* Recurrent (token-by-token) form, for decoding.  The page "Linear Attention Architectures:
+ * Mechanisms, Trade-offs, and Cross-Layer Routing" (section "Declaracion del Problema") gives
+ * linear attention a constant-size memory updated once per token, hence constant inference
+ * work per token; the update is the one of item 1 "Notacion Unificada" written out at the top
+ * of this file.  For every sequence n and head h, the memory
+ * state[n,h] (float32 [d_v, d_k]) takes the sequence's T tokens (or its packed span) in order
+ * with the update above and o receives scale * W_t q_t after each token; state is read once
+ * and overwritten in place with the memory after the last token (an empty sequence leaves it
+ * unchanged).  A memory that gdr_forward returned as ht continues here exactly as if the
+ * tokens had been part of that forward call.
+ *  - p: as for gdr_forward, except that chunk is not used (it must still be positive) and
+ *    head sizes dk == dv in {64, 128} are built for both dtypes.
+ *  - in: q, k, v, beta, alpha, erase, write as for gdr_forward; in->h0 must be NULL (the
+ *    initial memory is state).
+ *  - state: [N,H,d_v,d_k] float32, required, 16-byte aligned; read, then overwritten.
+ *  - o: [B,H,T,d_v] in the I/O dtype, required when T > 0.
+ * No workspace; nothing is allocated.  There is no backward for this entry point.
+ * Errors: INVALID_ARG, UNSUPPORTED (as for gdr_forward), HIP. */
+gdr_status gdr_decode(const gdr_problem *p, const gdr_inputs *in, float *state, void *o, void *stream);
+
 const char *gdr_status_string(gdr_status s);
 
 /* Per-launch timing, for profiling tools.  After gdr_trace_launches(events, capacity), the

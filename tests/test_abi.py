@@ -181,3 +181,25 @@ def test_trace_argument_checks(lib):
     assert lib.gdr_trace_launches(None, 8) == bd.GDR_ERR_INVALID_ARG
     ev = (ctypes.c_void_p * 2)()
     assert lib.gdr_trace_launches(ev, 1) == bd.GDR_ERR_INVALID_ARG
+
+
+def _dec(lib, p, ins, state=FAKE, o=FAKE):
+    return lib.gdr_decode(ctypes.byref(p), ctypes.byref(ins) if ins is not None else None, state, o, None)
+
+
+@pytest.mark.parametrize("pkw,ikw,state,o,status", [
+    (dict(), dict(h0=FAKE), FAKE, FAKE, bd.GDR_ERR_INVALID_ARG),          # memory comes through state
+    (dict(), dict(), None, FAKE, bd.GDR_ERR_INVALID_ARG),                  # state required
+    (dict(), dict(), FAKE + 8, FAKE, bd.GDR_ERR_INVALID_ARG),              # misaligned state
+    (dict(), dict(), FAKE, None, bd.GDR_ERR_INVALID_ARG),                  # o required when T > 0
+    (dict(), dict(alpha=None), FAKE, FAKE, bd.GDR_ERR_INVALID_ARG),        # gated needs alpha
+    (dict(dk=96, dv=96), dict(), FAKE, FAKE, bd.GDR_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=64), dict(), FAKE, FAKE, bd.GDR_ERR_UNSUPPORTED),
+    (dict(variant=9), dict(), FAKE, FAKE, bd.GDR_ERR_INVALID_ARG),
+    (dict(n_seqs=2, B=1), dict(), FAKE, FAKE, bd.GDR_ERR_INVALID_ARG),      # cu_seqlens missing
+])
+def test_decode_checks(lib, pkw, ikw, state, o, status):
+    p = _problem(T=1, **pkw)
+    assert _dec(lib, p, _inputs(**ikw), state=state, o=o) == status
+    assert lib.gdr_last_error().decode() != ""
+    assert _dec(lib, _problem(T=1), None) == bd.GDR_ERR_INVALID_ARG
