@@ -62,7 +62,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_backward.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, P(GdrGrads), _vp,
                                  ctypes.c_size_t, _vp]
     lib.gdr_decode.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp]
-    for f in ("gdr_workspace_size", "gdr_saved_size", "gdr_forward", "gdr_backward", "gdr_decode"):
+    lib.gdr_forward_residual.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.gdr_backward_residual.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, _vp, P(GdrGrads), _vp,
+                                          ctypes.c_size_t, _vp]
+    for f in ("gdr_workspace_size", "gdr_saved_size", "gdr_forward", "gdr_backward", "gdr_decode",
+              "gdr_forward_residual", "gdr_backward_residual"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -135,9 +139,10 @@ def _inputs(q, k, v, beta, alpha, erase, write, h0) -> GdrInputs:
 
 def gdr_forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *, variant: str,
                 cu_seqlens=None, scale: float = 1.0, chunk: int = 64, output_final_state: bool = True,
-                save: bool = False, workspace=None):
+                save: bool = False, workspace=None, residual=None):
     """Forward.  Returns (o, ht or None, saved or None).  Tensors must be contiguous and on
-    the GPU; the call is asynchronous on torch's current stream."""
+    the GPU; the call is asynchronous on torch's current stream.  `residual`: an optional
+    [B,H,T,dv] tensor (I/O dtype) that receives r_t = v_t - v_bar_t (gdr_forward_residual)."""
     import torch
     lib = load_library()
     p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk)
@@ -149,8 +154,8 @@ def gdr_forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None,
     ws = workspace if workspace is not None and workspace.numel() >= need else \
         torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ins = _inputs(q, k, v, beta, alpha, erase, write, h0)
-    st = lib.gdr_forward(ctypes.byref(p), ctypes.byref(ins), _ptr(o), _ptr(ht), _ptr(saved), _ptr(ws),
-                         ws.numel(), _stream(q))
+    st = lib.gdr_forward_residual(ctypes.byref(p), ctypes.byref(ins), _ptr(o), _ptr(residual), _ptr(ht),
+                                  _ptr(saved), _ptr(ws), ws.numel(), _stream(q))
     _check(lib, st)
     del keep
     return o, ht, saved
@@ -158,9 +163,10 @@ def gdr_forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None,
 
 def gdr_backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do=None, dht=None, *,
                  variant: str, cu_seqlens=None, scale: float = 1.0, chunk: int = 64, saved=None,
-                 want_dh0: bool = True, workspace=None) -> dict:
-    """Backward of sum(o * do) + sum(ht * dht).  Returns a dict of gradients (None where the
-    input is absent).  `saved` is the third result of gdr_forward(save=True), or None."""
+                 want_dh0: bool = True, workspace=None, dr=None) -> dict:
+    """Backward of sum(o * do) + sum(ht * dht) [+ sum(r * dr) with the residual's gradient dr,
+    gdr_backward_residual].  Returns a dict of gradients (None where the input is absent).
+    `saved` is the third result of gdr_forward(save=True), or None."""
     import torch
     lib = load_library()
     p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk)
@@ -174,8 +180,8 @@ def gdr_backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None
     ws = workspace if workspace is not None and workspace.numel() >= need else \
         torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ins = _inputs(q, k, v, beta, alpha, erase, write, h0)
-    st = lib.gdr_backward(ctypes.byref(p), ctypes.byref(ins), _ptr(do), _ptr(dht), _ptr(saved), ctypes.byref(g),
-                          _ptr(ws), ws.numel(), _stream(q))
+    st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(ins), _ptr(do), _ptr(dr), _ptr(dht), _ptr(saved),
+                                   ctypes.byref(g), _ptr(ws), ws.numel(), _stream(q))
     _check(lib, st)
     del keep
     return out

@@ -34,6 +34,10 @@ struct BwdScanOps {
   RegTile<E, CH, CH, 256> m;
   RegTile<E, CH, BV, 256> dO;
   float g;
+  // gradient w.r.t. the residual output (used with RES): this lane's four columns of each
+  // value tile of its chunk row, and 1 / beta of that row
+  f32x4 dr[BV / 16];
+  float binv;
 };
 template <typename E, int D, int BV>
 struct BwdScanOps<E, D, BV, VAR_GDN2> {
@@ -50,18 +54,22 @@ struct BwdScanOps<E, D, BV, VAR_KDA> {
   f32x4 eg[D / 64];
 };
 
-template <typename E, int D, int BV, int VAR>
+// RES (Delta family): the residual r_t = R_t / beta_t was an output too; its gradient dr adds
+// dr_t / beta_t to dR_t before dR feeds the memory gradient and the chunk kernel.
+template <typename E, int D, int BV, int VAR, bool RES>
 __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ dO, const E* __restrict__ Xg,
                                                   const E* __restrict__ Mg, const float* __restrict__ Gg,
                                                   const float* __restrict__ dht, E* __restrict__ dHs,
                                                   E* __restrict__ dRg, float* __restrict__ dh0,
-                                                  const E* __restrict__ beta, const E* __restrict__ erase) {
+                                                  const E* __restrict__ beta, const E* __restrict__ erase,
+                                                  const E* __restrict__ drin) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2;
   constexpr bool KDA = VAR == VAR_KDA;
   constexpr bool DEC = VAR == VAR_GATED || VAR == VAR_GDN2;  // scalar decay
+  static_assert(!RES || VAR == VAR_DELTANET || VAR == VAR_GATED, "residual gradient: Delta family");
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];  // a = beta e*k (GDN-2)
   __shared__ float bsh[CH];
   __shared__ __align__(16) E Qs[CH * LD];
@@ -142,6 +150,18 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
         p.k.load(k + tk * D, D, n);
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
       }
+      if constexpr (RES) {  // accumulator layout of dR^T: row 16 w + lrow, columns 16 it + 4 lgrp
+        const int t = 16 * w + lrow();
+        const bool ok = t < n && !virt;
+        p.binv = ok ? 1.f / (float)beta[tk + t] : 0.f;
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+          const E* src = drin + (tk + (ok ? t : 0)) * D + i0 + 16 * it + 4 * lgrp();
+          f32x4 x = zero4();
+          if (ok) x = get4(src);
+          p.dr[it] = x;
+        }
+      }
       if constexpr (G2) {
         p.e.load(erase + tk * D, D, n);
         const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
@@ -219,7 +239,8 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     for (int it = 0; it < NI; ++it) {
       const f32x4 a1 = mma_k<E, CH>(zero4(), colk(dOt, LDO), 16 * it, colk(Ms, LDR), 16 * w);
       const f32x4 a2 = mma_k<E, D>(zero4(), rowk(dWs, LD), 16 * it, rowk(G2 ? As : Ks, LD), 16 * w);
-      const f32x4 dr = a1 + dec * a2;
+      f32x4 dr = a1 + dec * a2;
+      if constexpr (RES) dr += p.binv * p.dr[it];
       const int c4 = 16 * it + 4 * lgrp();
       put4(dRt + tl * LDO + c4, -dr);
       put4(dRn + tl * LDV + c4, dr);
@@ -300,7 +321,8 @@ struct BwdLds {
 };
 
 
-template <typename E, int D, int VAR>
+// RES: the residual r = R / beta was an output; dbeta gains -(dr . r) / beta = -(dr . R) / beta^2.
+template <typename E, int D, int VAR, bool RES>
 __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ v, const E* __restrict__ beta,
                                                    const E* __restrict__ alpha, const E* __restrict__ dO,
@@ -309,7 +331,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
                                                    const E* __restrict__ dHs, const E* __restrict__ dRg,
                                                    const float* __restrict__ Ag, const float* __restrict__ Lig,
                                                    E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
-                                                   E* __restrict__ dbeta, E* __restrict__ dalpha) {
+                                                   E* __restrict__ dbeta, E* __restrict__ dalpha,
+                                                   const E* __restrict__ drin) {
   using Ly = BwdLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDR = Ly::LDR, LF = Ly::LF;
   constexpr int KH = 64, NH = D / KH;  // the memory is read in blocks of 64 value rows
@@ -319,6 +342,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   __shared__ __align__(16) float gs[CH], bs[CH], red[NT / 64];
   __shared__ float part8[NT / CH][CH], part8b[NT / CH][CH], part8c[NT / CH][CH];  // partial sums
   __shared__ float rq[4][CH], rkh[8][CH], rkb[8][CH];
+  __shared__ float rdr[RES ? CH : 1];  // dr_t . R_t (residual output)
 
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
   E* dRs = reinterpret_cast<E*>(smem + Ly::odR);
@@ -366,6 +390,21 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       pM.load(Mg + u * CH * CH, CH, CH);
       pA.load(Ag + u * CH * CH, CH, CH);
       pLi.load(Lig + u * CH * CH, CH, CH);
+      if constexpr (RES) {  // dr_t . R_t per row, from the registers: a row is VPR adjacent lanes
+        RegTile<E, CH, D, NT> rd;
+        rd.load(drin + tk * D, D, n);
+        using RT = decltype(rd);
+        static_assert(RT::TOTAL % NT == 0 && 64 % RT::VPR == 0, "whole rows per lane group");
+#pragma unroll
+        for (int it = 0; it < RT::IT; ++it) {
+          float a = 0.f;
+#pragma unroll
+          for (int x = 0; x < RT::VE; ++x) a += (float)r2.elem(it, x) * (float)rd.elem(it, x);
+#pragma unroll
+          for (int off = RT::VPR / 2; off > 0; off >>= 1) a += __shfl_xor(a, off, 64);
+          if (threadIdx.x % RT::VPR == 0) rdr[rd.row(it)] = a;
+        }
+      }
       r0.store(Ks, LD);
       r1.store(dOs, LD);
       r2.store(Rs, LD);
@@ -686,6 +725,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     float db = 0.f;
 #pragma unroll
     for (int i = 0; i < NT / CH; ++i) db += part8c[i][t] + part8b[i][t];
+    if constexpr (RES) {
+      if (t < n) {
+        const float bi = 1.f / (float)beta[tk + t];
+        db -= rdr[t] * bi * bi;
+      }
+    }
     if (t < n) dbeta[tk + t] = (E)db;
   }
   __syncthreads();
@@ -697,22 +742,31 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 // Host launchers
 // ---------------------------------------------------------------------------------------
 template <typename E, int D, int VAR>
-static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht,
+static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, const void* dr, const float* dht,
                            const gdr_grads& gr, hipStream_t st) {
   const Geo& g = p.geo;
   constexpr bool KDA = VAR == VAR_KDA;
   const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
   const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
   const float* gin = KDA ? p.Gn : p.G;
+  constexpr bool RES_OK = VAR == VAR_DELTANET || VAR == VAR_GATED;  // residual gradient: Delta family
+  const E* drp = RES_OK ? (const E*)dr : nullptr;
+  auto launch = [&](auto kern, int bv, const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult, const E* d) {
+    hipLaunchKernelGGL(kern, dim3(scan_grid(g, nv_mult * D / bv), sg.mode ? sg.max_seg : 1), dim3(256), 0, st, g, sg,
+                       qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp, (E*)p.dHs, (E*)p.dR, dh0p,
+                       (const E*)in.beta, (const E*)in.erase, d);
+  };
   auto scan = [&](const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult) {
     if (p.bv == 16) {
-      hipLaunchKernelGGL((k_bwd_scan<E, D, 16, VAR>), dim3(scan_grid(g, nv_mult * D / 16), sg.mode ? sg.max_seg : 1),
-                         dim3(256), 0, st, g, sg, qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp,
-                         (E*)p.dHs, (E*)p.dR, dh0p, (const E*)in.beta, (const E*)in.erase);
+      if constexpr (RES_OK) {
+        if (drp) return launch(k_bwd_scan<E, D, 16, VAR, true>, 16, sg, dhtp, dh0p, nv_mult, drp);
+      }
+      launch(k_bwd_scan<E, D, 16, VAR, false>, 16, sg, dhtp, dh0p, nv_mult, nullptr);
     } else {
-      hipLaunchKernelGGL((k_bwd_scan<E, D, 32, VAR>), dim3(scan_grid(g, nv_mult * D / 32), sg.mode ? sg.max_seg : 1),
-                         dim3(256), 0, st, g, sg, qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp,
-                         (E*)p.dHs, (E*)p.dR, dh0p, (const E*)in.beta, (const E*)in.erase);
+      if constexpr (RES_OK) {
+        if (drp) return launch(k_bwd_scan<E, D, 32, VAR, true>, 32, sg, dhtp, dh0p, nv_mult, drp);
+      }
+      launch(k_bwd_scan<E, D, 32, VAR, false>, 32, sg, dhtp, dh0p, nv_mult, nullptr);
     }
   };
   if (p.lseg == 0) {
@@ -735,23 +789,26 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
       return launch_bwd_kda<E, D>(p, in, dO, gr, st);
     } else {
       TraceScope ts_("bwd_chunk", st);
-      hipLaunchKernelGGL((k_bwd_chunk<E, D, VAR>), dim3(g.total_chunks, g.H), dim3(512), 0, st, g,
-                         (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
-                         (const E*)dO, (const E*)p.M, (const float*)p.G, (const E*)p.Hs, (const E*)p.R,
-                         (const E*)p.dHs, (const E*)p.dR, p.A1, p.Li, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv,
-                         (E*)gr.dbeta, (E*)gr.dalpha);
+      auto chunk = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, (const E*)in.q, (const E*)in.k,
+                           (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (const E*)dO, (const E*)p.M,
+                           (const float*)p.G, (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR, p.A1,
+                           p.Li, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta, (E*)gr.dalpha, drp);
+      };
+      if (drp) chunk(k_bwd_chunk<E, D, VAR, true>);
+      else chunk(k_bwd_chunk<E, D, VAR, false>);
     }
   }
   return hipGetLastError();
 }
 
-hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht, const gdr_grads& gr,
-                        hipStream_t st) {
+hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const void* dr, const float* dht,
+                        const gdr_grads& gr, hipStream_t st) {
   const bool bf = p.dtype == GDR_BF16;
 #define GDR_BWD_CASE(V)                                                                  \
-  if (bf && p.D == 128) return bwd_impl<bf16, 128, V>(p, in, dO, dht, gr, st);           \
-  if (bf && p.D == 64) return bwd_impl<bf16, 64, V>(p, in, dO, dht, gr, st);             \
-  if (!bf && p.D == 64) return bwd_impl<float, 64, V>(p, in, dO, dht, gr, st);           \
+  if (bf && p.D == 128) return bwd_impl<bf16, 128, V>(p, in, dO, dr, dht, gr, st);       \
+  if (bf && p.D == 64) return bwd_impl<bf16, 64, V>(p, in, dO, dr, dht, gr, st);         \
+  if (!bf && p.D == 64) return bwd_impl<float, 64, V>(p, in, dO, dr, dht, gr, st);       \
   break;
   switch (p.variant) {
     case GDR_DELTANET: GDR_BWD_CASE(VAR_DELTANET)

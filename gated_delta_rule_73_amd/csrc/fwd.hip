@@ -156,6 +156,9 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
 // key column of its value rows, so the output needs nothing from other tiles), records W0
 // and R for the backward, and carries W_next = e^{g_n} W0 + R^T (e^{g_n-g} K).
 // FULL = false is the segment-map pass (ScanSeg mode 1): no output and nothing recorded.
+// RES (with FULL, Delta family and Kimi Delta Attention): also write the delta-rule residual
+// r_t = v_t - v_bar_t of every token.  The chunk form's R_t is beta_t r_t (the memory gains
+// R_t k_t^T), so r_t = R_t / beta_t, formed from the float32 R before it is rounded.
 // ---------------------------------------------------------------------------------------
 // Operands of one chunk of the forward scan, held in registers while they are in flight.
 // Gated DeltaNet-2 also needs the erase gates (for the erase direction a = beta e*k) and the
@@ -171,7 +174,7 @@ struct FwdScanOps {
   f32x4 eg[D / 64];
 };
 
-template <typename E, int D, int BV, int VAR, bool FULL>
+template <typename E, int D, int BV, int VAR, bool FULL, bool RES>
 __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ k, const E* __restrict__ Xg,
                                                   const E* __restrict__ Ug, const float* __restrict__ Gg,
                                                   const float* __restrict__ h0, E* __restrict__ Hs,
@@ -179,7 +182,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
                                                   const E* __restrict__ vin, const E* __restrict__ beta,
                                                   const E* __restrict__ erase, const E* __restrict__ write,
                                                   const E* __restrict__ q, const E* __restrict__ Mg,
-                                                  const E* __restrict__ M2g, E* __restrict__ o) {
+                                                  const E* __restrict__ M2g, E* __restrict__ o,
+                                                  E* __restrict__ rout) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2;
@@ -204,6 +208,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
   __shared__ __align__(16) E Ms[FULL ? CH * LDR : 8];
   __shared__ __align__(16) E M2s[OUT_G2 ? CH * LDR : 8];
   __shared__ __align__(16) E Os[FULL ? CH * LDV : 8];
+  static_assert(!RES || (FULL && !G2), "the residual output is formed by the full pass of the delta family");
+  __shared__ __align__(16) E Rr[RES ? CH * LDV : 8];  // r = R / beta for this tile's value columns
   __shared__ float gs[CH];
 
   constexpr int NVR = D / BV;
@@ -275,6 +281,10 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         p.k.load(k + tk * D, D, n);
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
       }
+      if constexpr (RES) {
+        const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
+        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? 1.f / (float)beta[tk + t] : 0.f;
+      }
       if constexpr (G2) {
         p.e.load(erase + tk * D, D, n);
         p.vt.load(vin + tk * D + i0, D, n);
@@ -303,7 +313,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     } else {
       if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
     }
-    if constexpr (G2) {
+    if constexpr (G2 || RES) {  // GDN-2: beta; residual output: 1 / beta (0 past the end)
       if (threadIdx.x < CH) bsh[threadIdx.x] = p.b;
     }
 #pragma unroll
@@ -355,6 +365,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       const f32x4 rv = (virt ? zero4() : get4(Us + tl * LDV + c4)) - acc;
       put4(Rn + tl * LDV + c4, rv);
       put4(Rd + tl * LDD + c4, dec * rv);
+      if constexpr (RES) put4(Rr + tl * LDV + c4, bsh[tl] * rv);
     }
     if constexpr (FULL) s2g_full<E, BV, D, NT>(Hs + u * D * D + (long)i0 * D, D, Ws, LD);
     __syncthreads();
@@ -396,6 +407,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     if constexpr (FULL) {
       if (o) s2g_rows<E, CH, BV, NT>(o + tk * D + i0, D, Os, LDV, n);
     }
+    if constexpr (RES) s2g_rows<E, CH, BV, NT>(rout + tk * D + i0, D, Rr, LDV, n);
   };
   if (c1 > c0) {
     Ops pa, pb;
@@ -429,7 +441,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
 // Host launchers
 // ---------------------------------------------------------------------------------------
 template <typename E, int D, int VAR>
-static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st) {
+static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r, float* ht, bool want_out,
+                           hipStream_t st) {
   const Geo& g = p.geo;
   const dim3 cgrid(g.total_chunks, g.H);
   if (g.total_chunks > 0) {
@@ -451,19 +464,27 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, float* 
   const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
   const float* gin = KDA ? p.Gn : p.G;
   E* out = want_out ? (E*)o : nullptr;
+  E* rout = (want_out && r) ? (E*)r : nullptr;
+  auto launch = [&](auto kern, int bv, int nvm, const ScanSeg& sg, const float* h0, float* htp, E* rr) {
+    hipLaunchKernelGGL(kern, dim3(scan_grid(g, nvm * D / bv), sg.mode ? sg.max_seg : 1), dim3(256), 0, st, g, sg, kin,
+                       (const E*)p.X, (const E*)p.Ub, gin, h0, (E*)p.Hs, (E*)p.R, htp, (const E*)in.v,
+                       (const E*)in.beta, (const E*)in.erase, (const E*)in.write, qin, (const E*)p.M, (const E*)p.M2,
+                       out, rr);
+  };
   auto scan = [&](auto full, const ScanSeg& sg, const float* h0, float* htp) {
     constexpr bool F = decltype(full)::value;
+    constexpr bool RES_OK = F && VAR != VAR_GDN2;  // residual output: full pass, delta family and KDA
     const int nvm = F ? 1 : 2;
     if (std::is_same<E, float>::value || p.bv == 16) {
-      hipLaunchKernelGGL((k_fwd_scan<E, D, 16, VAR, F>), dim3(scan_grid(g, nvm * D / 16), sg.mode ? sg.max_seg : 1),
-                         dim3(256), 0, st, g, sg, kin, (const E*)p.X, (const E*)p.Ub, gin, h0, (E*)p.Hs, (E*)p.R, htp,
-                         (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write, qin,
-                         (const E*)p.M, (const E*)p.M2, out);
+      if constexpr (RES_OK) {
+        if (rout) return launch(k_fwd_scan<E, D, 16, VAR, F, true>, 16, nvm, sg, h0, htp, rout);
+      }
+      launch(k_fwd_scan<E, D, 16, VAR, F, false>, 16, nvm, sg, h0, htp, nullptr);
     } else if constexpr (!std::is_same<E, float>::value) {
-      hipLaunchKernelGGL((k_fwd_scan<E, D, 32, VAR, F>), dim3(scan_grid(g, nvm * D / 32), sg.mode ? sg.max_seg : 1),
-                         dim3(256), 0, st, g, sg, kin, (const E*)p.X, (const E*)p.Ub, gin, h0, (E*)p.Hs, (E*)p.R, htp,
-                         (const E*)in.v, (const E*)in.beta, (const E*)in.erase, (const E*)in.write, qin,
-                         (const E*)p.M, (const E*)p.M2, out);
+      if constexpr (RES_OK) {
+        if (rout) return launch(k_fwd_scan<E, D, 32, VAR, F, true>, 32, nvm, sg, h0, htp, rout);
+      }
+      launch(k_fwd_scan<E, D, 32, VAR, F, false>, 32, nvm, sg, h0, htp, nullptr);
     }
   };
   if (p.lseg == 0) {
@@ -482,12 +503,13 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, float* 
   return hipGetLastError();
 }
 
-hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st) {
+hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, void* r, float* ht, bool want_out,
+                       hipStream_t st) {
   const bool bf = p.dtype == GDR_BF16;
 #define GDR_FWD_CASE(V)                                                                  \
-  if (bf && p.D == 128) return fwd_impl<bf16, 128, V>(p, in, o, ht, want_out, st);       \
-  if (bf && p.D == 64) return fwd_impl<bf16, 64, V>(p, in, o, ht, want_out, st);         \
-  if (!bf && p.D == 64) return fwd_impl<float, 64, V>(p, in, o, ht, want_out, st);       \
+  if (bf && p.D == 128) return fwd_impl<bf16, 128, V>(p, in, o, r, ht, want_out, st);    \
+  if (bf && p.D == 64) return fwd_impl<bf16, 64, V>(p, in, o, r, ht, want_out, st);      \
+  if (!bf && p.D == 64) return fwd_impl<float, 64, V>(p, in, o, r, ht, want_out, st);    \
   break;
   switch (p.variant) {
     case GDR_DELTANET: GDR_FWD_CASE(VAR_DELTANET)

@@ -293,30 +293,46 @@ gdr_status gdr_saved_size(const gdr_problem* p, size_t* bytes) {
   return GDR_OK;
 }
 
-gdr_status gdr_forward(const gdr_problem* p, const gdr_inputs* in, void* o, float* ht, void* saved, void* ws,
-                       size_t ws_bytes, void* stream) {
+gdr_status gdr_forward_residual(const gdr_problem* p, const gdr_inputs* in, void* o, void* r, float* ht, void* saved,
+                                void* ws, size_t ws_bytes, void* stream) {
   Sizes s;
   gdr_status st = check_problem(p, &s);
   if (st != GDR_OK) return st;
   if ((st = check_inputs(p, in)) != GDR_OK) return st;
   if (!o && p->T > 0) return fail(GDR_ERR_INVALID_ARG, "o is required");
-  if ((o && !aligned(o, 16)) || (ht && !aligned(ht, 16)) || (saved && !aligned(saved, 256)))
-    return fail(GDR_ERR_INVALID_ARG, "o/ht must be 16-byte and saved 256-byte aligned");
+  if ((o && !aligned(o, 16)) || (r && !aligned(r, 16)) || (ht && !aligned(ht, 16)) || (saved && !aligned(saved, 256)))
+    return fail(GDR_ERR_INVALID_ARG, "o/r/ht must be 16-byte and saved 256-byte aligned");
+  if (r && p->variant == GDR_GDN2)
+    return fail(GDR_ERR_UNSUPPORTED, "the residual output is defined for the delta family and Kimi Delta Attention");
   if ((st = check_ws(ws, ws_bytes, s.cache() + s.fwd_ws())) != GDR_OK) return st;
   char* cache = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + s.fwd_ws();
   gdr::Plan pl = make_plan(p, s, cache, static_cast<char*>(ws), false);
   g_last_error.clear();
   TraceCall tc;
-  return hip_status(gdr::run_forward(pl, *in, o, ht, true, static_cast<hipStream_t>(stream)), "gdr_forward launch");
+  return hip_status(gdr::run_forward(pl, *in, o, r, ht, true, static_cast<hipStream_t>(stream)), "gdr_forward launch");
 }
 
-gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* dO, const float* dht,
-                        const void* saved, gdr_grads* g, void* ws, size_t ws_bytes, void* stream) {
+gdr_status gdr_forward(const gdr_problem* p, const gdr_inputs* in, void* o, float* ht, void* saved, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return gdr_forward_residual(p, in, o, nullptr, ht, saved, ws, ws_bytes, stream);
+}
+
+gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, const void* dO, const void* dr,
+                                 const float* dht, const void* saved, gdr_grads* g, void* ws, size_t ws_bytes,
+                                 void* stream) {
   Sizes s;
   gdr_status st = check_problem(p, &s);
   if (st != GDR_OK) return st;
   if ((st = check_inputs(p, in)) != GDR_OK) return st;
   if (!g) return fail(GDR_ERR_INVALID_ARG, "grads is NULL");
+  if (dr && p->variant != GDR_DELTANET && p->variant != GDR_GATED)
+    return fail(GDR_ERR_UNSUPPORTED, "the residual gradient is built for DeltaNet and Gated DeltaNet");
+  // dr enters as dR += dr / beta; the beta gradient then holds two terms of order |dr| |r| / beta
+  // that cancel, and with bfloat16 operands their rounding leaves errors above the tolerance at
+  // small beta.  float32 I/O keeps them accurate.
+  if (dr && p->dtype != GDR_F32)
+    return fail(GDR_ERR_UNSUPPORTED, "the residual gradient is built for float32 I/O only");
+  if (dr && !aligned(dr, 16)) return fail(GDR_ERR_INVALID_ARG, "dr must be 16-byte aligned");
   if (p->T > 0) {
     if (!dO) return fail(GDR_ERR_INVALID_ARG, "dO is required");
     if (!g->dq || !g->dk || !g->dv) return fail(GDR_ERR_INVALID_ARG, "dq, dk and dv are required");
@@ -339,10 +355,15 @@ gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* 
   g_last_error.clear();
   TraceCall tc;
   if (!saved) {
-    st = hip_status(gdr::run_forward(pl, *in, nullptr, nullptr, false, hs), "gdr_backward recompute launch");
+    st = hip_status(gdr::run_forward(pl, *in, nullptr, nullptr, nullptr, false, hs), "gdr_backward recompute launch");
     if (st != GDR_OK) return st;
   }
-  return hip_status(gdr::run_backward(pl, *in, dO, dht, *g, hs), "gdr_backward launch");
+  return hip_status(gdr::run_backward(pl, *in, dO, dr, dht, *g, hs), "gdr_backward launch");
+}
+
+gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* dO, const float* dht,
+                        const void* saved, gdr_grads* g, void* ws, size_t ws_bytes, void* stream) {
+  return gdr_backward_residual(p, in, dO, nullptr, dht, saved, g, ws, ws_bytes, stream);
 }
 
 gdr_status gdr_decode(const gdr_problem* p, const gdr_inputs* in, float* state, void* o, void* stream) {

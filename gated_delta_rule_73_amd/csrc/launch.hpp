@@ -88,8 +88,11 @@ hipError_t launch_seg_combine(const Plan& p, const ScanSeg& sg, const float* ini
 // Recurrent form over every sequence's tokens, memory updated in place (decoding).
 hipError_t run_decode(const Geo& g, int variant, int dtype, int D, const gdr_inputs& in, float* state, void* o,
                       hipStream_t st);
-hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, float* ht, bool want_out, hipStream_t st);
-hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const float* dht, const gdr_grads& gr,
-                        hipStream_t st);
+// r: optional residual output (Delta family and Kimi Delta Attention); dr: optional gradient
+// w.r.t. it (Delta family).  Both may be NULL.
+hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, void* r, float* ht, bool want_out,
+                       hipStream_t st);
+hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, const void* dr, const float* dht,
+                        const gdr_grads& gr, hipStream_t st);
 
 }  // namespace gdr

@@ -115,6 +115,31 @@ gdr_status gdr_backward(const gdr_problem *p, const gdr_inputs *in, const void *
                         const float *dht, const void *saved, gdr_grads *g, void *ws,
                         size_t ws_bytes, void *stream);
 
+/* Forward that also returns the delta-rule residual r_t = v_t - v_bar_t of every token: the
+ * "write error" of item 1 "Notacion Unificada" (page "Linear Attention Architectures:
+ * Mechanisms, Trade-offs, and Cross-Layer Routing", section "Metodologia y Marco de Trabajo"),
+ * which the cross-layer error routing of item 3 of the same section (CLER, CLER-H) passes on
+ * to another layer.  v_bar_t is the prediction of the decayed memory before token t's write.
+ *  - r: [B,H,T,d_v] in the I/O dtype, or NULL (then this is gdr_forward).  Every other
+ *    argument as for gdr_forward.
+ *  - Defined for GDR_DELTANET, GDR_GATED and GDR_KDA; GDR_GDN2 with r != NULL returns
+ *    UNSUPPORTED (its update has separate erase and write terms, not one residual).
+ *  - The chunk form writes R_t = beta_t r_t into the memory; r_t is returned as R_t / beta_t
+ *    from the float32 R_t, so it needs beta_t > 0: a token with beta_t == 0 gets r_t = 0.
+ * Errors: as gdr_forward. */
+gdr_status gdr_forward_residual(const gdr_problem *p, const gdr_inputs *in, void *o, void *r, float *ht,
+                                void *saved, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of sum(o * dO) + sum(r * dr) + sum(ht * dht), r the residual output of
+ * gdr_forward_residual.  dr: [B,H,T,d_v] in the I/O dtype, or NULL (then this is
+ * gdr_backward).  Built for GDR_DELTANET and GDR_GATED with float32 I/O; other variants and
+ * bfloat16 I/O with dr != NULL return UNSUPPORTED (the bfloat16 beta gradient of this form does
+ * not reach the library's tolerance at small beta).  Needs beta_t > 0 as above.  Every other
+ * argument as for gdr_backward. */
+gdr_status gdr_backward_residual(const gdr_problem *p, const gdr_inputs *in, const void *dO, const void *dr,
+                                 const float *dht, const void *saved, gdr_grads *g, void *ws,
+                                 size_t ws_bytes, void *stream);
+
 /* Recurrent (token-by-token) form, for decoding.  The page "Linear Attention Architectures:
  * Mechanisms, Trade-offs, and Cross-Layer Routing" (section "Declaracion del Problema") gives
  * linear attention a constant-size memory updated once per token, hence constant inference

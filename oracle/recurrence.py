@@ -32,6 +32,9 @@ listed with its justification in the design notes):
     channels:  W <- W' - v_bar (beta e*k)^T + (beta w*v) k^T.  beta is 1 when
     the workload has none.  With e = w = 1 this is the Gated DeltaNet update.
   * Output o_t = scale * W_t q_t with the memory after token t's write.
+  * Optionally the residual itself, r_t = v_t - v_bar_t (the delta rule's write
+    error, which the pages' cross-layer error routing passes to another layer),
+    for the delta family; Gated DeltaNet-2 has no single residual.
 
 Everything is float64.  Heads are independent memories; the per-token update
 is applied to all heads of one sequence at once (numpy batching over the head
@@ -128,8 +131,9 @@ def _check(variant, q, k, v, beta, alpha, erase, write):
 
 
 def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
-            variant, cu_seqlens=None, scale=1.0):
-    """Run the recurrence.  Returns (o [B,H,T,dv], ht [N,H,dv,dk]) in float64.
+            variant, cu_seqlens=None, scale=1.0, residual=False):
+    """Run the recurrence.  Returns (o [B,H,T,dv], ht [N,H,dv,dk]) in float64, and with
+    residual=True also r [B,H,T,dv], r_t = v_t - v_bar_t (delta family only).
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] (None -> 1, gdn2 only);
     alpha: None (deltanet), [B,H,T] (gated, gdn2) or [B,H,T,dk] (kda);
@@ -138,24 +142,29 @@ def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
     """
     q, k, v, beta, alpha, erase, write, h0 = map(_f64, (q, k, v, beta, alpha, erase, write, h0))
     _check(variant, q, k, v, beta, alpha, erase, write)
+    if residual and variant == "gdn2":
+        raise ValueError("gdn2 has separate erase and write terms, not one residual")
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     seqs = list(_sequences(B, T, cu_seqlens))
     o = np.zeros((B, H, T, dv))
+    r = np.zeros((B, H, T, dv))
     ht = np.zeros((len(seqs), H, dv, dk))
     for b, t0, t1, n in seqs:
         s = _Seq(variant, q, k, v, beta, alpha, erase, write, b, t0, t1)
         W = np.zeros((H, dv, dk)) if h0 is None else h0[n].copy()
         for t in range(s.L):
-            W = s.step(W, t)
+            W, v_bar = s.write_step(s.decay(W, t), t)
+            r[b, :, t0 + t] = s.v[:, t] - v_bar
             o[b, :, t0 + t] = scale * np.einsum("hij,hj->hi", W, s.q[:, t])
         ht[n] = W
-    return o, ht
+    return (o, ht, r) if residual else (o, ht)
 
 
 def backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do=None,
-             dht=None, *, variant, cu_seqlens=None, scale=1.0, checkpoint_every=64):
-    """Gradients of sum(o * do) + sum(ht * dht) by manual reverse mode through the recurrence.
+             dht=None, *, variant, cu_seqlens=None, scale=1.0, checkpoint_every=64, dr=None):
+    """Gradients of sum(o * do) + sum(ht * dht) [+ sum(r * dr), r the residual output of
+    forward(residual=True), when dr is given] by manual reverse mode through the recurrence.
 
     The memory is checkpointed every `checkpoint_every` tokens; each segment's
     per-token memories are recomputed from its checkpoint (the same float64
@@ -163,9 +172,11 @@ def backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do
     Returns a dict with dq, dk, dv, dbeta, dalpha, derase, dwrite, dh0 (None where
     the input is absent).  dalpha is the gradient with respect to alpha itself.
     """
-    q, k, v, beta, alpha, erase, write, h0, do, dht = map(
-        _f64, (q, k, v, beta, alpha, erase, write, h0, do, dht))
+    q, k, v, beta, alpha, erase, write, h0, do, dht, dr = map(
+        _f64, (q, k, v, beta, alpha, erase, write, h0, do, dht, dr))
     _check(variant, q, k, v, beta, alpha, erase, write)
+    if dr is not None and variant == "gdn2":
+        raise ValueError("gdn2 has separate erase and write terms, not one residual")
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     seqs = list(_sequences(B, T, cu_seqlens))
@@ -192,16 +203,18 @@ def backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do
                 before.append(W)
                 W = s.step(W, t)
             for t in range(c1 - 1, c0 - 1, -1):
-                _token_backward(s, t, before[t - c0], dW, do[b, :, t0 + t] * scale, g, b, t0)
+                _token_backward(s, t, before[t - c0], dW, do[b, :, t0 + t] * scale, g, b, t0,
+                                None if dr is None else dr[b, :, t0 + t])
                 dW = s.last_dW_prev
         dh0[n] = dW
     g["dh0"] = dh0
     return g
 
 
-def _token_backward(s, t, W_prev, dW, do_t, g, b, t0):
+def _token_backward(s, t, W_prev, dW, do_t, g, b, t0, dr_t=None):
     """Reverse mode through token t.  dW is the gradient w.r.t. W_t (post-write memory),
-    do_t the (scaled) output gradient.  Leaves the gradient w.r.t. W_{t-1} in s.last_dW_prev."""
+    do_t the (scaled) output gradient, dr_t the gradient w.r.t. the residual r_t = v_t - v_bar
+    (or None).  Leaves the gradient w.r.t. W_{t-1} in s.last_dW_prev."""
     k = s.k[:, t]
     v = s.v[:, t]
     beta = s.beta[:, t]
@@ -221,6 +234,9 @@ def _token_backward(s, t, W_prev, dW, do_t, g, b, t0):
         a = beta[:, None] * k
         bvec = beta[:, None] * v
     d_vbar = -np.einsum("hij,hj->hi", dW, a)
+    if dr_t is not None:                      # r_t = v_t - v_bar
+        d_vbar = d_vbar - dr_t
+        g["dv"][b, :, tt] += dr_t
     d_a = -np.einsum("hij,hi->hj", dW, v_bar)
     d_b = np.einsum("hij,hj->hi", dW, k)
     dk_t = np.einsum("hij,hi->hj", dW, bvec)

@@ -203,3 +203,26 @@ def test_decode_checks(lib, pkw, ikw, state, o, status):
     assert _dec(lib, p, _inputs(**ikw), state=state, o=o) == status
     assert lib.gdr_last_error().decode() != ""
     assert _dec(lib, _problem(T=1), None) == bd.GDR_ERR_INVALID_ARG
+
+
+def test_residual_checks(lib):
+    p = _problem(variant=3)  # GDN-2 has no single residual
+    ins = _inputs(erase=FAKE, write=FAKE)
+    st = lib.gdr_forward_residual(ctypes.byref(p), ctypes.byref(ins), FAKE, FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == bd.GDR_ERR_UNSUPPORTED
+    p = _problem()
+    st = lib.gdr_forward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE + 8, None, None, FAKE,
+                                  1 << 40, None)
+    assert st == bd.GDR_ERR_INVALID_ARG
+    p = _problem(variant=2)  # KDA: the residual's gradient is not built
+    st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE, None, None,
+                                   ctypes.byref(_grads()), FAKE, 1 << 40, None)
+    assert st == bd.GDR_ERR_UNSUPPORTED
+    p = _problem()  # bfloat16 I/O: the residual gradient is not built
+    st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE, None, None,
+                                   ctypes.byref(_grads()), FAKE, 1 << 40, None)
+    assert st == bd.GDR_ERR_UNSUPPORTED
+    p = _problem(dtype=0, dk=64, dv=64)
+    st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE + 4, None, None,
+                                   ctypes.byref(_grads()), FAKE, 1 << 40, None)
+    assert st == bd.GDR_ERR_INVALID_ARG

@@ -1,0 +1,121 @@
+"""GPU parity of the residual output r_t = v_t - v_bar_t (gdr_forward_residual) and of its
+gradient (gdr_backward_residual) against the float64 oracle."""
+import numpy as np
+import pytest
+
+import synth
+from tests._helpers import compare, gpu_inputs, to_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(variant, dtype, d, T, B=2, H=2, cu=None, seed=41):
+    w = synth.Workload("res", variant, dtype, B, H, T, d, d, seed=seed, h0_std=0.1,
+                       cu_seqlens=None if cu is None else tuple(cu))
+    inp = synth.make_inputs(w, alpha_mode="weak")
+    rng = np.random.default_rng(seed + 1)
+    inp["dr"] = synth.to_io(rng.standard_normal(inp["v"].shape), dtype)
+    return inp
+
+
+def _oracle(inp, variant, backward, scale=1.0):
+    from oracle import recurrence as R
+    kw = {n: inp.get(n) for n in ("q", "k", "v", "beta", "alpha", "erase", "write", "h0")}
+    cu = inp.get("cu_seqlens")
+    o, ht, r = R.forward(**kw, variant=variant, cu_seqlens=cu, scale=scale, residual=True)
+    ref = {"o": o, "ht": ht, "r": r}
+    if backward:
+        ref.update(R.backward(**kw, do=inp["do"], dr=inp["dr"], variant=variant, cu_seqlens=cu, scale=scale))
+    return ref
+
+
+def _hip(inp, variant, dtype, backward, use_saved=True, scale=1.0):
+    import torch
+    from gated_delta_rule_73_amd import gdr_backward, gdr_forward
+    g = gpu_inputs(inp, dtype)
+    cu = inp.get("cu_seqlens")
+    r = torch.empty_like(g["v"])
+    o, ht, saved = gdr_forward(**g, variant=variant, cu_seqlens=cu, scale=scale, save=backward and use_saved,
+                               residual=r)
+    got = {"o": to_np(o), "ht": to_np(ht), "r": to_np(r)}
+    if backward:
+        gr = gdr_backward(**g, do=to_gpu(inp["do"], dtype), dr=to_gpu(inp["dr"], dtype), variant=variant,
+                          cu_seqlens=cu, scale=scale, saved=saved if use_saved else None)
+        got.update({k: to_np(v) for k, v in gr.items()})
+    torch.cuda.synchronize()
+    return got
+
+
+FWD = [(v, dt, d) for v in ("deltanet", "gated", "kda") for dt, d in (("bf16", 128), ("f32", 64))]
+
+
+@pytest.mark.parametrize("variant,dtype,d", FWD, ids=[f"{v}-{dt}-{d}" for v, dt, d in FWD])
+def test_residual_forward(variant, dtype, d):
+    inp = _inputs(variant, dtype, d, T=150)
+    rep = []
+    compare(_hip(inp, variant, dtype, False, scale=0.8), _oracle(inp, variant, False, scale=0.8), dtype, report=rep)
+    print("\n".join(rep))
+
+
+BWD = [(v, dt, d, s) for v in ("deltanet", "gated") for dt, d in (("f32", 64),) for s in (True, False)]
+
+
+@pytest.mark.parametrize("variant,dtype,d,use_saved", BWD,
+                         ids=[f"{v}-{dt}-{d}-{'saved' if s else 'recompute'}" for v, dt, d, s in BWD])
+def test_residual_backward(variant, dtype, d, use_saved):
+    inp = _inputs(variant, dtype, d, T=150)
+    rep = []
+    compare(_hip(inp, variant, dtype, True, use_saved), _oracle(inp, variant, True), dtype, report=rep)
+    print("\n".join(rep))
+
+
+def test_residual_packed_sequences():
+    """Packed sequences (one empty, ragged tails), segmented scans forced on."""
+    import os
+    cu = [0, 70, 70, 200, 333]
+    inp = _inputs("gated", "f32", 64, T=333, B=1, H=3, cu=cu)
+    os.environ["GDR_SEG_CHUNKS"] = "1"
+    try:
+        got = _hip(inp, "gated", "f32", True)
+    finally:
+        del os.environ["GDR_SEG_CHUNKS"]
+    compare(got, _oracle(inp, "gated", True), "f32")
+
+
+def test_residual_forward_packed_bf16():
+    cu = [0, 70, 70, 200, 333]
+    inp = _inputs("gated", "bf16", 128, T=333, B=1, H=3, cu=cu)
+    compare(_hip(inp, "gated", "bf16", False), _oracle(inp, "gated", False), "bf16")
+
+
+def test_residual_gradient_zero_matches_plain_backward():
+    """dr = 0 through the residual kernels gives the plain backward's gradients."""
+    import torch
+    from gated_delta_rule_73_amd import gdr_backward, gdr_forward
+    inp = _inputs("gated", "f32", 64, T=200)
+    g = gpu_inputs(inp, "f32")
+    do = to_gpu(inp["do"], "f32")
+    _, _, saved = gdr_forward(**g, variant="gated", save=True)
+    a = gdr_backward(**g, do=do, variant="gated", saved=saved)
+    b = gdr_backward(**g, do=do, dr=torch.zeros_like(do), variant="gated", saved=saved)
+    torch.cuda.synchronize()
+    for name in a:  # the same arithmetic; at most a rounding-order difference of the last bit
+        if a[name] is not None:
+            assert torch.allclose(a[name].float(), b[name].float(), rtol=2 ** -7, atol=1e-5), name
+
+
+def test_residual_unsupported_variants():
+    import torch
+    from gated_delta_rule_73_amd import GdrError, gdr_backward, gdr_forward
+    inp = _inputs("gdn2", "bf16", 128, T=64)
+    g = gpu_inputs(inp, "bf16")
+    with pytest.raises(GdrError):
+        gdr_forward(**g, variant="gdn2", residual=torch.empty_like(g["v"]))
+    inp = _inputs("kda", "f32", 64, T=64)
+    g = gpu_inputs(inp, "f32")
+    with pytest.raises(GdrError):
+        gdr_backward(**g, do=to_gpu(inp["do"], "f32"), dr=to_gpu(inp["dr"], "f32"), variant="kda")
+    inp = _inputs("gated", "bf16", 128, T=64)
+    g = gpu_inputs(inp, "bf16")
+    with pytest.raises(GdrError):  # bfloat16 residual gradient: not built
+        gdr_backward(**g, do=to_gpu(inp["do"], "bf16"), dr=to_gpu(inp["dr"], "bf16"), variant="gated")

@@ -306,3 +306,90 @@ def test_backward_matches_finite_differences(variant, cu):
             xm[name][idx] -= eps
             fd[idx] = (loss(xp) - loss(xm)) / (2 * eps)
         np.testing.assert_allclose(g[gname], fd, rtol=1e-6, atol=1e-7, err_msg=gname)
+
+
+# ---------------------------------------------------------------------------------------
+# The residual output r_t = v_t - v_bar_t
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda"])
+def test_residual_basis_keys_is_value(variant):
+    """Keys that are distinct standard basis vectors never overlap, even after a per-channel
+    decay, so from a zero memory every prediction is 0 and r_t = v_t exactly."""
+    rng = np.random.default_rng(21)
+    d = 6
+    x = _rand_inputs(rng, variant, B=1, H=2, T=d, dk=d, dv=3)
+    perm = rng.permutation(d)
+    x["k"] = np.broadcast_to(np.eye(d)[perm], (1, 2, d, d)).copy()
+    _, _, r = R.forward(**x, variant=variant, residual=True)
+    np.testing.assert_array_equal(r, x["v"])
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda"])
+def test_residual_beta_zero_is_value_minus_decayed_prediction(variant):
+    """beta = 0 writes nothing, so the prediction is the decayed initial memory at k_t:
+    r_t = v_t - (W0 Gamma_t) k_t."""
+    rng = np.random.default_rng(22)
+    x = _rand_inputs(rng, variant, B=2, H=2, T=7, dk=5, dv=4)
+    x["beta"] = np.zeros((2, 2, 7))
+    h0 = rng.standard_normal((2, 2, 4, 5))
+    _, _, r = R.forward(**x, h0=h0, variant=variant, residual=True)
+    for b in range(2):
+        for h in range(2):
+            gam = np.ones(5)
+            for t in range(7):
+                gam = gam * _decay_vec(x["alpha"], variant, b, h, t, 5)
+                want = x["v"][b, h, t] - (h0[b, h] * gam[None, :]) @ x["k"][b, h, t]
+                np.testing.assert_allclose(r[b, h, t], want, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gated"])
+def test_residual_repeated_key(variant):
+    """Full-strength writes (beta = 1) at one unit key from a zero memory: the first residual
+    is v_1, the second v_2 - alpha_2 v_1 (v_2 - v_1 without decay)."""
+    rng = np.random.default_rng(23)
+    k1 = rng.standard_normal(5)
+    k1 /= np.linalg.norm(k1)
+    k = np.stack([k1, k1])[None, None]
+    v = rng.standard_normal((1, 1, 2, 3))
+    alpha = None if variant == "deltanet" else np.array([[[0.9, 0.6]]])
+    _, _, r = R.forward(k.copy(), k, v, np.ones((1, 1, 2)), alpha, variant=variant, residual=True)
+    a2 = 1.0 if alpha is None else 0.6
+    np.testing.assert_allclose(r[0, 0, 0], v[0, 0, 0], rtol=1e-14)
+    np.testing.assert_allclose(r[0, 0, 1], v[0, 0, 1] - a2 * v[0, 0, 0], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda"])
+def test_residual_backward_matches_finite_differences(variant):
+    rng = np.random.default_rng(24)
+    x = _rand_inputs(rng, variant, B=2, H=2, T=7, dk=3, dv=4, unit_keys=False)
+    x["h0"] = rng.standard_normal((2, 2, 4, 3))
+    G = rng.standard_normal((2, 2, 7, 4))
+    Gr = rng.standard_normal((2, 2, 7, 4))
+
+    def loss(xx):
+        o, _, r = R.forward(**xx, variant=variant, scale=0.9, residual=True)
+        return np.sum(o * G) + np.sum(r * Gr)
+
+    g = R.backward(**x, do=G, dr=Gr, variant=variant, scale=0.9, checkpoint_every=3)
+    eps = 1e-6
+    for name, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("beta", "dbeta"), ("alpha", "dalpha"),
+                        ("h0", "dh0")):
+        if x[name] is None:
+            continue
+        fd = np.zeros_like(x[name])
+        it = np.nditer(x[name], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp = {kk: (vv.copy() if vv is not None else None) for kk, vv in x.items()}
+            xm = {kk: (vv.copy() if vv is not None else None) for kk, vv in x.items()}
+            xp[name][idx] += eps
+            xm[name][idx] -= eps
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+        np.testing.assert_allclose(g[gname], fd, rtol=1e-6, atol=1e-7, err_msg=gname)
+
+
+def test_residual_refused_for_gdn2():
+    rng = np.random.default_rng(25)
+    x = _rand_inputs(rng, "gdn2", T=3)
+    with pytest.raises(ValueError):
+        R.forward(**x, variant="gdn2", residual=True)
