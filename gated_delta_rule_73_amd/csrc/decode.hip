@@ -8,7 +8,9 @@
 // touches row i only through v_i, w_i and v_bar_i.  So the rows are spread over the lanes with
 // no exchange beyond a sum along each row, and the kernel streams the float32 memory at HBM
 // speed: each lane holds four consecutive key columns of a row (one 16-byte load and store),
-// a row is a group of d_k/4 adjacent lanes, and a workgroup covers consecutive rows.
+// a row is a group of d_k/4 adjacent lanes, and a workgroup covers consecutive rows.  Four rows
+// per lane keep four 16-byte loads in flight per lane (measured faster than one or two rows,
+// and than non-temporal loads and stores of the memory).
 #include "chunk.hpp"
 #include "launch.hpp"
 
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q
                                                 E* __restrict__ o) {
   constexpr int LPR = D / 4;          // lanes per row
   constexpr int GROUPS = 256 / LPR;   // rows in flight per workgroup pass
-  constexpr int RPT = 2;              // rows per lane
+  constexpr int RPT = 4;              // rows per lane
   constexpr int RPB = GROUPS * RPT;   // rows per workgroup
   constexpr int NRB = D / RPB;        // workgroups per memory
   static_assert(D % RPB == 0, "row blocks tile the memory");
@@ -105,7 +107,7 @@ namespace {
 
 template <typename E, int D>
 hipError_t launch_decode_t(const Geo& g, int variant, const gdr_inputs& in, float* state, void* o, hipStream_t st) {
-  constexpr int RPB = 2 * 256 / (D / 4);
+  constexpr int RPB = 4 * 256 / (D / 4);
   const long blocks = (long)g.nseq * g.H * (D / RPB);
   if (blocks == 0) return hipSuccess;
   auto go = [&](auto kern) {

@@ -72,9 +72,9 @@ WORKLOADS = {
 }
 # Decoding: one new token per sequence against a batch of memories (the recurrent form).  Not
 # a workload of the operator study (the pages give no inference benchmark); sized so the
-# float32 memories (256 MiB) exceed the GPU's 256 MiB last-level cache.
+# float32 memories (512 MiB) are twice the GPU's 256 MiB last-level cache.
 DECODE_WORKLOADS = {
-    "gated_decode_B256H16": Workload("gated_decode_B256H16", "gated", "bf16", 256, 16, 1, 128, 128,
+    "gated_decode_B512H16": Workload("gated_decode_B512H16", "gated", "bf16", 512, 16, 1, 128, 128,
                                      seed=5, backward=False, h0_std=0.02),
 }
 SWEEP = [Workload(f"gated_B{b}H16T{t}", "gated", "bf16", b, 16, t, 128, 128, seed=1)

@@ -99,9 +99,9 @@ def test_decode_zero_tokens_is_a_no_op():
 
 
 def test_decode_fullsize():
-    """The timed decoding workload (B=256 sequences x 16 heads, one token each, d=128), every
+    """The timed decoding workload (B=512 sequences x 16 heads, one token each, d=128), every
     memory and output compared with the oracle."""
-    w = synth.DECODE_WORKLOADS["gated_decode_B256H16"]
+    w = synth.DECODE_WORKLOADS["gated_decode_B512H16"]
     inp = synth.make_inputs(w)
     o, ht = _decode(inp, w.variant, w.dtype, inp["h0"])
     ro, rht = _oracle(inp, w.variant, inp["h0"])

@@ -220,3 +220,28 @@ def test_segmented_matches_unsegmented(segments):
         if a[name] is not None:
             err = np.max(np.abs(a[name] - b[name]))
             assert err <= 1e-4 * max(1e-30, np.max(np.abs(a[name]))), (name, err)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_gdn2_erase_free_is_decayed_linear_attention(dtype, d):
+    """Gated DeltaNet-2 with the erase gate closed (e = 0) is the erase-free decayed memory
+    W <- alpha W + (beta w*v) k^T (RetNet-style scalar decay with a per-value write gate).  The
+    HIP path is checked against the float64 recurrence and, independently, against the closed
+    form of causal decayed linear attention computed here in float64."""
+    w = synth.Workload("g2e0", "gdn2", dtype, 2, 2, 150, d, d, seed=51, h0_std=0.1)
+    inp = synth.make_inputs(w, alpha_mode="weak")
+    inp["erase"] = np.zeros_like(inp["erase"])
+    got = run_hip(inp, "gdn2", dtype, backward=True)
+    ref = run_oracle(inp, "gdn2", backward=True)
+    compare(got, ref, dtype)
+    # closed form: o_t = Gamma_t W0 q_t + sum_{s<=t} (gamma_t/gamma_s) (k_s . q_t) beta_s (w_s*v_s)
+    for b in range(2):
+        for h in range(2):
+            logg = np.cumsum(np.log(inp["alpha"][b, h].astype(np.float64)))
+            Q = inp["q"][b, h].astype(np.float64)
+            K = inp["k"][b, h].astype(np.float64)
+            Bv = (inp["beta"][b, h][:, None] * inp["write"][b, h] * inp["v"][b, h]).astype(np.float64)
+            Dm = np.tril(np.exp(logg[:, None] - logg[None, :]))
+            want = (Dm * (Q @ K.T)) @ Bv + np.exp(logg)[:, None] * (Q @ inp["h0"][b, h].astype(np.float64).T)
+            tol = 1e-4 * np.max(np.abs(want)) if dtype == "f32" else 2e-2 * max(1.0, np.max(np.abs(want)))
+            assert np.max(np.abs(got["o"][b, h] - want)) <= tol
