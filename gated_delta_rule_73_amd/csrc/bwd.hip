@@ -322,7 +322,9 @@ struct BwdLds {
 
 
 // RES: the residual r = R / beta was an output; dbeta gains -(dr . r) / beta = -(dr . R) / beta^2.
-template <typename E, int D, int VAR, bool RES>
+// LOG: beta and alpha are logits x; the gradients returned are w.r.t. x:
+// dx_beta = dbeta beta (1 - beta), dx_alpha = d log(alpha) * (-sigmoid(x_alpha)).
+template <typename E, int D, int VAR, bool RES, bool LOG>
 __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ v, const E* __restrict__ beta,
                                                    const E* __restrict__ alpha, const E* __restrict__ dO,
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     if (threadIdx.x < CH) {
       const int t = threadIdx.x;
       gs[t] = Gg[u * CH + t];
-      bs[t] = (t < n) ? (float)beta[tk + t] : 0.f;
+      bs[t] = (t < n) ? (LOG ? gate_sigmoid((float)beta[tk + t]) : (float)beta[tk + t]) : 0.f;
     }
     for (int ih = 0; ih < NH; ++ih) {
       __syncthreads();
@@ -720,7 +722,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
       for (int i = 0; i < NT / 64; ++i) g4 += red[i];
       const float dla = rect + suf + pre + expf(gn) * g4;
-      if (t < n) dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
+      if (t < n) {
+        if constexpr (LOG) dalpha[tk + t] = (E)(-dla * gate_sigmoid((float)alpha[tk + t]));
+        else dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
+      }
     }
     float db = 0.f;
 #pragma unroll
@@ -731,6 +736,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
         db -= rdr[t] * bi * bi;
       }
     }
+    if constexpr (LOG) db *= bs[t] * (1.f - bs[t]);
     if (t < n) dbeta[tk + t] = (E)db;
   }
   __syncthreads();
@@ -795,8 +801,9 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
                            (const float*)p.G, (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR, p.A1,
                            p.Li, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta, (E*)gr.dalpha, drp);
       };
-      if (drp) chunk(k_bwd_chunk<E, D, VAR, true>);
-      else chunk(k_bwd_chunk<E, D, VAR, false>);
+      if (drp) chunk(k_bwd_chunk<E, D, VAR, true, false>);
+      else if (p.gates) chunk(k_bwd_chunk<E, D, VAR, false, true>);
+      else chunk(k_bwd_chunk<E, D, VAR, false, false>);
     }
   }
   return hipGetLastError();

@@ -376,6 +376,11 @@ __device__ __forceinline__ void s2g_full(S* g, long gs, const S* lds, int ld) {
 // ---------------------------------------------------------------------------------------
 // Problem geometry
 // ---------------------------------------------------------------------------------------
+// Gates given as logits x (the problem's gates == 1): beta = sigmoid(x), alpha = exp(-softplus(x)),
+// so log alpha = -softplus(x) comes without rounding alpha first.
+__device__ __forceinline__ float gate_sigmoid(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float gate_neg_softplus(float x) { return -(fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)))); }
+
 struct Geo {
   int B, H, T;        // batch, heads, tokens
   int nseq;           // independent sequences (B, or packed count)

@@ -42,7 +42,8 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a
 }  // namespace
 
 // Grid: one workgroup per (memory, block of RPB value rows), memory = sequence * H + head.
-template <typename E, int D, int VAR>
+// LOG: beta and alpha are logits (beta = sigmoid(x), alpha = exp(-softplus(x))).
+template <typename E, int D, int VAR, bool LOG>
 __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                 const E* __restrict__ v, const E* __restrict__ beta,
                                                 const E* __restrict__ alpha, const E* __restrict__ erase,
@@ -76,12 +77,13 @@ __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q
     const long tk = tok_index(geo, b, h, bos + t);
     const f32x4 kt = load4(k + tk * D + j0);
     const f32x4 qt = load4(q + tk * D + j0);
-    const float bt = beta ? (float)beta[tk] : 1.f;
+    float bt = beta ? (float)beta[tk] : 1.f;
+    if constexpr (LOG) bt = gate_sigmoid(bt);
     f32x4 dec = {1.f, 1.f, 1.f, 1.f};
     if constexpr (VAR == VAR_KDA) {
       dec = load4(alpha + tk * D + j0);
     } else if constexpr (VAR != VAR_DELTANET) {
-      const float a = (float)alpha[tk];
+      const float a = LOG ? expf(gate_neg_softplus((float)alpha[tk])) : (float)alpha[tk];
       dec = f32x4{a, a, a, a};
     }
     f32x4 ek = kt;  // direction along which the prediction is erased: beta (e*k), or beta k
@@ -106,7 +108,8 @@ __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q
 namespace {
 
 template <typename E, int D>
-hipError_t launch_decode_t(const Geo& g, int variant, const gdr_inputs& in, float* state, void* o, hipStream_t st) {
+hipError_t launch_decode_t(const Geo& g, int variant, int gates, const gdr_inputs& in, float* state, void* o,
+                           hipStream_t st) {
   constexpr int RPB = 4 * 256 / (D / 4);
   const long blocks = (long)g.nseq * g.H * (D / RPB);
   if (blocks == 0) return hipSuccess;
@@ -117,24 +120,28 @@ hipError_t launch_decode_t(const Geo& g, int variant, const gdr_inputs& in, floa
                        (const E*)in.write, state, (E*)o);
     return hipGetLastError();
   };
+  if (gates) {  // logits: Delta family only (checked by the caller)
+    if (variant == GDR_DELTANET) return go(k_decode<E, D, VAR_DELTANET, true>);
+    return go(k_decode<E, D, VAR_GATED, true>);
+  }
   switch (variant) {
-    case GDR_DELTANET: return go(k_decode<E, D, VAR_DELTANET>);
-    case GDR_GATED: return go(k_decode<E, D, VAR_GATED>);
-    case GDR_KDA: return go(k_decode<E, D, VAR_KDA>);
-    default: return go(k_decode<E, D, VAR_GDN2>);
+    case GDR_DELTANET: return go(k_decode<E, D, VAR_DELTANET, false>);
+    case GDR_GATED: return go(k_decode<E, D, VAR_GATED, false>);
+    case GDR_KDA: return go(k_decode<E, D, VAR_KDA, false>);
+    default: return go(k_decode<E, D, VAR_GDN2, false>);
   }
 }
 
 }  // namespace
 
-hipError_t run_decode(const Geo& g, int variant, int dtype, int D, const gdr_inputs& in, float* state, void* o,
-                      hipStream_t st) {
+hipError_t run_decode(const Geo& g, int variant, int gates, int dtype, int D, const gdr_inputs& in, float* state,
+                      void* o, hipStream_t st) {
   if (dtype == GDR_BF16) {
-    return D == 64 ? launch_decode_t<bf16, 64>(g, variant, in, state, o, st)
-                   : launch_decode_t<bf16, 128>(g, variant, in, state, o, st);
+    return D == 64 ? launch_decode_t<bf16, 64>(g, variant, gates, in, state, o, st)
+                   : launch_decode_t<bf16, 128>(g, variant, gates, in, state, o, st);
   }
-  return D == 64 ? launch_decode_t<float, 64>(g, variant, in, state, o, st)
-                 : launch_decode_t<float, 128>(g, variant, in, state, o, st);
+  return D == 64 ? launch_decode_t<float, 64>(g, variant, gates, in, state, o, st)
+                 : launch_decode_t<float, 128>(g, variant, gates, in, state, o, st);
 }
 
 }  // namespace gdr

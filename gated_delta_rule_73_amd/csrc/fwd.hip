@@ -20,7 +20,8 @@ namespace gdr {
 // ---------------------------------------------------------------------------------------
 // Prep: per (head, chunk) -- g, M, L^{-1}, X, U.
 // ---------------------------------------------------------------------------------------
-template <typename E, int D, int VAR>
+// LOG: beta and alpha are logits (beta = sigmoid(x), log alpha = -softplus(x)).
+template <typename E, int D, int VAR, bool LOG>
 __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ v, const E* __restrict__ beta,
                                                   const E* __restrict__ alpha, E* __restrict__ Xo,
@@ -50,9 +51,14 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
     const bool ok = t < cp.n;
-    bs[t] = ok ? (float)beta[tk + t] : 0.f;
     float la = 0.f;
-    if constexpr (VAR == VAR_GATED) la = ok ? logf((float)alpha[tk + t]) : 0.f;
+    if constexpr (LOG) {
+      bs[t] = ok ? gate_sigmoid((float)beta[tk + t]) : 0.f;
+      if constexpr (VAR == VAR_GATED) la = ok ? gate_neg_softplus((float)alpha[tk + t]) : 0.f;
+    } else {
+      bs[t] = ok ? (float)beta[tk + t] : 0.f;
+      if constexpr (VAR == VAR_GATED) la = ok ? logf((float)alpha[tk + t]) : 0.f;
+    }
     const float g = wave_incl_scan(la);
     gs[t] = g;
     Go[u * CH + t] = g;
@@ -454,9 +460,12 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
       if (e != hipSuccess) return e;
     } else {
       TraceScope ts_("fwd_prep", st);
-      hipLaunchKernelGGL((k_fwd_prep<E, D, VAR>), cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k,
-                         (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G,
-                         p.Li, p.A1);
+      auto prep = [&](auto kern) {
+        hipLaunchKernelGGL(kern, cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k, (const E*)in.v,
+                           (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G, p.Li, p.A1);
+      };
+      if (p.gates) prep(k_fwd_prep<E, D, VAR, true>);
+      else prep(k_fwd_prep<E, D, VAR, false>);
     }
   }
   constexpr bool KDA = VAR == VAR_KDA;

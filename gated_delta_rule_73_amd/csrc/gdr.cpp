@@ -85,6 +85,9 @@ gdr_status check_shape(const gdr_problem* p, long long* total_chunks_out, int* m
   if (!std::isfinite(p->scale)) return fail(GDR_ERR_INVALID_ARG, "scale must be finite");
   if (p->n_seqs < 0) return fail(GDR_ERR_INVALID_ARG, "n_seqs must be >= 0");
   if (p->H > 65535) return fail(GDR_ERR_UNSUPPORTED, "H > 65535 is not supported");
+  if (p->gates != 0 && p->gates != 1) return fail(GDR_ERR_INVALID_ARG, "gates must be 0 (values) or 1 (logits)");
+  if (p->gates && p->variant != GDR_DELTANET && p->variant != GDR_GATED)
+    return fail(GDR_ERR_UNSUPPORTED, "gates given as logits are built for DeltaNet and Gated DeltaNet");
   long long total_chunks = 0;
   int max_chunks = 0;
   if (p->n_seqs > 0) {
@@ -198,6 +201,7 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
   pl.geo.scale = p->scale;
   pl.variant = p->variant;
   pl.dtype = p->dtype;
+  pl.gates = p->gates;
   pl.D = p->dk;
   pl.bv = s.bv;
   pl.lseg = s.lseg;
@@ -304,6 +308,7 @@ gdr_status gdr_forward_residual(const gdr_problem* p, const gdr_inputs* in, void
     return fail(GDR_ERR_INVALID_ARG, "o/r/ht must be 16-byte and saved 256-byte aligned");
   if (r && p->variant == GDR_GDN2)
     return fail(GDR_ERR_UNSUPPORTED, "the residual output is defined for the delta family and Kimi Delta Attention");
+  if (r && p->gates) return fail(GDR_ERR_UNSUPPORTED, "the residual output takes gate values, not logits");
   if ((st = check_ws(ws, ws_bytes, s.cache() + s.fwd_ws())) != GDR_OK) return st;
   char* cache = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + s.fwd_ws();
   gdr::Plan pl = make_plan(p, s, cache, static_cast<char*>(ws), false);
@@ -332,6 +337,7 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
   // small beta.  float32 I/O keeps them accurate.
   if (dr && p->dtype != GDR_F32)
     return fail(GDR_ERR_UNSUPPORTED, "the residual gradient is built for float32 I/O only");
+  if (dr && p->gates) return fail(GDR_ERR_UNSUPPORTED, "the residual gradient takes gate values, not logits");
   if (dr && !aligned(dr, 16)) return fail(GDR_ERR_INVALID_ARG, "dr must be 16-byte aligned");
   if (p->T > 0) {
     if (!dO) return fail(GDR_ERR_INVALID_ARG, "dO is required");
@@ -390,7 +396,8 @@ gdr_status gdr_decode(const gdr_problem* p, const gdr_inputs* in, float* state, 
   g.scale = p->scale;
   g_last_error.clear();
   TraceCall tc;
-  return hip_status(gdr::run_decode(g, p->variant, p->dtype, p->dk, *in, state, o, static_cast<hipStream_t>(stream)),
+  return hip_status(gdr::run_decode(g, p->variant, p->gates, p->dtype, p->dk, *in, state, o,
+                                    static_cast<hipStream_t>(stream)),
                     "gdr_decode launch");
 }
 

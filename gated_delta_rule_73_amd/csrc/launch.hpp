@@ -13,6 +13,7 @@ namespace gdr {
 struct Plan {
   Geo geo;
   int variant, dtype, D, bv;
+  int gates;          // 1: beta and alpha are logits (Delta family)
   int lseg, max_seg;  // segmented scans: chunks per segment (0: off), largest segment count
   float* seg_maps;    // [memories][max_seg][2][D][D] float32 (workspace)
   float* seg_starts;  // [memories][max_seg][D][D] float32 (workspace)
@@ -86,8 +87,8 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
 hipError_t launch_seg_combine(const Plan& p, const ScanSeg& sg, const float* init, bool reverse, hipStream_t st);
 
 // Recurrent form over every sequence's tokens, memory updated in place (decoding).
-hipError_t run_decode(const Geo& g, int variant, int dtype, int D, const gdr_inputs& in, float* state, void* o,
-                      hipStream_t st);
+hipError_t run_decode(const Geo& g, int variant, int gates, int dtype, int D, const gdr_inputs& in, float* state,
+                      void* o, hipStream_t st);
 // r: optional residual output (Delta family and Kimi Delta Attention); dr: optional gradient
 // w.r.t. it (Delta family).  Both may be NULL.
 hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, void* r, float* ht, bool want_out,

@@ -71,6 +71,12 @@ typedef struct {
   const int32_t *cu_seqlens_host; /* n_seqs+1 offsets: [0] = 0, [n_seqs] = T, non-decreasing */
   const int32_t *cu_seqlens_dev;  /* the same offsets in device memory (read by kernels) */
   float scale;                    /* o = scale * W q; finite */
+  int32_t gates;                  /* 0: beta, alpha are the gate values.  1: they are logits x,
+                                     beta = sigmoid(x), alpha = exp(-softplus(x)) (the gate laws of
+                                     the operator's workloads), applied inside the kernels, and
+                                     dbeta, dalpha are gradients w.r.t. x.  1 is built for
+                                     GDR_DELTANET and GDR_GATED (gdr_forward, gdr_backward,
+                                     gdr_decode; not with a residual output or gradient) */
 } gdr_problem;
 
 typedef struct {

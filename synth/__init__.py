@@ -119,8 +119,12 @@ def _l2norm(x):
 
 
 def make_inputs(w: Workload, *, alpha_mode: str = "config", with_grad: Optional[bool] = None,
-                seed: Optional[int] = None, T: Optional[int] = None) -> dict:
+                seed: Optional[int] = None, T: Optional[int] = None, gate_logits: bool = False) -> dict:
     """Draw one workload's inputs.
+
+    gate_logits: return beta and alpha as the logits drawn for them (N(0,1), and N(0,1) plus
+    the alpha_mode's shift), rounded to the I/O precision, instead of the gate values; the
+    consumer applies sigmoid / exp(-softplus).  Same draws, same order.
 
     alpha_mode: "config" -> alpha = exp(-softplus(N(0,1) + 2)) (the workloads' law);
                 "weak"   -> alpha = exp(-softplus(N(0,1) - 5)) (about 0.99: long memory);
@@ -139,16 +143,20 @@ def make_inputs(w: Workload, *, alpha_mode: str = "config", with_grad: Optional[
     out["q"] = to_io(_l2norm(rng.standard_normal((B, H, T, dk))), w.dtype)
     out["k"] = to_io(_l2norm(rng.standard_normal((B, H, T, dk))), w.dtype)
     out["v"] = to_io(rng.standard_normal((B, H, T, dv)), w.dtype)
-    out["beta"] = to_io(_sigmoid(rng.standard_normal((B, H, T))), w.dtype) if w.has_beta else None
+    act_b = (lambda x: x) if gate_logits else _sigmoid
+    out["beta"] = to_io(act_b(rng.standard_normal((B, H, T))), w.dtype) if w.has_beta else None
     if w.variant == "deltanet":
         out["alpha"] = None
     else:
         shape = (B, H, T, dk) if w.variant == "kda" else (B, H, T)
         if alpha_mode == "one":
+            if gate_logits:
+                raise ValueError("alpha = 1 has no finite logit")
             out["alpha"] = np.ones(shape, np.float32)
         else:
             shift = {"config": 2.0, "weak": -5.0, "strong": 6.0}[alpha_mode]
-            out["alpha"] = to_io(np.exp(-_softplus(rng.standard_normal(shape) + shift)), w.dtype)
+            x = rng.standard_normal(shape) + shift
+            out["alpha"] = to_io(x if gate_logits else np.exp(-_softplus(x)), w.dtype)
     if w.variant == "gdn2":
         out["erase"] = to_io(_sigmoid(rng.standard_normal((B, H, T, dk))), w.dtype)
         out["write"] = to_io(_sigmoid(rng.standard_normal((B, H, T, dv))), w.dtype)
