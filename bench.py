@@ -122,9 +122,11 @@ def cpu_baseline(w):
 
 
 class Runner:
-    """Holds the device buffers of one workload and calls the C ABI directly."""
+    """Holds the device buffers of one workload and calls the C ABI directly.  residual: the
+    forward also writes r = v - v_bar (gdr_forward_residual); gate_logits: beta and alpha are
+    logits, activated inside the kernels."""
 
-    def __init__(self, w, inp):
+    def __init__(self, w, inp, residual: bool = False, gate_logits: bool = False):
         import torch
 
         from gated_delta_rule_73_amd import binding as bd
@@ -135,10 +137,12 @@ class Runner:
         g = gpu_inputs(inp, w.dtype)
         self.g = g
         self.do = to_gpu(inp["do"], w.dtype)
-        self.p, self.keep = bd.make_problem(g["q"], g["v"], variant=w.variant, cu_seqlens=inp.get("cu_seqlens"))
+        self.p, self.keep = bd.make_problem(g["q"], g["v"], variant=w.variant, cu_seqlens=inp.get("cu_seqlens"),
+                                            gate_logits=gate_logits)
         N = self.p.n_seqs if self.p.n_seqs > 0 else self.p.B
         dev = g["q"].device
         self.o = torch.empty_like(g["v"])
+        self.r = torch.empty_like(g["v"]) if residual else None
         self.ht = torch.empty((N, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
         self.saved = torch.empty(bd.gdr_saved_size(self.p), dtype=torch.uint8, device=dev)
         nws = bd.gdr_workspace_size(self.p, True)
@@ -152,9 +156,10 @@ class Runner:
         self.stream = torch.cuda.current_stream().cuda_stream
 
     def fwd(self):
-        st = self.lib.gdr_forward(ctypes.byref(self.p), ctypes.byref(self.ins), self.o.data_ptr(),
-                                  self.ht.data_ptr(), self.saved.data_ptr(), self.ws.data_ptr(),
-                                  self.ws.numel(), self.stream)
+        st = self.lib.gdr_forward_residual(ctypes.byref(self.p), ctypes.byref(self.ins), self.o.data_ptr(),
+                                           None if self.r is None else self.r.data_ptr(), self.ht.data_ptr(),
+                                           self.saved.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+                                           self.stream)
         self.bd._check(self.lib, st)
 
     def bwd(self):
@@ -304,6 +309,8 @@ def main():
     ap.add_argument("--workload", default="gated_varlen_T32768")
     ap.add_argument("--sweep", action="store_true", help="also time the T = 4k..32k sweep at B*T = 32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--residual", action="store_true", help="the forward also writes the residual r = v - v_bar")
+    ap.add_argument("--gate-logits", action="store_true", help="beta and alpha given as logits")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -319,8 +326,8 @@ def main():
         return
     w = synth.WORKLOADS.get(args.workload) or {s.name: s for s in synth.SWEEP}[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(w)
-    runner = Runner(w, inp)
+    inp = synth.make_inputs(w, gate_logits=args.gate_logits)
+    runner = Runner(w, inp, residual=args.residual, gate_logits=args.gate_logits)
     del inp
     # A plain device copy of known size: its HBM counters calibrate the kernels' counters.
     src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda")
@@ -354,7 +361,8 @@ def main():
         "dtype": w.dtype, "data": "synthetic (seeded; distributions of the workload definition)",
         "config": {"workload": w.name, "variant": w.variant, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk,
                    "d_v": w.dv, "chunk": w.chunk, "cu_seqlens": list(w.cu_seqlens) if w.cu_seqlens else None,
-                   "initial_state": w.h0_std > 0},
+                   "initial_state": w.h0_std > 0, "residual_output": args.residual,
+                   "gate_logits": args.gate_logits},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_ms": round(avg_ms, 4), "launches": launches,
