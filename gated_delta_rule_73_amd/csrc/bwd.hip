@@ -35,9 +35,10 @@ struct BwdScanOps {
   RegTile<E, CH, BV, 256> dO;
   float g;
   // gradient w.r.t. the residual output (used with RES): this lane's four columns of each
-  // value tile of its chunk row, and 1 / beta of that row
-  f32x4 dr[BV / 16];
-  float binv;
+  // value tile of its chunk row, and beta of that row, both as loaded (from a valid row; masked
+  // and converted where the step uses them, so the loads are never waited for early)
+  typename VecT<4 * sizeof(E)>::type dr[BV / 16];
+  E braw;
 };
 template <typename E, int D, int BV>
 struct BwdScanOps<E, D, BV, VAR_GDN2> {
@@ -151,16 +152,12 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
       }
       if constexpr (RES) {  // accumulator layout of dR^T: row 16 w + lrow, columns 16 it + 4 lgrp
-        const int t = 16 * w + lrow();
-        const bool ok = t < n && !virt;
-        p.binv = ok ? 1.f / (float)beta[tk + t] : 0.f;
+        const int t = min(16 * w + lrow(), n - 1);
+        p.braw = beta[tk + t];
 #pragma unroll
-        for (int it = 0; it < NI; ++it) {
-          const E* src = drin + (tk + (ok ? t : 0)) * D + i0 + 16 * it + 4 * lgrp();
-          f32x4 x = zero4();
-          if (ok) x = get4(src);
-          p.dr[it] = x;
-        }
+        for (int it = 0; it < NI; ++it)
+          p.dr[it] = *reinterpret_cast<const typename VecT<4 * sizeof(E)>::type*>(drin + (tk + t) * D + i0 + 16 * it +
+                                                                                 4 * lgrp());
       }
       if constexpr (G2) {
         p.e.load(erase + tk * D, D, n);
@@ -171,6 +168,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   };
   auto step = [&](int c, Ops& p) {
     const long u = (long)(sp.gc0 + c) * geo.H + h;
+    [[maybe_unused]] const int n = min(CH, sp.len - c * CH);
     p.q.store(Qs, LD);
     p.k.store(Ks, LD);
     p.x.store(Xs, LD);
@@ -240,7 +238,12 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
       const f32x4 a1 = mma_k<E, CH>(zero4(), colk(dOt, LDO), 16 * it, colk(Ms, LDR), 16 * w);
       const f32x4 a2 = mma_k<E, D>(zero4(), rowk(dWs, LD), 16 * it, rowk(G2 ? As : Ks, LD), 16 * w);
       f32x4 dr = a1 + dec * a2;
-      if constexpr (RES) dr += p.binv * p.dr[it];
+      if constexpr (RES) {  // + dr / beta for the rows of this chunk (none for the linear part)
+        const bool ok = tl < n && !virt;
+        const float binv = ok ? 1.f / (float)p.braw : 0.f;
+        const E* x = reinterpret_cast<const E*>(&p.dr[it]);
+        dr += binv * f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+      }
       const int c4 = 16 * it + 4 * lgrp();
       put4(dRt + tl * LDO + c4, -dr);
       put4(dRn + tl * LDV + c4, dr);

@@ -178,6 +178,7 @@ struct FwdScanOps {
   RegTile<E, CH, CH, 256> m, m2;
   float g, b;
   f32x4 eg[D / 64];
+  E braw;  // residual output: beta of this lane's token, as loaded (converted where it is used)
 };
 
 template <typename E, int D, int BV, int VAR, bool FULL, bool RES>
@@ -287,9 +288,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         p.k.load(k + tk * D, D, n);
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
       }
-      if constexpr (RES) {
+      if constexpr (RES) {  // a plain load (valid row), no arithmetic on it until the step uses it
         const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
-        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? 1.f / (float)beta[tk + t] : 0.f;
+        p.braw = beta[tk + t];
       }
       if constexpr (G2) {
         p.e.load(erase + tk * D, D, n);
@@ -319,8 +320,11 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     } else {
       if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
     }
-    if constexpr (G2 || RES) {  // GDN-2: beta; residual output: 1 / beta (0 past the end)
+    if constexpr (G2) {
       if (threadIdx.x < CH) bsh[threadIdx.x] = p.b;
+    }
+    if constexpr (RES) {  // residual output: 1 / beta (0 past the end)
+      if (threadIdx.x < CH) bsh[threadIdx.x] = ((int)threadIdx.x < n) ? 1.f / (float)p.braw : 0.f;
     }
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
