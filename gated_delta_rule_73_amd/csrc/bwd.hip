@@ -377,6 +377,15 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   RegTile<E, CH, D, NT> pV, pQ;       // V and Q, used in later phases
   RegTile<E, CH, CH, NT> pM;          // M, used for the decay gradient
   RegTile<float, CH, CH, NT> pA, pLi;  // the forward's A and L^{-1}, used in phase 2
+  // The per-token decay and beta are loaded before the tiles and staged after the first tile
+  // stores: waiting for them then waits for nothing else, where loaded after the tiles they
+  // would make the staging wait for every tile in flight (the wait counters are ordered).
+  float graw = 0.f;
+  E braw = E(0.f);
+  if (threadIdx.x < CH) {
+    graw = Gg[u * CH + threadIdx.x];
+    braw = beta[tk + min((int)threadIdx.x, n - 1)];
+  }
   {
     E* dOs = reinterpret_cast<E*>(smem + Ly::odO);
     E* Rs = reinterpret_cast<E*>(smem + Ly::oR);
@@ -417,8 +426,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
     if (threadIdx.x < CH) {
       const int t = threadIdx.x;
-      gs[t] = Gg[u * CH + t];
-      bs[t] = (t < n) ? (LOG ? gate_sigmoid((float)beta[tk + t]) : (float)beta[tk + t]) : 0.f;
+      gs[t] = graw;
+      bs[t] = (t < n) ? (LOG ? gate_sigmoid((float)braw) : (float)braw) : 0.f;
     }
     for (int ih = 0; ih < NH; ++ih) {
       __syncthreads();

@@ -42,6 +42,15 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id();
 
+  // The gates are loaded before the tiles (plain loads of a valid token) and used after the
+  // K and Q stores: their waits then cover nothing the stores did not already need, where
+  // loaded after the tiles they would also wait for V.
+  E braw = E(0.f), araw = E(1.f);
+  if (threadIdx.x < CH) {
+    const int t = min((int)threadIdx.x, cp.n - 1);
+    braw = beta[tk + t];
+    if constexpr (VAR == VAR_GATED) araw = alpha[tk + t];
+  }
   RegTile<E, CH, D, NT> rk, rq, rv;
   rk.load(k + tk * D, D, cp.n);
   rq.load(q + tk * D, D, cp.n);
@@ -53,11 +62,11 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
     const bool ok = t < cp.n;
     float la = 0.f;
     if constexpr (LOG) {
-      bs[t] = ok ? gate_sigmoid((float)beta[tk + t]) : 0.f;
-      if constexpr (VAR == VAR_GATED) la = ok ? gate_neg_softplus((float)alpha[tk + t]) : 0.f;
+      bs[t] = ok ? gate_sigmoid((float)braw) : 0.f;
+      if constexpr (VAR == VAR_GATED) la = ok ? gate_neg_softplus((float)araw) : 0.f;
     } else {
-      bs[t] = ok ? (float)beta[tk + t] : 0.f;
-      if constexpr (VAR == VAR_GATED) la = ok ? logf((float)alpha[tk + t]) : 0.f;
+      bs[t] = ok ? (float)braw : 0.f;
+      if constexpr (VAR == VAR_GATED) la = ok ? logf((float)araw) : 0.f;
     }
     const float g = wave_incl_scan(la);
     gs[t] = g;
