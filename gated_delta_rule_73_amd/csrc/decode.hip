@@ -82,6 +82,10 @@ __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q
     f32x4 dec = {1.f, 1.f, 1.f, 1.f};
     if constexpr (VAR == VAR_KDA) {
       dec = load4(alpha + tk * D + j0);
+      if constexpr (LOG) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dec[x] = expf(gate_neg_softplus(dec[x]));
+      }
     } else if constexpr (VAR != VAR_DELTANET) {
       const float a = LOG ? expf(gate_neg_softplus((float)alpha[tk])) : (float)alpha[tk];
       dec = f32x4{a, a, a, a};
@@ -120,8 +124,9 @@ hipError_t launch_decode_t(const Geo& g, int variant, int gates, const gdr_input
                        (const E*)in.write, state, (E*)o);
     return hipGetLastError();
   };
-  if (gates) {  // logits: Delta family only (checked by the caller)
+  if (gates) {  // logits: not Gated DeltaNet-2 (checked by the caller)
     if (variant == GDR_DELTANET) return go(k_decode<E, D, VAR_DELTANET, true>);
+    if (variant == GDR_KDA) return go(k_decode<E, D, VAR_KDA, true>);
     return go(k_decode<E, D, VAR_GATED, true>);
   }
   switch (variant) {

@@ -86,8 +86,8 @@ gdr_status check_shape(const gdr_problem* p, long long* total_chunks_out, int* m
   if (p->n_seqs < 0) return fail(GDR_ERR_INVALID_ARG, "n_seqs must be >= 0");
   if (p->H > 65535) return fail(GDR_ERR_UNSUPPORTED, "H > 65535 is not supported");
   if (p->gates != 0 && p->gates != 1) return fail(GDR_ERR_INVALID_ARG, "gates must be 0 (values) or 1 (logits)");
-  if (p->gates && p->variant != GDR_DELTANET && p->variant != GDR_GATED)
-    return fail(GDR_ERR_UNSUPPORTED, "gates given as logits are built for DeltaNet and Gated DeltaNet");
+  if (p->gates && p->variant == GDR_GDN2)
+    return fail(GDR_ERR_UNSUPPORTED, "gates given as logits are built for DeltaNet, Gated DeltaNet and Kimi Delta Attention");
   long long total_chunks = 0;
   int max_chunks = 0;
   if (p->n_seqs > 0) {

@@ -31,14 +31,18 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // Gs[t*ldg + j] = sum_{u<=t} log alpha_{u,j}.  Each column is summed in four runs of 16 rows
 // whose totals are then carried in order, the same arithmetic in every kernel, so all of them
 // see the same values of g.  tot: 4*JW floats of scratch.  Ends with a block barrier.
-template <typename E, int JW, int NT>
+// LOG: the tile holds logits x, log alpha = -softplus(x).
+template <typename E, int JW, int NT, bool LOG>
 __device__ void kda_cumlog(const RegTile<E, CH, JW, NT>& ra, int n, float* Gs, int ldg, float* tot) {
 #pragma unroll
   for (int it = 0; it < RegTile<E, CH, JW, NT>::IT; ++it) {
     if (RegTile<E, CH, JW, NT>::TOTAL % NT == 0 || threadIdx.x + it * NT < RegTile<E, CH, JW, NT>::TOTAL) {
       const int t = ra.row(it), j = ra.col(it);
 #pragma unroll
-      for (int x = 0; x < RegTile<E, CH, JW, NT>::VE; ++x) Gs[t * ldg + j + x] = (t < n) ? logf((float)ra.elem(it, x)) : 0.f;
+      for (int x = 0; x < RegTile<E, CH, JW, NT>::VE; ++x) {
+        const float a = (float)ra.elem(it, x);
+        Gs[t * ldg + j + x] = (t < n) ? (LOG ? gate_neg_softplus(a) : logf(a)) : 0.f;
+      }
     }
   }
   __syncthreads();
@@ -198,7 +202,8 @@ struct KdaPrepLds {
   static_assert(CH * LDT * (int)sizeof(E) >= 4 * 256 * 4, "T doubles as the solve's scratch");
 };
 
-template <typename E, int D>
+// LOG: beta and alpha are logits (beta = sigmoid(x), log alpha = -softplus(x) per channel).
+template <typename E, int D, bool LOG>
 __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ v, const E* __restrict__ beta,
                                                       const E* __restrict__ alpha, E* __restrict__ Xo,
@@ -228,11 +233,14 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   rk.load(k + tk * D, D, n);
   rq.load(q + tk * D, D, n);
   rv.load(v + tk * D, D, n);
-  if (threadIdx.x < CH) bs[threadIdx.x] = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
+  if (threadIdx.x < CH) {
+    const float b = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
+    bs[threadIdx.x] = (LOG && threadIdx.x < n) ? gate_sigmoid(b) : b;
+  }
   if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
   rk.store(Ks, LD);
   rq.store(Qs, LD);
-  kda_cumlog<E, D, NT>(ra, n, Gs, LDG, tot);
+  kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG, tot);
   kda_flags<D, NT>(Gs, LDG, unsafe);
 
   // Kbar and Qhat for the scans, e^{g_n} per channel, and the row
@@ -427,7 +435,8 @@ struct KdaWyLds {
   static constexpr int oLb = END, oTb = END + SQ, BYTES = END + (BCOPY ? 2 * SQ : 0);
 };
 
-template <typename E, int D>
+// LOG: beta and alpha are logits; dbeta is returned w.r.t. the logit (times beta (1 - beta)).
+template <typename E, int D, bool LOG>
 __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
                                                     const E* __restrict__ beta, const E* __restrict__ alpha,
                                                     const E* __restrict__ dRg, E* __restrict__ dv,
@@ -459,9 +468,12 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   rdx.load(p.kd_dx + u * CH * D, D, CH);
   rli.load(p.Li + u * CH * CH, CH, CH);
   raf.load(p.A1 + u * CH * CH, CH, CH);
-  if (threadIdx.x < CH) bs[threadIdx.x] = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
+  if (threadIdx.x < CH) {
+    const float b = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
+    bs[threadIdx.x] = (LOG && threadIdx.x < n) ? gate_sigmoid(b) : b;
+  }
   rk.store(Ks, LD);
-  kda_cumlog<E, D, NT>(ra, n, Gs, LDG, tot);
+  kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG, tot);
   {  // Khat = e^g K in place, 16 bytes at a time
     constexpr int VE = 16 / (int)sizeof(E);
     for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
@@ -576,6 +588,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
     float db = 0.f;
 #pragma unroll
     for (int i = 0; i < NT / CH; ++i) db += partc[i][t] + partr[i][t];
+    if constexpr (LOG) db *= bs[t] * (1.f - bs[t]);
     if (t < n) dbeta[tk + t] = (E)db;
   }
 }
@@ -609,7 +622,8 @@ struct KdaGramLds {
   static constexpr int BYTES = cmax(endOps, oX + 2 * ST);
 };
 
-template <typename E, int D>
+// LOG: alpha holds logits; dalpha is returned w.r.t. them: d log alpha * (-sigmoid(x)).
+template <typename E, int D, bool LOG>
 __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ alpha, E* __restrict__ dq,
                                                       E* __restrict__ dk, E* __restrict__ dalpha, Plan p) {
@@ -657,7 +671,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
         dMs[t * LDT + s0 + x] = (E)rdm.elem(it, x);
       }
     }
-    kda_cumlog<E, JW, NT>(ra, n, Gs, LDF, tot);
+    kda_cumlog<E, JW, NT, LOG>(ra, n, Gs, LDF, tot);
   }
   kda_flags<JW, NT>(Gs, LDF, unsafe);
   // Kend_s = k_s e^{g_{16(J+1)} - g_s} (s in block J < 3);  Kf_u, Qf_u = (k_u, q_u) e^{g_u - g_{16I}}
@@ -941,7 +955,10 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
       const int t = 16 * b + i;
       const float dla = n4[i] + suf[i] + run + cross;
       run += S2[t * LDF + l];
-      if (t < n) dalpha[(tk + t) * D + j0 + l] = (E)(dla / la[i]);
+      if (t < n) {
+        if constexpr (LOG) dalpha[(tk + t) * D + j0 + l] = (E)(-dla * gate_sigmoid(la[i]));
+        else dalpha[(tk + t) * D + j0 + l] = (E)(dla / la[i]);
+      }
     }
   }
 }
@@ -952,9 +969,13 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
 template <typename E, int D>
 hipError_t launch_fwd_prep_kda(const Plan& p, const gdr_inputs& in, hipStream_t st) {
   TraceScope ts_("fwd_prep_kda", st);
-  hipLaunchKernelGGL((k_fwd_prep_kda<E, D>), dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo,
-                     (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
-                     (E*)p.X, (E*)p.Ub, (E*)p.M, (E*)p.Kb, (E*)p.Qh, p.Gn, p.Li, p.A1);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo, (const E*)in.q,
+                       (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub,
+                       (E*)p.M, (E*)p.Kb, (E*)p.Qh, p.Gn, p.Li, p.A1);
+  };
+  if (p.gates) go(k_fwd_prep_kda<E, D, true>);
+  else go(k_fwd_prep_kda<E, D, false>);
   return hipGetLastError();
 }
 template hipError_t launch_fwd_prep_kda<bf16, 128>(const Plan&, const gdr_inputs&, hipStream_t);
@@ -971,13 +992,21 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
   }
   {
     TraceScope ts_("bwd_kda_wy", st);
-    hipLaunchKernelGGL((k_bwd_kda_wy<E, D>), grid, dim3(256), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
-                       (const E*)in.beta, (const E*)in.alpha, (const E*)p.dR, (E*)gr.dv, (E*)gr.dbeta, p);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, p.geo, (const E*)in.k, (const E*)in.v, (const E*)in.beta,
+                         (const E*)in.alpha, (const E*)p.dR, (E*)gr.dv, (E*)gr.dbeta, p);
+    };
+    if (p.gates) go(k_bwd_kda_wy<E, D, true>);
+    else go(k_bwd_kda_wy<E, D, false>);
   }
   {
     TraceScope ts_("bwd_kda_gram", st);
-    hipLaunchKernelGGL((k_bwd_kda_gram<E, D>), dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(256), 0, st, p.geo,
-                       (const E*)in.q, (const E*)in.k, (const E*)in.alpha, (E*)gr.dq, (E*)gr.dk, (E*)gr.dalpha, p);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(256), 0, st, p.geo, (const E*)in.q,
+                         (const E*)in.k, (const E*)in.alpha, (E*)gr.dq, (E*)gr.dk, (E*)gr.dalpha, p);
+    };
+    if (p.gates) go(k_bwd_kda_gram<E, D, true>);
+    else go(k_bwd_kda_gram<E, D, false>);
   }
   return hipGetLastError();
 }

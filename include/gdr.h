@@ -75,8 +75,9 @@ typedef struct {
                                      beta = sigmoid(x), alpha = exp(-softplus(x)) (the gate laws of
                                      the operator's workloads), applied inside the kernels, and
                                      dbeta, dalpha are gradients w.r.t. x.  1 is built for
-                                     GDR_DELTANET and GDR_GATED (gdr_forward, gdr_backward,
-                                     gdr_decode; not with a residual output or gradient) */
+                                     GDR_DELTANET, GDR_GATED and GDR_KDA (alpha per channel)
+                                     (gdr_forward, gdr_backward, gdr_decode; not with a
+                                     residual output or gradient) */
 } gdr_problem;
 
 typedef struct {

@@ -61,7 +61,7 @@ def _hip(inp, variant, dtype, backward, use_saved=True, scale=1.0):
     return res
 
 
-CASES = [(v, dt, d, m, s) for v in ("deltanet", "gated") for dt, d in (("bf16", 128), ("f32", 64))
+CASES = [(v, dt, d, m, s) for v in ("deltanet", "gated", "kda") for dt, d in (("bf16", 128), ("f32", 64))
          for m in ("config", "weak") for s in (True, False)]
 
 
@@ -93,7 +93,7 @@ def test_gate_logits_packed_bench_shape_sample():
     compare(mine, ref, "bf16")
 
 
-@pytest.mark.parametrize("variant", ["deltanet", "gated"])
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda"])
 def test_gate_logits_decode(variant):
     import torch
     from gated_delta_rule_73_amd import gdr_decode
