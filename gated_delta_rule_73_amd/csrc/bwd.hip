@@ -48,6 +48,8 @@ struct BwdScanOps<E, D, BV, VAR_GDN2> {
   float g, b;
 };
 template <typename E, int D, int BV>
+struct BwdScanOps<E, D, BV, VAR_GDN2L> : BwdScanOps<E, D, BV, VAR_GDN2> {};
+template <typename E, int D, int BV>
 struct BwdScanOps<E, D, BV, VAR_KDA> {
   RegTile<E, CH, D, 256> q, k, x;
   RegTile<E, CH, CH, 256> m;
@@ -67,9 +69,10 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
                                                   const E* __restrict__ drin) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
-  constexpr bool G2 = VAR == VAR_GDN2;
+  constexpr bool G2 = VAR == VAR_GDN2 || VAR == VAR_GDN2L;
+  constexpr bool G2L = VAR == VAR_GDN2L;  // its gates are logits
   constexpr bool KDA = VAR == VAR_KDA;
-  constexpr bool DEC = VAR == VAR_GATED || VAR == VAR_GDN2;  // scalar decay
+  constexpr bool DEC = VAR == VAR_GATED || G2;  // scalar decay
   static_assert(!RES || VAR == VAR_DELTANET || VAR == VAR_GATED, "residual gradient: Delta family");
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];  // a = beta e*k (GDN-2)
   __shared__ float bsh[CH];
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
       if constexpr (G2) {
         p.e.load(erase + tk * D, D, n);
         const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
-        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? g2_gate<G2L>((float)beta[tk + t]) : 1.f) : 0.f;
       }
     }
   };
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
         typename RE::V av;
         E* ae = reinterpret_cast<E*>(&av);
 #pragma unroll
-        for (int x = 0; x < RE::VE; ++x) ae[x] = (E)(bt * (float)p.e.elem(it, x) * (float)p.k.elem(it, x));
+        for (int x = 0; x < RE::VE; ++x) ae[x] = (E)(bt * g2_gate<G2L>((float)p.e.elem(it, x)) * (float)p.k.elem(it, x));
         *reinterpret_cast<typename RE::V*>(As + t * LD + j0) = av;
       }
     }
@@ -801,7 +804,7 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
     scan(ScanSeg{2, p.lseg, p.max_seg, nullptr, p.seg_starts}, nullptr, gr.dh0, 1);
   }
   if (g.total_chunks > 0) {
-    if constexpr (VAR == VAR_GDN2) {
+    if constexpr (VAR == VAR_GDN2 || VAR == VAR_GDN2L) {
       return launch_bwd_gdn2<E, D>(p, in, dO, gr, st);
     } else if constexpr (VAR == VAR_KDA) {
       return launch_bwd_kda<E, D>(p, in, dO, gr, st);
@@ -833,7 +836,9 @@ hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, con
     case GDR_DELTANET: GDR_BWD_CASE(VAR_DELTANET)
     case GDR_GATED: GDR_BWD_CASE(VAR_GATED)
     case GDR_KDA: GDR_BWD_CASE(VAR_KDA)
-    case GDR_GDN2: GDR_BWD_CASE(VAR_GDN2)
+    case GDR_GDN2:
+      if (p.gates) { GDR_BWD_CASE(VAR_GDN2L) }
+      GDR_BWD_CASE(VAR_GDN2)
     default: break;
   }
 #undef GDR_BWD_CASE

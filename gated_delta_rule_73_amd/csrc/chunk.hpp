@@ -5,7 +5,8 @@
 
 namespace gdr {
 
-enum Var { VAR_DELTANET = 0, VAR_GATED = 1, VAR_KDA = 2, VAR_GDN2 = 3 };
+// VAR_GDN2L: Gated DeltaNet-2 with its gates (beta, alpha, erase, write) given as logits.
+enum Var { VAR_DELTANET = 0, VAR_GATED = 1, VAR_KDA = 2, VAR_GDN2 = 3, VAR_GDN2L = 4 };
 
 // Li = L^{-1} for a unit lower-triangular 64x64 float matrix L (only entries strictly below
 // the diagonal are read).  Blocked:

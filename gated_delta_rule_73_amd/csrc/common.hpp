@@ -380,7 +380,7 @@ __device__ __forceinline__ void s2g_full(S* g, long gs, const S* lds, int ld) {
 // so log alpha = -softplus(x) comes without rounding alpha first.  The hardware exp2/log2 paths
 // (absolute error about 1e-7 here, far below the bfloat16 step of the results) keep the
 // per-channel decay of Kimi Delta Attention, 64 x d_k values per chunk, as cheap as its log.
-__device__ __forceinline__ float gate_sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float gate_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 __device__ __forceinline__ float gate_neg_softplus(float x) {
   return -(fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x))));
 }
@@ -393,6 +393,13 @@ struct Geo {
   int total_chunks;   // sum over sequences of ceil(len / 64)
   float scale;
 };
+
+// Gated DeltaNet-2's gates: the value, or (LOG) sigmoid of the logit.
+template <bool LOG>
+__device__ __forceinline__ float g2_gate(float x) {
+  if constexpr (LOG) return gate_sigmoid(x);
+  else return x;
+}
 
 struct ChunkPos {
   int b, seq, t0, n;  // batch row, sequence, first token (within [0,T)), valid tokens

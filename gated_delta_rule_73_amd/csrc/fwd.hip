@@ -202,9 +202,10 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
                                                   E* __restrict__ rout) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
-  constexpr bool G2 = VAR == VAR_GDN2;
+  constexpr bool G2 = VAR == VAR_GDN2 || VAR == VAR_GDN2L;
+  constexpr bool G2L = VAR == VAR_GDN2L;  // its gates are logits
   constexpr bool KDA = VAR == VAR_KDA;
-  constexpr bool DEC = VAR == VAR_GATED || VAR == VAR_GDN2;  // scalar decay
+  constexpr bool DEC = VAR == VAR_GATED || G2;  // scalar decay
   constexpr bool OUT_G2 = FULL && G2;
   __shared__ __align__(16) E Xs[CH * LD];
   __shared__ __align__(16) E Ks[CH * LD];
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         p.vt.load(vin + tk * D + i0, D, n);
         p.wt.load(write + tk * D + i0, D, n);
         const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
-        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? g2_gate<G2L>((float)beta[tk + t]) : 1.f) : 0.f;
       }
     }
   };
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         typename RE::V av;
         E* ae = reinterpret_cast<E*>(&av);
 #pragma unroll
-        for (int x = 0; x < RE::VE; ++x) ae[x] = (E)(bt * (float)p.e.elem(it, x) * (float)p.k.elem(it, x));
+        for (int x = 0; x < RE::VE; ++x) ae[x] = (E)(bt * g2_gate<G2L>((float)p.e.elem(it, x)) * (float)p.k.elem(it, x));
         *reinterpret_cast<typename RE::V*>(As + t * LD + j0) = av;
       }
 #pragma unroll
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         E* bn = reinterpret_cast<E*>(&bnv);
 #pragma unroll
         for (int x = 0; x < RV::VE; ++x) {
-          const float bv = (float)p.wt.elem(it, x) * (float)p.vt.elem(it, x);
+          const float bv = g2_gate<G2L>((float)p.wt.elem(it, x)) * (float)p.vt.elem(it, x);
           Bd[(i + x) * LDR + t] = (E)(sc * bv);
           bn[x] = (E)(bt * bv);
         }
@@ -465,7 +466,7 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
   const Geo& g = p.geo;
   const dim3 cgrid(g.total_chunks, g.H);
   if (g.total_chunks > 0) {
-    if constexpr (VAR == VAR_GDN2) {
+    if constexpr (VAR == VAR_GDN2 || VAR == VAR_GDN2L) {
       const hipError_t e = launch_fwd_prep_gdn2<E, D>(p, in, st);
       if (e != hipSuccess) return e;
     } else if constexpr (VAR == VAR_KDA) {
@@ -495,7 +496,7 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
   };
   auto scan = [&](auto full, const ScanSeg& sg, const float* h0, float* htp) {
     constexpr bool F = decltype(full)::value;
-    constexpr bool RES_OK = F && VAR != VAR_GDN2;  // residual output: full pass, delta family and KDA
+    constexpr bool RES_OK = F && VAR != VAR_GDN2 && VAR != VAR_GDN2L;  // residual output: full pass, delta family and KDA
     const int nvm = F ? 1 : 2;
     if (std::is_same<E, float>::value || p.bv == 16) {
       if constexpr (RES_OK) {
@@ -537,7 +538,9 @@ hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, void* r, fl
     case GDR_DELTANET: GDR_FWD_CASE(VAR_DELTANET)
     case GDR_GATED: GDR_FWD_CASE(VAR_GATED)
     case GDR_KDA: GDR_FWD_CASE(VAR_KDA)
-    case GDR_GDN2: GDR_FWD_CASE(VAR_GDN2)
+    case GDR_GDN2:
+      if (p.gates) { GDR_FWD_CASE(VAR_GDN2L) }
+      GDR_FWD_CASE(VAR_GDN2)
     default: break;
   }
 #undef GDR_FWD_CASE

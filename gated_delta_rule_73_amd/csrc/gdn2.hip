@@ -16,7 +16,7 @@
 
 namespace gdr {
 
-template <typename E, int D>
+template <typename E, int D, bool LOG>
 __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                        const E* __restrict__ v, const E* __restrict__ beta,
                                                        const E* __restrict__ alpha, const E* __restrict__ erase,
@@ -46,8 +46,9 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
     const bool ok = t < n;
-    bs[t] = ok ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
-    const float la = ok ? logf((float)alpha[tk + t]) : 0.f;
+    bs[t] = ok ? (beta ? g2_gate<LOG>((float)beta[tk + t]) : 1.f) : 0.f;
+    const float xa = (float)alpha[tk + t];
+    const float la = ok ? (LOG ? gate_neg_softplus(xa) : logf(xa)) : 0.f;
     const float g = wave_incl_scan(la);
     gs[t] = g;
     Go[u * CH + t] = g;
@@ -71,8 +72,8 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
       const float bt = bs[t];
 #pragma unroll
       for (int x = 0; x < RT::VE; ++x) {
-        ae[x] = (E)(bt * (float)re.elem(it, x) * (float)rk.elem(it, x));
-        be[x] = (E)(bt * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+        ae[x] = (E)(bt * g2_gate<LOG>((float)re.elem(it, x)) * (float)rk.elem(it, x));
+        be[x] = (E)(bt * g2_gate<LOG>((float)rw.elem(it, x)) * (float)rv.elem(it, x));
       }
       *reinterpret_cast<typename RT::V*>(As + t * LD + j) = av;
       *reinterpret_cast<typename RT::V*>(Bs + t * LD + j) = bv;
@@ -183,7 +184,7 @@ struct G2StateLds {
   static constexpr int BYTES = 6 * TK + 2 * TH;
 };
 
-template <typename E, int D>
+template <typename E, int D, bool LOG>
 __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
                                                         const E* __restrict__ beta, const E* __restrict__ erase,
                                                         const E* __restrict__ write, const E* __restrict__ dO,
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
     gs[t] = Gg[u * CH + t];
-    bs[t] = t < n ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+    bs[t] = t < n ? (beta ? g2_gate<LOG>((float)beta[tk + t]) : 1.f) : 0.f;
   }
   {
     RegTile<E, CH, D, NT> rk, re, rv, rw;
@@ -240,8 +241,8 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
       const float bt = bs[t];
 #pragma unroll
       for (int x = 0; x < RT::VE; ++x) {
-        ae[x] = (E)(bt * (float)re.elem(it, x) * (float)rk.elem(it, x));
-        be[x] = (E)(bt * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+        ae[x] = (E)(bt * g2_gate<LOG>((float)re.elem(it, x)) * (float)rk.elem(it, x));
+        be[x] = (E)(bt * g2_gate<LOG>((float)rw.elem(it, x)) * (float)rv.elem(it, x));
       }
       *reinterpret_cast<typename RT::V*>(As + t * LD + j) = av;
       *reinterpret_cast<typename RT::V*>(Bs + t * LD + j) = bv;
@@ -370,7 +371,7 @@ struct G2WyLds {
   static constexpr int BYTES = TK + 3 * SQ + 4 * TK;
 };
 
-template <typename E, int D>
+template <typename E, int D, bool LOG>
 __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
                                                      const E* __restrict__ beta, const E* __restrict__ erase,
                                                      const E* __restrict__ write, const E* __restrict__ dO,
@@ -405,7 +406,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
     gs[t] = Gg[u * CH + t];
-    bs[t] = t < n ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+    bs[t] = t < n ? (beta ? g2_gate<LOG>((float)beta[tk + t]) : 1.f) : 0.f;
   }
   g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
   g2s_rows<E, CH, CH, NT>(Mqk, LDT, M2g + u * CH * CH, CH, CH);
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
       E* be = reinterpret_cast<E*>(&bv);
       const float bt = bs[t];
 #pragma unroll
-      for (int x = 0; x < RT::VE; ++x) be[x] = (E)(bt * (float)rw.elem(it, x) * (float)rv.elem(it, x));
+      for (int x = 0; x < RT::VE; ++x) be[x] = (E)(bt * g2_gate<LOG>((float)rw.elem(it, x)) * (float)rv.elem(it, x));
       *reinterpret_cast<typename RT::V*>(P3 + t * LD + i) = bv;
     }
     g2s_rows<E, CH, D, NT>(P4, LD, dO + tk * D, D, n);
@@ -526,8 +527,15 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
 #pragma unroll
     for (int nt = 0; nt < D / 16; ++nt) {
       const int i0 = 16 * nt + 4 * lgrp();
-      const f32x4 vv = get4(P1 + tr * LD + i0), ww = get4(P3 + tr * LD + i0);
-      const f32x4 ov = bt * ww * dbt[nt], ow = bt * vv * dbt[nt];
+      const f32x4 vv = get4(P1 + tr * LD + i0);
+      f32x4 ww = get4(P3 + tr * LD + i0);
+      if constexpr (LOG) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) ww[x] = gate_sigmoid(ww[x]);
+      }
+      const f32x4 ov = bt * ww * dbt[nt];
+      f32x4 ow = bt * vv * dbt[nt];
+      if constexpr (LOG) ow *= ww * (1.f - ww);  // gradient w.r.t. the write-gate logit
       part += ww[0] * vv[0] * dbt[nt][0] + ww[1] * vv[1] * dbt[nt][1] + ww[2] * vv[2] * dbt[nt][2] + ww[3] * vv[3] * dbt[nt][3];
       store4_t(P2, LD, 16 * nt, 16 * w, ov);
       store4_t(P4, LD, 16 * nt, 16 * w, ow);
@@ -561,7 +569,7 @@ struct G2GramLds {
   static constexpr int BYTES = 4 * TK + 4 * SQ + F;
 };
 
-template <typename E, int D>
+template <typename E, int D, bool LOG>
 __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                        const E* __restrict__ beta, const E* __restrict__ alpha,
                                                        const E* __restrict__ erase, const float* __restrict__ Gg,
@@ -591,7 +599,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
     gs[t] = Gg[u * CH + t];
-    bs[t] = t < n ? (beta ? (float)beta[tk + t] : 1.f) : 0.f;
+    bs[t] = t < n ? (beta ? g2_gate<LOG>((float)beta[tk + t]) : 1.f) : 0.f;
   }
   g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
   g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
@@ -627,9 +635,16 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
       uint4 av;
       E* ae = reinterpret_cast<E*>(&av);
       const float bt = bs[t];
+      uint4 gv;  // the erase gates themselves (sigmoid of the logits when logits are given)
+      E* ge = reinterpret_cast<E*>(&gv);
 #pragma unroll
-      for (int e = 0; e < VE; ++e) ae[e] = (E)(bt * (float)ee[e] * (float)ke[e]);
+      for (int e = 0; e < VE; ++e) {
+        const float ev_ = g2_gate<LOG>((float)ee[e]);
+        ge[e] = (E)ev_;
+        ae[e] = (E)(bt * ev_ * (float)ke[e]);
+      }
       *reinterpret_cast<uint4*>(As + t * LD + j0) = av;
+      if constexpr (LOG) *reinterpret_cast<uint4*>(Es + t * LD + j0) = gv;
     }
   }
   {  // decayed gradients of the chunk matrices and the pair terms, four columns at a time
@@ -699,6 +714,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
       ak[nt] += bt * da * ee;
       part += da[0] * ee[0] * kk[0] + da[1] * ee[1] * kk[1] + da[2] * ee[2] * kk[2] + da[3] * ee[3] * kk[3];
       aa[nt] = bt * da * kk;  // now de
+      if constexpr (LOG) aa[nt] *= ee * (1.f - ee);  // w.r.t. the erase-gate logit
     }
     part += __shfl_xor(part, 16, 64);
     part += __shfl_xor(part, 32, 64);
@@ -733,8 +749,13 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
     if (t == 0) pre = 0.f;
     const float dla = rect + suf + pre + rows[3 * CH];
     if (t < n) {
-      dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
-      if (dbeta) dbeta[tk + t] = (E)(rows[2 * CH + t] + re_[t >> 4][t]);
+      if constexpr (LOG) {  // w.r.t. the logits: d log alpha (-sigmoid(x_alpha)), dbeta beta (1 - beta)
+        dalpha[tk + t] = (E)(-dla * gate_sigmoid((float)alpha[tk + t]));
+        if (dbeta) dbeta[tk + t] = (E)((rows[2 * CH + t] + re_[t >> 4][t]) * bs[t] * (1.f - bs[t]));
+      } else {
+        dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
+        if (dbeta) dbeta[tk + t] = (E)(rows[2 * CH + t] + re_[t >> 4][t]);
+      }
     }
   }
   __syncthreads();
@@ -743,28 +764,33 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   s2g_rows<E, CH, D, NT>(derase + tk * D, D, As, LD, n);
 }
 
-template <typename E, int D>
-hipError_t launch_bwd_gdn2(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr, hipStream_t st) {
+template <typename E, int D, bool LOG>
+static hipError_t bwd_gdn2_impl(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr,
+                                hipStream_t st) {
   const dim3 grid(p.geo.total_chunks, p.geo.H);
   {
     TraceScope ts_("bwd_gdn2_state", st);
-    hipLaunchKernelGGL((k_bwd_gdn2_state<E, D>), grid, dim3(512), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
+    hipLaunchKernelGGL((k_bwd_gdn2_state<E, D, LOG>), grid, dim3(512), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
                        (const E*)in.beta, (const E*)in.erase, (const E*)in.write, (const E*)dO, (const float*)p.G,
                        (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR, p);
   }
   {
     TraceScope ts_("bwd_gdn2_wy", st);
-    hipLaunchKernelGGL((k_bwd_gdn2_wy<E, D>), grid, dim3(256), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
+    hipLaunchKernelGGL((k_bwd_gdn2_wy<E, D, LOG>), grid, dim3(256), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
                        (const E*)in.beta, (const E*)in.erase, (const E*)in.write, (const E*)dO, (const float*)p.G,
                        (const E*)p.X, (const E*)p.U2, (const E*)p.M2, (const E*)p.dR, (E*)gr.dv, (E*)gr.dwrite, p);
   }
   {
     TraceScope ts_("bwd_gdn2_gram", st);
-    hipLaunchKernelGGL((k_bwd_gdn2_gram<E, D>), grid, dim3(256), 0, st, p.geo, (const E*)in.q, (const E*)in.k,
+    hipLaunchKernelGGL((k_bwd_gdn2_gram<E, D, LOG>), grid, dim3(256), 0, st, p.geo, (const E*)in.q, (const E*)in.k,
                        (const E*)in.beta, (const E*)in.alpha, (const E*)in.erase, (const float*)p.G, (const E*)p.M,
                        (const E*)p.M2, (E*)gr.dq, (E*)gr.dk, (E*)gr.dbeta, (E*)gr.dalpha, (E*)gr.derase, p);
   }
   return hipGetLastError();
+}
+template <typename E, int D>
+hipError_t launch_bwd_gdn2(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr, hipStream_t st) {
+  return p.gates ? bwd_gdn2_impl<E, D, true>(p, in, dO, gr, st) : bwd_gdn2_impl<E, D, false>(p, in, dO, gr, st);
 }
 template hipError_t launch_bwd_gdn2<bf16, 128>(const Plan&, const gdr_inputs&, const void*, const gdr_grads&, hipStream_t);
 template hipError_t launch_bwd_gdn2<bf16, 64>(const Plan&, const gdr_inputs&, const void*, const gdr_grads&, hipStream_t);
@@ -773,10 +799,13 @@ template hipError_t launch_bwd_gdn2<float, 64>(const Plan&, const gdr_inputs&, c
 template <typename E, int D>
 hipError_t launch_fwd_prep_gdn2(const Plan& p, const gdr_inputs& in, hipStream_t st) {
   TraceScope ts_("fwd_prep_gdn2", st);
-  hipLaunchKernelGGL((k_fwd_prep_gdn2<E, D>), dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo,
-                     (const E*)in.q, (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha,
-                     (const E*)in.erase, (const E*)in.write, (E*)p.X, (E*)p.Ub, (E*)p.U2, (E*)p.M, (E*)p.M2, p.G,
-                     p.Li, p.A1, p.A2);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo, (const E*)in.q,
+                       (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (const E*)in.erase,
+                       (const E*)in.write, (E*)p.X, (E*)p.Ub, (E*)p.U2, (E*)p.M, (E*)p.M2, p.G, p.Li, p.A1, p.A2);
+  };
+  if (p.gates) go(k_fwd_prep_gdn2<E, D, true>);
+  else go(k_fwd_prep_gdn2<E, D, false>);
   return hipGetLastError();
 }
 template hipError_t launch_fwd_prep_gdn2<bf16, 128>(const Plan&, const gdr_inputs&, hipStream_t);

@@ -86,8 +86,6 @@ gdr_status check_shape(const gdr_problem* p, long long* total_chunks_out, int* m
   if (p->n_seqs < 0) return fail(GDR_ERR_INVALID_ARG, "n_seqs must be >= 0");
   if (p->H > 65535) return fail(GDR_ERR_UNSUPPORTED, "H > 65535 is not supported");
   if (p->gates != 0 && p->gates != 1) return fail(GDR_ERR_INVALID_ARG, "gates must be 0 (values) or 1 (logits)");
-  if (p->gates && p->variant == GDR_GDN2)
-    return fail(GDR_ERR_UNSUPPORTED, "gates given as logits are built for DeltaNet, Gated DeltaNet and Kimi Delta Attention");
   long long total_chunks = 0;
   int max_chunks = 0;
   if (p->n_seqs > 0) {
@@ -381,6 +379,8 @@ gdr_status gdr_decode(const gdr_problem* p, const gdr_inputs* in, float* state, 
   if (p->dk != 64 && p->dk != 128) return fail(GDR_ERR_UNSUPPORTED, "head size %d: only 64 and 128 are built", p->dk);
   if ((st = check_inputs(p, in)) != GDR_OK) return st;
   if (in->h0) return fail(GDR_ERR_INVALID_ARG, "decode takes the memory through state; h0 must be NULL");
+  if (p->gates && p->variant == GDR_GDN2)
+    return fail(GDR_ERR_UNSUPPORTED, "decoding with gates given as logits is built for the delta family and Kimi");
   if (!state) return fail(GDR_ERR_INVALID_ARG, "state is required");
   if (!o && p->T > 0) return fail(GDR_ERR_INVALID_ARG, "o is required");
   if (!aligned(state, 16) || (o && !aligned(o, 16)))

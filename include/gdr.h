@@ -74,10 +74,11 @@ typedef struct {
   int32_t gates;                  /* 0: beta, alpha are the gate values.  1: they are logits x,
                                      beta = sigmoid(x), alpha = exp(-softplus(x)) (the gate laws of
                                      the operator's workloads), applied inside the kernels, and
-                                     dbeta, dalpha are gradients w.r.t. x.  1 is built for
-                                     GDR_DELTANET, GDR_GATED and GDR_KDA (alpha per channel)
-                                     (gdr_forward, gdr_backward, gdr_decode; not with a
-                                     residual output or gradient) */
+                                     dbeta, dalpha are gradients w.r.t. x; for GDR_GDN2 the
+                                     erase and write gates too (e = sigmoid(x), w = sigmoid(x),
+                                     derase, dwrite w.r.t. x).  Built for every variant in
+                                     gdr_forward and gdr_backward, for all but GDR_GDN2 in
+                                     gdr_decode; not with a residual output or gradient */
 } gdr_problem;
 
 typedef struct {

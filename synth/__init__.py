@@ -122,9 +122,10 @@ def make_inputs(w: Workload, *, alpha_mode: str = "config", with_grad: Optional[
                 seed: Optional[int] = None, T: Optional[int] = None, gate_logits: bool = False) -> dict:
     """Draw one workload's inputs.
 
-    gate_logits: return beta and alpha as the logits drawn for them (N(0,1), and N(0,1) plus
-    the alpha_mode's shift), rounded to the I/O precision, instead of the gate values; the
-    consumer applies sigmoid / exp(-softplus).  Same draws, same order.
+    gate_logits: return beta, alpha (and the erase/write gates) as the logits drawn for them
+    (N(0,1), and N(0,1) plus the alpha_mode's shift for alpha), rounded to the I/O precision,
+    instead of the gate values; the consumer applies sigmoid / exp(-softplus).  Same draws,
+    same order.
 
     alpha_mode: "config" -> alpha = exp(-softplus(N(0,1) + 2)) (the workloads' law);
                 "weak"   -> alpha = exp(-softplus(N(0,1) - 5)) (about 0.99: long memory);
@@ -158,8 +159,8 @@ def make_inputs(w: Workload, *, alpha_mode: str = "config", with_grad: Optional[
             x = rng.standard_normal(shape) + shift
             out["alpha"] = to_io(x if gate_logits else np.exp(-_softplus(x)), w.dtype)
     if w.variant == "gdn2":
-        out["erase"] = to_io(_sigmoid(rng.standard_normal((B, H, T, dk))), w.dtype)
-        out["write"] = to_io(_sigmoid(rng.standard_normal((B, H, T, dv))), w.dtype)
+        out["erase"] = to_io(act_b(rng.standard_normal((B, H, T, dk))), w.dtype)
+        out["write"] = to_io(act_b(rng.standard_normal((B, H, T, dv))), w.dtype)
     else:
         out["erase"] = out["write"] = None
     if w.h0_std > 0:

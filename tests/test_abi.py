@@ -231,7 +231,7 @@ def test_residual_checks(lib):
 def test_gate_logit_checks(lib):
     assert _ws(lib, _problem(gates=2))[0] == bd.GDR_ERR_INVALID_ARG
     assert _ws(lib, _problem(gates=1, variant=2))[0] == bd.GDR_OK  # Kimi: per-channel logits
-    assert _ws(lib, _problem(gates=1, variant=3))[0] == bd.GDR_ERR_UNSUPPORTED  # GDN-2: values only
+    assert _ws(lib, _problem(gates=1, variant=3))[0] == bd.GDR_OK  # GDN-2: e, w logits too
     assert _ws(lib, _problem(gates=1))[0] == bd.GDR_OK
     p = _problem(gates=1)
     st = lib.gdr_forward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE, None, None, FAKE, 1 << 40, None)

@@ -19,8 +19,9 @@ def _sig(x):
 def _gates(inp):
     """Gate values in float64 from the logits."""
     out = dict(inp)
-    xb = inp["beta"].astype(np.float64)
-    out["beta"] = _sig(xb)
+    for name in ("beta", "erase", "write"):
+        if inp.get(name) is not None:
+            out[name] = _sig(inp[name].astype(np.float64))
     if inp.get("alpha") is not None:
         xa = inp["alpha"].astype(np.float64)
         out["alpha"] = np.exp(-np.logaddexp(0.0, xa))
@@ -30,13 +31,15 @@ def _gates(inp):
 def _oracle(inp, variant, backward, cu=None, scale=1.0):
     from oracle import recurrence as R
     vals = _gates(inp)
-    kw = {n: vals.get(n) for n in ("q", "k", "v", "beta", "alpha", "h0")}
+    kw = {n: vals.get(n) for n in ("q", "k", "v", "beta", "alpha", "erase", "write", "h0")}
     o, ht = R.forward(**kw, variant=variant, cu_seqlens=cu, scale=scale)
     ref = {"o": o, "ht": ht}
     if backward:
         g = R.backward(**kw, do=inp["do"], variant=variant, cu_seqlens=cu, scale=scale)
-        b = vals["beta"]
-        g["dbeta"] = g["dbeta"] * b * (1.0 - b)
+        for name, gname in (("beta", "dbeta"), ("erase", "derase"), ("write", "dwrite")):
+            if g.get(gname) is not None:
+                x = vals[name]
+                g[gname] = g[gname] * x * (1.0 - x)
         if g.get("dalpha") is not None:
             a = vals["alpha"]
             g["dalpha"] = g["dalpha"] * a * (-_sig(inp["alpha"].astype(np.float64)))
@@ -61,7 +64,7 @@ def _hip(inp, variant, dtype, backward, use_saved=True, scale=1.0):
     return res
 
 
-CASES = [(v, dt, d, m, s) for v in ("deltanet", "gated", "kda") for dt, d in (("bf16", 128), ("f32", 64))
+CASES = [(v, dt, d, m, s) for v in ("deltanet", "gated", "kda", "gdn2") for dt, d in (("bf16", 128), ("f32", 64))
          for m in ("config", "weak") for s in (True, False)]
 
 
@@ -106,3 +109,10 @@ def test_gate_logits_decode(variant):
     torch.cuda.synchronize()
     ref = _oracle(inp, variant, False)
     compare({"o": to_np(o), "ht": to_np(state)}, ref, "bf16")
+
+
+def test_gate_logits_gdn2_without_beta():
+    """Gated DeltaNet-2 as in its workload (no beta), erase/write/alpha as logits."""
+    w = synth.Workload("lg2", "gdn2", "bf16", 1, 2, 200, 128, 128, seed=63, h0_std=0.1, has_beta=False)
+    inp = synth.make_inputs(w, alpha_mode="weak", gate_logits=True)
+    compare(_hip(inp, "gdn2", "bf16", True), _oracle(inp, "gdn2", True), "bf16")
