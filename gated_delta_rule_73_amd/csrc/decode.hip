@@ -42,7 +42,7 @@ __device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a
 }  // namespace
 
 // Grid: one workgroup per (memory, block of RPB value rows), memory = sequence * H + head.
-// LOG: beta and alpha are logits (beta = sigmoid(x), alpha = exp(-softplus(x))).
+// LOG: the gates are logits (beta, e, w = sigmoid(x), alpha = exp(-softplus(x))).
 template <typename E, int D, int VAR, bool LOG>
 __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                 const E* __restrict__ v, const E* __restrict__ beta,
@@ -91,14 +91,24 @@ __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q
       dec = f32x4{a, a, a, a};
     }
     f32x4 ek = kt;  // direction along which the prediction is erased: beta (e*k), or beta k
-    if constexpr (VAR == VAR_GDN2) ek = kt * load4(erase + tk * D + j0);
+    if constexpr (VAR == VAR_GDN2) {
+      f32x4 e = load4(erase + tk * D + j0);
+      if constexpr (LOG) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) e[x] = gate_sigmoid(e[x]);
+      }
+      ek = kt * e;
+    }
     ek *= bt;
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       const f32x4 Wd = W[r] * dec;
       const float vbar = row_sum<LPR>(dot4(Wd, kt));
       float stored = bt * (float)v[tk * D + row[r]];  // beta v_i, or beta w_i v_i
-      if constexpr (VAR == VAR_GDN2) stored *= (float)write[tk * D + row[r]];
+      if constexpr (VAR == VAR_GDN2) {
+        const float wr = (float)write[tk * D + row[r]];
+        stored *= LOG ? gate_sigmoid(wr) : wr;
+      }
       W[r] = Wd - vbar * ek + stored * kt;
       const float ov = row_sum<LPR>(dot4(W[r], qt));
       if (j0 == 0) o[tk * D + row[r]] = (E)(geo.scale * ov);
@@ -124,10 +134,13 @@ hipError_t launch_decode_t(const Geo& g, int variant, int gates, const gdr_input
                        (const E*)in.write, state, (E*)o);
     return hipGetLastError();
   };
-  if (gates) {  // logits: not Gated DeltaNet-2 (checked by the caller)
-    if (variant == GDR_DELTANET) return go(k_decode<E, D, VAR_DELTANET, true>);
-    if (variant == GDR_KDA) return go(k_decode<E, D, VAR_KDA, true>);
-    return go(k_decode<E, D, VAR_GATED, true>);
+  if (gates) {  // gates given as logits
+    switch (variant) {
+      case GDR_DELTANET: return go(k_decode<E, D, VAR_DELTANET, true>);
+      case GDR_GATED: return go(k_decode<E, D, VAR_GATED, true>);
+      case GDR_KDA: return go(k_decode<E, D, VAR_KDA, true>);
+      default: return go(k_decode<E, D, VAR_GDN2, true>);
+    }
   }
   switch (variant) {
     case GDR_DELTANET: return go(k_decode<E, D, VAR_DELTANET, false>);

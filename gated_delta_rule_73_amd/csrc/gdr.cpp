@@ -379,8 +379,6 @@ gdr_status gdr_decode(const gdr_problem* p, const gdr_inputs* in, float* state, 
   if (p->dk != 64 && p->dk != 128) return fail(GDR_ERR_UNSUPPORTED, "head size %d: only 64 and 128 are built", p->dk);
   if ((st = check_inputs(p, in)) != GDR_OK) return st;
   if (in->h0) return fail(GDR_ERR_INVALID_ARG, "decode takes the memory through state; h0 must be NULL");
-  if (p->gates && p->variant == GDR_GDN2)
-    return fail(GDR_ERR_UNSUPPORTED, "decoding with gates given as logits is built for the delta family and Kimi");
   if (!state) return fail(GDR_ERR_INVALID_ARG, "state is required");
   if (!o && p->T > 0) return fail(GDR_ERR_INVALID_ARG, "o is required");
   if (!aligned(state, 16) || (o && !aligned(o, 16)))

@@ -77,8 +77,8 @@ typedef struct {
                                      dbeta, dalpha are gradients w.r.t. x; for GDR_GDN2 the
                                      erase and write gates too (e = sigmoid(x), w = sigmoid(x),
                                      derase, dwrite w.r.t. x).  Built for every variant in
-                                     gdr_forward and gdr_backward, for all but GDR_GDN2 in
-                                     gdr_decode; not with a residual output or gradient */
+                                     gdr_forward, gdr_backward and gdr_decode; not with a
+                                     residual output or gradient */
 } gdr_problem;
 
 typedef struct {

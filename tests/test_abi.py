@@ -236,4 +236,3 @@ def test_gate_logit_checks(lib):
     p = _problem(gates=1)
     st = lib.gdr_forward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE, None, None, FAKE, 1 << 40, None)
     assert st == bd.GDR_ERR_UNSUPPORTED
-    assert _dec(lib, _problem(T=1, gates=1, variant=3), _inputs(erase=FAKE, write=FAKE)) == bd.GDR_ERR_UNSUPPORTED

@@ -96,14 +96,14 @@ def test_gate_logits_packed_bench_shape_sample():
     compare(mine, ref, "bf16")
 
 
-@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda"])
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2"])
 def test_gate_logits_decode(variant):
     import torch
     from gated_delta_rule_73_amd import gdr_decode
     from tests._helpers import to_gpu, to_np
     w = synth.Workload("lgd", variant, "bf16", 3, 2, 5, 128, 128, seed=62, backward=False, h0_std=0.3)
     inp = synth.make_inputs(w, alpha_mode="weak", gate_logits=True)
-    g = {n: to_gpu(inp.get(n), "bf16") for n in ("q", "k", "v", "beta", "alpha")}
+    g = {n: to_gpu(inp.get(n), "bf16") for n in ("q", "k", "v", "beta", "alpha", "erase", "write")}
     state = torch.from_numpy(inp["h0"]).cuda()
     o = gdr_decode(**g, state=state, variant=variant, gate_logits=True)
     torch.cuda.synchronize()
