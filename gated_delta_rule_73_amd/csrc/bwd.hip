@@ -104,6 +104,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   int c0 = 0, c1 = sp.nchunks;
   if (sg.mode != 0) {
     if (seg >= seg_count(sg, sp.nchunks)) return;
+    if (sg.mode == 1 && seg == 0) return;  // walked in reverse, the first segment's map is never applied
     c0 = seg * sg.lseg;
     c1 = min(sp.nchunks, c0 + sg.lseg);
   }
@@ -790,18 +791,18 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
       launch(k_bwd_scan<E, D, 32, VAR, false>, 32, sg, dhtp, dh0p, nv_mult, nullptr);
     }
   };
-  if (p.lseg == 0) {
+  if (p.lseg_b == 0) {
     TraceScope ts_("bwd_scan", st);
     scan(ScanSeg{0, 0, 1, nullptr, nullptr}, dht, gr.dh0, 1);
   } else {
     {
       TraceScope ts_("bwd_scan_maps", st);
-      scan(ScanSeg{1, p.lseg, p.max_seg, p.seg_maps, nullptr}, nullptr, nullptr, 2);
+      scan(ScanSeg{1, p.lseg_b, p.max_seg_b, p.seg_maps, nullptr}, nullptr, nullptr, 2);
     }
-    const hipError_t e = launch_seg_combine(p, ScanSeg{0, p.lseg, p.max_seg, p.seg_maps, nullptr}, dht, true, st);
+    const hipError_t e = launch_seg_combine(p, ScanSeg{0, p.lseg_b, p.max_seg_b, p.seg_maps, nullptr}, dht, true, st);
     if (e != hipSuccess) return e;
     TraceScope ts_("bwd_scan", st);
-    scan(ScanSeg{2, p.lseg, p.max_seg, nullptr, p.seg_starts}, nullptr, gr.dh0, 1);
+    scan(ScanSeg{2, p.lseg_b, p.max_seg_b, nullptr, p.seg_starts}, nullptr, gr.dh0, 1);
   }
   if (g.total_chunks > 0) {
     if constexpr (VAR == VAR_GDN2 || VAR == VAR_GDN2L) {

@@ -243,6 +243,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
   if (sg.mode != 0) {
     nseg = seg_count(sg, sp.nchunks);
     if (seg >= nseg) return;
+    if (!FULL && seg == nseg - 1) return;  // the last segment's map is never applied
     c0 = seg * sg.lseg;
     c1 = min(sp.nchunks, c0 + sg.lseg);
   }

@@ -37,7 +37,8 @@ struct Sizes {
   int total_chunks = 0;
   int nstates = 0;
   size_t esz = 0;
-  int bv = 16, lseg = 0, max_seg = 1;  // scan value tile; segmented scans (see plan_scans)
+  int bv = 16, lseg = 0, max_seg = 1;  // scan value tile; forward segmented scans (see plan_scans)
+  int lseg_b = 0, max_seg_b = 1;       // backward segmented scans
   size_t X, M, G, Hs, R, M2, U2, Li, A1, A2, Kb, Qh, Gn, Ub, dHs, dR, g2, seg;
   size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Li + A1 + A2 + Kb + Qh + Gn; }
   size_t fwd_ws() const { return Ub + seg; }                   // workspace before the cache
@@ -46,11 +47,27 @@ struct Sizes {
 
 // Scan shape.  Value tiles of 32 rows when the memories give at least one per CU, else 16
 // (always 16 for float32 I/O, whose operand tiles take twice the LDS).
-// When even then the memories' tiles number under 256 (fewer than one workgroup per CU), each
-// sequence's chunks are cut into segments (see ScanSeg) so that about 1024 workgroups run,
-// with at least 16 chunks per segment.  GDR_SEG_CHUNKS, if set, forces the segment length in
-// chunks (0: never segment) and GDR_SCAN_BV the value tile (16 or 32); they exist for tuning
-// and change nothing but speed.
+// Segmented scans (see ScanSeg) shorten the sequential chain at the price of a map pass and a
+// combine.  Measured on one MI355X at 16 memories x 512 chunks (128 value tiles): the forward
+// gains with segments that give about 512 workgroups (128 chunks: 0.72 ms against 0.85 ms
+// unsegmented; 64 chunks 0.78, 32 chunks 0.84, since the combine grows with the segment count),
+// while the backward's map pass costs more than it saves (0.83 ms against 0.75 unsegmented).
+// So the forward segments when its value tiles leave CUs idle (fewer than 256), aiming at about
+// 512 workgroups with at least 16 chunks per segment, and the backward only when fewer than 64
+// tiles would run.  GDR_SEG_CHUNKS, if set, forces the segment length of both (0: never
+// segment) and GDR_SCAN_BV the value tile (16 or 32); they exist for tuning and tests and
+// change nothing but speed.
+int seg_length(long long tiles, long long min_tiles, int max_chunks) {
+  if (const char* env = std::getenv("GDR_SEG_CHUNKS")) {
+    const int l = std::atoi(env);
+    return (l <= 0 || l >= max_chunks) ? 0 : l;
+  }
+  if (tiles >= min_tiles || max_chunks < 32) return 0;
+  const long long want = (512 + tiles - 1) / tiles;
+  const int l = (int)std::max<long long>(16, (max_chunks + want - 1) / want);
+  return l >= max_chunks ? 0 : l;
+}
+
 void plan_scans(long long memories, int d, int max_chunks, bool f32, Sizes* s) {
   s->bv = (!f32 && memories * (d / 32) >= 256) ? 32 : 16;
   if (const char* env = std::getenv("GDR_SCAN_BV")) {
@@ -58,16 +75,10 @@ void plan_scans(long long memories, int d, int max_chunks, bool f32, Sizes* s) {
     if (bv == 16 || (bv == 32 && !f32)) s->bv = bv;
   }
   const long long tiles = memories * (d / s->bv);
-  int lseg = 0;
-  if (const char* env = std::getenv("GDR_SEG_CHUNKS")) {
-    lseg = std::atoi(env);
-  } else if (tiles < 256 && max_chunks >= 32) {
-    const long long want = (1024 + tiles - 1) / tiles;
-    lseg = (int)std::max<long long>(16, (max_chunks + want - 1) / want);
-  }
-  if (lseg <= 0 || lseg >= max_chunks) lseg = 0;
-  s->lseg = lseg;
-  s->max_seg = lseg ? (max_chunks + lseg - 1) / lseg : 1;
+  s->lseg = seg_length(tiles, 256, max_chunks);
+  s->lseg_b = seg_length(tiles, 64, max_chunks);
+  s->max_seg = s->lseg ? (max_chunks + s->lseg - 1) / s->lseg : 1;
+  s->max_seg_b = s->lseg_b ? (max_chunks + s->lseg_b - 1) / s->lseg_b : 1;
 }
 
 // Checks the fields every entry point reads (variant, dtype, sizes, scale, packed offsets) and
@@ -157,7 +168,8 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   else if (kda) s.g2 = align_up(U * (4 * C * D + 2 * C * C + D) * 4, A);
   else s.g2 = 0;
   plan_scans((long long)s.nstates * p->H, p->dk, max_chunks, p->dtype == GDR_F32, &s);
-  s.seg = s.lseg ? align_up((size_t)s.nstates * p->H * s.max_seg * 3 * D * D * 4, A) : 0;
+  const size_t ms = (size_t)std::max(s.lseg ? s.max_seg : 0, s.lseg_b ? s.max_seg_b : 0);
+  s.seg = ms ? align_up((size_t)s.nstates * p->H * ms * 3 * D * D * 4, A) : 0;
   *sz = s;
   return GDR_OK;
 }
@@ -204,6 +216,8 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
   pl.bv = s.bv;
   pl.lseg = s.lseg;
   pl.max_seg = s.max_seg;
+  pl.lseg_b = s.lseg_b;
+  pl.max_seg_b = s.max_seg_b;
   char* c = cache;
   pl.X = c; c += s.X;
   pl.M = c; c += s.M;
@@ -221,7 +235,7 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
   char* w = ws;
   pl.Ub = w; w += s.Ub;
   pl.seg_maps = reinterpret_cast<float*>(w);
-  pl.seg_starts = pl.seg_maps + (size_t)s.nstates * p->H * s.max_seg * 2 * p->dk * p->dk;
+  pl.seg_starts = pl.seg_maps + (size_t)s.nstates * p->H * std::max(s.max_seg, s.max_seg_b) * 2 * p->dk * p->dk;
   w += s.seg;
   pl.dHs = pl.dR = nullptr;
   if (backward) {

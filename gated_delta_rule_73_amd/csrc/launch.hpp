@@ -14,9 +14,10 @@ struct Plan {
   Geo geo;
   int variant, dtype, D, bv;
   int gates;          // 1: beta and alpha are logits (Delta family)
-  int lseg, max_seg;  // segmented scans: chunks per segment (0: off), largest segment count
-  float* seg_maps;    // [memories][max_seg][2][D][D] float32 (workspace)
-  float* seg_starts;  // [memories][max_seg][D][D] float32 (workspace)
+  int lseg, max_seg;      // forward segmented scans: chunks per segment (0: off), largest segment count
+  int lseg_b, max_seg_b;  // the same for the backward scans
+  float* seg_maps;        // [memories][max_seg][2][D][D] float32 (workspace; max_seg of the pass)
+  float* seg_starts;      // [memories][max_seg][D][D] float32 (workspace)
   // forward cache (in the caller's saved buffer or in the workspace)
   void* X;    // [units][64][D]  WY factor X = T (e^g K)
   void* M;    // [units][64][64] decayed causal Q K^T

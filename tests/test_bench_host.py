@@ -1,0 +1,27 @@
+"""Host-side checks of bench.py (no GPU): it refuses more than one GPU, and its byte models
+give the operator's minima quoted for the workloads."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_byte_models():
+    sys.path.insert(0, ROOT)
+    import bench
+    import synth
+    # Gated DeltaNet, d = 128, bf16: forward q,k,v,beta,alpha -> o (1028 B) + backward (1800 B)
+    assert bench.path_bytes_per_head_token("gated", 128, 2, True) == 2828
+    assert bench.path_bytes_per_head_token("kda", 128, 2, True) == 3590
+    assert bench.path_bytes_per_head_token("gdn2", 128, 2, False) == 4358
+    w = synth.DECODE_WORKLOADS["gated_decode_B512H16"]
+    # 512 x 16 float32 memories read and written, plus q, k, v, o, beta, alpha per head-token
+    assert bench.decode_bytes(w, 2) == 2 * 512 * 16 * 128 * 128 * 4 + 512 * 16 * (4 * 128 * 2 + 2 + 2)
