@@ -366,7 +366,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   const int n = cp.n;
 
   // ================= phase 1: products with the memory W0 and its gradient dW
-  f32x4 acc1[D / 16];  // waves 0-3: row tile wm of dQhat = dO W0; waves 4-7: (dR W0)^T, column
+  f32x4 acc1[D / 16];  // waves 0-3: (dO W0)^T = dQhat^T; waves 4-7: (dR W0)^T; both column
                        // tile wm (stored four columns at a time)
   f32x4 dka[NQ];       // dk, held transposed: row t = 16 wm + lrow, four consecutive columns
                        // of column tiles wn*NQ + qq
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       __syncthreads();
       if (w < 4) {
 #pragma unroll
-        for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(dOs + ih * KH, LD), 16 * wm, colk(Wh, LD), 16 * nt);
+        for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], colk(Wh, LD), 16 * nt, rowk(dOs + ih * KH, LD), 16 * wm);
       } else {
 #pragma unroll
         for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], colk(Wh, LD), 16 * nt, rowk(dRs + ih * KH, LD), 16 * wm);
@@ -466,13 +466,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
   }
   const float gn = gs[CH - 1];
-  // e^{g_t} for the four accumulator rows this lane holds (row tile wm), and e^{g_t},
-  // e^{g_n - g_t} for the row of the transposed dk tiles
+  // e^{g_t}, e^{g_n - g_t} for the row t of the transposed dq and dk tiles this lane holds
   const int tr = 16 * wm + lrow();
-  float egr[4] = {1.f, 1.f, 1.f, 1.f}, egt = 1.f, egdt = 1.f;
+  float egt = 1.f, egdt = 1.f;
   if constexpr (GATED) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) egr[r] = expf(gs[acc_row(16 * wm, r)]);
     egt = expf(gs[tr]);
     egdt = expf(gn - gs[tr]);
   }
@@ -480,8 +477,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
     if (w < 4) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc1[nt][r] *= geo.scale * egr[r];
+      acc1[nt] *= geo.scale * egt;
     } else {
       store4_t(dXs, LD, 16 * nt, 16 * wm, -acc1[nt]);
     }
@@ -671,19 +667,18 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
   }
   __syncthreads();
-  if (w < 4) {
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+  if (w < 4) {  // the row's Qhat . dQhat (state term), four consecutive columns per lane
+    float part = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part[r] += (float)Qs[acc_row(16 * wm, r) * LD + acc_col(16 * nt)] * acc1[nt][r];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float s = sum16(part[r]);
-      if (lrow() == 0) rq[w][acc_row(16 * wm, r)] = s;
+    for (int nt = 0; nt < D / 16; ++nt) {
+      const f32x4 qv = get4(Qs + tr * LD + 16 * nt + 4 * lgrp());
+      part += qv[0] * acc1[nt][0] + qv[1] * acc1[nt][1] + qv[2] * acc1[nt][2] + qv[3] * acc1[nt][3];
     }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (lgrp() == 0) rq[w][tr] = part;
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, CH>(acc1[nt], rowk(Mts, LDR), 16 * wm, colk(Ks, LD), 16 * nt);
+    for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, CH>(acc1[nt], colk(Ks, LD), 16 * nt, rowk(Mts, LDR), 16 * wm);
   }
 #pragma unroll
   for (int qq = 0; qq < NQ; ++qq) {
@@ -714,7 +709,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   E* sk = reinterpret_cast<E*>(smem + Ly::odX);
   if (w < 4) {
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) store4_n(sq, LD, 16 * wm, 16 * nt, acc1[nt]);
+    for (int nt = 0; nt < D / 16; ++nt) store4_t(sq, LD, 16 * nt, 16 * wm, acc1[nt]);
   }
 #pragma unroll
   for (int qq = 0; qq < NQ; ++qq) store4_t(sk, LD, 16 * (wn * NQ + qq), 16 * wm, dka[qq]);
