@@ -116,3 +116,33 @@ def test_gate_logits_gdn2_without_beta():
     w = synth.Workload("lg2", "gdn2", "bf16", 1, 2, 200, 128, 128, seed=63, h0_std=0.1, has_beta=False)
     inp = synth.make_inputs(w, alpha_mode="weak", gate_logits=True)
     compare(_hip(inp, "gdn2", "bf16", True), _oracle(inp, "gdn2", True), "bf16")
+
+
+@pytest.mark.parametrize("variant", ["gated", "kda", "gdn2"])
+def test_gate_logits_segmented_scans(variant):
+    """Logit gates through the segmented scans (map pass, combine, rerun forced on), packed
+    sequences with ragged tails and an empty one; Gated DeltaNet-2 runs its logit scan variant."""
+    import os
+    cu = [0, 150, 150, 347]
+    w = synth.Workload("lgs", variant, "bf16", 1, 2, 347, 128, 128, seed=64, h0_std=0.1,
+                       cu_seqlens=tuple(cu))
+    inp = synth.make_inputs(w, alpha_mode="weak", gate_logits=True)
+    os.environ["GDR_SEG_CHUNKS"] = "1"
+    try:
+        got = _hip(inp, variant, "bf16", True)
+    finally:
+        del os.environ["GDR_SEG_CHUNKS"]
+    compare(got, _oracle(inp, variant, True, cu=np.asarray(cu)), "bf16")
+
+
+def test_gate_logits_decode_d64_f32():
+    import torch
+    from gated_delta_rule_73_amd import gdr_decode
+    from tests._helpers import to_gpu, to_np
+    w = synth.Workload("lgd64", "kda", "f32", 2, 3, 4, 64, 64, seed=65, backward=False, h0_std=0.3)
+    inp = synth.make_inputs(w, alpha_mode="weak", gate_logits=True)
+    g = {n: to_gpu(inp.get(n), "f32") for n in ("q", "k", "v", "beta", "alpha")}
+    state = torch.from_numpy(inp["h0"]).cuda()
+    o = gdr_decode(**g, state=state, variant="kda", gate_logits=True)
+    torch.cuda.synchronize()
+    compare({"o": to_np(o), "ht": to_np(state)}, _oracle(inp, "kda", False), "f32")

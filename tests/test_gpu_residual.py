@@ -119,3 +119,17 @@ def test_residual_unsupported_variants():
     g = gpu_inputs(inp, "bf16")
     with pytest.raises(GdrError):  # bfloat16 residual gradient: not built
         gdr_backward(**g, do=to_gpu(inp["do"], "bf16"), dr=to_gpu(inp["dr"], "bf16"), variant="gated")
+
+
+@pytest.mark.parametrize("variant", ["gated", "kda"])
+def test_residual_forward_segmented_bf16(variant):
+    """The residual output written by the rerun pass of forced segmented scans."""
+    import os
+    cu = [0, 130, 130, 333]
+    inp = _inputs(variant, "bf16", 128, T=333, B=1, H=2, cu=cu)
+    os.environ["GDR_SEG_CHUNKS"] = "1"
+    try:
+        got = _hip(inp, variant, "bf16", False)
+    finally:
+        del os.environ["GDR_SEG_CHUNKS"]
+    compare(got, _oracle(inp, variant, False), "bf16")
