@@ -45,7 +45,8 @@ struct BwdScanOps<E, D, BV, VAR_GDN2> {
   RegTile<E, CH, D, 256> q, k, x, e;
   RegTile<E, CH, CH, 256> m;
   RegTile<E, CH, BV, 256> dO;
-  float g, b;
+  float g;
+  uint32_t braw2;  // beta of this lane's token as loaded (0 if absent or past the end)
 };
 template <typename E, int D, int BV>
 struct BwdScanOps<E, D, BV, VAR_GDN2L> : BwdScanOps<E, D, BV, VAR_GDN2> {};
@@ -165,8 +166,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
       }
       if constexpr (G2) {
         p.e.load(erase + tk * D, D, n);
-        const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
-        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? g2_gate<G2L>((float)beta[tk + t]) : 1.f) : 0.f;
+        p.braw2 = load_gate_raw(beta ? beta + tk : nullptr, n, (int)(threadIdx.x & (CH - 1)));
       }
     }
   };
@@ -185,7 +185,8 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
       if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
     }
     if constexpr (G2) {
-      if (threadIdx.x < CH) bsh[threadIdx.x] = p.b;
+      if (threadIdx.x < CH)  // beta (1 when absent), 0 past the end; converted here, where it is used
+        bsh[threadIdx.x] = ((int)threadIdx.x < n) ? (beta ? g2_gate<G2L>(gate_from_raw<E>(p.braw2)) : 1.f) : 0.f;
     }
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)

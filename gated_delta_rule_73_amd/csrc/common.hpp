@@ -245,6 +245,20 @@ template <> __device__ __forceinline__ uint32_t buf_load<4>(__amdgpu_buffer_rsrc
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// One gate element per lane, as loaded: no arithmetic on it (so nothing waits for the load until
+// the value is used) and no branch around it.  A NULL gate, or a lane t >= n, reads 0.
+template <typename E>
+__device__ __forceinline__ uint32_t load_gate_raw(const E* g, int n, int t) {
+  const __amdgpu_buffer_rsrc_t r = buf_rsrc(g, g ? (long)n * (long)sizeof(E) : 0);
+  if constexpr (sizeof(E) == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, t * 2, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b32(r, t * 4, 0, 0);
+}
+template <typename E>
+__device__ __forceinline__ float gate_from_raw(uint32_t x) {
+  if constexpr (sizeof(E) == 2) return __builtin_bit_cast(float, x << 16);  // bfloat16: the top half
+  else return __builtin_bit_cast(float, x);
+}
+
 // Vector width (bytes) that spreads a tile of `bytes` over NT threads, 4..16.
 constexpr int tile_vec_bytes(int bytes, int nt) {
   return bytes / nt >= 16 ? 16 : bytes / nt >= 8 ? 8 : 4;

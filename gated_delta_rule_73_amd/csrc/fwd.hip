@@ -185,7 +185,8 @@ struct FwdScanOps {
   RegTile<E, CH, D, 256> x, k, q, e;
   RegTile<E, CH, BV, 256> u, vt, wt;
   RegTile<E, CH, CH, 256> m, m2;
-  float g, b;
+  float g;
+  uint32_t braw2;  // Gated DeltaNet-2: beta of this lane's token as loaded (0 if absent or past the end)
   f32x4 eg[D / 64];
   E braw;  // residual output: beta of this lane's token, as loaded (converted where it is used)
 };
@@ -307,8 +308,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         p.e.load(erase + tk * D, D, n);
         p.vt.load(vin + tk * D + i0, D, n);
         p.wt.load(write + tk * D + i0, D, n);
-        const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
-        p.b = ((int)(threadIdx.x & (CH - 1)) < n) ? (beta ? g2_gate<G2L>((float)beta[tk + t]) : 1.f) : 0.f;
+        p.braw2 = load_gate_raw(beta ? beta + tk : nullptr, n, (int)(threadIdx.x & (CH - 1)));
       }
     }
   };
@@ -332,7 +332,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       if (threadIdx.x < CH) gs[threadIdx.x] = p.g;
     }
     if constexpr (G2) {
-      if (threadIdx.x < CH) bsh[threadIdx.x] = p.b;
+      if (threadIdx.x < CH)  // beta (1 when absent), 0 past the end; converted here, where it is used
+        bsh[threadIdx.x] = ((int)threadIdx.x < n) ? (beta ? g2_gate<G2L>(gate_from_raw<E>(p.braw2)) : 1.f) : 0.f;
     }
     if constexpr (RES) {  // residual output: 1 / beta (0 past the end)
       if (threadIdx.x < CH) bsh[threadIdx.x] = ((int)threadIdx.x < n) ? 1.f / (float)p.braw : 0.f;
