@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
     const int t = threadIdx.x;
     const bool ok = t < n;
     bs[t] = ok ? (beta ? g2_gate<LOG>((float)beta[tk + t]) : 1.f) : 0.f;
-    const float xa = (float)alpha[tk + t];
+    const float xa = (float)alpha[tk + min(t, n - 1)];  // a valid token also for lanes past the end
     const float la = ok ? (LOG ? gate_neg_softplus(xa) : logf(xa)) : 0.f;
     const float g = wave_incl_scan(la);
     gs[t] = g;
