@@ -43,15 +43,12 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
   const int w = wave_id();
   const int n = cp.n;
 
+  // The gates are loaded first, as raw values (lanes past the end read 0), and staged after the
+  // first tile store: waiting for them then waits for nothing the store did not already need.
+  uint32_t braw = 0, araw = 0;
   if (threadIdx.x < CH) {
-    const int t = threadIdx.x;
-    const bool ok = t < n;
-    bs[t] = ok ? (beta ? g2_gate<LOG>((float)beta[tk + t]) : 1.f) : 0.f;
-    const float xa = (float)alpha[tk + min(t, n - 1)];  // a valid token also for lanes past the end
-    const float la = ok ? (LOG ? gate_neg_softplus(xa) : logf(xa)) : 0.f;
-    const float g = wave_incl_scan(la);
-    gs[t] = g;
-    Go[u * CH + t] = g;
+    braw = load_gate_raw(beta ? beta + tk : nullptr, n, threadIdx.x);
+    araw = load_gate_raw(alpha + tk, n, threadIdx.x);
   }
   {
     RegTile<E, CH, D, NT> rk, re, rv, rw;
@@ -61,6 +58,16 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
     rw.load(write + tk * D, D, n);
     g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
     rk.store(Ks, LD);
+    if (threadIdx.x < CH) {
+      const int t = threadIdx.x;
+      const bool ok = t < n;
+      bs[t] = ok ? (beta ? g2_gate<LOG>(gate_from_raw<E>(braw)) : 1.f) : 0.f;
+      const float xa = gate_from_raw<E>(araw);
+      const float la = ok ? (LOG ? gate_neg_softplus(xa) : logf(xa)) : 0.f;
+      const float g = wave_incl_scan(la);
+      gs[t] = g;
+      Go[u * CH + t] = g;
+    }
     __syncthreads();
     using RT = decltype(rk);
 #pragma unroll
@@ -215,10 +222,11 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
   // consecutive columns 4 lgrp .. +3 of each 16-column tile, so results go out as vectors.
   const int tr = 16 * wm + lrow();
 
+  float graw = 0.f;  // the gates first, raw; staged after the first tile stores
+  uint32_t braw = 0;
   if (threadIdx.x < CH) {
-    const int t = threadIdx.x;
-    gs[t] = Gg[u * CH + t];
-    bs[t] = t < n ? (beta ? g2_gate<LOG>((float)beta[tk + t]) : 1.f) : 0.f;
+    graw = Gg[u * CH + threadIdx.x];
+    braw = load_gate_raw(beta ? beta + tk : nullptr, n, threadIdx.x);
   }
   {
     RegTile<E, CH, D, NT> rk, re, rv, rw;
@@ -230,6 +238,11 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
     g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
     g2s_rows<E, CH, D, NT>(dRs, LD, dRg + u * CH * D, D, CH);
     rk.store(Ks, LD);
+    if (threadIdx.x < CH) {
+      const int t = threadIdx.x;
+      gs[t] = graw;
+      bs[t] = t < n ? (beta ? g2_gate<LOG>(gate_from_raw<E>(braw)) : 1.f) : 0.f;
+    }
     __syncthreads();
     using RT = decltype(rk);
 #pragma unroll
