@@ -228,18 +228,21 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id(), n = cp.n;
 
+  // beta is loaded before the tiles (raw) and staged after K and Q are: its wait then covers
+  // nothing those stores did not need, where loaded after V it would also wait for V.
+  const uint32_t braw = threadIdx.x < CH ? load_gate_raw(beta + tk, n, threadIdx.x) : 0u;
   RegTile<E, CH, D, NT> rv, rk, rq, ra;
   ra.load(alpha + tk * D, D, n);
   rk.load(k + tk * D, D, n);
   rq.load(q + tk * D, D, n);
   rv.load(v + tk * D, D, n);
-  if (threadIdx.x < CH) {
-    const float b = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
-    bs[threadIdx.x] = (LOG && threadIdx.x < n) ? gate_sigmoid(b) : b;
-  }
   if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
   rk.store(Ks, LD);
   rq.store(Qs, LD);
+  if (threadIdx.x < CH) {
+    const float b = gate_from_raw<E>(braw);  // 0 past the end
+    bs[threadIdx.x] = (LOG && threadIdx.x < n) ? gate_sigmoid(b) : b;
+  }
   kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG, tot);
   kda_flags<D, NT>(Gs, LDG, unsafe);
 
@@ -458,6 +461,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id(), n = cp.n;
 
+  const uint32_t braw = threadIdx.x < CH ? load_gate_raw(beta + tk, n, threadIdx.x) : 0u;  // staged after K
   RegTile<E, CH, D, NT> rv, rdr, rk, ra;
   RegTile<float, CH, D, NT> rdx;
   RegTile<float, CH, CH, NT> rli, raf;
@@ -468,11 +472,11 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   rdx.load(p.kd_dx + u * CH * D, D, CH);
   rli.load(p.Li + u * CH * CH, CH, CH);
   raf.load(p.A1 + u * CH * CH, CH, CH);
+  rk.store(Ks, LD);
   if (threadIdx.x < CH) {
-    const float b = (threadIdx.x < n) ? (float)beta[tk + threadIdx.x] : 0.f;
+    const float b = gate_from_raw<E>(braw);  // 0 past the end
     bs[threadIdx.x] = (LOG && threadIdx.x < n) ? gate_sigmoid(b) : b;
   }
-  rk.store(Ks, LD);
   kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG, tot);
   {  // Khat = e^g K in place, 16 bytes at a time
     constexpr int VE = 16 / (int)sizeof(E);
