@@ -9,7 +9,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/gdr.h"
 #include "launch.hpp"
@@ -280,6 +282,129 @@ struct TraceCall {
   ~TraceCall() { gdr::launch_trace().armed = false; }
 };
 
+// Per-sequence pipelines in the backward.  Packed sequences are independent, and the reverse
+// scan's time is set by the longest one, whose value tiles keep a few CUs busy while the rest of
+// the chip idles.  Cut into contiguous ranges of sequences, each range is a problem of its own
+// (the same kernels with cu_seqlens, the per-unit buffers and the per-sequence states offset to
+// the range) and runs its reverse scan and chunk-parallel gradients on a stream of its own, so
+// the short ranges' gradient kernels fill the CUs the long range's scan leaves idle.  (The
+// forward gains nothing this way: what could fill those CUs is the other ranges' chunk
+// preparation, whose HBM and L2 traffic slows the long scan by as much as it saves.)  Only the
+// delta family with unsegmented scans takes this path (its per-unit buffers are the ones offset
+// here).  GDR_PIPELINE=1 turns it on.
+constexpr int kSide = 3;  // side streams: with the caller's, four hardware queues
+struct Pipes {
+  hipStream_t side[kSide] = {};
+  hipEvent_t fork = nullptr, join[kSide] = {};
+  bool ready = false;
+};
+std::mutex g_pipe_mu;
+Pipes g_pipes[64];
+
+bool pipeline_wanted(const gdr_problem* p, const Sizes& s) {
+  const char* env = std::getenv("GDR_PIPELINE");
+  if (!env || std::atoi(env) != 1) return false;
+  return p->n_seqs >= 2 && (p->variant == GDR_DELTANET || p->variant == GDR_GATED) && s.lseg == 0 &&
+         s.lseg_b == 0;
+}
+
+// Streams and events of the calling thread's current device, created on first use and kept
+// for the life of the process.  Caller holds g_pipe_mu.  NULL if the caller's stream belongs to
+// another device or creation fails (the call then runs on the caller's stream alone).
+Pipes* pipes_for(hipStream_t caller) {
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (hipStreamGetDevice(caller, &sdev) != hipSuccess || sdev != dev) return nullptr;
+  Pipes& pp = g_pipes[dev];
+  if (!pp.ready) {
+    for (int i = 0; i < kSide; ++i) {
+      if (hipStreamCreateWithFlags(&pp.side[i], hipStreamNonBlocking) != hipSuccess) return nullptr;
+      if (hipEventCreateWithFlags(&pp.join[i], hipEventDisableTiming) != hipSuccess) return nullptr;
+    }
+    if (hipEventCreateWithFlags(&pp.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    pp.ready = true;
+  }
+  return &pp;
+}
+
+struct SeqRange {
+  int s0, s1;  // sequences [s0, s1)
+  int c0, nc;  // their first global chunk and chunk count
+  int longest;  // chunks of the longest sequence in the range
+};
+
+// Up to kSide + 1 contiguous ranges of about equal sequence counts, longest range first.
+std::vector<SeqRange> seq_ranges(const gdr_problem* p) {
+  const int n = p->n_seqs, G = std::min(n, kSide + 1);
+  std::vector<SeqRange> r;
+  int c = 0;
+  for (int g = 0; g < G; ++g) {
+    SeqRange x{g * n / G, (g + 1) * n / G, c, 0, 0};
+    for (int i = x.s0; i < x.s1; ++i) {
+      const int len = p->cu_seqlens_host[i + 1] - p->cu_seqlens_host[i];
+      const int ch = (len + gdr::CH - 1) / gdr::CH;
+      x.nc += ch;
+      x.longest = std::max(x.longest, ch);
+    }
+    c += x.nc;
+    r.push_back(x);
+  }
+  std::stable_sort(r.begin(), r.end(), [](const SeqRange& a, const SeqRange& b) { return a.longest > b.longest; });
+  return r;
+}
+
+// The plan of one range: every buffer indexed by unit (chunk * H + head) starts at the range's
+// first chunk, the states at its first sequence.
+gdr::Plan sub_plan(const gdr::Plan& pl, const gdr_problem* p, const Sizes& s, const SeqRange& x) {
+  gdr::Plan q = pl;
+  q.geo.cu = p->cu_seqlens_dev + x.s0;
+  q.geo.nseq = x.s1 - x.s0;
+  q.geo.total_chunks = x.nc;
+  const size_t u = (size_t)x.c0 * p->H, C = gdr::CH, D = (size_t)p->dk, e = s.esz;
+  auto adv = [u](auto* ptr, size_t per_unit_bytes) {
+    using P = decltype(ptr);
+    return ptr ? reinterpret_cast<P>(reinterpret_cast<char*>(ptr) + u * per_unit_bytes) : ptr;
+  };
+  q.X = adv(q.X, C * D * e);
+  q.M = adv(q.M, C * C * e);
+  q.G = adv(q.G, C * 4);
+  q.Hs = adv(q.Hs, D * D * e);
+  q.R = adv(q.R, C * D * e);
+  q.Li = adv(q.Li, C * C * 4);
+  q.A1 = adv(q.A1, C * C * 4);
+  q.Ub = adv(q.Ub, C * D * e);
+  q.dHs = adv(q.dHs, D * D * e);
+  q.dR = adv(q.dR, C * D * e);
+  return q;
+}
+
+float* state_at(const float* st, const gdr_problem* p, int s0) {
+  return st ? const_cast<float*>(st) + (size_t)s0 * p->H * p->dk * p->dv : nullptr;
+}
+
+// Runs body(plan, h0, state_offset_fn, stream) for every range, the first on the caller's
+// stream and the others on side streams forked from it and joined back into it.
+template <typename Body>
+hipError_t run_ranges(const gdr::Plan& pl, const gdr_problem* p, const Sizes& s, hipStream_t caller, Body body) {
+  std::lock_guard<std::mutex> lock(g_pipe_mu);
+  Pipes* pp = pipes_for(caller);
+  if (!pp) return body(pl, SeqRange{0, s.nstates, 0, s.total_chunks, 0}, caller);
+  const std::vector<SeqRange> rs = seq_ranges(p);
+  hipError_t e = hipEventRecord(pp->fork, caller);
+  if (e != hipSuccess) return e;
+  for (size_t i = 1; i < rs.size(); ++i)
+    if ((e = hipStreamWaitEvent(pp->side[i - 1], pp->fork, 0)) != hipSuccess) return e;
+  for (size_t i = 0; i < rs.size(); ++i) {
+    const hipStream_t st = i == 0 ? caller : pp->side[i - 1];
+    if ((e = body(sub_plan(pl, p, s, rs[i]), rs[i], st)) != hipSuccess) return e;
+  }
+  for (size_t i = 1; i < rs.size(); ++i) {
+    if ((e = hipEventRecord(pp->join[i - 1], pp->side[i - 1])) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(caller, pp->join[i - 1], 0)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 namespace gdr {
@@ -372,6 +497,19 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
   hipStream_t hs = static_cast<hipStream_t>(stream);
   g_last_error.clear();
   TraceCall tc;
+  if (pipeline_wanted(p, s)) {
+    return hip_status(run_ranges(pl, p, s, hs, [&](const gdr::Plan& q, const SeqRange& x, hipStream_t sq) {
+      gdr_inputs sub = *in;
+      sub.h0 = state_at(in->h0, p, x.s0);
+      if (!saved) {
+        const hipError_t e = gdr::run_forward(q, sub, nullptr, nullptr, nullptr, false, sq);
+        if (e != hipSuccess) return e;
+      }
+      gdr_grads gs = *g;
+      gs.dh0 = state_at(g->dh0, p, x.s0);
+      return gdr::run_backward(q, sub, dO, dr, state_at(dht, p, x.s0), gs, sq);
+    }), "gdr_backward launch");
+  }
   if (!saved) {
     st = hip_status(gdr::run_forward(pl, *in, nullptr, nullptr, nullptr, false, hs), "gdr_backward recompute launch");
     if (st != GDR_OK) return st;

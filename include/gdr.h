@@ -118,7 +118,14 @@ gdr_status gdr_forward(const gdr_problem *p, const gdr_inputs *in, void *o, floa
 /* Backward of sum(o * dO) + sum(ht * dht).  dO: [B,H,T,dv] I/O dtype (required).
  * dht: [N,H,dv,dk] float32 or NULL (zeros).  saved: the buffer a gdr_forward with the same
  * problem and inputs filled, or NULL to recompute it inside the workspace.
- * ws: gdr_workspace_size(p, 1) bytes.  Gradients are overwritten, not accumulated. */
+ * ws: gdr_workspace_size(p, 1) bytes.  Gradients are overwritten, not accumulated.
+ * With the environment variable GDR_PIPELINE=1, a packed call of the delta family (GDR_DELTANET,
+ * GDR_GATED) whose scans are not segmented runs up to four contiguous ranges of its sequences
+ * on separate streams: the caller's and three side streams the library creates once per device
+ * and keeps (default priority, non-blocking), forked from and joined back into the caller's
+ * stream with events, so the call stays ordered on the caller's stream.  Results are bitwise
+ * those of the single-stream path.  Calls from several host threads are serialised while they
+ * enqueue. */
 gdr_status gdr_backward(const gdr_problem *p, const gdr_inputs *in, const void *dO,
                         const float *dht, const void *saved, gdr_grads *g, void *ws,
                         size_t ws_bytes, void *stream);
