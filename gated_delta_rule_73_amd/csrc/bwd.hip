@@ -59,7 +59,9 @@ struct BwdScanOps<E, D, BV, VAR_KDA> {
 };
 
 // RES (Delta family): the residual r_t = R_t / beta_t was an output too; its gradient dr adds
-// dr_t / beta_t to dR_t before dR feeds the memory gradient and the chunk kernel.
+// dr_t / beta_t to dR_t before dR feeds the memory gradient and the chunk kernel.  dRog, if not
+// NULL, also receives dR without that term (the beta gradient is formed from it, see
+// k_bwd_res_dbeta).
 template <typename E, int D, int BV, int VAR, bool RES>
 __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ dO, const E* __restrict__ Xg,
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
                                                   const float* __restrict__ dht, E* __restrict__ dHs,
                                                   E* __restrict__ dRg, float* __restrict__ dh0,
                                                   const E* __restrict__ beta, const E* __restrict__ erase,
-                                                  const E* __restrict__ drin) {
+                                                  const E* __restrict__ drin, E* __restrict__ dRog) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2 || VAR == VAR_GDN2L;
@@ -90,6 +92,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   __shared__ __align__(16) E dWs[BV * LD];
   __shared__ __align__(16) E dRt[CH * LDO];   // -dR, row-major, read like dO
   __shared__ __align__(16) E dRn[CH * LDV];   // dR
+  __shared__ __align__(16) E dRo[RES ? CH * LDV : 8];  // dR without the residual's term
   __shared__ float gs[CH];
 
   constexpr int NVR = D / BV;
@@ -243,18 +246,24 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
       const f32x4 a1 = mma_k<E, CH>(zero4(), colk(dOt, LDO), 16 * it, colk(Ms, LDR), 16 * w);
       const f32x4 a2 = mma_k<E, D>(zero4(), rowk(dWs, LD), 16 * it, rowk(G2 ? As : Ks, LD), 16 * w);
       f32x4 dr = a1 + dec * a2;
+      const int c4 = 16 * it + 4 * lgrp();
       if constexpr (RES) {  // + dr / beta for the rows of this chunk (none for the linear part)
+        put4(dRo + tl * LDV + c4, dr);
         const bool ok = tl < n && !virt;
         const float binv = ok ? 1.f / (float)p.braw : 0.f;
         const E* x = reinterpret_cast<const E*>(&p.dr[it]);
         dr += binv * f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
       }
-      const int c4 = 16 * it + 4 * lgrp();
       put4(dRt + tl * LDO + c4, -dr);
       put4(dRn + tl * LDV + c4, dr);
     }
     __syncthreads();
-    if (snap) s2g_full<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV);
+    if (snap) {
+      s2g_full<E, CH, BV, NT>(dRg + u * CH * D + i0, D, dRn, LDV);
+      if constexpr (RES) {
+        if (dRog) s2g_full<E, CH, BV, NT>(dRog + u * CH * D + i0, D, dRo, LDV);
+      }
+    }
     load(p, c - 2, 1);
     float eg = 1.f;
     if constexpr (DEC) eg = __expf(gn);
@@ -757,6 +766,159 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------
+// The beta gradient when the residual r = R / beta was an output (its gradient dr given).
+// ---------------------------------------------------------------------------------------
+// Fed with dR + dr / beta, the chunk kernel's beta gradient holds two terms of order
+// |dr| |r| / beta that cancel exactly (the dr / beta in dR against the -dr.R / beta^2 of
+// r = R / beta), and with bfloat16 operands their rounding is larger than the result at small
+// beta.  The sum is linear, so the beta gradient is instead formed as
+//   dbeta = F(dR_o) + G,
+// where dR_o = M^T dO + Kbar dW^T is dR without the residual's term and F is the chunk
+// kernel's beta gradient for a given dR,
+//   dT = dR_o Y^T (Y = V - Khat W0^T = r + A R, since R = L^{-1} diag(beta) Y),
+//   F_s = sum_t dT_ts Linv_ts + sum_s' dL_ss' A_ss',  dL = -strictlower(L^-T dT diag(beta) L^-T),
+// and G is the residual's own term, from r = Lt^{-1} Y with Lt = I + A diag(beta):
+//   dY = Lt^-T dr = diag(beta) L^-T (dr / beta),  G_s = -r_s . (A^T dY)_s.
+// Neither part carries a term of order 1 / beta that another cancels.  The chunk kernel's
+// beta gradient is overwritten.  One workgroup of 256 threads per (chunk, head).
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_bwd_res_dbeta(Geo geo, const E* __restrict__ Rg, const E* __restrict__ dRog,
+                                                       const E* __restrict__ drin, const E* __restrict__ beta,
+                                                       const float* __restrict__ Ag, const float* __restrict__ Lig,
+                                                       E* __restrict__ dbeta) {
+  constexpr int NT = 256, LD = D + pad16<E>(), LF = CH + 4, NW = NT / 64;
+  constexpr int TE = CH * LD, TF = CH * LF;
+  __shared__ __align__(16) E Rs[TE], dRos[TE], Ds[TE], Ys[TE];  // Ys later holds dY
+  __shared__ __align__(16) float As[TF], Lis[TF], dTs[TF], Pts[TF];
+  __shared__ float bs[CH], binv[CH], colp[NW][CH], rowp[CH], gz[CH];
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int n = cp.n, w = wave_id();
+
+  const uint32_t braw = threadIdx.x < CH ? load_gate_raw(beta + tk, n, threadIdx.x) : 0u;
+  {
+    RegTile<E, CH, D, NT> rR, rO, rd;
+    RegTile<float, CH, CH, NT> rA, rL;
+    rR.load(Rg + u * CH * D, D, CH);
+    rO.load(dRog + u * CH * D, D, CH);
+    rA.load(Ag + u * CH * CH, CH, CH);
+    rL.load(Lig + u * CH * CH, CH, CH);
+    rd.load(drin + tk * D, D, n);
+    rR.store(Rs, LD);
+    rO.store(dRos, LD);
+    if (threadIdx.x < CH) {
+      const float b = gate_from_raw<E>(braw);  // 0 past the end
+      bs[threadIdx.x] = b;
+      binv[threadIdx.x] = threadIdx.x < n ? 1.f / b : 0.f;
+    }
+    rA.store(As, LF);
+    rL.store(Lis, LF);
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < decltype(rd)::IT; ++it) {  // dr / beta, zero past the end
+      const int r = rd.row(it), c = rd.col(it);
+      const float bi = binv[r];
+#pragma unroll
+      for (int x = 0; x < decltype(rd)::VE; ++x) Ds[r * LD + c + x] = (E)((float)rd.elem(it, x) * bi);
+    }
+  }
+  // Y = R / beta + A R; wave w forms rows 16 w .. 16 w + 15
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    f32x4 y = mma_k<E, CH>(zero4(), rowk(As, LF), 16 * w, colk(Rs, LD), 16 * nt);
+    const int j = acc_col(16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * w, r);
+      y[r] += (float)Rs[t * LD + j] * binv[t];
+    }
+    store4_n(Ys, LD, 16 * w, 16 * nt, y);
+  }
+  __syncthreads();
+  // dT = dR_o Y^T on and below the diagonal
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const f32x4 a = mma_k<E, D>(zero4(), rowk(dRos, LD), 16 * w, rowk(Ys, LD), 16 * nt);
+    const int sc = acc_col(16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = acc_row(16 * w, r);
+      dTs[t * LF + sc] = sc <= t ? a[r] : 0.f;
+    }
+  }
+  __syncthreads();
+  {  // F from T = Linv diag(beta): column sums, four threads per column
+    const int sc = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
+    float a = 0.f;
+    for (int t = pt; t < CH; t += NW) a += dTs[t * LF + sc] * Lis[t * LF + sc];
+    colp[pt][sc] = a;
+  }
+  // Pt = (dT diag(beta)) Linv^T, stored transposed
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * w, rowk(Lis, LF), 16 * nt);
+    store4_t(Pts, LF, 16 * w, 16 * nt, acc);
+  }
+  __syncthreads();
+  // dL = -strictlower(Linv^T Pt) over dT
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const f32x4 acc = mma_k<E, CH>(zero4(), colk(Lis, LF), 16 * w, rowk(Pts, LF), 16 * nt);
+    f32x4 dl;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[r] = (acc_col(16 * nt) < acc_row(16 * w, r)) ? -acc[r] : 0.f;
+    store4_n(dTs, LF, 16 * w, 16 * nt, dl);
+  }
+  // dY = diag(beta) Linv^T (dr / beta), over Y (free once dT is formed)
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) {
+    f32x4 y = mma_k<E, CH>(zero4(), colk(Lis, LF), 16 * w, colk(Ds, LD), 16 * nt);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] *= bs[acc_row(16 * w, r)];
+    store4_n(Ys, LD, 16 * w, 16 * nt, y);
+  }
+  __syncthreads();
+  if (threadIdx.x < CH) {  // F from L = I + diag(beta) A: row sums
+    const int t = threadIdx.x;
+    float a = 0.f;
+    for (int sc = 0; sc < t; ++sc) a += dTs[t * LF + sc] * As[t * LF + sc];
+    rowp[t] = a;
+  }
+  {  // G_s = -sum_j r_sj (A^T dY)_sj for the rows 16 w .. 16 w + 15 of this wave
+    f32x4 g = zero4();
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+      const f32x4 z = mma_k<E, CH>(zero4(), colk(As, LF), 16 * w, colk(Ys, LD), 16 * nt);
+      const int j = acc_col(16 * nt);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) g[r] += (float)Rs[acc_row(16 * w, r) * LD + j] * z[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) g[r] += __shfl_xor(g[r], off, 64);
+    }
+    if (lrow() == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int sr = acc_row(16 * w, r);
+        gz[sr] = -g[r] * binv[sr];
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < n) {
+    const int t = threadIdx.x;
+    float db = rowp[t] + gz[t];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) db += colp[i][t];
+    dbeta[tk + t] = (E)db;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------------------
 template <typename E, int D, int VAR>
@@ -769,10 +931,13 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
   const float* gin = KDA ? p.Gn : p.G;
   constexpr bool RES_OK = VAR == VAR_DELTANET || VAR == VAR_GATED;  // residual gradient: Delta family
   const E* drp = RES_OK ? (const E*)dr : nullptr;
+  // bfloat16 I/O forms the beta gradient of a residual output apart (k_bwd_res_dbeta), from dR
+  // without the residual's term, which the scan then also records, over U (not read backward)
+  E* dro = (RES_OK && drp && std::is_same<E, bf16>::value) ? (E*)p.Ub : nullptr;
   auto launch = [&](auto kern, int bv, const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult, const E* d) {
     hipLaunchKernelGGL(kern, dim3(scan_grid(g, nv_mult * D / bv), sg.mode ? sg.max_seg : 1), dim3(256), 0, st, g, sg,
                        qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp, (E*)p.dHs, (E*)p.dR, dh0p,
-                       (const E*)in.beta, (const E*)in.erase, d);
+                       (const E*)in.beta, (const E*)in.erase, d, d ? dro : nullptr);
   };
   auto scan = [&](const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult) {
     if (p.bv == 16) {
@@ -816,6 +981,15 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
       if (drp) chunk(k_bwd_chunk<E, D, VAR, true, false>);
       else if (p.gates) chunk(k_bwd_chunk<E, D, VAR, false, true>);
       else chunk(k_bwd_chunk<E, D, VAR, false, false>);
+    }
+    if constexpr (RES_OK) {
+      if (dro) {
+        TraceScope ts_("bwd_res_dbeta", st);
+        const auto kern = k_bwd_res_dbeta<E, D>;
+        hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(256), 0, st, g, (const E*)p.R,
+                           (const E*)dro, drp, (const E*)in.beta, (const float*)p.A1, (const float*)p.Li,
+                           (E*)gr.dbeta);
+      }
     }
   }
   return hipGetLastError();

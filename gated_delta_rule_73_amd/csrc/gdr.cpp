@@ -469,11 +469,6 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
   if (!g) return fail(GDR_ERR_INVALID_ARG, "grads is NULL");
   if (dr && p->variant != GDR_DELTANET && p->variant != GDR_GATED)
     return fail(GDR_ERR_UNSUPPORTED, "the residual gradient is built for DeltaNet and Gated DeltaNet");
-  // dr enters as dR += dr / beta; the beta gradient then holds two terms of order |dr| |r| / beta
-  // that cancel, and with bfloat16 operands their rounding leaves errors above the tolerance at
-  // small beta.  float32 I/O keeps them accurate.
-  if (dr && p->dtype != GDR_F32)
-    return fail(GDR_ERR_UNSUPPORTED, "the residual gradient is built for float32 I/O only");
   if (dr && p->gates) return fail(GDR_ERR_UNSUPPORTED, "the residual gradient takes gate values, not logits");
   if (dr && !aligned(dr, 16)) return fail(GDR_ERR_INVALID_ARG, "dr must be 16-byte aligned");
   if (p->T > 0) {

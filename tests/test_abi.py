@@ -218,10 +218,15 @@ def test_residual_checks(lib):
     st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE, None, None,
                                    ctypes.byref(_grads()), FAKE, 1 << 40, None)
     assert st == bd.GDR_ERR_UNSUPPORTED
-    p = _problem()  # bfloat16 I/O: the residual gradient is not built
+    p = _problem()  # logit gates: the residual gradient takes gate values
+    p.gates = 1
     st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE, None, None,
                                    ctypes.byref(_grads()), FAKE, 1 << 40, None)
     assert st == bd.GDR_ERR_UNSUPPORTED
+    p = _problem()  # bfloat16 I/O is built; a misaligned dr is still refused before any launch
+    st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE + 2, None, None,
+                                   ctypes.byref(_grads()), FAKE, 1 << 40, None)
+    assert st == bd.GDR_ERR_INVALID_ARG
     p = _problem(dtype=0, dk=64, dv=64)
     st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE + 4, None, None,
                                    ctypes.byref(_grads()), FAKE, 1 << 40, None)

@@ -57,7 +57,8 @@ def test_residual_forward(variant, dtype, d):
     print("\n".join(rep))
 
 
-BWD = [(v, dt, d, s) for v in ("deltanet", "gated") for dt, d in (("f32", 64),) for s in (True, False)]
+BWD = [(v, dt, d, s) for v in ("deltanet", "gated") for dt, d in (("f32", 64), ("bf16", 128), ("bf16", 64))
+       for s in (True, False)]
 
 
 @pytest.mark.parametrize("variant,dtype,d,use_saved", BWD,
@@ -117,8 +118,35 @@ def test_residual_unsupported_variants():
         gdr_backward(**g, do=to_gpu(inp["do"], "f32"), dr=to_gpu(inp["dr"], "f32"), variant="kda")
     inp = _inputs("gated", "bf16", 128, T=64)
     g = gpu_inputs(inp, "bf16")
-    with pytest.raises(GdrError):  # bfloat16 residual gradient: not built
-        gdr_backward(**g, do=to_gpu(inp["do"], "bf16"), dr=to_gpu(inp["dr"], "bf16"), variant="gated")
+    with pytest.raises(GdrError):  # the residual gradient takes gate values, not logits
+        gdr_backward(**g, do=to_gpu(inp["do"], "bf16"), dr=to_gpu(inp["dr"], "bf16"), variant="gated",
+                     gate_logits=True)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gated"])
+def test_residual_backward_bf16_small_beta(variant):
+    """bfloat16 residual gradient where beta is small (about 0.02 to 0.08): the regime in which
+    dR + dr / beta leaves two beta-gradient terms of order |dr| |r| / beta that cancel; the beta
+    gradient is formed without them."""
+    inp = _inputs(variant, "bf16", 128, T=200, seed=45)
+    inp["beta"] = synth.to_io(np.asarray(inp["beta"], np.float64) * 0.08, "bf16")
+    rep = []
+    compare(_hip(inp, variant, "bf16", True), _oracle(inp, variant, True), "bf16", report=rep)
+    print("\n".join(rep))
+
+
+def test_residual_backward_bf16_packed_segmented():
+    """Packed sequences (one empty, ragged tails) with segmented scans forced: dR without the
+    residual's term is recorded by the rerun pass."""
+    import os
+    cu = [0, 70, 70, 200, 333]
+    inp = _inputs("gated", "bf16", 128, T=333, B=1, H=3, cu=cu)
+    os.environ["GDR_SEG_CHUNKS"] = "1"
+    try:
+        got = _hip(inp, "gated", "bf16", True)
+    finally:
+        del os.environ["GDR_SEG_CHUNKS"]
+    compare(got, _oracle(inp, "gated", True), "bf16")
 
 
 @pytest.mark.parametrize("variant", ["gated", "kda"])
