@@ -33,11 +33,14 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 COPY_CAL_BYTES = 256 << 20   # size of the calibration copy (read + write of this many bytes)
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, published
 
-def kernel_bytes_per_unit(variant: str, kernel: str, D: int = 128, esz: int = 2, has_beta: bool = True) -> int:
+def kernel_bytes_per_unit(variant: str, kernel: str, D: int = 128, esz: int = 2, has_beta: bool = True,
+                          residual: bool = False) -> int:
     """Bytes a kernel must read and write once per (chunk, head) unit: its inputs and outputs,
     each touched once (C = 64 tokens, head size D, I/O element size esz).  The per-chunk
     intermediates the kernels hand to each other (X, U, M, R, memories, float32 partial
-    gradients) are inputs and outputs of the kernels that use them."""
+    gradients) are inputs and outputs of the kernels that use them.  residual: the forward also
+    writes r and the backward reads its gradient dr (with bfloat16 I/O the reverse scan then also
+    writes dR without the residual's term, for the separate beta gradient)."""
     C = 64
     TOK, SQR, GRAM, GATE = C * D * esz, D * D * esz, C * C * esz, C * esz
     GLOG, FTOK, FGRAM, FD = C * 4, C * D * 4, C * C * 4, D * 4
@@ -62,21 +65,27 @@ def kernel_bytes_per_unit(variant: str, kernel: str, D: int = 128, esz: int = 2,
         "bwd_gdn2_gram": 3 * TOK + BETA + ALPHA + GLOG + 2 * GRAM + 6 * FGRAM + 3 * FTOK + 4 * GLOG
                          + 3 * TOK + BETA + ALPHA,
         "fwd_seg_combine": 0, "bwd_seg_combine": 0,
+        "bwd_res_dbeta": 3 * TOK + BETA + 2 * FGRAM + BETA,
     }
+    if residual:
+        table["fwd_scan"] += TOK
+        table["bwd_scan"] += TOK + BETA + (TOK if esz == 2 else 0)
+        table["bwd_chunk"] += TOK
     if kernel in ("fwd_scan_maps", "bwd_scan_maps"):  # no per-chunk records, twice the value tiles
         base = table[kernel[:8]] - (SQR + TOK + (OUT if kernel.startswith("fwd") else 0))
         return base
     return table[kernel]
 
 
-def path_bytes_per_head_token(variant: str, D: int = 128, esz: int = 2, has_beta: bool = True) -> int:
+def path_bytes_per_head_token(variant: str, D: int = 128, esz: int = 2, has_beta: bool = True,
+                              residual: bool = False) -> int:
     """The operator's own minimum per head-token: the forward reads q, k, v and the gates and
     writes o; the backward reads q, k, v, the gates and dO and writes the gradients of q, k,
-    v and of every gate (Gated, d = 128, bf16: 2828 bytes)."""
+    v and of every gate (Gated, d = 128, bf16: 2828 bytes).  residual: r written, dr read."""
     tok = D * esz
     beta = esz if has_beta else 0
     gates = beta + {"deltanet": 0, "gated": esz, "kda": tok, "gdn2": esz + 2 * tok}[variant]
-    return (3 * tok + gates + tok) + (4 * tok + gates + 3 * tok + gates)
+    return (3 * tok + gates + tok) + (4 * tok + gates + 3 * tok + gates) + (2 * tok if residual else 0)
 
 
 def source_sha() -> str:
@@ -123,7 +132,8 @@ def cpu_baseline(w):
 
 class Runner:
     """Holds the device buffers of one workload and calls the C ABI directly.  residual: the
-    forward also writes r = v - v_bar (gdr_forward_residual); gate_logits: beta and alpha are
+    forward also writes r = v - v_bar (gdr_forward_residual) and the backward takes a seeded
+    standard-normal gradient dr of it (gdr_backward_residual); gate_logits: beta and alpha are
     logits, activated inside the kernels."""
 
     def __init__(self, w, inp, residual: bool = False, gate_logits: bool = False):
@@ -143,6 +153,10 @@ class Runner:
         dev = g["q"].device
         self.o = torch.empty_like(g["v"])
         self.r = torch.empty_like(g["v"]) if residual else None
+        self.dr = None
+        if residual:
+            import numpy as np
+            self.dr = to_gpu(np.random.default_rng(w.seed + 17).standard_normal(inp["v"].shape), w.dtype)
         self.ht = torch.empty((N, w.H, w.dv, w.dk), dtype=torch.float32, device=dev)
         self.saved = torch.empty(bd.gdr_saved_size(self.p), dtype=torch.uint8, device=dev)
         nws = bd.gdr_workspace_size(self.p, True)
@@ -163,9 +177,10 @@ class Runner:
         self.bd._check(self.lib, st)
 
     def bwd(self):
-        st = self.lib.gdr_backward(ctypes.byref(self.p), ctypes.byref(self.ins), self.do.data_ptr(), None,
-                                   self.saved.data_ptr(), ctypes.byref(self.gr), self.ws.data_ptr(),
-                                   self.ws.numel(), self.stream)
+        st = self.lib.gdr_backward_residual(ctypes.byref(self.p), ctypes.byref(self.ins), self.do.data_ptr(),
+                                            None if self.dr is None else self.dr.data_ptr(), None,
+                                            self.saved.data_ptr(), ctypes.byref(self.gr), self.ws.data_ptr(),
+                                            self.ws.numel(), self.stream)
         self.bd._check(self.lib, st)
 
     calls = property(lambda self: (self.fwd, self.bwd))
@@ -309,7 +324,7 @@ def main():
     ap.add_argument("--workload", default="gated_varlen_T32768")
     ap.add_argument("--sweep", action="store_true", help="also time the T = 4k..32k sweep at B*T = 32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--residual", action="store_true", help="the forward also writes the residual r = v - v_bar")
+    ap.add_argument("--residual", action="store_true", help="the forward also writes the residual r = v - v_bar and the backward takes its gradient")
     ap.add_argument("--gate-logits", action="store_true", help="beta and alpha given as logits")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -349,10 +364,11 @@ def main():
     units = chunks * w.H
     per_launch_units = units  # each launch of any kernel covers every (chunk, head) unit once
     esz = 2 if w.dtype == "bf16" else 4
-    kbytes = kernel_bytes_per_unit(w.variant, dom, w.dk, esz, w.has_beta) * per_launch_units
+    kbytes = kernel_bytes_per_unit(w.variant, dom, w.dk, esz, w.has_beta, args.residual) * per_launch_units
     achieved = kbytes / (avg_ms / 1e3) / 1e9
-    traffic = measured_traffic(dom, w.name)
-    path_bytes = path_bytes_per_head_token(w.variant, w.dk, esz, w.has_beta) * tokens * w.H
+    # counters are recorded for the plain workload only (other kernel instances run with these switches)
+    traffic = None if (args.residual or args.gate_logits) else measured_traffic(dom, w.name)
+    path_bytes = path_bytes_per_head_token(w.variant, w.dk, esz, w.has_beta, args.residual) * tokens * w.H
     path_gbs = path_bytes / (ms / 1e3) / 1e9
     out = {
         "metric": "tokens/s chunked gated-delta-rule fwd+bwd, H=16 d=128, T=4k-32k; % of roofline",

@@ -780,22 +780,23 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 // and G is the residual's own term, from r = Lt^{-1} Y with Lt = I + A diag(beta):
 //   dY = Lt^-T dr = diag(beta) L^-T (dr / beta),  G_s = -r_s . (A^T dY)_s.
 // Neither part carries a term of order 1 / beta that another cancels.  The chunk kernel's
-// beta gradient is overwritten.  One workgroup of 256 threads per (chunk, head).
+// beta gradient is overwritten.  One workgroup of 512 threads per (chunk, head).
 template <typename E, int D>
-__global__ __launch_bounds__(256) void k_bwd_res_dbeta(Geo geo, const E* __restrict__ Rg, const E* __restrict__ dRog,
+__global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restrict__ Rg, const E* __restrict__ dRog,
                                                        const E* __restrict__ drin, const E* __restrict__ beta,
                                                        const float* __restrict__ Ag, const float* __restrict__ Lig,
                                                        E* __restrict__ dbeta) {
-  constexpr int NT = 256, LD = D + pad16<E>(), LF = CH + 4, NW = NT / 64;
+  constexpr int NT = 512, LD = D + pad16<E>(), LF = CH + 4, NW = NT / 64;
+  constexpr int NH = D / 32;  // column tiles of a 64 x D product per wave (two waves per row block)
   constexpr int TE = CH * LD, TF = CH * LF;
   __shared__ __align__(16) E Rs[TE], dRos[TE], Ds[TE], Ys[TE];  // Ys later holds dY
   __shared__ __align__(16) float As[TF], Lis[TF], dTs[TF], Pts[TF];
-  __shared__ float bs[CH], binv[CH], colp[NW][CH], rowp[CH], gz[CH];
+  __shared__ float bs[CH], binv[CH], colp[NW][CH], rowp[CH], gz[2][CH];
   const int gc = blockIdx.x, h = blockIdx.y;
   const ChunkPos cp = chunk_pos(geo, gc);
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
-  const int n = cp.n, w = wave_id();
+  const int n = cp.n, wm = wave_id() & 3, wn = wave_id() >> 2;  // row block, column half
 
   const uint32_t braw = threadIdx.x < CH ? load_gate_raw(beta + tk, n, threadIdx.x) : 0u;
   {
@@ -824,32 +825,34 @@ __global__ __launch_bounds__(256) void k_bwd_res_dbeta(Geo geo, const E* __restr
       for (int x = 0; x < decltype(rd)::VE; ++x) Ds[r * LD + c + x] = (E)((float)rd.elem(it, x) * bi);
     }
   }
-  // Y = R / beta + A R; wave w forms rows 16 w .. 16 w + 15
+  // Y = R / beta + A R; wave (wm, wn) forms rows 16 wm .. 16 wm + 15, column tiles of half wn
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    f32x4 y = mma_k<E, CH>(zero4(), rowk(As, LF), 16 * w, colk(Rs, LD), 16 * nt);
+  for (int q = 0; q < NH; ++q) {
+    const int nt = wn * NH + q;
+    f32x4 y = mma_k<E, CH>(zero4(), rowk(As, LF), 16 * wm, colk(Rs, LD), 16 * nt);
     const int j = acc_col(16 * nt);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * w, r);
+      const int t = acc_row(16 * wm, r);
       y[r] += (float)Rs[t * LD + j] * binv[t];
     }
-    store4_n(Ys, LD, 16 * w, 16 * nt, y);
+    store4_n(Ys, LD, 16 * wm, 16 * nt, y);
   }
   __syncthreads();
   // dT = dR_o Y^T on and below the diagonal
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const f32x4 a = mma_k<E, D>(zero4(), rowk(dRos, LD), 16 * w, rowk(Ys, LD), 16 * nt);
+  for (int q = 0; q < 2; ++q) {
+    const int nt = 2 * wn + q;
+    const f32x4 a = mma_k<E, D>(zero4(), rowk(dRos, LD), 16 * wm, rowk(Ys, LD), 16 * nt);
     const int sc = acc_col(16 * nt);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * w, r);
+      const int t = acc_row(16 * wm, r);
       dTs[t * LF + sc] = sc <= t ? a[r] : 0.f;
     }
   }
   __syncthreads();
-  {  // F from T = Linv diag(beta): column sums, four threads per column
+  {  // F from T = Linv diag(beta): column sums, eight threads per column
     const int sc = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
     for (int t = pt; t < CH; t += NW) a += dTs[t * LF + sc] * Lis[t * LF + sc];
@@ -857,27 +860,30 @@ __global__ __launch_bounds__(256) void k_bwd_res_dbeta(Geo geo, const E* __restr
   }
   // Pt = (dT diag(beta)) Linv^T, stored transposed
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * w, rowk(Lis, LF), 16 * nt);
-    store4_t(Pts, LF, 16 * w, 16 * nt, acc);
+  for (int q = 0; q < 2; ++q) {
+    const int nt = 2 * wn + q;
+    const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * wm, rowk(Lis, LF), 16 * nt);
+    store4_t(Pts, LF, 16 * wm, 16 * nt, acc);
   }
   __syncthreads();
   // dL = -strictlower(Linv^T Pt) over dT
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const f32x4 acc = mma_k<E, CH>(zero4(), colk(Lis, LF), 16 * w, rowk(Pts, LF), 16 * nt);
+  for (int q = 0; q < 2; ++q) {
+    const int nt = 2 * wn + q;
+    const f32x4 acc = mma_k<E, CH>(zero4(), colk(Lis, LF), 16 * wm, rowk(Pts, LF), 16 * nt);
     f32x4 dl;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dl[r] = (acc_col(16 * nt) < acc_row(16 * w, r)) ? -acc[r] : 0.f;
-    store4_n(dTs, LF, 16 * w, 16 * nt, dl);
+    for (int r = 0; r < 4; ++r) dl[r] = (acc_col(16 * nt) < acc_row(16 * wm, r)) ? -acc[r] : 0.f;
+    store4_n(dTs, LF, 16 * wm, 16 * nt, dl);
   }
   // dY = diag(beta) Linv^T (dr / beta), over Y (free once dT is formed)
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    f32x4 y = mma_k<E, CH>(zero4(), colk(Lis, LF), 16 * w, colk(Ds, LD), 16 * nt);
+  for (int q = 0; q < NH; ++q) {
+    const int nt = wn * NH + q;
+    f32x4 y = mma_k<E, CH>(zero4(), colk(Lis, LF), 16 * wm, colk(Ds, LD), 16 * nt);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] *= bs[acc_row(16 * w, r)];
-    store4_n(Ys, LD, 16 * w, 16 * nt, y);
+    for (int r = 0; r < 4; ++r) y[r] *= bs[acc_row(16 * wm, r)];
+    store4_n(Ys, LD, 16 * wm, 16 * nt, y);
   }
   __syncthreads();
   if (threadIdx.x < CH) {  // F from L = I + diag(beta) A: row sums
@@ -886,14 +892,15 @@ __global__ __launch_bounds__(256) void k_bwd_res_dbeta(Geo geo, const E* __restr
     for (int sc = 0; sc < t; ++sc) a += dTs[t * LF + sc] * As[t * LF + sc];
     rowp[t] = a;
   }
-  {  // G_s = -sum_j r_sj (A^T dY)_sj for the rows 16 w .. 16 w + 15 of this wave
+  {  // G_s = -sum_j r_sj (A^T dY)_sj: rows 16 wm .. 16 wm + 15, columns of half wn
     f32x4 g = zero4();
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
-      const f32x4 z = mma_k<E, CH>(zero4(), colk(As, LF), 16 * w, colk(Ys, LD), 16 * nt);
+    for (int q = 0; q < NH; ++q) {
+      const int nt = wn * NH + q;
+      const f32x4 z = mma_k<E, CH>(zero4(), colk(As, LF), 16 * wm, colk(Ys, LD), 16 * nt);
       const int j = acc_col(16 * nt);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) g[r] += (float)Rs[acc_row(16 * w, r) * LD + j] * z[r];
+      for (int r = 0; r < 4; ++r) g[r] += (float)Rs[acc_row(16 * wm, r) * LD + j] * z[r];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -903,15 +910,15 @@ __global__ __launch_bounds__(256) void k_bwd_res_dbeta(Geo geo, const E* __restr
     if (lrow() == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int sr = acc_row(16 * w, r);
-        gz[sr] = -g[r] * binv[sr];
+        const int sr = acc_row(16 * wm, r);
+        gz[wn][sr] = -g[r] * binv[sr];
       }
     }
   }
   __syncthreads();
   if (threadIdx.x < n) {
     const int t = threadIdx.x;
-    float db = rowp[t] + gz[t];
+    float db = rowp[t] + gz[0][t] + gz[1][t];
 #pragma unroll
     for (int i = 0; i < NW; ++i) db += colp[i][t];
     dbeta[tk + t] = (E)db;
@@ -986,7 +993,7 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
       if (dro) {
         TraceScope ts_("bwd_res_dbeta", st);
         const auto kern = k_bwd_res_dbeta<E, D>;
-        hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(256), 0, st, g, (const E*)p.R,
+        hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, (const E*)p.R,
                            (const E*)dro, drp, (const E*)in.beta, (const float*)p.A1, (const float*)p.Li,
                            (E*)gr.dbeta);
       }
