@@ -56,9 +56,11 @@ struct BwdScanOps<E, D, BV, VAR_KDA> {
   RegTile<E, CH, CH, 256> m;
   RegTile<E, CH, BV, 256> dO;
   f32x4 eg[D / 64];
+  typename VecT<4 * sizeof(E)>::type dr[BV / 16];  // as in the general case (RES)
+  E braw;
 };
 
-// RES (Delta family): the residual r_t = R_t / beta_t was an output too; its gradient dr adds
+// RES (delta family, Kimi Delta Attention): the residual r_t = R_t / beta_t was an output too; its gradient dr adds
 // dr_t / beta_t to dR_t before dR feeds the memory gradient and the chunk kernel.  dRog, if not
 // NULL, also receives dR without that term (the beta gradient is formed from it, see
 // k_bwd_res_dbeta).
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   constexpr bool G2L = VAR == VAR_GDN2L;  // its gates are logits
   constexpr bool KDA = VAR == VAR_KDA;
   constexpr bool DEC = VAR == VAR_GATED || G2;  // scalar decay
-  static_assert(!RES || VAR == VAR_DELTANET || VAR == VAR_GATED, "residual gradient: Delta family");
+  static_assert(!RES || VAR == VAR_DELTANET || VAR == VAR_GATED || KDA, "residual gradient: no GDN-2");
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];  // a = beta e*k (GDN-2)
   __shared__ float bsh[CH];
   __shared__ __align__(16) E Qs[CH * LD];
@@ -936,11 +938,14 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
   const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
   const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
   const float* gin = KDA ? p.Gn : p.G;
-  constexpr bool RES_OK = VAR == VAR_DELTANET || VAR == VAR_GATED;  // residual gradient: Delta family
+  // residual gradient: delta family and Kimi Delta Attention (whose residual has the same form)
+  constexpr bool RES_OK = VAR == VAR_DELTANET || VAR == VAR_GATED || KDA;
   const E* drp = RES_OK ? (const E*)dr : nullptr;
-  // bfloat16 I/O forms the beta gradient of a residual output apart (k_bwd_res_dbeta), from dR
-  // without the residual's term, which the scan then also records, over U (not read backward)
-  E* dro = (RES_OK && drp && std::is_same<E, bf16>::value) ? (E*)p.Ub : nullptr;
+  // The beta gradient of a residual output is formed apart (k_bwd_res_dbeta) from dR without the
+  // residual's term, which the scan then also records, over U (not read backward): with
+  // bfloat16 I/O for the delta family, whose chunk kernel otherwise adds the direct term itself,
+  // and always for Kimi Delta Attention, whose backward stages take no residual.
+  E* dro = (RES_OK && drp && (KDA || std::is_same<E, bf16>::value)) ? (E*)p.Ub : nullptr;
   auto launch = [&](auto kern, int bv, const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult, const E* d) {
     hipLaunchKernelGGL(kern, dim3(scan_grid(g, nv_mult * D / bv), sg.mode ? sg.max_seg : 1), dim3(256), 0, st, g, sg,
                        qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp, (E*)p.dHs, (E*)p.dR, dh0p,
@@ -976,7 +981,8 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
     if constexpr (VAR == VAR_GDN2 || VAR == VAR_GDN2L) {
       return launch_bwd_gdn2<E, D>(p, in, dO, gr, st);
     } else if constexpr (VAR == VAR_KDA) {
-      return launch_bwd_kda<E, D>(p, in, dO, gr, st);
+      const hipError_t e = launch_bwd_kda<E, D>(p, in, dO, gr, st);
+      if (e != hipSuccess) return e;
     } else {
       TraceScope ts_("bwd_chunk", st);
       auto chunk = [&](auto kern) {

@@ -467,8 +467,8 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
   if (st != GDR_OK) return st;
   if ((st = check_inputs(p, in)) != GDR_OK) return st;
   if (!g) return fail(GDR_ERR_INVALID_ARG, "grads is NULL");
-  if (dr && p->variant != GDR_DELTANET && p->variant != GDR_GATED)
-    return fail(GDR_ERR_UNSUPPORTED, "the residual gradient is built for DeltaNet and Gated DeltaNet");
+  if (dr && p->variant == GDR_GDN2)
+    return fail(GDR_ERR_UNSUPPORTED, "Gated DeltaNet-2 has no residual output, hence no residual gradient");
   if (dr && p->gates) return fail(GDR_ERR_UNSUPPORTED, "the residual gradient takes gate values, not logits");
   if (dr && !aligned(dr, 16)) return fail(GDR_ERR_INVALID_ARG, "dr must be 16-byte aligned");
   if (p->T > 0) {

@@ -147,10 +147,11 @@ gdr_status gdr_forward_residual(const gdr_problem *p, const gdr_inputs *in, void
 
 /* Backward of sum(o * dO) + sum(r * dr) + sum(ht * dht), r the residual output of
  * gdr_forward_residual.  dr: [B,H,T,d_v] in the I/O dtype, or NULL (then this is
- * gdr_backward).  Built for GDR_DELTANET and GDR_GATED with gate values (gates == 0); other
- * variants, and logit gates, with dr != NULL return UNSUPPORTED.  With bfloat16 I/O the beta
- * gradient is formed in a second pass from dR without the residual's term plus the residual's
- * own term (no two large terms left to cancel); the workspace size is that of gdr_backward.
+ * gdr_backward).  Built for GDR_DELTANET, GDR_GATED and GDR_KDA with gate values (gates == 0);
+ * GDR_GDN2, and logit gates, with dr != NULL return UNSUPPORTED.  With bfloat16 I/O (and for
+ * GDR_KDA always) the beta gradient is formed in a second pass from dR without the residual's
+ * term plus the residual's own term (no two large terms left to cancel); the workspace size is
+ * that of gdr_backward.
  * Needs beta_t > 0 as above.  Every other argument as for gdr_backward. */
 gdr_status gdr_backward_residual(const gdr_problem *p, const gdr_inputs *in, const void *dO, const void *dr,
                                  const float *dht, const void *saved, gdr_grads *g, void *ws,

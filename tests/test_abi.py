@@ -214,9 +214,9 @@ def test_residual_checks(lib):
     st = lib.gdr_forward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE + 8, None, None, FAKE,
                                   1 << 40, None)
     assert st == bd.GDR_ERR_INVALID_ARG
-    p = _problem(variant=2)  # KDA: the residual's gradient is not built
-    st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE, None, None,
-                                   ctypes.byref(_grads()), FAKE, 1 << 40, None)
+    p = _problem(variant=3)  # GDN-2: no residual output, hence no residual gradient
+    st = lib.gdr_backward_residual(ctypes.byref(p), ctypes.byref(_inputs(erase=FAKE, write=FAKE)), FAKE, FAKE,
+                                   None, None, ctypes.byref(_grads(derase=FAKE, dwrite=FAKE)), FAKE, 1 << 40, None)
     assert st == bd.GDR_ERR_UNSUPPORTED
     p = _problem()  # logit gates: the residual gradient takes gate values
     p.gates = 1

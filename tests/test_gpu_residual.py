@@ -57,7 +57,7 @@ def test_residual_forward(variant, dtype, d):
     print("\n".join(rep))
 
 
-BWD = [(v, dt, d, s) for v in ("deltanet", "gated") for dt, d in (("f32", 64), ("bf16", 128), ("bf16", 64))
+BWD = [(v, dt, d, s) for v in ("deltanet", "gated", "kda") for dt, d in (("f32", 64), ("bf16", 128), ("bf16", 64))
        for s in (True, False)]
 
 
@@ -112,10 +112,10 @@ def test_residual_unsupported_variants():
     g = gpu_inputs(inp, "bf16")
     with pytest.raises(GdrError):
         gdr_forward(**g, variant="gdn2", residual=torch.empty_like(g["v"]))
-    inp = _inputs("kda", "f32", 64, T=64)
+    inp = _inputs("gdn2", "f32", 64, T=64)
     g = gpu_inputs(inp, "f32")
-    with pytest.raises(GdrError):
-        gdr_backward(**g, do=to_gpu(inp["do"], "f32"), dr=to_gpu(inp["dr"], "f32"), variant="kda")
+    with pytest.raises(GdrError):  # no residual output, hence no residual gradient
+        gdr_backward(**g, do=to_gpu(inp["do"], "f32"), dr=to_gpu(inp["dr"], "f32"), variant="gdn2")
     inp = _inputs("gated", "bf16", 128, T=64)
     g = gpu_inputs(inp, "bf16")
     with pytest.raises(GdrError):  # the residual gradient takes gate values, not logits
@@ -123,7 +123,7 @@ def test_residual_unsupported_variants():
                      gate_logits=True)
 
 
-@pytest.mark.parametrize("variant", ["deltanet", "gated"])
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda"])
 def test_residual_backward_bf16_small_beta(variant):
     """bfloat16 residual gradient where beta is small (about 0.02 to 0.08): the regime in which
     dR + dr / beta leaves two beta-gradient terms of order |dr| |r| / beta that cancel; the beta
@@ -135,18 +135,19 @@ def test_residual_backward_bf16_small_beta(variant):
     print("\n".join(rep))
 
 
-def test_residual_backward_bf16_packed_segmented():
+@pytest.mark.parametrize("variant", ["gated", "kda"])
+def test_residual_backward_bf16_packed_segmented(variant):
     """Packed sequences (one empty, ragged tails) with segmented scans forced: dR without the
     residual's term is recorded by the rerun pass."""
     import os
     cu = [0, 70, 70, 200, 333]
-    inp = _inputs("gated", "bf16", 128, T=333, B=1, H=3, cu=cu)
+    inp = _inputs(variant, "bf16", 128, T=333, B=1, H=3, cu=cu)
     os.environ["GDR_SEG_CHUNKS"] = "1"
     try:
-        got = _hip(inp, "gated", "bf16", True)
+        got = _hip(inp, variant, "bf16", True)
     finally:
         del os.environ["GDR_SEG_CHUNKS"]
-    compare(got, _oracle(inp, "gated", True), "bf16")
+    compare(got, _oracle(inp, variant, True), "bf16")
 
 
 @pytest.mark.parametrize("variant", ["gated", "kda"])
