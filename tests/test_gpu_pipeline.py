@@ -53,6 +53,22 @@ def test_pipelined_equals_single_stream(monkeypatch, variant, dtype, d, cu, use_
         assert np.array_equal(got[k], ref[k], equal_nan=True), k
 
 
+@pytest.mark.parametrize("variant", ["deltanet", "gated"])
+def test_pipelined_residual_bf16_equals_single_stream(monkeypatch, variant):
+    """bfloat16 residual gradient (its beta gradient formed in a second pass from dR without the
+    residual's term, recorded per range) through the pipelines: bitwise the single-stream result."""
+    cu = (0, 64 * 3 + 7, 64 * 5, 64 * 11 + 40)
+    w = synth.Workload("pipe", variant, "bf16", 1, 2, cu[-1], 128, 128, seed=64, h0_std=0.1, cu_seqlens=cu)
+    inp = synth.make_inputs(w, alpha_mode="weak")
+    dr = synth.to_io(np.random.default_rng(65).standard_normal(inp["v"].shape), "bf16")
+    monkeypatch.delenv("GDR_PIPELINE", raising=False)
+    ref = _run(inp, variant, "bf16", True, 1.0, dr=dr)
+    monkeypatch.setenv("GDR_PIPELINE", "1")
+    got = _run(inp, variant, "bf16", True, 1.0, dr=dr)
+    for k in ref:
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
+
+
 def test_pipelined_residual_against_oracle(monkeypatch):
     from oracle import recurrence as R
     cu = (0, 64 + 9, 64 * 4, 64 * 6 + 2)
