@@ -79,3 +79,38 @@ def test_fullsize_sampled(name, samples):
         print("  literal max|err| <= 2e-2 holds for: "
               + ", ".join(k for k, e in lit.items() if e <= 2e-2)
               + " | exceeds (scaled rule applies): " + ", ".join(k for k, e in lit.items() if e > 2e-2), flush=True)
+
+
+def test_fullsize_residual_sampled():
+    """The residual output and its gradient at the packed long-context workload's full size, in
+    the configuration `bench.py --residual` times (forward writing r and keeping the cache, then
+    the backward taking dr); sampled (sequence, head) pairs against the oracle."""
+    import torch
+    from gated_delta_rule_73_amd import gdr_backward, gdr_forward
+    from oracle import recurrence as R
+    from tests._helpers import gpu_inputs, to_gpu, to_np
+    w = synth.WORKLOADS["gated_varlen_T32768"]
+    inp = synth.make_inputs(w)
+    dr = synth.to_io(np.random.default_rng(w.seed + 17).standard_normal(inp["v"].shape), w.dtype)
+    g = gpu_inputs(inp, w.dtype)
+    cu = inp["cu_seqlens"]
+    r = torch.empty_like(g["v"])
+    o, ht, saved = gdr_forward(**g, variant=w.variant, cu_seqlens=cu, save=True, residual=r)
+    grads = gdr_backward(**g, do=to_gpu(inp["do"], w.dtype), dr=to_gpu(dr, w.dtype), variant=w.variant,
+                         cu_seqlens=cu, saved=saved)
+    torch.cuda.synchronize()
+    got = {"o": to_np(o), "ht": to_np(ht), "r": to_np(r), **{k: to_np(v) for k, v in grads.items()}}
+    for s, h in [(0, 0), (2, 9), (3, 15)]:
+        b, t0, t1 = _span(w, inp, s)
+        kw = {n: (None if inp.get(n) is None else inp[n][b:b + 1, h:h + 1, t0:t1])
+              for n in ("q", "k", "v", "beta", "alpha", "erase", "write")}
+        kw["h0"] = inp["h0"][s:s + 1, h:h + 1]
+        do, drs = inp["do"][b:b + 1, h:h + 1, t0:t1], dr[b:b + 1, h:h + 1, t0:t1]
+        oo, hh, rr = R.forward(**kw, variant=w.variant, residual=True)
+        ref = {"o": oo, "ht": hh, "r": rr}
+        ref.update(R.backward(**kw, do=do, dr=drs, variant=w.variant))
+        sub = _hip_sample(w, inp, got, s, h)
+        sub["r"] = got["r"][b:b + 1, h:h + 1, t0:t1]
+        rep = []
+        compare(sub, ref, w.dtype, report=rep)
+        print(f"sample (sequence {s}, head {h}):\n" + "\n".join(rep), flush=True)
