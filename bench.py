@@ -50,12 +50,12 @@ def kernel_bytes_per_unit(variant: str, kernel: str, D: int = 128, esz: int = 2,
     DEC = FD if kda else GLOG  # per-chunk decay handed to the scans
     OUT = TOK + GRAM + TOK  # the forward scan also reads q and M and writes o
     table = {
-        "fwd_prep": 3 * TOK + BETA + ALPHA + 2 * TOK + GRAM + GLOG + 2 * FGRAM,
+        "fwd_prep": 3 * TOK + BETA + ALPHA + 2 * TOK + GRAM + GLOG + FGRAM,
         "fwd_prep_kda": 3 * TOK + BETA + ALPHA + 4 * TOK + GRAM + FD + 2 * FGRAM,
         "fwd_prep_gdn2": 5 * TOK + BETA + ALPHA + 3 * TOK + 2 * GRAM + GLOG + 3 * FGRAM,
         "fwd_scan": (6 * TOK + BETA if g2 else 3 * TOK) + DEC + SQR + TOK + OUT + (GRAM if g2 else 0),
         "bwd_scan": 3 * TOK + TOK + GRAM + DEC + SQR + TOK + ((TOK + BETA) if g2 else 0),
-        "bwd_chunk": 4 * TOK + BETA + ALPHA + GRAM + GLOG + 2 * SQR + 2 * TOK + 3 * TOK + BETA + ALPHA + 2 * FGRAM,
+        "bwd_chunk": 4 * TOK + BETA + ALPHA + GRAM + GLOG + 2 * SQR + 2 * TOK + 3 * TOK + BETA + ALPHA + FGRAM,
         "bwd_kda_state": 3 * TOK + 2 * SQR + FD + 3 * FTOK + FGRAM + FD,
         "bwd_kda_wy": 3 * TOK + BETA + ALPHA + FTOK + 2 * FGRAM + TOK + BETA + FTOK + FGRAM,
         "bwd_kda_gram": 2 * TOK + ALPHA + 2 * FGRAM + 3 * FTOK + FD + 2 * TOK + ALPHA,
@@ -65,7 +65,8 @@ def kernel_bytes_per_unit(variant: str, kernel: str, D: int = 128, esz: int = 2,
         "bwd_gdn2_gram": 3 * TOK + BETA + ALPHA + GLOG + 2 * GRAM + 6 * FGRAM + 3 * FTOK + 4 * GLOG
                          + 3 * TOK + BETA + ALPHA,
         "fwd_seg_combine": 0, "bwd_seg_combine": 0,
-        "bwd_res_dbeta": 3 * TOK + BETA + 2 * FGRAM + BETA,
+        # the delta family forms A from K and the log decays; Kimi Delta Attention reads it
+        "bwd_res_dbeta": 3 * TOK + BETA + (2 * FGRAM if kda else TOK + GLOG + FGRAM) + BETA,
     }
     if residual:
         table["fwd_scan"] += TOK
@@ -281,7 +282,16 @@ def make_events(n):
     return evs
 
 
-def timed(runner, steps: int, warmup: int, trace: bool = True, trace_every: int = 4):
+TRACE_EVERY = 4
+
+
+def traced_steps(steps: int, trace_every: int = TRACE_EVERY) -> int:
+    """How many of `steps` timed steps timed() brackets with events (the last and every
+    trace_every-th before it)."""
+    return (steps - 1) // trace_every + 1
+
+
+def timed(runner, steps: int, warmup: int, trace: bool = True, trace_every: int = TRACE_EVERY):
     """Warm up, then time `steps` steps between two events (synchronized on both sides).
     With trace, every kernel launch of every `trace_every`-th timed step (counted back from the
     last, which is always traced) is bracketed by its own event pair.  The event records stall
@@ -390,7 +400,7 @@ def main():
                      "algorithmic_bytes_per_launch": kbytes},
         "path_roofline": {"bound": "hbm", "algorithmic_bytes_per_step": path_bytes, "achieved": round(path_gbs, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
-        "kernels_ms_per_step": {k: round(v / args.steps, 4) for k, v in tot.items()},
+        "kernels_ms_per_step": {k: round(v / traced_steps(args.steps), 4) for k, v in tot.items()},
     }
     if args.sweep:
         sw = {}

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
                                                    const E* __restrict__ Mg, const float* __restrict__ Gg,
                                                    const E* __restrict__ Hs, const E* __restrict__ Rg,
                                                    const E* __restrict__ dHs, const E* __restrict__ dRg,
-                                                   const float* __restrict__ Ag, const float* __restrict__ Lig,
+                                                   const float* __restrict__ Lig,
                                                    E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
                                                    E* __restrict__ dbeta, E* __restrict__ dalpha,
                                                    const E* __restrict__ drin) {
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   RegTile<E, KH, D, NT> pW, pdW;      // one 64-row block of W0 and of dW, next block prefetched
   RegTile<E, CH, D, NT> pV, pQ;       // V and Q, used in later phases
   RegTile<E, CH, CH, NT> pM;          // M, used for the decay gradient
-  RegTile<float, CH, CH, NT> pA, pLi;  // the forward's A and L^{-1}, used in phase 2
+  RegTile<float, CH, CH, NT> pLi;     // the forward's L^{-1}, used in phase 2
   // The per-token decay and beta are loaded before the tiles and staged after the first tile
   // stores: waiting for them then waits for nothing else, where loaded after the tiles they
   // would make the staging wait for every tile in flight (the wait counters are ordered).
@@ -418,7 +418,6 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       pV.load(v + tk * D, D, n);
       pQ.load(q + tk * D, D, n);
       pM.load(Mg + u * CH * CH, CH, CH);
-      pA.load(Ag + u * CH * CH, CH, CH);
       pLi.load(Lig + u * CH * CH, CH, CH);
       if constexpr (RES) {  // dr_t . R_t per row, from the registers: a row is VPR adjacent lanes
         RegTile<E, CH, D, NT> rd;
@@ -527,8 +526,28 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   float* Li = reinterpret_cast<float*>(smem + Ly::oLi);
   E* Vs = reinterpret_cast<E*>(smem + Ly::oVP);
   pV.store(Vs, LD);
-  pA.store(As, LF);  // A and L^{-1} as the forward computed them
-  pLi.store(Li, LF);
+  pLi.store(Li, LF);  // L^{-1} as the forward computed it
+  // A (strictly lower) formed again from K as the forward formed it (the same products of the
+  // same operands, so the same values): 16 KiB less to write forward and to read here
+  for (int job = w; job < 10; job += NT / 64) {
+    int mt, nt;
+    tri_tile(job, mt, nt);
+    const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * nt, rowk(Ks, LD), 16 * mt);
+    const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
+    float val[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sc = s0 + r;
+      float dec = 1.f;
+      if constexpr (GATED) dec = __expf(gs[t] - gs[sc]);
+      val[r] = sc < t ? acc[r] * dec : 0.f;
+    }
+    *reinterpret_cast<float4*>(As + t * LF + s0) = make_float4(val[0], val[1], val[2], val[3]);
+  }
+  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // tiles above the diagonal
+    const int t = idx >> 4, s0 = (idx & 15) * 4;
+    if ((s0 >> 4) > (t >> 4)) *reinterpret_cast<float4*>(As + t * LF + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   E* Lb = reinterpret_cast<E*>(smem + Ly::oLb);
   E* Tb = reinterpret_cast<E*>(smem + Ly::oTb);
   if constexpr (Ly::BCOPY) {  // from the registers: L^{-1} and L^{-1} diag(beta) in bfloat16
@@ -783,17 +802,20 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 //   dY = Lt^-T dr = diag(beta) L^-T (dr / beta),  G_s = -r_s . (A^T dY)_s.
 // Neither part carries a term of order 1 / beta that another cancels.  The chunk kernel's
 // beta gradient is overwritten.  One workgroup of 512 threads per (chunk, head).
-template <typename E, int D>
+// OWN_A (delta family): A is formed from K and the log decays as the forward formed it (the
+// forward keeps no copy); otherwise (Kimi Delta Attention) it is read from the forward's cache.
+template <typename E, int D, bool OWN_A>
 __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restrict__ Rg, const E* __restrict__ dRog,
                                                        const E* __restrict__ drin, const E* __restrict__ beta,
-                                                       const float* __restrict__ Ag, const float* __restrict__ Lig,
+                                                       const float* __restrict__ Ag, const E* __restrict__ k,
+                                                       const float* __restrict__ Gg, const float* __restrict__ Lig,
                                                        E* __restrict__ dbeta) {
   constexpr int NT = 512, LD = D + pad16<E>(), LF = CH + 4, NW = NT / 64;
   constexpr int NH = D / 32;  // column tiles of a 64 x D product per wave (two waves per row block)
   constexpr int TE = CH * LD, TF = CH * LF;
   __shared__ __align__(16) E Rs[TE], dRos[TE], Ds[TE], Ys[TE];  // Ys later holds dY
   __shared__ __align__(16) float As[TF], Lis[TF], dTs[TF], Pts[TF];
-  __shared__ float bs[CH], binv[CH], colp[NW][CH], rowp[CH], gz[2][CH];
+  __shared__ float bs[CH], binv[CH], colp[NW][CH], rowp[CH], gz[2][CH], gs[OWN_A ? CH : 1];
   const int gc = blockIdx.x, h = blockIdx.y;
   const ChunkPos cp = chunk_pos(geo, gc);
   const long u = (long)gc * geo.H + h;
@@ -801,24 +823,51 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
   const int n = cp.n, wm = wave_id() & 3, wn = wave_id() >> 2;  // row block, column half
 
   const uint32_t braw = threadIdx.x < CH ? load_gate_raw(beta + tk, n, threadIdx.x) : 0u;
+  float graw = 0.f;
+  if constexpr (OWN_A) {
+    if (threadIdx.x < CH) graw = Gg[u * CH + threadIdx.x];
+  }
   {
-    RegTile<E, CH, D, NT> rR, rO, rd;
+    RegTile<E, CH, D, NT> rR, rO, rd, rk;
     RegTile<float, CH, CH, NT> rA, rL;
+    if constexpr (OWN_A) rk.load(k + tk * D, D, n);
+    else rA.load(Ag + u * CH * CH, CH, CH);
     rR.load(Rg + u * CH * D, D, CH);
     rO.load(dRog + u * CH * D, D, CH);
-    rA.load(Ag + u * CH * CH, CH, CH);
     rL.load(Lig + u * CH * CH, CH, CH);
     rd.load(drin + tk * D, D, n);
+    if constexpr (OWN_A) rk.store(Ys, LD);  // K, in the region Y takes later
     rR.store(Rs, LD);
     rO.store(dRos, LD);
     if (threadIdx.x < CH) {
       const float b = gate_from_raw<E>(braw);  // 0 past the end
       bs[threadIdx.x] = b;
       binv[threadIdx.x] = threadIdx.x < n ? 1.f / b : 0.f;
+      if constexpr (OWN_A) gs[threadIdx.x] = graw;
     }
-    rA.store(As, LF);
+    if constexpr (!OWN_A) rA.store(As, LF);
     rL.store(Lis, LF);
     __syncthreads();
+    if constexpr (OWN_A) {  // A = strictlower(K K^T) e^{g_t - g_s}, the forward's products
+      const int w = wave_id();
+      for (int job = w; job < 10; job += NT / 64) {
+        int mt, nt;
+        tri_tile(job, mt, nt);
+        const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ys, LD), 16 * nt, rowk(Ys, LD), 16 * mt);
+        const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
+        float val[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sc = s0 + r;
+          val[r] = sc < t ? acc[r] * __expf(gs[t] - gs[sc]) : 0.f;
+        }
+        *reinterpret_cast<float4*>(As + t * LF + s0) = make_float4(val[0], val[1], val[2], val[3]);
+      }
+      for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {
+        const int t = idx >> 4, s0 = (idx & 15) * 4;
+        if ((s0 >> 4) > (t >> 4)) *reinterpret_cast<float4*>(As + t * LF + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
 #pragma unroll
     for (int it = 0; it < decltype(rd)::IT; ++it) {  // dr / beta, zero past the end
       const int r = rd.row(it), c = rd.col(it);
@@ -827,6 +876,7 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
       for (int x = 0; x < decltype(rd)::VE; ++x) Ds[r * LD + c + x] = (E)((float)rd.elem(it, x) * bi);
     }
   }
+  __syncthreads();  // A complete (and, with OWN_A, K read) before Y overwrites K
   // Y = R / beta + A R; wave (wm, wn) forms rows 16 wm .. 16 wm + 15, column tiles of half wn
 #pragma unroll
   for (int q = 0; q < NH; ++q) {
@@ -988,7 +1038,7 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
       auto chunk = [&](auto kern) {
         hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, (const E*)in.q, (const E*)in.k,
                            (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (const E*)dO, (const E*)p.M,
-                           (const float*)p.G, (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR, p.A1,
+                           (const float*)p.G, (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR,
                            p.Li, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta, (E*)gr.dalpha, drp);
       };
       if (drp) chunk(k_bwd_chunk<E, D, VAR, true, false>);
@@ -998,10 +1048,10 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
     if constexpr (RES_OK) {
       if (dro) {
         TraceScope ts_("bwd_res_dbeta", st);
-        const auto kern = k_bwd_res_dbeta<E, D>;
+        const auto kern = k_bwd_res_dbeta<E, D, !KDA>;
         hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, (const E*)p.R,
-                           (const E*)dro, drp, (const E*)in.beta, (const float*)p.A1, (const float*)p.Li,
-                           (E*)gr.dbeta);
+                           (const E*)dro, drp, (const E*)in.beta, (const float*)p.A1, kin, gin,
+                           (const float*)p.Li, (E*)gr.dbeta);
       }
     }
   }

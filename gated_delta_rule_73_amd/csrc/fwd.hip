@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
                                                   const E* __restrict__ v, const E* __restrict__ beta,
                                                   const E* __restrict__ alpha, E* __restrict__ Xo,
                                                   E* __restrict__ Uo, E* __restrict__ Mo, float* __restrict__ Go,
-                                                  float* __restrict__ Lio, float* __restrict__ Ao) {
+                                                  float* __restrict__ Lio) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   static_assert(CH * LDT * (int)sizeof(E) >= 4 * 256 * 4, "T buffer doubles as the solve's scratch");
   __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g * K, then X
@@ -101,7 +101,6 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
     } else {
       const float bt = bs[t];
       *reinterpret_cast<float4*>(Ls + t * LF + s0) = make_float4(bt * val[0], bt * val[1], bt * val[2], bt * val[3]);
-      *reinterpret_cast<float4*>(Ao + (u * CH + t) * CH + s0) = make_float4(val[0], val[1], val[2], val[3]);
     }
   }
   for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // tiles above the diagonal
@@ -112,7 +111,6 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
       } else {
         *reinterpret_cast<float4*>(Mo + (u * CH + t) * CH + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
       }
-      *reinterpret_cast<float4*>(Ao + (u * CH + t) * CH + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   __syncthreads();
@@ -478,7 +476,7 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
       TraceScope ts_("fwd_prep", st);
       auto prep = [&](auto kern) {
         hipLaunchKernelGGL(kern, cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k, (const E*)in.v,
-                           (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G, p.Li, p.A1);
+                           (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G, p.Li);
       };
       if (p.gates) prep(k_fwd_prep<E, D, VAR, true>);
       else prep(k_fwd_prep<E, D, VAR, false>);

@@ -159,7 +159,8 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   s.M2 = g2 ? align_up(U * C * C * s.esz, A) : 0;
   s.U2 = g2 ? align_up(U * C * D * s.esz, A) : 0;
   s.Li = align_up(U * C * C * 4, A);
-  s.A1 = align_up(U * C * C * 4, A);
+  // the delta family's backward forms A again from K (see k_bwd_chunk); the others keep it
+  s.A1 = (g2 || kda) ? align_up(U * C * C * 4, A) : 0;
   s.A2 = g2 ? align_up(U * C * C * 4, A) : 0;
   s.Kb = kda ? align_up(U * C * D * s.esz, A) : 0;
   s.Qh = kda ? align_up(U * C * D * s.esz, A) : 0;
@@ -229,7 +230,7 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
   pl.M2 = c; c += s.M2;
   pl.U2 = c; c += s.U2;
   pl.Li = reinterpret_cast<float*>(c); c += s.Li;
-  pl.A1 = reinterpret_cast<float*>(c); c += s.A1;
+  pl.A1 = s.A1 ? reinterpret_cast<float*>(c) : nullptr; c += s.A1;
   pl.A2 = reinterpret_cast<float*>(c); c += s.A2;
   pl.Kb = c; c += s.Kb;
   pl.Qh = c; c += s.Qh;

@@ -27,7 +27,8 @@ struct Plan {
   void* M2;   // Gated DeltaNet-2: [units][64][64] decayed causal Q K^T (M holds Q A^T)
   void* U2;   // Gated DeltaNet-2: [units][64][D]  -L^{-1} A_kk B
   float* Li;  // [units][64][64] L^{-1} (float32) of the chunk's unit lower-triangular L
-  float* A1;  // [units][64][64] the chunk's strictly lower Gram (float32): A, or GDN-2's A_kk
+  float* A1;  // [units][64][64] the chunk's strictly lower Gram (float32): KDA's A or GDN-2's A_kk
+              // (NULL for the delta family, whose backward forms A again from K)
   float* A2;  // Gated DeltaNet-2: [units][64][64] A_ak (float32)
   void* Kb;   // Kimi Delta Attention: [units][64][D] Kbar = e^{g_n - g} K
   void* Qh;   // Kimi Delta Attention: [units][64][D] Qhat = e^g Q

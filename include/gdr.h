@@ -105,7 +105,9 @@ gdr_status gdr_workspace_size(const gdr_problem *p, int backward, size_t *bytes)
 
 /* Bytes of the optional forward->backward buffer: the forward's per-chunk WY factor X, the
  * decayed causal Gram M, the in-chunk cumulative log decay, the memory at the start of every
- * chunk and the scaled residuals R (all in the I/O dtype except the log decay, float32).
+ * chunk, the scaled residuals R (all in the I/O dtype except the log decay, float32), and the
+ * float32 inverse L^{-1} of the chunk's triangular factor (Kimi Delta Attention and Gated
+ * DeltaNet-2 also keep their key Grams and per-channel or erase-gate factors).
  * Errors: INVALID_ARG, UNSUPPORTED. */
 gdr_status gdr_saved_size(const gdr_problem *p, size_t *bytes);
 

@@ -64,7 +64,8 @@ def test_workspace_sizes(lib):
     assert lib.gdr_saved_size(ctypes.byref(p), ctypes.byref(n)) == bd.GDR_OK
     units = 8 * 64 * 8
     per = 64 * 128 * 2
-    cache = units * (per + 64 * 64 * 2 + 64 * 4 + 128 * 128 * 2 + per + 2 * 64 * 64 * 4)
+    # X, M, log decays, chunk-start memories, R, and L^{-1} (float32); the backward forms A again
+    cache = units * (per + 64 * 64 * 2 + 64 * 4 + 128 * 128 * 2 + per + 64 * 64 * 4)
     assert n.value == cache
     assert fwd == cache + units * per
     assert bwd == fwd + units * (128 * 128 * 2 + per)

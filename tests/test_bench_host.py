@@ -25,3 +25,11 @@ def test_byte_models():
     w = synth.DECODE_WORKLOADS["gated_decode_B512H16"]
     # 512 x 16 float32 memories read and written, plus q, k, v, o, beta, alpha per head-token
     assert bench.decode_bytes(w, 2) == 2 * 512 * 16 * 128 * 128 * 4 + 512 * 16 * (4 * 128 * 2 + 2 + 2)
+
+
+def test_traced_steps_counts_the_sampled_steps():
+    import bench
+    for steps in (1, 3, 4, 5, 20, 21):
+        want = sum(1 for i in range(steps) if (steps - 1 - i) % bench.TRACE_EVERY == 0)
+        assert bench.traced_steps(steps) == want
+    assert bench.traced_steps(20) == 5
