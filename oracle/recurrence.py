@@ -130,10 +130,28 @@ def _check(variant, q, k, v, beta, alpha, erase, write):
         raise ValueError("beta is required by the delta family")
 
 
+def l2_normalize(x):
+    """x / ||x||_2 over the last axis (a zero row stays zero): queries and keys of unit length,
+    so that the delta rule's rank-1 factor I - beta k k^T has its eigenvalue 1 - beta in (0, 1)."""
+    x = _f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
+def l2_normalize_backward(x, dy):
+    """Gradient w.r.t. x of sum(y * dy), y = l2_normalize(x): (dy - y (y . dy)) / ||x||."""
+    x, dy = _f64(x), _f64(dy)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    y = np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+    g = dy - y * np.sum(y * dy, axis=-1, keepdims=True)
+    return np.divide(g, n, out=np.zeros_like(g), where=n > 0)
+
+
 def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
-            variant, cu_seqlens=None, scale=1.0, residual=False):
+            variant, cu_seqlens=None, scale=1.0, residual=False, qk_l2norm=False):
     """Run the recurrence.  Returns (o [B,H,T,dv], ht [N,H,dv,dk]) in float64, and with
     residual=True also r [B,H,T,dv], r_t = v_t - v_bar_t (delta family only).
+    qk_l2norm: q and k are first scaled to unit length per token (l2_normalize).
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] (None -> 1, gdn2 only);
     alpha: None (deltanet), [B,H,T] (gated, gdn2) or [B,H,T,dk] (kda);
@@ -141,6 +159,8 @@ def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
     where N = B, or the number of packed sequences when cu_seqlens is given (then B == 1).
     """
     q, k, v, beta, alpha, erase, write, h0 = map(_f64, (q, k, v, beta, alpha, erase, write, h0))
+    if qk_l2norm:
+        q, k = l2_normalize(q), l2_normalize(k)
     _check(variant, q, k, v, beta, alpha, erase, write)
     if residual and variant == "gdn2":
         raise ValueError("gdn2 has separate erase and write terms, not one residual")
@@ -162,7 +182,8 @@ def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
 
 
 def backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do=None,
-             dht=None, *, variant, cu_seqlens=None, scale=1.0, checkpoint_every=64, dr=None):
+             dht=None, *, variant, cu_seqlens=None, scale=1.0, checkpoint_every=64, dr=None,
+             qk_l2norm=False):
     """Gradients of sum(o * do) + sum(ht * dht) [+ sum(r * dr), r the residual output of
     forward(residual=True), when dr is given] by manual reverse mode through the recurrence.
 
@@ -171,9 +192,16 @@ def backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do
     steps, so the result does not depend on the checkpoint spacing).
     Returns a dict with dq, dk, dv, dbeta, dalpha, derase, dwrite, dh0 (None where
     the input is absent).  dalpha is the gradient with respect to alpha itself.
+    qk_l2norm: as in forward; dq and dk are then w.r.t. the raw q and k.
     """
     q, k, v, beta, alpha, erase, write, h0, do, dht, dr = map(
         _f64, (q, k, v, beta, alpha, erase, write, h0, do, dht, dr))
+    if qk_l2norm:
+        g = backward(l2_normalize(q), l2_normalize(k), v, beta, alpha, erase, write, h0, do, dht,
+                     variant=variant, cu_seqlens=cu_seqlens, scale=scale,
+                     checkpoint_every=checkpoint_every, dr=dr)
+        g["dq"], g["dk"] = l2_normalize_backward(q, g["dq"]), l2_normalize_backward(k, g["dk"])
+        return g
     _check(variant, q, k, v, beta, alpha, erase, write)
     if dr is not None and variant == "gdn2":
         raise ValueError("gdn2 has separate erase and write terms, not one residual")

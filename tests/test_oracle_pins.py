@@ -393,3 +393,45 @@ def test_residual_refused_for_gdn2():
     x = _rand_inputs(rng, "gdn2", T=3)
     with pytest.raises(ValueError):
         R.forward(**x, variant="gdn2", residual=True)
+
+
+# q/k L2-normalisation (q, k scaled to unit length per token before the recurrence)
+def test_l2_normalize_unit_length_and_zero_row():
+    x = np.array([[3.0, 4.0], [0.0, 0.0], [-1e-3, 0.0]])
+    y = R.l2_normalize(x)
+    np.testing.assert_allclose(y, [[0.6, 0.8], [0.0, 0.0], [-1.0, 0.0]], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2"])
+def test_qk_l2norm_scale_invariance(variant):
+    """Normalised queries and keys make the outputs independent of each token's q and k scale."""
+    rng = np.random.default_rng(31)
+    x = _rand_inputs(rng, variant, B=1, H=2, T=6, dk=3, dv=4, unit_keys=False)
+    o1, h1 = R.forward(**x, variant=variant, qk_l2norm=True)
+    y = dict(x)
+    y["q"] = x["q"] * rng.uniform(0.1, 5.0, size=x["q"].shape[:-1] + (1,))
+    y["k"] = x["k"] * rng.uniform(0.1, 5.0, size=x["k"].shape[:-1] + (1,))
+    o2, h2 = R.forward(**y, variant=variant, qk_l2norm=True)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(h1, h2, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("variant", ["gated", "kda", "gdn2"])
+def test_qk_l2norm_backward_matches_finite_differences(variant):
+    rng = np.random.default_rng(32)
+    x = _rand_inputs(rng, variant, B=1, H=1, T=5, dk=3, dv=2, unit_keys=False)
+    G = rng.standard_normal((1, 1, 5, 2))
+
+    def loss(xx):
+        o, _ = R.forward(**xx, variant=variant, qk_l2norm=True)
+        return float(np.sum(o * G))
+
+    g = R.backward(**x, do=G, variant=variant, qk_l2norm=True)
+    for name in ("q", "k"):
+        num = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp, xm = dict(x), dict(x)
+            xp[name] = x[name].copy(); xp[name][idx] += 1e-6
+            xm[name] = x[name].copy(); xm[name][idx] -= 1e-6
+            num[idx] = (loss(xp) - loss(xm)) / 2e-6
+        np.testing.assert_allclose(g["d" + name], num, rtol=1e-6, atol=1e-8)
