@@ -25,7 +25,7 @@ class GdrProblem(ctypes.Structure):
     _fields_ = [("variant", _i32), ("dtype", _i32), ("B", _i32), ("H", _i32), ("T", _i32),
                 ("dk", _i32), ("dv", _i32), ("chunk", _i32), ("n_seqs", _i32),
                 ("cu_seqlens_host", ctypes.POINTER(_i32)), ("cu_seqlens_dev", _vp),
-                ("scale", ctypes.c_float), ("gates", _i32)]
+                ("scale", ctypes.c_float), ("gates", _i32), ("qk_norm", _i32)]
 
 
 class GdrInputs(ctypes.Structure):
@@ -92,9 +92,10 @@ def _ptr(t) -> Optional[int]:
 
 
 def make_problem(q, v, *, variant: str, cu_seqlens=None, scale: float = 1.0, chunk: int = 64,
-                 gate_logits: bool = False):
+                 gate_logits: bool = False, qk_norm: bool = False):
     """Build a GdrProblem from the query and value tensors ([B,H,T,dk], [B,H,T,dv]).
     gate_logits: beta and alpha are logits (beta = sigmoid(x), alpha = exp(-softplus(x))).
+    qk_norm: q and k are scaled to unit length per token inside the library.
 
     cu_seqlens: None, or a sequence / CPU tensor of n+1 int offsets.  Returns (problem,
     keepalive) where keepalive holds the host and device copies of the offsets."""
@@ -104,7 +105,7 @@ def make_problem(q, v, *, variant: str, cu_seqlens=None, scale: float = 1.0, chu
     keep = []
     p = GdrProblem(variant=VARIANTS[variant], dtype=DTYPES[dtype], B=B, H=H, T=T, dk=dk,
                    dv=v.shape[-1], chunk=chunk, n_seqs=0, cu_seqlens_host=None, cu_seqlens_dev=None,
-                   scale=float(scale), gates=int(bool(gate_logits)))
+                   scale=float(scale), gates=int(bool(gate_logits)), qk_norm=int(bool(qk_norm)))
     if cu_seqlens is not None:
         host = torch.as_tensor(cu_seqlens, dtype=torch.int32).cpu().contiguous()
         dev = host.to(q.device)
@@ -141,14 +142,15 @@ def _inputs(q, k, v, beta, alpha, erase, write, h0) -> GdrInputs:
 
 def gdr_forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *, variant: str,
                 cu_seqlens=None, scale: float = 1.0, chunk: int = 64, output_final_state: bool = True,
-                save: bool = False, workspace=None, residual=None, gate_logits: bool = False):
+                save: bool = False, workspace=None, residual=None, gate_logits: bool = False,
+                qk_norm: bool = False):
     """Forward.  Returns (o, ht or None, saved or None).  Tensors must be contiguous and on
     the GPU; the call is asynchronous on torch's current stream.  `residual`: an optional
     [B,H,T,dv] tensor (I/O dtype) that receives r_t = v_t - v_bar_t (gdr_forward_residual)."""
     import torch
     lib = load_library()
     p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk,
-                           gate_logits=gate_logits)
+                           gate_logits=gate_logits, qk_norm=qk_norm)
     N = p.n_seqs if p.n_seqs > 0 else p.B
     o = torch.empty(q.shape[:3] + (p.dv,), dtype=q.dtype, device=q.device)
     ht = torch.empty((N, p.H, p.dv, p.dk), dtype=torch.float32, device=q.device) if output_final_state else None
@@ -166,14 +168,15 @@ def gdr_forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None,
 
 def gdr_backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do=None, dht=None, *,
                  variant: str, cu_seqlens=None, scale: float = 1.0, chunk: int = 64, saved=None,
-                 want_dh0: bool = True, workspace=None, dr=None, gate_logits: bool = False) -> dict:
+                 want_dh0: bool = True, workspace=None, dr=None, gate_logits: bool = False,
+                 qk_norm: bool = False) -> dict:
     """Backward of sum(o * do) + sum(ht * dht) [+ sum(r * dr) with the residual's gradient dr,
     gdr_backward_residual].  Returns a dict of gradients (None where the input is absent).
     `saved` is the third result of gdr_forward(save=True), or None."""
     import torch
     lib = load_library()
     p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk,
-                           gate_logits=gate_logits)
+                           gate_logits=gate_logits, qk_norm=qk_norm)
     N = p.n_seqs if p.n_seqs > 0 else p.B
     e = lambda x: None if x is None else torch.empty_like(x)
     out = {"dq": e(q), "dk": e(k), "dv": e(v), "dbeta": e(beta), "dalpha": e(alpha),

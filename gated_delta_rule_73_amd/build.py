@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
-SOURCES = ["gdr.cpp", "fwd.hip", "bwd.hip", "gdn2.hip", "kda.hip", "seg.hip", "decode.hip"]
+SOURCES = ["gdr.cpp", "fwd.hip", "bwd.hip", "gdn2.hip", "kda.hip", "seg.hip", "decode.hip", "norm.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

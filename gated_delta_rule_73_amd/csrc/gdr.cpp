@@ -42,6 +42,7 @@ struct Sizes {
   int bv = 16, lseg = 0, max_seg = 1;  // scan value tile; forward segmented scans (see plan_scans)
   int lseg_b = 0, max_seg_b = 1;       // backward segmented scans
   size_t X, M, G, Hs, R, M2, U2, Li, A1, A2, Kb, Qh, Gn, Ub, dHs, dR, g2, seg;
+  size_t qn = 0;  // with qk_norm: the normalised q and k (after the cache in the workspace)
   size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Li + A1 + A2 + Kb + Qh + Gn; }
   size_t fwd_ws() const { return Ub + seg; }                   // workspace before the cache
   size_t bwd_ws() const { return Ub + dHs + dR + g2 + seg; }
@@ -99,6 +100,7 @@ gdr_status check_shape(const gdr_problem* p, long long* total_chunks_out, int* m
   if (p->n_seqs < 0) return fail(GDR_ERR_INVALID_ARG, "n_seqs must be >= 0");
   if (p->H > 65535) return fail(GDR_ERR_UNSUPPORTED, "H > 65535 is not supported");
   if (p->gates != 0 && p->gates != 1) return fail(GDR_ERR_INVALID_ARG, "gates must be 0 (values) or 1 (logits)");
+  if (p->qk_norm != 0 && p->qk_norm != 1) return fail(GDR_ERR_INVALID_ARG, "qk_norm must be 0 or 1");
   long long total_chunks = 0;
   int max_chunks = 0;
   if (p->n_seqs > 0) {
@@ -173,6 +175,7 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   plan_scans((long long)s.nstates * p->H, p->dk, max_chunks, p->dtype == GDR_F32, &s);
   const size_t ms = (size_t)std::max(s.lseg ? s.max_seg : 0, s.lseg_b ? s.max_seg_b : 0);
   s.seg = ms ? align_up((size_t)s.nstates * p->H * ms * 3 * D * D * 4, A) : 0;
+  s.qn = p->qk_norm ? 2 * align_up((size_t)p->B * p->H * p->T * D * s.esz, A) : 0;
   *sz = s;
   return GDR_OK;
 }
@@ -272,6 +275,22 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
 gdr_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return GDR_OK;
   return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// With qk_norm, writes q / ||q|| and k / ||k|| (per token) into the workspace region at `dst`
+// and points the inputs at them; otherwise leaves the inputs as they are.
+gdr_status normalize_qk(const gdr_problem* p, const Sizes& s, char* dst, gdr_inputs* ins, hipStream_t st) {
+  if (!p->qk_norm || p->T == 0) return GDR_OK;
+  const long rows = (long)p->B * p->H * p->T;
+  char* qn = dst;
+  char* kn = dst + s.qn / 2;
+  gdr_status r = hip_status(gdr::run_l2norm(p->dtype, p->dk, ins->q, qn, rows, false, st), "q normalisation");
+  if (r != GDR_OK) return r;
+  if ((r = hip_status(gdr::run_l2norm(p->dtype, p->dk, ins->k, kn, rows, false, st), "k normalisation")) != GDR_OK)
+    return r;
+  ins->q = qn;
+  ins->k = kn;
+  return GDR_OK;
 }
 
 // Arms/disarms the per-launch trace around one public call.
@@ -422,7 +441,7 @@ gdr_status gdr_workspace_size(const gdr_problem* p, int backward, size_t* bytes)
   gdr_status st = check_problem(p, &s);
   if (st != GDR_OK) return st;
   if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = s.cache() + (backward ? s.bwd_ws() : s.fwd_ws());
+  *bytes = s.cache() + (backward ? s.bwd_ws() : s.fwd_ws()) + s.qn;
   return GDR_OK;
 }
 
@@ -447,12 +466,15 @@ gdr_status gdr_forward_residual(const gdr_problem* p, const gdr_inputs* in, void
   if (r && p->variant == GDR_GDN2)
     return fail(GDR_ERR_UNSUPPORTED, "the residual output is defined for the delta family and Kimi Delta Attention");
   if (r && p->gates) return fail(GDR_ERR_UNSUPPORTED, "the residual output takes gate values, not logits");
-  if ((st = check_ws(ws, ws_bytes, s.cache() + s.fwd_ws())) != GDR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, s.cache() + s.fwd_ws() + s.qn)) != GDR_OK) return st;
   char* cache = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + s.fwd_ws();
   gdr::Plan pl = make_plan(p, s, cache, static_cast<char*>(ws), false);
   g_last_error.clear();
   TraceCall tc;
-  return hip_status(gdr::run_forward(pl, *in, o, r, ht, true, static_cast<hipStream_t>(stream)), "gdr_forward launch");
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  gdr_inputs ins = *in;
+  if ((st = normalize_qk(p, s, static_cast<char*>(ws) + s.fwd_ws() + s.cache(), &ins, hs)) != GDR_OK) return st;
+  return hip_status(gdr::run_forward(pl, ins, o, r, ht, true, hs), "gdr_forward launch");
 }
 
 gdr_status gdr_forward(const gdr_problem* p, const gdr_inputs* in, void* o, float* ht, void* saved, void* ws,
@@ -486,16 +508,18 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
   for (const void* x : ptrs)
     if (x && !aligned(x, 16)) return fail(GDR_ERR_INVALID_ARG, "gradient pointers must be 16-byte aligned");
   if (saved && !aligned(saved, 256)) return fail(GDR_ERR_INVALID_ARG, "saved must be 256-byte aligned");
-  if ((st = check_ws(ws, ws_bytes, s.cache() + s.bwd_ws())) != GDR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, s.cache() + s.bwd_ws() + s.qn)) != GDR_OK) return st;
   char* base = static_cast<char*>(ws);
   char* cache = saved ? const_cast<char*>(static_cast<const char*>(saved)) : base + s.bwd_ws();
   gdr::Plan pl = make_plan(p, s, cache, base, true);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   g_last_error.clear();
   TraceCall tc;
+  gdr_inputs ins = *in;  // q and k replaced by their normalised copies with qk_norm
+  if ((st = normalize_qk(p, s, base + s.bwd_ws() + s.cache(), &ins, hs)) != GDR_OK) return st;
   if (pipeline_wanted(p, s)) {
-    return hip_status(run_ranges(pl, p, s, hs, [&](const gdr::Plan& q, const SeqRange& x, hipStream_t sq) {
-      gdr_inputs sub = *in;
+    st = hip_status(run_ranges(pl, p, s, hs, [&](const gdr::Plan& q, const SeqRange& x, hipStream_t sq) {
+      gdr_inputs sub = ins;
       sub.h0 = state_at(in->h0, p, x.s0);
       if (!saved) {
         const hipError_t e = gdr::run_forward(q, sub, nullptr, nullptr, nullptr, false, sq);
@@ -505,12 +529,19 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
       gs.dh0 = state_at(g->dh0, p, x.s0);
       return gdr::run_backward(q, sub, dO, dr, state_at(dht, p, x.s0), gs, sq);
     }), "gdr_backward launch");
+  } else {
+    if (!saved) {
+      st = hip_status(gdr::run_forward(pl, ins, nullptr, nullptr, nullptr, false, hs), "gdr_backward recompute launch");
+      if (st != GDR_OK) return st;
+    }
+    st = hip_status(gdr::run_backward(pl, ins, dO, dr, dht, *g, hs), "gdr_backward launch");
   }
-  if (!saved) {
-    st = hip_status(gdr::run_forward(pl, *in, nullptr, nullptr, nullptr, false, hs), "gdr_backward recompute launch");
-    if (st != GDR_OK) return st;
-  }
-  return hip_status(gdr::run_backward(pl, *in, dO, dr, dht, *g, hs), "gdr_backward launch");
+  if (st != GDR_OK || !p->qk_norm) return st;
+  // gradients w.r.t. the raw q and k, through the normalisation
+  const long rows = (long)p->B * p->H * p->T;
+  st = hip_status(gdr::run_l2norm(p->dtype, p->dk, in->q, g->dq, rows, true, hs), "gdr_backward q normalisation");
+  if (st != GDR_OK) return st;
+  return hip_status(gdr::run_l2norm(p->dtype, p->dk, in->k, g->dk, rows, true, hs), "gdr_backward k normalisation");
 }
 
 gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* dO, const float* dht,
@@ -519,6 +550,7 @@ gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* 
 }
 
 gdr_status gdr_decode(const gdr_problem* p, const gdr_inputs* in, float* state, void* o, void* stream) {
+  if (p && p->qk_norm) return fail(GDR_ERR_UNSUPPORTED, "gdr_decode takes normalised q and k (qk_norm must be 0)");
   long long total_chunks = 0;
   int max_chunks = 0;
   gdr_status st = check_shape(p, &total_chunks, &max_chunks);

@@ -242,3 +242,20 @@ def test_gate_logit_checks(lib):
     p = _problem(gates=1)
     st = lib.gdr_forward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE, None, None, FAKE, 1 << 40, None)
     assert st == bd.GDR_ERR_UNSUPPORTED
+
+
+def test_qk_norm_checks_and_workspace(lib):
+    p = _problem(B=2, H=4, T=300)
+    st, plain = _ws(lib, p, True)
+    assert st == bd.GDR_OK
+    p.qk_norm = 1
+    st, normed = _ws(lib, p, True)
+    assert st == bd.GDR_OK
+    tok = 2 * 4 * 300 * 128 * 2  # one normalised copy of q (bf16)
+    assert normed == plain + 2 * ((tok + 255) // 256 * 256)
+    p.qk_norm = 2
+    st, _ = _ws(lib, p, True)
+    assert st == bd.GDR_ERR_INVALID_ARG
+    p = _problem(T=1)
+    p.qk_norm = 1
+    assert _dec(lib, p, _inputs()) == bd.GDR_ERR_UNSUPPORTED
