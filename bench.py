@@ -137,7 +137,7 @@ class Runner:
     standard-normal gradient dr of it (gdr_backward_residual); gate_logits: beta and alpha are
     logits, activated inside the kernels."""
 
-    def __init__(self, w, inp, residual: bool = False, gate_logits: bool = False):
+    def __init__(self, w, inp, residual: bool = False, gate_logits: bool = False, qk_norm: bool = False):
         import torch
 
         from gated_delta_rule_73_amd import binding as bd
@@ -149,7 +149,7 @@ class Runner:
         self.g = g
         self.do = to_gpu(inp["do"], w.dtype)
         self.p, self.keep = bd.make_problem(g["q"], g["v"], variant=w.variant, cu_seqlens=inp.get("cu_seqlens"),
-                                            gate_logits=gate_logits)
+                                            gate_logits=gate_logits, qk_norm=qk_norm)
         N = self.p.n_seqs if self.p.n_seqs > 0 else self.p.B
         dev = g["q"].device
         self.o = torch.empty_like(g["v"])
@@ -341,6 +341,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--residual", action="store_true", help="the forward also writes the residual r = v - v_bar and the backward takes its gradient")
     ap.add_argument("--gate-logits", action="store_true", help="beta and alpha given as logits")
+    ap.add_argument("--qk-norm", action="store_true", help="q and k scaled to unit length inside the library")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -357,7 +358,7 @@ def main():
     w = synth.WORKLOADS.get(args.workload) or {s.name: s for s in synth.SWEEP}[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(w, gate_logits=args.gate_logits)
-    runner = Runner(w, inp, residual=args.residual, gate_logits=args.gate_logits)
+    runner = Runner(w, inp, residual=args.residual, gate_logits=args.gate_logits, qk_norm=args.qk_norm)
     del inp
     # A plain device copy of known size: its HBM counters calibrate the kernels' counters.
     src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda")
@@ -382,7 +383,7 @@ def main():
     kbytes = kernel_bytes_per_unit(w.variant, dom, w.dk, esz, w.has_beta, args.residual) * per_launch_units
     achieved = kbytes / (avg_ms / 1e3) / 1e9
     # counters are recorded for the plain workload only (other kernel instances run with these switches)
-    traffic = None if (args.residual or args.gate_logits) else measured_traffic(dom, w.name)
+    traffic = None if (args.residual or args.gate_logits or args.qk_norm) else measured_traffic(dom, w.name)
     path_bytes = path_bytes_per_head_token(w.variant, w.dk, esz, w.has_beta, args.residual) * tokens * w.H
     path_gbs = path_bytes / (ms / 1e3) / 1e9
     out = {
@@ -393,7 +394,7 @@ def main():
         "config": {"workload": w.name, "variant": w.variant, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk,
                    "d_v": w.dv, "chunk": w.chunk, "cu_seqlens": list(w.cu_seqlens) if w.cu_seqlens else None,
                    "initial_state": w.h0_std > 0, "residual_output": args.residual,
-                   "gate_logits": args.gate_logits},
+                   "gate_logits": args.gate_logits, "qk_norm": args.qk_norm},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_ms": round(avg_ms, 4), "launches": launches,

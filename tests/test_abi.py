@@ -259,3 +259,35 @@ def test_qk_norm_checks_and_workspace(lib):
     p = _problem(T=1)
     p.qk_norm = 1
     assert _dec(lib, p, _inputs()) == bd.GDR_ERR_UNSUPPORTED
+
+
+def _header_fields(struct_name):
+    """(name, kind) of each field of a typedef'd struct in include/gdr.h, in order; kind is
+    'i32', 'f32' or 'ptr'."""
+    import os
+    import re
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "gdr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    body = re.search(r"typedef struct\s*\{([^{}]*)\}\s*" + struct_name + r"\s*;", text).group(1)
+    out = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        m = re.match(r"((?:const\s+)?\w+)\s*(.*)", decl)
+        base, rest = m.group(1), m.group(2)
+        for item in rest.split(","):
+            item = item.strip()
+            ptr = item.startswith("*") or base.endswith("*")
+            name = item.lstrip("*").strip()
+            kind = "ptr" if ptr else {"int32_t": "i32", "float": "f32"}[base.split()[-1]]
+            out.append((name, kind))
+    return out
+
+
+@pytest.mark.parametrize("struct_name,cls", [("gdr_problem", bd.GdrProblem), ("gdr_inputs", bd.GdrInputs),
+                                             ("gdr_grads", bd.GdrGrads)])
+def test_binding_structs_match_header(struct_name, cls):
+    kinds = {ctypes.c_int32: "i32", ctypes.c_float: "f32"}
+    got = [(name, kinds.get(t, "ptr")) for name, t in cls._fields_]
+    assert got == _header_fields(struct_name)
