@@ -402,8 +402,9 @@ float* state_at(const float* st, const gdr_problem* p, int s0) {
   return st ? const_cast<float*>(st) + (size_t)s0 * p->H * p->dk * p->dv : nullptr;
 }
 
-// Runs body(plan, h0, state_offset_fn, stream) for every range, the first on the caller's
-// stream and the others on side streams forked from it and joined back into it.
+// Runs body(range plan, range, stream) for every range, the first (longest) on the caller's
+// stream and the others on side streams forked from it and joined back into it.  Without side
+// streams, body runs once on the whole problem on the caller's stream.
 template <typename Body>
 hipError_t run_ranges(const gdr::Plan& pl, const gdr_problem* p, const Sizes& s, hipStream_t caller, Body body) {
   std::lock_guard<std::mutex> lock(g_pipe_mu);
