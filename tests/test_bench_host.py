@@ -1,8 +1,10 @@
 """Host-side checks of bench.py (no GPU): it refuses more than one GPU, and its byte models
-give the operator's minima quoted for the workloads."""
+give the operator's minima quoted for the workloads and agree with the recorded counters."""
 import os
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -33,3 +35,23 @@ def test_traced_steps_counts_the_sampled_steps():
         want = sum(1 for i in range(steps) if (steps - 1 - i) % bench.TRACE_EVERY == 0)
         assert bench.traced_steps(steps) == want
     assert bench.traced_steps(20) == 5
+
+
+def test_byte_models_agree_with_recorded_counters():
+    """The algorithmic bytes the roofline uses agree (within 2%) with the calibrated HBM counters
+    committed under profiles/, whenever those were taken on the current kernel sources."""
+    import bench
+    import synth
+    w = synth.WORKLOADS["gated_varlen_T32768"]
+    cu = w.cu_seqlens
+    units = sum((b - a + 63) // 64 for a, b in zip(cu[:-1], cu[1:])) * w.H
+    measured = bench.measured_traffic("bwd_chunk", w.name)
+    if measured is None:
+        pytest.skip("counters were taken on other kernel sources")
+    model = bench.kernel_bytes_per_unit(w.variant, "bwd_chunk", w.dk, 2, w.has_beta) * units
+    assert abs(model - measured) / measured < 0.02
+    d = synth.DECODE_WORKLOADS["gated_decode_B512H16"]
+    measured = bench.measured_traffic("decode", d.name)
+    if measured is not None:
+        model = bench.decode_bytes(d, 2)
+        assert abs(model - measured) / measured < 0.02
