@@ -140,21 +140,87 @@ def _inputs(q, k, v, beta, alpha, erase, write, h0) -> GdrInputs:
                      erase=_ptr(erase), write=_ptr(write), h0=_ptr(h0))
 
 
+def _expect(name, t, shape, dtype, device):
+    """Raise ValueError unless t is a contiguous tensor of this shape and dtype on `device`
+    (None passes: presence is checked by the library)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device} (the device of q)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _token_shapes(p: GdrProblem, variant: str) -> dict:
+    """Shapes of every tensor the ABI reads or writes, by input name (gradients share them)."""
+    B, H, T, dk, dv = p.B, p.H, p.T, p.dk, p.dv
+    N = p.n_seqs if p.n_seqs > 0 else B
+    return {"q": (B, H, T, dk), "k": (B, H, T, dk), "v": (B, H, T, dv), "beta": (B, H, T),
+            "alpha": (B, H, T, dk) if variant == "kda" else (B, H, T), "erase": (B, H, T, dk),
+            "write": (B, H, T, dv), "h0": (N, H, dv, dk), "o": (B, H, T, dv), "state": (N, H, dv, dk)}
+
+
+def _validate(p: GdrProblem, variant: str, tensors: dict, require_gpu: bool = True):
+    """Checks every tensor handed to the library (shape, dtype, contiguity, device) before any
+    call: token tensors in q's dtype, states (h0, ht, dht, dh0) in float32."""
+    import torch
+    q = tensors["q"]
+    if q is None or q.dim() != 4:
+        raise ValueError("q must be a [B, H, T, d_k] tensor")
+    if require_gpu and q.device.type != "cuda":
+        raise ValueError(f"tensors must be on the GPU (q is on {q.device})")
+    shapes = _token_shapes(p, variant)
+    state_like = {"h0", "ht", "dht", "dh0", "state"}
+    base = {"dq": "q", "dk": "k", "dv": "v", "dbeta": "beta", "dalpha": "alpha", "derase": "erase",
+            "dwrite": "write", "do": "o", "r": "o", "dr": "o", "ht": "h0", "dht": "h0", "dh0": "h0"}
+    for name, t in tensors.items():
+        if name == "saved" or t is None:
+            continue
+        key = base.get(name, name)
+        dtype = torch.float32 if name in state_like else q.dtype
+        _expect(name, t, shapes[key], dtype, q.device)
+
+
+def _check_saved(saved, p: GdrProblem, device):
+    import torch
+    if saved is None:
+        return
+    need = gdr_saved_size(p)
+    if saved.dtype != torch.uint8 or saved.numel() != need or not saved.is_contiguous() or saved.device != device:
+        raise ValueError(f"saved must be the contiguous uint8 buffer of {need} bytes that gdr_forward(save=True) "
+                         f"returned for this problem (got {saved.dtype}, {saved.numel()} bytes, {saved.device})")
+
+
 def gdr_forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *, variant: str,
                 cu_seqlens=None, scale: float = 1.0, chunk: int = 64, output_final_state: bool = True,
                 save: bool = False, workspace=None, residual=None, gate_logits: bool = False,
-                qk_norm: bool = False):
+                qk_norm: bool = False, out: Optional[dict] = None):
     """Forward.  Returns (o, ht or None, saved or None).  Tensors must be contiguous and on
     the GPU; the call is asynchronous on torch's current stream.  `residual`: an optional
-    [B,H,T,dv] tensor (I/O dtype) that receives r_t = v_t - v_bar_t (gdr_forward_residual)."""
+    [B,H,T,dv] tensor (I/O dtype) that receives r_t = v_t - v_bar_t (gdr_forward_residual).
+    `out`: optional preallocated results by name ("o", "ht", "saved"), written in place."""
     import torch
     lib = load_library()
     p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk,
                            gate_logits=gate_logits, qk_norm=qk_norm)
+    out = dict(out or {})
     N = p.n_seqs if p.n_seqs > 0 else p.B
-    o = torch.empty(q.shape[:3] + (p.dv,), dtype=q.dtype, device=q.device)
-    ht = torch.empty((N, p.H, p.dv, p.dk), dtype=torch.float32, device=q.device) if output_final_state else None
-    saved = torch.empty(gdr_saved_size(p), dtype=torch.uint8, device=q.device) if save else None
+    o = out.get("o")
+    if o is None:
+        o = torch.empty(q.shape[:3] + (p.dv,), dtype=q.dtype, device=q.device)
+    ht = out.get("ht")
+    if ht is None and output_final_state:
+        ht = torch.empty((N, p.H, p.dv, p.dk), dtype=torch.float32, device=q.device)
+    saved = out.get("saved")
+    if saved is None and save:
+        saved = torch.empty(gdr_saved_size(p), dtype=torch.uint8, device=q.device)
+    _validate(p, variant, dict(q=q, k=k, v=v, beta=beta, alpha=alpha, erase=erase, write=write, h0=h0, o=o,
+                               ht=ht, r=residual))
+    _check_saved(saved, p, q.device)
     need = gdr_workspace_size(p, False)
     ws = workspace if workspace is not None and workspace.numel() >= need else \
         torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -169,20 +235,27 @@ def gdr_forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None,
 def gdr_backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do=None, dht=None, *,
                  variant: str, cu_seqlens=None, scale: float = 1.0, chunk: int = 64, saved=None,
                  want_dh0: bool = True, workspace=None, dr=None, gate_logits: bool = False,
-                 qk_norm: bool = False) -> dict:
+                 qk_norm: bool = False, out: Optional[dict] = None) -> dict:
     """Backward of sum(o * do) + sum(ht * dht) [+ sum(r * dr) with the residual's gradient dr,
     gdr_backward_residual].  Returns a dict of gradients (None where the input is absent).
-    `saved` is the third result of gdr_forward(save=True), or None."""
+    `saved` is the third result of gdr_forward(save=True), or None.  `out`: optional
+    preallocated gradients by name (dq, dk, dv, dbeta, dalpha, derase, dwrite, dh0)."""
     import torch
     lib = load_library()
     p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk,
                            gate_logits=gate_logits, qk_norm=qk_norm)
     N = p.n_seqs if p.n_seqs > 0 else p.B
-    e = lambda x: None if x is None else torch.empty_like(x)
-    out = {"dq": e(q), "dk": e(k), "dv": e(v), "dbeta": e(beta), "dalpha": e(alpha),
-           "derase": e(erase), "dwrite": e(write),
-           "dh0": torch.empty((N, p.H, p.dv, p.dk), dtype=torch.float32, device=q.device) if want_dh0 else None}
-    g = GdrGrads(**{name: _ptr(t) for name, t in out.items()})
+    given = dict(out or {})
+    e = lambda name, x: None if x is None else (given[name] if given.get(name) is not None else torch.empty_like(x))
+    res = {"dq": e("dq", q), "dk": e("dk", k), "dv": e("dv", v), "dbeta": e("dbeta", beta),
+           "dalpha": e("dalpha", alpha), "derase": e("derase", erase), "dwrite": e("dwrite", write)}
+    res["dh0"] = given.get("dh0")
+    if res["dh0"] is None and want_dh0:
+        res["dh0"] = torch.empty((N, p.H, p.dv, p.dk), dtype=torch.float32, device=q.device)
+    _validate(p, variant, dict(q=q, k=k, v=v, beta=beta, alpha=alpha, erase=erase, write=write, h0=h0, do=do,
+                               dht=dht, dr=dr, **res))
+    _check_saved(saved, p, q.device)
+    g = GdrGrads(**{name: _ptr(t) for name, t in res.items()})
     need = gdr_workspace_size(p, True)
     ws = workspace if workspace is not None and workspace.numel() >= need else \
         torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -191,7 +264,7 @@ def gdr_backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None
                                    ctypes.byref(g), _ptr(ws), ws.numel(), _stream(q))
     _check(lib, st)
     del keep
-    return out
+    return res
 
 
 def gdr_decode(q, k, v, beta=None, alpha=None, erase=None, write=None, *, state, variant: str,
@@ -203,6 +276,7 @@ def gdr_decode(q, k, v, beta=None, alpha=None, erase=None, write=None, *, state,
     lib = load_library()
     p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, gate_logits=gate_logits)
     o = out if out is not None else torch.empty(q.shape[:3] + (p.dv,), dtype=q.dtype, device=q.device)
+    _validate(p, variant, dict(q=q, k=k, v=v, beta=beta, alpha=alpha, erase=erase, write=write, o=o, state=state))
     ins = _inputs(q, k, v, beta, alpha, erase, write, None)
     st = lib.gdr_decode(ctypes.byref(p), ctypes.byref(ins), _ptr(state), _ptr(o), _stream(q))
     _check(lib, st)

@@ -422,6 +422,28 @@ struct SeqPos {
   int b, bos, len, gc0, nchunks;
 };
 
+// Inclusive prefix sum / total of an int over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return x;
+}
+
+// Packed sequences are found with the whole wave: each lane reads one sequence's offsets, a
+// prefix sum over the lanes gives the sequences' first chunks, and a ballot picks the one that
+// holds the chunk -- 64 sequences per round of coalesced loads, so hundreds of packed
+// documents cost a few rounds instead of a serial walk over cu_seqlens.  Every lane of the
+// wave must call these together (they are called at the top of each kernel, or after an exit
+// taken by the whole block).
 __device__ __forceinline__ ChunkPos chunk_pos(const Geo& g, int gc) {
   ChunkPos p;
   if (!g.varlen) {
@@ -432,18 +454,29 @@ __device__ __forceinline__ ChunkPos chunk_pos(const Geo& g, int gc) {
     p.n = min(CH, g.T - p.t0);
     return p;
   }
-  int off = 0;
   p.b = 0; p.seq = 0; p.t0 = 0; p.n = 0;
-  for (int s = 0; s < g.nseq; ++s) {
-    const int a = g.cu[s], e = g.cu[s + 1];
-    const int nc = (e - a + CH - 1) / CH;
-    if (gc < off + nc) {
-      p.seq = s;
-      p.t0 = a + (gc - off) * CH;
-      p.n = min(CH, e - p.t0);
+  const int l = threadIdx.x & 63;
+  int off = 0;  // chunks of the sequences before this round
+  for (int base = 0; base < g.nseq; base += 64) {
+    const int s = base + l;
+    int a = 0, e = 0, nc = 0;
+    if (s < g.nseq) {
+      a = g.cu[s];
+      e = g.cu[s + 1];
+      nc = (e - a + CH - 1) / CH;
+    }
+    const int incl = wave_incl_scan_i(nc);
+    const int first = off + incl - nc;  // this lane's sequence starts at global chunk `first`
+    const unsigned long long hit = __ballot(nc > 0 && gc >= first && gc < first + nc);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int a_s = __shfl(a, src, 64), e_s = __shfl(e, src, 64), f_s = __shfl(first, src, 64);
+      p.seq = base + src;
+      p.t0 = a_s + (gc - f_s) * CH;
+      p.n = min(CH, e_s - p.t0);
       return p;
     }
-    off += nc;
+    off += __shfl(incl, 63, 64);
   }
   return p;
 }
@@ -455,8 +488,13 @@ __device__ __forceinline__ SeqPos seq_pos(const Geo& g, int s) {
     p.b = s; p.bos = 0; p.len = g.T; p.gc0 = s * nt; p.nchunks = nt;
     return p;
   }
-  int off = 0;
-  for (int i = 0; i < s; ++i) off += (g.cu[i + 1] - g.cu[i] + CH - 1) / CH;
+  const int l = threadIdx.x & 63;
+  int off = 0;  // chunks of the sequences before s, 64 sequences per round
+  for (int base = 0; base < s; base += 64) {
+    const int i = base + l;
+    const int nc = i < s ? (g.cu[i + 1] - g.cu[i] + CH - 1) / CH : 0;
+    off += wave_sum_i(nc);
+  }
   p.b = 0;
   p.bos = g.cu[s];
   p.len = g.cu[s + 1] - g.cu[s];

@@ -413,17 +413,26 @@ hipError_t run_ranges(const gdr::Plan& pl, const gdr_problem* p, const Sizes& s,
   const std::vector<SeqRange> rs = seq_ranges(p);
   hipError_t e = hipEventRecord(pp->fork, caller);
   if (e != hipSuccess) return e;
-  for (size_t i = 1; i < rs.size(); ++i)
-    if ((e = hipStreamWaitEvent(pp->side[i - 1], pp->fork, 0)) != hipSuccess) return e;
-  for (size_t i = 0; i < rs.size(); ++i) {
+  // Side streams that wait on the fork are joined back into the caller's stream whatever
+  // happens after it, so that no work already enqueued on them outlives the call unordered
+  // (the caller may free the workspace and gradients as soon as an error is returned).
+  size_t forked = 1;
+  for (; forked < rs.size(); ++forked)
+    if ((e = hipStreamWaitEvent(pp->side[forked - 1], pp->fork, 0)) != hipSuccess) break;
+  for (size_t i = 0; i < forked && e == hipSuccess; ++i) {
     const hipStream_t st = i == 0 ? caller : pp->side[i - 1];
-    if ((e = body(sub_plan(pl, p, s, rs[i]), rs[i], st)) != hipSuccess) return e;
+    e = body(sub_plan(pl, p, s, rs[i]), rs[i], st);
   }
-  for (size_t i = 1; i < rs.size(); ++i) {
-    if ((e = hipEventRecord(pp->join[i - 1], pp->side[i - 1])) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(caller, pp->join[i - 1], 0)) != hipSuccess) return e;
+  for (size_t i = 1; i < forked; ++i) {
+    hipError_t j = hipEventRecord(pp->join[i - 1], pp->side[i - 1]);
+    if (j == hipSuccess) j = hipStreamWaitEvent(caller, pp->join[i - 1], 0);
+    if (j != hipSuccess) {
+      // the ordering could not be expressed through the caller's stream: wait on the host
+      (void)hipStreamSynchronize(pp->side[i - 1]);
+      if (e == hipSuccess) e = j;
+    }
   }
-  return hipSuccess;
+  return e;
 }
 
 }  // namespace

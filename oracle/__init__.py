@@ -7,6 +7,8 @@ the product path.
 
 Contents:
   recurrence.forward / recurrence.backward -- the token-by-token float64
-  recurrence of the pages' update rule, and its manual reverse mode.
+  recurrence of the pages' update rule, and its manual reverse mode;
+  recurrence.gates_from_logits / logit_gradients -- the gate activations of the workloads
+  (sigmoid, exp(-softplus)) and their chain rule, for gates given as logits.
 """
-from .recurrence import forward, backward  # noqa: F401
+from .recurrence import backward, forward, gates_from_logits, logit_gradients  # noqa: F401

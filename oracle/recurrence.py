@@ -147,11 +147,50 @@ def l2_normalize_backward(x, dy):
     return np.divide(g, n, out=np.zeros_like(g), where=n > 0)
 
 
+# -- gates given as logits -----------------------------------------------------------------
+# The workloads draw every gate from a standard-normal logit x: the write strength beta and
+# GDN-2's erase and write gates as the logistic sigmoid of x, the decay as alpha = exp(-softplus(x))
+# (so log alpha = -softplus(x) < 0 and alpha lies in (0, 1)).  A caller may pass the logits and
+# receive gradients with respect to them.
+def sigmoid(x):
+    """1 / (1 + e^-x), evaluated without overflow for either sign of x."""
+    x = _f64(x)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def neg_softplus(x):
+    """-log(1 + e^x), the log of the decay alpha = exp(-softplus(x))."""
+    return -np.logaddexp(0.0, _f64(x))
+
+
+def gates_from_logits(beta=None, alpha=None, erase=None, write=None):
+    """Gate values from logits: beta, erase, write = sigmoid(x); alpha = exp(-softplus(x)).
+    None stays None."""
+    f = lambda x, m: None if x is None else m(x)
+    return (f(beta, sigmoid), f(alpha, lambda x: np.exp(neg_softplus(x))), f(erase, sigmoid),
+            f(write, sigmoid))
+
+
+def logit_gradients(g, beta=None, alpha=None, erase=None, write=None):
+    """Carries gradients w.r.t. the gate values (dbeta, dalpha, derase, dwrite in g) to the
+    logits they came from, in place: d/dx sigmoid(x) = s (1 - s), and
+    d/dx exp(-softplus(x)) = alpha * (-sigmoid(x))."""
+    for x, name in ((beta, "dbeta"), (erase, "derase"), (write, "dwrite")):
+        if x is not None:
+            s = sigmoid(x)
+            g[name] = g[name] * s * (1.0 - s)
+    if alpha is not None:
+        g["dalpha"] = g["dalpha"] * np.exp(neg_softplus(alpha)) * (-sigmoid(alpha))
+    return g
+
+
 def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
-            variant, cu_seqlens=None, scale=1.0, residual=False, qk_l2norm=False):
+            variant, cu_seqlens=None, scale=1.0, residual=False, qk_l2norm=False, gate_logits=False):
     """Run the recurrence.  Returns (o [B,H,T,dv], ht [N,H,dv,dk]) in float64, and with
     residual=True also r [B,H,T,dv], r_t = v_t - v_bar_t (delta family only).
     qk_l2norm: q and k are first scaled to unit length per token (l2_normalize).
+    gate_logits: beta, alpha, erase and write are logits, mapped by gates_from_logits first.
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] (None -> 1, gdn2 only);
     alpha: None (deltanet), [B,H,T] (gated, gdn2) or [B,H,T,dk] (kda);
@@ -161,6 +200,8 @@ def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
     q, k, v, beta, alpha, erase, write, h0 = map(_f64, (q, k, v, beta, alpha, erase, write, h0))
     if qk_l2norm:
         q, k = l2_normalize(q), l2_normalize(k)
+    if gate_logits:
+        beta, alpha, erase, write = gates_from_logits(beta, alpha, erase, write)
     _check(variant, q, k, v, beta, alpha, erase, write)
     if residual and variant == "gdn2":
         raise ValueError("gdn2 has separate erase and write terms, not one residual")
@@ -183,7 +224,7 @@ def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
 
 def backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do=None,
              dht=None, *, variant, cu_seqlens=None, scale=1.0, checkpoint_every=64, dr=None,
-             qk_l2norm=False):
+             qk_l2norm=False, gate_logits=False):
     """Gradients of sum(o * do) + sum(ht * dht) [+ sum(r * dr), r the residual output of
     forward(residual=True), when dr is given] by manual reverse mode through the recurrence.
 
@@ -193,9 +234,15 @@ def backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do
     Returns a dict with dq, dk, dv, dbeta, dalpha, derase, dwrite, dh0 (None where
     the input is absent).  dalpha is the gradient with respect to alpha itself.
     qk_l2norm: as in forward; dq and dk are then w.r.t. the raw q and k.
+    gate_logits: as in forward; the gate gradients are then w.r.t. the logits (logit_gradients).
     """
     q, k, v, beta, alpha, erase, write, h0, do, dht, dr = map(
         _f64, (q, k, v, beta, alpha, erase, write, h0, do, dht, dr))
+    if gate_logits:
+        vals = gates_from_logits(beta, alpha, erase, write)
+        g = backward(q, k, v, *vals, h0, do, dht, variant=variant, cu_seqlens=cu_seqlens, scale=scale,
+                     checkpoint_every=checkpoint_every, dr=dr, qk_l2norm=qk_l2norm)
+        return logit_gradients(g, beta, alpha, erase, write)
     if qk_l2norm:
         g = backward(l2_normalize(q), l2_normalize(k), v, beta, alpha, erase, write, h0, do, dht,
                      variant=variant, cu_seqlens=cu_seqlens, scale=scale,

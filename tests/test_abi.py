@@ -291,3 +291,28 @@ def test_binding_structs_match_header(struct_name, cls):
     kinds = {ctypes.c_int32: "i32", ctypes.c_float: "f32"}
     got = [(name, kinds.get(t, "ptr")) for name, t in cls._fields_]
     assert got == _header_fields(struct_name)
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks every tensor before the library sees a pointer: shape, dtype (token
+    tensors in q's dtype, states in float32), contiguity and device."""
+    import torch
+    B, H, T, d = 1, 2, 70, 128
+    q = torch.zeros(B, H, T, d, dtype=torch.bfloat16)
+    p, _ = bd.make_problem(q, q, variant="gated")
+    ok = dict(q=q, k=q.clone(), v=q.clone(), beta=torch.zeros(B, H, T, dtype=torch.bfloat16),
+              alpha=torch.zeros(B, H, T, dtype=torch.bfloat16), h0=torch.zeros(B, H, d, d))
+    bd._validate(p, "gated", ok, require_gpu=False)
+    bad = [dict(beta=torch.zeros(B, H, T)),                                    # float32 gate with bf16 q
+           dict(k=torch.zeros(B, H, T - 1, d, dtype=torch.bfloat16)),          # short tensor
+           dict(v=torch.zeros(B, T, H, d, dtype=torch.bfloat16).transpose(1, 2)),  # strided view
+           dict(h0=torch.zeros(B, H, d, d, dtype=torch.bfloat16)),             # state not float32
+           dict(alpha=torch.zeros(B, H, T, d, dtype=torch.bfloat16)),          # per-channel decay for gated
+           dict(dq=torch.zeros(B, H, T, d))]                                   # gradient dtype
+    for kw in bad:
+        with pytest.raises(ValueError):
+            bd._validate(p, "gated", {**ok, **kw}, require_gpu=False)
+    with pytest.raises(ValueError):
+        bd._validate(p, "gated", ok)  # CPU tensors are refused when a GPU is required
+    pk, _ = bd.make_problem(q, q, variant="kda")
+    bd._validate(pk, "kda", {**ok, "alpha": torch.zeros(B, H, T, d, dtype=torch.bfloat16)}, require_gpu=False)

@@ -29,6 +29,27 @@ def test_byte_models():
     assert bench.decode_bytes(w, 2) == 2 * 512 * 16 * 128 * 128 * 4 + 512 * 16 * (4 * 128 * 2 + 2 + 2)
 
 
+def test_operator_bytes_attribution():
+    """Each kernel is charged the operator tensors it reads or writes (no intermediates): the
+    delta family's chunk-parallel backward reads every token tensor of the backward and writes
+    every gradient (1800 B per head-token at d = 128, bf16), the preparation reads the
+    forward's inputs, the forward scan writes o (reading q and k), the reverse scan reads dO."""
+    import bench
+    tok = 256
+    assert bench.kernel_operator_bytes("gated", "bwd_chunk") == 1800
+    assert bench.kernel_operator_bytes("gated", "fwd_prep") == 3 * tok + 4
+    assert bench.kernel_operator_bytes("gated", "fwd_scan") == 3 * tok
+    assert bench.kernel_operator_bytes("gated", "bwd_scan") == 3 * tok
+    assert bench.kernel_operator_bytes("deltanet", "bwd_chunk") == 7 * tok + 4
+    # every operator tensor of the Gated path is charged to some kernel
+    fwd = bench.kernel_operator_bytes("gated", "fwd_prep") + tok  # + o, written by the scan
+    assert fwd + bench.kernel_operator_bytes("gated", "bwd_chunk") == bench.path_bytes_per_head_token("gated")
+    # Kimi Delta Attention's backward stages together write every gradient and read every input
+    k = sum(bench.kernel_operator_bytes("kda", s) for s in ("bwd_kda_wy", "bwd_kda_gram"))
+    assert k == (2 * tok + 2 + tok + tok) + (2 * tok + tok) * 2 + 2
+    assert bench.kernel_state_bytes("fwd_scan", 128, True) == 2 * 128 * 128 * 4
+
+
 def test_traced_steps_counts_the_sampled_steps():
     import bench
     for steps in (1, 3, 4, 5, 20, 21):

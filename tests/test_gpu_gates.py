@@ -1,8 +1,8 @@
 """GPU parity with the gates given as logits (gdr_problem.gates = 1): beta = sigmoid(x) and
 alpha = exp(-softplus(x)) are applied inside the kernels and the gradients come back w.r.t.
-the logits.  The float64 reference applies the same maps to the same (rounded) logits, runs the
-oracle on the gate values, and carries its gate gradients to the logits by the chain rule:
-dx_beta = dbeta beta (1 - beta), dx_alpha = dalpha alpha (-sigmoid(x_alpha))."""
+the logits.  The float64 reference is the oracle run on the same (rounded) logits with
+gate_logits=True: it applies the same maps and carries its gate gradients to the logits by the
+chain rule (both pinned against closed forms and finite differences in the oracle's tests)."""
 import numpy as np
 import pytest
 
@@ -12,38 +12,13 @@ from tests._helpers import compare, run_hip
 pytestmark = pytest.mark.gpu
 
 
-def _sig(x):
-    return 1.0 / (1.0 + np.exp(-x))
-
-
-def _gates(inp):
-    """Gate values in float64 from the logits."""
-    out = dict(inp)
-    for name in ("beta", "erase", "write"):
-        if inp.get(name) is not None:
-            out[name] = _sig(inp[name].astype(np.float64))
-    if inp.get("alpha") is not None:
-        xa = inp["alpha"].astype(np.float64)
-        out["alpha"] = np.exp(-np.logaddexp(0.0, xa))
-    return out
-
-
 def _oracle(inp, variant, backward, cu=None, scale=1.0):
     from oracle import recurrence as R
-    vals = _gates(inp)
-    kw = {n: vals.get(n) for n in ("q", "k", "v", "beta", "alpha", "erase", "write", "h0")}
-    o, ht = R.forward(**kw, variant=variant, cu_seqlens=cu, scale=scale)
+    kw = {n: inp.get(n) for n in ("q", "k", "v", "beta", "alpha", "erase", "write", "h0")}
+    o, ht = R.forward(**kw, variant=variant, cu_seqlens=cu, scale=scale, gate_logits=True)
     ref = {"o": o, "ht": ht}
     if backward:
-        g = R.backward(**kw, do=inp["do"], variant=variant, cu_seqlens=cu, scale=scale)
-        for name, gname in (("beta", "dbeta"), ("erase", "derase"), ("write", "dwrite")):
-            if g.get(gname) is not None:
-                x = vals[name]
-                g[gname] = g[gname] * x * (1.0 - x)
-        if g.get("dalpha") is not None:
-            a = vals["alpha"]
-            g["dalpha"] = g["dalpha"] * a * (-_sig(inp["alpha"].astype(np.float64)))
-        ref.update(g)
+        ref.update(R.backward(**kw, do=inp["do"], variant=variant, cu_seqlens=cu, scale=scale, gate_logits=True))
     return ref
 
 

@@ -27,8 +27,17 @@ def test_deltanet_f32_T256_d64_forward():
     print("\n".join(rep))
 
 
+@pytest.fixture(params=[16, 32], ids=["bv16", "bv32"])
+def scan_bv(request, monkeypatch):
+    """Value-tile height of the scans, forced: 32-row tiles are what the planner picks at the
+    benchmarked sizes (many memories), 16 what it picks for small problems; both are tested
+    with a long memory (weak or no decay) and a visible initial memory."""
+    monkeypatch.setenv("GDR_SCAN_BV", str(request.param))
+    return request.param
+
+
 @pytest.mark.parametrize("alpha_mode", ["config", "weak", "one"])
-def test_gated_bf16_small(alpha_mode):
+def test_gated_bf16_small(alpha_mode, scan_bv):
     w, inp = _small("gated", "bf16", alpha_mode=alpha_mode, h0=True)
     dht = np.random.default_rng(5).standard_normal((2, 2, 128, 128)).astype(np.float32)
     rep = []
@@ -55,7 +64,7 @@ def test_gated_f32_d64_fwd_bwd():
     print("\n".join(rep))
 
 
-def test_gated_varlen_with_initial_state():
+def test_gated_varlen_with_initial_state(scan_bv):
     cu = (0, 100, 164, 165, 300)
     w, inp = _small("gated", "bf16", B=1, H=3, T=300, cu=cu, h0=True, alpha_mode="weak")
     dht = np.random.default_rng(6).standard_normal((4, 3, 128, 128)).astype(np.float32) * 0.1
@@ -82,7 +91,7 @@ def test_run_to_run_bitwise_determinism():
             assert np.array_equal(a[name], b[name]), name
 
 
-def test_initial_state_is_visible():
+def test_initial_state_is_visible(scan_bv):
     """With weak decay the initial memory changes the outputs by far more than the tolerance,
     so the parity of test_gated_bf16_small[weak] also pins the h0 path."""
     w, inp = _small("gated", "bf16", alpha_mode="weak", h0=True)
@@ -105,7 +114,7 @@ def test_empty_sequences_and_empty_input():
 
 @pytest.mark.parametrize("alpha_mode,with_beta", [("config", False), ("weak", False), ("one", True),
                                                    ("config", True)])
-def test_gdn2_bf16_small(alpha_mode, with_beta):
+def test_gdn2_bf16_small(alpha_mode, with_beta, scan_bv):
     """Gated DeltaNet-2: separate erase (key channels) and write (value channels) gates."""
     w = synth.Workload("t", "gdn2", "bf16", 2, 2, 190, 128, 128, seed=21, has_beta=with_beta, h0_std=0.5)
     inp = synth.make_inputs(w, alpha_mode=alpha_mode)
@@ -138,7 +147,7 @@ def test_gdn2_varlen_saved_vs_recomputed():
 
 
 @pytest.mark.parametrize("alpha_mode", ["config", "weak", "strong"])
-def test_kda_bf16_small(alpha_mode):
+def test_kda_bf16_small(alpha_mode, scan_bv):
     """Kimi Delta Attention: decay per key channel.  "strong" decays by more than e^-60 within
     16 tokens, so every diagonal block takes the exact path."""
     w = synth.Workload("t", "kda", "bf16", 2, 2, 190, 128, 128, seed=31, h0_std=0.5)
@@ -245,3 +254,21 @@ def test_gdn2_erase_free_is_decayed_linear_attention(dtype, d):
             want = (Dm * (Q @ K.T)) @ Bv + np.exp(logg)[:, None] * (Q @ inp["h0"][b, h].astype(np.float64).T)
             tol = 1e-4 * np.max(np.abs(want)) if dtype == "f32" else 2e-2 * max(1.0, np.max(np.abs(want)))
             assert np.max(np.abs(got["o"][b, h] - want)) <= tol
+
+
+@pytest.mark.parametrize("variant", ["gated", "kda"])
+def test_many_ragged_packed_sequences(variant):
+    """300 packed sequences of ragged lengths (0 to 160 tokens: empty ones, single tokens,
+    ragged tails, several chunks) in one call: every sequence restarts from its own initial
+    memory, found by the kernels' wave-parallel lookup of the chunk's sequence."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 161, size=300)
+    lens[:6] = [0, 1, 64, 0, 65, 128]
+    cu = tuple(int(x) for x in np.concatenate([[0], np.cumsum(lens)]))
+    w = synth.Workload("t", variant, "bf16", 1, 2, cu[-1], 128, 128, seed=71, cu_seqlens=cu, h0_std=0.5)
+    inp = synth.make_inputs(w, alpha_mode="weak")
+    dht = np.random.default_rng(78).standard_normal((300, 2, 128, 128)).astype(np.float32) * 0.1
+    rep = []
+    compare(run_hip(inp, variant, "bf16", backward=True, dht=dht),
+            run_oracle(inp, variant, backward=True, dht=dht), "bf16", report=rep)
+    print("\n".join(rep))

@@ -435,3 +435,56 @@ def test_qk_l2norm_backward_matches_finite_differences(variant):
             xm[name] = x[name].copy(); xm[name][idx] -= 1e-6
             num[idx] = (loss(xp) - loss(xm)) / 2e-6
         np.testing.assert_allclose(g["d" + name], num, rtol=1e-6, atol=1e-8)
+
+
+# ---------------------------------------------------------------------------------------
+# Gates given as logits: the activation maps and their chain rule
+# ---------------------------------------------------------------------------------------
+def test_logit_gate_maps_closed_forms():
+    """sigmoid against scipy's expit; alpha = exp(-softplus(x)) is 1 / (1 + e^x) = sigmoid(-x);
+    both are 1/2 at x = 0 and stay finite and in (0, 1) at large |x|."""
+    from scipy.special import expit
+    x = np.array([-800.0, -30.0, -2.5, -1e-3, 0.0, 1e-3, 0.7, 2.0, 30.0, 800.0])
+    b, a, e, w = R.gates_from_logits(x, x, x, x)
+    np.testing.assert_allclose(b, expit(x), rtol=1e-15, atol=0)
+    np.testing.assert_array_equal(e, b)
+    np.testing.assert_array_equal(w, b)
+    np.testing.assert_allclose(a, expit(-x), rtol=1e-13, atol=1e-300)
+    assert b[4] == 0.5 and a[4] == 0.5
+    assert np.all((a >= 0) & (a <= 1) & np.isfinite(a))
+    np.testing.assert_allclose(b + R.sigmoid(-x), 1.0, rtol=1e-15)
+    # log alpha = -softplus(x): -log 2 at 0, about -x for large x, about -e^x for very negative x
+    np.testing.assert_allclose(R.neg_softplus(np.array([0.0, 40.0, -40.0])),
+                               [-np.log(2.0), -40.0, -np.exp(-40.0)], rtol=1e-14)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2"])
+def test_logit_gradients_match_finite_differences(variant):
+    """The whole map from logits to outputs, differentiated by central differences in the
+    logits, against the chain rule of backward(gate_logits=True)."""
+    rng = np.random.default_rng(41)
+    x = _rand_inputs(rng, variant, B=1, H=2, T=6, dk=3, dv=4, unit_keys=False)
+    for name in ("beta", "alpha", "erase", "write"):
+        if x.get(name) is not None:
+            x[name] = rng.standard_normal(x[name].shape) * 1.5   # logits
+    x["h0"] = rng.standard_normal((1, 2, 4, 3))
+    G = rng.standard_normal((1, 2, 6, 4))
+
+    def loss(xx):
+        o, ht = R.forward(**xx, variant=variant, scale=0.7, gate_logits=True)
+        return np.sum(o * G) + 0.3 * np.sum(ht)
+
+    g = R.backward(**x, do=G, dht=np.full((1, 2, 4, 3), 0.3), variant=variant, scale=0.7,
+                   gate_logits=True)
+    eps = 1e-6
+    for name in ("beta", "alpha", "erase", "write"):
+        if x.get(name) is None:
+            continue
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp = {kk: (vv.copy() if vv is not None else None) for kk, vv in x.items()}
+            xm = {kk: (vv.copy() if vv is not None else None) for kk, vv in x.items()}
+            xp[name][idx] += eps
+            xm[name][idx] -= eps
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+        np.testing.assert_allclose(g["d" + name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
