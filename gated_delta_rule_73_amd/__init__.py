@@ -6,5 +6,5 @@ Gated DeltaNet-2) for AMD MI355X (gfx950): hand-written HIP kernels behind a C A
 """
 from .binding import (  # noqa: F401
     GdrError, GdrGrads, GdrInputs, GdrProblem, LIB_PATH, VARIANTS, gdr_backward, gdr_decode, gdr_forward,
-    gdr_saved_size, gdr_workspace_size, load_library, make_problem,
+    gdr_forward_noalloc, gdr_saved_size, gdr_workspace_size, load_library, make_problem,
 )

@@ -65,8 +65,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gdr_forward_residual.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.gdr_backward_residual.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, _vp, P(GdrGrads), _vp,
                                           ctypes.c_size_t, _vp]
+    lib.gdr_forward_noalloc.argtypes = [P(GdrProblem), P(GdrInputs), _vp, _vp, _vp, _vp]
     for f in ("gdr_workspace_size", "gdr_saved_size", "gdr_forward", "gdr_backward", "gdr_decode",
-              "gdr_forward_residual", "gdr_backward_residual"):
+              "gdr_forward_residual", "gdr_backward_residual", "gdr_forward_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -227,6 +228,24 @@ def gdr_forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None,
     ins = _inputs(q, k, v, beta, alpha, erase, write, h0)
     st = lib.gdr_forward_residual(ctypes.byref(p), ctypes.byref(ins), _ptr(o), _ptr(residual), _ptr(ht),
                                   _ptr(saved), _ptr(ws), ws.numel(), _stream(q))
+    _check(lib, st)
+    del keep
+    return o, ht, saved
+
+
+def gdr_forward_noalloc(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *, variant: str,
+                        o, ht=None, saved=None, cu_seqlens=None, scale: float = 1.0, chunk: int = 64,
+                        gate_logits: bool = False, qk_norm: bool = False):
+    """Forward through gdr_forward_noalloc: the caller passes the outputs (o, and optionally ht
+    and saved), and the library's own scratch replaces the workspace, so the call allocates
+    nothing (neither here nor in the library).  Asynchronous on torch's current stream."""
+    lib = load_library()
+    p, keep = make_problem(q, v, variant=variant, cu_seqlens=cu_seqlens, scale=scale, chunk=chunk,
+                           gate_logits=gate_logits, qk_norm=qk_norm)
+    _validate(p, variant, dict(q=q, k=k, v=v, beta=beta, alpha=alpha, erase=erase, write=write, h0=h0, o=o, ht=ht))
+    _check_saved(saved, p, q.device)
+    ins = _inputs(q, k, v, beta, alpha, erase, write, h0)
+    st = lib.gdr_forward_noalloc(ctypes.byref(p), ctypes.byref(ins), _ptr(o), _ptr(ht), _ptr(saved), _stream(q))
     _check(lib, st)
     del keep
     return o, ht, saved

@@ -435,6 +435,77 @@ hipError_t run_ranges(const gdr::Plan& pl, const gdr_problem* p, const Sizes& s,
   return e;
 }
 
+// The forward behind gdr_forward_residual and gdr_forward_noalloc.  Workspace layout: the scan
+// workspace (fwd_ws), then the per-chunk cache when it is not in `saved` (always reserved when
+// reserve_cache, the layout gdr_workspace_size describes), then the normalised q and k.
+gdr_status forward_impl(const gdr_problem* p, const gdr_inputs* in, void* o, void* r, float* ht, void* saved,
+                        const Sizes& s, char* ws, bool reserve_cache, void* stream) {
+  const char* cache_end = ws + s.fwd_ws() + ((reserve_cache || !saved) ? s.cache() : 0);
+  char* cache = saved ? static_cast<char*>(saved) : ws + s.fwd_ws();
+  gdr::Plan pl = make_plan(p, s, cache, ws, false);
+  g_last_error.clear();
+  TraceCall tc;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  gdr_inputs ins = *in;
+  gdr_status st = normalize_qk(p, s, const_cast<char*>(cache_end), &ins, hs);
+  if (st != GDR_OK) return st;
+  return hip_status(gdr::run_forward(pl, ins, o, r, ht, true, hs), "gdr_forward launch");
+}
+
+// Checks shared by the forward entry points (everything but the workspace).
+gdr_status check_forward(const gdr_problem* p, const gdr_inputs* in, void* o, void* r, float* ht, void* saved,
+                         Sizes* s) {
+  gdr_status st = check_problem(p, s);
+  if (st != GDR_OK) return st;
+  if ((st = check_inputs(p, in)) != GDR_OK) return st;
+  if (!o && p->T > 0) return fail(GDR_ERR_INVALID_ARG, "o is required");
+  if ((o && !aligned(o, 16)) || (r && !aligned(r, 16)) || (ht && !aligned(ht, 16)) || (saved && !aligned(saved, 256)))
+    return fail(GDR_ERR_INVALID_ARG, "o/r/ht must be 16-byte and saved 256-byte aligned");
+  if (r && p->variant == GDR_GDN2)
+    return fail(GDR_ERR_UNSUPPORTED, "the residual output is defined for the delta family and Kimi Delta Attention");
+  if (r && p->gates) return fail(GDR_ERR_UNSUPPORTED, "the residual output takes gate values, not logits");
+  return GDR_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+// Library-held scratch for gdr_forward_noalloc.  `scratch` is a device array: every GPU the
+// library runs on holds its own copy (at its own address) from the moment the code object is
+// loaded there until the process ends.  In host code its name is only a stand-in for the
+// symbol; the device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is ever passed to kernels or copies.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)GDR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch (looked up on the first call there).
+gdr_status scratch_on_current_device(void* stream, char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDR_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  if (stream) {  // the stream must belong to the current device, whose scratch is used
+    int sdev = -1;
+    if ((e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev)) != hipSuccess)
+      return hip_status(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(GDR_ERR_INVALID_ARG, "the stream belongs to device %d, the current device is %d", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256)) return fail(GDR_ERR_HIP, "scratch has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return GDR_OK;
+}
+
 }  // namespace
 
 namespace gdr {
@@ -467,29 +538,30 @@ gdr_status gdr_saved_size(const gdr_problem* p, size_t* bytes) {
 gdr_status gdr_forward_residual(const gdr_problem* p, const gdr_inputs* in, void* o, void* r, float* ht, void* saved,
                                 void* ws, size_t ws_bytes, void* stream) {
   Sizes s;
-  gdr_status st = check_problem(p, &s);
+  gdr_status st = check_forward(p, in, o, r, ht, saved, &s);
   if (st != GDR_OK) return st;
-  if ((st = check_inputs(p, in)) != GDR_OK) return st;
-  if (!o && p->T > 0) return fail(GDR_ERR_INVALID_ARG, "o is required");
-  if ((o && !aligned(o, 16)) || (r && !aligned(r, 16)) || (ht && !aligned(ht, 16)) || (saved && !aligned(saved, 256)))
-    return fail(GDR_ERR_INVALID_ARG, "o/r/ht must be 16-byte and saved 256-byte aligned");
-  if (r && p->variant == GDR_GDN2)
-    return fail(GDR_ERR_UNSUPPORTED, "the residual output is defined for the delta family and Kimi Delta Attention");
-  if (r && p->gates) return fail(GDR_ERR_UNSUPPORTED, "the residual output takes gate values, not logits");
   if ((st = check_ws(ws, ws_bytes, s.cache() + s.fwd_ws() + s.qn)) != GDR_OK) return st;
-  char* cache = saved ? static_cast<char*>(saved) : static_cast<char*>(ws) + s.fwd_ws();
-  gdr::Plan pl = make_plan(p, s, cache, static_cast<char*>(ws), false);
-  g_last_error.clear();
-  TraceCall tc;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
-  gdr_inputs ins = *in;
-  if ((st = normalize_qk(p, s, static_cast<char*>(ws) + s.fwd_ws() + s.cache(), &ins, hs)) != GDR_OK) return st;
-  return hip_status(gdr::run_forward(pl, ins, o, r, ht, true, hs), "gdr_forward launch");
+  return forward_impl(p, in, o, r, ht, saved, s, static_cast<char*>(ws), true, stream);
 }
 
 gdr_status gdr_forward(const gdr_problem* p, const gdr_inputs* in, void* o, float* ht, void* saved, void* ws,
                        size_t ws_bytes, void* stream) {
   return gdr_forward_residual(p, in, o, nullptr, ht, saved, ws, ws_bytes, stream);
+}
+
+gdr_status gdr_forward_noalloc(const gdr_problem* p, const gdr_inputs* in, void* o, float* ht, void* saved,
+                               void* stream) {
+  Sizes s;
+  gdr_status st = check_forward(p, in, o, nullptr, ht, saved, &s);
+  if (st != GDR_OK) return st;
+  const size_t need = s.fwd_ws() + (saved ? 0 : s.cache()) + s.qn;
+  if (need > kScratchBytes)
+    return fail(GDR_ERR_WORKSPACE, "gdr_forward_noalloc: this problem needs %zu bytes of scratch, more than the "
+                "%zu the library holds; pass a saved buffer or call gdr_forward with a workspace",
+                need, kScratchBytes);
+  char* ws = nullptr;
+  if ((st = scratch_on_current_device(stream, &ws)) != GDR_OK) return st;
+  return forward_impl(p, in, o, nullptr, ht, saved, s, ws, false, stream);
 }
 
 gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, const void* dO, const void* dr,

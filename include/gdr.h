@@ -25,7 +25,8 @@
  *    N = B for a dense batch, N = n_seqs for packed variable-length sequences (then B == 1
  *    and sequence n covers tokens [cu_seqlens[n], cu_seqlens[n+1]) of every head).
  *  - Every pointer is owned by the caller.  The library allocates no device memory and
- *    keeps no state between calls; scratch lives in the caller's workspace.
+ *    keeps no state between calls; scratch lives in the caller's workspace (the exception is
+ *    gdr_forward_noalloc, whose scratch is a device array the library holds).
  *  - Calls are asynchronous on the given stream (a hipStream_t passed as void*; NULL is the
  *    default stream).  cu_seqlens_host is read on the host for checking and planning only.
  *  - Every argument is checked before anything is launched.  On any non-OK return nothing
@@ -124,6 +125,27 @@ gdr_status gdr_saved_size(const gdr_problem *p, size_t *bytes);
  * backward needs are written there for a later gdr_backward.  ws: gdr_workspace_size(p, 0) bytes. */
 gdr_status gdr_forward(const gdr_problem *p, const gdr_inputs *in, void *o, float *ht,
                        void *saved, void *ws, size_t ws_bytes, void *stream);
+
+/* Forward that allocates nothing, for callers that cannot call hipMalloc (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation) and so cannot provide a
+ * workspace.  The workspace comes from a scratch array the library holds in device memory,
+ * GDR_NOALLOC_SCRATCH_BYTES bytes per GPU (every GPU the library is loaded on holds its own copy
+ * until the process ends).  Everything else is as for gdr_forward: o, ht and saved are the
+ * caller's; with saved given the per-chunk results go there and the scratch holds only the
+ * scan's own buffers (about 16 KiB per chunk and head at d = 128, bfloat16), without it the
+ * scratch also holds them (about 104 KiB per chunk and head).
+ *  - Returns GDR_ERR_WORKSPACE, launching nothing, when the problem needs more scratch than the
+ *    library holds (call gdr_forward with a workspace instead).
+ *  - The stream must belong to the current device (NULL: the default stream); INVALID_ARG if not.
+ *  - Every call on one GPU uses that GPU's one scratch array and leaves its contents behind
+ *    (nothing in it needs to start at zero).  Calls that overlap on one GPU race: order them,
+ *    e.g. on one stream.
+ *  - The first call on a device looks up that device's scratch address (no allocation);
+ *    no call allocates device or pinned host memory.
+ * Errors: as gdr_forward, plus WORKSPACE as above. */
+#define GDR_NOALLOC_SCRATCH_BYTES (64u << 20)
+gdr_status gdr_forward_noalloc(const gdr_problem *p, const gdr_inputs *in, void *o, float *ht,
+                               void *saved, void *stream);
 
 /* Backward of sum(o * dO) + sum(ht * dht).  dO: [B,H,T,dv] I/O dtype (required).
  * dht: [N,H,dv,dk] float32 or NULL (zeros).  saved: the buffer a gdr_forward with the same

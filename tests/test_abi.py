@@ -316,3 +316,25 @@ def test_binding_rejects_mismatched_tensors():
         bd._validate(p, "gated", ok)  # CPU tensors are refused when a GPU is required
     pk, _ = bd.make_problem(q, q, variant="kda")
     bd._validate(pk, "kda", {**ok, "alpha": torch.zeros(B, H, T, d, dtype=torch.bfloat16)}, require_gpu=False)
+
+
+def test_noalloc_checks(lib):
+    """gdr_forward_noalloc checks its arguments like gdr_forward and refuses, before touching a
+    device, a problem whose workspace exceeds the library's scratch (the size in the header)."""
+    header = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    limit = eval(re.search(r"#define GDR_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", header).expand(r"\1 << \2"))
+    assert limit == 64 << 20
+
+    def call(p, ins, o=FAKE, ht=None, saved=None):
+        return lib.gdr_forward_noalloc(ctypes.byref(p) if p is not None else None,
+                                       ctypes.byref(ins) if ins is not None else None, o, ht, saved, None)
+    assert call(None, _inputs()) == bd.GDR_ERR_INVALID_ARG
+    assert call(_problem(), None) == bd.GDR_ERR_INVALID_ARG
+    assert call(_problem(chunk=32), _inputs()) == bd.GDR_ERR_UNSUPPORTED
+    assert call(_problem(), _inputs(), o=None) == bd.GDR_ERR_INVALID_ARG
+    big = _problem(B=1, H=16, T=8192)
+    assert call(big, _inputs()) == bd.GDR_ERR_WORKSPACE
+    assert "scratch" in lib.gdr_last_error().decode()
+    # with a saved buffer only the scan's own buffers live in the scratch: the same problem fits
+    # (the call then goes on to look up the device, which fails here without a GPU)
+    assert call(big, _inputs(), saved=FAKE) != bd.GDR_ERR_WORKSPACE
