@@ -64,7 +64,8 @@ struct BwdScanOps<E, D, BV, VAR_KDA> {
 // dr_t / beta_t to dR_t before dR feeds the memory gradient and the chunk kernel.  dRog, if not
 // NULL, also receives dR without that term (the beta gradient is formed from it, see
 // k_bwd_res_dbeta).
-template <typename E, int D, int BV, int VAR, bool RES>
+// QKN (delta family): q and k are the preparation's per-unit scaled copies (see k_fwd_prep).
+template <typename E, int D, int BV, int VAR, bool RES, bool QKN>
 __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ dO, const E* __restrict__ Xg,
                                                   const E* __restrict__ Mg, const float* __restrict__ Gg,
@@ -79,6 +80,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   constexpr bool KDA = VAR == VAR_KDA;
   constexpr bool DEC = VAR == VAR_GATED || G2;  // scalar decay
   static_assert(!RES || VAR == VAR_DELTANET || VAR == VAR_GATED || KDA, "residual gradient: no GDN-2");
+  static_assert(!QKN || VAR == VAR_DELTANET || VAR == VAR_GATED, "fused q/k normalisation: delta family");
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];  // a = beta e*k (GDN-2)
   __shared__ float bsh[CH];
   __shared__ __align__(16) E Qs[CH * LD];
@@ -157,8 +159,8 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
 #pragma unroll
         for (int qq = 0; qq < NJ; ++qq) p.eg[qq] = *reinterpret_cast<const f32x4*>(Gg + u * D + acc_row(16 * (w + 4 * qq), 0));
       } else {
-        p.q.load(q + tk * D, D, n);
-        p.k.load(k + tk * D, D, n);
+        p.q.load(q + (QKN ? u * CH : tk) * D, D, QKN ? CH : n);
+        p.k.load(k + (QKN ? u * CH : tk) * D, D, QKN ? CH : n);
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
       }
       if constexpr (RES) {  // accumulator layout of dR^T: row 16 w + lrow, columns 16 it + 4 lgrp
@@ -343,7 +345,10 @@ struct BwdLds {
 // RES: the residual r = R / beta was an output; dbeta gains -(dr . r) / beta = -(dr . R) / beta^2.
 // LOG: beta and alpha are logits x; the gradients returned are w.r.t. x:
 // dx_beta = dbeta beta (1 - beta), dx_alpha = d log(alpha) * (-sigmoid(x_alpha)).
-template <typename E, int D, int VAR, bool RES, bool LOG>
+// QKN: q and k are the preparation's per-unit scaled copies x~ = x / ||x|| (rn = 1/||x|| per
+// token in Rn), and dq, dk are returned w.r.t. the raw rows: dx = (dx~ - x~ (x~ . dx~)) / ||x||,
+// formed in float32 before the gradients are rounded.
+template <typename E, int D, int VAR, bool RES, bool LOG, bool QKN>
 __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ v, const E* __restrict__ beta,
                                                    const E* __restrict__ alpha, const E* __restrict__ dO,
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
                                                    const float* __restrict__ Lig,
                                                    E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
                                                    E* __restrict__ dbeta, E* __restrict__ dalpha,
-                                                   const E* __restrict__ drin) {
+                                                   const E* __restrict__ drin, const float* __restrict__ Rng) {
   using Ly = BwdLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDR = Ly::LDR, LF = Ly::LF;
   constexpr int KH = 64, NH = D / KH;  // the memory is read in blocks of 64 value rows
@@ -364,6 +369,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   __shared__ float part8[NT / CH][CH], part8b[NT / CH][CH], part8c[NT / CH][CH];  // partial sums
   __shared__ float rq[4][CH], rkh[8][CH], rkb[8][CH];
   __shared__ float rdr[RES ? CH : 1];  // dr_t . R_t (residual output)
+  __shared__ float invq[QKN ? CH : 1], invk[QKN ? CH : 1];  // 1 / ||x|| of the rows of q and k
 
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
   E* dRs = reinterpret_cast<E*>(smem + Ly::odR);
@@ -409,14 +415,16 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     E* dWh = reinterpret_cast<E*>(smem + Ly::odWh);
     {
       RegTile<E, CH, D, NT> r0, r1, r2, r3;
-      r0.load(k + tk * D, D, n);
+      if constexpr (QKN) r0.load(k + u * CH * D, D, CH);
+      else r0.load(k + tk * D, D, n);
       r1.load(dO + tk * D, D, n);
       r2.load(Rg + u * CH * D, D, CH);
       r3.load(dRg + u * CH * D, D, CH);
       pW.load(Hs + u * D * D, D, KH);
       pdW.load(dHs + u * D * D, D, KH);
       pV.load(v + tk * D, D, n);
-      pQ.load(q + tk * D, D, n);
+      if constexpr (QKN) pQ.load(q + u * CH * D, D, CH);
+      else pQ.load(q + tk * D, D, n);
       pM.load(Mg + u * CH * CH, CH, CH);
       pLi.load(Lig + u * CH * CH, CH, CH);
       if constexpr (RES) {  // dr_t . R_t per row, from the registers: a row is VPR adjacent lanes
@@ -443,6 +451,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       const int t = threadIdx.x;
       gs[t] = graw;
       bs[t] = (t < n) ? (LOG ? gate_sigmoid((float)braw) : (float)braw) : 0.f;
+      if constexpr (QKN) {
+        invq[t] = Rng[u * 2 * CH + t];
+        invk[t] = Rng[u * 2 * CH + CH + t];
+      }
     }
     for (int ih = 0; ih < NH; ++ih) {
       __syncthreads();
@@ -735,6 +747,41 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     part8[pt][t] = a;
   }
   __syncthreads();
+  if constexpr (QKN) {  // gradients w.r.t. the raw rows: dx = (dx~ - x~ (x~ . dx~)) / ||x||
+    // k~ . dk~ per row: a row's columns are split over waves w and w ^ 4; the partial sums go
+    // through the pair-term region, no longer read
+    float* rkn = reinterpret_cast<float*>(smem + Ly::oPair);
+    {
+      float part = 0.f;
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        const f32x4 kv = get4(Ks + tr * LD + 16 * (wn * NQ + qq) + 4 * lgrp());
+        part += kv[0] * dka[qq][0] + kv[1] * dka[qq][1] + kv[2] * dka[qq][2] + kv[3] * dka[qq][3];
+      }
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      if (lgrp() == 0) rkn[w * CH + tr] = part;
+    }
+    __syncthreads();
+    if (w < 4) {  // dq: this wave holds every column of rows tr
+      float dot = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) {
+        const f32x4 qv = get4(Qs + tr * LD + 16 * nt + 4 * lgrp());
+        dot += qv[0] * acc1[nt][0] + qv[1] * acc1[nt][1] + qv[2] * acc1[nt][2] + qv[3] * acc1[nt][3];
+      }
+      dot += __shfl_xor(dot, 16, 64);
+      dot += __shfl_xor(dot, 32, 64);
+      const float rn = invq[tr];
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = (acc1[nt] - dot * get4(Qs + tr * LD + 16 * nt + 4 * lgrp())) * rn;
+    }
+    const float dot = rkn[wm * CH + tr] + rkn[(wm + 4) * CH + tr];
+    const float rn = invk[tr];
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq)
+      dka[qq] = (dka[qq] - dot * get4(Ks + tr * LD + 16 * (wn * NQ + qq) + 4 * lgrp())) * rn;
+  }
   // outputs: dq, dk through LDS (the dR/dX regions are free now)
   E* sq = reinterpret_cast<E*>(smem + Ly::odR);
   E* sk = reinterpret_cast<E*>(smem + Ly::odX);
@@ -804,7 +851,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
 // beta gradient is overwritten.  One workgroup of 512 threads per (chunk, head).
 // OWN_A (delta family): A is formed from K and the log decays as the forward formed it (the
 // forward keeps no copy); otherwise (Kimi Delta Attention) it is read from the forward's cache.
-template <typename E, int D, bool OWN_A>
+template <typename E, int D, bool OWN_A, bool QKN>
 __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restrict__ Rg, const E* __restrict__ dRog,
                                                        const E* __restrict__ drin, const E* __restrict__ beta,
                                                        const float* __restrict__ Ag, const E* __restrict__ k,
@@ -830,8 +877,12 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
   {
     RegTile<E, CH, D, NT> rR, rO, rd, rk;
     RegTile<float, CH, CH, NT> rA, rL;
-    if constexpr (OWN_A) rk.load(k + tk * D, D, n);
-    else rA.load(Ag + u * CH * CH, CH, CH);
+    if constexpr (OWN_A) {
+      if constexpr (QKN) rk.load(k + u * CH * D, D, CH);  // the forward's scaled keys
+      else rk.load(k + tk * D, D, n);
+    } else {
+      rA.load(Ag + u * CH * CH, CH, CH);
+    }
     rR.load(Rg + u * CH * D, D, CH);
     rO.load(dRog + u * CH * D, D, CH);
     rL.load(Lig + u * CH * CH, CH, CH);
@@ -985,8 +1036,8 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
                            const gdr_grads& gr, hipStream_t st) {
   const Geo& g = p.geo;
   constexpr bool KDA = VAR == VAR_KDA;
-  const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
-  const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
+  const E* qin = KDA ? (const E*)p.Qh : p.qkn ? (const E*)p.Qn : (const E*)in.q;
+  const E* kin = KDA ? (const E*)p.Kb : p.qkn ? (const E*)p.Kn : (const E*)in.k;
   const float* gin = KDA ? p.Gn : p.G;
   // residual gradient: delta family and Kimi Delta Attention (whose residual has the same form)
   constexpr bool RES_OK = VAR == VAR_DELTANET || VAR == VAR_GATED || KDA;
@@ -1001,18 +1052,26 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
                        qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp, (E*)p.dHs, (E*)p.dR, dh0p,
                        (const E*)in.beta, (const E*)in.erase, d, d ? dro : nullptr);
   };
-  auto scan = [&](const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult) {
+  constexpr bool QOK = VAR == VAR_DELTANET || VAR == VAR_GATED;  // fused q/k normalisation
+  auto scan_q = [&](auto qkn, const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult) {
+    constexpr bool Q = decltype(qkn)::value;
     if (p.bv == 16) {
       if constexpr (RES_OK) {
-        if (drp) return launch(k_bwd_scan<E, D, 16, VAR, true>, 16, sg, dhtp, dh0p, nv_mult, drp);
+        if (drp) return launch(k_bwd_scan<E, D, 16, VAR, true, Q>, 16, sg, dhtp, dh0p, nv_mult, drp);
       }
-      launch(k_bwd_scan<E, D, 16, VAR, false>, 16, sg, dhtp, dh0p, nv_mult, nullptr);
+      launch(k_bwd_scan<E, D, 16, VAR, false, Q>, 16, sg, dhtp, dh0p, nv_mult, nullptr);
     } else {
       if constexpr (RES_OK) {
-        if (drp) return launch(k_bwd_scan<E, D, 32, VAR, true>, 32, sg, dhtp, dh0p, nv_mult, drp);
+        if (drp) return launch(k_bwd_scan<E, D, 32, VAR, true, Q>, 32, sg, dhtp, dh0p, nv_mult, drp);
       }
-      launch(k_bwd_scan<E, D, 32, VAR, false>, 32, sg, dhtp, dh0p, nv_mult, nullptr);
+      launch(k_bwd_scan<E, D, 32, VAR, false, Q>, 32, sg, dhtp, dh0p, nv_mult, nullptr);
     }
+  };
+  auto scan = [&](const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult) {
+    if constexpr (QOK) {
+      if (p.qkn) return scan_q(std::true_type{}, sg, dhtp, dh0p, nv_mult);
+    }
+    scan_q(std::false_type{}, sg, dhtp, dh0p, nv_mult);
   };
   if (p.lseg_b == 0) {
     TraceScope ts_("bwd_scan", st);
@@ -1036,22 +1095,36 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
     } else {
       TraceScope ts_("bwd_chunk", st);
       auto chunk = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, (const E*)in.q, (const E*)in.k,
+        hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, qin, kin,
                            (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (const E*)dO, (const E*)p.M,
                            (const float*)p.G, (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR,
-                           p.Li, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta, (E*)gr.dalpha, drp);
+                           p.Li, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta, (E*)gr.dalpha, drp,
+                           (const float*)p.Rn);
       };
-      if (drp) chunk(k_bwd_chunk<E, D, VAR, true, false>);
-      else if (p.gates) chunk(k_bwd_chunk<E, D, VAR, false, true>);
-      else chunk(k_bwd_chunk<E, D, VAR, false, false>);
+      if (p.qkn) {
+        if (drp) chunk(k_bwd_chunk<E, D, VAR, true, false, true>);
+        else if (p.gates) chunk(k_bwd_chunk<E, D, VAR, false, true, true>);
+        else chunk(k_bwd_chunk<E, D, VAR, false, false, true>);
+      } else {
+        if (drp) chunk(k_bwd_chunk<E, D, VAR, true, false, false>);
+        else if (p.gates) chunk(k_bwd_chunk<E, D, VAR, false, true, false>);
+        else chunk(k_bwd_chunk<E, D, VAR, false, false, false>);
+      }
     }
     if constexpr (RES_OK) {
       if (dro) {
         TraceScope ts_("bwd_res_dbeta", st);
-        const auto kern = k_bwd_res_dbeta<E, D, !KDA>;
-        hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, (const E*)p.R,
-                           (const E*)dro, drp, (const E*)in.beta, (const float*)p.A1, kin, gin,
-                           (const float*)p.Li, (E*)gr.dbeta);
+        auto res = [&](auto kern) {
+          hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, (const E*)p.R,
+                             (const E*)dro, drp, (const E*)in.beta, (const float*)p.A1, kin, gin,
+                             (const float*)p.Li, (E*)gr.dbeta);
+        };
+        if constexpr (QOK) {
+          if (p.qkn) res(k_bwd_res_dbeta<E, D, true, true>);
+          else res(k_bwd_res_dbeta<E, D, true, false>);
+        } else {
+          res(k_bwd_res_dbeta<E, D, false, false>);
+        }
       }
     }
   }

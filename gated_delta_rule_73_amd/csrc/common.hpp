@@ -303,6 +303,17 @@ struct RegTile {
       }
     }
   }
+  // G[r*gs + c] <- v, every row (a whole tile, e.g. a per-chunk copy in the workspace)
+  __device__ __forceinline__ void store_global(S* g, long gs) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = threadIdx.x + it * NT;
+      if (TOTAL % NT == 0 || idx < TOTAL) {
+        const int r = idx / VPR, c = (idx % VPR) * VE;
+        *reinterpret_cast<V*>(g + (long)r * gs + c) = v[it];
+      }
+    }
+  }
   // LDS[c*ld + r] <- v (transposed), element by element
   __device__ __forceinline__ void store_t(S* lds, int ld) const {
 #pragma unroll
@@ -320,6 +331,50 @@ struct RegTile {
   __device__ __forceinline__ int row(int it) const { return (threadIdx.x + it * NT) / VPR; }
   __device__ __forceinline__ int col(int it) const { return ((threadIdx.x + it * NT) % VPR) * VE; }
 };
+
+// q/k L2-normalisation of a tile as it is loaded: every row of a register tile scaled to unit
+// length, x / ||x||_2 over its COLS elements in float32 (a zero row, e.g. past a sequence's end,
+// stays zero).  A row lives in VPR adjacent lanes, so its sum of squares is reduced inside that
+// lane group.  inv, if not NULL, receives 1 / ||x|| per row (ROWS floats).
+// Sum over aligned groups of N adjacent lanes (N = 8 or 16) with DPP lane exchanges (plain
+// vector adds, no trip through the LDS crossbar): quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror.  Each exchange pairs lanes symmetrically, so every lane of a
+// group adds the same two operands (in either order) at every step and all of them end with
+// bitwise the same total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum_dpp(float x) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  x += dpp_read<0xB1>(x);
+  x += dpp_read<0x4E>(x);
+  x += dpp_read<0x141>(x);
+  if constexpr (N == 16) x += dpp_read<0x140>(x);
+  return x;
+}
+
+template <typename S, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void normalize_rows(RegTile<S, ROWS, COLS, NT>& t, float* inv) {
+  using RT = RegTile<S, ROWS, COLS, NT>;
+  static_assert(RT::VB == 16 && RT::TOTAL % NT == 0 && 64 % RT::VPR == 0, "whole rows per lane group");
+#pragma unroll
+  for (int it = 0; it < RT::IT; ++it) {
+    S* e = reinterpret_cast<S*>(&t.v[it]);
+    float ss = 0.f;
+#pragma unroll
+    for (int x = 0; x < RT::VE; ++x) {
+      const float f = (float)e[x];
+      ss += f * f;
+    }
+    ss = group_sum_dpp<RT::VPR>(ss);
+    const float rn = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
+#pragma unroll
+    for (int x = 0; x < RT::VE; ++x) e[x] = (S)((float)e[x] * rn);
+    if (inv && threadIdx.x % RT::VPR == 0) inv[t.row(it)] = rn;
+  }
+}
 
 // LDS[r*ld + c] = G[r*gs + c] for r < nrows, 0 for nrows <= r < ROWS; c < COLS.
 template <typename S, int ROWS, int COLS, int NT>

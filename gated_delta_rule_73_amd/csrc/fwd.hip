@@ -21,12 +21,16 @@ namespace gdr {
 // Prep: per (head, chunk) -- g, M, L^{-1}, X, U.
 // ---------------------------------------------------------------------------------------
 // LOG: beta and alpha are logits (beta = sigmoid(x), log alpha = -softplus(x)).
-template <typename E, int D, int VAR, bool LOG>
+// QKN: q and k are scaled to unit length per token as they are loaded (normalize_rows); the
+// scaled tiles (zero past the sequence's end) and 1/||q||, 1/||k|| are kept per unit in Qno,
+// Kno, Rno, and every later kernel reads those instead of q and k.
+template <typename E, int D, int VAR, bool LOG, bool QKN>
 __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ v, const E* __restrict__ beta,
                                                   const E* __restrict__ alpha, E* __restrict__ Xo,
                                                   E* __restrict__ Uo, E* __restrict__ Mo, float* __restrict__ Go,
-                                                  float* __restrict__ Lio) {
+                                                  float* __restrict__ Lio, E* __restrict__ Qno, E* __restrict__ Kno,
+                                                  float* __restrict__ Rno) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   static_assert(CH * LDT * (int)sizeof(E) >= 4 * 256 * 4, "T buffer doubles as the solve's scratch");
   __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g * K, then X
@@ -55,6 +59,12 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   rk.load(k + tk * D, D, cp.n);
   rq.load(q + tk * D, D, cp.n);
   rv.load(v + tk * D, D, cp.n);
+  if constexpr (QKN) {
+    normalize_rows(rq, Rno + u * 2 * CH);
+    normalize_rows(rk, Rno + u * 2 * CH + CH);
+    rq.store_global(Qno + u * CH * D, D);
+    rk.store_global(Kno + u * CH * D, D);
+  }
   rk.store(Ks, LD);
   rq.store(QV, LD);
   if (threadIdx.x < CH) {
@@ -189,7 +199,9 @@ struct FwdScanOps {
   E braw;  // residual output: beta of this lane's token, as loaded (converted where it is used)
 };
 
-template <typename E, int D, int BV, int VAR, bool FULL, bool RES>
+// QKN (delta family): q and k are the preparation's per-unit scaled copies (unit length per
+// token, zero past the end), read like Kimi Delta Attention's per-unit operands.
+template <typename E, int D, int BV, int VAR, bool FULL, bool RES, bool QKN>
 __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ k, const E* __restrict__ Xg,
                                                   const E* __restrict__ Ug, const float* __restrict__ Gg,
                                                   const float* __restrict__ h0, E* __restrict__ Hs,
@@ -225,6 +237,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
   __shared__ __align__(16) E M2s[OUT_G2 ? CH * LDR : 8];
   __shared__ __align__(16) E Os[FULL ? CH * LDV : 8];
   static_assert(!RES || (FULL && !G2), "the residual output is formed by the full pass of the delta family");
+  static_assert(!QKN || VAR == VAR_DELTANET || VAR == VAR_GATED, "fused q/k normalisation: delta family");
   __shared__ __align__(16) E Rr[RES ? CH * LDV : 8];  // r = R / beta for this tile's value columns
   __shared__ float gs[CH];
 
@@ -286,7 +299,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     }
     if (part < 0 || part == 1) {
       if constexpr (FULL) {
-        p.q.load(q + (KDA ? u * CH : tk) * D, D, KDA ? CH : n);
+        p.q.load(q + ((KDA || QKN) ? u * CH : tk) * D, D, (KDA || QKN) ? CH : n);
         p.m.load(Mg + u * CH * CH, CH, CH);
         if constexpr (G2) p.m2.load(M2g + u * CH * CH, CH, CH);
       }
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       if constexpr (KDA) {
         p.k.load(k + u * CH * D, D, CH);
       } else {
-        p.k.load(k + tk * D, D, n);
+        p.k.load(k + (QKN ? u * CH : tk) * D, D, QKN ? CH : n);
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
       }
       if constexpr (RES) {  // a plain load (valid row), no arithmetic on it until the step uses it
@@ -314,7 +327,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     const long u = (long)(sp.gc0 + c) * geo.H + h;
     const int n = min(CH, sp.len - c * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + c * CH);
-    p.x.store(Xs, LD);
+      p.x.store(Xs, LD);
     p.k.store(Ks, LD);
     p.u.store(Us, LDV);
     if constexpr (FULL) {
@@ -476,15 +489,21 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
       TraceScope ts_("fwd_prep", st);
       auto prep = [&](auto kern) {
         hipLaunchKernelGGL(kern, cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k, (const E*)in.v,
-                           (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G, p.Li);
+                           (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G, p.Li,
+                           (E*)p.Qn, (E*)p.Kn, p.Rn);
       };
-      if (p.gates) prep(k_fwd_prep<E, D, VAR, true>);
-      else prep(k_fwd_prep<E, D, VAR, false>);
+      if (p.qkn) {
+        if (p.gates) prep(k_fwd_prep<E, D, VAR, true, true>);
+        else prep(k_fwd_prep<E, D, VAR, false, true>);
+      } else {
+        if (p.gates) prep(k_fwd_prep<E, D, VAR, true, false>);
+        else prep(k_fwd_prep<E, D, VAR, false, false>);
+      }
     }
   }
   constexpr bool KDA = VAR == VAR_KDA;
-  const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
-  const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
+  const E* kin = KDA ? (const E*)p.Kb : p.qkn ? (const E*)p.Kn : (const E*)in.k;
+  const E* qin = KDA ? (const E*)p.Qh : p.qkn ? (const E*)p.Qn : (const E*)in.q;
   const float* gin = KDA ? p.Gn : p.G;
   E* out = want_out ? (E*)o : nullptr;
   E* rout = (want_out && r) ? (E*)r : nullptr;
@@ -494,21 +513,28 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
                        (const E*)in.beta, (const E*)in.erase, (const E*)in.write, qin, (const E*)p.M, (const E*)p.M2,
                        out, rr);
   };
-  auto scan = [&](auto full, const ScanSeg& sg, const float* h0, float* htp) {
+  auto scan_q = [&](auto full, auto qkn, const ScanSeg& sg, const float* h0, float* htp) {
     constexpr bool F = decltype(full)::value;
+    constexpr bool Q = decltype(qkn)::value;
     constexpr bool RES_OK = F && VAR != VAR_GDN2 && VAR != VAR_GDN2L;  // residual output: full pass, delta family and KDA
     const int nvm = F ? 1 : 2;
     if (std::is_same<E, float>::value || p.bv == 16) {
       if constexpr (RES_OK) {
-        if (rout) return launch(k_fwd_scan<E, D, 16, VAR, F, true>, 16, nvm, sg, h0, htp, rout);
+        if (rout) return launch(k_fwd_scan<E, D, 16, VAR, F, true, Q>, 16, nvm, sg, h0, htp, rout);
       }
-      launch(k_fwd_scan<E, D, 16, VAR, F, false>, 16, nvm, sg, h0, htp, nullptr);
+      launch(k_fwd_scan<E, D, 16, VAR, F, false, Q>, 16, nvm, sg, h0, htp, nullptr);
     } else if constexpr (!std::is_same<E, float>::value) {
       if constexpr (RES_OK) {
-        if (rout) return launch(k_fwd_scan<E, D, 32, VAR, F, true>, 32, nvm, sg, h0, htp, rout);
+        if (rout) return launch(k_fwd_scan<E, D, 32, VAR, F, true, Q>, 32, nvm, sg, h0, htp, rout);
       }
-      launch(k_fwd_scan<E, D, 32, VAR, F, false>, 32, nvm, sg, h0, htp, nullptr);
+      launch(k_fwd_scan<E, D, 32, VAR, F, false, Q>, 32, nvm, sg, h0, htp, nullptr);
     }
+  };
+  auto scan = [&](auto full, const ScanSeg& sg, const float* h0, float* htp) {
+    if constexpr (VAR == VAR_DELTANET || VAR == VAR_GATED) {
+      if (p.qkn) return scan_q(full, std::true_type{}, sg, h0, htp);
+    }
+    scan_q(full, std::false_type{}, sg, h0, htp);
   };
   if (p.lseg == 0) {
     TraceScope ts_("fwd_scan", st);

@@ -42,8 +42,10 @@ struct Sizes {
   int bv = 16, lseg = 0, max_seg = 1;  // scan value tile; forward segmented scans (see plan_scans)
   int lseg_b = 0, max_seg_b = 1;       // backward segmented scans
   size_t X, M, G, Hs, R, M2, U2, Li, A1, A2, Kb, Qh, Gn, Ub, dHs, dR, g2, seg;
-  size_t qn = 0;  // with qk_norm: the normalised q and k (after the cache in the workspace)
-  size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Li + A1 + A2 + Kb + Qh + Gn; }
+  size_t Qn = 0, Kn = 0, Rn = 0;  // q/k normalisation of the delta family: scaled copies, inverse norms
+  size_t qn = 0;  // with qk_norm outside the kernels: the normalised q and k (after the cache)
+  bool qkn = false;  // with qk_norm: the kernels normalise q and k as they load them
+  size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Li + A1 + A2 + Kb + Qh + Gn + Qn + Kn + Rn; }
   size_t fwd_ws() const { return Ub + seg; }                   // workspace before the cache
   size_t bwd_ws() const { return Ub + dHs + dR + g2 + seg; }
 };
@@ -175,7 +177,15 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   plan_scans((long long)s.nstates * p->H, p->dk, max_chunks, p->dtype == GDR_F32, &s);
   const size_t ms = (size_t)std::max(s.lseg ? s.max_seg : 0, s.lseg_b ? s.max_seg_b : 0);
   s.seg = ms ? align_up((size_t)s.nstates * p->H * ms * 3 * D * D * 4, A) : 0;
-  s.qn = p->qk_norm ? 2 * align_up((size_t)p->B * p->H * p->T * D * s.esz, A) : 0;
+  // q/k normalisation: the delta family's preparation kernel normalises the rows it loads and
+  // keeps per-chunk copies (and the inverse norms) in the cache for the scans and the backward;
+  // Kimi Delta Attention and Gated DeltaNet-2 normalise into workspace copies first
+  s.qkn = p->qk_norm && (p->variant == GDR_DELTANET || p->variant == GDR_GATED);
+  s.qn = (p->qk_norm && !s.qkn) ? 2 * align_up((size_t)p->B * p->H * p->T * D * s.esz, A) : 0;
+  if (s.qkn) {
+    s.Qn = s.Kn = align_up(U * C * D * s.esz, A);
+    s.Rn = align_up(U * 2 * C * 4, A);
+  }
   *sz = s;
   return GDR_OK;
 }
@@ -218,6 +228,7 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
   pl.variant = p->variant;
   pl.dtype = p->dtype;
   pl.gates = p->gates;
+  pl.qkn = s.qkn ? 1 : 0;
   pl.D = p->dk;
   pl.bv = s.bv;
   pl.lseg = s.lseg;
@@ -238,6 +249,9 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
   pl.Kb = c; c += s.Kb;
   pl.Qh = c; c += s.Qh;
   pl.Gn = reinterpret_cast<float*>(c); c += s.Gn;
+  pl.Qn = s.Qn ? c : nullptr; c += s.Qn;
+  pl.Kn = s.Kn ? c : nullptr; c += s.Kn;
+  pl.Rn = s.Rn ? reinterpret_cast<float*>(c) : nullptr; c += s.Rn;
   char* w = ws;
   pl.Ub = w; w += s.Ub;
   pl.seg_maps = reinterpret_cast<float*>(w);
@@ -280,7 +294,7 @@ gdr_status hip_status(hipError_t e, const char* what) {
 // With qk_norm, writes q / ||q|| and k / ||k|| (per token) into the workspace region at `dst`
 // and points the inputs at them; otherwise leaves the inputs as they are.
 gdr_status normalize_qk(const gdr_problem* p, const Sizes& s, char* dst, gdr_inputs* ins, hipStream_t st) {
-  if (!p->qk_norm || p->T == 0) return GDR_OK;
+  if (!p->qk_norm || s.qkn || p->T == 0) return GDR_OK;
   const long rows = (long)p->B * p->H * p->T;
   char* qn = dst;
   char* kn = dst + s.qn / 2;
@@ -395,6 +409,9 @@ gdr::Plan sub_plan(const gdr::Plan& pl, const gdr_problem* p, const Sizes& s, co
   q.Ub = adv(q.Ub, C * D * e);
   q.dHs = adv(q.dHs, D * D * e);
   q.dR = adv(q.dR, C * D * e);
+  q.Qn = adv(q.Qn, C * D * e);
+  q.Kn = adv(q.Kn, C * D * e);
+  q.Rn = adv(q.Rn, 2 * C * 4);
   return q;
 }
 
@@ -618,7 +635,7 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
     }
     st = hip_status(gdr::run_backward(pl, ins, dO, dr, dht, *g, hs), "gdr_backward launch");
   }
-  if (st != GDR_OK || !p->qk_norm) return st;
+  if (st != GDR_OK || !p->qk_norm || s.qkn) return st;
   // gradients w.r.t. the raw q and k, through the normalisation
   const long rows = (long)p->B * p->H * p->T;
   st = hip_status(gdr::run_l2norm(p->dtype, p->dk, in->q, g->dq, rows, true, hs), "gdr_backward q normalisation");

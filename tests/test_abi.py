@@ -245,7 +245,19 @@ def test_gate_logit_checks(lib):
 
 
 def test_qk_norm_checks_and_workspace(lib):
+    # the delta family's preparation keeps per-chunk scaled copies of q and k and the inverse
+    # norms in the forward->backward cache (zero past each sequence's end)
     p = _problem(B=2, H=4, T=300)
+    st, plain = _ws(lib, p, True)
+    assert st == bd.GDR_OK
+    p.qk_norm = 1
+    st, normed = _ws(lib, p, True)
+    assert st == bd.GDR_OK
+    units = 2 * 5 * 4
+    al = lambda x: (x + 255) // 256 * 256
+    assert normed == plain + 2 * al(units * 64 * 128 * 2) + al(units * 2 * 64 * 4)
+    # Kimi Delta Attention normalises into two workspace copies first
+    p = _problem(B=2, H=4, T=300, variant=2)
     st, plain = _ws(lib, p, True)
     assert st == bd.GDR_OK
     p.qk_norm = 1

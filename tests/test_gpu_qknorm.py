@@ -62,3 +62,36 @@ def test_qk_norm_packed_pipelined(monkeypatch):
     cu = [0, 70, 70, 200, 333]
     inp = _inputs("gated", "bf16", 128, T=333, B=1, H=3, cu=cu)
     compare(_hip(inp, "gated", "bf16", True), _oracle(inp, "gated"), "bf16")
+
+
+@pytest.mark.parametrize("variant,dtype,d", [("gated", "bf16", 128), ("deltanet", "f32", 64)])
+def test_qk_norm_segmented_scans(monkeypatch, variant, dtype, d):
+    """Fused normalisation through the segmented scans (map pass, combine, rerun forced on),
+    packed sequences with an empty one and ragged tails."""
+    monkeypatch.setenv("GDR_SEG_CHUNKS", "1")
+    cu = [0, 150, 150, 347]
+    inp = _inputs(variant, dtype, d, T=347, B=1, H=2, cu=cu)
+    compare(_hip(inp, variant, dtype, False), _oracle(inp, variant), dtype)
+
+
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda"])
+def test_qk_norm_with_residual(variant):
+    """Normalised q and k with the residual output and its gradient (bf16: the beta gradient's
+    second pass forms A again from the normalised keys)."""
+    import torch
+    from gated_delta_rule_73_amd import gdr_backward, gdr_forward
+    from oracle import recurrence as R
+    inp = _inputs(variant, "bf16", 128, T=200)
+    dr = synth.to_io(np.random.default_rng(5).standard_normal(inp["v"].shape), "bf16")
+    g = gpu_inputs(inp, "bf16")
+    r = torch.empty_like(g["v"])
+    o, ht, saved = gdr_forward(**g, variant=variant, save=True, residual=r, qk_norm=True)
+    gr = gdr_backward(**g, do=to_gpu(inp["do"], "bf16"), dr=to_gpu(dr, "bf16"), variant=variant, saved=saved,
+                      qk_norm=True)
+    torch.cuda.synchronize()
+    got = {"o": to_np(o), "ht": to_np(ht), "r": to_np(r), **{k: to_np(v) for k, v in gr.items()}}
+    kw = {n: inp.get(n) for n in ("q", "k", "v", "beta", "alpha", "erase", "write", "h0")}
+    oo, hh, rr = R.forward(**kw, variant=variant, residual=True, qk_l2norm=True)
+    ref = {"o": oo, "ht": hh, "r": rr}
+    ref.update(R.backward(**kw, do=inp["do"], dr=dr, variant=variant, qk_l2norm=True))
+    compare(got, ref, "bf16")
