@@ -19,6 +19,15 @@ controlling decay, erasing and writing:
                        which key channels are erased, the other which value
                        channels are stored.
 
+The erase-free decayed memories of the earlier generation of matrix-state
+models (RetNet with a fixed decay, GLA with data-dependent gates: page "Resumen
+Tecnico: Un Analisis Sistematico de la Atencion Lineal Hibrida" (gist.science),
+section "Metodologia", list "Modelos Evaluados", item 2; the same page's
+"Olvido Controlado" bullet calls GLA's update purely additive) are the same
+memory with nothing erased: Gated DeltaNet-2 with a closed erase gate (scalar
+decay), and here variant "gla", a decay per key channel:
+W <- W diag(alpha) + beta v k^T (beta optional, 1 when absent).
+
 The pages print no formula beyond r = v - v_bar.  Readings taken here (each is
 listed with its justification in the design notes):
 
@@ -34,7 +43,8 @@ listed with its justification in the design notes):
   * Output o_t = scale * W_t q_t with the memory after token t's write.
   * Optionally the residual itself, r_t = v_t - v_bar_t (the delta rule's write
     error, which the pages' cross-layer error routing passes to another layer),
-    for the delta family; Gated DeltaNet-2 has no single residual.
+    for the delta family; Gated DeltaNet-2 and the erase-free "gla" have no
+    single residual.
 
 Everything is float64.  Heads are independent memories; the per-token update
 is applied to all heads of one sequence at once (numpy batching over the head
@@ -44,7 +54,7 @@ from __future__ import annotations
 
 import numpy as np
 
-_VARIANTS = ("deltanet", "gated", "kda", "gdn2")
+_VARIANTS = ("deltanet", "gated", "kda", "gdn2", "gla")
 
 
 def _f64(x):
@@ -89,7 +99,7 @@ class _Seq:
         """W' = W D_t: no decay, a scalar per head, or one factor per key channel (columns)."""
         if self.variant == "deltanet":
             return W.copy()
-        if self.variant == "kda":
+        if self.variant in ("kda", "gla"):
             return W * self.alpha[:, t][:, None, :]
         return W * self.alpha[:, t][:, None, None]
 
@@ -105,6 +115,8 @@ class _Seq:
             erase_dir = beta[:, None] * self.erase[:, t] * k          # which key channels lose v_bar
             stored = beta[:, None] * self.write[:, t] * v             # which value channels are stored
             Wt = Wd - v_bar[:, :, None] * erase_dir[:, None, :] + stored[:, :, None] * k[:, None, :]
+        elif self.variant == "gla":
+            Wt = Wd + (beta[:, None] * v)[:, :, None] * k[:, None, :]  # nothing erased, v written at k
         else:
             r = v - v_bar                                             # the delta-rule residual
             Wt = Wd + (beta[:, None] * r)[:, :, None] * k[:, None, :]
@@ -120,13 +132,13 @@ def _check(variant, q, k, v, beta, alpha, erase, write):
         raise ValueError(f"unknown variant {variant!r}")
     if (alpha is None) != (variant == "deltanet"):
         raise ValueError("alpha is required by every variant except deltanet")
-    if variant == "kda" and alpha.shape != k.shape:
-        raise ValueError("kda takes one decay per key channel: alpha must be [B,H,T,dk]")
+    if variant in ("kda", "gla") and alpha.shape != k.shape:
+        raise ValueError(f"{variant} takes one decay per key channel: alpha must be [B,H,T,dk]")
     if variant in ("gated", "gdn2") and alpha.shape != k.shape[:3]:
         raise ValueError("scalar decay alpha must be [B,H,T]")
     if (erase is None or write is None) != (variant != "gdn2"):
         raise ValueError("erase/write gates are used by gdn2 only")
-    if beta is None and variant != "gdn2":
+    if beta is None and variant not in ("gdn2", "gla"):
         raise ValueError("beta is required by the delta family")
 
 
@@ -192,8 +204,8 @@ def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
     qk_l2norm: q and k are first scaled to unit length per token (l2_normalize).
     gate_logits: beta, alpha, erase and write are logits, mapped by gates_from_logits first.
 
-    q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] (None -> 1, gdn2 only);
-    alpha: None (deltanet), [B,H,T] (gated, gdn2) or [B,H,T,dk] (kda);
+    q, k: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] (None -> 1, gdn2 and gla only);
+    alpha: None (deltanet), [B,H,T] (gated, gdn2) or [B,H,T,dk] (kda, gla);
     erase: [B,H,T,dk], write: [B,H,T,dv] (gdn2 only); h0: [N,H,dv,dk] or None (zeros),
     where N = B, or the number of packed sequences when cu_seqlens is given (then B == 1).
     """
@@ -203,8 +215,8 @@ def forward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, *,
     if gate_logits:
         beta, alpha, erase, write = gates_from_logits(beta, alpha, erase, write)
     _check(variant, q, k, v, beta, alpha, erase, write)
-    if residual and variant == "gdn2":
-        raise ValueError("gdn2 has separate erase and write terms, not one residual")
+    if residual and variant in ("gdn2", "gla"):
+        raise ValueError(f"{variant} writes without a residual (no single residual)")
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     seqs = list(_sequences(B, T, cu_seqlens))
@@ -250,8 +262,8 @@ def backward(q, k, v, beta=None, alpha=None, erase=None, write=None, h0=None, do
         g["dq"], g["dk"] = l2_normalize_backward(q, g["dq"]), l2_normalize_backward(k, g["dk"])
         return g
     _check(variant, q, k, v, beta, alpha, erase, write)
-    if dr is not None and variant == "gdn2":
-        raise ValueError("gdn2 has separate erase and write terms, not one residual")
+    if dr is not None and variant in ("gdn2", "gla"):
+        raise ValueError(f"{variant} writes without a residual (no single residual)")
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     seqs = list(_sequences(B, T, cu_seqlens))
@@ -305,6 +317,9 @@ def _token_backward(s, t, W_prev, dW, do_t, g, b, t0, dr_t=None):
         w = s.write[:, t]
         a = beta[:, None] * e * k
         bvec = beta[:, None] * w * v
+    elif s.variant == "gla":
+        a = np.zeros_like(k)                  # nothing erased
+        bvec = beta[:, None] * v
     else:
         a = beta[:, None] * k
         bvec = beta[:, None] * v
@@ -325,6 +340,10 @@ def _token_backward(s, t, W_prev, dW, do_t, g, b, t0, dr_t=None):
         g["dv"][b, :, tt] += beta[:, None] * d_b * w
         if g["dbeta"] is not None:
             g["dbeta"][b, :, tt] += np.sum(d_a * e * k, -1) + np.sum(d_b * w * v, -1)
+    elif s.variant == "gla":
+        g["dv"][b, :, tt] += beta[:, None] * d_b
+        if g["dbeta"] is not None:
+            g["dbeta"][b, :, tt] += np.sum(d_b * v, -1)
     else:
         dk_t += beta[:, None] * d_a
         g["dv"][b, :, tt] += beta[:, None] * d_b
@@ -333,7 +352,7 @@ def _token_backward(s, t, W_prev, dW, do_t, g, b, t0, dr_t=None):
     # decay: Wd = W_prev D_t
     if s.variant == "deltanet":
         s.last_dW_prev = dWd
-    elif s.variant == "kda":
+    elif s.variant in ("kda", "gla"):
         al = s.alpha[:, t]
         g["dalpha"][b, :, tt] += np.einsum("hij,hij->hj", dWd, W_prev)
         s.last_dW_prev = dWd * al[:, None, :]

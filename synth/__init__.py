@@ -26,7 +26,7 @@ from typing import Optional
 
 import numpy as np
 
-VARIANTS = ("deltanet", "gated", "kda", "gdn2")
+VARIANTS = ("deltanet", "gated", "kda", "gdn2", "gla")
 
 
 @dataclasses.dataclass(frozen=True)
@@ -69,6 +69,11 @@ WORKLOADS = {
     "gated_varlen_T32768": Workload("gated_varlen_T32768", "gated", "bf16", 1, 16, 32768, 128, 128,
                                     seed=4, cu_seqlens=(0, 4096, 12288, 24576, 32768),
                                     h0_std=0.02),
+}
+# The erase-free memory with a decay per key channel (GLA form), at the Kimi Delta Attention
+# workload's shape and laws (no workload of the operator study uses it; timed with --workload).
+EXTRA_WORKLOADS = {
+    "gla_B4H16T8192": Workload("gla_B4H16T8192", "gla", "bf16", 4, 16, 8192, 128, 128, seed=6),
 }
 # Decoding: one new token per sequence against a batch of memories (the recurrent form).  Not
 # a workload of the operator study (the pages give no inference benchmark); sized so the
@@ -149,7 +154,7 @@ def make_inputs(w: Workload, *, alpha_mode: str = "config", with_grad: Optional[
     if w.variant == "deltanet":
         out["alpha"] = None
     else:
-        shape = (B, H, T, dk) if w.variant == "kda" else (B, H, T)
+        shape = (B, H, T, dk) if w.variant in ("kda", "gla") else (B, H, T)
         if alpha_mode == "one":
             if gate_logits:
                 raise ValueError("alpha = 1 has no finite logit")

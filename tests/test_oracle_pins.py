@@ -28,7 +28,7 @@ def _rand_inputs(rng, variant, B=1, H=2, T=9, dk=5, dv=4, unit_keys=True, beta=T
     b = rng.uniform(0.05, 0.95, (B, H, T)) if beta else None
     if variant == "deltanet":
         a = None
-    elif variant == "kda":
+    elif variant in ("kda", "gla"):
         a = rng.uniform(0.3, 0.99, (B, H, T, dk))
     else:
         a = rng.uniform(0.3, 0.99, (B, H, T))
@@ -41,7 +41,7 @@ def _decay_vec(alpha, variant, b, h, t, dk):
     """Per-key-channel decay of token t as a vector (ones for deltanet)."""
     if variant == "deltanet":
         return np.ones(dk)
-    if variant == "kda":
+    if variant in ("kda", "gla"):
         return alpha[b, h, t]
     return np.full(dk, alpha[b, h, t])
 
@@ -49,7 +49,7 @@ def _decay_vec(alpha, variant, b, h, t, dk):
 # ---------------------------------------------------------------------------------------
 # Special cases with closed forms
 # ---------------------------------------------------------------------------------------
-@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2"])
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2", "gla"])
 def test_beta_zero_is_pure_decay(variant):
     """beta = 0 writes nothing: W_t = W0 Gamma_t, Gamma_t = prod of the decays (key columns)."""
     rng = np.random.default_rng(1)
@@ -148,6 +148,9 @@ def _brute(x, variant, h0, scale):
                 if variant == "gdn2":
                     a = beta * x["erase"][b, h, t] * kt
                     bb = beta * x["write"][b, h, t] * x["v"][b, h, t]
+                elif variant == "gla":
+                    a = np.zeros(dk)
+                    bb = beta * x["v"][b, h, t]
                 else:
                     a = beta * kt
                     bb = beta * x["v"][b, h, t]
@@ -169,7 +172,7 @@ def _brute(x, variant, h0, scale):
     return o, ht
 
 
-@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2"])
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2", "gla"])
 def test_brute_force_transition_products(variant):
     rng = np.random.default_rng(6)
     x = _rand_inputs(rng, variant, B=2, H=2, T=7, dk=4, dv=3, unit_keys=False)
@@ -183,7 +186,7 @@ def test_brute_force_transition_products(variant):
 # ---------------------------------------------------------------------------------------
 # Invariants
 # ---------------------------------------------------------------------------------------
-@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2"])
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2", "gla"])
 def test_joint_linearity_in_values_and_initial_memory(variant):
     """Given keys, queries and gates, (o, h_T) is linear in (v, h0) jointly."""
     rng = np.random.default_rng(7)
@@ -199,7 +202,7 @@ def test_joint_linearity_in_values_and_initial_memory(variant):
     np.testing.assert_allclose(s3, l1 * s1 + l2 * s2, rtol=1e-10, atol=1e-12)
 
 
-@pytest.mark.parametrize("variant", ["gated", "kda", "gdn2"])
+@pytest.mark.parametrize("variant", ["gated", "kda", "gdn2", "gla"])
 def test_packed_sequences_equal_separate_runs(variant):
     rng = np.random.default_rng(8)
     cu = [0, 5, 6, 14, 20]
@@ -272,7 +275,7 @@ def test_variant_reductions():
 # Reverse mode against central finite differences of the forward
 # ---------------------------------------------------------------------------------------
 @pytest.mark.parametrize("variant,cu", [("deltanet", None), ("gated", None), ("kda", None),
-                                        ("gdn2", None), ("gated", [0, 3, 8])])
+                                        ("gdn2", None), ("gla", None), ("gated", [0, 3, 8])])
 def test_backward_matches_finite_differences(variant, cu):
     rng = np.random.default_rng(12)
     B = 1 if cu else 2
@@ -458,7 +461,7 @@ def test_logit_gate_maps_closed_forms():
                                [-np.log(2.0), -40.0, -np.exp(-40.0)], rtol=1e-14)
 
 
-@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2"])
+@pytest.mark.parametrize("variant", ["deltanet", "gated", "kda", "gdn2", "gla"])
 def test_logit_gradients_match_finite_differences(variant):
     """The whole map from logits to outputs, differentiated by central differences in the
     logits, against the chain rule of backward(gate_logits=True)."""
@@ -488,3 +491,61 @@ def test_logit_gradients_match_finite_differences(variant):
             xm[name][idx] -= eps
             fd[idx] = (loss(xp) - loss(xm)) / (2 * eps)
         np.testing.assert_allclose(g["d" + name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+
+# ---------------------------------------------------------------------------------------
+# The erase-free memory with a decay per key channel (variant "gla")
+# ---------------------------------------------------------------------------------------
+def test_gla_is_causal_linear_attention_with_channel_decay():
+    """Nothing erased: with G_t = sum_{u<=t} log alpha_u per key channel,
+    o_t = W0 (e^{G_t} * q_t) + sum_{s<=t} beta_s v_s (k_s * e^{G_t - G_s}) . q_t and
+    h_T = W0 diag(e^{G_T}) + sum_s beta_s v_s (k_s * e^{G_T - G_s})^T, written here as one
+    masked product over (t, s, channel) -- no recurrence."""
+    rng = np.random.default_rng(51)
+    x = _rand_inputs(rng, "gla", B=1, H=2, T=11, dk=5, dv=4)
+    h0 = rng.standard_normal((1, 2, 4, 5))
+    o, ht = R.forward(**x, h0=h0, variant="gla", scale=0.8)
+    for h in range(2):
+        G = np.cumsum(np.log(x["alpha"][0, h]), axis=0)            # [T, dk]
+        Q, K, V = x["q"][0, h], x["k"][0, h], x["v"][0, h]
+        Bv = x["beta"][0, h][:, None] * V
+        E = np.exp(G[:, None, :] - G[None, :, :])                   # [t, s, j]
+        S = np.einsum("tj,sj,tsj->ts", Q, K, E) * np.tril(np.ones((11, 11)))
+        want = 0.8 * (S @ Bv + (Q * np.exp(G)) @ h0[0, h].T)
+        np.testing.assert_allclose(o[0, h], want, rtol=1e-11, atol=1e-12)
+        hw = h0[0, h] * np.exp(G[-1])[None, :] + Bv.T @ (K * np.exp(G[-1][None, :] - G))
+        np.testing.assert_allclose(ht[0, h], hw, rtol=1e-11, atol=1e-12)
+
+
+def test_gla_with_equal_channels_is_gdn2_with_closed_erase():
+    """One decay shared by every channel is the scalar-decay erase-free memory: Gated
+    DeltaNet-2 with e = 0 and w = 1 (different code paths: column scaling and no erase term
+    against scalar scaling and a zero erase direction).  Without beta both mean beta = 1."""
+    rng = np.random.default_rng(52)
+    x = _rand_inputs(rng, "gdn2", B=2, H=2, T=9, dk=4, dv=3)
+    h0 = rng.standard_normal((2, 2, 3, 4))
+    G = rng.standard_normal((2, 2, 9, 3))
+    for beta in (x["beta"], None):
+        x2 = {**x, "beta": beta, "erase": np.zeros((2, 2, 9, 4)), "write": np.ones((2, 2, 9, 3))}
+        o2, h2 = R.forward(**x2, h0=h0, variant="gdn2")
+        g2 = R.backward(**x2, h0=h0, do=G, variant="gdn2")
+        xg = {**x, "beta": beta, "erase": None, "write": None,
+              "alpha": np.repeat(x["alpha"][..., None], 4, axis=-1)}
+        og, hg = R.forward(**xg, h0=h0, variant="gla")
+        gg = R.backward(**xg, h0=h0, do=G, variant="gla")
+        np.testing.assert_allclose(og, o2, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(hg, h2, rtol=1e-12, atol=1e-13)
+        for name in ("dq", "dk", "dv", "dh0") + (("dbeta",) if beta is not None else ()):
+            np.testing.assert_allclose(gg[name], g2[name], rtol=1e-11, atol=1e-12, err_msg=name)
+        np.testing.assert_allclose(gg["dalpha"].sum(-1), g2["dalpha"], rtol=1e-11, atol=1e-12)
+
+
+def test_gla_without_beta_and_refuses_a_residual():
+    rng = np.random.default_rng(53)
+    x = _rand_inputs(rng, "gla", B=1, H=2, T=6, dk=3, dv=2)
+    o1, _ = R.forward(**{**x, "beta": None}, variant="gla")
+    o2, _ = R.forward(**{**x, "beta": np.ones((1, 2, 6))}, variant="gla")
+    assert np.array_equal(o1, o2)
+    with pytest.raises(ValueError):
+        R.forward(**x, variant="gla", residual=True)
