@@ -49,17 +49,22 @@ def kernel_bytes_per_unit(variant: str, kernel: str, D: int = 128, esz: int = 2,
     C = 64
     TOK, SQR, GRAM, GATE = C * D * esz, D * D * esz, C * C * esz, C * esz
     GLOG, FTOK, FGRAM, FD = C * 4, C * D * 4, C * C * 4, D * 4
-    kda, g2 = variant == "kda", variant == "gdn2"
-    ALPHA = 0 if variant == "deltanet" else (TOK if kda else GATE)
+    kda, g2, gla = variant == "kda", variant == "gdn2", variant == "gla"
+    ALPHA = 0 if variant == "deltanet" else (TOK if (kda or gla) else GATE)
     BETA = GATE if has_beta else 0
-    DEC = FD if kda else GLOG  # per-chunk decay handed to the scans
+    DEC = FD if (kda or gla) else GLOG  # per-chunk decay handed to the scans
     OUT = TOK + GRAM + TOK  # the forward scan also reads q and M and writes o
+    XT = 0 if gla else TOK  # the erase-free memory has no X
     table = {
         "fwd_prep": 3 * TOK + BETA + ALPHA + 2 * TOK + GRAM + GLOG + FGRAM,
         "fwd_prep_kda": 3 * TOK + BETA + ALPHA + 4 * TOK + GRAM + FD + 2 * FGRAM,
         "fwd_prep_gdn2": 5 * TOK + BETA + ALPHA + 3 * TOK + 2 * GRAM + GLOG + 3 * FGRAM,
-        "fwd_scan": (6 * TOK + BETA if g2 else 3 * TOK) + DEC + SQR + TOK + OUT + (GRAM if g2 else 0),
-        "bwd_scan": 3 * TOK + TOK + GRAM + DEC + SQR + TOK + ((TOK + BETA) if g2 else 0),
+        "fwd_prep_gla": 3 * TOK + BETA + ALPHA + 3 * TOK + GRAM + FD,
+        "fwd_scan": (6 * TOK + BETA if g2 else 2 * TOK + XT) + DEC + SQR + TOK + OUT + (GRAM if g2 else 0),
+        "bwd_scan": 2 * TOK + XT + TOK + GRAM + DEC + SQR + TOK + ((TOK + BETA) if g2 else 0),
+        "bwd_gla_state": 2 * TOK + 2 * SQR + FD + 2 * FTOK + FGRAM + FD,
+        "bwd_gla_wv": 3 * TOK + 2 * BETA,
+        "bwd_gla_gram": 2 * TOK + ALPHA + FGRAM + 2 * FTOK + FD + 2 * TOK + ALPHA,
         "bwd_chunk": 4 * TOK + BETA + ALPHA + GRAM + GLOG + 2 * SQR + 2 * TOK + 3 * TOK + BETA + ALPHA + FGRAM,
         "bwd_kda_state": 3 * TOK + 2 * SQR + FD + 3 * FTOK + FGRAM + FD,
         "bwd_kda_wy": 3 * TOK + BETA + ALPHA + FTOK + 2 * FGRAM + TOK + BETA + FTOK + FGRAM,
@@ -93,10 +98,10 @@ def kernel_operator_bytes(variant: str, kernel: str, D: int = 128, esz: int = 2,
     backward needs and writes every gradient: the backward's whole 1800 B at d = 128 (bf16)."""
     TOK = D * esz
     BETA = esz if has_beta else 0
-    kda, g2 = variant == "kda", variant == "gdn2"
-    ALPHA = {"deltanet": 0, "gated": esz, "kda": TOK, "gdn2": esz}[variant]
+    kda, g2 = variant in ("kda", "gla"), variant == "gdn2"
+    ALPHA = {"deltanet": 0, "gated": esz, "kda": TOK, "gdn2": esz, "gla": TOK}[variant]
     EW = 2 * TOK if g2 else 0                         # erase [d_k] and write [d_v] gates
-    qk = 0 if kda else 2 * TOK                        # Kimi's scans read its own per-chunk copies
+    qk = 0 if kda else 2 * TOK                        # per-channel decay: the scans read per-chunk copies
     table = {
         "fwd_prep": 3 * TOK + BETA + ALPHA + EW,
         "fwd_scan": TOK + qk + ((TOK + EW + BETA) if g2 else 0),
@@ -110,9 +115,12 @@ def kernel_operator_bytes(variant: str, kernel: str, D: int = 128, esz: int = 2,
         "bwd_gdn2_wy": 3 * TOK + EW + BETA + 2 * TOK,
         "bwd_gdn2_gram": 3 * TOK + BETA + ALPHA + 3 * TOK + BETA + ALPHA,
         "bwd_res_dbeta": TOK + BETA + (0 if kda else TOK) + BETA,
+        "bwd_gla_state": TOK,
+        "bwd_gla_wv": 2 * TOK + 2 * BETA,
+        "bwd_gla_gram": 2 * TOK + ALPHA + 2 * TOK + ALPHA,
         "fwd_seg_combine": 0, "bwd_seg_combine": 0,
     }
-    table["fwd_prep_kda"] = table["fwd_prep_gdn2"] = table["fwd_prep"]
+    table["fwd_prep_kda"] = table["fwd_prep_gdn2"] = table["fwd_prep_gla"] = table["fwd_prep"]
     table["bwd_scan_maps"] = table["bwd_scan"]
     if residual:
         table["fwd_scan"] += TOK
@@ -135,7 +143,7 @@ def path_bytes_per_head_token(variant: str, D: int = 128, esz: int = 2, has_beta
     v and of every gate (Gated, d = 128, bf16: 2828 bytes).  residual: r written, dr read."""
     tok = D * esz
     beta = esz if has_beta else 0
-    gates = beta + {"deltanet": 0, "gated": esz, "kda": tok, "gdn2": esz + 2 * tok}[variant]
+    gates = beta + {"deltanet": 0, "gated": esz, "kda": tok, "gdn2": esz + 2 * tok, "gla": tok}[variant]
     return (3 * tok + gates + tok) + (4 * tok + gates + 3 * tok + gates) + (2 * tok if residual else 0)
 
 
@@ -494,7 +502,8 @@ def main():
     if args.workload in synth.DECODE_WORKLOADS:
         bench_decode(args, synth.DECODE_WORKLOADS[args.workload])
         return
-    w = synth.WORKLOADS.get(args.workload) or {s.name: s for s in synth.SWEEP}[args.workload]
+    w = synth.WORKLOADS.get(args.workload) or synth.EXTRA_WORKLOADS.get(args.workload) \
+        or {s.name: s for s in synth.SWEEP}[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(w, gate_logits=args.gate_logits)
     cpu = None

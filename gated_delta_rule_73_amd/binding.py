@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgdr.so")
 
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
-VARIANTS = {"deltanet": 0, "gated": 1, "kda": 2, "gdn2": 3}
+VARIANTS = {"deltanet": 0, "gated": 1, "kda": 2, "gdn2": 3, "gla": 4}
 DTYPES = {"f32": 0, "bf16": 1}
 
 _vp = ctypes.c_void_p
@@ -161,7 +161,7 @@ def _token_shapes(p: GdrProblem, variant: str) -> dict:
     B, H, T, dk, dv = p.B, p.H, p.T, p.dk, p.dv
     N = p.n_seqs if p.n_seqs > 0 else B
     return {"q": (B, H, T, dk), "k": (B, H, T, dk), "v": (B, H, T, dv), "beta": (B, H, T),
-            "alpha": (B, H, T, dk) if variant == "kda" else (B, H, T), "erase": (B, H, T, dk),
+            "alpha": (B, H, T, dk) if variant in ("kda", "gla") else (B, H, T), "erase": (B, H, T, dk),
             "write": (B, H, T, dv), "h0": (N, H, dv, dk), "o": (B, H, T, dv), "state": (N, H, dv, dk)}
 
 

@@ -59,6 +59,13 @@ struct BwdScanOps<E, D, BV, VAR_KDA> {
   typename VecT<4 * sizeof(E)>::type dr[BV / 16];  // as in the general case (RES)
   E braw;
 };
+template <typename E, int D, int BV>
+struct BwdScanOps<E, D, BV, VAR_GLA> {  // nothing erased: no X
+  RegTile<E, CH, D, 256> q, k;
+  RegTile<E, CH, CH, 256> m;
+  RegTile<E, CH, BV, 256> dO;
+  f32x4 eg[D / 64];
+};
 
 // RES (delta family, Kimi Delta Attention): the residual r_t = R_t / beta_t was an output too; its gradient dr adds
 // dr_t / beta_t to dR_t before dR feeds the memory gradient and the chunk kernel.  dRog, if not
@@ -77,15 +84,16 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2 || VAR == VAR_GDN2L;
   constexpr bool G2L = VAR == VAR_GDN2L;  // its gates are logits
-  constexpr bool KDA = VAR == VAR_KDA;
+  constexpr bool KDA = VAR == VAR_KDA || VAR == VAR_GLA;  // decay per key channel, per-unit operands
+  constexpr bool NOX = VAR == VAR_GLA;  // nothing erased: X = 0, no dR^T X term
   constexpr bool DEC = VAR == VAR_GATED || G2;  // scalar decay
-  static_assert(!RES || VAR == VAR_DELTANET || VAR == VAR_GATED || KDA, "residual gradient: no GDN-2");
+  static_assert(!RES || VAR == VAR_DELTANET || VAR == VAR_GATED || VAR == VAR_KDA, "residual gradient: not GDN-2, GLA");
   static_assert(!QKN || VAR == VAR_DELTANET || VAR == VAR_GATED, "fused q/k normalisation: delta family");
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];  // a = beta e*k (GDN-2)
   __shared__ float bsh[CH];
   __shared__ __align__(16) E Qs[CH * LD];
   __shared__ __align__(16) E Ks[CH * LD];
-  __shared__ __align__(16) E Xs[CH * LD];
+  __shared__ __align__(16) E Xs[VAR == VAR_GLA ? 8 : CH * LD];
   __shared__ __align__(16) E Ms[CH * LDR];
   // scale * dO and scale * e^g * dO, row-major, read through transposing reads; for bfloat16,
   // rows 64 bytes apart keep those reads free of bank conflicts
@@ -148,7 +156,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
     if (part <= 0) {
-      p.x.load(Xg + u * CH * D, D, CH);
+      if constexpr (!NOX) p.x.load(Xg + u * CH * D, D, CH);
       p.m.load(Mg + u * CH * CH, CH, CH);
       p.dO.load(dO + tk * D + i0, D, n);
     }
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     [[maybe_unused]] const int n = min(CH, sp.len - c * CH);
     p.q.store(Qs, LD);
     p.k.store(Ks, LD);
-    p.x.store(Xs, LD);
+    if constexpr (!NOX) p.x.store(Xs, LD);
     p.m.store(Ms, LDR);
     f32x4 egk[NJ];  // KDA: this chunk's per-row decay, kept before p is refilled
     if constexpr (KDA) {
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
         if constexpr (KDA) S[qq][it] *= egk[qq];
         else S[qq][it] *= eg;
         S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Qs, LD), 16 * (w + 4 * qq), colk(dOg, LDO), 16 * it);
-        S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Xs, LD), 16 * (w + 4 * qq), colk(dRt, LDO), 16 * it);
+        if constexpr (!NOX) S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Xs, LD), 16 * (w + 4 * qq), colk(dRt, LDO), 16 * it);
       }
     __syncthreads();
   };
@@ -1036,9 +1044,10 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
                            const gdr_grads& gr, hipStream_t st) {
   const Geo& g = p.geo;
   constexpr bool KDA = VAR == VAR_KDA;
-  const E* qin = KDA ? (const E*)p.Qh : p.qkn ? (const E*)p.Qn : (const E*)in.q;
-  const E* kin = KDA ? (const E*)p.Kb : p.qkn ? (const E*)p.Kn : (const E*)in.k;
-  const float* gin = KDA ? p.Gn : p.G;
+  constexpr bool PCH = KDA || VAR == VAR_GLA;  // decay per key channel: per-unit operands
+  const E* qin = PCH ? (const E*)p.Qh : p.qkn ? (const E*)p.Qn : (const E*)in.q;
+  const E* kin = PCH ? (const E*)p.Kb : p.qkn ? (const E*)p.Kn : (const E*)in.k;
+  const float* gin = PCH ? p.Gn : p.G;
   // residual gradient: delta family and Kimi Delta Attention (whose residual has the same form)
   constexpr bool RES_OK = VAR == VAR_DELTANET || VAR == VAR_GATED || KDA;
   const E* drp = RES_OK ? (const E*)dr : nullptr;
@@ -1089,7 +1098,7 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
   if (g.total_chunks > 0) {
     if constexpr (VAR == VAR_GDN2 || VAR == VAR_GDN2L) {
       return launch_bwd_gdn2<E, D>(p, in, dO, gr, st);
-    } else if constexpr (VAR == VAR_KDA) {
+    } else if constexpr (PCH) {
       const hipError_t e = launch_bwd_kda<E, D>(p, in, dO, gr, st);
       if (e != hipSuccess) return e;
     } else {
@@ -1143,6 +1152,7 @@ hipError_t run_backward(const Plan& p, const gdr_inputs& in, const void* dO, con
     case GDR_DELTANET: GDR_BWD_CASE(VAR_DELTANET)
     case GDR_GATED: GDR_BWD_CASE(VAR_GATED)
     case GDR_KDA: GDR_BWD_CASE(VAR_KDA)
+    case GDR_GLA: GDR_BWD_CASE(VAR_GLA)
     case GDR_GDN2:
       if (p.gates) { GDR_BWD_CASE(VAR_GDN2L) }
       GDR_BWD_CASE(VAR_GDN2)

@@ -6,7 +6,9 @@
 namespace gdr {
 
 // VAR_GDN2L: Gated DeltaNet-2 with its gates (beta, alpha, erase, write) given as logits.
-enum Var { VAR_DELTANET = 0, VAR_GATED = 1, VAR_KDA = 2, VAR_GDN2 = 3, VAR_GDN2L = 4 };
+// VAR_GLA: the erase-free memory with a decay per key channel, W <- W diag(alpha) + beta v k^T:
+// Kimi Delta Attention's chunk form with nothing erased (A = 0, L = I, X = 0, R = U = beta V).
+enum Var { VAR_DELTANET = 0, VAR_GATED = 1, VAR_KDA = 2, VAR_GDN2 = 3, VAR_GDN2L = 4, VAR_GLA = 5 };
 
 // Li = L^{-1} for a unit lower-triangular 64x64 float matrix L (only entries strictly below
 // the diagonal are read).  Blocked:

@@ -3,6 +3,7 @@
 // back once.  Per token, with D_t the decay and v_bar = (W D_t) k the memory's prediction:
 //   Delta family:     W <- W D_t + beta (v - v_bar) k^T
 //   Gated DeltaNet-2: W <- W D_t - v_bar (beta e*k)^T + (beta w*v) k^T
+//   erase-free (GLA): W <- W D_t + beta v k^T   (D_t per key channel, nothing predicted)
 //   o_t = scale * W q_t   (the memory after the token's write)
 // Every value row i of W evolves on its own: v_bar_i needs only row i and k, and the write
 // touches row i only through v_i, w_i and v_bar_i.  So the rows are spread over the lanes with
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q
     float bt = beta ? (float)beta[tk] : 1.f;
     if constexpr (LOG) bt = gate_sigmoid(bt);
     f32x4 dec = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (VAR == VAR_KDA) {
+    if constexpr (VAR == VAR_KDA || VAR == VAR_GLA) {
       dec = load4(alpha + tk * D + j0);
       if constexpr (LOG) {
 #pragma unroll
@@ -103,13 +104,17 @@ __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
       const f32x4 Wd = W[r] * dec;
-      const float vbar = row_sum<LPR>(dot4(Wd, kt));
       float stored = bt * (float)v[tk * D + row[r]];  // beta v_i, or beta w_i v_i
       if constexpr (VAR == VAR_GDN2) {
         const float wr = (float)write[tk * D + row[r]];
         stored *= LOG ? gate_sigmoid(wr) : wr;
       }
-      W[r] = Wd - vbar * ek + stored * kt;
+      if constexpr (VAR == VAR_GLA) {
+        W[r] = Wd + stored * kt;
+      } else {
+        const float vbar = row_sum<LPR>(dot4(Wd, kt));
+        W[r] = Wd - vbar * ek + stored * kt;
+      }
       const float ov = row_sum<LPR>(dot4(W[r], qt));
       if (j0 == 0) o[tk * D + row[r]] = (E)(geo.scale * ov);
     }
@@ -139,6 +144,7 @@ hipError_t launch_decode_t(const Geo& g, int variant, int gates, const gdr_input
       case GDR_DELTANET: return go(k_decode<E, D, VAR_DELTANET, true>);
       case GDR_GATED: return go(k_decode<E, D, VAR_GATED, true>);
       case GDR_KDA: return go(k_decode<E, D, VAR_KDA, true>);
+      case GDR_GLA: return go(k_decode<E, D, VAR_GLA, true>);
       default: return go(k_decode<E, D, VAR_GDN2, true>);
     }
   }
@@ -146,6 +152,7 @@ hipError_t launch_decode_t(const Geo& g, int variant, int gates, const gdr_input
     case GDR_DELTANET: return go(k_decode<E, D, VAR_DELTANET, false>);
     case GDR_GATED: return go(k_decode<E, D, VAR_GATED, false>);
     case GDR_KDA: return go(k_decode<E, D, VAR_KDA, false>);
+    case GDR_GLA: return go(k_decode<E, D, VAR_GLA, false>);
     default: return go(k_decode<E, D, VAR_GDN2, false>);
   }
 }

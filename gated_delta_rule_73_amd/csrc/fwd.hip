@@ -215,10 +215,11 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2 || VAR == VAR_GDN2L;
   constexpr bool G2L = VAR == VAR_GDN2L;  // its gates are logits
-  constexpr bool KDA = VAR == VAR_KDA;
+  constexpr bool KDA = VAR == VAR_KDA || VAR == VAR_GLA;  // decay per key channel, per-unit operands
+  constexpr bool NOX = VAR == VAR_GLA;  // nothing erased: X = 0, so R = U (no product with W0)
   constexpr bool DEC = VAR == VAR_GATED || G2;  // scalar decay
   constexpr bool OUT_G2 = FULL && G2;
-  __shared__ __align__(16) E Xs[CH * LD];
+  __shared__ __align__(16) E Xs[VAR == VAR_GLA ? 8 : CH * LD];
   __shared__ __align__(16) E Ks[CH * LD];
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];      // a = beta e*k (GDN-2)
   __shared__ __align__(16) E Bd[G2 ? BV * LDR : 8];     // e^{g_n-g} b^T (GDN-2)
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
     if (part <= 0) {
-      p.x.load(Xg + u * CH * D, D, CH);
+      if constexpr (!NOX) p.x.load(Xg + u * CH * D, D, CH);
       p.u.load(Ug + u * CH * D + i0, D, CH);
       if constexpr (KDA) {
 #pragma unroll
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     const long u = (long)(sp.gc0 + c) * geo.H + h;
     const int n = min(CH, sp.len - c * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + c * CH);
-      p.x.store(Xs, LD);
+      if constexpr (!NOX) p.x.store(Xs, LD);
     p.k.store(Ks, LD);
     p.u.store(Us, LDV);
     if constexpr (FULL) {
@@ -393,7 +394,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     if constexpr (DEC) dec = __expf(gn - gs[tl]);
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
-      const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ws, LD), 16 * it, rowk(Xs, LD), 16 * w);
+      f32x4 acc = zero4();
+      if constexpr (!NOX) acc = mma_k<E, D>(zero4(), rowk(Ws, LD), 16 * it, rowk(Xs, LD), 16 * w);
       const int c4 = 16 * it + 4 * lgrp();
       const f32x4 rv = (virt ? zero4() : get4(Us + tl * LDV + c4)) - acc;
       put4(Rn + tl * LDV + c4, rv);
@@ -482,7 +484,7 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
     if constexpr (VAR == VAR_GDN2 || VAR == VAR_GDN2L) {
       const hipError_t e = launch_fwd_prep_gdn2<E, D>(p, in, st);
       if (e != hipSuccess) return e;
-    } else if constexpr (VAR == VAR_KDA) {
+    } else if constexpr (VAR == VAR_KDA || VAR == VAR_GLA) {
       const hipError_t e = launch_fwd_prep_kda<E, D>(p, in, st);
       if (e != hipSuccess) return e;
     } else {
@@ -501,7 +503,7 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
       }
     }
   }
-  constexpr bool KDA = VAR == VAR_KDA;
+  constexpr bool KDA = VAR == VAR_KDA || VAR == VAR_GLA;
   const E* kin = KDA ? (const E*)p.Kb : p.qkn ? (const E*)p.Kn : (const E*)in.k;
   const E* qin = KDA ? (const E*)p.Qh : p.qkn ? (const E*)p.Qn : (const E*)in.q;
   const float* gin = KDA ? p.Gn : p.G;
@@ -516,7 +518,7 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
   auto scan_q = [&](auto full, auto qkn, const ScanSeg& sg, const float* h0, float* htp) {
     constexpr bool F = decltype(full)::value;
     constexpr bool Q = decltype(qkn)::value;
-    constexpr bool RES_OK = F && VAR != VAR_GDN2 && VAR != VAR_GDN2L;  // residual output: full pass, delta family and KDA
+    constexpr bool RES_OK = F && (VAR == VAR_DELTANET || VAR == VAR_GATED || VAR == VAR_KDA);  // residual output
     const int nvm = F ? 1 : 2;
     if (std::is_same<E, float>::value || p.bv == 16) {
       if constexpr (RES_OK) {
@@ -564,6 +566,7 @@ hipError_t run_forward(const Plan& p, const gdr_inputs& in, void* o, void* r, fl
     case GDR_DELTANET: GDR_FWD_CASE(VAR_DELTANET)
     case GDR_GATED: GDR_FWD_CASE(VAR_GATED)
     case GDR_KDA: GDR_FWD_CASE(VAR_KDA)
+    case GDR_GLA: GDR_FWD_CASE(VAR_GLA)
     case GDR_GDN2:
       if (p.gates) { GDR_FWD_CASE(VAR_GDN2L) }
       GDR_FWD_CASE(VAR_GDN2)

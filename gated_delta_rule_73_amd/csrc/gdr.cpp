@@ -90,7 +90,7 @@ void plan_scans(long long memories, int d, int max_chunks, bool f32, Sizes* s) {
 // counts the chunks of 64 tokens over all sequences.
 gdr_status check_shape(const gdr_problem* p, long long* total_chunks_out, int* max_chunks_out) {
   if (!p) return fail(GDR_ERR_INVALID_ARG, "problem is NULL");
-  if (p->variant < GDR_DELTANET || p->variant > GDR_GDN2)
+  if (p->variant < GDR_DELTANET || p->variant > GDR_GLA)
     return fail(GDR_ERR_INVALID_ARG, "variant %d is not a gdr_variant", p->variant);
   if (p->dtype != GDR_F32 && p->dtype != GDR_BF16)
     return fail(GDR_ERR_INVALID_ARG, "dtype %d is not a gdr_dtype", p->dtype);
@@ -159,20 +159,20 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   s.Ub = align_up(U * C * D * s.esz, A);
   s.dHs = align_up(U * D * D * s.esz, A);
   s.dR = align_up(U * C * D * s.esz, A);
-  const bool g2 = p->variant == GDR_GDN2, kda = p->variant == GDR_KDA;
+  const bool g2 = p->variant == GDR_GDN2, kda = p->variant == GDR_KDA, gla = p->variant == GDR_GLA;
   s.M2 = g2 ? align_up(U * C * C * s.esz, A) : 0;
   s.U2 = g2 ? align_up(U * C * D * s.esz, A) : 0;
-  s.Li = align_up(U * C * C * 4, A);
+  s.Li = gla ? 0 : align_up(U * C * C * 4, A);  // nothing erased: L = I, no inverse kept
   // the delta family's backward forms A again from K (see k_bwd_chunk); the others keep it
   s.A1 = (g2 || kda) ? align_up(U * C * C * 4, A) : 0;
   s.A2 = g2 ? align_up(U * C * C * 4, A) : 0;
-  s.Kb = kda ? align_up(U * C * D * s.esz, A) : 0;
-  s.Qh = kda ? align_up(U * C * D * s.esz, A) : 0;
-  s.Gn = kda ? align_up(U * D * 4, A) : 0;
+  s.Kb = (kda || gla) ? align_up(U * C * D * s.esz, A) : 0;
+  s.Qh = (kda || gla) ? align_up(U * C * D * s.esz, A) : 0;
+  s.Gn = (kda || gla) ? align_up(U * D * 4, A) : 0;
   // float32 backward intermediates per unit -- GDN-2: 5 of 64xD, 4 of 64x64, 4x64;
   // KDA: 4 of 64xD, 2 of 64x64, D
   if (g2) s.g2 = align_up(U * (5 * C * D + 4 * C * C + 4 * C) * 4, A);
-  else if (kda) s.g2 = align_up(U * (4 * C * D + 2 * C * C + D) * 4, A);
+  else if (kda || gla) s.g2 = align_up(U * (4 * C * D + 2 * C * C + D) * 4, A);
   else s.g2 = 0;
   plan_scans((long long)s.nstates * p->H, p->dk, max_chunks, p->dtype == GDR_F32, &s);
   const size_t ms = (size_t)std::max(s.lseg ? s.max_seg : 0, s.lseg_b ? s.max_seg_b : 0);
@@ -198,7 +198,7 @@ gdr_status check_inputs(const gdr_problem* p, const gdr_inputs* in) {
   if (p->T == 0) return GDR_OK;  // no token is read: token tensors may be empty (NULL)
   if (!in->q || !in->k || !in->v) return fail(GDR_ERR_INVALID_ARG, "q, k and v are required");
   const bool gdn2 = p->variant == GDR_GDN2;
-  if (!in->beta && !gdn2) return fail(GDR_ERR_INVALID_ARG, "beta is required for this variant");
+  if (!in->beta && !gdn2 && p->variant != GDR_GLA) return fail(GDR_ERR_INVALID_ARG, "beta is required for this variant");
   if ((in->alpha != nullptr) != (p->variant != GDR_DELTANET))
     return fail(GDR_ERR_INVALID_ARG, p->variant == GDR_DELTANET ? "alpha must be NULL for DeltaNet"
                                                                  : "alpha is required for this variant");
@@ -478,7 +478,7 @@ gdr_status check_forward(const gdr_problem* p, const gdr_inputs* in, void* o, vo
   if (!o && p->T > 0) return fail(GDR_ERR_INVALID_ARG, "o is required");
   if ((o && !aligned(o, 16)) || (r && !aligned(r, 16)) || (ht && !aligned(ht, 16)) || (saved && !aligned(saved, 256)))
     return fail(GDR_ERR_INVALID_ARG, "o/r/ht must be 16-byte and saved 256-byte aligned");
-  if (r && p->variant == GDR_GDN2)
+  if (r && (p->variant == GDR_GDN2 || p->variant == GDR_GLA))
     return fail(GDR_ERR_UNSUPPORTED, "the residual output is defined for the delta family and Kimi Delta Attention");
   if (r && p->gates) return fail(GDR_ERR_UNSUPPORTED, "the residual output takes gate values, not logits");
   return GDR_OK;
@@ -589,8 +589,8 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
   if (st != GDR_OK) return st;
   if ((st = check_inputs(p, in)) != GDR_OK) return st;
   if (!g) return fail(GDR_ERR_INVALID_ARG, "grads is NULL");
-  if (dr && p->variant == GDR_GDN2)
-    return fail(GDR_ERR_UNSUPPORTED, "Gated DeltaNet-2 has no residual output, hence no residual gradient");
+  if (dr && (p->variant == GDR_GDN2 || p->variant == GDR_GLA))
+    return fail(GDR_ERR_UNSUPPORTED, "this variant has no residual output, hence no residual gradient");
   if (dr && p->gates) return fail(GDR_ERR_UNSUPPORTED, "the residual gradient takes gate values, not logits");
   if (dr && !aligned(dr, 16)) return fail(GDR_ERR_INVALID_ARG, "dr must be 16-byte aligned");
   if (p->T > 0) {

@@ -13,6 +13,11 @@
 // which keeps the factors in range unless the block's decay is stronger than e^{-60} in some
 // channel -- those (rare) diagonal blocks are summed exactly, one exponential per term.
 //
+// The erase-free memory with the same per-channel decay (GLA form, W <- W diag(alpha) + beta v k^T)
+// is this chunk form with nothing erased: A = 0, L = I, X = 0 and R = U = diag(beta) V.  Its
+// kernels are these with EF = true: the preparation forms only M (no key Gram, no solve), the
+// scans skip X, the state stage skips dX, a short stage replaces the solve side (dV = beta dR,
+// dbeta = sum v dR) and the Gram stage has no dA slot.
 // The forward scan (which also writes the output) is the delta family's (fwd.hip) fed with
 // Kbar = e^{g_n - g} * K and Qhat = e^g * Q from the prep kernel and a per-row decay of the
 // carried memory.  The backward is the reverse scan (bwd.hip) and three chunk stages here.
@@ -82,9 +87,11 @@ __device__ void kda_flags(const float* Gs, int ldg, int* unsafe) {
 // Outputs: Ls[t][s] = lsc_t A_ts below the diagonal, optionally (Af != NULL) Af[t*ldaf + s] = A_ts
 // (zero on and above the diagonal), Mo[t][s] = M_ts (global, zero above the diagonal).
 // qg: Q in global memory (token rows, used only for exact diagonal blocks).  Ends with a barrier.
-template <typename E, int D, int NT, bool WITH_M>
+// WITH_A = false (nothing erased): M only; Ls and Af are not touched.
+template <typename E, int D, int NT, bool WITH_M, bool WITH_A = true>
 __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const float* Gs, const int* unsafe,
                           float* Ls, const float* lsc, float* Af, int ldaf, E* Mo, const E* qg, int n) {
+  static_assert(WITH_A || WITH_M, "at least one Gram");
   constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 4;
   const int w = wave_id();
   for (int I = 0; I < 4; ++I) {
@@ -107,10 +114,10 @@ __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const fl
     __syncthreads();
     // Tiles (row block I, column block J <= I), formed transposed so each lane holds four
     // consecutive columns s of one row t and writes them with one vector store.
-    const int njobs = (WITH_M ? 2 : 1) * (I + 1);
+    const int njobs = (WITH_A && WITH_M ? 2 : 1) * (I + 1);
     for (int job = w; job < njobs; job += NT / 64) {
-      const bool isM = job > I;
-      const int J = isM ? job - I - 1 : job;
+      const bool isM = WITH_A ? job > I : true;
+      const int J = (WITH_A && isM) ? job - I - 1 : job;
       if (J == I && uns) continue;
       const f32x4 acc = mma_k<E, D>(zero4(), rowk(Cl, LD), 16 * J, rowk(isM ? Qr : Kr, LD), ref);
       const int t = ref + lrow(), s0 = 16 * J + 4 * lgrp();
@@ -174,11 +181,13 @@ __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const fl
         a += (float)Ks[t * LD + j] * ks * e;
         if constexpr (WITH_M) m += (t < n ? (float)qg[(long)t * D + j] : 0.f) * ks * e;
       }
-      if (s < t) {
-        Ls[t * LF + s] = lsc[t] * a;
-        if (Af) Af[t * ldaf + s] = a;
-      } else if (Af) {
-        Af[t * ldaf + s] = 0.f;
+      if constexpr (WITH_A) {
+        if (s < t) {
+          Ls[t * LF + s] = lsc[t] * a;
+          if (Af) Af[t * ldaf + s] = a;
+        } else if (Af) {
+          Af[t * ldaf + s] = 0.f;
+        }
       }
       if constexpr (WITH_M) Mo[t * CH + s] = (E)m;
     }
@@ -203,7 +212,8 @@ struct KdaPrepLds {
 };
 
 // LOG: beta and alpha are logits (beta = sigmoid(x), log alpha = -softplus(x) per channel).
-template <typename E, int D, bool LOG>
+// EF: nothing erased (see the top of this file); beta may be NULL (1).
+template <typename E, int D, bool LOG, bool EF>
 __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ v, const E* __restrict__ beta,
                                                       const E* __restrict__ alpha, E* __restrict__ Xo,
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
 
   // beta is loaded before the tiles (raw) and staged after K and Q are: its wait then covers
   // nothing those stores did not need, where loaded after V it would also wait for V.
-  const uint32_t braw = threadIdx.x < CH ? load_gate_raw(beta + tk, n, threadIdx.x) : 0u;
+  const uint32_t braw = threadIdx.x < CH ? load_gate_raw(beta ? beta + tk : nullptr, n, threadIdx.x) : 0u;
   RegTile<E, CH, D, NT> rv, rk, rq, ra;
   ra.load(alpha + tk * D, D, n);
   rk.load(k + tk * D, D, n);
@@ -240,8 +250,10 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   rk.store(Ks, LD);
   rq.store(Qs, LD);
   if (threadIdx.x < CH) {
-    const float b = gate_from_raw<E>(braw);  // 0 past the end
-    bs[threadIdx.x] = (LOG && threadIdx.x < n) ? gate_sigmoid(b) : b;
+    float b = gate_from_raw<E>(braw);  // 0 past the end
+    if (LOG && (int)threadIdx.x < n) b = gate_sigmoid(b);
+    if (EF && !beta) b = (int)threadIdx.x < n ? 1.f : 0.f;
+    bs[threadIdx.x] = b;
   }
   kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG, tot);
   kda_flags<D, NT>(Gs, LDG, unsafe);
@@ -281,6 +293,22 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
   if (threadIdx.x < D) Gno[u * D + threadIdx.x] = __expf(Gs[(CH - 1) * LDG + threadIdx.x]);
   __syncthreads();
   E* Mc = Mo + u * CH * CH;
+  if constexpr (EF) {
+    // M only; nothing erased, so L = I and U = diag(beta) V (rows past the end load as zero)
+    kda_grams<E, D, NT, true, false>(Ks, Qs, Kr, Cl, Gs, unsafe, nullptr, bs, nullptr, CH, Mc, q + tk * D, n);
+    using RV = decltype(rv);
+#pragma unroll
+    for (int it = 0; it < RV::IT; ++it) {
+      if (RV::TOTAL % NT == 0 || threadIdx.x + it * NT < RV::TOTAL) {
+        E* e = reinterpret_cast<E*>(&rv.v[it]);
+        const float b = bs[rv.row(it)];
+#pragma unroll
+        for (int x = 0; x < RV::VE; ++x) e[x] = (E)(b * (float)e[x]);
+      }
+    }
+    rv.store_global(Uo + u * CH * D, D);
+    return;
+  }
   kda_grams<E, D, NT, true>(Ks, Qs, Kr, Cl, Gs, unsafe, Ls, bs, Ao + u * CH * CH, CH, Mc, q + tk * D, n);
 
   // Khat = e^g K in place; V into the Q buffer
@@ -332,7 +360,8 @@ struct KdaStateLds {
   static constexpr int BYTES = 3 * TK + 2 * TH;
 };
 
-template <typename E, int D>
+// EF: nothing erased, no dX (waves 4-7 form only dKbar and dM).
+template <typename E, int D, bool EF>
 __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restrict__ dO, const float* __restrict__ Gn,
                                                        const E* __restrict__ Hs, const E* __restrict__ Rg,
                                                        const E* __restrict__ dHs, const E* __restrict__ dRg, Plan p) {
@@ -354,7 +383,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restr
 
   g2s_rows<E, CH, D, NT>(dOs, LD, dO + tk * D, D, n);
   g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
-  g2s_rows<E, CH, D, NT>(dRs, LD, dRg + u * CH * D, D, CH);
+  if constexpr (!EF) g2s_rows<E, CH, D, NT>(dRs, LD, dRg + u * CH * D, D, CH);
   f32x4 acc1[D / 16], dkb[NQ], mq[2];
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc1[i] = zero4();
@@ -369,8 +398,10 @@ __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restr
     g2s_rows_t<E, KH, D, NT>(dWh, LDR, dHs + u * D * D + (long)ih * KH * D, D, KH);
     __syncthreads();
     const E* Aop = (w < 4 ? dOs : dRs) + ih * KH;
+    if (!EF || w < 4) {
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(Aop, LD), 16 * wm, rowk(Wh, LDR), 16 * nt);
+      for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, KH>(acc1[nt], rowk(Aop, LD), 16 * wm, rowk(Wh, LDR), 16 * nt);
+    }
 #pragma unroll
     for (int qq = 0; qq < NQ; ++qq)
       dkb[qq] = mma_k<E, KH>(dkb[qq], rowk(Rs + ih * KH, LD), 16 * wm, rowk(dWh, LDR), 16 * (wn * NQ + qq));
@@ -392,7 +423,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restr
     for (int r = 0; r < 4; ++r) {
       const int t = acc_row(16 * wm, r), j = acc_col(16 * nt);
       if (w < 4) dqh[t * D + j] = geo.scale * acc1[nt][r];
-      else dx[t * D + j] = -acc1[nt][r];
+      else if (!EF) dx[t * D + j] = -acc1[nt][r];
     }
 #pragma unroll
   for (int qq = 0; qq < NQ; ++qq)
@@ -627,7 +658,8 @@ struct KdaGramLds {
 };
 
 // LOG: alpha holds logits; dalpha is returned w.r.t. them: d log alpha * (-sigmoid(x)).
-template <typename E, int D, bool LOG>
+// EF: nothing erased: no dA slot (held at zero, its products skipped) and no dKhat term.
+template <typename E, int D, bool LOG, bool EF>
 __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ alpha, E* __restrict__ dq,
                                                       E* __restrict__ dk, E* __restrict__ dalpha, Plan p) {
@@ -661,7 +693,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
     ra.load(alpha + tk * D + j0, D, n);
     rk.load(k + tk * D + j0, D, n);
     rq.load(q + tk * D + j0, D, n);
-    rda.load(p.kd_da + u * CH * CH, CH, CH);
+    if constexpr (!EF) rda.load(p.kd_da + u * CH * CH, CH, CH);
     rdm.load(p.kd_dm + u * CH * CH, CH, CH);
     if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
     rk.store(Ks, LDJ);
@@ -671,7 +703,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
       const int t = rda.row(it), s0 = rda.col(it);
 #pragma unroll
       for (int x = 0; x < decltype(rda)::VE; ++x) {
-        dAs[t * LDT + s0 + x] = (E)rda.elem(it, x);
+        dAs[t * LDT + s0 + x] = EF ? (E)0.f : (E)rda.elem(it, x);
         dMs[t * LDT + s0 + x] = (E)rdm.elem(it, x);
       }
     }
@@ -727,7 +759,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
     for (int r = 0; r < 4; ++r) {
       const long o = (long)acc_row(16 * b, r) * D + j0 + acc_col(16 * c);
       lq[c][r] = dqh[o];
-      lk[c][r] = dkh[o];
+      lk[c][r] = EF ? 0.f : dkh[o];
       lb[c][r] = dkb[o];
     }
 #pragma unroll
@@ -827,7 +859,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
 #pragma unroll
     for (int J = 0; J < 3; ++J) {
       if (J < b) {  // lower: u in block b, s in block J
-        const f32x4 pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Ke, LDJ), 16 * c, 16 * J);
+        f32x4 pa = zero4();
+        if constexpr (!EF) pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Ke, LDJ), 16 * c, 16 * J);
         const f32x4 pm = mma16<E>(zero4(), rowk(dMs, LDT), 16 * b, colk(Ke, LDJ), 16 * c, 16 * J);
         const float gref = Gs[16 * (J + 1) * LDF + j];
         float ps = 0.f;
@@ -852,7 +885,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
 #pragma unroll
     for (int I = 1; I < 4; ++I) {
       if (I > b) {  // upper: s in block b, u in block I
-        f32x4 ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * I);
+        f32x4 ua = zero4();
+        if constexpr (!EF) ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * I);
         ua = mma16<E>(ua, colk(dMs, LDT), 16 * b, colk(Qf, LDJ), 16 * c, 16 * I);
         const float gref = Gs[16 * I * LDF + j];
 #pragma unroll
@@ -864,9 +898,12 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
       }
     }
     if (!exact) {  // pairs inside block b, first token of the block as reference
-      const f32x4 pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Krf, LDJ), 16 * c, 16 * b);
+      f32x4 pa = zero4(), ua = zero4();
+      if constexpr (!EF) {
+        pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Krf, LDJ), 16 * c, 16 * b);
+        ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * b);
+      }
       const f32x4 pm = mma16<E>(zero4(), rowk(dMs, LDT), 16 * b, colk(Krf, LDJ), 16 * c, 16 * b);
-      f32x4 ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * b);
       ua = mma16<E>(ua, colk(dMs, LDT), 16 * b, colk(Qf, LDJ), 16 * c, 16 * b);
       const float g0 = Gs[16 * b * LDF + j];
 #pragma unroll
@@ -968,18 +1005,71 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
 }
 
 // ---------------------------------------------------------------------------------------
+// Erase-free backward, stage 2: with R = U = diag(beta) V the solve side reduces to
+//   dv_t = beta_t dR_t,  dbeta_t = v_t . dR_t   (beta absent: dv = dR, no dbeta).
+// One workgroup per (chunk, head); a row of the tile is VPR adjacent lanes.
+// LOG: beta is a logit; dbeta is returned w.r.t. it (times beta (1 - beta)).
+// ---------------------------------------------------------------------------------------
+template <typename E, int D, bool LOG>
+__global__ __launch_bounds__(256) void k_bwd_gla_wv(Geo geo, const E* __restrict__ v, const E* __restrict__ beta,
+                                                    const E* __restrict__ dRg, E* __restrict__ dv,
+                                                    E* __restrict__ dbeta) {
+  constexpr int NT = 256;
+  using RT = RegTile<E, CH, D, NT>;
+  static_assert(RT::VB == 16 && RT::TOTAL % NT == 0, "whole 16-byte rows per lane group");
+  const int gc = blockIdx.x, h = blockIdx.y;
+  const ChunkPos cp = chunk_pos(geo, gc);
+  const long u = (long)gc * geo.H + h;
+  const long tk = tok_index(geo, cp.b, h, cp.t0);
+  const int n = cp.n;
+  RT rv, rd;
+  rv.load(v + tk * D, D, n);
+  rd.load(dRg + u * CH * D, D, CH);
+#pragma unroll
+  for (int it = 0; it < RT::IT; ++it) {
+    const int t = rv.row(it), c = rv.col(it);
+    float b = 1.f;
+    if (beta) {
+      b = (float)beta[tk + min(t, n - 1)];
+      if constexpr (LOG) b = gate_sigmoid(b);
+    }
+    const E* de = reinterpret_cast<const E*>(&rd.v[it]);
+    typename RT::V ov;
+    E* oe = reinterpret_cast<E*>(&ov);
+    float dot = 0.f;
+#pragma unroll
+    for (int x = 0; x < RT::VE; ++x) {
+      const float d = (float)de[x];
+      dot += (float)rv.elem(it, x) * d;
+      oe[x] = (E)(b * d);
+    }
+    if (t < n) *reinterpret_cast<typename RT::V*>(dv + (tk + t) * D + c) = ov;
+    if (dbeta) {
+      dot = group_sum_dpp<RT::VPR>(dot);
+      if (threadIdx.x % RT::VPR == 0 && t < n) dbeta[tk + t] = (E)(LOG ? dot * b * (1.f - b) : dot);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------------------
 template <typename E, int D>
 hipError_t launch_fwd_prep_kda(const Plan& p, const gdr_inputs& in, hipStream_t st) {
-  TraceScope ts_("fwd_prep_kda", st);
+  const bool ef = p.variant == GDR_GLA;
+  TraceScope ts_(ef ? "fwd_prep_gla" : "fwd_prep_kda", st);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo, (const E*)in.q,
                        (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub,
                        (E*)p.M, (E*)p.Kb, (E*)p.Qh, p.Gn, p.Li, p.A1);
   };
-  if (p.gates) go(k_fwd_prep_kda<E, D, true>);
-  else go(k_fwd_prep_kda<E, D, false>);
+  if (ef) {
+    if (p.gates) go(k_fwd_prep_kda<E, D, true, true>);
+    else go(k_fwd_prep_kda<E, D, false, true>);
+  } else {
+    if (p.gates) go(k_fwd_prep_kda<E, D, true, false>);
+    else go(k_fwd_prep_kda<E, D, false, false>);
+  }
   return hipGetLastError();
 }
 template hipError_t launch_fwd_prep_kda<bf16, 128>(const Plan&, const gdr_inputs&, hipStream_t);
@@ -989,10 +1079,37 @@ template hipError_t launch_fwd_prep_kda<float, 64>(const Plan&, const gdr_inputs
 template <typename E, int D>
 hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, const gdr_grads& gr, hipStream_t st) {
   const dim3 grid(p.geo.total_chunks, p.geo.H);
+  if (p.variant == GDR_GLA) {
+    {
+      TraceScope ts_("bwd_gla_state", st);
+      hipLaunchKernelGGL((k_bwd_kda_state<E, D, true>), grid, dim3(512), 0, st, p.geo, (const E*)dO,
+                         (const float*)p.Gn, (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR, p);
+    }
+    {
+      TraceScope ts_("bwd_gla_wv", st);
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, p.geo, (const E*)in.v, (const E*)in.beta, (const E*)p.dR,
+                           (E*)gr.dv, (E*)gr.dbeta);
+      };
+      if (p.gates) go(k_bwd_gla_wv<E, D, true>);
+      else go(k_bwd_gla_wv<E, D, false>);
+    }
+    {
+      TraceScope ts_("bwd_gla_gram", st);
+      auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(256), 0, st, p.geo,
+                           (const E*)in.q, (const E*)in.k, (const E*)in.alpha, (E*)gr.dq, (E*)gr.dk,
+                           (E*)gr.dalpha, p);
+      };
+      if (p.gates) go(k_bwd_kda_gram<E, D, true, true>);
+      else go(k_bwd_kda_gram<E, D, false, true>);
+    }
+    return hipGetLastError();
+  }
   {
     TraceScope ts_("bwd_kda_state", st);
-    hipLaunchKernelGGL((k_bwd_kda_state<E, D>), grid, dim3(512), 0, st, p.geo, (const E*)dO, (const float*)p.Gn,
-                       (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR, p);
+    hipLaunchKernelGGL((k_bwd_kda_state<E, D, false>), grid, dim3(512), 0, st, p.geo, (const E*)dO,
+                       (const float*)p.Gn, (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR, p);
   }
   {
     TraceScope ts_("bwd_kda_wy", st);
@@ -1009,8 +1126,8 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
       hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(256), 0, st, p.geo, (const E*)in.q,
                          (const E*)in.k, (const E*)in.alpha, (E*)gr.dq, (E*)gr.dk, (E*)gr.dalpha, p);
     };
-    if (p.gates) go(k_bwd_kda_gram<E, D, true>);
-    else go(k_bwd_kda_gram<E, D, false>);
+    if (p.gates) go(k_bwd_kda_gram<E, D, true, false>);
+    else go(k_bwd_kda_gram<E, D, false, false>);
   }
   return hipGetLastError();
 }

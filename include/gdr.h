@@ -13,6 +13,12 @@
  *   Gated DeltaNet-2 W <- alpha W; W <- W - v_bar (beta e*k)^T + (beta w*v) k^T
  *                                    (e: per-key-channel erase gate, w: per-value-channel
  *                                     write gate; beta may be absent, meaning 1)
+ *   erase-free (GLA) W <- W diag(alpha) + beta v k^T  (alpha per key channel, nothing
+ *                                    erased, beta may be absent: the purely additive memory
+ *                                    of the earlier generation of matrix-state models, page
+ *                                    "Resumen Tecnico: Un Analisis Sistematico de la Atencion
+ *                                    Lineal Hibrida", section "Metodologia", list "Modelos
+ *                                    Evaluados", item 2)
  *   output          o_t = scale * W_t q_t   (memory after token t's write)
  *
  * The library computes it in chunkwise-parallel form (chunks of 64 tokens: per-chunk
@@ -57,7 +63,8 @@ typedef enum {
   GDR_DELTANET = 0, /* alpha absent */
   GDR_GATED = 1,    /* alpha [B,H,T] */
   GDR_KDA = 2,      /* alpha [B,H,T,d_k] */
-  GDR_GDN2 = 3      /* alpha [B,H,T]; erase [B,H,T,d_k]; write [B,H,T,d_v]; beta optional */
+  GDR_GDN2 = 3,     /* alpha [B,H,T]; erase [B,H,T,d_k]; write [B,H,T,d_v]; beta optional */
+  GDR_GLA = 4       /* alpha [B,H,T,d_k]; beta optional; no erase/write; no residual output */
 } gdr_variant;
 
 typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
@@ -92,7 +99,7 @@ typedef struct {
 
 typedef struct {
   const void *q, *k, *v;   /* [B,H,T,dk], [B,H,T,dk], [B,H,T,dv]; required */
-  const void *beta;        /* [B,H,T]; required except for GDR_GDN2, where NULL means 1 */
+  const void *beta;        /* [B,H,T]; required except for GDR_GDN2 and GDR_GLA, where NULL means 1 */
   const void *alpha;       /* NULL for GDR_DELTANET, else see gdr_variant; values in (0,1] */
   const void *erase;       /* GDR_GDN2 only: [B,H,T,dk]; NULL otherwise */
   const void *write;       /* GDR_GDN2 only: [B,H,T,dv]; NULL otherwise */

@@ -347,6 +347,21 @@ def test_noalloc_checks(lib):
     big = _problem(B=1, H=16, T=8192)
     assert call(big, _inputs()) == bd.GDR_ERR_WORKSPACE
     assert "scratch" in lib.gdr_last_error().decode()
-    # with a saved buffer only the scan's own buffers live in the scratch: the same problem fits
-    # (the call then goes on to look up the device, which fails here without a GPU)
-    assert call(big, _inputs(), saved=FAKE) != bd.GDR_ERR_WORKSPACE
+
+
+def test_erase_free_variant_checks(lib):
+    """GDR_GLA: alpha per key channel required, beta optional, no erase/write gates, no residual."""
+    p = _problem(variant=4)
+    assert _fwd(lib, p, _inputs(alpha=None)) == bd.GDR_ERR_INVALID_ARG
+    assert _fwd(lib, p, _inputs(erase=FAKE, write=FAKE)) == bd.GDR_ERR_INVALID_ARG
+    r = lib.gdr_forward_residual(ctypes.byref(p), ctypes.byref(_inputs()), FAKE, FAKE, None, None, FAKE, 1 << 40,
+                                 None)
+    assert r == bd.GDR_ERR_UNSUPPORTED
+    assert _fwd(lib, _problem(variant=5), _inputs()) == bd.GDR_ERR_INVALID_ARG
+    # workspace: per chunk and head the scaled copies of K and Q and the channel decays, no L^{-1}
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_saved_size(ctypes.byref(_problem(variant=4, B=1, H=1, T=64)), ctypes.byref(n)) == bd.GDR_OK
+    per = 64 * 128 * 2
+    al = lambda x: (x + 255) // 256 * 256
+    want = per + al(64 * 64 * 2) + 256 + al(128 * 128 * 2) + per + 0 + per + per + al(128 * 4)
+    assert n.value == want
