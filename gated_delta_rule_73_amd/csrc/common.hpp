@@ -598,14 +598,22 @@ __device__ __forceinline__ int seg_count(const ScanSeg& sg, int nchunks) {
   return max(1, (nchunks + sg.lseg - 1) / sg.lseg);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP lane exchanges only (vector adds,
+// no trip through the LDS crossbar): a Hillis-Steele scan inside each row of 16 lanes
+// (row_shr 1, 2, 4, 8; a lane whose source lies before its row adds 0), then the rows' totals
+// carried forward (row_bcast 15 adds row 0's total to row 1 and row 2's to row 3, row_bcast 31
+// adds the total of rows 0-1 to rows 2 and 3).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
+}
 __device__ __forceinline__ float wave_incl_scan(float x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float y = __shfl_up(x, d, 64);
-    if (l >= d) x += y;
-  }
+  x += dpp_or_zero<0x111, 0xF>(x);
+  x += dpp_or_zero<0x112, 0xF>(x);
+  x += dpp_or_zero<0x114, 0xF>(x);
+  x += dpp_or_zero<0x118, 0xF>(x);
+  x += dpp_or_zero<0x142, 0xA>(x);
+  x += dpp_or_zero<0x143, 0xC>(x);
   return x;
 }
 __device__ __forceinline__ float wave_sum(float x) {
