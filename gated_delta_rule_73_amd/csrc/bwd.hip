@@ -522,8 +522,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       const f32x4 kv = get4(Ks + tr * LD + 16 * (wn * NQ + qq) + 4 * lgrp());
       part += kv[0] * dka[qq][0] + kv[1] * dka[qq][1] + kv[2] * dka[qq][2] + kv[3] * dka[qq][3];
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    part = sum_rows4(part);
     if (lgrp() == 0) rkb[w][tr] = part;
   }
 #pragma unroll
@@ -614,8 +613,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       part += kv[0] * kh[0] + kv[1] * kh[1] + kv[2] * kh[2] + kv[3] * kh[3];
       dka[qq] += kh;
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    part = sum_rows4(part);
     if (lgrp() == 0) rkh[w][tr] = part;
   }
   __syncthreads();
@@ -651,12 +649,18 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     store4_n(dTs, LF, 16 * mt, 16 * nt, dl);
   }
   __syncthreads();
-  {  // dbeta from L = I + diag(beta) A: row sums (dL is zero on and above the diagonal)
-    const int t = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
-    float a = 0.f;
-#pragma unroll
-    for (int s = pt; s < CH; s += NT / CH) a += dTs[t * LF + s] * As[t * LF + s];
-    part8b[pt][t] = a;
+  {  // dbeta from L = I + diag(beta) A: row sums (dL is zero on and above the diagonal); eight
+     // adjacent lanes per row, eight consecutive columns each (vector reads), summed with DPP
+    static_assert(NT == 8 * CH, "eight lanes per row");
+    const int t = threadIdx.x >> 3, s0 = (threadIdx.x & 7) * 8;
+    const float4 l0 = *reinterpret_cast<const float4*>(dTs + t * LF + s0);
+    const float4 l1 = *reinterpret_cast<const float4*>(dTs + t * LF + s0 + 4);
+    const float4 a0 = *reinterpret_cast<const float4*>(As + t * LF + s0);
+    const float4 a1 = *reinterpret_cast<const float4*>(As + t * LF + s0 + 4);
+    float a = l0.x * a0.x + l0.y * a0.y + l0.z * a0.z + l0.w * a0.w + l1.x * a1.x + l1.y * a1.y + l1.z * a1.z +
+              l1.w * a1.w;
+    a = group_sum_dpp<8>(a);
+    if ((threadIdx.x & 7) == 0) part8b[0][t] = a;
   }
 
   // ================= phase 3: Gram slots and the decay gradient
@@ -725,8 +729,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       const f32x4 qv = get4(Qs + tr * LD + 16 * nt + 4 * lgrp());
       part += qv[0] * acc1[nt][0] + qv[1] * acc1[nt][1] + qv[2] * acc1[nt][2] + qv[3] * acc1[nt][3];
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    part = sum_rows4(part);
     if (lgrp() == 0) rq[w][tr] = part;
 #pragma unroll
     for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, CH>(acc1[nt], colk(Ks, LD), 16 * nt, rowk(Mts, LDR), 16 * wm);
@@ -766,8 +769,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
         const f32x4 kv = get4(Ks + tr * LD + 16 * (wn * NQ + qq) + 4 * lgrp());
         part += kv[0] * dka[qq][0] + kv[1] * dka[qq][1] + kv[2] * dka[qq][2] + kv[3] * dka[qq][3];
       }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
+      part = sum_rows4(part);
       if (lgrp() == 0) rkn[w * CH + tr] = part;
     }
     __syncthreads();
@@ -778,8 +780,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
         const f32x4 qv = get4(Qs + tr * LD + 16 * nt + 4 * lgrp());
         dot += qv[0] * acc1[nt][0] + qv[1] * acc1[nt][1] + qv[2] * acc1[nt][2] + qv[3] * acc1[nt][3];
       }
-      dot += __shfl_xor(dot, 16, 64);
-      dot += __shfl_xor(dot, 32, 64);
+      dot = sum_rows4(dot);
       const float rn = invq[tr];
 #pragma unroll
       for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = (acc1[nt] - dot * get4(Qs + tr * LD + 16 * nt + 4 * lgrp())) * rn;
@@ -824,9 +825,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
         else dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
       }
     }
-    float db = 0.f;
+    float db = part8b[0][t];
 #pragma unroll
-    for (int i = 0; i < NT / CH; ++i) db += part8c[i][t] + part8b[i][t];
+    for (int i = 0; i < NT / CH; ++i) db += part8c[i][t];
     if constexpr (RES) {
       if (t < n) {
         const float bi = 1.f / (float)beta[tk + t];

@@ -355,6 +355,13 @@ __device__ __forceinline__ float group_sum_dpp(float x) {
   return x;
 }
 
+// x_l + x_{l^16} + x_{l^32} + x_{l^48} in every lane: the sum over the four 16-lane rows of a wave.
+__device__ __forceinline__ float sum_rows4(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
 template <typename S, int ROWS, int COLS, int NT>
 __device__ __forceinline__ void normalize_rows(RegTile<S, ROWS, COLS, NT>& t, float* inv) {
   using RT = RegTile<S, ROWS, COLS, NT>;
@@ -616,10 +623,13 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
   x += dpp_or_zero<0x143, 0xC>(x);
   return x;
 }
+// Sum over the 64 lanes of a wave, returned to every lane: DPP row sums, the rows' totals
+// carried into the last row as in wave_incl_scan, then lane 63 read out.
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-  return x;
+  x = group_sum_dpp<16>(x);
+  x += dpp_or_zero<0x142, 0xA>(x);
+  x += dpp_or_zero<0x143, 0xC>(x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 // Sum over the 16 lanes sharing lgrp() (i.e. over a tile's columns).
 __device__ __forceinline__ float sum16(float x) {

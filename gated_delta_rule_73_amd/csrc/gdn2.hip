@@ -330,10 +330,8 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
       pk += kk[0] * xk[0] + kk[1] * xk[1] + kk[2] * xk[2] + kk[3] * xk[3];
       pa += aa[0] * xa[0] + aa[1] * xa[1] + aa[2] * xa[2] + aa[3] * xa[3];
     }
-    pk += __shfl_xor(pk, 16, 64);
-    pk += __shfl_xor(pk, 32, 64);
-    pa += __shfl_xor(pa, 16, 64);
-    pa += __shfl_xor(pa, 32, 64);
+    pk = sum_rows4(pk);
+    pa = sum_rows4(pa);
     if (lgrp() == 0) {
       rkb[w][tr] = pk;
       rab[w][tr] = pa;
@@ -469,8 +467,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
       const f32x4 kv = get4(Ks + tr * LD + j0);
       part += kv[0] * x[0] + kv[1] * x[1] + kv[2] * x[2] + kv[3] * x[3];
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    part = sum_rows4(part);
     if (lgrp() == 0) rk[w][tr] = part;
   }
   g2s_rows<E, CH, D, NT>(P3, LD, Xg + u * CH * D, D, CH);
@@ -553,8 +550,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
       store4_t(P2, LD, 16 * nt, 16 * w, ov);
       store4_t(P4, LD, 16 * nt, 16 * w, ow);
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    part = sum_rows4(part);
     if (lgrp() == 0) rb[w][tr] = part;
   }
   __syncthreads();
@@ -701,8 +697,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
       const f32x4 qv = get4(Qs + tr * LD + 16 * nt + 4 * lgrp());
       part += qv[0] * aq[nt][0] + qv[1] * aq[nt][1] + qv[2] * aq[nt][2] + qv[3] * aq[nt][3];
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    part = sum_rows4(part);
     if (lgrp() == 0) rq[w][tr] = part;
   }
 #pragma unroll
@@ -729,8 +724,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
       aa[nt] = bt * da * kk;  // now de
       if constexpr (LOG) aa[nt] *= ee * (1.f - ee);  // w.r.t. the erase-gate logit
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
+    part = sum_rows4(part);
     if (lgrp() == 0) re_[w][tr] = part;
   }
   // prefix sums along each row of the pair terms: lanes over columns, rows over the waves
