@@ -411,10 +411,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   // stores: waiting for them then waits for nothing else, where loaded after the tiles they
   // would make the staging wait for every tile in flight (the wait counters are ordered).
   float graw = 0.f;
-  E braw = E(0.f);
+  E braw = E(0.f), araw = E(1.f);  // araw: alpha (or its logit) of this lane's token, for the end
   if (threadIdx.x < CH) {
     graw = Gg[u * CH + threadIdx.x];
     braw = beta[tk + min((int)threadIdx.x, n - 1)];
+    if constexpr (GATED) araw = alpha[tk + min((int)threadIdx.x, n - 1)];
   }
   {
     E* dOs = reinterpret_cast<E*>(smem + Ly::odO);
@@ -501,8 +502,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   const int tr = 16 * wm + lrow();
   float egt = 1.f, egdt = 1.f;
   if constexpr (GATED) {
-    egt = expf(gs[tr]);
-    egdt = expf(gn - gs[tr]);
+    egt = __expf(gs[tr]);
+    egdt = __expf(gn - gs[tr]);
   }
   // dq (first term) stays in acc1 for waves 0-3; dX goes to LDS from waves 4-7
 #pragma unroll
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     const f32x4 b = mma_k<E, D>(zero4(), rowk(dXs, LD), 16 * mt, rowk(Ks, LD), 16 * nt);
     const int s = acc_col(16 * nt);
     float es = 1.f;
-    if constexpr (GATED) es = expf(gs[s]);
+    if constexpr (GATED) es = __expf(gs[s]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = acc_row(16 * mt, r);
@@ -819,10 +820,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       float g4 = 0.f;
 #pragma unroll
       for (int i = 0; i < NT / 64; ++i) g4 += red[i];
-      const float dla = rect + suf + pre + expf(gn) * g4;
+      const float dla = rect + suf + pre + __expf(gn) * g4;
       if (t < n) {
-        if constexpr (LOG) dalpha[tk + t] = (E)(-dla * gate_sigmoid((float)alpha[tk + t]));
-        else dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
+        if constexpr (LOG) dalpha[tk + t] = (E)(-dla * gate_sigmoid((float)araw));
+        else dalpha[tk + t] = (E)(dla / (float)araw);
       }
     }
     float db = part8b[0][t];
@@ -830,7 +831,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     for (int i = 0; i < NT / CH; ++i) db += part8c[i][t];
     if constexpr (RES) {
       if (t < n) {
-        const float bi = 1.f / (float)beta[tk + t];
+        const float bi = 1.f / (float)braw;
         db -= rdr[t] * bi * bi;
       }
     }
