@@ -11,7 +11,8 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgdr.so")
+# GDR_LIBRARY selects another build of the same C ABI (the host-sanitized one for the ABI tests)
+LIB_PATH = os.environ.get("GDR_LIBRARY") or os.path.join(PKG, "libgdr.so")
 
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_WORKSPACE, GDR_ERR_HIP = range(5)
 VARIANTS = {"deltanet": 0, "gated": 1, "kda": 2, "gdn2": 3, "gla": 4}

@@ -59,6 +59,49 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(PKG, "libgdr_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The library with its host code (the C ABI: argument checks, planning, workspace carving)
+    built with AddressSanitizer and UndefinedBehaviorSanitizer, for the ABI tests on a host
+    without a GPU; the kernels' objects are the regular ones.  Load it only in a process started
+    with the ASan runtime preloaded, and never to launch kernels (device code is not instrumented)."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src == "gdr.cpp":
+            obj = os.path.join(BUILD, "gdr_san.o")
+            cmd = [hipcc(), *FLAGS, *SAN_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+            objs.append(obj)
+        else:
+            obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+            objs.append(obj if os.path.exists(obj) else _compile(src))
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang++")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang++"
+    cmd = [clang, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan", "-o", SAN_LIB, *objs,
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
+def asan_runtime() -> str:
+    """Path of the ASan runtime the sanitized library needs preloaded."""
+    clang = "/opt/rocm/llvm/bin/clang++"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -678,7 +678,7 @@ gdr_status gdr_decode(const gdr_problem* p, const gdr_inputs* in, float* state, 
                     "gdr_decode launch");
 }
 
-const char* gdr_status_string(gdr_status s) {
+const char* gdr_status_string(int s) {
   switch (s) {
     case GDR_OK: return "GDR_OK";
     case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG";

@@ -216,7 +216,9 @@ gdr_status gdr_backward_residual(const gdr_problem *p, const gdr_inputs *in, con
  * Errors: INVALID_ARG, UNSUPPORTED (as for gdr_forward), HIP. */
 gdr_status gdr_decode(const gdr_problem *p, const gdr_inputs *in, float *state, void *o, void *stream);
 
-const char *gdr_status_string(gdr_status s);
+/* Name of a status code.  Takes any int, so a code from a newer or foreign caller is safe:
+ * values that are not a gdr_status give "GDR_UNKNOWN_STATUS".  The string is static. */
+const char *gdr_status_string(int s);
 
 /* Per-launch timing, for profiling tools.  After gdr_trace_launches(events, capacity), the
  * next gdr_forward or gdr_backward call made by the same thread records events[2i] on its
