@@ -533,12 +533,15 @@ __device__ __forceinline__ ChunkPos chunk_pos(const Geo& g, int gc) {
     if (hit) {
       const int src = __ffsll((unsigned long long)hit) - 1;
       const int a_s = __shfl(a, src, 64), e_s = __shfl(e, src, 64), f_s = __shfl(first, src, 64);
-      p.seq = base + src;
-      p.t0 = a_s + (gc - f_s) * CH;
-      p.n = min(CH, e_s - p.t0);
+      // every lane holds the same values; readfirstlane tells the compiler so, which keeps the
+      // addresses built from them in scalar registers (a buffer resource in vector registers
+      // would need a loop over lanes around every load)
+      p.seq = __builtin_amdgcn_readfirstlane(base + src);
+      p.t0 = __builtin_amdgcn_readfirstlane(a_s + (gc - f_s) * CH);
+      p.n = min(CH, __builtin_amdgcn_readfirstlane(e_s) - p.t0);
       return p;
     }
-    off += __shfl(incl, 63, 64);
+    off = __builtin_amdgcn_readfirstlane(off + __shfl(incl, 63, 64));
   }
   return p;
 }
@@ -560,7 +563,7 @@ __device__ __forceinline__ SeqPos seq_pos(const Geo& g, int s) {
   p.b = 0;
   p.bos = g.cu[s];
   p.len = g.cu[s + 1] - g.cu[s];
-  p.gc0 = off;
+  p.gc0 = __builtin_amdgcn_readfirstlane(off);  // the same in every lane (see chunk_pos)
   p.nchunks = (p.len + CH - 1) / CH;
   return p;
 }
