@@ -21,7 +21,7 @@ enum Var { VAR_DELTANET = 0, VAR_GATED = 1, VAR_KDA = 2, VAR_GDN2 = 3, VAR_GDN2L
 // ends with a block barrier.  Li's entries above the diagonal are set to zero.  ldl, ldi must
 // be multiples of 4 (16-byte rows).
 template <int NT>
-__device__ void solve_unit_lower64(const float* L, int ldl, float* Li, int ldi, float* scratch) {
+__device__ __forceinline__ void solve_unit_lower64(const float* L, int ldl, float* Li, int ldi, float* scratch) {
   static_assert(NT >= 256, "solve needs four waves");
   const int w = wave_id(), l = lane_id();
   if (w < 4 && l < 16) {
