@@ -87,8 +87,11 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   // Gram tiles: jobs 0..9 -> A (strict lower, times beta_t, into Ls), 10..19 -> M (lower).
   // Formed transposed, so each lane holds four consecutive columns s of one row t and writes
   // them with one vector store.
-  for (int job = w; job < 20; job += 4) {
-    const bool isM = job >= 10;
+  // five jobs per wave, unrolled so that one job's operand reads overlap another's products
+#pragma unroll
+  for (int jr = 0; jr < 5; ++jr) {
+    const int job = w + 4 * jr;
+    const bool isM = jr >= 3 || (jr == 2 && w >= 2);  // job >= 10
     int mt, nt;
     tri_tile(isM ? job - 10 : job, mt, nt);
     const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * nt, rowk(isM ? QV : Ks, LD), 16 * mt);
