@@ -549,7 +549,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   pLi.store(Li, LF);  // L^{-1} as the forward computed it
   // A (strictly lower) formed again from K as the forward formed it (the same products of the
   // same operands, so the same values): 16 KiB less to write forward and to read here
-  for (int job = w; job < 10; job += NT / 64) {
+#pragma unroll
+  for (int jr = 0; jr < 2; ++jr) {  // ten tiles: waves 0 and 1 take a second one
+    const int job = w + jr * (NT / 64);
+    if (job >= 10) break;
     int mt, nt;
     tri_tile(job, mt, nt);
     const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * nt, rowk(Ks, LD), 16 * mt);
@@ -564,8 +567,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
     *reinterpret_cast<float4*>(As + t * LF + s0) = make_float4(val[0], val[1], val[2], val[3]);
   }
-  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // tiles above the diagonal
-    const int t = idx >> 4, s0 = (idx & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < CH * CH / 4 / NT; ++i) {  // tiles above the diagonal
+    const int idx = threadIdx.x + i * NT, t = idx >> 4, s0 = (idx & 15) * 4;
     if ((s0 >> 4) > (t >> 4)) *reinterpret_cast<float4*>(As + t * LF + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   E* Lb = reinterpret_cast<E*>(smem + Ly::oLb);
@@ -624,7 +628,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     const int s = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
 #pragma unroll
-    for (int t = pt; t < CH; t += NT / CH) a += dTs[t * LF + s] * Li[t * LF + s];
+    for (int i = 0; i < CH / (NT / CH); ++i) a += dTs[(pt + i * (NT / CH)) * LF + s] * Li[(pt + i * (NT / CH)) * LF + s];
     part8c[pt][s] = a;  // summed when dbeta is written
   }
   __syncthreads();
@@ -743,8 +747,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     dka[qq] = mma_k<E, CH>(dka[qq], colk(Qs, LD), 16 * nt, colk(Mts, LDR), 16 * wm);
   }
   if constexpr (GATED) {  // prefix sums along each row of the pair terms: lanes over columns
-    for (int uu = w; uu < CH; uu += NT / 64) {
-      float* row = Pair + uu * LF;
+#pragma unroll
+    for (int i = 0; i < CH / (NT / 64); ++i) {  // rows w, w + 8, ...: independent, interleaved
+      float* row = Pair + (w + i * (NT / 64)) * LF;
       row[lane_id()] = wave_incl_scan(row[lane_id()]);
     }
   }
@@ -754,7 +759,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     float a = 0.f;
     if (t > 0) {
 #pragma unroll
-      for (int uu = pt; uu < CH; uu += NT / CH) a += (uu >= t) ? Pair[uu * LF + t - 1] : 0.f;
+      for (int i = 0; i < CH / (NT / CH); ++i) {
+        const int uu = pt + i * (NT / CH);
+        a += (uu >= t) ? Pair[uu * LF + t - 1] : 0.f;
+      }
     }
     part8[pt][t] = a;
   }

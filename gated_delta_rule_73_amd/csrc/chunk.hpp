@@ -44,9 +44,11 @@ __device__ __forceinline__ void solve_unit_lower64(const float* L, int ldl, floa
 #pragma unroll
     for (int r = 0; r < 16; ++r) Li[(o + r) * ldi + o + c] = x[r];
   }
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += NT) {
-    const int r = idx >> 6, cc = idx & 63;
-    if ((cc >> 4) > (r >> 4)) Li[r * ldi + cc] = 0.f;
+  static_assert(64 * 16 % NT == 0, "whole 16-byte vectors per thread");
+#pragma unroll
+  for (int i = 0; i < 64 * 16 / NT; ++i) {  // four columns at a time
+    const int idx = threadIdx.x + i * NT, r = idx >> 4, c0 = (idx & 15) * 4;
+    if ((c0 >> 4) > (r >> 4)) *reinterpret_cast<float4*>(Li + r * ldi + c0) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
   if (w < 2) {  // 16x16 merge inside half w: rows 32w+16.., columns 32w..

@@ -116,8 +116,9 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
       *reinterpret_cast<float4*>(Ls + t * LF + s0) = make_float4(bt * val[0], bt * val[1], bt * val[2], bt * val[3]);
     }
   }
-  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // tiles above the diagonal
-    const int t = idx >> 4, s0 = (idx & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < CH * CH / 4 / NT; ++i) {  // tiles above the diagonal
+    const int idx = threadIdx.x + i * NT, t = idx >> 4, s0 = (idx & 15) * 4;
     if ((s0 >> 4) > (t >> 4)) {
       if constexpr (sizeof(E) == 2) {
         *reinterpret_cast<bf16x4*>(Mo + (u * CH + t) * CH + s0) = bf16x4{(E)0.f, (E)0.f, (E)0.f, (E)0.f};
@@ -130,8 +131,9 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   rv.store(QV, LD);
   solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ts));
 
-  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // T = L^{-1} diag(beta), four columns at a time
-    const int t = idx >> 4, s0 = (idx & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < CH * CH / 4 / NT; ++i) {  // T = L^{-1} diag(beta), four columns at a time
+    const int idx = threadIdx.x + i * NT, t = idx >> 4, s0 = (idx & 15) * 4;
     const float4 l = *reinterpret_cast<const float4*>(Li + t * LF + s0);
     const float4 bb = *reinterpret_cast<const float4*>(bs + s0);
     const float lv[4] = {l.x * bb.x, l.y * bb.y, l.z * bb.z, l.w * bb.w};
@@ -144,8 +146,10 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   s2g_full<float, CH, CH, NT>(Lio + u * CH * CH, CH, Li, LF);  // L^{-1} for the backward
   if constexpr (VAR == VAR_GATED) {  // Khat = e^g K in place, 16 bytes at a time
     constexpr int VE = 16 / (int)sizeof(E);
-    for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
-      const int t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
+    static_assert(CH * D / VE % NT == 0, "whole vectors per thread");
+#pragma unroll
+    for (int i = 0; i < CH * D / VE / NT; ++i) {
+      const int idx = threadIdx.x + i * NT, t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
       const float f = __expf(gs[t]);
       uint4 kv = *reinterpret_cast<const uint4*>(Ks + t * LD + j0);
       E* ke = reinterpret_cast<E*>(&kv);
