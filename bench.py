@@ -7,18 +7,23 @@ synthetic inputs already resident in HBM.  The default workload is the long-cont
 DeltaNet case: B=1, H=16, T=32768 packed as four sequences (4096, 8192, 12288, 8192 tokens),
 d_k = d_v = 128, bf16 inputs, float32 initial memory per sequence.
 
-Prints one JSON line.  `value` is tokens/s = B*T / (time of one step).  `roofline` is the
-dominant kernel against MI355X's 8 TB/s: its algorithmic bytes (the operator's own tensors it
-reads or writes, each once; no per-chunk intermediate) over its average launch time, timed with
-HIP events around its launches in every fourth step of the timed region (the last included);
-`io_bytes`/`io_frac` beside it count everything the kernel moves, intermediates included.
+Prints one JSON line.  `value` is tokens/s = B*T / (time of one step), timed with the
+backward's pipelines on (GDR_PIPELINE=1: the reverse scans of the longest sequences, or the
+earlier half of a single long one, overlap the chunk gradients of the rest on side streams;
+results bitwise the single-stream ones); `ms_per_step_single_stream` is the same step with them
+off (--single-stream times the headline that way too).  `roofline` is the dominant kernel
+against MI355X's 8 TB/s: its algorithmic bytes (the operator's own tensors it reads or writes,
+each once; no per-chunk intermediate) over its average launch time, timed with HIP events
+around its launches in every fourth step of a separate single-stream pass (the last included),
+where no launch overlaps another; `io_bytes`/`io_frac` beside it count everything the kernel
+moves, intermediates included.
 `path_roofline` is the whole step against the bytes the operator must move at minimum.
 `sweep` times T = 4k..32k at B*T = 32768 (ratio t(32k)/t(4k) beside the pages' ~1.1x);
 `ms_per_step_flushed` times steps separated by a 512 MiB write that evicts the last-level cache.
 `cpu_baseline` is the float64 oracle, timed on a bounded sample of the same workload over a
 process pool on this host's cores, before the GPU is touched.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME] [--no-sweep]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME] [--no-sweep] [--single-stream]
 """
 from __future__ import annotations
 
@@ -433,7 +438,7 @@ def timed(runner, steps: int, warmup: int, trace: bool = True, trace_every: int 
     for _ in range(warmup):
         runner.step()
     torch.cuda.synchronize()
-    per_call = 16
+    per_call = 64  # launches recorded per call at most (the library names 64)
     evs = make_events(2 * per_call * 2 * steps) if trace else []
     handles = (ctypes.c_void_p * max(1, len(evs)))(*[e.cuda_event for e in evs]) if trace else None
     names = []
@@ -449,7 +454,7 @@ def timed(runner, steps: int, warmup: int, trace: bool = True, trace_every: int 
                                                           ctypes.c_void_p), 2 * per_call)
             call()
             if traced:
-                n = runner.lib.gdr_traced_launches()
+                n = min(runner.lib.gdr_traced_launches(), per_call)  # later launches are not recorded
                 names.append([(off, k, runner.lib.gdr_traced_launch_name(k).decode()) for k in range(n)])
     end.record()
     torch.cuda.synchronize()
@@ -492,6 +497,8 @@ def main():
     ap.add_argument("--residual", action="store_true", help="the forward also writes the residual r = v - v_bar and the backward takes its gradient")
     ap.add_argument("--gate-logits", action="store_true", help="beta and alpha given as logits")
     ap.add_argument("--qk-norm", action="store_true", help="q and k scaled to unit length inside the library")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="time the headline with the backward's pipelines off (GDR_PIPELINE=0)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -520,8 +527,17 @@ def main():
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    print("[bench] timing", file=sys.stderr, flush=True)
-    ms, per_kernel = timed(runner, args.steps, args.warmup)
+    # Per-kernel launch durations (and the roofline) come from a traced pass with the backward's
+    # pipelines off, where no launch overlaps another; the headline step time from an untraced
+    # pass with them on (GDR_PIPELINE=1: side streams overlap the reverse scans with the chunk
+    # gradients of finished sequences or parts), unless --single-stream.
+    pipe = "0" if args.single_stream else "1"
+    print("[bench] timing kernels (single stream, traced)", file=sys.stderr, flush=True)
+    os.environ["GDR_PIPELINE"] = "0"
+    ms_single, per_kernel = timed(runner, args.steps, args.warmup)
+    os.environ["GDR_PIPELINE"] = pipe
+    print(f"[bench] timing (GDR_PIPELINE={pipe})", file=sys.stderr, flush=True)
+    ms, _ = timed(runner, args.steps, args.warmup, trace=False)
     print("[bench] timing with the last-level cache flushed between steps", file=sys.stderr, flush=True)
     ms_flushed = timed_flushed(runner, max(5, args.steps // 2))
     tokens = w.B * w.T
@@ -549,16 +565,19 @@ def main():
     out = {
         "metric": "tokens/s chunked gated-delta-rule fwd+bwd, H=16 d=128, T=4k-32k; % of roofline",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4), "ms_per_step_flushed": round(ms_flushed, 4), "higher_is_better": True,
+        "ms_per_step": round(ms, 4), "ms_per_step_flushed": round(ms_flushed, 4),
+        "ms_per_step_single_stream": round(ms_single, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded; distributions of the workload definition)",
         "config": {"workload": w.name, "variant": w.variant, "B": w.B, "H": w.H, "T": w.T, "d_k": w.dk,
                    "d_v": w.dv, "chunk": w.chunk, "cu_seqlens": list(w.cu_seqlens) if w.cu_seqlens else None,
                    "initial_state": w.h0_std > 0, "residual_output": args.residual,
-                   "gate_logits": args.gate_logits, "qk_norm": args.qk_norm},
+                   "gate_logits": args.gate_logits, "qk_norm": args.qk_norm,
+                   "backward_pipelines": not args.single_stream},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_ms": round(avg_ms, 4), "launches": launches,
+                     "timed_in": "single-stream traced pass",
                      "algorithmic_bytes_per_launch": algo,
                      "io_bytes": io, "io_achieved": round(io_gbs, 1), "io_frac": round(io_gbs / HBM_PEAK_GBS, 4)},
         "path_roofline": {"bound": "hbm", "algorithmic_bytes_per_step": path_bytes, "achieved": round(path_gbs, 1),

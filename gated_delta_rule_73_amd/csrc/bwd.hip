@@ -116,10 +116,11 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   const int w = wave_id();
   const long mem = (long)sq * geo.H + h;
   const long sbase = mem * D;
-  const int seg = blockIdx.y;
+  const int nsg = sg.mode != 0 ? seg_count(sg, sp.nchunks) : 1;
+  const int seg = sg.mode == 3 ? nsg - 1 - sg.part : (int)blockIdx.y;
   int c0 = 0, c1 = sp.nchunks;
   if (sg.mode != 0) {
-    if (seg >= seg_count(sg, sp.nchunks)) return;
+    if (seg < 0 || seg >= nsg) return;  // mode 3: this sequence has no such part
     if (sg.mode == 1 && seg == 0) return;  // walked in reverse, the first segment's map is never applied
     c0 = seg * sg.lseg;
     c1 = min(sp.nchunks, c0 + sg.lseg);
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   const bool snap = sg.mode != 1;  // record dW and dR per chunk
   const float* init = nullptr;      // memory gradient at the end of the covered chunks
   if (sg.mode == 2) init = sg.starts + (mem * sg.max_seg + seg) * D * D;
+  else if (sg.mode == 3) init = seg == nsg - 1 ? (dht ? dht + sbase * D : nullptr) : sg.maps + (mem * sg.max_seg + seg) * D * D;
   else if (sg.mode == 0 && dht) init = dht + sbase * D;
 
   f32x4 S[NJ][NI];  // dW^T tiles
@@ -303,8 +305,9 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     }
     if (c >= c0) step(c, pa);
   }
-  float* out = nullptr;  // dh0, or this segment's map
+  float* out = nullptr;  // dh0, this segment's map, or (mode 3) the next part's start
   if (sg.mode == 1) out = sg.maps + ((mem * sg.max_seg + seg) * 2 + (virt ? 1 : 0)) * D * D;
+  else if (sg.mode == 3 && seg > 0) out = sg.maps + (mem * sg.max_seg + seg - 1) * D * D;
   else if (dh0 && seg == 0) out = dh0 + sbase * D;
   if (out) {
 #pragma unroll
@@ -366,7 +369,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
                                                    const float* __restrict__ Lig,
                                                    E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
                                                    E* __restrict__ dbeta, E* __restrict__ dalpha,
-                                                   const E* __restrict__ drin, const float* __restrict__ Rng) {
+                                                   const E* __restrict__ drin, const float* __restrict__ Rng,
+                                                   int ts_part, int ts_lseg) {
   using Ly = BwdLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDR = Ly::LDR, LF = Ly::LF;
   constexpr int KH = 64, NH = D / KH;  // the memory is read in blocks of 64 value rows
@@ -384,7 +388,17 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   E* dXs = reinterpret_cast<E*>(smem + Ly::odX);
   E* dMs = reinterpret_cast<E*>(smem + Ly::odM);
 
-  const int gc = blockIdx.x, h = blockIdx.y;
+  // ts_lseg > 0: blocks (c, head, sequence) cover the chunks of part ts_part of every sequence,
+  // its segment nseg - 1 - ts_part of ts_lseg chunks (as the reverse scan's mode 3 counts them)
+  int gc = blockIdx.x;
+  if (ts_lseg > 0) {
+    const SeqPos sp = seq_pos(geo, blockIdx.z);
+    const int seg = max(1, (sp.nchunks + ts_lseg - 1) / ts_lseg) - 1 - ts_part;
+    const int c = seg * ts_lseg + (int)blockIdx.x;
+    if (seg < 0 || c >= sp.nchunks) return;
+    gc = sp.gc0 + c;
+  }
+  const int h = blockIdx.y;
   const ChunkPos cp = chunk_pos(geo, gc);
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
@@ -1067,7 +1081,8 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
   // and always for Kimi Delta Attention, whose backward stages take no residual.
   E* dro = (RES_OK && drp && (KDA || std::is_same<E, bf16>::value)) ? (E*)p.Ub : nullptr;
   auto launch = [&](auto kern, int bv, const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult, const E* d) {
-    hipLaunchKernelGGL(kern, dim3(scan_grid(g, nv_mult * D / bv), sg.mode ? sg.max_seg : 1), dim3(256), 0, st, g, sg,
+    const int ny = (sg.mode == 1 || sg.mode == 2) ? sg.max_seg : 1;  // mode 3: one segment per sequence
+    hipLaunchKernelGGL(kern, dim3(scan_grid(g, nv_mult * D / bv), ny), dim3(256), 0, st, g, sg,
                        qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp, (E*)p.dHs, (E*)p.dR, dh0p,
                        (const E*)in.beta, (const E*)in.erase, d, d ? dro : nullptr);
   };
@@ -1092,34 +1107,18 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
     }
     scan_q(std::false_type{}, sg, dhtp, dh0p, nv_mult);
   };
-  if (p.lseg_b == 0) {
-    TraceScope ts_("bwd_scan", st);
-    scan(ScanSeg{0, 0, 1, nullptr, nullptr}, dht, gr.dh0, 1);
-  } else {
-    {
-      TraceScope ts_("bwd_scan_maps", st);
-      scan(ScanSeg{1, p.lseg_b, p.max_seg_b, p.seg_maps, nullptr}, nullptr, nullptr, 2);
-    }
-    const hipError_t e = launch_seg_combine(p, ScanSeg{0, p.lseg_b, p.max_seg_b, p.seg_maps, nullptr}, dht, true, st);
-    if (e != hipSuccess) return e;
-    TraceScope ts_("bwd_scan", st);
-    scan(ScanSeg{2, p.lseg_b, p.max_seg_b, nullptr, p.seg_starts}, nullptr, gr.dh0, 1);
-  }
-  if (g.total_chunks > 0) {
-    if constexpr (VAR == VAR_GDN2 || VAR == VAR_GDN2L) {
-      return launch_bwd_gdn2<E, D>(p, in, dO, gr, st);
-    } else if constexpr (PCH) {
-      const hipError_t e = launch_bwd_kda<E, D>(p, in, dO, gr, st);
-      if (e != hipSuccess) return e;
-    } else {
-      TraceScope ts_("bwd_chunk", st);
-      auto chunk = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, qin, kin,
-                           (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (const E*)dO, (const E*)p.M,
-                           (const float*)p.G, (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR,
-                           p.Li, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta, (E*)gr.dalpha, drp,
-                           (const float*)p.Rn);
-      };
+  // the chunk-parallel gradients of the delta family, over every chunk (grid (chunks, H)) or,
+  // with lseg > 0, over part `part` of every sequence (grid (lseg, H, sequences))
+  auto chunk_grads = [&](hipStream_t cs, int part, int lseg) {
+    const dim3 grid = lseg > 0 ? dim3(lseg, g.H, g.nseq) : dim3(g.total_chunks, g.H);
+    auto chunk = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(512), 0, cs, g, qin, kin,
+                         (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (const E*)dO, (const E*)p.M,
+                         (const float*)p.G, (const E*)p.Hs, (const E*)p.R, (const E*)p.dHs, (const E*)p.dR,
+                         p.Li, (E*)gr.dq, (E*)gr.dk, (E*)gr.dv, (E*)gr.dbeta, (E*)gr.dalpha, drp,
+                         (const float*)p.Rn, part, lseg);
+    };
+    if constexpr (!PCH && VAR != VAR_GDN2 && VAR != VAR_GDN2L) {
       if (p.qkn) {
         if (drp) chunk(k_bwd_chunk<E, D, VAR, true, false, true>);
         else if (p.gates) chunk(k_bwd_chunk<E, D, VAR, false, true, true>);
@@ -1129,6 +1128,62 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
         else if (p.gates) chunk(k_bwd_chunk<E, D, VAR, false, true, false>);
         else chunk(k_bwd_chunk<E, D, VAR, false, false, false>);
       }
+    }
+  };
+  // Time-split backward (delta family, unsegmented reverse scan, a side stream given): the
+  // reverse scan runs part by part (ScanSeg mode 3) on the caller's stream, and each finished
+  // part's chunk gradients run on the side stream while the next part scans, on the CUs the
+  // scan's few value tiles leave idle.  The side stream is joined back into the caller's
+  // stream before anything else is enqueued, also after an error.
+  constexpr bool DELTA = VAR == VAR_DELTANET || VAR == VAR_GATED;
+  const bool tsplit = DELTA && p.ts_lseg > 0 && p.ts_side && p.lseg_b == 0 && g.total_chunks > 0;
+  if (tsplit) {
+    hipError_t e = hipSuccess;
+    bool forked = false;
+    for (int part = 0; part < p.ts_parts && e == hipSuccess; ++part) {
+      {
+        TraceScope ts_("bwd_scan", st);
+        scan(ScanSeg{3, p.ts_lseg, p.ts_parts, p.seg_maps, nullptr, part}, dht, gr.dh0, 1);
+      }
+      if ((e = hipGetLastError()) != hipSuccess) break;
+      if ((e = hipEventRecord(p.ts_fork, st)) != hipSuccess) break;
+      if ((e = hipStreamWaitEvent(p.ts_side, p.ts_fork, 0)) != hipSuccess) break;
+      forked = true;
+      TraceScope ts_("bwd_chunk", p.ts_side);
+      chunk_grads(p.ts_side, part, p.ts_lseg);
+      e = hipGetLastError();
+    }
+    if (forked) {
+      hipError_t j = hipEventRecord(p.ts_join, p.ts_side);
+      if (j == hipSuccess) j = hipStreamWaitEvent(st, p.ts_join, 0);
+      if (j != hipSuccess) {
+        (void)hipStreamSynchronize(p.ts_side);  // the ordering could not be expressed on the stream
+        if (e == hipSuccess) e = j;
+      }
+    }
+    if (e != hipSuccess) return e;
+  } else if (p.lseg_b == 0) {
+    TraceScope ts_("bwd_scan", st);
+    scan(ScanSeg{0, 0, 1, nullptr, nullptr, 0}, dht, gr.dh0, 1);
+  } else {
+    {
+      TraceScope ts_("bwd_scan_maps", st);
+      scan(ScanSeg{1, p.lseg_b, p.max_seg_b, p.seg_maps, nullptr, 0}, nullptr, nullptr, 2);
+    }
+    const hipError_t e = launch_seg_combine(p, ScanSeg{0, p.lseg_b, p.max_seg_b, p.seg_maps, nullptr, 0}, dht, true, st);
+    if (e != hipSuccess) return e;
+    TraceScope ts_("bwd_scan", st);
+    scan(ScanSeg{2, p.lseg_b, p.max_seg_b, nullptr, p.seg_starts, 0}, nullptr, gr.dh0, 1);
+  }
+  if (g.total_chunks > 0) {
+    if constexpr (VAR == VAR_GDN2 || VAR == VAR_GDN2L) {
+      return launch_bwd_gdn2<E, D>(p, in, dO, gr, st);
+    } else if constexpr (PCH) {
+      const hipError_t e = launch_bwd_kda<E, D>(p, in, dO, gr, st);
+      if (e != hipSuccess) return e;
+    } else if (!tsplit) {  // (time-split: done above)
+      TraceScope ts_("bwd_chunk", st);
+      chunk_grads(st, 0, 0);
     }
     if constexpr (RES_OK) {
       if (dro) {

@@ -597,12 +597,19 @@ __device__ __forceinline__ bool scan_block(const Geo& g, int nv, int& seq, int& 
 // in extra "virtual" value tiles, from the identity with the write term removed (giving its
 // linear part); a combine kernel composes the segments' maps in order to find each segment's
 // start memory; mode 2 reruns every segment from that start, writing the per-chunk results.
+// Mode 3 (reverse scan only) runs one segment per sequence, part `part` counted from the end
+// (segment nseg - 1 - part), from the end state that part - 1 left in maps (the final-state
+// gradient for part 0), and leaves its own end state there for part + 1 (dh0 for segment 0):
+// launched part after part, the parts chain into the whole scan, and the chunk kernels of a
+// finished part can run while later parts scan.
 // A sequence has max(1, ceil(chunks / lseg)) segments; mode 0 is the unsegmented scan.
 struct ScanSeg {
-  int mode;             // 0, 1 or 2 as above
+  int mode;             // 0, 1, 2 or 3 as above
   int lseg, max_seg;    // chunks per segment; largest segment count of any sequence
-  float* maps;          // mode 1 output: [memories][max_seg][2][D][D] (additive part, linear part)
+  float* maps;          // mode 1 output: [memories][max_seg][2][D][D] (additive part, linear part);
+                        // mode 3: [memories][max_seg][D][D] state at the start of each segment
   const float* starts;  // mode 2 input: [memories][max_seg][D][D] start memory of each segment
+  int part;             // mode 3: the part run by this launch
 };
 __device__ __forceinline__ int seg_count(const ScanSeg& sg, int nchunks) {
   return max(1, (nchunks + sg.lseg - 1) / sg.lseg);

@@ -547,16 +547,16 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
   };
   if (p.lseg == 0) {
     TraceScope ts_("fwd_scan", st);
-    scan(std::true_type{}, ScanSeg{0, 0, 1, nullptr, nullptr}, in.h0, ht);
+    scan(std::true_type{}, ScanSeg{0, 0, 1, nullptr, nullptr, 0}, in.h0, ht);
   } else {
     {
       TraceScope ts_("fwd_scan_maps", st);
-      scan(std::false_type{}, ScanSeg{1, p.lseg, p.max_seg, p.seg_maps, nullptr}, nullptr, nullptr);
+      scan(std::false_type{}, ScanSeg{1, p.lseg, p.max_seg, p.seg_maps, nullptr, 0}, nullptr, nullptr);
     }
-    const hipError_t e = launch_seg_combine(p, ScanSeg{0, p.lseg, p.max_seg, p.seg_maps, nullptr}, in.h0, false, st);
+    const hipError_t e = launch_seg_combine(p, ScanSeg{0, p.lseg, p.max_seg, p.seg_maps, nullptr, 0}, in.h0, false, st);
     if (e != hipSuccess) return e;
     TraceScope ts_("fwd_scan", st);
-    scan(std::true_type{}, ScanSeg{2, p.lseg, p.max_seg, nullptr, p.seg_starts}, nullptr, ht);
+    scan(std::true_type{}, ScanSeg{2, p.lseg, p.max_seg, nullptr, p.seg_starts, 0}, nullptr, ht);
   }
   return hipGetLastError();
 }

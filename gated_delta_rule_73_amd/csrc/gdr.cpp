@@ -41,6 +41,7 @@ struct Sizes {
   size_t esz = 0;
   int bv = 16, lseg = 0, max_seg = 1;  // scan value tile; forward segmented scans (see plan_scans)
   int lseg_b = 0, max_seg_b = 1;       // backward segmented scans
+  int ts_lseg = 0, ts_parts = 0;       // time-split backward (see ts_length)
   size_t X, M, G, Hs, R, M2, U2, Li, A1, A2, Kb, Qh, Gn, Ub, dHs, dR, g2, seg;
   size_t Qn = 0, Kn = 0, Rn = 0;  // q/k normalisation of the delta family: scaled copies, inverse norms
   size_t qn = 0;  // with qk_norm outside the kernels: the normalised q and k (after the cache)
@@ -71,6 +72,23 @@ int seg_length(long long tiles, long long min_tiles, int max_chunks) {
   const long long want = (512 + tiles - 1) / tiles;
   const int l = (int)std::max<long long>(16, (max_chunks + want - 1) / want);
   return l >= max_chunks ? 0 : l;
+}
+
+// Time-split backward of the delta family (ScanSeg mode 3): when the reverse scan's value tiles
+// leave CUs idle (fewer than 256) and it is not segmented, it runs in two parts, so that the
+// later half's chunk gradients overlap the earlier half's scan (on a side stream; see the
+// backward entry point).  Measured on one MI355X at 16 memories x 512 chunks: 2.09 ms per
+// training step in two parts, 2.14 in four, 2.17 in sixteen, 2.18 unsplit; more parts lose
+// because each part's gradient kernel, one workgroup per CU, holds the CUs the next part's scan
+// waits for.  GDR_TSPLIT_CHUNKS, if set, forces the part length (0: never split); like the other
+// planning variables it changes nothing but speed.
+int ts_length(long long tiles, int max_chunks) {
+  if (const char* env = std::getenv("GDR_TSPLIT_CHUNKS")) {
+    const int l = std::atoi(env);
+    return (l <= 0 || l >= max_chunks) ? 0 : l;
+  }
+  if (tiles >= 256 || max_chunks < 64) return 0;
+  return (max_chunks + 1) / 2;
 }
 
 void plan_scans(long long memories, int d, int max_chunks, bool f32, Sizes* s) {
@@ -175,8 +193,14 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   else if (kda || gla) s.g2 = align_up(U * (4 * C * D + 2 * C * C + D) * 4, A);
   else s.g2 = 0;
   plan_scans((long long)s.nstates * p->H, p->dk, max_chunks, p->dtype == GDR_F32, &s);
+  if ((p->variant == GDR_DELTANET || p->variant == GDR_GATED) && s.lseg_b == 0) {
+    s.ts_lseg = ts_length((long long)s.nstates * p->H * (p->dk / s.bv), max_chunks);
+    s.ts_parts = s.ts_lseg ? (max_chunks + s.ts_lseg - 1) / s.ts_lseg : 0;
+  }
+  // segmented scans: two maps and a start per segment; the time-split backward: one state per part
   const size_t ms = (size_t)std::max(s.lseg ? s.max_seg : 0, s.lseg_b ? s.max_seg_b : 0);
-  s.seg = ms ? align_up((size_t)s.nstates * p->H * ms * 3 * D * D * 4, A) : 0;
+  const size_t nst = std::max(3 * ms, (size_t)s.ts_parts);
+  s.seg = nst ? align_up((size_t)s.nstates * p->H * nst * D * D * 4, A) : 0;
   // q/k normalisation: the delta family's preparation kernel normalises the rows it loads and
   // keeps per-chunk copies (and the inverse norms) in the cache for the scans and the backward;
   // Kimi Delta Attention and Gated DeltaNet-2 normalise into workspace copies first
@@ -235,6 +259,8 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
   pl.max_seg = s.max_seg;
   pl.lseg_b = s.lseg_b;
   pl.max_seg_b = s.max_seg_b;
+  pl.ts_lseg = s.ts_lseg;  // used only once a side stream is given (ts_side)
+  pl.ts_parts = s.ts_parts;
   char* c = cache;
   pl.X = c; c += s.X;
   pl.M = c; c += s.M;
@@ -325,7 +351,7 @@ struct TraceCall {
 // forward gains nothing this way: what could fill those CUs is the other ranges' chunk
 // preparation, whose HBM and L2 traffic slows the long scan by as much as it saves.)  Only the
 // delta family with unsegmented scans takes this path (its per-unit buffers are the ones offset
-// here).  GDR_PIPELINE=1 turns it on.
+// here).  GDR_PIPELINE=1 turns it on (see pipeline_mode).
 constexpr int kSide = 3;  // side streams: with the caller's, four hardware queues
 struct Pipes {
   hipStream_t side[kSide] = {};
@@ -335,11 +361,22 @@ struct Pipes {
 std::mutex g_pipe_mu;
 Pipes g_pipes[64];
 
-bool pipeline_wanted(const gdr_problem* p, const Sizes& s) {
+// GDR_PIPELINE: 1 = per-sequence ranges, else the time split (below); 2 = the time split only
+// (for tests of it with packed sequences); unset or other values = neither.
+int pipeline_mode() {
   const char* env = std::getenv("GDR_PIPELINE");
-  if (!env || std::atoi(env) != 1) return false;
-  return p->n_seqs >= 2 && (p->variant == GDR_DELTANET || p->variant == GDR_GATED) && s.lseg == 0 &&
-         s.lseg_b == 0;
+  const int m = env ? std::atoi(env) : 0;
+  return (m == 1 || m == 2) ? m : 0;
+}
+
+bool pipeline_wanted(const gdr_problem* p, const Sizes& s) {
+  return pipeline_mode() == 1 && p->n_seqs >= 2 && (p->variant == GDR_DELTANET || p->variant == GDR_GATED) &&
+         s.lseg == 0 && s.lseg_b == 0;
+}
+
+// The time-split backward (see ts_length) where the per-sequence ranges do not apply.
+bool tsplit_wanted(const gdr_problem* p, const Sizes& s) {
+  return pipeline_mode() != 0 && s.ts_lseg > 0 && !pipeline_wanted(p, s);
 }
 
 // Streams and events of the calling thread's current device, created on first use and kept
@@ -632,6 +669,16 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
     if (!saved) {
       st = hip_status(gdr::run_forward(pl, ins, nullptr, nullptr, nullptr, false, hs), "gdr_backward recompute launch");
       if (st != GDR_OK) return st;
+    }
+    // the side stream and its events are shared by every call on this device: held while used
+    std::unique_lock<std::mutex> lock;
+    if (tsplit_wanted(p, s)) {
+      lock = std::unique_lock<std::mutex>(g_pipe_mu);
+      if (Pipes* pp = pipes_for(hs)) {
+        pl.ts_side = pp->side[0];
+        pl.ts_fork = pp->fork;
+        pl.ts_join = pp->join[0];
+      }
     }
     st = hip_status(gdr::run_backward(pl, ins, dO, dr, dht, *g, hs), "gdr_backward launch");
   }

@@ -18,6 +18,12 @@ struct Plan {
                       //    keeps the scaled copies Qn, Kn and 1/||q||, 1/||k|| for the other kernels
   int lseg, max_seg;      // forward segmented scans: chunks per segment (0: off), largest segment count
   int lseg_b, max_seg_b;  // the same for the backward scans
+  // time-split backward (ScanSeg mode 3; delta family): parts of ts_lseg chunks, ts_parts of
+  // them (0: off); the chained states live in seg_maps.  Used only with a side stream, on which
+  // each part's chunk gradients run (ts_fork / ts_join order it against the caller's stream).
+  int ts_lseg, ts_parts;
+  hipStream_t ts_side;
+  hipEvent_t ts_fork, ts_join;
   float* seg_maps;        // [memories][max_seg][2][D][D] float32 (workspace; max_seg of the pass)
   float* seg_starts;      // [memories][max_seg][D][D] float32 (workspace)
   // forward cache (in the caller's saved buffer or in the workspace)

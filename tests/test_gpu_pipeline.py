@@ -84,3 +84,34 @@ def test_pipelined_residual_against_oracle(monkeypatch):
     rep = []
     compare(got, ref, "f32", report=rep)
     print("\n".join(rep))
+
+
+# Time-split backward (ScanSeg mode 3): the reverse scan in parts of GDR_TSPLIT_CHUNKS chunks,
+# each finished part's chunk gradients on a side stream.  Parts of three chunks give several
+# parts with a ragged last one; the carried state crosses parts in float32, so the results are
+# bitwise the single-stream ones.  GDR_PIPELINE=2 takes the time split also for packed
+# sequences (whose part counts then differ, one of them empty).
+TS_CASES = [
+    ("gated", "bf16", 128, 1, 64 * 13 + 21, None, True),
+    ("gated", "bf16", 128, 1, 64 * 10, None, False),
+    ("deltanet", "bf16", 64, 2, 64 * 9 + 5, None, True),
+    ("gated", "f32", 64, 1, 64 * 11, (0, 64 * 3 + 5, 64 * 3 + 5, 64 * 11), True),
+    ("deltanet", "bf16", 128, 1, 64 * 12 + 7, (0, 64 * 8 + 7, 64 * 12 + 7), False),
+]
+
+
+@pytest.mark.parametrize("variant,dtype,d,B,T,cu,use_saved", TS_CASES,
+                         ids=[f"{c[0]}-{c[1]}-{c[2]}-B{c[3]}-T{c[4]}-{'packed' if c[5] else 'dense'}-"
+                              f"{'saved' if c[6] else 'recompute'}" for c in TS_CASES])
+def test_time_split_equals_single_stream(monkeypatch, variant, dtype, d, B, T, cu, use_saved):
+    w = synth.Workload("tsplit", variant, dtype, B, 2, T, d, d, seed=71, h0_std=0.5, cu_seqlens=cu)
+    inp = synth.make_inputs(w, alpha_mode="weak")
+    monkeypatch.delenv("GDR_PIPELINE", raising=False)
+    monkeypatch.delenv("GDR_TSPLIT_CHUNKS", raising=False)
+    ref = _run(inp, variant, dtype, use_saved, 0.9)
+    monkeypatch.setenv("GDR_PIPELINE", "2" if cu else "1")
+    monkeypatch.setenv("GDR_TSPLIT_CHUNKS", "3")
+    got = _run(inp, variant, dtype, use_saved, 0.9)
+    assert set(got) == set(ref)
+    for k in ref:
+        assert np.array_equal(got[k], ref[k], equal_nan=True), k
