@@ -32,12 +32,13 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
                                                   float* __restrict__ Lio, E* __restrict__ Qno, E* __restrict__ Kno,
                                                   float* __restrict__ Rno) {
   constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
-  static_assert(CH * LDT * (int)sizeof(E) >= 4 * 256 * 4, "T buffer doubles as the solve's scratch");
-  __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g * K, then X
-  __shared__ __align__(16) E QV[CH * LD];   // Q, then V, then U
-  __shared__ __align__(16) E Ts[CH * LDT];  // solve scratch, then T = Linv diag(beta)
-  __shared__ __align__(16) float Ls[CH * LF];
-  __shared__ __align__(16) float Li[CH * LF];
+  // Three 64-row buffers (about 52 KiB, so three workgroups share a CU):
+  static_assert(CH * LD * (int)sizeof(E) >= 4 * 256 * 4, "the Q/V buffer doubles as the solve's scratch");
+  static_assert(LDT * (int)sizeof(E) <= LF * 4, "T fits the buffer of L");
+  __shared__ __align__(16) E Ks[CH * LD];     // K, then e^g * K, then X
+  __shared__ __align__(16) E QV[CH * LD];     // Q, then the solve's scratch, then V, then U
+  __shared__ __align__(16) float Ls[CH * LF];  // L, then L^{-1} (solved in place), then T = L^{-1} diag(beta)
+  E* Ts = reinterpret_cast<E*>(Ls);
   __shared__ __align__(16) float gs[CH], bs[CH];
 
   const int gc = blockIdx.x, h = blockIdx.y;
@@ -128,22 +129,33 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
     }
   }
   __syncthreads();
+  solve_unit_lower64<NT>(Ls, LF, Ls, LF, reinterpret_cast<float*>(QV));  // Q is no longer read
   rv.store(QV, LD);
-  solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ts));
 
+  // T = L^{-1} diag(beta), four columns at a time: L^{-1} is read into registers (and written
+  // out for the backward) before T overwrites it in the same buffer
+  constexpr int TI = CH * CH / 4 / NT;
+  float tv[TI][4];
 #pragma unroll
-  for (int i = 0; i < CH * CH / 4 / NT; ++i) {  // T = L^{-1} diag(beta), four columns at a time
+  for (int i = 0; i < TI; ++i) {
     const int idx = threadIdx.x + i * NT, t = idx >> 4, s0 = (idx & 15) * 4;
-    const float4 l = *reinterpret_cast<const float4*>(Li + t * LF + s0);
+    const float4 l = *reinterpret_cast<const float4*>(Ls + t * LF + s0);
+    *reinterpret_cast<float4*>(Lio + u * CH * CH + t * CH + s0) = l;  // L^{-1} for the backward
     const float4 bb = *reinterpret_cast<const float4*>(bs + s0);
     const float lv[4] = {l.x * bb.x, l.y * bb.y, l.z * bb.z, l.w * bb.w};
-    E tv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tv[r] = (E)(s0 + r <= t ? lv[r] : 0.f);
-    if constexpr (sizeof(E) == 2) *reinterpret_cast<bf16x4*>(Ts + t * LDT + s0) = bf16x4{tv[0], tv[1], tv[2], tv[3]};
-    else *reinterpret_cast<float4*>(Ts + t * LDT + s0) = make_float4(tv[0], tv[1], tv[2], tv[3]);
+    for (int r = 0; r < 4; ++r) tv[i][r] = s0 + r <= t ? lv[r] : 0.f;
   }
-  s2g_full<float, CH, CH, NT>(Lio + u * CH * CH, CH, Li, LF);  // L^{-1} for the backward
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int idx = threadIdx.x + i * NT, t = idx >> 4, s0 = (idx & 15) * 4;
+    if constexpr (sizeof(E) == 2) {
+      *reinterpret_cast<bf16x4*>(Ts + t * LDT + s0) = bf16x4{(E)tv[i][0], (E)tv[i][1], (E)tv[i][2], (E)tv[i][3]};
+    } else {
+      *reinterpret_cast<float4*>(Ts + t * LDT + s0) = make_float4(tv[i][0], tv[i][1], tv[i][2], tv[i][3]);
+    }
+  }
   if constexpr (VAR == VAR_GATED) {  // Khat = e^g K in place, 16 bytes at a time
     constexpr int VE = 16 / (int)sizeof(E);
     static_assert(CH * D / VE % NT == 0, "whole vectors per thread");
