@@ -933,7 +933,10 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
     __syncthreads();
     if constexpr (OWN_A) {  // A = strictlower(K K^T) e^{g_t - g_s}, the forward's products
       const int w = wave_id();
-      for (int job = w; job < 10; job += NT / 64) {
+#pragma unroll
+      for (int job_r = 0; job_r < ((10) + (NT / 64) - 1) / (NT / 64); ++job_r) {
+        const int job = w + job_r * (NT / 64);
+        if (job >= 10) break;
         int mt, nt;
         tri_tile(job, mt, nt);
         const f32x4 acc = mma_k<E, D>(zero4(), rowk(Ys, LD), 16 * nt, rowk(Ys, LD), 16 * mt);
@@ -946,7 +949,10 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
         }
         *reinterpret_cast<float4*>(As + t * LF + s0) = make_float4(val[0], val[1], val[2], val[3]);
       }
-      for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {
+#pragma unroll
+      for (int idx_r = 0; idx_r < ((CH * CH / 4) + NT - 1) / NT; ++idx_r) {
+        const int idx = (int)threadIdx.x + idx_r * NT;
+        if (idx >= CH * CH / 4) break;
         const int t = idx >> 4, s0 = (idx & 15) * 4;
         if ((s0 >> 4) > (t >> 4)) *reinterpret_cast<float4*>(As + t * LF + s0) = make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -990,7 +996,8 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
   {  // F from T = Linv diag(beta): column sums, eight threads per column
     const int sc = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
-    for (int t = pt; t < CH; t += NW) a += dTs[t * LF + sc] * Lis[t * LF + sc];
+#pragma unroll
+    for (int t = pt, t_r = 0; t_r < CH / (NW); ++t_r, t += NW) a += dTs[t * LF + sc] * Lis[t * LF + sc];
     colp[pt][sc] = a;
   }
   // Pt = (dT diag(beta)) Linv^T, stored transposed

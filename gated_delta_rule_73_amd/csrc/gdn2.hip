@@ -94,7 +94,10 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
     if constexpr (sizeof(E) == 2) *reinterpret_cast<bf16x4*>(dst) = bf16x4{(E)v[0], (E)v[1], (E)v[2], (E)v[3]};
     else *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
   };
-  for (int job = w; job < 40; job += 4) {
+#pragma unroll
+  for (int job_r = 0; job_r < ((40) + (4) - 1) / (4); ++job_r) {
+    const int job = w + job_r * (4);
+    if (job >= 40) break;
     const int which = job / 10;
     int mt, nt;
     tri_tile(job % 10, mt, nt);
@@ -120,7 +123,10 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
       put4((which == 2 ? Mqk : Mqa) + (u * CH + t) * CH + s0, val);
     }
   }
-  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // tiles above the diagonal
+#pragma unroll
+  for (int idx_r = 0; idx_r < ((CH * CH / 4) + NT - 1) / NT; ++idx_r) {  // tiles above the diagonal
+    const int idx = (int)threadIdx.x + idx_r * NT;
+    if (idx >= CH * CH / 4) break;
     const int t = idx >> 4, s0 = (idx & 15) * 4;
     if ((s0 >> 4) > (t >> 4)) {
       const float z[4] = {0.f, 0.f, 0.f, 0.f};
@@ -134,7 +140,10 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
   __syncthreads();
   solve_unit_lower64<NT>(Ls, LF, Li, LF, reinterpret_cast<float*>(Ti));
   s2g_full<float, CH, CH, NT>(Lio + u * CH * CH, CH, Li, LF);  // L^{-1} for the backward
-  for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {  // L^{-1} as an operand, four columns at a time
+#pragma unroll
+  for (int idx_r = 0; idx_r < ((CH * CH / 4) + NT - 1) / NT; ++idx_r) {  // L^{-1} as an operand, four columns at a time
+    const int idx = (int)threadIdx.x + idx_r * NT;
+    if (idx >= CH * CH / 4) break;
     const int t = idx >> 4, s0 = (idx & 15) * 4;
     const float4 l = *reinterpret_cast<const float4*>(Li + t * LF + s0);
     const float v[4] = {s0 <= t ? l.x : 0.f, s0 + 1 <= t ? l.y : 0.f, s0 + 2 <= t ? l.z : 0.f, s0 + 3 <= t ? l.w : 0.f};
@@ -146,7 +155,10 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
   for (int nt = 0; nt < D / 16; ++nt) cu[nt] = mma_k<E, CH>(zero4(), colk(Bs, LD), 16 * nt, rowk(Akk, LDT), 16 * w);
   {  // Khat = e^g K in place, 16 bytes at a time
     constexpr int VE = 16 / (int)sizeof(E);
-    for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
+#pragma unroll
+    for (int idx_r = 0; idx_r < ((CH * D / VE) + NT - 1) / NT; ++idx_r) {
+      const int idx = (int)threadIdx.x + idx_r * NT;
+      if (idx >= CH * D / VE) break;
       const int t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
       const float f = __expf(gs[t]);
       uint4 kv = *reinterpret_cast<const uint4*>(Ks + t * LD + j0);
@@ -296,7 +308,10 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
     }
     {  // <W0, dW> over this block, 16 bytes at a time
       constexpr int VE = 16 / (int)sizeof(E);
-      for (int idx = threadIdx.x; idx < KH * D / VE; idx += NT) {
+#pragma unroll
+      for (int idx_r = 0; idx_r < ((KH * D / VE) + NT - 1) / NT; ++idx_r) {
+        const int idx = (int)threadIdx.x + idx_r * NT;
+        if (idx >= KH * D / VE) break;
         const int i = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
         const uint4 a = *reinterpret_cast<const uint4*>(Wh + i * LD + j0);
         const uint4 c = *reinterpret_cast<const uint4*>(dWh + i * LD + j0);
@@ -435,7 +450,10 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   }
   {  // dX' (float32 workspace) and dR' into the union region
     const float* dx = p.g2_dx + u * CH * D;
-    for (int idx = threadIdx.x; idx < CH * D / 4; idx += NT) {
+#pragma unroll
+    for (int idx_r = 0; idx_r < ((CH * D / 4) + NT - 1) / NT; ++idx_r) {
+      const int idx = (int)threadIdx.x + idx_r * NT;
+      if (idx >= CH * D / 4) break;
       const int t = idx / (D / 4), j0 = (idx % (D / 4)) * 4;
       const float4 x = *reinterpret_cast<const float4*>(dx + t * D + j0);
       put4(P1 + t * LD + j0, f32x4{x.x, x.y, x.z, x.w});
@@ -474,7 +492,10 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   g2s_rows<E, CH, D, NT>(P4, LD, U2g + u * CH * D, D, CH);
   __syncthreads();
   float* daak = p.g2_daak + u * CH * CH;
-  for (int id = w; id < 16; id += 4) {
+#pragma unroll
+  for (int id_r = 0; id_r < ((16) + (4) - 1) / (4); ++id_r) {
+    const int id = w + id_r * (4);
+    if (id >= 16) break;
     const int mt = id >> 2, nt = id & 3;
     f32x4 acc = mma_k<E, D>(zero4(), rowk(P4, LD), 16 * nt, rowk(P2, LD), 16 * mt);
     acc = acc - mma_k<E, D>(zero4(), rowk(P3, LD), 16 * nt, rowk(P1, LD), 16 * mt);
@@ -503,7 +524,10 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   }
   __syncthreads();
   float* dakk = p.g2_dakk + u * CH * CH;
-  for (int id = w; id < 16; id += 4) {
+#pragma unroll
+  for (int id_r = 0; id_r < ((16) + (4) - 1) / (4); ++id_r) {
+    const int id = w + id_r * (4);
+    if (id >= 16) break;
     const int mt = id >> 2, nt = id & 3;
     f32x4 acc = mma_k<E, D>(zero4(), rowk(P3, LD), 16 * nt, rowk(P2, LD), 16 * mt);
     const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
@@ -635,7 +659,10 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   __syncthreads();
   {  // a = beta e*k, 16 bytes at a time
     constexpr int VE = 16 / (int)sizeof(E);
-    for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
+#pragma unroll
+    for (int idx_r = 0; idx_r < ((CH * D / VE) + NT - 1) / NT; ++idx_r) {
+      const int idx = (int)threadIdx.x + idx_r * NT;
+      if (idx >= CH * D / VE) break;
       const int t = idx / (D / VE), j0 = (idx % (D / VE)) * VE;
       const uint4 ev = *reinterpret_cast<const uint4*>(Es + t * LD + j0);
       const uint4 kv = *reinterpret_cast<const uint4*>(Ks + t * LD + j0);
@@ -658,7 +685,10 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   }
   {  // decayed gradients of the chunk matrices and the pair terms, four columns at a time
     const long o0 = u * CH * CH;
-    for (int idx = threadIdx.x; idx < CH * CH / 4; idx += NT) {
+#pragma unroll
+    for (int idx_r = 0; idx_r < ((CH * CH / 4) + NT - 1) / NT; ++idx_r) {
+      const int idx = (int)threadIdx.x + idx_r * NT;
+      if (idx >= CH * CH / 4) break;
       const int t = idx >> 4, s0 = (idx & 15) * 4;
       const long o = o0 + t * CH + s0;
       const float4 d1 = *reinterpret_cast<const float4*>(p.g2_dakk + o);
@@ -728,7 +758,10 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
     if (lgrp() == 0) re_[w][tr] = part;
   }
   // prefix sums along each row of the pair terms: lanes over columns, rows over the waves
-  for (int uu = w; uu < CH; uu += NT / 64) {
+#pragma unroll
+  for (int uu_r = 0; uu_r < ((CH) + (NT / 64) - 1) / (NT / 64); ++uu_r) {
+    const int uu = w + uu_r * (NT / 64);
+    if (uu >= CH) break;
     float* row = Pair + uu * LF;
     row[lane_id()] = wave_incl_scan(row[lane_id()]);
   }
