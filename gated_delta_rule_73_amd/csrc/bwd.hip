@@ -752,6 +752,20 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     if (lgrp() == 0) rq[w][tr] = part;
 #pragma unroll
     for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = mma_k<E, CH>(acc1[nt], colk(Ks, LD), 16 * nt, rowk(Mts, LDR), 16 * wm);
+    if constexpr (QKN) {  // dq~ is complete: dq = (dq~ - q~ (q~ . dq~)) / ||q|| at once, this wave
+      // holding every column of rows tr.  Done after the remaining products instead, it kept
+      // acc1 live across them and the D = 128 kernels spilled some 600 registers.
+      float dot = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) {
+        const f32x4 qv = get4(Qs + tr * LD + 16 * nt + 4 * lgrp());
+        dot += qv[0] * acc1[nt][0] + qv[1] * acc1[nt][1] + qv[2] * acc1[nt][2] + qv[3] * acc1[nt][3];
+      }
+      dot = sum_rows4(dot);
+      const float rn = invq[tr];
+#pragma unroll
+      for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = (acc1[nt] - dot * get4(Qs + tr * LD + 16 * nt + 4 * lgrp())) * rn;
+    }
   }
 #pragma unroll
   for (int qq = 0; qq < NQ; ++qq) {
@@ -781,7 +795,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     part8[pt][t] = a;
   }
   __syncthreads();
-  if constexpr (QKN) {  // gradients w.r.t. the raw rows: dx = (dx~ - x~ (x~ . dx~)) / ||x||
+  if constexpr (QKN) {  // dk w.r.t. the raw rows: dk = (dk~ - k~ (k~ . dk~)) / ||k|| (dq was done above)
     // k~ . dk~ per row: a row's columns are split over waves w and w ^ 4; the partial sums go
     // through the pair-term region, no longer read
     float* rkn = reinterpret_cast<float*>(smem + Ly::oPair);
@@ -796,18 +810,6 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       if (lgrp() == 0) rkn[w * CH + tr] = part;
     }
     __syncthreads();
-    if (w < 4) {  // dq: this wave holds every column of rows tr
-      float dot = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) {
-        const f32x4 qv = get4(Qs + tr * LD + 16 * nt + 4 * lgrp());
-        dot += qv[0] * acc1[nt][0] + qv[1] * acc1[nt][1] + qv[2] * acc1[nt][2] + qv[3] * acc1[nt][3];
-      }
-      dot = sum_rows4(dot);
-      const float rn = invq[tr];
-#pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) acc1[nt] = (acc1[nt] - dot * get4(Qs + tr * LD + 16 * nt + 4 * lgrp())) * rn;
-    }
     const float dot = rkn[wm * CH + tr] + rkn[(wm + 4) * CH + tr];
     const float rn = invk[tr];
 #pragma unroll
