@@ -27,6 +27,16 @@ constexpr int CH = 64;  // chunk length (tokens)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// f(std::integral_constant<int, I>{}) for I = A .. B-1 in order: the body sees its index as a
+// compile-time constant, so register arrays it indexes stay in registers.
+template <int A, int B, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (A < B) {
+    f(std::integral_constant<int, A>{});
+    static_for<A + 1, B>(f);
+  }
+}
 __device__ __forceinline__ int lrow() { return threadIdx.x & 15; }
 __device__ __forceinline__ int lgrp() { return (threadIdx.x >> 4) & 3; }
 

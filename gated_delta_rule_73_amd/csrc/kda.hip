@@ -643,6 +643,9 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
 // block use the block's first token as reference for dk and dq (matrix cores) and one lane
 // per channel for their d log alpha terms; a block whose decay is too strong for that
 // reference is summed exactly instead, one exponential per term.
+// Eight waves: waves b and b + 4 share block b, each taking half of its column tiles in the
+// matrix-core part, and in the channel layout half of the in-block pairs (by the later token)
+// and half of the block's tokens for d log alpha.
 // ---------------------------------------------------------------------------------------
 template <typename E>
 struct KdaGramLds {
@@ -650,21 +653,23 @@ struct KdaGramLds {
   static constexpr int GB = CH * LDF * 4, TJ = CH * LDJ * (int)sizeof(E), SQ = CH * LDT * (int)sizeof(E);
   static constexpr int ST = CH * LDF * 4;
   static constexpr int oG = 0, oK = GB, oQ = GB + TJ, oX = GB + 2 * TJ;
-  // region X: dA | dM | Kend (48 rows) | Kf | Qf | Krf, later two float staging arrays
+  // region X: dA | dM | Kend (48 rows) | Kf | Qf | Krf, later two float staging arrays and the
+  // in-block pair sums one half of a block's waves hands to the other
   static constexpr int odA = oX, odM = oX + SQ, oKe = oX + 2 * SQ, oKf = oKe + 48 * LDJ * (int)sizeof(E);
   static constexpr int oQf = oKf + TJ, oKrf = oQf + TJ, endOps = oKrf + TJ;
-  static constexpr int oS1 = oX, oS2 = oX + ST;
-  static constexpr int BYTES = cmax(endOps, oX + 2 * ST);
+  static constexpr int oS1 = oX, oS2 = oX + ST, oN4 = oX + 2 * ST;
+  static constexpr int BYTES = cmax(endOps, oN4 + CH * JW * 4);
 };
 
 // LOG: alpha holds logits; dalpha is returned w.r.t. them: d log alpha * (-sigmoid(x)).
 // EF: nothing erased: no dA slot (held at zero, its products skipped) and no dKhat term.
 template <typename E, int D, bool LOG, bool EF>
-__global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ alpha, E* __restrict__ dq,
                                                       E* __restrict__ dk, E* __restrict__ dalpha, Plan p) {
   using Ly = KdaGramLds<E>;
-  constexpr int NT = 256, JW = Ly::JW, LDJ = Ly::LDJ, LDT = Ly::LDT, LDF = Ly::LDF, NC = JW / 16;
+  constexpr int NT = 512, JW = Ly::JW, LDJ = Ly::LDJ, LDT = Ly::LDT, LDF = Ly::LDF, NC = JW / 16;
+  constexpr int NCW = NC / 2;  // column tiles per wave
   __shared__ __align__(16) char smem[Ly::BYTES];
   __shared__ float c1s[3][JW], tota[4][JW], totc[4][JW], tot[4 * JW];
   __shared__ int unsafe[4];
@@ -679,13 +684,15 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
   E* Krf = reinterpret_cast<E*>(smem + Ly::oKrf);
   float* S1 = reinterpret_cast<float*>(smem + Ly::oS1);
   float* S2 = reinterpret_cast<float*>(smem + Ly::oS2);
+  float* N4 = reinterpret_cast<float*>(smem + Ly::oN4);
 
   const int gc = blockIdx.x, h = blockIdx.y, j0 = blockIdx.z * JW;
   const ChunkPos cp = chunk_pos(geo, gc);
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id(), l = lane_id(), n = cp.n;
-  const int b = w;  // this wave's 16-token block
+  const int b = w & 3;   // this wave's 16-token block
+  const int hf = w >> 2; // this wave's half of the block's work
 
   {
     RegTile<E, CH, JW, NT> rk, rq, ra;
@@ -752,19 +759,19 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
   const float* dqh = p.kd_dqh + u * CH * D;
   const float* dkh = p.kd_dkh + u * CH * D;
   const float* dkb = p.kd_dkb + u * CH * D;
-  float lq[NC][4], lk[NC][4], lb[NC][4], la[16];
+  float lq[NCW][4], lk[NCW][4], lb[NCW][4], la[8];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+  for (int cc = 0; cc < NCW; ++cc)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const long o = (long)acc_row(16 * b, r) * D + j0 + acc_col(16 * c);
-      lq[c][r] = dqh[o];
-      lk[c][r] = EF ? 0.f : dkh[o];
-      lb[c][r] = dkb[o];
+      const long o = (long)acc_row(16 * b, r) * D + j0 + acc_col(16 * (hf * NCW + cc));
+      lq[cc][r] = dqh[o];
+      lk[cc][r] = EF ? 0.f : dkh[o];
+      lb[cc][r] = dkb[o];
     }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = min(16 * b + i, n - 1);
+  for (int i = 0; i < 8; ++i) {  // this half's tokens of the block
+    const int t = min(16 * b + 8 * hf + i, n - 1);
     la[i] = (float)alpha[(tk + t) * D + j0 + l];
   }
   const float gam_l = p.kd_gam[u * D + j0 + l];
@@ -792,8 +799,9 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
         qf[i] = (float)qcol[i * LDJ] * f;
         y[i] = kv * __expf(g0 - gi);
       }
-#pragma unroll
-      for (int uu = 1; uu < 16; ++uu) {
+      // later tokens uu = 1..10 in the first half, 11..15 in the second (55 and 65 pairs)
+      const auto later = [&](auto uu_c) {
+        constexpr int uu = decltype(uu_c)::value;
         float run = 0.f;
 #pragma unroll
         for (int s = 0; s < uu; ++s) {
@@ -801,8 +809,13 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
           run = fmaf(c, y[s], run);
           n4[s + 1] += run;
         }
+      };
+      if (hf == 0) {
+        static_for<1, 11>(later);
+      } else {
+        static_for<11, 16>(later);
       }
-    } else {
+    } else if (hf == 0) {
       // exact: one exponential per pair; also the pairs' dk and dq
       float kk[16], gg[16];
 #pragma unroll
@@ -839,14 +852,16 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
     }
   }
 
-  // ---- matrix-core part (wave b owns the output rows of block b).  Accumulated per element:
+  // ---- matrix-core part (waves b and b + 4 own the output rows of block b, half of the column
+  // tiles each).  Accumulated per element:
   // dkacc, dqacc: every dk / dq term from these products;  y2 = k * (dk lower, other blocks)
   // + q * (dq, other blocks): block-suffix terms;  x3 = k * (dk upper, other blocks): block-prefix terms.
-  f32x4 dkacc[NC], dqacc[NC], y2[NC], x3[NC];
+  f32x4 dkacc[NCW], dqacc[NCW], y2[NCW], x3[NCW];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) dkacc[c] = dqacc[c] = y2[c] = x3[c] = zero4();
+  for (int cc = 0; cc < NCW; ++cc) dkacc[cc] = dqacc[cc] = y2[cc] = x3[cc] = zero4();
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
+  for (int cc = 0; cc < NCW; ++cc) {
+    const int c = hf * NCW + cc;
     const int j = acc_col(16 * c);
     float kv[4], qv[4], gv[4];
 #pragma unroll
@@ -868,10 +883,10 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
         for (int r = 0; r < 4; ++r) {
           const float f = __expf(gv[r] - gref);
           const float a = f * pa[r], m = f * pm[r];
-          dkacc[c][r] += a;
-          dqacc[c][r] += m;
+          dkacc[cc][r] += a;
+          dqacc[cc][r] += m;
           const float pr = kv[r] * a + qv[r] * m;
-          y2[c][r] += pr;
+          y2[cc][r] += pr;
           ps += pr;
         }
         // the pair (b, J)'s total, needed by the blocks strictly between J and b
@@ -892,8 +907,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float x = __expf(gref - gv[r]) * ua[r];
-          dkacc[c][r] += x;
-          x3[c][r] += kv[r] * x;
+          dkacc[cc][r] += x;
+          x3[cc][r] += kv[r] * x;
         }
       }
     }
@@ -909,13 +924,13 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float f = __expf(gv[r] - g0), rf = __expf(g0 - gv[r]);
-        dkacc[c][r] += f * pa[r] + rf * ua[r];
-        dqacc[c][r] += f * pm[r];
+        dkacc[cc][r] += f * pa[r] + rf * ua[r];
+        dqacc[cc][r] += f * pm[r];
       }
     }
   }
   __syncthreads();  // region X becomes the staging area
-  if (exact) {
+  if (exact && hf == 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       S1[(16 * b + i) * LDF + l] = dkd[i];
@@ -925,9 +940,10 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
   __syncthreads();
 
   // ---- dq, dk, and the per-row terms of d log alpha (matrix-core layout)
-  float pa_[NC], pc_[NC];
+  float pa_[NCW], pc_[NCW];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
+  for (int cc = 0; cc < NCW; ++cc) {
+    const int c = hf * NCW + cc;
     const int j = acc_col(16 * c);
     const float gn = Gs[(CH - 1) * LDF + j];
     float sa = 0.f, sc = 0.f;
@@ -936,8 +952,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
       const int uu = acc_row(16 * b, r);
       const float g = Gs[uu * LDF + j], eg = __expf(g), egb = __expf(gn - g);
       const float kv = (float)Ks[uu * LDJ + j], qv = (float)Qs[uu * LDJ + j];
-      const float xq = eg * lq[c][r], xk = eg * lk[c][r], xb = egb * lb[c][r];
-      float dkv = dkacc[c][r] + xk + xb, dqv = dqacc[c][r] + xq;
+      const float xq = eg * lq[cc][r], xk = eg * lk[cc][r], xb = egb * lb[cc][r];
+      float dkv = dkacc[cc][r] + xk + xb, dqv = dqacc[cc][r] + xq;
       if (exact) {
         dkv += S1[uu * LDF + j];
         dqv += S2[uu * LDF + j];
@@ -946,31 +962,35 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
       // are read by this wave only) and go out as whole rows below
       Ks[uu * LDJ + j] = (E)dkv;
       Qs[uu * LDJ + j] = (E)dqv;
-      const float a = qv * xq + kv * xk, cc = kv * xb;
-      y2[c][r] += a;
-      x3[c][r] += cc;
+      const float a = qv * xq + kv * xk, bt = kv * xb;
+      y2[cc][r] += a;
+      x3[cc][r] += bt;
       sa += a;
-      sc += cc;
+      sc += bt;
     }
     sa += __shfl_xor(sa, 16, 64);
     sa += __shfl_xor(sa, 32, 64);
     sc += __shfl_xor(sc, 16, 64);
     sc += __shfl_xor(sc, 32, 64);
-    pa_[c] = sa;
-    pc_[c] = sc;
+    pa_[cc] = sa;
+    pc_[cc] = sc;
   }
   __syncthreads();
   s2g_rows<E, CH, JW, NT>(dk + tk * D + j0, D, Ks, LDJ, n);
   s2g_rows<E, CH, JW, NT>(dq + tk * D + j0, D, Qs, LDJ, n);
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    store4_n(S1, LDF, 16 * b, 16 * c, y2[c]);
-    store4_n(S2, LDF, 16 * b, 16 * c, x3[c]);
+  for (int cc = 0; cc < NCW; ++cc) {
+    const int c = hf * NCW + cc;
+    store4_n(S1, LDF, 16 * b, 16 * c, y2[cc]);
+    store4_n(S2, LDF, 16 * b, 16 * c, x3[cc]);
     if (l < 16) {
-      tota[b][16 * c + l] = pa_[c];
-      totc[b][16 * c + l] = pc_[c];
+      tota[b][16 * c + l] = pa_[cc];
+      totc[b][16 * c + l] = pc_[cc];
     }
   }
+  // the in-block pair sums at the other half's tokens
+#pragma unroll
+  for (int i = 0; i < 8; ++i) N4[(16 * b + 8 * (1 - hf) + i) * JW + l] = hf ? n4[i] : n4[8 + i];
   __syncthreads();
 
   // ---- d log alpha, channel layout
@@ -983,18 +1003,29 @@ __global__ __launch_bounds__(256) void k_bwd_kda_gram(Geo geo, const E* __restri
     }
     if (b == 1) cross += c1s[0][l] + c1s[1][l];
     if (b == 2) cross += c1s[1][l] + c1s[2][l];
-    float suf[16];
+    // this half's tokens t0 .. t0 + 7: suffix sums of S1 from the block's end, prefix sums of S2
+    // from its start, in the same order as over the whole block
+    const int t0 = 16 * b + 8 * hf;
+    float suf[8];
     float run = 0.f;
+    if (hf == 0) {
 #pragma unroll
-    for (int i = 15; i >= 0; --i) {
-      run += S1[(16 * b + i) * LDF + l];
+      for (int i = 15; i >= 8; --i) run += S1[(16 * b + i) * LDF + l];
+    }
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      run += S1[(t0 + i) * LDF + l];
       suf[i] = run;
     }
     run = 0.f;
+    if (hf == 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 16 * b + i;
-      const float dla = n4[i] + suf[i] + run + cross;
+      for (int i = 0; i < 8; ++i) run += S2[(16 * b + i) * LDF + l];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = t0 + i;
+      const float dla = ((hf ? n4[8 + i] : n4[i]) + N4[t * JW + l]) + suf[i] + run + cross;
       run += S2[t * LDF + l];
       if (t < n) {
         if constexpr (LOG) dalpha[(tk + t) * D + j0 + l] = (E)(-dla * gate_sigmoid(la[i]));
@@ -1097,7 +1128,7 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
     {
       TraceScope ts_("bwd_gla_gram", st);
       auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(256), 0, st, p.geo,
+        hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(512), 0, st, p.geo,
                            (const E*)in.q, (const E*)in.k, (const E*)in.alpha, (E*)gr.dq, (E*)gr.dk,
                            (E*)gr.dalpha, p);
       };
@@ -1123,7 +1154,7 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
   {
     TraceScope ts_("bwd_kda_gram", st);
     auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(256), 0, st, p.geo, (const E*)in.q,
+      hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(512), 0, st, p.geo, (const E*)in.q,
                          (const E*)in.k, (const E*)in.alpha, (E*)gr.dq, (E*)gr.dk, (E*)gr.dalpha, p);
     };
     if (p.gates) go(k_bwd_kda_gram<E, D, true, false>);
