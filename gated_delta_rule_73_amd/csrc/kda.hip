@@ -214,14 +214,14 @@ struct KdaPrepLds {
 // LOG: beta and alpha are logits (beta = sigmoid(x), log alpha = -softplus(x) per channel).
 // EF: nothing erased (see the top of this file); beta may be NULL (1).
 template <typename E, int D, bool LOG, bool EF>
-__global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(512) void k_fwd_prep_kda(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ v, const E* __restrict__ beta,
                                                       const E* __restrict__ alpha, E* __restrict__ Xo,
                                                       E* __restrict__ Uo, E* __restrict__ Mo, E* __restrict__ Kbo,
                                                       E* __restrict__ Qho, float* __restrict__ Gno,
                                                       float* __restrict__ Lio, float* __restrict__ Ao) {
   using Ly = KdaPrepLds<E, D>;
-  constexpr int NT = 256, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, LDT = Ly::LDT;
+  constexpr int NT = 512, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, LDT = Ly::LDT;
   __shared__ __align__(16) char smem[Ly::BYTES];
   __shared__ float bs[CH], tot[4 * D];
   __shared__ int unsafe[4];
@@ -331,17 +331,22 @@ __global__ __launch_bounds__(256) void k_fwd_prep_kda(Geo geo, const E* __restri
     Ts[t * LDT + s] = (E)(s <= t ? Li[t * LF + s] * bs[s] : 0.f);
   }
   __syncthreads();
-  f32x4 xa[D / 16], ua[D / 16];
+  // X = T Khat, U = T V: wave w takes row tile w & 3 and half of the column tiles
+  constexpr int NQ = D / 32;
+  const int wr = w & 3, wc = w >> 2;
+  f32x4 xa[NQ], ua[NQ];
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    xa[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Ks, LD), 16 * nt);
-    ua[nt] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * w, colk(Qs, LD), 16 * nt);
+  for (int q = 0; q < NQ; ++q) {
+    const int nt = wc * NQ + q;
+    xa[q] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * wr, colk(Ks, LD), 16 * nt);
+    ua[q] = mma_k<E, CH>(zero4(), rowk(Ts, LDT), 16 * wr, colk(Qs, LD), 16 * nt);
   }
   __syncthreads();
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    store4_n(Ks, LD, 16 * w, 16 * nt, xa[nt]);
-    store4_n(Qs, LD, 16 * w, 16 * nt, ua[nt]);
+  for (int q = 0; q < NQ; ++q) {
+    const int nt = wc * NQ + q;
+    store4_n(Ks, LD, 16 * wr, 16 * nt, xa[q]);
+    store4_n(Qs, LD, 16 * wr, 16 * nt, ua[q]);
   }
   __syncthreads();
   s2g_full<E, CH, D, NT>(Xo + u * CH * D, D, Ks, LD);
@@ -471,15 +476,16 @@ struct KdaWyLds {
 
 // LOG: beta and alpha are logits; dbeta is returned w.r.t. the logit (times beta (1 - beta)).
 template <typename E, int D, bool LOG>
-__global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
+__global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
                                                     const E* __restrict__ beta, const E* __restrict__ alpha,
                                                     const E* __restrict__ dRg, E* __restrict__ dv,
                                                     E* __restrict__ dbeta, Plan p) {
   using Ly = KdaWyLds<E, D>;
-  constexpr int NT = 256, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF;
+  constexpr int NT = 512, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, NW = NT / 64;
   __shared__ __align__(16) char smem[Ly::BYTES];
   __shared__ __align__(16) float bs[CH], tot[4 * D];
-  __shared__ float partc[4][CH], partr[4][CH];
+  constexpr int PS = 4;  // threads per row or column in the beta-gradient sums (the first four waves)
+  __shared__ float partc[PS][CH], partr[PS][CH];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
   float* Ls = reinterpret_cast<float*>(smem + Ly::oL);
@@ -555,8 +561,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   __syncthreads();
   // dT^T tiles (columns s, rows t), four consecutive columns per lane
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
+  for (int e = 0; e < 16 / NW; ++e) {
+    const int id = w + NW * e, mt = id >> 2, nt = id & 3;
     const f32x4 a = mma_k<E, D>(zero4(), rowk(Vs, LD), 16 * nt, rowk(dRs, LD), 16 * mt);
     const f32x4 bb = mma_k<E, D>(zero4(), rowk(Ks, LD), 16 * nt, rowk(dXs, LD), 16 * mt);
     const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
@@ -566,23 +572,27 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
     put4(dTs + t * LF + s0, x);
   }
   const auto Tt = [&]() { if constexpr (Ly::BCOPY) return colk(Tb, LDT); else return TtView{Li, LF, bs}; }();
-  f32x4 dva[D / 16];
-  {  // dV^T and dKhat^T (columns j, rows t)
-    float* dkh = p.kd_dkh + u * CH * D + (16 * w + lrow()) * D + 4 * lgrp();
+  // dV^T and dKhat^T (columns j, rows t): wave w takes row tile w & 3 and half of the column tiles
+  constexpr int NQ = D / 32;
+  const int wr = w & 3, wc = w >> 2;
+  f32x4 dva[NQ];
+  {
+    float* dkh = p.kd_dkh + u * CH * D + (16 * wr + lrow()) * D + 4 * lgrp();
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
-      dva[nt] = mma_k<E, CH>(zero4(), colk(dRs, LD), 16 * nt, Tt, 16 * w);
-      put4(dkh + 16 * nt, mma_k<E, CH>(zero4(), colk(dXs, LD), 16 * nt, Tt, 16 * w));
+    for (int q = 0; q < NQ; ++q) {
+      const int nt = wc * NQ + q;
+      dva[q] = mma_k<E, CH>(zero4(), colk(dRs, LD), 16 * nt, Tt, 16 * wr);
+      put4(dkh + 16 * nt, mma_k<E, CH>(zero4(), colk(dXs, LD), 16 * nt, Tt, 16 * wr));
     }
   }
   __syncthreads();
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) store4_t(Vs, LD, 16 * nt, 16 * w, dva[nt]);
-  {  // dbeta from T = Linv diag(beta): column sums, four threads per column
+  for (int q = 0; q < NQ; ++q) store4_t(Vs, LD, 16 * (wc * NQ + q), 16 * wr, dva[q]);
+  if (threadIdx.x < PS * CH) {  // dbeta from T = Linv diag(beta): column sums
     const int s = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
 #pragma unroll
-    for (int t = pt; t < CH; t += NT / CH) a += dTs[t * LF + s] * Li[t * LF + s];
+    for (int t = pt; t < CH; t += PS) a += dTs[t * LF + s] * Li[t * LF + s];
     partc[pt][s] = a;
   }
   __syncthreads();
@@ -590,8 +600,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   // the gradient w.r.t. Linv is dT diag(beta): Pt = (dT diag(beta)) Linv^T
   float* Pt = Ls;  // L is no longer needed
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
+  for (int e = 0; e < 16 / NW; ++e) {
+    const int id = w + NW * e, mt = id >> 2, nt = id & 3;
     const f32x4 acc = mma_k<E, CH>(zero4(), RowKScaled{dTs, LF, bs}, 16 * mt, LiRow, 16 * nt);
     store4_t(Pt, LF, 16 * mt, 16 * nt, acc);
   }
@@ -599,8 +609,8 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
   // dL (strictly lower), transposed: dT is no longer read, so dL overwrites it in place
   float* da = p.kd_da + u * CH * CH;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int id = w + 4 * e, mt = id >> 2, nt = id & 3;
+  for (int e = 0; e < 16 / NW; ++e) {
+    const int id = w + NW * e, mt = id >> 2, nt = id & 3;
     const f32x4 acc = mma_k<E, CH>(zero4(), rowk(Pt, LF), 16 * nt, LiCol, 16 * mt);
     const int t = 16 * mt + lrow(), s0 = 16 * nt + 4 * lgrp();
     f32x4 dl;
@@ -610,11 +620,11 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
     put4(da + t * CH + s0, bs[t] * dl);
   }
   __syncthreads();
-  {  // dbeta from L = I + diag(beta) A: row sums, four threads per row
+  if (threadIdx.x < PS * CH) {  // dbeta from L = I + diag(beta) A: row sums
     const int t = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
 #pragma unroll
-    for (int s = pt; s < CH; s += NT / CH) a += dTs[t * LF + s] * Af[t * LF + s];
+    for (int s = pt; s < CH; s += PS) a += dTs[t * LF + s] * Af[t * LF + s];
     partr[pt][t] = a;
   }
   __syncthreads();
@@ -622,7 +632,7 @@ __global__ __launch_bounds__(256) void k_bwd_kda_wy(Geo geo, const E* __restrict
     const int t = threadIdx.x;
     float db = 0.f;
 #pragma unroll
-    for (int i = 0; i < NT / CH; ++i) db += partc[i][t] + partr[i][t];
+    for (int i = 0; i < PS; ++i) db += partc[i][t] + partr[i][t];
     if constexpr (LOG) db *= bs[t] * (1.f - bs[t]);
     if (t < n) dbeta[tk + t] = (E)db;
   }
@@ -1090,7 +1100,7 @@ hipError_t launch_fwd_prep_kda(const Plan& p, const gdr_inputs& in, hipStream_t 
   const bool ef = p.variant == GDR_GLA;
   TraceScope ts_(ef ? "fwd_prep_gla" : "fwd_prep_kda", st);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo, (const E*)in.q,
+    hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H), dim3(512), 0, st, p.geo, (const E*)in.q,
                        (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub,
                        (E*)p.M, (E*)p.Kb, (E*)p.Qh, p.Gn, p.Li, p.A1);
   };
@@ -1145,7 +1155,7 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
   {
     TraceScope ts_("bwd_kda_wy", st);
     auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, p.geo, (const E*)in.k, (const E*)in.v, (const E*)in.beta,
+      hipLaunchKernelGGL(kern, grid, dim3(512), 0, st, p.geo, (const E*)in.k, (const E*)in.v, (const E*)in.beta,
                          (const E*)in.alpha, (const E*)p.dR, (E*)gr.dv, (E*)gr.dbeta, p);
     };
     if (p.gates) go(k_bwd_kda_wy<E, D, true>);
