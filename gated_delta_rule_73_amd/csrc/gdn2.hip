@@ -17,7 +17,7 @@
 namespace gdr {
 
 template <typename E, int D, bool LOG>
-__global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(512) void k_fwd_prep_gdn2(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                        const E* __restrict__ v, const E* __restrict__ beta,
                                                        const E* __restrict__ alpha, const E* __restrict__ erase,
                                                        const E* __restrict__ write, E* __restrict__ Xo,
@@ -25,7 +25,8 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
                                                        E* __restrict__ Mqk, float* __restrict__ Go,
                                                        float* __restrict__ Lio, float* __restrict__ Akko,
                                                        float* __restrict__ Aako) {
-  constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
+  constexpr int NT = 512, NW = NT / 64, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
+  constexpr int NQ = D / 32;  // column tiles per wave in the 64 x D products
   __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g K, then X'
   __shared__ __align__(16) E Qs[CH * LD];   // Q, then A_kk B, then U''
   __shared__ __align__(16) E As[CH * LD];   // a = beta e*k
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
   const ChunkPos cp = chunk_pos(geo, gc);
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
-  const int w = wave_id();
+  const int w = wave_id(), wr = w & 3, wc = w >> 2;  // 64 x D products: row tile wr, column half wc
   const int n = cp.n;
 
   // The gates are loaded first, as raw values (lanes past the end read 0), and staged after the
@@ -95,8 +96,8 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
     else *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
   };
 #pragma unroll
-  for (int job_r = 0; job_r < ((40) + (4) - 1) / (4); ++job_r) {
-    const int job = w + job_r * (4);
+  for (int job_r = 0; job_r < (40 + NW - 1) / NW; ++job_r) {
+    const int job = w + job_r * NW;
     if (job >= 40) break;
     const int which = job / 10;
     int mt, nt;
@@ -150,9 +151,9 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
     put4(Ti + t * LDT + s0, v);
   }
   // (A_kk B)^T into registers (the Q buffer receives it below)
-  f32x4 cu[D / 16];
+  f32x4 cu[NQ];
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) cu[nt] = mma_k<E, CH>(zero4(), colk(Bs, LD), 16 * nt, rowk(Akk, LDT), 16 * w);
+  for (int q = 0; q < NQ; ++q) cu[q] = mma_k<E, CH>(zero4(), colk(Bs, LD), 16 * (wc * NQ + q), rowk(Akk, LDT), 16 * wr);
   {  // Khat = e^g K in place, 16 bytes at a time
     constexpr int VE = 16 / (int)sizeof(E);
 #pragma unroll
@@ -170,20 +171,22 @@ __global__ __launch_bounds__(256) void k_fwd_prep_gdn2(Geo geo, const E* __restr
   }
   __syncthreads();
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) store4_t(Qs, LD, 16 * nt, 16 * w, cu[nt]);
+  for (int q = 0; q < NQ; ++q) store4_t(Qs, LD, 16 * (wc * NQ + q), 16 * wr, cu[q]);
   __syncthreads();
   // X'^T and U''^T tiles: each lane writes four consecutive columns
-  f32x4 xa[D / 16], ua[D / 16];
+  f32x4 xa[NQ], ua[NQ];
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    xa[nt] = mma_k<E, CH>(zero4(), colk(Ks, LD), 16 * nt, rowk(Ti, LDT), 16 * w);
-    ua[nt] = -mma_k<E, CH>(zero4(), colk(Qs, LD), 16 * nt, rowk(Ti, LDT), 16 * w);
+  for (int q = 0; q < NQ; ++q) {
+    const int nt = wc * NQ + q;
+    xa[q] = mma_k<E, CH>(zero4(), colk(Ks, LD), 16 * nt, rowk(Ti, LDT), 16 * wr);
+    ua[q] = -mma_k<E, CH>(zero4(), colk(Qs, LD), 16 * nt, rowk(Ti, LDT), 16 * wr);
   }
   __syncthreads();
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    store4_t(Ks, LD, 16 * nt, 16 * w, xa[nt]);
-    store4_t(Qs, LD, 16 * nt, 16 * w, ua[nt]);
+  for (int q = 0; q < NQ; ++q) {
+    const int nt = wc * NQ + q;
+    store4_t(Ks, LD, 16 * nt, 16 * wr, xa[q]);
+    store4_t(Qs, LD, 16 * nt, 16 * wr, ua[q]);
   }
   __syncthreads();
   s2g_full<E, CH, D, NT>(Xo + u * CH * D, D, Ks, LD);
@@ -398,7 +401,7 @@ struct G2WyLds {
 };
 
 template <typename E, int D, bool LOG>
-__global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
+__global__ __launch_bounds__(512) void k_bwd_gdn2_wy(Geo geo, const E* __restrict__ k, const E* __restrict__ v,
                                                      const E* __restrict__ beta, const E* __restrict__ erase,
                                                      const E* __restrict__ write, const E* __restrict__ dO,
                                                      const float* __restrict__ Gg, const E* __restrict__ Xg,
@@ -406,9 +409,9 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
                                                      const E* __restrict__ dRg, E* __restrict__ dv,
                                                      E* __restrict__ dw, Plan p) {
   using Ly = G2WyLds<E, D>;
-  constexpr int NT = 256, LD = Ly::LD, LDT = Ly::LDT;
+  constexpr int NT = 512, NW = NT / 64, LD = Ly::LD, LDT = Ly::LDT, NQ = D / 32;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ float gs[CH], bs[CH], rk[4][CH], rb[4][CH];
+  __shared__ float gs[CH], bs[CH], rk[NW][CH], rb[NW][CH];  // row sums, one part per wave
   E* Ks = reinterpret_cast<E*>(smem);
   E* LiN = Ks + CH * LD;  // L^{-1}, row-major (read k-major where its transpose is needed)
   E* AkkE = LiN + CH * LDT;
@@ -423,11 +426,11 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   const ChunkPos cp = chunk_pos(geo, gc);
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
-  const int w = wave_id(), n = cp.n;
-  // Products below are formed transposed: lane (lrow, lgrp) of wave w holds row t = 16w + lrow
-  // and four consecutive columns 4 lgrp .. +3 of each 16-column tile, so every global or LDS
-  // access of a result is one vector access.
-  const int tr = 16 * w + lrow();
+  const int w = wave_id(), wr = w & 3, wc = w >> 2, n = cp.n;
+  // Products below are formed transposed: lane (lrow, lgrp) of wave w holds row t = 16 (w & 3)
+  // + lrow and four consecutive columns 4 lgrp .. +3 of each of its 16-column tiles (half of
+  // them: tiles NQ (w >> 2) ..), so every global or LDS access of a result is one vector access.
+  const int tr = 16 * wr + lrow();
 
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
@@ -462,11 +465,12 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   }
   __syncthreads();
   // dKhat^T = dX'^T L^{-1} and dC^T = -dR'^T L^{-1} (columns j, rows t)
-  f32x4 dkh[D / 16], dc[D / 16];
+  f32x4 dkh[NQ], dc[NQ];
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    dkh[nt] = mma_k<E, CH>(zero4(), colk(P1, LD), 16 * nt, colk(LiN, LDT), 16 * w);
-    dc[nt] = -mma_k<E, CH>(zero4(), colk(P2, LD), 16 * nt, colk(LiN, LDT), 16 * w);
+  for (int q = 0; q < NQ; ++q) {
+    const int nt = wc * NQ + q;
+    dkh[q] = mma_k<E, CH>(zero4(), colk(P1, LD), 16 * nt, colk(LiN, LDT), 16 * wr);
+    dc[q] = -mma_k<E, CH>(zero4(), colk(P2, LD), 16 * nt, colk(LiN, LDT), 16 * wr);
   }
   __syncthreads();
   {
@@ -474,11 +478,12 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
     const float et = __expf(gs[tr]);
     float part = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
-      store4_t(P1, LD, 16 * nt, 16 * w, dkh[nt]);
-      store4_t(P2, LD, 16 * nt, 16 * w, dc[nt]);
+    for (int q = 0; q < NQ; ++q) {
+      const int nt = wc * NQ + q;
+      store4_t(P1, LD, 16 * nt, 16 * wr, dkh[q]);
+      store4_t(P2, LD, 16 * nt, 16 * wr, dc[q]);
       const int j0 = 16 * nt + 4 * lgrp();
-      const f32x4 x = et * dkh[nt];
+      const f32x4 x = et * dkh[q];
       float4 d = *reinterpret_cast<const float4*>(dk1 + tr * D + j0);
       d.x += x[0]; d.y += x[1]; d.z += x[2]; d.w += x[3];
       *reinterpret_cast<float4*>(dk1 + tr * D + j0) = d;
@@ -493,8 +498,8 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   __syncthreads();
   float* daak = p.g2_daak + u * CH * CH;
 #pragma unroll
-  for (int id_r = 0; id_r < ((16) + (4) - 1) / (4); ++id_r) {
-    const int id = w + id_r * (4);
+  for (int id_r = 0; id_r < (16 + NW - 1) / NW; ++id_r) {
+    const int id = w + id_r * NW;
     if (id >= 16) break;
     const int mt = id >> 2, nt = id & 3;
     f32x4 acc = mma_k<E, D>(zero4(), rowk(P4, LD), 16 * nt, rowk(P2, LD), 16 * mt);
@@ -525,8 +530,8 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   __syncthreads();
   float* dakk = p.g2_dakk + u * CH * CH;
 #pragma unroll
-  for (int id_r = 0; id_r < ((16) + (4) - 1) / (4); ++id_r) {
-    const int id = w + id_r * (4);
+  for (int id_r = 0; id_r < (16 + NW - 1) / NW; ++id_r) {
+    const int id = w + id_r * NW;
     if (id >= 16) break;
     const int mt = id >> 2, nt = id & 3;
     f32x4 acc = mma_k<E, D>(zero4(), rowk(P3, LD), 16 * nt, rowk(P2, LD), 16 * mt);
@@ -536,18 +541,19 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
     put4(dakk + t * CH + s0, acc);
   }
   // dB^T = dB_state^T + dC^T A_kk + (scale dO)^T M_qk
-  f32x4 dbt[D / 16];
+  f32x4 dbt[NQ];
   const float* db1 = p.g2_db + u * CH * D;
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    f32x4 a = mma_k<E, CH>(zero4(), colk(P2, LD), 16 * nt, colk(AkkE, LDT), 16 * w);
-    const f32x4 bq = mma_k<E, CH>(zero4(), colk(P4, LD), 16 * nt, colk(Mqk, LDT), 16 * w);
+  for (int q = 0; q < NQ; ++q) {
+    const int nt = wc * NQ + q;
+    f32x4 a = mma_k<E, CH>(zero4(), colk(P2, LD), 16 * nt, colk(AkkE, LDT), 16 * wr);
+    const f32x4 bq = mma_k<E, CH>(zero4(), colk(P4, LD), 16 * nt, colk(Mqk, LDT), 16 * wr);
     const float4 d = *reinterpret_cast<const float4*>(db1 + tr * D + 16 * nt + 4 * lgrp());
     a[0] += geo.scale * bq[0] + d.x;
     a[1] += geo.scale * bq[1] + d.y;
     a[2] += geo.scale * bq[2] + d.z;
     a[3] += geo.scale * bq[3] + d.w;
-    dbt[nt] = a;
+    dbt[q] = a;
   }
   __syncthreads();
   {  // v and w into P1 / P3 for the gate products; outputs staged through P2 / P4
@@ -559,7 +565,8 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
     const float bt = bs[tr];
     float part = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
+    for (int q = 0; q < NQ; ++q) {
+      const int nt = wc * NQ + q;
       const int i0 = 16 * nt + 4 * lgrp();
       const f32x4 vv = get4(P1 + tr * LD + i0);
       f32x4 ww = get4(P3 + tr * LD + i0);
@@ -567,12 +574,12 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
 #pragma unroll
         for (int x = 0; x < 4; ++x) ww[x] = gate_sigmoid(ww[x]);
       }
-      const f32x4 ov = bt * ww * dbt[nt];
-      f32x4 ow = bt * vv * dbt[nt];
+      const f32x4 ov = bt * ww * dbt[q];
+      f32x4 ow = bt * vv * dbt[q];
       if constexpr (LOG) ow *= ww * (1.f - ww);  // gradient w.r.t. the write-gate logit
-      part += ww[0] * vv[0] * dbt[nt][0] + ww[1] * vv[1] * dbt[nt][1] + ww[2] * vv[2] * dbt[nt][2] + ww[3] * vv[3] * dbt[nt][3];
-      store4_t(P2, LD, 16 * nt, 16 * w, ov);
-      store4_t(P4, LD, 16 * nt, 16 * w, ow);
+      part += ww[0] * vv[0] * dbt[q][0] + ww[1] * vv[1] * dbt[q][1] + ww[2] * vv[2] * dbt[q][2] + ww[3] * vv[3] * dbt[q][3];
+      store4_t(P2, LD, 16 * nt, 16 * wr, ov);
+      store4_t(P4, LD, 16 * nt, 16 * wr, ow);
     }
     part = sum_rows4(part);
     if (lgrp() == 0) rb[w][tr] = part;
@@ -583,8 +590,8 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_wy(Geo geo, const E* __restric
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
     float* rows = p.g2_rows + u * 4 * CH;
-    rows[CH + t] = rk[t >> 4][t];
-    rows[2 * CH + t] = rb[t >> 4][t];
+    rows[CH + t] = rk[t >> 4][t] + rk[(t >> 4) + 4][t];
+    rows[2 * CH + t] = rb[t >> 4][t] + rb[(t >> 4) + 4][t];
   }
 }
 
@@ -603,16 +610,16 @@ struct G2GramLds {
 };
 
 template <typename E, int D, bool LOG>
-__global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(512) void k_bwd_gdn2_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                        const E* __restrict__ beta, const E* __restrict__ alpha,
                                                        const E* __restrict__ erase, const float* __restrict__ Gg,
                                                        const E* __restrict__ Mqag, const E* __restrict__ Mqkg,
                                                        E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dbeta,
                                                        E* __restrict__ dalpha, E* __restrict__ derase, Plan p) {
   using Ly = G2GramLds<E, D>;
-  constexpr int NT = 256, LD = Ly::LD, LDT = Ly::LDT, LF = Ly::LF;
+  constexpr int NT = 512, NW = NT / 64, LD = Ly::LD, LDT = Ly::LDT, LF = Ly::LF, NQ = D / 32;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ float gs[CH], bs[CH], rq[4][CH], re_[4][CH];
+  __shared__ float gs[CH], bs[CH], rq[NW][CH], re_[NW][CH];  // row sums, one part per wave
   E* Ks = reinterpret_cast<E*>(smem);
   E* As = Ks + CH * LD;
   E* Qs = As + CH * LD;
@@ -627,7 +634,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   const ChunkPos cp = chunk_pos(geo, gc);
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
-  const int w = wave_id(), n = cp.n;
+  const int w = wave_id(), wr = w & 3, wc = w >> 2, n = cp.n;
 
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
@@ -637,23 +644,24 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
   g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
   g2s_rows<E, CH, D, NT>(Es, LD, erase + tk * D, D, n);
-  // Products are formed transposed: lane (lrow, lgrp) of wave w holds row t = 16w + lrow and
-  // four consecutive columns 4 lgrp .. +3 of each 16-column tile, so every access of a result
-  // is one vector access.
-  const int tr = 16 * w + lrow();
-  f32x4 aq[D / 16], ak[D / 16], aa[D / 16];
+  // Products are formed transposed: lane (lrow, lgrp) of wave w holds row t = 16 (w & 3) + lrow
+  // and four consecutive columns 4 lgrp .. +3 of each of its 16-column tiles (half of them:
+  // tiles NQ (w >> 2) ..), so every access of a result is one vector access.
+  const int tr = 16 * wr + lrow();
+  f32x4 aq[NQ], ak[NQ], aa[NQ];
   {  // the partial gradients from the earlier stages, issued early
     const float* dq1 = p.g2_dq + u * CH * D + tr * D + 4 * lgrp();
     const float* dk1 = p.g2_dk + u * CH * D + tr * D + 4 * lgrp();
     const float* da1 = p.g2_da + u * CH * D + tr * D + 4 * lgrp();
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
+    for (int q = 0; q < NQ; ++q) {
+      const int nt = wc * NQ + q;
       const float4 x = *reinterpret_cast<const float4*>(dq1 + 16 * nt);
       const float4 y = *reinterpret_cast<const float4*>(dk1 + 16 * nt);
       const float4 z = *reinterpret_cast<const float4*>(da1 + 16 * nt);
-      aq[nt] = f32x4{x.x, x.y, x.z, x.w};
-      ak[nt] = f32x4{y.x, y.y, y.z, y.w};
-      aa[nt] = f32x4{z.x, z.y, z.z, z.w};
+      aq[q] = f32x4{x.x, x.y, x.z, x.w};
+      ak[q] = f32x4{y.x, y.y, y.z, y.w};
+      aa[q] = f32x4{z.x, z.y, z.z, z.w};
     }
   }
   __syncthreads();
@@ -723,36 +731,37 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   {
     float part = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
-      const f32x4 qv = get4(Qs + tr * LD + 16 * nt + 4 * lgrp());
-      part += qv[0] * aq[nt][0] + qv[1] * aq[nt][1] + qv[2] * aq[nt][2] + qv[3] * aq[nt][3];
+    for (int q = 0; q < NQ; ++q) {
+      const f32x4 qv = get4(Qs + tr * LD + 16 * (wc * NQ + q) + 4 * lgrp());
+      part += qv[0] * aq[q][0] + qv[1] * aq[q][1] + qv[2] * aq[q][2] + qv[3] * aq[q][3];
     }
     part = sum_rows4(part);
     if (lgrp() == 0) rq[w][tr] = part;
   }
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    ak[nt] = mma_k<E, CH>(ak[nt], colk(Ks, LD), 16 * nt, rowk(Tkk, LDT), 16 * w);
-    ak[nt] = mma_k<E, CH>(ak[nt], colk(Ks, LD), 16 * nt, colk(Tkk, LDT), 16 * w);
-    ak[nt] = mma_k<E, CH>(ak[nt], colk(As, LD), 16 * nt, rowk(Tak, LDT), 16 * w);
-    ak[nt] = mma_k<E, CH>(ak[nt], colk(Qs, LD), 16 * nt, colk(Tqk, LDT), 16 * w);
-    aq[nt] = mma_k<E, CH>(aq[nt], colk(Ks, LD), 16 * nt, rowk(Tqk, LDT), 16 * w);
-    aq[nt] = mma_k<E, CH>(aq[nt], colk(As, LD), 16 * nt, rowk(Tqa, LDT), 16 * w);
-    aa[nt] = mma_k<E, CH>(aa[nt], colk(Ks, LD), 16 * nt, colk(Tak, LDT), 16 * w);
-    aa[nt] = mma_k<E, CH>(aa[nt], colk(Qs, LD), 16 * nt, colk(Tqa, LDT), 16 * w);
+  for (int q = 0; q < NQ; ++q) {
+    const int nt = wc * NQ + q;
+    ak[q] = mma_k<E, CH>(ak[q], colk(Ks, LD), 16 * nt, rowk(Tkk, LDT), 16 * wr);
+    ak[q] = mma_k<E, CH>(ak[q], colk(Ks, LD), 16 * nt, colk(Tkk, LDT), 16 * wr);
+    ak[q] = mma_k<E, CH>(ak[q], colk(As, LD), 16 * nt, rowk(Tak, LDT), 16 * wr);
+    ak[q] = mma_k<E, CH>(ak[q], colk(Qs, LD), 16 * nt, colk(Tqk, LDT), 16 * wr);
+    aq[q] = mma_k<E, CH>(aq[q], colk(Ks, LD), 16 * nt, rowk(Tqk, LDT), 16 * wr);
+    aq[q] = mma_k<E, CH>(aq[q], colk(As, LD), 16 * nt, rowk(Tqa, LDT), 16 * wr);
+    aa[q] = mma_k<E, CH>(aa[q], colk(Ks, LD), 16 * nt, colk(Tak, LDT), 16 * wr);
+    aa[q] = mma_k<E, CH>(aa[q], colk(Qs, LD), 16 * nt, colk(Tqa, LDT), 16 * wr);
   }
   // gates: de = beta da*k, dk += beta da*e, dbeta_a = sum_j da*e*k
   {
     const float bt = bs[tr];
     float part = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
-      const int j0 = 16 * nt + 4 * lgrp();
-      const f32x4 kk = get4(Ks + tr * LD + j0), ee = get4(Es + tr * LD + j0), da = aa[nt];
-      ak[nt] += bt * da * ee;
+    for (int q = 0; q < NQ; ++q) {
+      const int j0 = 16 * (wc * NQ + q) + 4 * lgrp();
+      const f32x4 kk = get4(Ks + tr * LD + j0), ee = get4(Es + tr * LD + j0), da = aa[q];
+      ak[q] += bt * da * ee;
       part += da[0] * ee[0] * kk[0] + da[1] * ee[1] * kk[1] + da[2] * ee[2] * kk[2] + da[3] * ee[3] * kk[3];
-      aa[nt] = bt * da * kk;  // now de
-      if constexpr (LOG) aa[nt] *= ee * (1.f - ee);  // w.r.t. the erase-gate logit
+      aa[q] = bt * da * kk;  // now de
+      if constexpr (LOG) aa[q] *= ee * (1.f - ee);  // w.r.t. the erase-gate logit
     }
     part = sum_rows4(part);
     if (lgrp() == 0) re_[w][tr] = part;
@@ -768,10 +777,11 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   __syncthreads();
   // outputs through LDS (K, A, Q regions are free now)
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt) {
-    store4_t(Ks, LD, 16 * nt, 16 * w, ak[nt]);
-    store4_t(Qs, LD, 16 * nt, 16 * w, aq[nt]);
-    store4_t(As, LD, 16 * nt, 16 * w, aa[nt]);
+  for (int q = 0; q < NQ; ++q) {
+    const int nt = wc * NQ + q;
+    store4_t(Ks, LD, 16 * nt, 16 * wr, ak[q]);
+    store4_t(Qs, LD, 16 * nt, 16 * wr, aq[q]);
+    store4_t(As, LD, 16 * nt, 16 * wr, aa[q]);
   }
   if (threadIdx.x < CH) {
     const int t = threadIdx.x;
@@ -782,7 +792,7 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
       for (int uu = 0; uu < CH; ++uu) rect += (uu >= t) ? Pair[uu * LF + t - 1] : 0.f;
     }
     const int tq = CH - 1 - t;
-    const float suf_r = wave_incl_scan(rq[tq >> 4][tq] + rows[CH + tq]);
+    const float suf_r = wave_incl_scan(rq[tq >> 4][tq] + rq[(tq >> 4) + 4][tq] + rows[CH + tq]);
     const float suf = __shfl(suf_r, CH - 1 - t, 64);
     const float inc = wave_incl_scan(rows[t]);
     float pre = __shfl_up(inc, 1, 64);
@@ -791,10 +801,10 @@ __global__ __launch_bounds__(256) void k_bwd_gdn2_gram(Geo geo, const E* __restr
     if (t < n) {
       if constexpr (LOG) {  // w.r.t. the logits: d log alpha (-sigmoid(x_alpha)), dbeta beta (1 - beta)
         dalpha[tk + t] = (E)(-dla * gate_sigmoid((float)alpha[tk + t]));
-        if (dbeta) dbeta[tk + t] = (E)((rows[2 * CH + t] + re_[t >> 4][t]) * bs[t] * (1.f - bs[t]));
+        if (dbeta) dbeta[tk + t] = (E)((rows[2 * CH + t] + re_[t >> 4][t] + re_[(t >> 4) + 4][t]) * bs[t] * (1.f - bs[t]));
       } else {
         dalpha[tk + t] = (E)(dla / (float)alpha[tk + t]);
-        if (dbeta) dbeta[tk + t] = (E)(rows[2 * CH + t] + re_[t >> 4][t]);
+        if (dbeta) dbeta[tk + t] = (E)(rows[2 * CH + t] + re_[t >> 4][t] + re_[(t >> 4) + 4][t]);
       }
     }
   }
@@ -816,13 +826,13 @@ static hipError_t bwd_gdn2_impl(const Plan& p, const gdr_inputs& in, const void*
   }
   {
     TraceScope ts_("bwd_gdn2_wy", st);
-    hipLaunchKernelGGL((k_bwd_gdn2_wy<E, D, LOG>), grid, dim3(256), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
+    hipLaunchKernelGGL((k_bwd_gdn2_wy<E, D, LOG>), grid, dim3(512), 0, st, p.geo, (const E*)in.k, (const E*)in.v,
                        (const E*)in.beta, (const E*)in.erase, (const E*)in.write, (const E*)dO, (const float*)p.G,
                        (const E*)p.X, (const E*)p.U2, (const E*)p.M2, (const E*)p.dR, (E*)gr.dv, (E*)gr.dwrite, p);
   }
   {
     TraceScope ts_("bwd_gdn2_gram", st);
-    hipLaunchKernelGGL((k_bwd_gdn2_gram<E, D, LOG>), grid, dim3(256), 0, st, p.geo, (const E*)in.q, (const E*)in.k,
+    hipLaunchKernelGGL((k_bwd_gdn2_gram<E, D, LOG>), grid, dim3(512), 0, st, p.geo, (const E*)in.q, (const E*)in.k,
                        (const E*)in.beta, (const E*)in.alpha, (const E*)in.erase, (const float*)p.G, (const E*)p.M,
                        (const E*)p.M2, (E*)gr.dq, (E*)gr.dk, (E*)gr.dbeta, (E*)gr.dalpha, (E*)gr.derase, p);
   }
@@ -840,7 +850,7 @@ template <typename E, int D>
 hipError_t launch_fwd_prep_gdn2(const Plan& p, const gdr_inputs& in, hipStream_t st) {
   TraceScope ts_("fwd_prep_gdn2", st);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H), dim3(256), 0, st, p.geo, (const E*)in.q,
+    hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H), dim3(512), 0, st, p.geo, (const E*)in.q,
                        (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (const E*)in.erase,
                        (const E*)in.write, (E*)p.X, (E*)p.Ub, (E*)p.U2, (E*)p.M, (E*)p.M2, p.G, p.Li, p.A1, p.A2);
   };
