@@ -67,13 +67,13 @@ def kernel_bytes_per_unit(variant: str, kernel: str, D: int = 128, esz: int = 2,
         "fwd_prep_gla": 3 * TOK + BETA + ALPHA + 3 * TOK + GRAM + FD,
         "fwd_scan": (6 * TOK + BETA if g2 else 2 * TOK + XT) + DEC + SQR + TOK + OUT + (GRAM if g2 else 0),
         "bwd_scan": 2 * TOK + XT + TOK + GRAM + DEC + SQR + TOK + ((TOK + BETA) if g2 else 0),
-        "bwd_gla_state": 2 * TOK + 2 * SQR + FD + 2 * FTOK + FGRAM + FD,
+        "bwd_gla_state": 2 * TOK + 2 * SQR + FD + 2 * FTOK + GRAM + FD,
         "bwd_gla_wv": 3 * TOK + 2 * BETA,
-        "bwd_gla_gram": 2 * TOK + ALPHA + FGRAM + 2 * FTOK + FD + 2 * TOK + ALPHA,
+        "bwd_gla_gram": 2 * TOK + ALPHA + GRAM + 2 * FTOK + FD + 2 * TOK + ALPHA,
         "bwd_chunk": 4 * TOK + BETA + ALPHA + GRAM + GLOG + 2 * SQR + 2 * TOK + 3 * TOK + BETA + ALPHA + FGRAM,
-        "bwd_kda_state": 3 * TOK + 2 * SQR + FD + 3 * FTOK + FGRAM + FD,
-        "bwd_kda_wy": 3 * TOK + BETA + ALPHA + FTOK + 2 * FGRAM + TOK + BETA + FTOK + FGRAM,
-        "bwd_kda_gram": 2 * TOK + ALPHA + 2 * FGRAM + 3 * FTOK + FD + 2 * TOK + ALPHA,
+        "bwd_kda_state": 3 * TOK + 2 * SQR + FD + 3 * FTOK + GRAM + FD,
+        "bwd_kda_wy": 3 * TOK + BETA + ALPHA + FTOK + 2 * FGRAM + TOK + BETA + FTOK + GRAM,
+        "bwd_kda_gram": 2 * TOK + ALPHA + 2 * GRAM + 3 * FTOK + FD + 2 * TOK + ALPHA,
         "bwd_gdn2_state": 5 * TOK + GLOG + BETA + 2 * SQR + 2 * TOK + 5 * FTOK + 2 * FGRAM + 4 * GLOG,
         "bwd_gdn2_wy": 3 * TOK + GLOG + BETA + 2 * FGRAM + 3 * TOK + GRAM + 3 * FTOK + 2 * TOK + 2 * FGRAM + FTOK
                        + 4 * GLOG,

@@ -413,7 +413,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restr
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int id = w + 8 * e;
-      mq[e] = mma_k<E, KH>(mq[e], rowk(dOs + ih * KH, LD), 16 * (id >> 2), rowk(Rs + ih * KH, LD), 16 * (id & 3));
+      mq[e] = mma_k<E, KH>(mq[e], rowk(Rs + ih * KH, LD), 16 * (id & 3), rowk(dOs + ih * KH, LD), 16 * (id >> 2));  // dM^T
     }
     for (int i = gp; i < KH; i += NP) gam += (float)Wh[gj * LDR + i] * (float)dWh[gj * LDR + i];
   }
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restr
   float* dqh = p.kd_dqh + u * CH * D;
   float* dx = p.kd_dx + u * CH * D;
   float* dk1 = p.kd_dkb + u * CH * D;
-  float* dm = p.kd_dm + u * CH * CH;
+  E* dm = reinterpret_cast<E*>(p.kd_dm) + u * CH * CH;
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt)
 #pragma unroll
@@ -435,13 +435,13 @@ __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restr
 #pragma unroll
     for (int r = 0; r < 4; ++r) dk1[acc_row(16 * wm, r) * D + acc_col(16 * (wn * NQ + qq))] = dkb[qq][r];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
+  for (int e = 0; e < 2; ++e) {  // tile (rows mt, columns nt) held transposed: four consecutive columns of row t
     const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
+    const int t = acc_col(16 * mt), s0 = acc_row(16 * nt, 0);
+    f32x4 x;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * mt, r), s = acc_col(16 * nt);
-      dm[t * CH + s] = (s <= t) ? geo.scale * mq[e][r] : 0.f;
-    }
+    for (int r = 0; r < 4; ++r) x[r] = (s0 + r <= t) ? geo.scale * mq[e][r] : 0.f;
+    put4(dm + t * CH + s0, x);
   }
   __syncthreads();
   if (threadIdx.x < D) {
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict
   }
   __syncthreads();
   // dL (strictly lower), transposed: dT is no longer read, so dL overwrites it in place
-  float* da = p.kd_da + u * CH * CH;
+  E* da = reinterpret_cast<E*>(p.kd_da) + u * CH * CH;
 #pragma unroll
   for (int e = 0; e < 16 / NW; ++e) {
     const int id = w + NW * e, mt = id >> 2, nt = id & 3;
@@ -706,23 +706,25 @@ __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restri
 
   {
     RegTile<E, CH, JW, NT> rk, rq, ra;
-    RegTile<float, CH, CH, NT> rda, rdm;
+    RegTile<E, CH, CH, NT> rda, rdm;
     ra.load(alpha + tk * D + j0, D, n);
     rk.load(k + tk * D + j0, D, n);
     rq.load(q + tk * D + j0, D, n);
-    if constexpr (!EF) rda.load(p.kd_da + u * CH * CH, CH, CH);
-    rdm.load(p.kd_dm + u * CH * CH, CH, CH);
+    if constexpr (!EF) rda.load(reinterpret_cast<const E*>(p.kd_da) + u * CH * CH, CH, CH);
+    rdm.load(reinterpret_cast<const E*>(p.kd_dm) + u * CH * CH, CH, CH);
     if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
     rk.store(Ks, LDJ);
     rq.store(Qs, LDJ);
+    rdm.store(dMs, LDT);
+    if constexpr (EF) {
+      using RA = decltype(rda);
 #pragma unroll
-    for (int it = 0; it < decltype(rda)::IT; ++it) {
-      const int t = rda.row(it), s0 = rda.col(it);
-#pragma unroll
-      for (int x = 0; x < decltype(rda)::VE; ++x) {
-        dAs[t * LDT + s0 + x] = EF ? (E)0.f : (E)rda.elem(it, x);
-        dMs[t * LDT + s0 + x] = (E)rdm.elem(it, x);
+      for (int it = 0; it < RA::IT; ++it) {
+        if (RA::TOTAL % NT == 0 || threadIdx.x + it * NT < RA::TOTAL)
+          *reinterpret_cast<typename RA::V*>(dAs + rda.row(it) * LDT + rda.col(it)) = typename RA::V{};
       }
+    } else {
+      rda.store(dAs, LDT);
     }
     kda_cumlog<E, JW, NT, LOG>(ra, n, Gs, LDF, tot);
   }

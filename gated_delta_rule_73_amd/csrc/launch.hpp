@@ -54,10 +54,12 @@ struct Plan {
   float *g2_dq, *g2_dk, *g2_da, *g2_db, *g2_dx;
   float *g2_dakk, *g2_daak, *g2_dmqk, *g2_dmqa;
   float* g2_rows;  // [units][4][64]: prefix-type sums, Khat.dKhat, dbeta from b, gamma term
-  // Kimi Delta Attention backward intermediates (float32, the same workspace region): per unit
-  // 64 x D gradients w.r.t. Qhat, X, Kbar, Khat; 64 x 64 gradients w.r.t. M and A; D values
-  // e^{g_n} <W0, dW> per key channel.
-  float *kd_dqh, *kd_dx, *kd_dkb, *kd_dkh, *kd_dm, *kd_da, *kd_gam;
+  // Kimi Delta Attention backward intermediates (the same workspace region): per unit 64 x D
+  // float32 gradients w.r.t. Qhat, X, Kbar, Khat; 64 x 64 gradients w.r.t. M and A in the I/O
+  // type (the Gram stage uses them only as matrix-core operands, rounded to that type; their
+  // slots keep the float32 size); D float32 values e^{g_n} <W0, dW> per key channel.
+  float *kd_dqh, *kd_dx, *kd_dkb, *kd_dkh, *kd_gam;
+  void *kd_dm, *kd_da;
 };
 
 // Optional per-launch event recording (see gdr_trace_launches in gdr.h).
