@@ -3,7 +3,9 @@
     python -m gated_delta_rule_73_amd.build      # or gated_delta_rule_73_amd.build.build()
 
 Sources are compiled in parallel to objects under gated_delta_rule_73_amd/_build/ and linked
-into gated_delta_rule_73_amd/libgdr.so.
+into gated_delta_rule_73_amd/libgdr.so.  The same sources built with -DGDR_LDS_POISON are linked
+into libgdr_poison.so (objects under _build/poison/), the LDS-poisoning debug build the tests
+compare with the release library.
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
+POISON_LIB = os.path.join(PKG, "libgdr_poison.so")
+POISON_BUILD = os.path.join(BUILD, "poison")
 SOURCES = ["gdr.cpp", "fwd.hip", "bwd.hip", "gdn2.hip", "kda.hip", "seg.hip", "decode.hip", "norm.hip"]
 ARCH = "gfx950"
 FLAGS = [
@@ -34,29 +38,59 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, poison: bool = False) -> str:
+    out_dir = POISON_BUILD if poison else BUILD
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *FLAGS, *(["-DGDR_LDS_POISON"] if poison else []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, poison: bool = True) -> str:
+    """Build libgdr.so and (poison=True) the LDS-poisoning debug build libgdr_poison.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(POISON_BUILD, exist_ok=True)
+    variants = [False, True] if poison else [False]
+    jobs = min(len(SOURCES) * len(variants), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        futs = {v: [ex.submit(_compile, src, v) for src in SOURCES] for v in variants}
+        objs = {v: [f.result() for f in fs] for v, fs in futs.items()}
+    _link(objs[False], LIB)
     if verbose:
         print(f"built {LIB}")
+    if poison:
+        _link(objs[True], POISON_LIB)
+        if verbose:
+            print(f"built {POISON_LIB}")
     return LIB
+
+
+def build_poisoned(verbose: bool = False) -> str:
+    """libgdr_poison.so alone: the kernels built with -DGDR_LDS_POISON, which fill a kernel's LDS
+    with 0xFF bytes (NaN in bfloat16 and float32) at entry, the scans' LDS between chunk steps and
+    the chunk kernels' LDS regions where their contents die.  A read of LDS that was never written
+    (or of dead contents) then shows up as NaN; otherwise the results are the release build's,
+    bit for bit.  Slower (extra barriers and stores): for tests only."""
+    os.makedirs(POISON_BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda src: _compile(src, True), SOURCES))
+    _link(objs, POISON_LIB)
+    if verbose:
+        print(f"built {POISON_LIB}")
+    return POISON_LIB
 
 
 SAN_LIB = os.path.join(PKG, "libgdr_san.so")

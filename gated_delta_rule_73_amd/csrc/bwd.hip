@@ -80,6 +80,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
                                                   E* __restrict__ dRg, float* __restrict__ dh0,
                                                   const E* __restrict__ beta, const E* __restrict__ erase,
                                                   const E* __restrict__ drin, E* __restrict__ dRog) {
+  GDR_POISON_ALL();
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2 || VAR == VAR_GDN2L;
@@ -291,6 +292,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
         if constexpr (!NOX) S[qq][it] = mma_k<E, CH>(S[qq][it], colk(Xs, LD), 16 * (w + 4 * qq), colk(dRt, LDO), 16 * it);
       }
     __syncthreads();
+    GDR_POISON_ALL();  // debug builds: nothing in LDS is carried to the next step
   };
   if (c1 > c0) {
     Ops pa, pb;
@@ -371,6 +373,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
                                                    E* __restrict__ dbeta, E* __restrict__ dalpha,
                                                    const E* __restrict__ drin, const float* __restrict__ Rng,
                                                    int ts_part, int ts_lseg) {
+  GDR_POISON_ALL();
   using Ly = BwdLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDR = Ly::LDR, LF = Ly::LF;
   constexpr int KH = 64, NH = D / KH;  // the memory is read in blocks of 64 value rows
@@ -553,6 +556,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     if (lane_id() == 0) red[w] = gam;
   }
   __syncthreads();
+  GDR_POISON(smem + Ly::oU, Ly::endP1 - Ly::oU);  // dO, R and the memory blocks are no longer read
 
   // ================= phase 2: the WY / triangular-solve part
   float* As = reinterpret_cast<float*>(smem + Ly::oA);
@@ -636,6 +640,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     if (lgrp() == 0) rkh[w][tr] = part;
   }
   __syncthreads();
+  GDR_POISON(dXs, Ly::TK);  // dX, dR and V are no longer read
+  GDR_POISON(dRs, Ly::TK);
+  GDR_POISON(smem + Ly::oVP, Ly::endVP - Ly::oVP);
 #pragma unroll
   for (int qq = 0; qq < NQ; ++qq) store4_t(Vs, LD, 16 * (wn * NQ + qq), 16 * wm, dva[qq]);
   {  // dbeta from T = Linv diag(beta): column sums, eight threads per column
@@ -657,6 +664,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     store4_t(Pt, LF, 16 * mt, 16 * nt, acc);
   }
   __syncthreads();
+  GDR_POISON(smem + Ly::oVP, Ly::endVP - Ly::oVP);  // dV has been written out
   // dL (strictly lower); dT is no longer read, so dL overwrites it in place
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -668,6 +676,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     store4_n(dTs, LF, 16 * mt, 16 * nt, dl);
   }
   __syncthreads();
+  GDR_POISON(Pt, Ly::F);  // Pt and the float32 L^{-1} are no longer read
+  GDR_POISON(Li, Ly::F);
   {  // dbeta from L = I + diag(beta) A: row sums (dL is zero on and above the diagonal); eight
      // adjacent lanes per row, eight consecutive columns each (vector reads), summed with DPP
     static_assert(NT == 8 * CH, "eight lanes per row");
@@ -741,6 +751,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
   }
   __syncthreads();
+  GDR_POISON(As, Ly::F);  // A, dT (now dL) and dM are no longer read
+  GDR_POISON(dTs, Ly::F);
+  GDR_POISON(dMs, Ly::SQ);
   if (w < 4) {  // the row's Qhat . dQhat (state term), four consecutive columns per lane
     float part = 0.f;
 #pragma unroll
@@ -782,6 +795,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     }
   }
   __syncthreads();
+  GDR_POISON(smem + Ly::odR, 2 * Ly::SQ);  // At, Mt and Q are no longer read
+  GDR_POISON(Qs, Ly::TK);
   if constexpr (GATED) {  // rectangle sums: sum over u >= t of the prefix at column t-1
     const int t = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
@@ -795,6 +810,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     part8[pt][t] = a;
   }
   __syncthreads();
+  GDR_POISON(smem + Ly::oPair, Ly::F);  // the pair terms are no longer read
   if constexpr (QKN) {  // dk w.r.t. the raw rows: dk = (dk~ - k~ (k~ . dk~)) / ||k|| (dq was done above)
     // k~ . dk~ per row: a row's columns are split over waves w and w ^ 4; the partial sums go
     // through the pair-term region, no longer read
@@ -891,6 +907,7 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
                                                        const float* __restrict__ Ag, const E* __restrict__ k,
                                                        const float* __restrict__ Gg, const float* __restrict__ Lig,
                                                        E* __restrict__ dbeta) {
+  GDR_POISON_ALL();
   constexpr int NT = 512, LD = D + pad16<E>(), LF = CH + 4, NW = NT / 64;
   constexpr int NH = D / 32;  // column tiles of a 64 x D product per wave (two waves per row block)
   constexpr int TE = CH * LD, TF = CH * LF;

@@ -28,6 +28,36 @@ constexpr int CH = 64;  // chunk length (tokens)
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
+// LDS poisoning, debug builds only (GDR_LDS_POISON; the release library compiles both to
+// nothing).  LDS keeps whatever the previous workgroup on the CU left there, so a read of an
+// element this workgroup never wrote (or of a region whose contents are dead) is a latent bug
+// even where the release build happens to get a finite value.  Poisoned bytes are 0xFF, a NaN in
+// bfloat16 and in float32, so such a read shows up as NaN in the results.  Both calls are made
+// by every thread of the block and are bracketed by block barriers.
+//   GDR_POISON_ALL():       the kernel's whole static LDS allocation (at entry; the scans also
+//                           between chunk steps, where nothing in LDS is carried over).
+//   GDR_POISON(p, bytes):   one LDS region (bytes a multiple of 4) whose contents are dead.
+#ifdef GDR_LDS_POISON
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+__device__ __forceinline__ void lds_poison_all() {
+  __syncthreads();
+  const unsigned n = __builtin_amdgcn_groupstaticsize() / 4;  // static LDS starts at address 0
+  for (unsigned i = threadIdx.x; i < n; i += blockDim.x) *(lds_u32*)(size_t)(4u * i) = 0xFFFFFFFFu;
+  __syncthreads();
+}
+__device__ __forceinline__ void lds_poison(void* p, int bytes) {
+  __syncthreads();
+  uint32_t* w = reinterpret_cast<uint32_t*>(p);
+  for (int i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = 0xFFFFFFFFu;
+  __syncthreads();
+}
+#define GDR_POISON_ALL() lds_poison_all()
+#define GDR_POISON(p, bytes) lds_poison((p), (bytes))
+#else
+#define GDR_POISON_ALL() ((void)0)
+#define GDR_POISON(p, bytes) ((void)0)
+#endif
+
 // f(std::integral_constant<int, I>{}) for I = A .. B-1 in order: the body sees its index as a
 // compile-time constant, so register arrays it indexes stay in registers.
 template <int A, int B, typename F>

@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void k_decode(Geo geo, const E* __restrict__ q
                                                 const E* __restrict__ alpha, const E* __restrict__ erase,
                                                 const E* __restrict__ write, float* __restrict__ state,
                                                 E* __restrict__ o) {
+  GDR_POISON_ALL();
   constexpr int LPR = D / 4;          // lanes per row
   constexpr int GROUPS = 256 / LPR;   // rows in flight per workgroup pass
   constexpr int RPT = 4;              // rows per lane

@@ -31,6 +31,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
                                                   E* __restrict__ Uo, E* __restrict__ Mo, float* __restrict__ Go,
                                                   float* __restrict__ Lio, E* __restrict__ Qno, E* __restrict__ Kno,
                                                   float* __restrict__ Rno) {
+  GDR_POISON_ALL();
   constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   // Three 64-row buffers (about 52 KiB, so three workgroups share a CU):
   static_assert(CH * LD * (int)sizeof(E) >= 4 * 256 * 4, "the Q/V buffer doubles as the solve's scratch");
@@ -129,7 +130,9 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
     }
   }
   __syncthreads();
-  solve_unit_lower64<NT>(Ls, LF, Ls, LF, reinterpret_cast<float*>(QV));  // Q is no longer read
+  GDR_POISON(QV, (int)sizeof(QV));  // Q is no longer read
+  solve_unit_lower64<NT>(Ls, LF, Ls, LF, reinterpret_cast<float*>(QV));
+  GDR_POISON(QV, (int)sizeof(QV));  // nor the solve's scratch
   rv.store(QV, LD);
 
   // T = L^{-1} diag(beta), four columns at a time: L^{-1} is read into registers (and written
@@ -147,6 +150,7 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
     for (int r = 0; r < 4; ++r) tv[i][r] = s0 + r <= t ? lv[r] : 0.f;
   }
   __syncthreads();
+  GDR_POISON(Ls, (int)sizeof(Ls));  // L^{-1} is held in registers
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
     const int idx = threadIdx.x + i * NT, t = idx >> 4, s0 = (idx & 15) * 4;
@@ -180,6 +184,8 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
     ua[nt] = mma_k<E, CH>(zero4(), colk(QV, LD), 16 * nt, rowk(Ts, LDT), 16 * w);
   }
   __syncthreads();
+  GDR_POISON(Ks, (int)sizeof(Ks));  // Khat and V are no longer read
+  GDR_POISON(QV, (int)sizeof(QV));
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) {
     store4_t(Ks, LD, 16 * nt, 16 * w, xa[nt]);
@@ -230,6 +236,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
                                                   const E* __restrict__ q, const E* __restrict__ Mg,
                                                   const E* __restrict__ M2g, E* __restrict__ o,
                                                   E* __restrict__ rout) {
+  GDR_POISON_ALL();
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
   constexpr bool G2 = VAR == VAR_GDN2 || VAR == VAR_GDN2L;
@@ -462,6 +469,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       if (o) s2g_rows<E, CH, BV, NT>(o + tk * D + i0, D, Os, LDV, n);
     }
     if constexpr (RES) s2g_rows<E, CH, BV, NT>(rout + tk * D + i0, D, Rr, LDV, n);
+    GDR_POISON_ALL();  // debug builds: nothing in LDS is carried to the next step
   };
   if (c1 > c0) {
     Ops pa, pb;

@@ -25,6 +25,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep_gdn2(Geo geo, const E* __restr
                                                        E* __restrict__ Mqk, float* __restrict__ Go,
                                                        float* __restrict__ Lio, float* __restrict__ Akko,
                                                        float* __restrict__ Aako) {
+  GDR_POISON_ALL();
   constexpr int NT = 512, NW = NT / 64, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   constexpr int NQ = D / 32;  // column tiles per wave in the 64 x D products
   __shared__ __align__(16) E Ks[CH * LD];   // K, then e^g K, then X'
@@ -213,6 +214,7 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
                                                         const float* __restrict__ Gg, const E* __restrict__ Hs,
                                                         const E* __restrict__ Rg, const E* __restrict__ dHs,
                                                         const E* __restrict__ dRg, Plan p) {
+  GDR_POISON_ALL();
   using Ly = G2StateLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDR = Ly::LDR, KH = 64, NH = D / KH, NQ = D / 32;
   __shared__ __align__(16) char smem[Ly::BYTES];
@@ -408,6 +410,7 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_wy(Geo geo, const E* __restric
                                                      const E* __restrict__ U2g, const E* __restrict__ M2g,
                                                      const E* __restrict__ dRg, E* __restrict__ dv,
                                                      E* __restrict__ dw, Plan p) {
+  GDR_POISON_ALL();
   using Ly = G2WyLds<E, D>;
   constexpr int NT = 512, NW = NT / 64, LD = Ly::LD, LDT = Ly::LDT, NQ = D / 32;
   __shared__ __align__(16) char smem[Ly::BYTES];
@@ -616,6 +619,7 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_gram(Geo geo, const E* __restr
                                                        const E* __restrict__ Mqag, const E* __restrict__ Mqkg,
                                                        E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dbeta,
                                                        E* __restrict__ dalpha, E* __restrict__ derase, Plan p) {
+  GDR_POISON_ALL();
   using Ly = G2GramLds<E, D>;
   constexpr int NT = 512, NW = NT / 64, LD = Ly::LD, LDT = Ly::LDT, LF = Ly::LF, NQ = D / 32;
   __shared__ __align__(16) char smem[Ly::BYTES];

@@ -220,6 +220,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep_kda(Geo geo, const E* __restri
                                                       E* __restrict__ Uo, E* __restrict__ Mo, E* __restrict__ Kbo,
                                                       E* __restrict__ Qho, float* __restrict__ Gno,
                                                       float* __restrict__ Lio, float* __restrict__ Ao) {
+  GDR_POISON_ALL();
   using Ly = KdaPrepLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, LDT = Ly::LDT;
   __shared__ __align__(16) char smem[Ly::BYTES];
@@ -370,6 +371,7 @@ template <typename E, int D, bool EF>
 __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restrict__ dO, const float* __restrict__ Gn,
                                                        const E* __restrict__ Hs, const E* __restrict__ Rg,
                                                        const E* __restrict__ dHs, const E* __restrict__ dRg, Plan p) {
+  GDR_POISON_ALL();
   using Ly = KdaStateLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDR = Ly::LDR, KH = 64, NH = D / KH, NQ = D / 32, NP = NT / D;
   __shared__ __align__(16) char smem[Ly::BYTES];
@@ -480,6 +482,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict
                                                     const E* __restrict__ beta, const E* __restrict__ alpha,
                                                     const E* __restrict__ dRg, E* __restrict__ dv,
                                                     E* __restrict__ dbeta, Plan p) {
+  GDR_POISON_ALL();
   using Ly = KdaWyLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, NW = NT / 64;
   __shared__ __align__(16) char smem[Ly::BYTES];
@@ -677,6 +680,7 @@ template <typename E, int D, bool LOG, bool EF>
 __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ alpha, E* __restrict__ dq,
                                                       E* __restrict__ dk, E* __restrict__ dalpha, Plan p) {
+  GDR_POISON_ALL();
   using Ly = KdaGramLds<E>;
   constexpr int NT = 512, JW = Ly::JW, LDJ = Ly::LDJ, LDT = Ly::LDT, LDF = Ly::LDF, NC = JW / 16;
   constexpr int NCW = NC / 2;  // column tiles per wave
@@ -1057,6 +1061,7 @@ template <typename E, int D, bool LOG>
 __global__ __launch_bounds__(256) void k_bwd_gla_wv(Geo geo, const E* __restrict__ v, const E* __restrict__ beta,
                                                     const E* __restrict__ dRg, E* __restrict__ dv,
                                                     E* __restrict__ dbeta) {
+  GDR_POISON_ALL();
   constexpr int NT = 256;
   using RT = RegTile<E, CH, D, NT>;
   static_assert(RT::VB == 16 && RT::TOTAL % NT == 0, "whole 16-byte rows per lane group");

@@ -40,6 +40,7 @@ __device__ __forceinline__ void store_vec(E* p, const float* v) {
 // y = x / ||x|| per row of D.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void k_l2norm_rows(const E* __restrict__ x, E* __restrict__ y, long rows) {
+  GDR_POISON_ALL();
   using RV = RowVec<E, D>;
   constexpr int VE = RV::VE, LPR = RV::LPR;
   const long g0 = ((long)blockIdx.x * 256 + threadIdx.x) / LPR, stride = (long)gridDim.x * 256 / LPR;
@@ -64,6 +65,7 @@ __global__ __launch_bounds__(256) void k_l2norm_rows(const E* __restrict__ x, E*
 // dx = (dy - y (y . dy)) / ||x|| in place over dy, y recomputed from x.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void k_l2norm_grad_rows(const E* __restrict__ x, E* __restrict__ dxy, long rows) {
+  GDR_POISON_ALL();
   using RV = RowVec<E, D>;
   constexpr int VE = RV::VE, LPR = RV::LPR;
   const long g0 = ((long)blockIdx.x * 256 + threadIdx.x) / LPR, stride = (long)gridDim.x * 256 / LPR;

@@ -14,6 +14,7 @@ namespace gdr {
 template <int D, int BV>
 __global__ __launch_bounds__(256) void k_seg_combine(Geo geo, ScanSeg sg, const float* __restrict__ init,
                                                      float* __restrict__ starts, int reverse) {
+  GDR_POISON_ALL();
   constexpr int NJ = D / 64, NI = BV / 16, LDP = D + 4, NT = 256;
   __shared__ __align__(16) float Ps[D * LDP];   // linear part, rows k, columns j
   __shared__ __align__(16) float Wl[BV * LDP];  // this tile's rows of the running memory
