@@ -32,6 +32,14 @@ constexpr float KDA_REF_LIMIT = -60.f;
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 }  // namespace
 
+// The float32 64 x D partial gradients handed between the backward stages (dQhat, dX, dKbar,
+// dKhat) are stored tile by tile in the matrix-core accumulator layout: 16 x 16 tile (rt, ct) of
+// a unit at floats ((rt * D/16 + ct) * 64 + lane) * 4, the lane's four values being rows
+// 16 rt + 4 lgrp .. +3 of column 16 ct + lrow.  A tile is then one 16-byte store or load per
+// lane, where row-major storage took four scattered 4-byte accesses per lane.
+template <int D>
+__device__ __forceinline__ int frag_off(int rt, int ct) { return ((rt * (D / 16) + ct) * 64 + lane_id()) * 4; }
+
 // g for JW channels from a tile of alpha already loaded (rows >= n taken as log 1 = 0):
 // Gs[t*ldg + j] = sum_{u<=t} log alpha_{u,j}.  Each column is summed in four runs of 16 rows
 // whose totals are then carried in order, the same arithmetic in every kernel, so all of them
@@ -425,17 +433,12 @@ __global__ __launch_bounds__(512) void k_bwd_kda_state(Geo geo, const E* __restr
   float* dk1 = p.kd_dkb + u * CH * D;
   E* dm = reinterpret_cast<E*>(p.kd_dm) + u * CH * CH;
 #pragma unroll
-  for (int nt = 0; nt < D / 16; ++nt)
+  for (int nt = 0; nt < D / 16; ++nt) {
+    if (w < 4) *reinterpret_cast<f32x4*>(dqh + frag_off<D>(wm, nt)) = geo.scale * acc1[nt];
+    else if (!EF) *reinterpret_cast<f32x4*>(dx + frag_off<D>(wm, nt)) = -acc1[nt];
+  }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = acc_row(16 * wm, r), j = acc_col(16 * nt);
-      if (w < 4) dqh[t * D + j] = geo.scale * acc1[nt][r];
-      else if (!EF) dx[t * D + j] = -acc1[nt][r];
-    }
-#pragma unroll
-  for (int qq = 0; qq < NQ; ++qq)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dk1[acc_row(16 * wm, r) * D + acc_col(16 * (wn * NQ + qq))] = dkb[qq][r];
+  for (int qq = 0; qq < NQ; ++qq) *reinterpret_cast<f32x4*>(dk1 + frag_off<D>(wm, wn * NQ + qq)) = dkb[qq];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {  // tile (rows mt, columns nt) held transposed: four consecutive columns of row t
     const int id = w + 8 * e, mt = id >> 2, nt = id & 3;
@@ -503,13 +506,17 @@ __global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict
 
   const uint32_t braw = threadIdx.x < CH ? load_gate_raw(beta + tk, n, threadIdx.x) : 0u;  // staged after K
   RegTile<E, CH, D, NT> rv, rdr, rk, ra;
-  RegTile<float, CH, D, NT> rdx;
+  // dX tiles of this wave (row tile w & 3, half of the column tiles), in the hand-off layout
+  constexpr int NQ = D / 32;
+  const int wr = w & 3, wc = w >> 2;
+  f32x4 xf[NQ];
   RegTile<float, CH, CH, NT> rli, raf;
   ra.load(alpha + tk * D, D, n);
   rk.load(k + tk * D, D, n);
   rv.load(v + tk * D, D, n);
   rdr.load(dRg + u * CH * D, D, CH);
-  rdx.load(p.kd_dx + u * CH * D, D, CH);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) xf[q] = *reinterpret_cast<const f32x4*>(p.kd_dx + u * CH * D + frag_off<D>(wr, wc * NQ + q));
   rli.load(p.Li + u * CH * CH, CH, CH);
   raf.load(p.A1 + u * CH * CH, CH, CH);
   rk.store(Ks, LD);
@@ -529,12 +536,8 @@ __global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict
       *reinterpret_cast<uint4*>(Ks + t * LD + j0) = kv;
     }
   }
-  static_assert(decltype(rdx)::VE == 4, "four floats per vector");
 #pragma unroll
-  for (int it = 0; it < decltype(rdx)::IT; ++it) {
-    if (decltype(rdx)::TOTAL % NT == 0 || threadIdx.x + it * NT < decltype(rdx)::TOTAL)
-      put4(dXs + rdx.row(it) * LD + rdx.col(it), f32x4{rdx.elem(it, 0), rdx.elem(it, 1), rdx.elem(it, 2), rdx.elem(it, 3)});
-  }
+  for (int q = 0; q < NQ; ++q) store4_n(dXs, LD, 16 * wr, 16 * (wc * NQ + q), xf[q]);
   raf.store(Af, LF);
   __syncthreads();  // G is free from here on
   float* Li = reinterpret_cast<float*>(smem + Ly::oLi);
@@ -575,17 +578,16 @@ __global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict
     put4(dTs + t * LF + s0, x);
   }
   const auto Tt = [&]() { if constexpr (Ly::BCOPY) return colk(Tb, LDT); else return TtView{Li, LF, bs}; }();
-  // dV^T and dKhat^T (columns j, rows t): wave w takes row tile w & 3 and half of the column tiles
-  constexpr int NQ = D / 32;
-  const int wr = w & 3, wc = w >> 2;
+  // dV^T (columns j, rows t) and dKhat (rows t, columns j, in the hand-off layout): wave w takes
+  // row tile w & 3 and half of the column tiles
   f32x4 dva[NQ];
   {
-    float* dkh = p.kd_dkh + u * CH * D + (16 * wr + lrow()) * D + 4 * lgrp();
+    float* dkh = p.kd_dkh + u * CH * D;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int nt = wc * NQ + q;
       dva[q] = mma_k<E, CH>(zero4(), colk(dRs, LD), 16 * nt, Tt, 16 * wr);
-      put4(dkh + 16 * nt, mma_k<E, CH>(zero4(), colk(dXs, LD), 16 * nt, Tt, 16 * wr));
+      *reinterpret_cast<f32x4*>(dkh + frag_off<D>(wr, nt)) = mma_k<E, CH>(zero4(), Tt, 16 * wr, colk(dXs, LD), 16 * nt);
     }
   }
   __syncthreads();
@@ -777,14 +779,18 @@ __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restri
   const float* dkb = p.kd_dkb + u * CH * D;
   float lq[NCW][4], lk[NCW][4], lb[NCW][4], la[8];
 #pragma unroll
-  for (int cc = 0; cc < NCW; ++cc)
+  for (int cc = 0; cc < NCW; ++cc) {
+    const int o = frag_off<D>(b, j0 / 16 + hf * NCW + cc);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(dqh + o);
+    const f32x4 y = EF ? zero4() : *reinterpret_cast<const f32x4*>(dkh + o);
+    const f32x4 z = *reinterpret_cast<const f32x4*>(dkb + o);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const long o = (long)acc_row(16 * b, r) * D + j0 + acc_col(16 * (hf * NCW + cc));
-      lq[cc][r] = dqh[o];
-      lk[cc][r] = EF ? 0.f : dkh[o];
-      lb[cc][r] = dkb[o];
+      lq[cc][r] = x[r];
+      lk[cc][r] = y[r];
+      lb[cc][r] = z[r];
     }
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {  // this half's tokens of the block
     const int t = min(16 * b + 8 * hf + i, n - 1);
