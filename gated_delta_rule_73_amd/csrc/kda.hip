@@ -911,8 +911,9 @@ __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restri
           y2[cc][r] += pr;
           ps += pr;
         }
-        // the pair (b, J)'s total, needed by the blocks strictly between J and b
-        if ((b == 2 && J == 0) || b == 3) {
+        // the pair (b, J)'s total, needed by the blocks strictly between J and b: pairs (2, 0),
+        // (3, 0) and (3, 1) into c1s[0..2] (no block lies between 2 and 3)
+        if ((b == 2 && J == 0) || (b == 3 && J < 2)) {
           ps += __shfl_xor(ps, 16, 64);
           ps += __shfl_xor(ps, 32, 64);
           if (l < 16) c1s[(b == 2) ? 0 : 1 + J][j] = ps;
