@@ -41,12 +41,12 @@ template <int D>
 __device__ __forceinline__ int frag_off(int rt, int ct) { return ((rt * (D / 16) + ct) * 64 + lane_id()) * 4; }
 
 // g for JW channels from a tile of alpha already loaded (rows >= n taken as log 1 = 0):
-// Gs[t*ldg + j] = sum_{u<=t} log alpha_{u,j}.  Each column is summed in four runs of 16 rows
-// whose totals are then carried in order, the same arithmetic in every kernel, so all of them
-// see the same values of g.  tot: 4*JW floats of scratch.  Ends with a block barrier.
+// Gs[t*ldg + j] = sum_{u<=t} log alpha_{u,j}.  Each column is one wave's inclusive scan over its
+// 64 lanes (lane = token), the same arithmetic in every kernel, so all of them see the same
+// values of g.  Ends with a block barrier.
 // LOG: the tile holds logits x, log alpha = -softplus(x).
 template <typename E, int JW, int NT, bool LOG>
-__device__ void kda_cumlog(const RegTile<E, CH, JW, NT>& ra, int n, float* Gs, int ldg, float* tot) {
+__device__ void kda_cumlog(const RegTile<E, CH, JW, NT>& ra, int n, float* Gs, int ldg) {
 #pragma unroll
   for (int it = 0; it < RegTile<E, CH, JW, NT>::IT; ++it) {
     if (RegTile<E, CH, JW, NT>::TOTAL % NT == 0 || threadIdx.x + it * NT < RegTile<E, CH, JW, NT>::TOTAL) {
@@ -59,23 +59,13 @@ __device__ void kda_cumlog(const RegTile<E, CH, JW, NT>& ra, int n, float* Gs, i
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 4 * JW; idx += NT) {
-    const int j = idx % JW, r0 = 16 * (idx / JW);
-    float run = 0.f;
+  constexpr int NW = NT / 64;
+  static_assert(JW % NW == 0, "whole columns per wave");
+  const int w = wave_id(), l = lane_id();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      run += Gs[(r0 + r) * ldg + j];
-      Gs[(r0 + r) * ldg + j] = run;
-    }
-    tot[idx] = run;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x + JW; idx < 4 * JW; idx += NT) {
-    const int j = idx % JW, part = idx / JW, r0 = 16 * part;
-    float off = tot[j];
-    for (int q = 1; q < part; ++q) off += tot[q * JW + j];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Gs[(r0 + r) * ldg + j] += off;
+  for (int i = 0; i < JW / NW; ++i) {
+    const int j = w + i * NW;
+    Gs[l * ldg + j] = wave_incl_scan(Gs[l * ldg + j]);
   }
   __syncthreads();
 }
@@ -232,7 +222,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep_kda(Geo geo, const E* __restri
   using Ly = KdaPrepLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, LDT = Ly::LDT;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ float bs[CH], tot[4 * D];
+  __shared__ float bs[CH];
   __shared__ int unsafe[4];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
   E* Kr = reinterpret_cast<E*>(smem + Ly::oKr);
@@ -264,7 +254,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep_kda(Geo geo, const E* __restri
     if (EF && !beta) b = (int)threadIdx.x < n ? 1.f : 0.f;
     bs[threadIdx.x] = b;
   }
-  kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG, tot);
+  kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG);
   kda_flags<D, NT>(Gs, LDG, unsafe);
 
   // Kbar and Qhat for the scans, e^{g_n} per channel, and the row
@@ -489,7 +479,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict
   using Ly = KdaWyLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, NW = NT / 64;
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ __align__(16) float bs[CH], tot[4 * D];
+  __shared__ __align__(16) float bs[CH];
   constexpr int PS = 4;  // threads per row or column in the beta-gradient sums (the first four waves)
   __shared__ float partc[PS][CH], partr[PS][CH];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
@@ -524,7 +514,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict
     const float b = gate_from_raw<E>(braw);  // 0 past the end
     bs[threadIdx.x] = (LOG && threadIdx.x < n) ? gate_sigmoid(b) : b;
   }
-  kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG, tot);
+  kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG);
   {  // Khat = e^g K in place, 16 bytes at a time
     constexpr int VE = 16 / (int)sizeof(E);
     for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
@@ -687,7 +677,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restri
   constexpr int NT = 512, JW = Ly::JW, LDJ = Ly::LDJ, LDT = Ly::LDT, LDF = Ly::LDF, NC = JW / 16;
   constexpr int NCW = NC / 2;  // column tiles per wave
   __shared__ __align__(16) char smem[Ly::BYTES];
-  __shared__ float c1s[3][JW], tota[4][JW], totc[4][JW], tot[4 * JW];
+  __shared__ float c1s[3][JW], tota[4][JW], totc[4][JW];
   __shared__ int unsafe[4];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
@@ -732,7 +722,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restri
     } else {
       rda.store(dAs, LDT);
     }
-    kda_cumlog<E, JW, NT, LOG>(ra, n, Gs, LDF, tot);
+    kda_cumlog<E, JW, NT, LOG>(ra, n, Gs, LDF);
   }
   kda_flags<JW, NT>(Gs, LDF, unsafe);
   // Kend_s = k_s e^{g_{16(J+1)} - g_s} (s in block J < 3);  Kf_u, Qf_u = (k_u, q_u) e^{g_u - g_{16I}}
