@@ -39,6 +39,9 @@ struct BwdScanOps {
   // and converted where the step uses them, so the loads are never waited for early)
   typename VecT<4 * sizeof(E)>::type dr[BV / 16];
   E braw;
+  // fused q/k normalisation: 1 / ||q|| of the dO rows this lane holds, 1 / ||k|| of dR^T's
+  // chunk row 16 w + lrow
+  float rnq[RegTile<E, CH, BV, 256>::IT], rnk;
 };
 template <typename E, int D, int BV>
 struct BwdScanOps<E, D, BV, VAR_GDN2> {
@@ -71,7 +74,9 @@ struct BwdScanOps<E, D, BV, VAR_GLA> {  // nothing erased: no X
 // dr_t / beta_t to dR_t before dR feeds the memory gradient and the chunk kernel.  dRog, if not
 // NULL, also receives dR without that term (the beta gradient is formed from it, see
 // k_bwd_res_dbeta).
-// QKN (delta family): q and k are the preparation's per-unit scaled copies (see k_fwd_prep).
+// QKN (delta family): q and k are normalised to unit length per token.  The raw rows are read
+// and the preparation's factors Rng (1 / ||q||, 1 / ||k|| per unit) are applied to the rows
+// that meet them: to scale e^g dO in the update Q^T (e^g dO), to e^{g_n-g} (dW K^T) in dR.
 template <typename E, int D, int BV, int VAR, bool RES, bool QKN>
 __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ dO, const E* __restrict__ Xg,
@@ -79,7 +84,8 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
                                                   const float* __restrict__ dht, E* __restrict__ dHs,
                                                   E* __restrict__ dRg, float* __restrict__ dh0,
                                                   const E* __restrict__ beta, const E* __restrict__ erase,
-                                                  const E* __restrict__ drin, E* __restrict__ dRog) {
+                                                  const E* __restrict__ drin, E* __restrict__ dRog,
+                                                  const float* __restrict__ Rng) {
   GDR_POISON_ALL();
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
@@ -170,9 +176,13 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
 #pragma unroll
         for (int qq = 0; qq < NJ; ++qq) p.eg[qq] = *reinterpret_cast<const f32x4*>(Gg + u * D + acc_row(16 * (w + 4 * qq), 0));
       } else {
-        p.q.load(q + (QKN ? u * CH : tk) * D, D, QKN ? CH : n);
-        p.k.load(k + (QKN ? u * CH : tk) * D, D, QKN ? CH : n);
+        p.q.load(q + tk * D, D, n);
+        p.k.load(k + tk * D, D, n);
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+        if constexpr (QKN) {  // read before the next refill of this set
+          load_row_factors(p.dO, Rng + u * 2 * CH, p.rnq);
+          p.rnk = Rng[u * 2 * CH + CH + 16 * w + lrow()];
+        }
       }
       if constexpr (RES) {  // accumulator layout of dR^T: row 16 w + lrow, columns 16 it + 4 lgrp
         const int t = min(16 * w + lrow(), n - 1);
@@ -219,8 +229,9 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
         if (RT::TOTAL % NT == 0 || threadIdx.x + it * NT < RT::TOTAL) {
           const int t = p.dO.row(it), i = p.dO.col(it);
           const E* e = reinterpret_cast<const E*>(&p.dO.v[it]);
-          float eg = 1.f;
+          float eg = 1.f;  // e^{g_t} (times 1 / ||q_t||: the update meets the raw q_t)
           if constexpr (DEC) eg = __expf(gs[t]);
+          if constexpr (QKN) eg *= p.rnq[it];
           typename RT::V pv, gv;
           E* pe = reinterpret_cast<E*>(&pv);
           E* ge = reinterpret_cast<E*>(&gv);
@@ -254,8 +265,9 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     const float gn = gs[CH - 1];
     // dR^T: the lane holds chunk row tl and four consecutive value columns
     const int tl = 16 * w + lrow();
-    float dec = 1.f;
+    float dec = 1.f;  // e^{g_n - g_t} (times 1 / ||k_t||: dW meets the raw k_t)
     if constexpr (DEC) dec = __expf(gn - gs[tl]);
+    if constexpr (QKN) dec *= p.rnk;
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const f32x4 a1 = mma_k<E, CH>(zero4(), colk(dOt, LDO), 16 * it, colk(Ms, LDR), 16 * w);
@@ -358,9 +370,10 @@ struct BwdLds {
 // RES: the residual r = R / beta was an output; dbeta gains -(dr . r) / beta = -(dr . R) / beta^2.
 // LOG: beta and alpha are logits x; the gradients returned are w.r.t. x:
 // dx_beta = dbeta beta (1 - beta), dx_alpha = d log(alpha) * (-sigmoid(x_alpha)).
-// QKN: q and k are the preparation's per-unit scaled copies x~ = x / ||x|| (rn = 1/||x|| per
-// token in Rn), and dq, dk are returned w.r.t. the raw rows: dx = (dx~ - x~ (x~ . dx~)) / ||x||,
-// formed in float32 before the gradients are rounded.
+// QKN: q and k are normalised per token, x~ = x / ||x||: the raw rows are read and scaled by
+// the preparation's factors rn = 1/||x|| (Rng) as the preparation scaled them, and dq, dk are
+// returned w.r.t. the raw rows: dx = (dx~ - x~ (x~ . dx~)) / ||x||, formed in float32 before the
+// gradients are rounded.
 template <typename E, int D, int VAR, bool RES, bool LOG, bool QKN>
 __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ v, const E* __restrict__ beta,
@@ -381,8 +394,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   constexpr bool GATED = VAR == VAR_GATED;
   __shared__ __align__(16) char smem[Ly::BIG];
   __shared__ __align__(16) float gs[CH], bs[CH], red[NT / 64];
-  __shared__ float part8[NT / CH][CH], part8b[NT / CH][CH], part8c[NT / CH][CH];  // partial sums
+  __shared__ float part8[NT / CH][CH], pdb[CH], part8c[NT / CH][CH];  // partial sums
   __shared__ float rq[4][CH], rkh[8][CH], rkb[8][CH];
+  __shared__ float rkn[QKN ? 8 : 1][CH];  // QKN: k~ . dk~ per row, the part of each wave
   __shared__ float rdr[RES ? CH : 1];  // dr_t . R_t (residual output)
   __shared__ float invq[QKN ? CH : 1], invk[QKN ? CH : 1];  // 1 / ||x|| of the rows of q and k
 
@@ -424,15 +438,20 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   RegTile<E, CH, D, NT> pV, pQ;       // V and Q, used in later phases
   RegTile<E, CH, CH, NT> pM;          // M, used for the decay gradient
   RegTile<float, CH, CH, NT> pLi;     // the forward's L^{-1}, used in phase 2
+  float rnq[decltype(pQ)::IT];        // QKN: 1 / ||q|| of the rows of pQ this thread holds
   // The per-token decay and beta are loaded before the tiles and staged after the first tile
   // stores: waiting for them then waits for nothing else, where loaded after the tiles they
   // would make the staging wait for every tile in flight (the wait counters are ordered).
-  float graw = 0.f;
+  float graw = 0.f, iqraw = 0.f, ikraw = 0.f;  // iqraw, ikraw: 1 / ||q||, 1 / ||k|| (QKN)
   E braw = E(0.f), araw = E(1.f);  // araw: alpha (or its logit) of this lane's token, for the end
   if (threadIdx.x < CH) {
     graw = Gg[u * CH + threadIdx.x];
     braw = beta[tk + min((int)threadIdx.x, n - 1)];
     if constexpr (GATED) araw = alpha[tk + min((int)threadIdx.x, n - 1)];
+    if constexpr (QKN) {
+      iqraw = Rng[u * 2 * CH + threadIdx.x];
+      ikraw = Rng[u * 2 * CH + CH + threadIdx.x];
+    }
   }
   {
     E* dOs = reinterpret_cast<E*>(smem + Ly::odO);
@@ -441,18 +460,24 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     E* dWh = reinterpret_cast<E*>(smem + Ly::odWh);
     {
       RegTile<E, CH, D, NT> r0, r1, r2, r3;
-      if constexpr (QKN) r0.load(k + u * CH * D, D, CH);
-      else r0.load(k + tk * D, D, n);
+      // QKN: the factors of the rows this thread holds, loaded first (the waits are ordered:
+      // loaded after the tiles, scaling K would wait for every tile in flight)
+      float rnk[decltype(r0)::IT];
+      if constexpr (QKN) {
+        load_row_factors(pQ, Rng + u * 2 * CH, rnq);
+        load_row_factors(r0, Rng + u * 2 * CH + CH, rnk);
+      }
+      r0.load(k + tk * D, D, n);
       r1.load(dO + tk * D, D, n);
       r2.load(Rg + u * CH * D, D, CH);
       r3.load(dRg + u * CH * D, D, CH);
       pW.load(Hs + u * D * D, D, KH);
       pdW.load(dHs + u * D * D, D, KH);
       pV.load(v + tk * D, D, n);
-      if constexpr (QKN) pQ.load(q + u * CH * D, D, CH);
-      else pQ.load(q + tk * D, D, n);
+      pQ.load(q + tk * D, D, n);
       pM.load(Mg + u * CH * CH, CH, CH);
       pLi.load(Lig + u * CH * CH, CH, CH);
+      if constexpr (QKN) scale_rows(r0, rnk);
       if constexpr (RES) {  // dr_t . R_t per row, from the registers: a row is VPR adjacent lanes
         RegTile<E, CH, D, NT> rd;
         rd.load(drin + tk * D, D, n);
@@ -478,8 +503,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
       gs[t] = graw;
       bs[t] = (t < n) ? (LOG ? gate_sigmoid((float)braw) : (float)braw) : 0.f;
       if constexpr (QKN) {
-        invq[t] = Rng[u * 2 * CH + t];
-        invk[t] = Rng[u * 2 * CH + CH + t];
+        invq[t] = iqraw;
+        invk[t] = ikraw;
       }
     }
     for (int ih = 0; ih < NH; ++ih) {
@@ -689,7 +714,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     float a = l0.x * a0.x + l0.y * a0.y + l0.z * a0.z + l0.w * a0.w + l1.x * a1.x + l1.y * a1.y + l1.z * a1.z +
               l1.w * a1.w;
     a = group_sum_dpp<8>(a);
-    if ((threadIdx.x & 7) == 0) part8b[0][t] = a;
+    if ((threadIdx.x & 7) == 0) pdb[t] = a;
   }
 
   // ================= phase 3: Gram slots and the decay gradient
@@ -697,6 +722,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   E* Ats = reinterpret_cast<E*>(smem + Ly::oAt);
   E* Mts = reinterpret_cast<E*>(smem + Ly::oMt);
   float* Pair = reinterpret_cast<float*>(smem + Ly::oPair);
+  if constexpr (QKN) scale_rows(pQ, rnq);
   pQ.store(Qs, LD);
   // Each thread handles the (t, s) entries of M it holds in registers.
   {  // VE consecutive columns per thread: vector LDS reads and writes
@@ -787,6 +813,17 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
     dka[qq] = mma_k<E, CH>(dka[qq], colk(Ks, LD), 16 * nt, colk(Ats, LDR), 16 * wm);
     dka[qq] = mma_k<E, CH>(dka[qq], colk(Qs, LD), 16 * nt, colk(Mts, LDR), 16 * wm);
   }
+  if constexpr (QKN) {  // dk~ is complete: k~ . dk~ over this wave's columns of rows tr (a row's
+    // columns are split over waves w and w ^ 4), summed after the next barrier
+    float part = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+      const f32x4 kv = get4(Ks + tr * LD + 16 * (wn * NQ + qq) + 4 * lgrp());
+      part += kv[0] * dka[qq][0] + kv[1] * dka[qq][1] + kv[2] * dka[qq][2] + kv[3] * dka[qq][3];
+    }
+    part = sum_rows4(part);
+    if (lgrp() == 0) rkn[w][tr] = part;
+  }
   if constexpr (GATED) {  // prefix sums along each row of the pair terms: lanes over columns
 #pragma unroll
     for (int i = 0; i < CH / (NT / 64); ++i) {  // rows w, w + 8, ...: independent, interleaved
@@ -797,6 +834,13 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   __syncthreads();
   GDR_POISON(smem + Ly::odR, 2 * Ly::SQ);  // At, Mt and Q are no longer read
   GDR_POISON(Qs, Ly::TK);
+  if constexpr (QKN) {  // dk w.r.t. the raw rows: dk = (dk~ - k~ (k~ . dk~)) / ||k|| (dq was done above)
+    const float dot = rkn[wm][tr] + rkn[wm + 4][tr];
+    const float rn = invk[tr];
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq)
+      dka[qq] = (dka[qq] - dot * get4(Ks + tr * LD + 16 * (wn * NQ + qq) + 4 * lgrp())) * rn;
+  }
   if constexpr (GATED) {  // rectangle sums: sum over u >= t of the prefix at column t-1
     const int t = threadIdx.x & (CH - 1), pt = threadIdx.x >> 6;
     float a = 0.f;
@@ -811,27 +855,6 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
   }
   __syncthreads();
   GDR_POISON(smem + Ly::oPair, Ly::F);  // the pair terms are no longer read
-  if constexpr (QKN) {  // dk w.r.t. the raw rows: dk = (dk~ - k~ (k~ . dk~)) / ||k|| (dq was done above)
-    // k~ . dk~ per row: a row's columns are split over waves w and w ^ 4; the partial sums go
-    // through the pair-term region, no longer read
-    float* rkn = reinterpret_cast<float*>(smem + Ly::oPair);
-    {
-      float part = 0.f;
-#pragma unroll
-      for (int qq = 0; qq < NQ; ++qq) {
-        const f32x4 kv = get4(Ks + tr * LD + 16 * (wn * NQ + qq) + 4 * lgrp());
-        part += kv[0] * dka[qq][0] + kv[1] * dka[qq][1] + kv[2] * dka[qq][2] + kv[3] * dka[qq][3];
-      }
-      part = sum_rows4(part);
-      if (lgrp() == 0) rkn[w * CH + tr] = part;
-    }
-    __syncthreads();
-    const float dot = rkn[wm * CH + tr] + rkn[(wm + 4) * CH + tr];
-    const float rn = invk[tr];
-#pragma unroll
-    for (int qq = 0; qq < NQ; ++qq)
-      dka[qq] = (dka[qq] - dot * get4(Ks + tr * LD + 16 * (wn * NQ + qq) + 4 * lgrp())) * rn;
-  }
   // outputs: dq, dk through LDS (the dR/dX regions are free now)
   E* sq = reinterpret_cast<E*>(smem + Ly::odR);
   E* sk = reinterpret_cast<E*>(smem + Ly::odX);
@@ -866,7 +889,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(Geo geo, const E* __restrict_
         else dalpha[tk + t] = (E)(dla / (float)araw);
       }
     }
-    float db = part8b[0][t];
+    float db = pdb[t];
 #pragma unroll
     for (int i = 0; i < NT / CH; ++i) db += part8c[i][t];
     if constexpr (RES) {
@@ -906,7 +929,7 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
                                                        const E* __restrict__ drin, const E* __restrict__ beta,
                                                        const float* __restrict__ Ag, const E* __restrict__ k,
                                                        const float* __restrict__ Gg, const float* __restrict__ Lig,
-                                                       E* __restrict__ dbeta) {
+                                                       E* __restrict__ dbeta, const float* __restrict__ Rng) {
   GDR_POISON_ALL();
   constexpr int NT = 512, LD = D + pad16<E>(), LF = CH + 4, NW = NT / 64;
   constexpr int NH = D / 32;  // column tiles of a 64 x D product per wave (two waves per row block)
@@ -928,9 +951,10 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
   {
     RegTile<E, CH, D, NT> rR, rO, rd, rk;
     RegTile<float, CH, CH, NT> rA, rL;
+    float rnk[decltype(rk)::IT];  // QKN: 1 / ||k|| of the rows of rk this thread holds
     if constexpr (OWN_A) {
-      if constexpr (QKN) rk.load(k + u * CH * D, D, CH);  // the forward's scaled keys
-      else rk.load(k + tk * D, D, n);
+      if constexpr (QKN) load_row_factors(rk, Rng + u * 2 * CH + CH, rnk);  // before the tiles
+      rk.load(k + tk * D, D, n);
     } else {
       rA.load(Ag + u * CH * CH, CH, CH);
     }
@@ -938,7 +962,10 @@ __global__ __launch_bounds__(512) void k_bwd_res_dbeta(Geo geo, const E* __restr
     rO.load(dRog + u * CH * D, D, CH);
     rL.load(Lig + u * CH * CH, CH, CH);
     rd.load(drin + tk * D, D, n);
-    if constexpr (OWN_A) rk.store(Ys, LD);  // K, in the region Y takes later
+    if constexpr (OWN_A) {  // K (scaled to unit length as the forward scaled it), in the region Y takes later
+      if constexpr (QKN) scale_rows(rk, rnk);
+      rk.store(Ys, LD);
+    }
     rR.store(Rs, LD);
     rO.store(dRos, LD);
     if (threadIdx.x < CH) {
@@ -1095,8 +1122,8 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
   const Geo& g = p.geo;
   constexpr bool KDA = VAR == VAR_KDA;
   constexpr bool PCH = KDA || VAR == VAR_GLA;  // decay per key channel: per-unit operands
-  const E* qin = PCH ? (const E*)p.Qh : p.qkn ? (const E*)p.Qn : (const E*)in.q;
-  const E* kin = PCH ? (const E*)p.Kb : p.qkn ? (const E*)p.Kn : (const E*)in.k;
+  const E* qin = PCH ? (const E*)p.Qh : (const E*)in.q;
+  const E* kin = PCH ? (const E*)p.Kb : (const E*)in.k;
   const float* gin = PCH ? p.Gn : p.G;
   // residual gradient: delta family and Kimi Delta Attention (whose residual has the same form)
   constexpr bool RES_OK = VAR == VAR_DELTANET || VAR == VAR_GATED || KDA;
@@ -1110,7 +1137,7 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
     const int ny = (sg.mode == 1 || sg.mode == 2) ? sg.max_seg : 1;  // mode 3: one segment per sequence
     hipLaunchKernelGGL(kern, dim3(scan_grid(g, nv_mult * D / bv), ny), dim3(256), 0, st, g, sg,
                        qin, kin, (const E*)dO, (const E*)p.X, (const E*)p.M, gin, dhtp, (E*)p.dHs, (E*)p.dR, dh0p,
-                       (const E*)in.beta, (const E*)in.erase, d, d ? dro : nullptr);
+                       (const E*)in.beta, (const E*)in.erase, d, d ? dro : nullptr, (const float*)p.Rn);
   };
   constexpr bool QOK = VAR == VAR_DELTANET || VAR == VAR_GATED;  // fused q/k normalisation
   auto scan_q = [&](auto qkn, const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult) {
@@ -1217,7 +1244,7 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
         auto res = [&](auto kern) {
           hipLaunchKernelGGL(kern, dim3(g.total_chunks, g.H), dim3(512), 0, st, g, (const E*)p.R,
                              (const E*)dro, drp, (const E*)in.beta, (const float*)p.A1, kin, gin,
-                             (const float*)p.Li, (E*)gr.dbeta);
+                             (const float*)p.Li, (E*)gr.dbeta, (const float*)p.Rn);
         };
         if constexpr (QOK) {
           if (p.qkn) res(k_bwd_res_dbeta<E, D, true, true>);

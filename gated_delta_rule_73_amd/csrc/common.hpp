@@ -423,6 +423,26 @@ __device__ __forceinline__ void normalize_rows(RegTile<S, ROWS, COLS, NT>& t, fl
   }
 }
 
+// The factors normalize_rows wrote for the rows this thread holds of a tile (inv: one float per
+// row), and the tile's rows scaled by them with normalize_rows' own arithmetic: raw rows scaled
+// this way are the normalised rows, bit for bit.
+template <typename S, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void load_row_factors(const RegTile<S, ROWS, COLS, NT>& t, const float* inv,
+                                                 float (&rn)[RegTile<S, ROWS, COLS, NT>::IT]) {
+#pragma unroll
+  for (int it = 0; it < RegTile<S, ROWS, COLS, NT>::IT; ++it) rn[it] = inv[min(t.row(it), ROWS - 1)];
+}
+template <typename S, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void scale_rows(RegTile<S, ROWS, COLS, NT>& t, const float (&rn)[RegTile<S, ROWS, COLS, NT>::IT]) {
+  using RT = RegTile<S, ROWS, COLS, NT>;
+#pragma unroll
+  for (int it = 0; it < RT::IT; ++it) {
+    S* e = reinterpret_cast<S*>(&t.v[it]);
+#pragma unroll
+    for (int x = 0; x < RT::VE; ++x) e[x] = (S)((float)e[x] * rn[it]);
+  }
+}
+
 // LDS[r*ld + c] = G[r*gs + c] for r < nrows, 0 for nrows <= r < ROWS; c < COLS.
 template <typename S, int ROWS, int COLS, int NT>
 __device__ __forceinline__ void g2s_rows(S* lds, int ld, const S* g, long gs, int nrows) {

@@ -21,16 +21,15 @@ namespace gdr {
 // Prep: per (head, chunk) -- g, M, L^{-1}, X, U.
 // ---------------------------------------------------------------------------------------
 // LOG: beta and alpha are logits (beta = sigmoid(x), log alpha = -softplus(x)).
-// QKN: q and k are scaled to unit length per token as they are loaded (normalize_rows); the
-// scaled tiles (zero past the sequence's end) and 1/||q||, 1/||k|| are kept per unit in Qno,
-// Kno, Rno, and every later kernel reads those instead of q and k.
+// QKN: q and k are scaled to unit length per token as they are loaded (normalize_rows), and
+// 1/||q||, 1/||k|| are kept per unit in Rno (zero for a zero row and past the sequence's end);
+// the later kernels read the raw rows and apply those factors themselves.
 template <typename E, int D, int VAR, bool LOG, bool QKN>
 __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ v, const E* __restrict__ beta,
                                                   const E* __restrict__ alpha, E* __restrict__ Xo,
                                                   E* __restrict__ Uo, E* __restrict__ Mo, float* __restrict__ Go,
-                                                  float* __restrict__ Lio, E* __restrict__ Qno, E* __restrict__ Kno,
-                                                  float* __restrict__ Rno) {
+                                                  float* __restrict__ Lio, float* __restrict__ Rno) {
   GDR_POISON_ALL();
   constexpr int NT = 256, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   // Three 64-row buffers (about 52 KiB, so three workgroups share a CU):
@@ -64,8 +63,6 @@ __global__ __launch_bounds__(256) void k_fwd_prep(Geo geo, const E* __restrict__
   if constexpr (QKN) {
     normalize_rows(rq, Rno + u * 2 * CH);
     normalize_rows(rk, Rno + u * 2 * CH + CH);
-    rq.store_global(Qno + u * CH * D, D);
-    rk.store_global(Kno + u * CH * D, D);
   }
   rk.store(Ks, LD);
   rq.store(QV, LD);
@@ -222,10 +219,13 @@ struct FwdScanOps {
   uint32_t braw2;  // Gated DeltaNet-2: beta of this lane's token as loaded (0 if absent or past the end)
   f32x4 eg[D / 64];
   E braw;  // residual output: beta of this lane's token, as loaded (converted where it is used)
+  float rnq, rnk;  // fused q/k normalisation: 1 / ||q||, 1 / ||k|| of chunk row 16 w + lrow
 };
 
-// QKN (delta family): q and k are the preparation's per-unit scaled copies (unit length per
-// token, zero past the end), read like Kimi Delta Attention's per-unit operands.
+// QKN (delta family): q and k are normalised to unit length per token.  The raw rows are read
+// and the preparation's factors Rng (1 / ||q||, 1 / ||k|| per unit) are applied where a row
+// enters a product: to the output's row (Q W0^T) and to the rows of e^{g_n-g} R that meet K in
+// the memory update.
 template <typename E, int D, int BV, int VAR, bool FULL, bool RES, bool QKN>
 __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ k, const E* __restrict__ Xg,
                                                   const E* __restrict__ Ug, const float* __restrict__ Gg,
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
                                                   const E* __restrict__ erase, const E* __restrict__ write,
                                                   const E* __restrict__ q, const E* __restrict__ Mg,
                                                   const E* __restrict__ M2g, E* __restrict__ o,
-                                                  E* __restrict__ rout) {
+                                                  E* __restrict__ rout, const float* __restrict__ Rng) {
   GDR_POISON_ALL();
   constexpr int NT = 256, LD = D + pad16<E>(), LDV = BV + pad16<E>(), LDR = CH + pad16<E>();
   constexpr int NJ = D / 64, NI = BV / 16;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     }
     if (part < 0 || part == 1) {
       if constexpr (FULL) {
-        p.q.load(q + ((KDA || QKN) ? u * CH : tk) * D, D, (KDA || QKN) ? CH : n);
+        p.q.load(q + (KDA ? u * CH : tk) * D, D, KDA ? CH : n);
         p.m.load(Mg + u * CH * CH, CH, CH);
         if constexpr (G2) p.m2.load(M2g + u * CH * CH, CH, CH);
       }
@@ -335,8 +335,12 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       if constexpr (KDA) {
         p.k.load(k + u * CH * D, D, CH);
       } else {
-        p.k.load(k + (QKN ? u * CH : tk) * D, D, QKN ? CH : n);
+        p.k.load(k + tk * D, D, n);
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
+        if constexpr (QKN) {  // for the row this lane holds in R^T and O^T (read before the next refill)
+          p.rnq = Rng[u * 2 * CH + 16 * w + lrow()];
+          p.rnk = Rng[u * 2 * CH + CH + 16 * w + lrow()];
+        }
       }
       if constexpr (RES) {  // a plain load (valid row), no arithmetic on it until the step uses it
         const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
@@ -416,8 +420,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     const float gn = gs[CH - 1];
     // R^T = U^T - W X^T: the lane holds chunk row tl and four consecutive value columns
     const int tl = 16 * w + lrow();
-    float dec = 1.f;
+    float dec = 1.f;  // e^{g_n - g_t} (times 1 / ||k_t||: the row of R that meets the raw k_t)
     if constexpr (DEC) dec = __expf(gn - gs[tl]);
+    if constexpr (QKN) dec *= p.rnk;
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       f32x4 acc = zero4();
@@ -441,8 +446,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
           const f32x4 a1 = mma_k<E, D>(zero4(), rowk(Ws, LD), 16 * it, rowk(Qs, LD), 16 * w);
           f32x4 a2 = mma_k<E, CH>(zero4(), colk(Rn, LDV), 16 * it, rowk(Ms, LDR), 16 * w);
           if constexpr (G2) a2 = mma_k<E, CH>(a2, colk(Bn, LDV), 16 * it, rowk(M2s, LDR), 16 * w);
-          float e = 1.f;
+          float e = 1.f;  // e^{g_t} (times 1 / ||q_t||: the product used the raw q_t)
           if constexpr (DEC) e = __expf(gs[tl]);
+          if constexpr (QKN) e *= p.rnq;
           put4(Os + tl * LDV + 16 * it + 4 * lgrp(), geo.scale * (e * a1 + a2));
         }
       }
@@ -518,8 +524,7 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
       TraceScope ts_("fwd_prep", st);
       auto prep = [&](auto kern) {
         hipLaunchKernelGGL(kern, cgrid, dim3(256), 0, st, g, (const E*)in.q, (const E*)in.k, (const E*)in.v,
-                           (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G, p.Li,
-                           (E*)p.Qn, (E*)p.Kn, p.Rn);
+                           (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub, (E*)p.M, p.G, p.Li, p.Rn);
       };
       if (p.qkn) {
         if (p.gates) prep(k_fwd_prep<E, D, VAR, true, true>);
@@ -531,8 +536,8 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
     }
   }
   constexpr bool KDA = VAR == VAR_KDA || VAR == VAR_GLA;
-  const E* kin = KDA ? (const E*)p.Kb : p.qkn ? (const E*)p.Kn : (const E*)in.k;
-  const E* qin = KDA ? (const E*)p.Qh : p.qkn ? (const E*)p.Qn : (const E*)in.q;
+  const E* kin = KDA ? (const E*)p.Kb : (const E*)in.k;
+  const E* qin = KDA ? (const E*)p.Qh : (const E*)in.q;
   const float* gin = KDA ? p.Gn : p.G;
   E* out = want_out ? (E*)o : nullptr;
   E* rout = (want_out && r) ? (E*)r : nullptr;
@@ -540,7 +545,7 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
     hipLaunchKernelGGL(kern, dim3(scan_grid(g, nvm * D / bv), sg.mode ? sg.max_seg : 1), dim3(256), 0, st, g, sg, kin,
                        (const E*)p.X, (const E*)p.Ub, gin, h0, (E*)p.Hs, (E*)p.R, htp, (const E*)in.v,
                        (const E*)in.beta, (const E*)in.erase, (const E*)in.write, qin, (const E*)p.M, (const E*)p.M2,
-                       out, rr);
+                       out, rr, (const float*)p.Rn);
   };
   auto scan_q = [&](auto full, auto qkn, const ScanSeg& sg, const float* h0, float* htp) {
     constexpr bool F = decltype(full)::value;

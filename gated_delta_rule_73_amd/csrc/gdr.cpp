@@ -43,10 +43,10 @@ struct Sizes {
   int lseg_b = 0, max_seg_b = 1;       // backward segmented scans
   int ts_lseg = 0, ts_parts = 0;       // time-split backward (see ts_length)
   size_t X, M, G, Hs, R, M2, U2, Li, A1, A2, Kb, Qh, Gn, Ub, dHs, dR, g2, seg;
-  size_t Qn = 0, Kn = 0, Rn = 0;  // q/k normalisation of the delta family: scaled copies, inverse norms
+  size_t Rn = 0;  // q/k normalisation of the delta family: the inverse norms
   size_t qn = 0;  // with qk_norm outside the kernels: the normalised q and k (after the cache)
   bool qkn = false;  // with qk_norm: the kernels normalise q and k as they load them
-  size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Li + A1 + A2 + Kb + Qh + Gn + Qn + Kn + Rn; }
+  size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Li + A1 + A2 + Kb + Qh + Gn + Rn; }
   size_t fwd_ws() const { return Ub + seg; }                   // workspace before the cache
   size_t bwd_ws() const { return Ub + dHs + dR + g2 + seg; }
 };
@@ -202,14 +202,11 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   const size_t nst = std::max(3 * ms, (size_t)s.ts_parts);
   s.seg = nst ? align_up((size_t)s.nstates * p->H * nst * D * D * 4, A) : 0;
   // q/k normalisation: the delta family's preparation kernel normalises the rows it loads and
-  // keeps per-chunk copies (and the inverse norms) in the cache for the scans and the backward;
-  // Kimi Delta Attention and Gated DeltaNet-2 normalise into workspace copies first
+  // keeps the inverse norms in the cache, with which the scans and the backward scale the raw
+  // rows themselves; Kimi Delta Attention and Gated DeltaNet-2 normalise into workspace copies first
   s.qkn = p->qk_norm && (p->variant == GDR_DELTANET || p->variant == GDR_GATED);
   s.qn = (p->qk_norm && !s.qkn) ? 2 * align_up((size_t)p->B * p->H * p->T * D * s.esz, A) : 0;
-  if (s.qkn) {
-    s.Qn = s.Kn = align_up(U * C * D * s.esz, A);
-    s.Rn = align_up(U * 2 * C * 4, A);
-  }
+  if (s.qkn) s.Rn = align_up(U * 2 * C * 4, A);
   *sz = s;
   return GDR_OK;
 }
@@ -275,8 +272,6 @@ gdr::Plan make_plan(const gdr_problem* p, const Sizes& s, char* cache, char* ws,
   pl.Kb = c; c += s.Kb;
   pl.Qh = c; c += s.Qh;
   pl.Gn = reinterpret_cast<float*>(c); c += s.Gn;
-  pl.Qn = s.Qn ? c : nullptr; c += s.Qn;
-  pl.Kn = s.Kn ? c : nullptr; c += s.Kn;
   pl.Rn = s.Rn ? reinterpret_cast<float*>(c) : nullptr; c += s.Rn;
   char* w = ws;
   pl.Ub = w; w += s.Ub;
@@ -446,8 +441,6 @@ gdr::Plan sub_plan(const gdr::Plan& pl, const gdr_problem* p, const Sizes& s, co
   q.Ub = adv(q.Ub, C * D * e);
   q.dHs = adv(q.dHs, D * D * e);
   q.dR = adv(q.dR, C * D * e);
-  q.Qn = adv(q.Qn, C * D * e);
-  q.Kn = adv(q.Kn, C * D * e);
   q.Rn = adv(q.Rn, 2 * C * 4);
   return q;
 }

@@ -90,11 +90,14 @@ typedef struct {
   int32_t qk_norm;                /* 0: q and k are used as given.  1: each token's q and k are
                                      first scaled to unit length over d_k (x / ||x||_2, a zero
                                      row left zero) and dq, dk are gradients w.r.t. the raw q, k.
-                                     Runs as passes before the forward and backward and after the
-                                     backward (their copies take 2 B H T d_k elements of
-                                     workspace, counted by gdr_workspace_size).  Every variant in
-                                     gdr_forward and gdr_backward; gdr_decode returns
-                                     UNSUPPORTED (normalise there before the call) */
+                                     DeltaNet and Gated DeltaNet do it inside their kernels (the
+                                     inverse norms, 2 floats per token and head, are part of the
+                                     saved cache); the other variants run passes before the
+                                     forward and backward and after the backward (their copies
+                                     take 2 B H T d_k elements of workspace, counted by
+                                     gdr_workspace_size).  Every variant in gdr_forward and
+                                     gdr_backward; gdr_decode returns UNSUPPORTED (normalise
+                                     there before the call) */
 } gdr_problem;
 
 typedef struct {
