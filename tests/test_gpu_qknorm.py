@@ -95,3 +95,15 @@ def test_qk_norm_with_residual(variant):
     ref = {"o": oo, "ht": hh, "r": rr}
     ref.update(R.backward(**kw, do=inp["do"], dr=dr, variant=variant, qk_l2norm=True))
     compare(got, ref, "bf16")
+
+
+@pytest.mark.parametrize("env", [{"GDR_SCAN_BV": "32"}, {"GDR_PIPELINE": "1", "GDR_TSPLIT_CHUNKS": "3"}],
+                         ids=["bv32", "time-split"])
+def test_qk_norm_scan_tiles_and_time_split(monkeypatch, env):
+    """The normalisation factors through the 32-row value-tile scans (the instantiation the
+    32k-token workloads run) and through the time-split backward (one long sequence whose chunk
+    gradients run part by part)."""
+    for k_, v_ in env.items():
+        monkeypatch.setenv(k_, v_)
+    inp = _inputs("gated", "bf16", 128, T=600, B=1, H=2)
+    compare(_hip(inp, "gated", "bf16", True), _oracle(inp, "gated"), "bf16")
