@@ -16,7 +16,9 @@ against MI355X's 8 TB/s: its algorithmic bytes (the operator's own tensors it re
 each once; no per-chunk intermediate) over its average launch time, timed with HIP events
 around its launches in every fourth step of a separate single-stream pass (the last included),
 where no launch overlaps another; `io_bytes`/`io_frac` beside it count everything the kernel
-moves, intermediates included.
+moves, intermediates included; `measured_copy_GBps` is what a plain 1 GiB device copy reaches
+on the same GPU (the practical ceiling beside the published peak) and `frac_of_measured_copy`
+the kernel's algorithmic rate against it.  `device` names the GPU as the runtime reports it.
 `path_roofline` is the whole step against the bytes the operator must move at minimum.
 `sweep` times T = 4k..32k at B*T = 32768 (ratio t(32k)/t(4k) beside the pages' ~1.1x);
 `ms_per_step_flushed` times steps separated by a 512 MiB write that evicts the last-level cache.
@@ -384,6 +386,7 @@ def bench_decode(args, w):
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     runner = DecodeRunner(w, inp)
+    copy_gbs = measured_copy_gbs()
     print("[bench] timing", file=sys.stderr, flush=True)
     ms, per_kernel = timed(runner, args.steps, args.warmup)
     esz = 2 if w.dtype == "bf16" else 4
@@ -402,7 +405,9 @@ def bench_decode(args, w):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("decode", w.name),
                      "avg_launch_ms": round(avg_ms, 4), "launches": len(per_kernel["decode"]),
-                     "algorithmic_bytes_per_launch": nbytes},
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "measured_copy_GBps": round(copy_gbs, 1), "frac_of_measured_copy": round(achieved / copy_gbs, 4)},
+        "device": device_info(),
     }
     if cpu is not None:
         out["cpu_baseline"] = cpu
@@ -468,6 +473,34 @@ def timed(runner, steps: int, warmup: int, trace: bool = True, trace_every: int 
 
 
 FLUSH_BYTES = 512 << 20  # twice MI355X's 256 MiB last-level (Infinity) cache
+COPY_BW_BYTES = 1 << 30  # the bandwidth copy: four times the last-level cache
+
+
+def device_info() -> dict:
+    """The GPU the line was measured on, as the runtime reports it."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "memory_GiB": round(pr.total_memory / (1 << 30), 1)}
+
+
+def measured_copy_gbs(reps: int = 10) -> float:
+    """HBM bandwidth a plain device-to-device copy reaches on this GPU (read + write bytes over
+    the median time of `reps` copies of 1 GiB), the practical ceiling beside the published peak."""
+    import torch
+    src = torch.empty(COPY_BW_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    evs = make_events(2 * reps)
+    for i in range(reps):
+        evs[2 * i].record()
+        dst.copy_(src)
+        evs[2 * i + 1].record()
+    torch.cuda.synchronize()
+    ms = sorted(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(reps))[reps // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * COPY_BW_BYTES / (ms / 1e3) / 1e9
 
 
 def timed_flushed(runner, steps: int) -> float:
@@ -527,6 +560,7 @@ def main():
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+    copy_gbs = measured_copy_gbs()
     # Per-kernel launch durations (and the roofline) come from a traced pass with the backward's
     # pipelines off, where no launch overlaps another; the headline step time from an untraced
     # pass with them on (GDR_PIPELINE=1: side streams overlap the reverse scans with the chunk
@@ -579,10 +613,12 @@ def main():
                      "traffic": traffic, "avg_launch_ms": round(avg_ms, 4), "launches": launches,
                      "timed_in": "single-stream traced pass",
                      "algorithmic_bytes_per_launch": algo,
-                     "io_bytes": io, "io_achieved": round(io_gbs, 1), "io_frac": round(io_gbs / HBM_PEAK_GBS, 4)},
+                     "io_bytes": io, "io_achieved": round(io_gbs, 1), "io_frac": round(io_gbs / HBM_PEAK_GBS, 4),
+                     "measured_copy_GBps": round(copy_gbs, 1), "frac_of_measured_copy": round(achieved / copy_gbs, 4)},
         "path_roofline": {"bound": "hbm", "algorithmic_bytes_per_step": path_bytes, "achieved": round(path_gbs, 1),
                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
         "kernels_ms_per_step": {k: round(v / traced_steps(args.steps), 4) for k, v in tot.items()},
+        "device": device_info(),
     }
     del runner
     torch.cuda.empty_cache()
