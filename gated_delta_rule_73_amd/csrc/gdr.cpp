@@ -201,10 +201,12 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   const size_t ms = (size_t)std::max(s.lseg ? s.max_seg : 0, s.lseg_b ? s.max_seg_b : 0);
   const size_t nst = std::max(3 * ms, (size_t)s.ts_parts);
   s.seg = nst ? align_up((size_t)s.nstates * p->H * nst * D * D * 4, A) : 0;
-  // q/k normalisation: the delta family's preparation kernel normalises the rows it loads and
-  // keeps the inverse norms in the cache, with which the scans and the backward scale the raw
-  // rows themselves; Kimi Delta Attention and Gated DeltaNet-2 normalise into workspace copies first
-  s.qkn = p->qk_norm && (p->variant == GDR_DELTANET || p->variant == GDR_GATED);
+  // q/k normalisation: the preparation kernel of the delta family, of Kimi Delta Attention and of
+  // the erase-free variant normalises the rows it loads and keeps the inverse norms in the cache,
+  // with which the later kernels scale the raw rows themselves (the delta family's chunk backward
+  // also maps dq, dk back to the raw rows; the per-channel variants leave that to a pass after the
+  // backward); Gated DeltaNet-2 normalises into workspace copies first
+  s.qkn = p->qk_norm && p->variant != GDR_GDN2;
   s.qn = (p->qk_norm && !s.qkn) ? 2 * align_up((size_t)p->B * p->H * p->T * D * s.esz, A) : 0;
   if (s.qkn) s.Rn = align_up(U * 2 * C * 4, A);
   *sz = s;
@@ -675,7 +677,7 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
     }
     st = hip_status(gdr::run_backward(pl, ins, dO, dr, dht, *g, hs), "gdr_backward launch");
   }
-  if (st != GDR_OK || !p->qk_norm || s.qkn) return st;
+  if (st != GDR_OK || !p->qk_norm || (s.qkn && (p->variant == GDR_DELTANET || p->variant == GDR_GATED))) return st;
   // gradients w.r.t. the raw q and k, through the normalisation
   const long rows = (long)p->B * p->H * p->T;
   st = hip_status(gdr::run_l2norm(p->dtype, p->dk, in->q, g->dq, rows, true, hs), "gdr_backward q normalisation");

@@ -84,11 +84,13 @@ __device__ void kda_flags(const float* Gs, int ldg, int* unsafe) {
 // (ref = the first token of the row's 16-token block), Gs, unsafe flags; Cl is scratch.
 // Outputs: Ls[t][s] = lsc_t A_ts below the diagonal, optionally (Af != NULL) Af[t*ldaf + s] = A_ts
 // (zero on and above the diagonal), Mo[t][s] = M_ts (global, zero above the diagonal).
-// qg: Q in global memory (token rows, used only for exact diagonal blocks).  Ends with a barrier.
-// WITH_A = false (nothing erased): M only; Ls and Af are not touched.
+// qg: Q in global memory (token rows, used only for exact diagonal blocks); qinv, if not NULL,
+// 1 / ||q|| per row, with which those rows are scaled as normalize_rows scaled the tile's.
+// Ends with a barrier.  WITH_A = false (nothing erased): M only; Ls and Af are not touched.
 template <typename E, int D, int NT, bool WITH_M, bool WITH_A = true>
 __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const float* Gs, const int* unsafe,
-                          float* Ls, const float* lsc, float* Af, int ldaf, E* Mo, const E* qg, int n) {
+                          float* Ls, const float* lsc, float* Af, int ldaf, E* Mo, const E* qg, int n,
+                          const float* qinv) {
   static_assert(WITH_A || WITH_M, "at least one Gram");
   constexpr int LD = D + pad16<E>(), LDG = D + 4, LF = CH + 4;
   const int w = wave_id();
@@ -177,7 +179,11 @@ __device__ void kda_grams(const E* Ks, const E* Qr, const E* Kr, E* Cl, const fl
         const float e = __expf(Gs[t * LDG + j] - Gs[s * LDG + j]);
         const float ks = (float)Ks[s * LD + j];
         a += (float)Ks[t * LD + j] * ks * e;
-        if constexpr (WITH_M) m += (t < n ? (float)qg[(long)t * D + j] : 0.f) * ks * e;
+        if constexpr (WITH_M) {
+          float qv = t < n ? (float)qg[(long)t * D + j] : 0.f;
+          if (qinv) qv = (float)(E)(qv * qinv[t]);
+          m += qv * ks * e;
+        }
       }
       if constexpr (WITH_A) {
         if (s < t) {
@@ -211,18 +217,24 @@ struct KdaPrepLds {
 
 // LOG: beta and alpha are logits (beta = sigmoid(x), log alpha = -softplus(x) per channel).
 // EF: nothing erased (see the top of this file); beta may be NULL (1).
+// Rno (q/k normalisation; NULL without): q and k are scaled to unit length per token as they are
+// loaded (normalize_rows), so Kbar, Qhat and every product here take the normalised rows, and
+// 1/||q||, 1/||k|| are kept per unit in Rno (zero past the end) for the backward stages, which
+// scale the raw rows they load with them.
 template <typename E, int D, bool LOG, bool EF>
 __global__ __launch_bounds__(512) void k_fwd_prep_kda(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ v, const E* __restrict__ beta,
                                                       const E* __restrict__ alpha, E* __restrict__ Xo,
                                                       E* __restrict__ Uo, E* __restrict__ Mo, E* __restrict__ Kbo,
                                                       E* __restrict__ Qho, float* __restrict__ Gno,
-                                                      float* __restrict__ Lio, float* __restrict__ Ao) {
+                                                      float* __restrict__ Lio, float* __restrict__ Ao,
+                                                      float* __restrict__ Rno) {
   GDR_POISON_ALL();
   using Ly = KdaPrepLds<E, D>;
   constexpr int NT = 512, LD = Ly::LD, LDG = Ly::LDG, LF = Ly::LF, LDT = Ly::LDT;
   __shared__ __align__(16) char smem[Ly::BYTES];
   __shared__ float bs[CH];
+  __shared__ float rnq[CH];  // Rno given: 1 / ||q|| per token
   __shared__ int unsafe[4];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
   E* Kr = reinterpret_cast<E*>(smem + Ly::oKr);
@@ -246,6 +258,10 @@ __global__ __launch_bounds__(512) void k_fwd_prep_kda(Geo geo, const E* __restri
   rq.load(q + tk * D, D, n);
   rv.load(v + tk * D, D, n);
   if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
+  if (Rno) {  // q and k scaled to unit length per token; 1 / ||k|| straight to Rno, 1 / ||q|| via LDS
+    normalize_rows(rq, rnq);
+    normalize_rows(rk, Rno + u * 2 * CH + CH);
+  }
   rk.store(Ks, LD);
   rq.store(Qs, LD);
   if (threadIdx.x < CH) {
@@ -255,6 +271,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep_kda(Geo geo, const E* __restri
     bs[threadIdx.x] = b;
   }
   kda_cumlog<E, D, NT, LOG>(ra, n, Gs, LDG);
+  if (Rno && threadIdx.x < CH) Rno[u * 2 * CH + threadIdx.x] = rnq[threadIdx.x];
   kda_flags<D, NT>(Gs, LDG, unsafe);
 
   // Kbar and Qhat for the scans, e^{g_n} per channel, and the row
@@ -294,7 +311,8 @@ __global__ __launch_bounds__(512) void k_fwd_prep_kda(Geo geo, const E* __restri
   E* Mc = Mo + u * CH * CH;
   if constexpr (EF) {
     // M only; nothing erased, so L = I and U = diag(beta) V (rows past the end load as zero)
-    kda_grams<E, D, NT, true, false>(Ks, Qs, Kr, Cl, Gs, unsafe, nullptr, bs, nullptr, CH, Mc, q + tk * D, n);
+    kda_grams<E, D, NT, true, false>(Ks, Qs, Kr, Cl, Gs, unsafe, nullptr, bs, nullptr, CH, Mc, q + tk * D, n,
+                                     Rno ? rnq : nullptr);
     using RV = decltype(rv);
 #pragma unroll
     for (int it = 0; it < RV::IT; ++it) {
@@ -308,7 +326,8 @@ __global__ __launch_bounds__(512) void k_fwd_prep_kda(Geo geo, const E* __restri
     rv.store_global(Uo + u * CH * D, D);
     return;
   }
-  kda_grams<E, D, NT, true>(Ks, Qs, Kr, Cl, Gs, unsafe, Ls, bs, Ao + u * CH * CH, CH, Mc, q + tk * D, n);
+  kda_grams<E, D, NT, true>(Ks, Qs, Kr, Cl, Gs, unsafe, Ls, bs, Ao + u * CH * CH, CH, Mc, q + tk * D, n,
+                            Rno ? rnq : nullptr);
 
   // Khat = e^g K in place; V into the Q buffer
   for (int idx = threadIdx.x; idx < CH * D / VE; idx += NT) {
@@ -501,6 +520,8 @@ __global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict
   const int wr = w & 3, wc = w >> 2;
   f32x4 xf[NQ];
   RegTile<float, CH, CH, NT> rli, raf;
+  float rnk[decltype(rk)::IT];  // q/k normalisation: 1 / ||k|| of the rows of rk this thread holds
+  if (p.qkn) load_row_factors(rk, p.Rn + u * 2 * CH + CH, rnk);
   ra.load(alpha + tk * D, D, n);
   rk.load(k + tk * D, D, n);
   rv.load(v + tk * D, D, n);
@@ -509,6 +530,7 @@ __global__ __launch_bounds__(512) void k_bwd_kda_wy(Geo geo, const E* __restrict
   for (int q = 0; q < NQ; ++q) xf[q] = *reinterpret_cast<const f32x4*>(p.kd_dx + u * CH * D + frag_off<D>(wr, wc * NQ + q));
   rli.load(p.Li + u * CH * CH, CH, CH);
   raf.load(p.A1 + u * CH * CH, CH, CH);
+  if (p.qkn) scale_rows(rk, rnk);  // the keys as the preparation normalised them
   rk.store(Ks, LD);
   if (threadIdx.x < CH) {
     const float b = gate_from_raw<E>(braw);  // 0 past the end
@@ -703,12 +725,21 @@ __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restri
   {
     RegTile<E, CH, JW, NT> rk, rq, ra;
     RegTile<E, CH, CH, NT> rda, rdm;
+    float rnk[decltype(rk)::IT], rnq[decltype(rq)::IT];  // q/k normalisation: 1 / ||x|| of this thread's rows
+    if (p.qkn) {
+      load_row_factors(rk, p.Rn + u * 2 * CH + CH, rnk);
+      load_row_factors(rq, p.Rn + u * 2 * CH, rnq);
+    }
     ra.load(alpha + tk * D + j0, D, n);
     rk.load(k + tk * D + j0, D, n);
     rq.load(q + tk * D + j0, D, n);
     if constexpr (!EF) rda.load(reinterpret_cast<const E*>(p.kd_da) + u * CH * CH, CH, CH);
     rdm.load(reinterpret_cast<const E*>(p.kd_dm) + u * CH * CH, CH, CH);
     if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
+    if (p.qkn) {  // this block's channels of the rows the preparation normalised
+      scale_rows(rk, rnk);
+      scale_rows(rq, rnq);
+    }
     rk.store(Ks, LDJ);
     rq.store(Qs, LDJ);
     rdm.store(dMs, LDT);
@@ -1106,7 +1137,7 @@ hipError_t launch_fwd_prep_kda(const Plan& p, const gdr_inputs& in, hipStream_t 
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H), dim3(512), 0, st, p.geo, (const E*)in.q,
                        (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (E*)p.X, (E*)p.Ub,
-                       (E*)p.M, (E*)p.Kb, (E*)p.Qh, p.Gn, p.Li, p.A1);
+                       (E*)p.M, (E*)p.Kb, (E*)p.Qh, p.Gn, p.Li, p.A1, p.qkn ? p.Rn : nullptr);
   };
   if (ef) {
     if (p.gates) go(k_fwd_prep_kda<E, D, true, true>);

@@ -14,8 +14,9 @@ struct Plan {
   Geo geo;
   int variant, dtype, D, bv;
   int gates;          // 1: beta and alpha are logits (Delta family)
-  int qkn;            // 1: q and k scaled to unit length per token (Delta family): the preparation
-                      //    keeps 1/||q||, 1/||k|| (Rn) and every kernel applies them to the raw rows
+  int qkn;            // 1: q and k scaled to unit length per token (every variant but Gated
+                      //    DeltaNet-2): the preparation keeps 1/||q||, 1/||k|| (Rn) and every later
+                      //    kernel applies them to the raw rows
   int lseg, max_seg;      // forward segmented scans: chunks per segment (0: off), largest segment count
   int lseg_b, max_seg_b;  // the same for the backward scans
   // time-split backward (ScanSeg mode 3; delta family): parts of ts_lseg chunks, ts_parts of
@@ -41,7 +42,7 @@ struct Plan {
   void* Kb;   // Kimi Delta Attention: [units][64][D] Kbar = e^{g_n - g} K
   void* Qh;   // Kimi Delta Attention: [units][64][D] Qhat = e^g Q
   float* Gn;  // Kimi Delta Attention: [units][D]     e^{g_n} per key channel
-  float* Rn;  // q/k normalisation (Delta family): [units][2][64] 1/||q||, 1/||k|| per token (zero past the end)
+  float* Rn;  // q/k normalisation (qkn): [units][2][64] 1/||q||, 1/||k|| per token (zero past the end)
   // workspace only
   void* Ub;   // [units][64][D]  WY factor U = T V
   void* dHs;  // [units][D][D]   gradient w.r.t. the memory at the end of each chunk

@@ -42,7 +42,10 @@ CASES = [
     dict(name="kda_bf16_residual", variant="kda", dtype="bf16", d=128, B=2, H=2, T=150, residual=True),
     dict(name="kda_bf16_strong_decay", variant="kda", dtype="bf16", d=128, B=1, H=2, T=200, alpha="strong"),
     dict(name="kda_f32", variant="kda", dtype="f32", d=64, B=2, H=2, T=150),
+    dict(name="kda_bf16_strong_qknorm", variant="kda", dtype="bf16", d=128, B=1, H=2, T=330, cu=PACK,
+         alpha="strong", qk_norm=True),
     dict(name="gla_bf16", variant="gla", dtype="bf16", d=128, B=1, H=2, T=330, cu=PACK),
+    dict(name="gla_f32_qknorm", variant="gla", dtype="f32", d=64, B=2, H=2, T=150, qk_norm=True),
     dict(name="gdn2_bf16_packed", variant="gdn2", dtype="bf16", d=128, B=1, H=2, T=330, cu=PACK),
     dict(name="gdn2_bf16_logits", variant="gdn2", dtype="bf16", d=128, B=2, H=2, T=150, logits=True),
     dict(name="gdn2_f32", variant="gdn2", dtype="f32", d=64, B=2, H=2, T=150),

@@ -257,8 +257,17 @@ def test_qk_norm_checks_and_workspace(lib):
     units = 2 * 5 * 4
     al = lambda x: (x + 255) // 256 * 256
     assert normed == plain + al(units * 2 * 64 * 4)
-    # Kimi Delta Attention normalises into two workspace copies first
-    p = _problem(B=2, H=4, T=300, variant=2)
+    # so do Kimi Delta Attention and the erase-free variant
+    for variant in (2, 4):
+        p = _problem(B=2, H=4, T=300, variant=variant)
+        st, plain = _ws(lib, p, True)
+        assert st == bd.GDR_OK
+        p.qk_norm = 1
+        st, normed = _ws(lib, p, True)
+        assert st == bd.GDR_OK
+        assert normed == plain + al(units * 2 * 64 * 4), variant
+    # Gated DeltaNet-2 normalises into two workspace copies first
+    p = _problem(B=2, H=4, T=300, variant=3)
     st, plain = _ws(lib, p, True)
     assert st == bd.GDR_OK
     p.qk_norm = 1

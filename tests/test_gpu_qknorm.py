@@ -10,10 +10,10 @@ from tests._helpers import compare, gpu_inputs, to_gpu, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(variant, dtype, d, T, B=2, H=2, cu=None, seed=71):
+def _inputs(variant, dtype, d, T, B=2, H=2, cu=None, seed=71, alpha_mode="weak"):
     w = synth.Workload("qkn", variant, dtype, B, H, T, d, d, seed=seed, h0_std=0.1,
                        cu_seqlens=None if cu is None else tuple(cu))
-    inp = synth.make_inputs(w, alpha_mode="weak")
+    inp = synth.make_inputs(w, alpha_mode=alpha_mode)
     rng = np.random.default_rng(seed + 1)
     for name in ("q", "k"):  # the generator's rows have unit length: give each its own scale
         x = np.asarray(inp[name], np.float64)
@@ -43,7 +43,7 @@ def _hip(inp, variant, dtype, use_saved):
     return {"o": to_np(o), "ht": to_np(ht), **{k: to_np(v) for k, v in gr.items()}}
 
 
-CASES = [(v, dt, d, s) for v in ("deltanet", "gated", "kda", "gdn2") for dt, d in (("bf16", 128), ("f32", 64))
+CASES = [(v, dt, d, s) for v in ("deltanet", "gated", "kda", "gdn2", "gla") for dt, d in (("bf16", 128), ("f32", 64))
          for s in (True, False)]
 
 
@@ -107,3 +107,13 @@ def test_qk_norm_scan_tiles_and_time_split(monkeypatch, env):
         monkeypatch.setenv(k_, v_)
     inp = _inputs("gated", "bf16", 128, T=600, B=1, H=2)
     compare(_hip(inp, "gated", "bf16", True), _oracle(inp, "gated"), "bf16")
+
+
+@pytest.mark.parametrize("variant", ["kda", "gla"])
+def test_qk_norm_per_channel_strong_decay_packed(variant):
+    """Per-channel decay strong enough that some 16-token blocks take the exact in-block sums
+    (their query rows scaled inside the preparation's exact path), packed sequences with an
+    empty one and ragged tails."""
+    cu = [0, 70, 70, 200, 333]
+    inp = _inputs(variant, "bf16", 128, T=333, B=1, H=2, cu=cu, alpha_mode="strong")
+    compare(_hip(inp, variant, "bf16", True), _oracle(inp, variant), "bf16")
