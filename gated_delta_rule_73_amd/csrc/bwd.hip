@@ -50,6 +50,8 @@ struct BwdScanOps<E, D, BV, VAR_GDN2> {
   RegTile<E, CH, BV, 256> dO;
   float g;
   uint32_t braw2;  // beta of this lane's token as loaded (0 if absent or past the end)
+  // fused q/k normalisation: 1 / ||q|| of the dO rows this lane holds, 1 / ||k|| of its token
+  float rnq[RegTile<E, CH, BV, 256>::IT], rnk;
 };
 template <typename E, int D, int BV>
 struct BwdScanOps<E, D, BV, VAR_GDN2L> : BwdScanOps<E, D, BV, VAR_GDN2> {};
@@ -74,9 +76,11 @@ struct BwdScanOps<E, D, BV, VAR_GLA> {  // nothing erased: no X
 // dr_t / beta_t to dR_t before dR feeds the memory gradient and the chunk kernel.  dRog, if not
 // NULL, also receives dR without that term (the beta gradient is formed from it, see
 // k_bwd_res_dbeta).
-// QKN (delta family): q and k are normalised to unit length per token.  The raw rows are read
-// and the preparation's factors Rng (1 / ||q||, 1 / ||k|| per unit) are applied to the rows
-// that meet them: to scale e^g dO in the update Q^T (e^g dO), to e^{g_n-g} (dW K^T) in dR.
+// QKN (delta family, Gated DeltaNet-2): q and k are normalised to unit length per token.  The
+// raw rows are read and the preparation's factors Rng (1 / ||q||, 1 / ||k|| per unit) are
+// applied to the rows that meet them: to scale e^g dO in the update Q^T (e^g dO), to
+// e^{g_n-g} (dW K^T) in dR.  Gated DeltaNet-2 folds 1 / ||k_t|| into beta_t of its erase
+// direction a = beta e*k, the only product its keys enter here.
 template <typename E, int D, int BV, int VAR, bool RES, bool QKN>
 __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ q, const E* __restrict__ k,
                                                   const E* __restrict__ dO, const E* __restrict__ Xg,
@@ -95,9 +99,10 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   constexpr bool NOX = VAR == VAR_GLA;  // nothing erased: X = 0, no dR^T X term
   constexpr bool DEC = VAR == VAR_GATED || G2;  // scalar decay
   static_assert(!RES || VAR == VAR_DELTANET || VAR == VAR_GATED || VAR == VAR_KDA, "residual gradient: not GDN-2, GLA");
-  static_assert(!QKN || VAR == VAR_DELTANET || VAR == VAR_GATED, "fused q/k normalisation: delta family");
+  static_assert(!QKN || (VAR != VAR_KDA && VAR != VAR_GLA), "fused q/k normalisation: not the per-unit operands");
   __shared__ __align__(16) E As[G2 ? CH * LD : 8];  // a = beta e*k (GDN-2)
   __shared__ float bsh[CH];
+  __shared__ float rks[QKN && (VAR == VAR_GDN2 || VAR == VAR_GDN2L) ? CH : 1];  // Gated DeltaNet-2: 1 / ||k_t||
   __shared__ __align__(16) E Qs[CH * LD];
   __shared__ __align__(16) E Ks[CH * LD];
   __shared__ __align__(16) E Xs[VAR == VAR_GLA ? 8 : CH * LD];
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
         if constexpr (QKN) {  // read before the next refill of this set
           load_row_factors(p.dO, Rng + u * 2 * CH, p.rnq);
-          p.rnk = Rng[u * 2 * CH + CH + 16 * w + lrow()];
+          p.rnk = Rng[u * 2 * CH + CH + (G2 ? (int)(threadIdx.x & (CH - 1)) : 16 * w + lrow())];
         }
       }
       if constexpr (RES) {  // accumulator layout of dR^T: row 16 w + lrow, columns 16 it + 4 lgrp
@@ -215,6 +220,9 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     if constexpr (G2) {
       if (threadIdx.x < CH)  // beta (1 when absent), 0 past the end; converted here, where it is used
         bsh[threadIdx.x] = ((int)threadIdx.x < n) ? (beta ? g2_gate<G2L>(gate_from_raw<E>(p.braw2)) : 1.f) : 0.f;
+      if constexpr (QKN) {
+        if (threadIdx.x < CH) rks[threadIdx.x] = p.rnk;
+      }
     }
 #pragma unroll
     for (int qq = 0; qq < NJ; ++qq)
@@ -251,7 +259,8 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
 #pragma unroll
       for (int it = 0; it < RE::IT; ++it) {  // one vector store per register vector
         const int t = p.e.row(it), j0 = p.e.col(it);
-        const float bt = bsh[t];
+        float bt = bsh[t];
+        if constexpr (QKN) bt *= rks[t];  // the raw k_t scaled to unit length
         typename RE::V av;
         E* ae = reinterpret_cast<E*>(&av);
 #pragma unroll
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     const int tl = 16 * w + lrow();
     float dec = 1.f;  // e^{g_n - g_t} (times 1 / ||k_t||: dW meets the raw k_t)
     if constexpr (DEC) dec = __expf(gn - gs[tl]);
-    if constexpr (QKN) dec *= p.rnk;
+    if constexpr (QKN && !G2) dec *= p.rnk;
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const f32x4 a1 = mma_k<E, CH>(zero4(), colk(dOt, LDO), 16 * it, colk(Ms, LDR), 16 * w);
@@ -1155,7 +1164,7 @@ static hipError_t bwd_impl(const Plan& p, const gdr_inputs& in, const void* dO, 
     }
   };
   auto scan = [&](const ScanSeg& sg, const float* dhtp, float* dh0p, int nv_mult) {
-    if constexpr (QOK) {
+    if constexpr (!PCH) {
       if (p.qkn) return scan_q(std::true_type{}, sg, dhtp, dh0p, nv_mult);
     }
     scan_q(std::false_type{}, sg, dhtp, dh0p, nv_mult);

@@ -270,9 +270,17 @@ template <> __device__ __forceinline__ uint32_t vzero<4>() { return 0u; }
 
 // Raw buffer resource over [base, base + bytes): a load at an offset at or past `bytes` returns
 // zero in hardware, so a ragged tile needs neither a clamp nor a select on the loaded data.
+// Every caller passes the same base and size in all lanes of a wave (a workgroup's tile or gate
+// row); they are read from the first lane so that the resource sits in scalar registers even
+// where the compiler cannot prove it uniform, which would otherwise wrap every load in a loop
+// over the distinct resources of the wave.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, long bytes) {
   const long lim = bytes < 0x7fffffffL ? bytes : 0x7fffffffL;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim, 0x00020000);
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  void* ub = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane((int)lim), 0x00020000);
 }
 template <int B> __device__ __forceinline__ typename VecT<B>::type buf_load(__amdgpu_buffer_rsrc_t r, int off);
 template <> __device__ __forceinline__ uint4 buf_load<16>(__amdgpu_buffer_rsrc_t r, int off) {
@@ -448,6 +456,17 @@ template <typename S, int ROWS, int COLS, int NT>
 __device__ __forceinline__ void g2s_rows(S* lds, int ld, const S* g, long gs, int nrows) {
   RegTile<S, ROWS, COLS, NT> t;
   t.load(g, gs, nrows);
+  t.store(lds, ld);
+}
+// The same with every row scaled by inv[row] as normalize_rows scaled it (inv NULL: a plain copy);
+// the factors are loaded before the tile, so scaling waits for nothing loaded after them.
+template <typename S, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void g2s_rows_scaled(S* lds, int ld, const S* g, long gs, int nrows, const float* inv) {
+  RegTile<S, ROWS, COLS, NT> t;
+  float rn[RegTile<S, ROWS, COLS, NT>::IT];
+  if (inv) load_row_factors(t, inv, rn);
+  t.load(g, gs, nrows);
+  if (inv) scale_rows(t, rn);
   t.store(lds, ld);
 }
 // Transposed staging: LDS[c*ld + r] = mul * G[r*gs + c] (zero for r >= nrows), r < ROWS, c < COLS.

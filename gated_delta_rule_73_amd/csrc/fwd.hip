@@ -219,13 +219,17 @@ struct FwdScanOps {
   uint32_t braw2;  // Gated DeltaNet-2: beta of this lane's token as loaded (0 if absent or past the end)
   f32x4 eg[D / 64];
   E braw;  // residual output: beta of this lane's token, as loaded (converted where it is used)
-  float rnq, rnk;  // fused q/k normalisation: 1 / ||q||, 1 / ||k|| of chunk row 16 w + lrow
+  // fused q/k normalisation: 1 / ||q|| of chunk row 16 w + lrow; 1 / ||k|| of that row (Gated
+  // DeltaNet-2: of this lane's token)
+  float rnq, rnk;
 };
 
-// QKN (delta family): q and k are normalised to unit length per token.  The raw rows are read
-// and the preparation's factors Rng (1 / ||q||, 1 / ||k|| per unit) are applied where a row
-// enters a product: to the output's row (Q W0^T) and to the rows of e^{g_n-g} R that meet K in
-// the memory update.
+// QKN (delta family, Gated DeltaNet-2): q and k are normalised to unit length per token.  The
+// raw rows are read and the preparation's factors Rng (1 / ||q||, 1 / ||k|| per unit) are
+// applied where a row enters a product: to the output's row (Q W0^T) and to the rows of
+// e^{g_n-g} R that meet K in the memory update.  Gated DeltaNet-2 folds 1 / ||k_t|| into the
+// per-token scalars of the products its keys enter: beta_t of a = beta e*k and e^{g_n-g_t} beta_t
+// of the write term.
 template <typename E, int D, int BV, int VAR, bool FULL, bool RES, bool QKN>
 __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* __restrict__ k, const E* __restrict__ Xg,
                                                   const E* __restrict__ Ug, const float* __restrict__ Gg,
@@ -251,6 +255,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
   __shared__ __align__(16) E Bd[G2 ? BV * LDR : 8];     // e^{g_n-g} b^T (GDN-2)
   __shared__ __align__(16) E Bn[OUT_G2 ? CH * LDV : 8]; // b (GDN-2 output)
   __shared__ float bsh[CH];
+  __shared__ float rks[QKN && (VAR == VAR_GDN2 || VAR == VAR_GDN2L) ? CH : 1];  // Gated DeltaNet-2: 1 / ||k_t||
   __shared__ __align__(16) E Us[CH * LDV];
   __shared__ __align__(16) E Ws[BV * LD];
   __shared__ __align__(16) E Rn[CH * LDV];
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
   __shared__ __align__(16) E M2s[OUT_G2 ? CH * LDR : 8];
   __shared__ __align__(16) E Os[FULL ? CH * LDV : 8];
   static_assert(!RES || (FULL && !G2), "the residual output is formed by the full pass of the delta family");
-  static_assert(!QKN || VAR == VAR_DELTANET || VAR == VAR_GATED, "fused q/k normalisation: delta family");
+  static_assert(!QKN || (VAR != VAR_KDA && VAR != VAR_GLA), "fused q/k normalisation: not the per-unit operands");
   __shared__ __align__(16) E Rr[RES ? CH * LDV : 8];  // r = R / beta for this tile's value columns
   __shared__ float gs[CH];
 
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
         if constexpr (QKN) {  // for the row this lane holds in R^T and O^T (read before the next refill)
           p.rnq = Rng[u * 2 * CH + 16 * w + lrow()];
-          p.rnk = Rng[u * 2 * CH + CH + 16 * w + lrow()];
+          p.rnk = Rng[u * 2 * CH + CH + (G2 ? (int)(threadIdx.x & (CH - 1)) : 16 * w + lrow())];
         }
       }
       if constexpr (RES) {  // a plain load (valid row), no arithmetic on it until the step uses it
@@ -376,6 +381,9 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     if constexpr (G2) {
       if (threadIdx.x < CH)  // beta (1 when absent), 0 past the end; converted here, where it is used
         bsh[threadIdx.x] = ((int)threadIdx.x < n) ? (beta ? g2_gate<G2L>(gate_from_raw<E>(p.braw2)) : 1.f) : 0.f;
+      if constexpr (QKN) {
+        if (threadIdx.x < CH) rks[threadIdx.x] = p.rnk;
+      }
     }
     if constexpr (RES) {  // residual output: 1 / beta (0 past the end)
       if (threadIdx.x < CH) bsh[threadIdx.x] = ((int)threadIdx.x < n) ? 1.f / (float)p.braw : 0.f;
@@ -393,7 +401,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
 #pragma unroll
       for (int it = 0; it < RE::IT; ++it) {  // one vector store per register vector
         const int t = p.e.row(it), j0 = p.e.col(it);
-        const float bt = bsh[t];
+        float bt = bsh[t];
+        if constexpr (QKN) bt *= rks[t];  // the raw k_t scaled to unit length
         typename RE::V av;
         E* ae = reinterpret_cast<E*>(&av);
 #pragma unroll
@@ -404,7 +413,8 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       for (int it = 0; it < RV::IT; ++it) {
         const int t = p.vt.row(it), i = p.vt.col(it);
         const float bt = virt ? 0.f : bsh[t];
-        const float sc = bt * __expf(gn0 - gs[t]);
+        float sc = bt * __expf(gn0 - gs[t]);  // (times 1 / ||k_t||: the write term meets the raw k_t)
+        if constexpr (QKN) sc *= rks[t];
         typename RV::V bnv;
         E* bn = reinterpret_cast<E*>(&bnv);
 #pragma unroll
@@ -422,7 +432,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     const int tl = 16 * w + lrow();
     float dec = 1.f;  // e^{g_n - g_t} (times 1 / ||k_t||: the row of R that meets the raw k_t)
     if constexpr (DEC) dec = __expf(gn - gs[tl]);
-    if constexpr (QKN) dec *= p.rnk;
+    if constexpr (QKN && !G2) dec *= p.rnk;
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       f32x4 acc = zero4();
@@ -565,7 +575,7 @@ static hipError_t fwd_impl(const Plan& p, const gdr_inputs& in, void* o, void* r
     }
   };
   auto scan = [&](auto full, const ScanSeg& sg, const float* h0, float* htp) {
-    if constexpr (VAR == VAR_DELTANET || VAR == VAR_GATED) {
+    if constexpr (!KDA) {
       if (p.qkn) return scan_q(full, std::true_type{}, sg, h0, htp);
     }
     scan_q(full, std::false_type{}, sg, h0, htp);

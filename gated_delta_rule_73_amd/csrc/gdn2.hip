@@ -16,6 +16,9 @@
 
 namespace gdr {
 
+// Rno (q/k normalisation; NULL without): q and k are scaled to unit length per token as they are
+// loaded (normalize_rows) and 1/||q||, 1/||k|| are kept per unit in Rno (zero past the end); the
+// scans and the backward stages scale the raw rows they load with them.
 template <typename E, int D, bool LOG>
 __global__ __launch_bounds__(512) void k_fwd_prep_gdn2(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                        const E* __restrict__ v, const E* __restrict__ beta,
@@ -24,7 +27,7 @@ __global__ __launch_bounds__(512) void k_fwd_prep_gdn2(Geo geo, const E* __restr
                                                        E* __restrict__ Uo, E* __restrict__ U2o, E* __restrict__ Mqa,
                                                        E* __restrict__ Mqk, float* __restrict__ Go,
                                                        float* __restrict__ Lio, float* __restrict__ Akko,
-                                                       float* __restrict__ Aako) {
+                                                       float* __restrict__ Aako, float* __restrict__ Rno) {
   GDR_POISON_ALL();
   constexpr int NT = 512, NW = NT / 64, LD = D + pad16<E>(), LDT = CH + pad16<E>(), LF = CH + 4;
   constexpr int NQ = D / 32;  // column tiles per wave in the 64 x D products
@@ -53,12 +56,17 @@ __global__ __launch_bounds__(512) void k_fwd_prep_gdn2(Geo geo, const E* __restr
     araw = load_gate_raw(alpha + tk, n, threadIdx.x);
   }
   {
-    RegTile<E, CH, D, NT> rk, re, rv, rw;
+    RegTile<E, CH, D, NT> rk, re, rv, rw, rq;
     rk.load(k + tk * D, D, n);
     re.load(erase + tk * D, D, n);
     rv.load(v + tk * D, D, n);
     rw.load(write + tk * D, D, n);
-    g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
+    rq.load(q + tk * D, D, n);
+    if (Rno) {
+      normalize_rows(rk, Rno + u * 2 * CH + CH);
+      normalize_rows(rq, Rno + u * 2 * CH);
+    }
+    rq.store(Qs, LD);
     rk.store(Ks, LD);
     if (threadIdx.x < CH) {
       const int t = threadIdx.x;
@@ -247,6 +255,8 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
   }
   {
     RegTile<E, CH, D, NT> rk, re, rv, rw;
+    float rnk[decltype(rk)::IT];  // q/k normalisation: 1 / ||k|| of the rows of rk this thread holds
+    if (p.qkn) load_row_factors(rk, p.Rn + u * 2 * CH + CH, rnk);
     rk.load(k + tk * D, D, n);
     re.load(erase + tk * D, D, n);
     rv.load(v + tk * D, D, n);
@@ -254,6 +264,7 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_state(Geo geo, const E* __rest
     g2s_rows<E, CH, D, NT>(dOs, LD, dO + tk * D, D, n);
     g2s_rows<E, CH, D, NT>(Rs, LD, Rg + u * CH * D, D, CH);
     g2s_rows<E, CH, D, NT>(dRs, LD, dRg + u * CH * D, D, CH);
+    if (p.qkn) scale_rows(rk, rnk);  // the keys as the preparation normalised them
     rk.store(Ks, LD);
     if (threadIdx.x < CH) {
       const int t = threadIdx.x;
@@ -440,7 +451,7 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_wy(Geo geo, const E* __restric
     gs[t] = Gg[u * CH + t];
     bs[t] = t < n ? (beta ? g2_gate<LOG>((float)beta[tk + t]) : 1.f) : 0.f;
   }
-  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
+  g2s_rows_scaled<E, CH, D, NT>(Ks, LD, k + tk * D, D, n, p.qkn ? p.Rn + u * 2 * CH + CH : nullptr);
   g2s_rows<E, CH, CH, NT>(Mqk, LDT, M2g + u * CH * CH, CH, CH);
   {  // L^{-1} and A_kk as the forward computed them
     RegTile<float, CH, CH, NT> rli, rakk;
@@ -645,8 +656,8 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_gram(Geo geo, const E* __restr
     gs[t] = Gg[u * CH + t];
     bs[t] = t < n ? (beta ? g2_gate<LOG>((float)beta[tk + t]) : 1.f) : 0.f;
   }
-  g2s_rows<E, CH, D, NT>(Ks, LD, k + tk * D, D, n);
-  g2s_rows<E, CH, D, NT>(Qs, LD, q + tk * D, D, n);
+  g2s_rows_scaled<E, CH, D, NT>(Ks, LD, k + tk * D, D, n, p.qkn ? p.Rn + u * 2 * CH + CH : nullptr);
+  g2s_rows_scaled<E, CH, D, NT>(Qs, LD, q + tk * D, D, n, p.qkn ? p.Rn + u * 2 * CH : nullptr);
   g2s_rows<E, CH, D, NT>(Es, LD, erase + tk * D, D, n);
   // Products are formed transposed: lane (lrow, lgrp) of wave w holds row t = 16 (w & 3) + lrow
   // and four consecutive columns 4 lgrp .. +3 of each of its 16-column tiles (half of them:
@@ -856,7 +867,8 @@ hipError_t launch_fwd_prep_gdn2(const Plan& p, const gdr_inputs& in, hipStream_t
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H), dim3(512), 0, st, p.geo, (const E*)in.q,
                        (const E*)in.k, (const E*)in.v, (const E*)in.beta, (const E*)in.alpha, (const E*)in.erase,
-                       (const E*)in.write, (E*)p.X, (E*)p.Ub, (E*)p.U2, (E*)p.M, (E*)p.M2, p.G, p.Li, p.A1, p.A2);
+                       (const E*)in.write, (E*)p.X, (E*)p.Ub, (E*)p.U2, (E*)p.M, (E*)p.M2, p.G, p.Li, p.A1, p.A2,
+                       p.qkn ? p.Rn : nullptr);
   };
   if (p.gates) go(k_fwd_prep_gdn2<E, D, true>);
   else go(k_fwd_prep_gdn2<E, D, false>);

@@ -44,7 +44,6 @@ struct Sizes {
   int ts_lseg = 0, ts_parts = 0;       // time-split backward (see ts_length)
   size_t X, M, G, Hs, R, M2, U2, Li, A1, A2, Kb, Qh, Gn, Ub, dHs, dR, g2, seg;
   size_t Rn = 0;  // q/k normalisation of the delta family: the inverse norms
-  size_t qn = 0;  // with qk_norm outside the kernels: the normalised q and k (after the cache)
   bool qkn = false;  // with qk_norm: the kernels normalise q and k as they load them
   size_t cache() const { return X + M + G + Hs + R + M2 + U2 + Li + A1 + A2 + Kb + Qh + Gn + Rn; }
   size_t fwd_ws() const { return Ub + seg; }                   // workspace before the cache
@@ -201,13 +200,11 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   const size_t ms = (size_t)std::max(s.lseg ? s.max_seg : 0, s.lseg_b ? s.max_seg_b : 0);
   const size_t nst = std::max(3 * ms, (size_t)s.ts_parts);
   s.seg = nst ? align_up((size_t)s.nstates * p->H * nst * D * D * 4, A) : 0;
-  // q/k normalisation: the preparation kernel of the delta family, of Kimi Delta Attention and of
-  // the erase-free variant normalises the rows it loads and keeps the inverse norms in the cache,
-  // with which the later kernels scale the raw rows themselves (the delta family's chunk backward
-  // also maps dq, dk back to the raw rows; the per-channel variants leave that to a pass after the
-  // backward); Gated DeltaNet-2 normalises into workspace copies first
-  s.qkn = p->qk_norm && p->variant != GDR_GDN2;
-  s.qn = (p->qk_norm && !s.qkn) ? 2 * align_up((size_t)p->B * p->H * p->T * D * s.esz, A) : 0;
+  // q/k normalisation: the preparation kernel normalises the rows it loads and keeps the inverse
+  // norms in the cache, with which the later kernels scale the raw rows themselves (the delta
+  // family's chunk backward also maps dq, dk back to the raw rows; the other variants leave that
+  // to a pass after the backward)
+  s.qkn = p->qk_norm != 0;
   if (s.qkn) s.Rn = align_up(U * 2 * C * 4, A);
   *sz = s;
   return GDR_OK;
@@ -314,21 +311,6 @@ gdr_status hip_status(hipError_t e, const char* what) {
   return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// With qk_norm, writes q / ||q|| and k / ||k|| (per token) into the workspace region at `dst`
-// and points the inputs at them; otherwise leaves the inputs as they are.
-gdr_status normalize_qk(const gdr_problem* p, const Sizes& s, char* dst, gdr_inputs* ins, hipStream_t st) {
-  if (!p->qk_norm || s.qkn || p->T == 0) return GDR_OK;
-  const long rows = (long)p->B * p->H * p->T;
-  char* qn = dst;
-  char* kn = dst + s.qn / 2;
-  gdr_status r = hip_status(gdr::run_l2norm(p->dtype, p->dk, ins->q, qn, rows, false, st), "q normalisation");
-  if (r != GDR_OK) return r;
-  if ((r = hip_status(gdr::run_l2norm(p->dtype, p->dk, ins->k, kn, rows, false, st), "k normalisation")) != GDR_OK)
-    return r;
-  ins->q = qn;
-  ins->k = kn;
-  return GDR_OK;
-}
 
 // Arms/disarms the per-launch trace around one public call.
 struct TraceCall {
@@ -485,20 +467,15 @@ hipError_t run_ranges(const gdr::Plan& pl, const gdr_problem* p, const Sizes& s,
 }
 
 // The forward behind gdr_forward_residual and gdr_forward_noalloc.  Workspace layout: the scan
-// workspace (fwd_ws), then the per-chunk cache when it is not in `saved` (always reserved when
-// reserve_cache, the layout gdr_workspace_size describes), then the normalised q and k.
+// workspace (fwd_ws), then the per-chunk cache when it is not in `saved` (the layout
+// gdr_workspace_size describes).
 gdr_status forward_impl(const gdr_problem* p, const gdr_inputs* in, void* o, void* r, float* ht, void* saved,
-                        const Sizes& s, char* ws, bool reserve_cache, void* stream) {
-  const char* cache_end = ws + s.fwd_ws() + ((reserve_cache || !saved) ? s.cache() : 0);
+                        const Sizes& s, char* ws, void* stream) {
   char* cache = saved ? static_cast<char*>(saved) : ws + s.fwd_ws();
   gdr::Plan pl = make_plan(p, s, cache, ws, false);
   g_last_error.clear();
   TraceCall tc;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
-  gdr_inputs ins = *in;
-  gdr_status st = normalize_qk(p, s, const_cast<char*>(cache_end), &ins, hs);
-  if (st != GDR_OK) return st;
-  return hip_status(gdr::run_forward(pl, ins, o, r, ht, true, hs), "gdr_forward launch");
+  return hip_status(gdr::run_forward(pl, *in, o, r, ht, true, static_cast<hipStream_t>(stream)), "gdr_forward launch");
 }
 
 // Checks shared by the forward entry points (everything but the workspace).
@@ -571,7 +548,7 @@ gdr_status gdr_workspace_size(const gdr_problem* p, int backward, size_t* bytes)
   gdr_status st = check_problem(p, &s);
   if (st != GDR_OK) return st;
   if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = s.cache() + (backward ? s.bwd_ws() : s.fwd_ws()) + s.qn;
+  *bytes = s.cache() + (backward ? s.bwd_ws() : s.fwd_ws());
   return GDR_OK;
 }
 
@@ -589,8 +566,8 @@ gdr_status gdr_forward_residual(const gdr_problem* p, const gdr_inputs* in, void
   Sizes s;
   gdr_status st = check_forward(p, in, o, r, ht, saved, &s);
   if (st != GDR_OK) return st;
-  if ((st = check_ws(ws, ws_bytes, s.cache() + s.fwd_ws() + s.qn)) != GDR_OK) return st;
-  return forward_impl(p, in, o, r, ht, saved, s, static_cast<char*>(ws), true, stream);
+  if ((st = check_ws(ws, ws_bytes, s.cache() + s.fwd_ws())) != GDR_OK) return st;
+  return forward_impl(p, in, o, r, ht, saved, s, static_cast<char*>(ws), stream);
 }
 
 gdr_status gdr_forward(const gdr_problem* p, const gdr_inputs* in, void* o, float* ht, void* saved, void* ws,
@@ -603,14 +580,14 @@ gdr_status gdr_forward_noalloc(const gdr_problem* p, const gdr_inputs* in, void*
   Sizes s;
   gdr_status st = check_forward(p, in, o, nullptr, ht, saved, &s);
   if (st != GDR_OK) return st;
-  const size_t need = s.fwd_ws() + (saved ? 0 : s.cache()) + s.qn;
+  const size_t need = s.fwd_ws() + (saved ? 0 : s.cache());
   if (need > kScratchBytes)
     return fail(GDR_ERR_WORKSPACE, "gdr_forward_noalloc: this problem needs %zu bytes of scratch, more than the "
                 "%zu the library holds; pass a saved buffer or call gdr_forward with a workspace",
                 need, kScratchBytes);
   char* ws = nullptr;
   if ((st = scratch_on_current_device(stream, &ws)) != GDR_OK) return st;
-  return forward_impl(p, in, o, nullptr, ht, saved, s, ws, false, stream);
+  return forward_impl(p, in, o, nullptr, ht, saved, s, ws, stream);
 }
 
 gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, const void* dO, const void* dr,
@@ -639,15 +616,14 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
   for (const void* x : ptrs)
     if (x && !aligned(x, 16)) return fail(GDR_ERR_INVALID_ARG, "gradient pointers must be 16-byte aligned");
   if (saved && !aligned(saved, 256)) return fail(GDR_ERR_INVALID_ARG, "saved must be 256-byte aligned");
-  if ((st = check_ws(ws, ws_bytes, s.cache() + s.bwd_ws() + s.qn)) != GDR_OK) return st;
+  if ((st = check_ws(ws, ws_bytes, s.cache() + s.bwd_ws())) != GDR_OK) return st;
   char* base = static_cast<char*>(ws);
   char* cache = saved ? const_cast<char*>(static_cast<const char*>(saved)) : base + s.bwd_ws();
   gdr::Plan pl = make_plan(p, s, cache, base, true);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   g_last_error.clear();
   TraceCall tc;
-  gdr_inputs ins = *in;  // q and k replaced by their normalised copies with qk_norm
-  if ((st = normalize_qk(p, s, base + s.bwd_ws() + s.cache(), &ins, hs)) != GDR_OK) return st;
+  const gdr_inputs ins = *in;
   if (pipeline_wanted(p, s)) {
     st = hip_status(run_ranges(pl, p, s, hs, [&](const gdr::Plan& q, const SeqRange& x, hipStream_t sq) {
       gdr_inputs sub = ins;
@@ -677,12 +653,12 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
     }
     st = hip_status(gdr::run_backward(pl, ins, dO, dr, dht, *g, hs), "gdr_backward launch");
   }
-  if (st != GDR_OK || !p->qk_norm || (s.qkn && (p->variant == GDR_DELTANET || p->variant == GDR_GATED))) return st;
-  // gradients w.r.t. the raw q and k, through the normalisation
+  if (st != GDR_OK || !s.qkn || p->variant == GDR_DELTANET || p->variant == GDR_GATED) return st;
+  // the other variants' dq, dk are w.r.t. the normalised rows: through the normalisation
   const long rows = (long)p->B * p->H * p->T;
-  st = hip_status(gdr::run_l2norm(p->dtype, p->dk, in->q, g->dq, rows, true, hs), "gdr_backward q normalisation");
+  st = hip_status(gdr::run_l2norm_grad(p->dtype, p->dk, in->q, g->dq, rows, hs), "gdr_backward q normalisation");
   if (st != GDR_OK) return st;
-  return hip_status(gdr::run_l2norm(p->dtype, p->dk, in->k, g->dk, rows, true, hs), "gdr_backward k normalisation");
+  return hip_status(gdr::run_l2norm_grad(p->dtype, p->dk, in->k, g->dk, rows, hs), "gdr_backward k normalisation");
 }
 
 gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* dO, const float* dht,

@@ -1,9 +1,9 @@
-// q/k L2-normalisation around the chunked operator: queries and keys scaled to unit length per
-// token (y = x / ||x||_2 over the head dimension, a zero row left zero) before the forward and
-// backward, and the gradient carried back through the scaling after the backward,
+// The gradient of the q/k L2-normalisation (queries and keys scaled to unit length per token,
+// y = x / ||x||_2 over the head dimension, a zero row left zero) for the variants whose backward
+// produces dq, dk w.r.t. the normalised rows (the kernels apply the normalisation itself):
 //   dx = (dy - y (y . dy)) / ||x||.
 // Unit-length keys keep the delta rule's rank-1 factor I - beta k k^T with eigenvalue 1 - beta.
-// Memory-bound elementwise passes over [rows, d] token rows, 16-byte vectors, float32 arithmetic.
+// A memory-bound elementwise pass over [rows, d] token rows, 16-byte vectors, float32 arithmetic.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -37,31 +37,6 @@ __device__ __forceinline__ void store_vec(E* p, const float* v) {
   *reinterpret_cast<uint4*>(p) = raw;
 }
 
-// y = x / ||x|| per row of D.
-template <typename E, int D>
-__global__ __launch_bounds__(256) void k_l2norm_rows(const E* __restrict__ x, E* __restrict__ y, long rows) {
-  GDR_POISON_ALL();
-  using RV = RowVec<E, D>;
-  constexpr int VE = RV::VE, LPR = RV::LPR;
-  const long g0 = ((long)blockIdx.x * 256 + threadIdx.x) / LPR, stride = (long)gridDim.x * 256 / LPR;
-  const int c = (threadIdx.x % LPR) * VE;
-  for (long row = g0; row < rows; row += stride) {
-    RV a;
-    a.load(x + row * D + c);
-    float v[VE], ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < VE; ++i) {
-      v[i] = a.at(i);
-      ss += v[i] * v[i];
-    }
-    ss = group_sum<LPR>(ss);
-    const float rn = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;
-#pragma unroll
-    for (int i = 0; i < VE; ++i) v[i] *= rn;
-    store_vec<E, VE>(y + row * D + c, v);
-  }
-}
-
 // dx = (dy - y (y . dy)) / ||x|| in place over dy, y recomputed from x.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void k_l2norm_grad_rows(const E* __restrict__ x, E* __restrict__ dxy, long rows) {
@@ -92,25 +67,20 @@ __global__ __launch_bounds__(256) void k_l2norm_grad_rows(const E* __restrict__ 
   }
 }
 
-hipError_t run_l2norm(int dtype, int D, const void* x, void* y, long rows, bool grad, hipStream_t st) {
+hipError_t run_l2norm_grad(int dtype, int D, const void* x, void* dxy, long rows, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  TraceScope ts_(grad ? "l2norm_grad" : "l2norm", st);
+  TraceScope ts_("l2norm_grad", st);
   // 16-byte vectors: D * esz / 16 threads per row; at most eight workgroups per CU, then stride
   const long threads = rows * ((long)D * (dtype == GDR_BF16 ? 2 : 4) / 16);
   const dim3 grid((unsigned)std::min<long>((threads + 255) / 256, 2048));
-  auto go = [&](auto fwd, auto bwd, auto* px, auto* py) {
-    if (grad) hipLaunchKernelGGL(bwd, grid, dim3(256), 0, st, px, py, rows);
-    else hipLaunchKernelGGL(fwd, grid, dim3(256), 0, st, px, py, rows);
-  };
+  auto go = [&](auto kern, auto* px, auto* py) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, px, py, rows); };
   if (dtype == GDR_BF16) {
     const bf16* px = static_cast<const bf16*>(x);
-    bf16* py = static_cast<bf16*>(y);
-    if (D == 128) go(k_l2norm_rows<bf16, 128>, k_l2norm_grad_rows<bf16, 128>, px, py);
-    else go(k_l2norm_rows<bf16, 64>, k_l2norm_grad_rows<bf16, 64>, px, py);
+    bf16* py = static_cast<bf16*>(dxy);
+    if (D == 128) go(k_l2norm_grad_rows<bf16, 128>, px, py);
+    else go(k_l2norm_grad_rows<bf16, 64>, px, py);
   } else {
-    const float* px = static_cast<const float*>(x);
-    float* py = static_cast<float*>(y);
-    go(k_l2norm_rows<float, 64>, k_l2norm_grad_rows<float, 64>, px, py);
+    go(k_l2norm_grad_rows<float, 64>, static_cast<const float*>(x), static_cast<float*>(dxy));
   }
   return hipGetLastError();
 }

@@ -90,16 +90,12 @@ typedef struct {
   int32_t qk_norm;                /* 0: q and k are used as given.  1: each token's q and k are
                                      first scaled to unit length over d_k (x / ||x||_2, a zero
                                      row left zero) and dq, dk are gradients w.r.t. the raw q, k.
-                                     Every variant but Gated DeltaNet-2 does it inside its
-                                     kernels (the inverse norms, 2 floats per token and head,
-                                     are part of the saved cache); Kimi Delta Attention and the
-                                     erase-free variant map dq, dk back to the raw rows in a pass
-                                     after the backward.  Gated DeltaNet-2 runs passes before the
-                                     forward and backward and after the backward (their copies
-                                     take 2 B H T d_k elements of workspace, counted by
-                                     gdr_workspace_size).  Every variant in gdr_forward and
-                                     gdr_backward; gdr_decode returns UNSUPPORTED (normalise
-                                     there before the call) */
+                                     Done inside the kernels (the inverse norms, 2 floats per
+                                     token and head, are part of the saved cache); DeltaNet and
+                                     Gated DeltaNet map dq, dk back to the raw rows inside their
+                                     backward, the other variants in a pass after it.  Every
+                                     variant in gdr_forward and gdr_backward; gdr_decode returns
+                                     UNSUPPORTED (normalise there before the call) */
 } gdr_problem;
 
 typedef struct {

@@ -49,6 +49,8 @@ CASES = [
     dict(name="gdn2_bf16_packed", variant="gdn2", dtype="bf16", d=128, B=1, H=2, T=330, cu=PACK),
     dict(name="gdn2_bf16_logits", variant="gdn2", dtype="bf16", d=128, B=2, H=2, T=150, logits=True),
     dict(name="gdn2_f32", variant="gdn2", dtype="f32", d=64, B=2, H=2, T=150),
+    dict(name="gdn2_bf16_logits_qknorm", variant="gdn2", dtype="bf16", d=128, B=1, H=2, T=330, cu=PACK,
+         logits=True, qk_norm=True),
     dict(name="gated_decode", variant="gated", dtype="bf16", d=128, B=3, H=2, T=5, decode=True),
 ]
 

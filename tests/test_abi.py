@@ -245,9 +245,8 @@ def test_gate_logit_checks(lib):
 
 
 def test_qk_norm_checks_and_workspace(lib):
-    # the delta family's preparation keeps the inverse norms of q and k in the forward->backward
-    # cache (two floats per token and head, zero past each sequence's end); the kernels scale the
-    # raw rows themselves
+    # the preparation keeps the inverse norms of q and k in the forward->backward cache (two floats
+    # per token and head, zero past each sequence's end); the kernels scale the raw rows themselves
     p = _problem(B=2, H=4, T=300)
     st, plain = _ws(lib, p, True)
     assert st == bd.GDR_OK
@@ -257,8 +256,8 @@ def test_qk_norm_checks_and_workspace(lib):
     units = 2 * 5 * 4
     al = lambda x: (x + 255) // 256 * 256
     assert normed == plain + al(units * 2 * 64 * 4)
-    # so do Kimi Delta Attention and the erase-free variant
-    for variant in (2, 4):
+    # so does every other variant (Kimi Delta Attention, Gated DeltaNet-2, erase-free)
+    for variant in (2, 3, 4):
         p = _problem(B=2, H=4, T=300, variant=variant)
         st, plain = _ws(lib, p, True)
         assert st == bd.GDR_OK
@@ -266,15 +265,6 @@ def test_qk_norm_checks_and_workspace(lib):
         st, normed = _ws(lib, p, True)
         assert st == bd.GDR_OK
         assert normed == plain + al(units * 2 * 64 * 4), variant
-    # Gated DeltaNet-2 normalises into two workspace copies first
-    p = _problem(B=2, H=4, T=300, variant=3)
-    st, plain = _ws(lib, p, True)
-    assert st == bd.GDR_OK
-    p.qk_norm = 1
-    st, normed = _ws(lib, p, True)
-    assert st == bd.GDR_OK
-    tok = 2 * 4 * 300 * 128 * 2  # one normalised copy of q (bf16)
-    assert normed == plain + 2 * ((tok + 255) // 256 * 256)
     p.qk_norm = 2
     st, _ = _ws(lib, p, True)
     assert st == bd.GDR_ERR_INVALID_ARG

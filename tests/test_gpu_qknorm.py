@@ -64,7 +64,7 @@ def test_qk_norm_packed_pipelined(monkeypatch):
     compare(_hip(inp, "gated", "bf16", True), _oracle(inp, "gated"), "bf16")
 
 
-@pytest.mark.parametrize("variant,dtype,d", [("gated", "bf16", 128), ("deltanet", "f32", 64)])
+@pytest.mark.parametrize("variant,dtype,d", [("gated", "bf16", 128), ("deltanet", "f32", 64), ("gdn2", "bf16", 128)])
 def test_qk_norm_segmented_scans(monkeypatch, variant, dtype, d):
     """Fused normalisation through the segmented scans (map pass, combine, rerun forced on),
     packed sequences with an empty one and ragged tails."""
@@ -105,8 +105,9 @@ def test_qk_norm_scan_tiles_and_time_split(monkeypatch, env):
     gradients run part by part)."""
     for k_, v_ in env.items():
         monkeypatch.setenv(k_, v_)
-    inp = _inputs("gated", "bf16", 128, T=600, B=1, H=2)
-    compare(_hip(inp, "gated", "bf16", True), _oracle(inp, "gated"), "bf16")
+    for variant in ("gated", "gdn2"):
+        inp = _inputs(variant, "bf16", 128, T=600, B=1, H=2)
+        compare(_hip(inp, variant, "bf16", True), _oracle(inp, variant), "bf16")
 
 
 @pytest.mark.parametrize("variant", ["kda", "gla"])
