@@ -635,6 +635,7 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   constexpr int NT = 512, NW = NT / 64, LD = Ly::LD, LDT = Ly::LDT, LF = Ly::LF, NQ = D / 32;
   __shared__ __align__(16) char smem[Ly::BYTES];
   __shared__ float gs[CH], bs[CH], rq[NW][CH], re_[NW][CH];  // row sums, one part per wave
+  __shared__ float rkn[2][CH], rqn[2][CH];  // q/k normalisation: k~ . dk~, q~ . dq~, one part per column half
   E* Ks = reinterpret_cast<E*>(smem);
   E* As = Ks + CH * LD;
   E* Qs = As + CH * LD;
@@ -664,6 +665,11 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_gram(Geo geo, const E* __restr
   // tiles NQ (w >> 2) ..), so every access of a result is one vector access.
   const int tr = 16 * wr + lrow();
   f32x4 aq[NQ], ak[NQ], aa[NQ];
+  float rnq = 0.f, rnk = 0.f;  // q/k normalisation: 1 / ||q||, 1 / ||k|| of row tr
+  if (p.qkn) {
+    rnq = p.Rn[u * 2 * CH + tr];
+    rnk = p.Rn[u * 2 * CH + CH + tr];
+  }
   {  // the partial gradients from the earlier stages, issued early
     const float* dq1 = p.g2_dq + u * CH * D + tr * D + 4 * lgrp();
     const float* dk1 = p.g2_dk + u * CH * D + tr * D + 4 * lgrp();
@@ -781,6 +787,23 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_gram(Geo geo, const E* __restr
     part = sum_rows4(part);
     if (lgrp() == 0) re_[w][tr] = part;
   }
+  if (p.qkn) {  // dq~, dk~ are complete: x~ . dx~ over this wave's columns of row tr (a row's
+    // columns are split over waves w and w ^ 4), summed after the next barrier
+    float pq = 0.f, pk = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int j0 = 16 * (wc * NQ + q) + 4 * lgrp();
+      const f32x4 kv = get4(Ks + tr * LD + j0), qv = get4(Qs + tr * LD + j0);
+      pk += kv[0] * ak[q][0] + kv[1] * ak[q][1] + kv[2] * ak[q][2] + kv[3] * ak[q][3];
+      pq += qv[0] * aq[q][0] + qv[1] * aq[q][1] + qv[2] * aq[q][2] + qv[3] * aq[q][3];
+    }
+    pk = sum_rows4(pk);
+    pq = sum_rows4(pq);
+    if (lgrp() == 0) {
+      rkn[wc][tr] = pk;
+      rqn[wc][tr] = pq;
+    }
+  }
   // prefix sums along each row of the pair terms: lanes over columns, rows over the waves
 #pragma unroll
   for (int uu_r = 0; uu_r < ((CH) + (NT / 64) - 1) / (NT / 64); ++uu_r) {
@@ -790,6 +813,16 @@ __global__ __launch_bounds__(512) void k_bwd_gdn2_gram(Geo geo, const E* __restr
     row[lane_id()] = wave_incl_scan(row[lane_id()]);
   }
   __syncthreads();
+  if (p.qkn) {  // w.r.t. the raw rows: dx = (dx~ - x~ (x~ . dx~)) / ||x||, in float32; each lane
+    // reads only the elements of K and Q it overwrites below
+    const float dk_ = rkn[0][tr] + rkn[1][tr], dq_ = rqn[0][tr] + rqn[1][tr];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int j0 = 16 * (wc * NQ + q) + 4 * lgrp();
+      ak[q] = (ak[q] - dk_ * get4(Ks + tr * LD + j0)) * rnk;
+      aq[q] = (aq[q] - dq_ * get4(Qs + tr * LD + j0)) * rnq;
+    }
+  }
   // outputs through LDS (K, A, Q regions are free now)
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
