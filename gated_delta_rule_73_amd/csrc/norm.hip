@@ -1,6 +1,7 @@
 // The gradient of the q/k L2-normalisation (queries and keys scaled to unit length per token,
 // y = x / ||x||_2 over the head dimension, a zero row left zero) for the variants whose backward
-// produces dq, dk w.r.t. the normalised rows (the kernels apply the normalisation itself):
+// produces dq, dk w.r.t. the normalised rows (Kimi Delta Attention and the erase-free variant,
+// whose Gram stage holds half of a row's channels; the kernels apply the normalisation itself):
 //   dx = (dy - y (y . dy)) / ||x||.
 // Unit-length keys keep the delta rule's rank-1 factor I - beta k k^T with eigenvalue 1 - beta.
 // A memory-bound elementwise pass over [rows, d] token rows, 16-byte vectors, float32 arithmetic.
