@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
 POISON_LIB = os.path.join(PKG, "libgdr_poison.so")
 POISON_BUILD = os.path.join(BUILD, "poison")
-SOURCES = ["gdr.cpp", "fwd.hip", "bwd.hip", "gdn2.hip", "kda.hip", "seg.hip", "decode.hip", "norm.hip"]
+SOURCES = ["gdr.cpp", "fwd.hip", "bwd.hip", "gdn2.hip", "kda.hip", "seg.hip", "decode.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

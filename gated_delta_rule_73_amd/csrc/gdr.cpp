@@ -201,9 +201,8 @@ gdr_status check_problem(const gdr_problem* p, Sizes* sz) {
   const size_t nst = std::max(3 * ms, (size_t)s.ts_parts);
   s.seg = nst ? align_up((size_t)s.nstates * p->H * nst * D * D * 4, A) : 0;
   // q/k normalisation: the preparation kernel normalises the rows it loads and keeps the inverse
-  // norms in the cache, with which the later kernels scale the raw rows themselves (the backward's
-  // last stage also maps dq, dk back to the raw rows, except for Kimi Delta Attention and the
-  // erase-free variant, whose Gram stage holds half of a row's channels: a pass after the backward)
+  // norms in the cache, with which the later kernels scale the raw rows themselves; the backward's
+  // last stage also maps dq, dk back to the raw rows
   s.qkn = p->qk_norm != 0;
   if (s.qkn) s.Rn = align_up(U * 2 * C * 4, A);
   *sz = s;
@@ -653,13 +652,7 @@ gdr_status gdr_backward_residual(const gdr_problem* p, const gdr_inputs* in, con
     }
     st = hip_status(gdr::run_backward(pl, ins, dO, dr, dht, *g, hs), "gdr_backward launch");
   }
-  if (st != GDR_OK || !s.qkn || p->variant == GDR_DELTANET || p->variant == GDR_GATED || p->variant == GDR_GDN2)
-    return st;
-  // the other variants' dq, dk are w.r.t. the normalised rows: through the normalisation
-  const long rows = (long)p->B * p->H * p->T;
-  st = hip_status(gdr::run_l2norm_grad(p->dtype, p->dk, in->q, g->dq, rows, hs), "gdr_backward q normalisation");
-  if (st != GDR_OK) return st;
-  return hip_status(gdr::run_l2norm_grad(p->dtype, p->dk, in->k, g->dk, rows, hs), "gdr_backward k normalisation");
+  return st;
 }
 
 gdr_status gdr_backward(const gdr_problem* p, const gdr_inputs* in, const void* dO, const float* dht,

@@ -690,7 +690,7 @@ struct KdaGramLds {
 
 // LOG: alpha holds logits; dalpha is returned w.r.t. them: d log alpha * (-sigmoid(x)).
 // EF: nothing erased: no dA slot (held at zero, its products skipped) and no dKhat term.
-template <typename E, int D, bool LOG, bool EF>
+template <typename E, int D, bool LOG, bool EF, bool QKN>
 __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restrict__ q, const E* __restrict__ k,
                                                       const E* __restrict__ alpha, E* __restrict__ dq,
                                                       E* __restrict__ dk, E* __restrict__ dalpha, Plan p) {
@@ -701,6 +701,13 @@ __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restri
   __shared__ __align__(16) char smem[Ly::BYTES];
   __shared__ float c1s[3][JW], tota[4][JW], totc[4][JW];
   __shared__ int unsafe[4];
+  // QKN (q/k normalisation): both channel halves run in this workgroup, one after the other;
+  // the first half's dk~, dq~ wait in stK, stQ for the rows' x~ . dx~, whose parts (channel
+  // half, column half of the waves) collect in pdk, pdq
+  constexpr int NHZ = D / JW;
+  static_assert(NHZ == 1 || NHZ == 2, "one or two channel halves");
+  __shared__ __align__(16) E stK[NHZ > 1 ? CH * LDJ : 8], stQ[NHZ > 1 ? CH * LDJ : 8];
+  __shared__ float pdk[NHZ][2][CH], pdq[NHZ][2][CH];
   float* Gs = reinterpret_cast<float*>(smem + Ly::oG);
   E* Ks = reinterpret_cast<E*>(smem + Ly::oK);
   E* Qs = reinterpret_cast<E*>(smem + Ly::oQ);
@@ -714,366 +721,443 @@ __global__ __launch_bounds__(512) void k_bwd_kda_gram(Geo geo, const E* __restri
   float* S2 = reinterpret_cast<float*>(smem + Ly::oS2);
   float* N4 = reinterpret_cast<float*>(smem + Ly::oN4);
 
-  const int gc = blockIdx.x, h = blockIdx.y, j0 = blockIdx.z * JW;
+  const int gc = blockIdx.x, h = blockIdx.y;
   const ChunkPos cp = chunk_pos(geo, gc);
   const long u = (long)gc * geo.H + h;
   const long tk = tok_index(geo, cp.b, h, cp.t0);
   const int w = wave_id(), l = lane_id(), n = cp.n;
   const int b = w & 3;   // this wave's 16-token block
   const int hf = w >> 2; // this wave's half of the block's work
+  constexpr int nhz = QKN ? NHZ : 1;
+  // the halves as separate copies of the body (a loop kept registers live across them)
+  static_for<0, nhz>([&](auto hzc) {
+    constexpr int hz = decltype(hzc)::value;
+    const int j0 = (QKN ? hz : (int)blockIdx.z) * JW;
 
-  {
-    RegTile<E, CH, JW, NT> rk, rq, ra;
-    RegTile<E, CH, CH, NT> rda, rdm;
-    float rnk[decltype(rk)::IT], rnq[decltype(rq)::IT];  // q/k normalisation: 1 / ||x|| of this thread's rows
-    if (p.qkn) {
-      load_row_factors(rk, p.Rn + u * 2 * CH + CH, rnk);
-      load_row_factors(rq, p.Rn + u * 2 * CH, rnq);
-    }
-    ra.load(alpha + tk * D + j0, D, n);
-    rk.load(k + tk * D + j0, D, n);
-    rq.load(q + tk * D + j0, D, n);
-    if constexpr (!EF) rda.load(reinterpret_cast<const E*>(p.kd_da) + u * CH * CH, CH, CH);
-    rdm.load(reinterpret_cast<const E*>(p.kd_dm) + u * CH * CH, CH, CH);
-    if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
-    if (p.qkn) {  // this block's channels of the rows the preparation normalised
-      scale_rows(rk, rnk);
-      scale_rows(rq, rnq);
-    }
-    rk.store(Ks, LDJ);
-    rq.store(Qs, LDJ);
-    rdm.store(dMs, LDT);
-    if constexpr (EF) {
-      using RA = decltype(rda);
-#pragma unroll
-      for (int it = 0; it < RA::IT; ++it) {
-        if (RA::TOTAL % NT == 0 || threadIdx.x + it * NT < RA::TOTAL)
-          *reinterpret_cast<typename RA::V*>(dAs + rda.row(it) * LDT + rda.col(it)) = typename RA::V{};
+    {
+      RegTile<E, CH, JW, NT> rk, rq, ra;
+      RegTile<E, CH, CH, NT> rda, rdm;
+      float rnk[decltype(rk)::IT], rnq[decltype(rq)::IT];  // q/k normalisation: 1 / ||x|| of this thread's rows
+      if constexpr (QKN) {
+        load_row_factors(rk, p.Rn + u * 2 * CH + CH, rnk);
+        load_row_factors(rq, p.Rn + u * 2 * CH, rnq);
       }
-    } else {
-      rda.store(dAs, LDT);
-    }
-    kda_cumlog<E, JW, NT, LOG>(ra, n, Gs, LDF);
-  }
-  kda_flags<JW, NT>(Gs, LDF, unsafe);
-  // Kend_s = k_s e^{g_{16(J+1)} - g_s} (s in block J < 3);  Kf_u, Qf_u = (k_u, q_u) e^{g_u - g_{16I}}
-  // (u in block I);  Krf_s = k_s e^{g_{16I} - g_s} (zero in blocks summed exactly)
-  {
-    constexpr int VE = 16 / (int)sizeof(E);  // 16 bytes per step
-    for (int idx = threadIdx.x; idx < CH * JW / VE; idx += NT) {
-      const int s = idx / (JW / VE), jv = (idx % (JW / VE)) * VE, r0 = s & ~15;
-      const bool uns = unsafe[s >> 4] != 0;
-      const uint4 kv4 = *reinterpret_cast<const uint4*>(Ks + s * LDJ + jv);
-      const uint4 qv4 = *reinterpret_cast<const uint4*>(Qs + s * LDJ + jv);
-      const E* ke = reinterpret_cast<const E*>(&kv4);
-      const E* qe = reinterpret_cast<const E*>(&qv4);
-      uint4 ev, fv, qfv, rv;
-      E* eo = reinterpret_cast<E*>(&ev);
-      E* fo = reinterpret_cast<E*>(&fv);
-      E* qo = reinterpret_cast<E*>(&qfv);
-      E* ro = reinterpret_cast<E*>(&rv);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        const int j = jv + e;
-        const float gs_ = Gs[s * LDF + j], g0 = Gs[r0 * LDF + j];
-        const float kv = (float)ke[e];
-        eo[e] = (E)(s < 48 ? kv * __expf(Gs[(min(r0 + 16, CH - 1)) * LDF + j] - gs_) : 0.f);
-        const float f = __expf(gs_ - g0);
-        fo[e] = (E)(kv * f);
-        qo[e] = (E)((float)qe[e] * f);
-        ro[e] = (E)(uns ? 0.f : kv * __expf(g0 - gs_));
+      ra.load(alpha + tk * D + j0, D, n);
+      rk.load(k + tk * D + j0, D, n);
+      rq.load(q + tk * D + j0, D, n);
+      if constexpr (!EF) rda.load(reinterpret_cast<const E*>(p.kd_da) + u * CH * CH, CH, CH);
+      rdm.load(reinterpret_cast<const E*>(p.kd_dm) + u * CH * CH, CH, CH);
+      if (threadIdx.x < 4) unsafe[threadIdx.x] = 0;
+      if constexpr (QKN) {  // this block's channels of the rows the preparation normalised
+        scale_rows(rk, rnk);
+        scale_rows(rq, rnq);
       }
-      if (s < 48) *reinterpret_cast<uint4*>(Ke + s * LDJ + jv) = ev;
-      *reinterpret_cast<uint4*>(Kf + s * LDJ + jv) = fv;
-      *reinterpret_cast<uint4*>(Qf + s * LDJ + jv) = qfv;
-      *reinterpret_cast<uint4*>(Krf + s * LDJ + jv) = rv;
-    }
-  }
-  __syncthreads();
-  const bool exact = unsafe[b] != 0;  // wave-uniform
-
-  // Loads of the last phases, issued now so that their latency is hidden: the partial
-  // gradients from the earlier stages at this wave's matrix-core elements, and alpha and the
-  // memory term at this lane's channel.
-  const float* dqh = p.kd_dqh + u * CH * D;
-  const float* dkh = p.kd_dkh + u * CH * D;
-  const float* dkb = p.kd_dkb + u * CH * D;
-  float lq[NCW][4], lk[NCW][4], lb[NCW][4], la[8];
-#pragma unroll
-  for (int cc = 0; cc < NCW; ++cc) {
-    const int o = frag_off<D>(b, j0 / 16 + hf * NCW + cc);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(dqh + o);
-    const f32x4 y = EF ? zero4() : *reinterpret_cast<const f32x4*>(dkh + o);
-    const f32x4 z = *reinterpret_cast<const f32x4*>(dkb + o);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      lq[cc][r] = x[r];
-      lk[cc][r] = y[r];
-      lb[cc][r] = z[r];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {  // this half's tokens of the block
-    const int t = min(16 * b + 8 * hf + i, n - 1);
-    la[i] = (float)alpha[(tk + t) * D + j0 + l];
-  }
-  const float gam_l = p.kd_gam[u * D + j0 + l];
-
-  // ---- pairs inside block b, channel j0 + l: one lane per channel
-  float n4[16], dkd[16], dqd[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) n4[i] = dkd[i] = dqd[i] = 0.f;
-  {
-    const E* dAb = dAs + 16 * b * LDT + 16 * b;
-    const E* dMb = dMs + 16 * b * LDT + 16 * b;
-    const float* gcol = Gs + 16 * b * LDF + l;
-    const E* kcol = Ks + 16 * b * LDJ + l;
-    const E* qcol = Qs + 16 * b * LDJ + l;
-    if (!exact) {
-      // d log alpha terms only: sum_{s<t<=u} c_us y_s with c_us = dA_us kF_u + dM_us qF_u,
-      // y_s = k_s e^{g_b - g_s}, kF_u = k_u e^{g_u - g_b} (b = the block's first token)
-      float kf[16], qf[16], y[16];
-      const float g0 = gcol[0];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float gi = gcol[i * LDF], kv = (float)kcol[i * LDJ];
-        const float f = __expf(gi - g0);
-        kf[i] = kv * f;
-        qf[i] = (float)qcol[i * LDJ] * f;
-        y[i] = kv * __expf(g0 - gi);
-      }
-      // later tokens uu = 1..10 in the first half, 11..15 in the second (55 and 65 pairs)
-      const auto later = [&](auto uu_c) {
-        constexpr int uu = decltype(uu_c)::value;
-        float run = 0.f;
-#pragma unroll
-        for (int s = 0; s < uu; ++s) {
-          const float c = fmaf((float)dMb[uu * LDT + s], qf[uu], (float)dAb[uu * LDT + s] * kf[uu]);
-          run = fmaf(c, y[s], run);
-          n4[s + 1] += run;
+      rk.store(Ks, LDJ);
+      rq.store(Qs, LDJ);
+      rdm.store(dMs, LDT);
+      if constexpr (EF) {
+        using RA = decltype(rda);
+  #pragma unroll
+        for (int it = 0; it < RA::IT; ++it) {
+          if (RA::TOTAL % NT == 0 || threadIdx.x + it * NT < RA::TOTAL)
+            *reinterpret_cast<typename RA::V*>(dAs + rda.row(it) * LDT + rda.col(it)) = typename RA::V{};
         }
-      };
-      if (hf == 0) {
-        static_for<1, 11>(later);
       } else {
-        static_for<11, 16>(later);
+        rda.store(dAs, LDT);
       }
-    } else if (hf == 0) {
-      // exact: one exponential per pair; also the pairs' dk and dq
-      float kk[16], gg[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        kk[i] = (float)kcol[i * LDJ];
-        gg[i] = gcol[i * LDF];
-      }
-#pragma unroll 1
-      for (int uu = 0; uu < 16; ++uu) {
-        const float guu = gcol[uu * LDF], kuu = (float)kcol[uu * LDJ], quu = (float)qcol[uu * LDJ];
-        float run = 0.f, ak = 0.f, aq = 0.f;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          const bool m = s < uu;
-          const float e = m ? __expf(guu - gg[s]) : 0.f;
-          const float da = m ? (float)dAb[uu * LDT + s] : 0.f, dm = m ? (float)dMb[uu * LDT + s] : 0.f;
-          const float ce = (da * kuu + dm * quu) * e;
-          dkd[s] += ce;
-          const float ke = kk[s] * e;
-          ak += da * ke;
-          aq += dm * ke;
-          run += ce * kk[s];
-          if (s < 15 && m) n4[s + 1] += run;
+      kda_cumlog<E, JW, NT, LOG>(ra, n, Gs, LDF);
+    }
+    kda_flags<JW, NT>(Gs, LDF, unsafe);
+    // Kend_s = k_s e^{g_{16(J+1)} - g_s} (s in block J < 3);  Kf_u, Qf_u = (k_u, q_u) e^{g_u - g_{16I}}
+    // (u in block I);  Krf_s = k_s e^{g_{16I} - g_s} (zero in blocks summed exactly)
+    {
+      constexpr int VE = 16 / (int)sizeof(E);  // 16 bytes per step
+      for (int idx = threadIdx.x; idx < CH * JW / VE; idx += NT) {
+        const int s = idx / (JW / VE), jv = (idx % (JW / VE)) * VE, r0 = s & ~15;
+        const bool uns = unsafe[s >> 4] != 0;
+        const uint4 kv4 = *reinterpret_cast<const uint4*>(Ks + s * LDJ + jv);
+        const uint4 qv4 = *reinterpret_cast<const uint4*>(Qs + s * LDJ + jv);
+        const E* ke = reinterpret_cast<const E*>(&kv4);
+        const E* qe = reinterpret_cast<const E*>(&qv4);
+        uint4 ev, fv, qfv, rv;
+        E* eo = reinterpret_cast<E*>(&ev);
+        E* fo = reinterpret_cast<E*>(&fv);
+        E* qo = reinterpret_cast<E*>(&qfv);
+        E* ro = reinterpret_cast<E*>(&rv);
+  #pragma unroll
+        for (int e = 0; e < VE; ++e) {
+          const int j = jv + e;
+          const float gs_ = Gs[s * LDF + j], g0 = Gs[r0 * LDF + j];
+          const float kv = (float)ke[e];
+          eo[e] = (E)(s < 48 ? kv * __expf(Gs[(min(r0 + 16, CH - 1)) * LDF + j] - gs_) : 0.f);
+          const float f = __expf(gs_ - g0);
+          fo[e] = (E)(kv * f);
+          qo[e] = (E)((float)qe[e] * f);
+          ro[e] = (E)(uns ? 0.f : kv * __expf(g0 - gs_));
         }
-        const float dmd = (float)dMb[uu * LDT + uu];
-#pragma unroll
+        if (s < 48) *reinterpret_cast<uint4*>(Ke + s * LDJ + jv) = ev;
+        *reinterpret_cast<uint4*>(Kf + s * LDJ + jv) = fv;
+        *reinterpret_cast<uint4*>(Qf + s * LDJ + jv) = qfv;
+        *reinterpret_cast<uint4*>(Krf + s * LDJ + jv) = rv;
+      }
+    }
+    __syncthreads();
+    const bool exact = unsafe[b] != 0;  // wave-uniform
+
+    // Loads of the last phases, issued now so that their latency is hidden: the partial
+    // gradients from the earlier stages at this wave's matrix-core elements, and alpha and the
+    // memory term at this lane's channel.
+    const float* dqh = p.kd_dqh + u * CH * D;
+    const float* dkh = p.kd_dkh + u * CH * D;
+    const float* dkb = p.kd_dkb + u * CH * D;
+    float lq[NCW][4], lk[NCW][4], lb[NCW][4], la[8];
+  #pragma unroll
+    for (int cc = 0; cc < NCW; ++cc) {
+      const int o = frag_off<D>(b, j0 / 16 + hf * NCW + cc);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(dqh + o);
+      const f32x4 y = EF ? zero4() : *reinterpret_cast<const f32x4*>(dkh + o);
+      const f32x4 z = *reinterpret_cast<const f32x4*>(dkb + o);
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        lq[cc][r] = x[r];
+        lk[cc][r] = y[r];
+        lb[cc][r] = z[r];
+      }
+    }
+  #pragma unroll
+    for (int i = 0; i < 8; ++i) {  // this half's tokens of the block
+      const int t = min(16 * b + 8 * hf + i, n - 1);
+      la[i] = (float)alpha[(tk + t) * D + j0 + l];
+    }
+    const float gam_l = p.kd_gam[u * D + j0 + l];
+
+    // ---- pairs inside block b, channel j0 + l: one lane per channel
+    float n4[16], dkd[16], dqd[16];
+  #pragma unroll
+    for (int i = 0; i < 16; ++i) n4[i] = dkd[i] = dqd[i] = 0.f;
+    {
+      const E* dAb = dAs + 16 * b * LDT + 16 * b;
+      const E* dMb = dMs + 16 * b * LDT + 16 * b;
+      const float* gcol = Gs + 16 * b * LDF + l;
+      const E* kcol = Ks + 16 * b * LDJ + l;
+      const E* qcol = Qs + 16 * b * LDJ + l;
+      if (!exact) {
+        // d log alpha terms only: sum_{s<t<=u} c_us y_s with c_us = dA_us kF_u + dM_us qF_u,
+        // y_s = k_s e^{g_b - g_s}, kF_u = k_u e^{g_u - g_b} (b = the block's first token)
+        float kf[16], qf[16], y[16];
+        const float g0 = gcol[0];
+  #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          if (i == uu) {
-            dkd[i] += ak + dmd * quu;
-            dqd[i] += aq + dmd * kuu;
+          const float gi = gcol[i * LDF], kv = (float)kcol[i * LDJ];
+          const float f = __expf(gi - g0);
+          kf[i] = kv * f;
+          qf[i] = (float)qcol[i * LDJ] * f;
+          y[i] = kv * __expf(g0 - gi);
+        }
+        // later tokens uu = 1..10 in the first half, 11..15 in the second (55 and 65 pairs)
+        const auto later = [&](auto uu_c) {
+          constexpr int uu = decltype(uu_c)::value;
+          float run = 0.f;
+  #pragma unroll
+          for (int s = 0; s < uu; ++s) {
+            const float c = fmaf((float)dMb[uu * LDT + s], qf[uu], (float)dAb[uu * LDT + s] * kf[uu]);
+            run = fmaf(c, y[s], run);
+            n4[s + 1] += run;
+          }
+        };
+        if (hf == 0) {
+          static_for<1, 11>(later);
+        } else {
+          static_for<11, 16>(later);
+        }
+      } else if (hf == 0) {
+        // exact: one exponential per pair; also the pairs' dk and dq
+        float kk[16], gg[16];
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          kk[i] = (float)kcol[i * LDJ];
+          gg[i] = gcol[i * LDF];
+        }
+  #pragma unroll 1
+        for (int uu = 0; uu < 16; ++uu) {
+          const float guu = gcol[uu * LDF], kuu = (float)kcol[uu * LDJ], quu = (float)qcol[uu * LDJ];
+          float run = 0.f, ak = 0.f, aq = 0.f;
+  #pragma unroll
+          for (int s = 0; s < 16; ++s) {
+            const bool m = s < uu;
+            const float e = m ? __expf(guu - gg[s]) : 0.f;
+            const float da = m ? (float)dAb[uu * LDT + s] : 0.f, dm = m ? (float)dMb[uu * LDT + s] : 0.f;
+            const float ce = (da * kuu + dm * quu) * e;
+            dkd[s] += ce;
+            const float ke = kk[s] * e;
+            ak += da * ke;
+            aq += dm * ke;
+            run += ce * kk[s];
+            if (s < 15 && m) n4[s + 1] += run;
+          }
+          const float dmd = (float)dMb[uu * LDT + uu];
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (i == uu) {
+              dkd[i] += ak + dmd * quu;
+              dqd[i] += aq + dmd * kuu;
+            }
           }
         }
       }
     }
-  }
 
-  // ---- matrix-core part (waves b and b + 4 own the output rows of block b, half of the column
-  // tiles each).  Accumulated per element:
-  // dkacc, dqacc: every dk / dq term from these products;  y2 = k * (dk lower, other blocks)
-  // + q * (dq, other blocks): block-suffix terms;  x3 = k * (dk upper, other blocks): block-prefix terms.
-  f32x4 dkacc[NCW], dqacc[NCW], y2[NCW], x3[NCW];
-#pragma unroll
-  for (int cc = 0; cc < NCW; ++cc) dkacc[cc] = dqacc[cc] = y2[cc] = x3[cc] = zero4();
-#pragma unroll
-  for (int cc = 0; cc < NCW; ++cc) {
-    const int c = hf * NCW + cc;
-    const int j = acc_col(16 * c);
-    float kv[4], qv[4], gv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int uu = acc_row(16 * b, r);
-      kv[r] = (float)Ks[uu * LDJ + j];
-      qv[r] = (float)Qs[uu * LDJ + j];
-      gv[r] = Gs[uu * LDF + j];
-    }
-#pragma unroll
-    for (int J = 0; J < 3; ++J) {
-      if (J < b) {  // lower: u in block b, s in block J
-        f32x4 pa = zero4();
-        if constexpr (!EF) pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Ke, LDJ), 16 * c, 16 * J);
-        const f32x4 pm = mma16<E>(zero4(), rowk(dMs, LDT), 16 * b, colk(Ke, LDJ), 16 * c, 16 * J);
-        const float gref = Gs[16 * (J + 1) * LDF + j];
-        float ps = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float f = __expf(gv[r] - gref);
-          const float a = f * pa[r], m = f * pm[r];
-          dkacc[cc][r] += a;
-          dqacc[cc][r] += m;
-          const float pr = kv[r] * a + qv[r] * m;
-          y2[cc][r] += pr;
-          ps += pr;
-        }
-        // the pair (b, J)'s total, needed by the blocks strictly between J and b: pairs (2, 0),
-        // (3, 0) and (3, 1) into c1s[0..2] (no block lies between 2 and 3)
-        if ((b == 2 && J == 0) || (b == 3 && J < 2)) {
-          ps += __shfl_xor(ps, 16, 64);
-          ps += __shfl_xor(ps, 32, 64);
-          if (l < 16) c1s[(b == 2) ? 0 : 1 + J][j] = ps;
-        }
-      }
-    }
-#pragma unroll
-    for (int I = 1; I < 4; ++I) {
-      if (I > b) {  // upper: s in block b, u in block I
-        f32x4 ua = zero4();
-        if constexpr (!EF) ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * I);
-        ua = mma16<E>(ua, colk(dMs, LDT), 16 * b, colk(Qf, LDJ), 16 * c, 16 * I);
-        const float gref = Gs[16 * I * LDF + j];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = __expf(gref - gv[r]) * ua[r];
-          dkacc[cc][r] += x;
-          x3[cc][r] += kv[r] * x;
-        }
-      }
-    }
-    if (!exact) {  // pairs inside block b, first token of the block as reference
-      f32x4 pa = zero4(), ua = zero4();
-      if constexpr (!EF) {
-        pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Krf, LDJ), 16 * c, 16 * b);
-        ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * b);
-      }
-      const f32x4 pm = mma16<E>(zero4(), rowk(dMs, LDT), 16 * b, colk(Krf, LDJ), 16 * c, 16 * b);
-      ua = mma16<E>(ua, colk(dMs, LDT), 16 * b, colk(Qf, LDJ), 16 * c, 16 * b);
-      const float g0 = Gs[16 * b * LDF + j];
-#pragma unroll
+    // ---- matrix-core part (waves b and b + 4 own the output rows of block b, half of the column
+    // tiles each).  Accumulated per element:
+    // dkacc, dqacc: every dk / dq term from these products;  y2 = k * (dk lower, other blocks)
+    // + q * (dq, other blocks): block-suffix terms;  x3 = k * (dk upper, other blocks): block-prefix terms.
+    f32x4 dkacc[NCW], dqacc[NCW], y2[NCW], x3[NCW];
+  #pragma unroll
+    for (int cc = 0; cc < NCW; ++cc) dkacc[cc] = dqacc[cc] = y2[cc] = x3[cc] = zero4();
+  #pragma unroll
+    for (int cc = 0; cc < NCW; ++cc) {
+      const int c = hf * NCW + cc;
+      const int j = acc_col(16 * c);
+      float kv[4], qv[4], gv[4];
+  #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float f = __expf(gv[r] - g0), rf = __expf(g0 - gv[r]);
-        dkacc[cc][r] += f * pa[r] + rf * ua[r];
-        dqacc[cc][r] += f * pm[r];
+        const int uu = acc_row(16 * b, r);
+        kv[r] = (float)Ks[uu * LDJ + j];
+        qv[r] = (float)Qs[uu * LDJ + j];
+        gv[r] = Gs[uu * LDF + j];
+      }
+  #pragma unroll
+      for (int J = 0; J < 3; ++J) {
+        if (J < b) {  // lower: u in block b, s in block J
+          f32x4 pa = zero4();
+          if constexpr (!EF) pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Ke, LDJ), 16 * c, 16 * J);
+          const f32x4 pm = mma16<E>(zero4(), rowk(dMs, LDT), 16 * b, colk(Ke, LDJ), 16 * c, 16 * J);
+          const float gref = Gs[16 * (J + 1) * LDF + j];
+          float ps = 0.f;
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float f = __expf(gv[r] - gref);
+            const float a = f * pa[r], m = f * pm[r];
+            dkacc[cc][r] += a;
+            dqacc[cc][r] += m;
+            const float pr = kv[r] * a + qv[r] * m;
+            y2[cc][r] += pr;
+            ps += pr;
+          }
+          // the pair (b, J)'s total, needed by the blocks strictly between J and b: pairs (2, 0),
+          // (3, 0) and (3, 1) into c1s[0..2] (no block lies between 2 and 3)
+          if ((b == 2 && J == 0) || (b == 3 && J < 2)) {
+            ps += __shfl_xor(ps, 16, 64);
+            ps += __shfl_xor(ps, 32, 64);
+            if (l < 16) c1s[(b == 2) ? 0 : 1 + J][j] = ps;
+          }
+        }
+      }
+  #pragma unroll
+      for (int I = 1; I < 4; ++I) {
+        if (I > b) {  // upper: s in block b, u in block I
+          f32x4 ua = zero4();
+          if constexpr (!EF) ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * I);
+          ua = mma16<E>(ua, colk(dMs, LDT), 16 * b, colk(Qf, LDJ), 16 * c, 16 * I);
+          const float gref = Gs[16 * I * LDF + j];
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float x = __expf(gref - gv[r]) * ua[r];
+            dkacc[cc][r] += x;
+            x3[cc][r] += kv[r] * x;
+          }
+        }
+      }
+      if (!exact) {  // pairs inside block b, first token of the block as reference
+        f32x4 pa = zero4(), ua = zero4();
+        if constexpr (!EF) {
+          pa = mma16<E>(zero4(), rowk(dAs, LDT), 16 * b, colk(Krf, LDJ), 16 * c, 16 * b);
+          ua = mma16<E>(zero4(), colk(dAs, LDT), 16 * b, colk(Kf, LDJ), 16 * c, 16 * b);
+        }
+        const f32x4 pm = mma16<E>(zero4(), rowk(dMs, LDT), 16 * b, colk(Krf, LDJ), 16 * c, 16 * b);
+        ua = mma16<E>(ua, colk(dMs, LDT), 16 * b, colk(Qf, LDJ), 16 * c, 16 * b);
+        const float g0 = Gs[16 * b * LDF + j];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float f = __expf(gv[r] - g0), rf = __expf(g0 - gv[r]);
+          dkacc[cc][r] += f * pa[r] + rf * ua[r];
+          dqacc[cc][r] += f * pm[r];
+        }
       }
     }
-  }
-  __syncthreads();  // region X becomes the staging area
-  if (exact && hf == 0) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      S1[(16 * b + i) * LDF + l] = dkd[i];
-      S2[(16 * b + i) * LDF + l] = dqd[i];
-    }
-  }
-  __syncthreads();
-
-  // ---- dq, dk, and the per-row terms of d log alpha (matrix-core layout)
-  float pa_[NCW], pc_[NCW];
-#pragma unroll
-  for (int cc = 0; cc < NCW; ++cc) {
-    const int c = hf * NCW + cc;
-    const int j = acc_col(16 * c);
-    const float gn = Gs[(CH - 1) * LDF + j];
-    float sa = 0.f, sc = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int uu = acc_row(16 * b, r);
-      const float g = Gs[uu * LDF + j], eg = __expf(g), egb = __expf(gn - g);
-      const float kv = (float)Ks[uu * LDJ + j], qv = (float)Qs[uu * LDJ + j];
-      const float xq = eg * lq[cc][r], xk = eg * lk[cc][r], xb = egb * lb[cc][r];
-      float dkv = dkacc[cc][r] + xk + xb, dqv = dqacc[cc][r] + xq;
-      if (exact) {
-        dkv += S1[uu * LDF + j];
-        dqv += S2[uu * LDF + j];
+    __syncthreads();  // region X becomes the staging area
+    if (exact && hf == 0) {
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        S1[(16 * b + i) * LDF + l] = dkd[i];
+        S2[(16 * b + i) * LDF + l] = dqd[i];
       }
-      // dk, dq replace this lane's own elements of K and Q (read just above; rows of block b
-      // are read by this wave only) and go out as whole rows below
-      Ks[uu * LDJ + j] = (E)dkv;
-      Qs[uu * LDJ + j] = (E)dqv;
-      const float a = qv * xq + kv * xk, bt = kv * xb;
-      y2[cc][r] += a;
-      x3[cc][r] += bt;
-      sa += a;
-      sc += bt;
     }
-    sa += __shfl_xor(sa, 16, 64);
-    sa += __shfl_xor(sa, 32, 64);
-    sc += __shfl_xor(sc, 16, 64);
-    sc += __shfl_xor(sc, 32, 64);
-    pa_[cc] = sa;
-    pc_[cc] = sc;
-  }
-  __syncthreads();
-  s2g_rows<E, CH, JW, NT>(dk + tk * D + j0, D, Ks, LDJ, n);
-  s2g_rows<E, CH, JW, NT>(dq + tk * D + j0, D, Qs, LDJ, n);
-#pragma unroll
-  for (int cc = 0; cc < NCW; ++cc) {
-    const int c = hf * NCW + cc;
-    store4_n(S1, LDF, 16 * b, 16 * c, y2[cc]);
-    store4_n(S2, LDF, 16 * b, 16 * c, x3[cc]);
-    if (l < 16) {
-      tota[b][16 * c + l] = pa_[cc];
-      totc[b][16 * c + l] = pc_[cc];
-    }
-  }
-  // the in-block pair sums at the other half's tokens
-#pragma unroll
-  for (int i = 0; i < 8; ++i) N4[(16 * b + 8 * (1 - hf) + i) * JW + l] = hf ? n4[i] : n4[8 + i];
-  __syncthreads();
+    __syncthreads();
 
-  // ---- d log alpha, channel layout
-  {
-    float cross = gam_l;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      if (bb > b) cross += tota[bb][l];
-      if (bb < b) cross += totc[bb][l];
+    // ---- dq, dk, and the per-row terms of d log alpha (matrix-core layout)
+    float pa_[NCW], pc_[NCW];
+    float xk4[4] = {0.f, 0.f, 0.f, 0.f}, xq4[4] = {0.f, 0.f, 0.f, 0.f};  // k~ . dk~, q~ . dq~ (QKN)
+  #pragma unroll
+    for (int cc = 0; cc < NCW; ++cc) {
+      const int c = hf * NCW + cc;
+      const int j = acc_col(16 * c);
+      const float gn = Gs[(CH - 1) * LDF + j];
+      float sa = 0.f, sc = 0.f;
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int uu = acc_row(16 * b, r);
+        const float g = Gs[uu * LDF + j], eg = __expf(g), egb = __expf(gn - g);
+        const float kv = (float)Ks[uu * LDJ + j], qv = (float)Qs[uu * LDJ + j];
+        const float xq = eg * lq[cc][r], xk = eg * lk[cc][r], xb = egb * lb[cc][r];
+        float dkv = dkacc[cc][r] + xk + xb, dqv = dqacc[cc][r] + xq;
+        if (exact) {
+          dkv += S1[uu * LDF + j];
+          dqv += S2[uu * LDF + j];
+        }
+        // dk, dq replace this lane's own elements of K and Q (read just above; rows of block b
+        // are read by this wave only) and go out as whole rows below
+        Ks[uu * LDJ + j] = (E)dkv;
+        Qs[uu * LDJ + j] = (E)dqv;
+        if constexpr (QKN) {
+          xk4[r] += kv * dkv;
+          xq4[r] += qv * dqv;
+        }
+        const float a = qv * xq + kv * xk, bt = kv * xb;
+        y2[cc][r] += a;
+        x3[cc][r] += bt;
+        sa += a;
+        sc += bt;
+      }
+      sa += __shfl_xor(sa, 16, 64);
+      sa += __shfl_xor(sa, 32, 64);
+      sc += __shfl_xor(sc, 16, 64);
+      sc += __shfl_xor(sc, 32, 64);
+      pa_[cc] = sa;
+      pc_[cc] = sc;
     }
-    if (b == 1) cross += c1s[0][l] + c1s[1][l];
-    if (b == 2) cross += c1s[1][l] + c1s[2][l];
-    // this half's tokens t0 .. t0 + 7: suffix sums of S1 from the block's end, prefix sums of S2
-    // from its start, in the same order as over the whole block
-    const int t0 = 16 * b + 8 * hf;
-    float suf[8];
-    float run = 0.f;
-    if (hf == 0) {
-#pragma unroll
-      for (int i = 15; i >= 8; --i) run += S1[(16 * b + i) * LDF + l];
+    if constexpr (QKN) {  // this wave's part of each row's dot: its columns are the 16 lanes of a row group
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float a = xk4[r], c = xq4[r];
+  #pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          a += __shfl_xor(a, off, 64);
+          c += __shfl_xor(c, off, 64);
+        }
+        if (lrow() == 0) {
+          pdk[hz][hf][acc_row(16 * b, r)] = a;
+          pdq[hz][hf][acc_row(16 * b, r)] = c;
+        }
+      }
     }
-#pragma unroll
-    for (int i = 7; i >= 0; --i) {
-      run += S1[(t0 + i) * LDF + l];
-      suf[i] = run;
+    __syncthreads();
+    if constexpr (!QKN) {
+      s2g_rows<E, CH, JW, NT>(dk + tk * D + j0, D, Ks, LDJ, n);
+      s2g_rows<E, CH, JW, NT>(dq + tk * D + j0, D, Qs, LDJ, n);
+    } else if constexpr (hz + 1 < nhz) {  // kept until the other half's dots are in
+      constexpr int VE = 16 / (int)sizeof(E);
+      for (int idx = threadIdx.x; idx < CH * JW / VE; idx += NT) {
+        const int t = idx / (JW / VE), c0 = (idx % (JW / VE)) * VE;
+        *reinterpret_cast<uint4*>(stK + t * LDJ + c0) = *reinterpret_cast<const uint4*>(Ks + t * LDJ + c0);
+        *reinterpret_cast<uint4*>(stQ + t * LDJ + c0) = *reinterpret_cast<const uint4*>(Qs + t * LDJ + c0);
+      }
     }
-    run = 0.f;
-    if (hf == 1) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) run += S2[(16 * b + i) * LDF + l];
+  #pragma unroll
+    for (int cc = 0; cc < NCW; ++cc) {
+      const int c = hf * NCW + cc;
+      store4_n(S1, LDF, 16 * b, 16 * c, y2[cc]);
+      store4_n(S2, LDF, 16 * b, 16 * c, x3[cc]);
+      if (l < 16) {
+        tota[b][16 * c + l] = pa_[cc];
+        totc[b][16 * c + l] = pc_[cc];
+      }
     }
+    // the in-block pair sums at the other half's tokens
+  #pragma unroll
+    for (int i = 0; i < 8; ++i) N4[(16 * b + 8 * (1 - hf) + i) * JW + l] = hf ? n4[i] : n4[8 + i];
+    __syncthreads();
+
+    // ---- d log alpha, channel layout
+    {
+      float cross = gam_l;
+  #pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        if (bb > b) cross += tota[bb][l];
+        if (bb < b) cross += totc[bb][l];
+      }
+      if (b == 1) cross += c1s[0][l] + c1s[1][l];
+      if (b == 2) cross += c1s[1][l] + c1s[2][l];
+      // this half's tokens t0 .. t0 + 7: suffix sums of S1 from the block's end, prefix sums of S2
+      // from its start, in the same order as over the whole block
+      const int t0 = 16 * b + 8 * hf;
+      float suf[8];
+      float run = 0.f;
+      if (hf == 0) {
+  #pragma unroll
+        for (int i = 15; i >= 8; --i) run += S1[(16 * b + i) * LDF + l];
+      }
+  #pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        run += S1[(t0 + i) * LDF + l];
+        suf[i] = run;
+      }
+      run = 0.f;
+      if (hf == 1) {
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) run += S2[(16 * b + i) * LDF + l];
+      }
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int t = t0 + i;
+        const float dla = ((hf ? n4[8 + i] : n4[i]) + N4[t * JW + l]) + suf[i] + run + cross;
+        run += S2[t * LDF + l];
+        if (t < n) {
+          if constexpr (LOG) dalpha[(tk + t) * D + j0 + l] = (E)(-dla * gate_sigmoid(la[i]));
+          else dalpha[(tk + t) * D + j0 + l] = (E)(dla / la[i]);
+        }
+      }
+    }
+    __syncthreads();  // the next channel half reuses the LDS regions
+  });
+  if constexpr (QKN) {  // dq, dk w.r.t. the raw rows: dx = (dx~ - x~ (x~ . dx~)) / ||x||, both halves
+    for (int hz = 0; hz < nhz; ++hz) {
+      const int j0 = hz * JW;
+      const E* sk = hz + 1 < nhz ? stK : Ks;
+      const E* sq = hz + 1 < nhz ? stQ : Qs;
+      using RT = RegTile<E, CH, JW, NT>;
+      RT xk, xq;  // this half of the normalised rows, formed as the preparation formed them
+      float fk[RT::IT], fq[RT::IT];
+      load_row_factors(xk, p.Rn + u * 2 * CH + CH, fk);
+      load_row_factors(xq, p.Rn + u * 2 * CH, fq);
+      xk.load(k + tk * D + j0, D, n);
+      xq.load(q + tk * D + j0, D, n);
+      scale_rows(xk, fk);
+      scale_rows(xq, fq);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = t0 + i;
-      const float dla = ((hf ? n4[8 + i] : n4[i]) + N4[t * JW + l]) + suf[i] + run + cross;
-      run += S2[t * LDF + l];
-      if (t < n) {
-        if constexpr (LOG) dalpha[(tk + t) * D + j0 + l] = (E)(-dla * gate_sigmoid(la[i]));
-        else dalpha[(tk + t) * D + j0 + l] = (E)(dla / la[i]);
+      for (int it = 0; it < RT::IT; ++it) {
+        const int t = xk.row(it), c0 = xk.col(it);
+        if ((RT::TOTAL % NT != 0 && threadIdx.x + it * NT >= RT::TOTAL) || t >= n) continue;
+        float dk_ = 0.f, dq_ = 0.f;
+#pragma unroll
+        for (int z = 0; z < NHZ; ++z) {
+          dk_ += pdk[z][0][t] + pdk[z][1][t];
+          dq_ += pdq[z][0][t] + pdq[z][1][t];
+        }
+        typename RT::V ok, oq;
+        E* oke = reinterpret_cast<E*>(&ok);
+        E* oqe = reinterpret_cast<E*>(&oq);
+        const typename RT::V gk = *reinterpret_cast<const typename RT::V*>(sk + t * LDJ + c0);
+        const typename RT::V gq = *reinterpret_cast<const typename RT::V*>(sq + t * LDJ + c0);
+        const E* gke = reinterpret_cast<const E*>(&gk);
+        const E* gqe = reinterpret_cast<const E*>(&gq);
+#pragma unroll
+        for (int x = 0; x < RT::VE; ++x) {
+          oke[x] = (E)(((float)gke[x] - dk_ * (float)xk.elem(it, x)) * fk[it]);
+          oqe[x] = (E)(((float)gqe[x] - dq_ * (float)xq.elem(it, x)) * fq[it]);
+        }
+        *reinterpret_cast<typename RT::V*>(dk + (tk + t) * D + j0 + c0) = ok;
+        *reinterpret_cast<typename RT::V*>(dq + (tk + t) * D + j0 + c0) = oq;
       }
     }
   }
@@ -1173,12 +1257,17 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
     {
       TraceScope ts_("bwd_gla_gram", st);
       auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(512), 0, st, p.geo,
+        hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, p.qkn ? 1 : D / 64), dim3(512), 0, st, p.geo,
                            (const E*)in.q, (const E*)in.k, (const E*)in.alpha, (E*)gr.dq, (E*)gr.dk,
                            (E*)gr.dalpha, p);
       };
-      if (p.gates) go(k_bwd_kda_gram<E, D, true, true>);
-      else go(k_bwd_kda_gram<E, D, false, true>);
+      if (p.qkn) {
+        if (p.gates) go(k_bwd_kda_gram<E, D, true, true, true>);
+        else go(k_bwd_kda_gram<E, D, false, true, true>);
+      } else {
+        if (p.gates) go(k_bwd_kda_gram<E, D, true, true, false>);
+        else go(k_bwd_kda_gram<E, D, false, true, false>);
+      }
     }
     return hipGetLastError();
   }
@@ -1199,11 +1288,16 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
   {
     TraceScope ts_("bwd_kda_gram", st);
     auto go = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, D / 64), dim3(512), 0, st, p.geo, (const E*)in.q,
+      hipLaunchKernelGGL(kern, dim3(p.geo.total_chunks, p.geo.H, p.qkn ? 1 : D / 64), dim3(512), 0, st, p.geo, (const E*)in.q,
                          (const E*)in.k, (const E*)in.alpha, (E*)gr.dq, (E*)gr.dk, (E*)gr.dalpha, p);
     };
-    if (p.gates) go(k_bwd_kda_gram<E, D, true, false>);
-    else go(k_bwd_kda_gram<E, D, false, false>);
+    if (p.qkn) {
+      if (p.gates) go(k_bwd_kda_gram<E, D, true, false, true>);
+      else go(k_bwd_kda_gram<E, D, false, false, true>);
+    } else {
+      if (p.gates) go(k_bwd_kda_gram<E, D, true, false, false>);
+      else go(k_bwd_kda_gram<E, D, false, false, false>);
+    }
   }
   return hipGetLastError();
 }

@@ -100,9 +100,6 @@ hipError_t launch_bwd_kda(const Plan& p, const gdr_inputs& in, const void* dO, c
 
 hipError_t launch_seg_combine(const Plan& p, const ScanSeg& sg, const float* init, bool reverse, hipStream_t st);
 
-// The gradient through the q/k L2-normalisation of `rows` token rows of D, in place over dxy:
-// dxy <- (dxy - x^ (x^ . dxy)) / ||x|| with x^ = x / ||x||.
-hipError_t run_l2norm_grad(int dtype, int D, const void* x, void* dxy, long rows, hipStream_t st);
 
 // Recurrent form over every sequence's tokens, memory updated in place (decoding).
 hipError_t run_decode(const Geo& g, int variant, int gates, int dtype, int D, const gdr_inputs& in, float* state,

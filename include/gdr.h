@@ -92,9 +92,8 @@ typedef struct {
                                      row left zero) and dq, dk are gradients w.r.t. the raw q, k.
                                      Done inside the kernels (the inverse norms, 2 floats per
                                      token and head, are part of the saved cache); the backward
-                                     maps dq, dk back to the raw rows inside its last kernel,
-                                     except for Kimi Delta Attention and the erase-free variant
-                                     (a pass after the backward).  Every
+                                     maps dq, dk back to the raw rows inside its last kernel.
+                                     Every
                                      variant in gdr_forward and gdr_backward; gdr_decode returns
                                      UNSUPPORTED (normalise there before the call) */
 } gdr_problem;
