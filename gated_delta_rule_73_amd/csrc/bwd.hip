@@ -170,6 +170,10 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
     if (part <= 0) {
+      if constexpr (QKN) {  // first, so that the step's waits for them wait for little else
+        load_row_factors(p.dO, Rng + u * 2 * CH, p.rnq);
+        p.rnk = Rng[u * 2 * CH + CH + (G2 ? (int)(threadIdx.x & (CH - 1)) : 16 * w + lrow())];
+      }
       if constexpr (!NOX) p.x.load(Xg + u * CH * D, D, CH);
       p.m.load(Mg + u * CH * CH, CH, CH);
       p.dO.load(dO + tk * D + i0, D, n);
@@ -184,10 +188,6 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
         p.q.load(q + tk * D, D, n);
         p.k.load(k + tk * D, D, n);
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
-        if constexpr (QKN) {  // read before the next refill of this set
-          load_row_factors(p.dO, Rng + u * 2 * CH, p.rnq);
-          p.rnk = Rng[u * 2 * CH + CH + (G2 ? (int)(threadIdx.x & (CH - 1)) : 16 * w + lrow())];
-        }
       }
       if constexpr (RES) {  // accumulator layout of dR^T: row 16 w + lrow, columns 16 it + 4 lgrp
         const int t = min(16 * w + lrow(), n - 1);
@@ -206,6 +206,8 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
   auto step = [&](int c, Ops& p) {
     const long u = (long)(sp.gc0 + c) * geo.H + h;
     [[maybe_unused]] const int n = min(CH, sp.len - c * CH);
+    float rnk_c = 0.f;  // this chunk's key factor, kept before p is refilled (the dO rows' are used first)
+    if constexpr (QKN) rnk_c = p.rnk;
     p.q.store(Qs, LD);
     p.k.store(Ks, LD);
     if constexpr (!NOX) p.x.store(Xs, LD);
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
       if (threadIdx.x < CH)  // beta (1 when absent), 0 past the end; converted here, where it is used
         bsh[threadIdx.x] = ((int)threadIdx.x < n) ? (beta ? g2_gate<G2L>(gate_from_raw<E>(p.braw2)) : 1.f) : 0.f;
       if constexpr (QKN) {
-        if (threadIdx.x < CH) rks[threadIdx.x] = p.rnk;
+        if (threadIdx.x < CH) rks[threadIdx.x] = rnk_c;
       }
     }
 #pragma unroll
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(256) void k_bwd_scan(Geo geo, ScanSeg sg, const E* 
     const int tl = 16 * w + lrow();
     float dec = 1.f;  // e^{g_n - g_t} (times 1 / ||k_t||: dW meets the raw k_t)
     if constexpr (DEC) dec = __expf(gn - gs[tl]);
-    if constexpr (QKN && !G2) dec *= p.rnk;
+    if constexpr (QKN && !G2) dec *= rnk_c;
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const f32x4 a1 = mma_k<E, CH>(zero4(), colk(dOt, LDO), 16 * it, colk(Ms, LDR), 16 * w);

@@ -322,6 +322,10 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     const int n = min(CH, sp.len - cc * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + cc * CH);
     if (part <= 0) {
+      if constexpr (QKN) {  // first, so that the step's wait for them waits for little else
+        p.rnq = Rng[u * 2 * CH + 16 * w + lrow()];  // the row this lane holds in R^T and O^T
+        p.rnk = Rng[u * 2 * CH + CH + (G2 ? (int)(threadIdx.x & (CH - 1)) : 16 * w + lrow())];
+      }
       if constexpr (!NOX) p.x.load(Xg + u * CH * D, D, CH);
       p.u.load(Ug + u * CH * D + i0, D, CH);
       if constexpr (KDA) {
@@ -342,10 +346,6 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       } else {
         p.k.load(k + tk * D, D, n);
         p.g = Gg[u * CH + (threadIdx.x & (CH - 1))];
-        if constexpr (QKN) {  // for the row this lane holds in R^T and O^T (read before the next refill)
-          p.rnq = Rng[u * 2 * CH + 16 * w + lrow()];
-          p.rnk = Rng[u * 2 * CH + CH + (G2 ? (int)(threadIdx.x & (CH - 1)) : 16 * w + lrow())];
-        }
       }
       if constexpr (RES) {  // a plain load (valid row), no arithmetic on it until the step uses it
         const int t = min((int)(threadIdx.x & (CH - 1)), n - 1);
@@ -363,7 +363,12 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     const long u = (long)(sp.gc0 + c) * geo.H + h;
     const int n = min(CH, sp.len - c * CH);
     const long tk = tok_index(geo, sp.b, h, sp.bos + c * CH);
-      if constexpr (!NOX) p.x.store(Xs, LD);
+    float rnq_c = 0.f, rnk_c = 0.f;  // this chunk's factors, kept before p is refilled
+    if constexpr (QKN) {
+      rnq_c = p.rnq;
+      rnk_c = p.rnk;
+    }
+    if constexpr (!NOX) p.x.store(Xs, LD);
     p.k.store(Ks, LD);
     p.u.store(Us, LDV);
     if constexpr (FULL) {
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
       if (threadIdx.x < CH)  // beta (1 when absent), 0 past the end; converted here, where it is used
         bsh[threadIdx.x] = ((int)threadIdx.x < n) ? (beta ? g2_gate<G2L>(gate_from_raw<E>(p.braw2)) : 1.f) : 0.f;
       if constexpr (QKN) {
-        if (threadIdx.x < CH) rks[threadIdx.x] = p.rnk;
+        if (threadIdx.x < CH) rks[threadIdx.x] = rnk_c;
       }
     }
     if constexpr (RES) {  // residual output: 1 / beta (0 past the end)
@@ -432,7 +437,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
     const int tl = 16 * w + lrow();
     float dec = 1.f;  // e^{g_n - g_t} (times 1 / ||k_t||: the row of R that meets the raw k_t)
     if constexpr (DEC) dec = __expf(gn - gs[tl]);
-    if constexpr (QKN && !G2) dec *= p.rnk;
+    if constexpr (QKN && !G2) dec *= rnk_c;
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       f32x4 acc = zero4();
@@ -458,7 +463,7 @@ __global__ __launch_bounds__(256) void k_fwd_scan(Geo geo, ScanSeg sg, const E* 
           if constexpr (G2) a2 = mma_k<E, CH>(a2, colk(Bn, LDV), 16 * it, rowk(M2s, LDR), 16 * w);
           float e = 1.f;  // e^{g_t} (times 1 / ||q_t||: the product used the raw q_t)
           if constexpr (DEC) e = __expf(gs[tl]);
-          if constexpr (QKN) e *= p.rnq;
+          if constexpr (QKN) e *= rnq_c;
           put4(Os + tl * LDV + 16 * it + 4 * lgrp(), geo.scale * (e * a1 + a2));
         }
       }
